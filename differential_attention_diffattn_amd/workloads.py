@@ -1,0 +1,154 @@
+"""Seeded synthetic workloads for differential attention.
+
+This module only draws random tensors and names shapes; it holds none of the
+method's arithmetic.  Both the HIP path (tests, bench) and the fp64 oracle
+(tests) take their inputs from here, so the two sides see identical values.
+
+Distributions follow the pages: activations N(0, 1); the four V1 lambda
+vectors N(0, 0.1) in fp32 (nanoGPT issue "How best to implement a
+differential transformer?", Wilsontomass's module, the lambda parameter
+initialisation); V2 lambda logits N(0, 1) in fp32.  Values are drawn in fp32
+with a seeded ``torch.Generator`` and then rounded (RNE) to the working dtype;
+the order of draws is fixed per workload.
+
+Shapes: the five workloads below.  The GPT-2-small and 3B-class shapes stand
+in for the models the pages name (a GPT-2 124M nanoGPT run; a 3B model with
+28 layers, hidden 3072, 12 heads); no dataset, checkpoint or real activation
+is available, so seeded N(0, 1) tensors stand in for them.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Tuple
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str  # "v1", "v2", "decode"
+    dtype: str  # "fp32" or "bf16"
+    B: int
+    H: int = 0  # V1: differential heads
+    T: int = 0  # V1/V2: tokens; decode: cache length L
+    d: int = 0
+    Hq: int = 0
+    Hkv: int = 0
+    layers: Tuple[int, ...] = ()
+    seed: int = 0
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+    def flops(self) -> float:
+        """Algorithmic flops of one call, counting only unmasked (i, j<=i)
+        pairs: V1 = 2 maps x (QK^T over d + PV over 2d) = 6*B*H*d*T(T+1);
+        V2 prefill = 2*B*Hq*d*T(T+1); decode = 4*B*Hq*d*L."""
+        if self.kind == "v1":
+            return 6.0 * self.B * self.H * self.d * self.T * (self.T + 1)
+        if self.kind == "v2":
+            return 2.0 * self.B * self.Hq * self.d * self.T * (self.T + 1)
+        return 4.0 * self.B * self.Hq * self.d * self.T
+
+    def compulsory_bytes(self) -> int:
+        """Bytes every call must move between HBM and the chip at least once:
+        each input read once, the output written once."""
+        e = 4 if self.dtype == "fp32" else 2
+        if self.kind == "v1":
+            B, H, T, d = self.B, self.H, self.T, self.d
+            return e * (4 * B * H * T * d + B * H * T * 2 * d + B * T * H * 2 * d) + 4 * 4 * d
+        if self.kind == "v2":
+            B, T, Hq, Hkv, d = self.B, self.T, self.Hq, self.Hkv, self.d
+            return e * (B * T * Hq * d + 2 * B * T * Hkv * d + B * T * (Hq // 2) * d) + 4 * B * T * (Hq // 2)
+        B, L, Hq, Hkv, d = self.B, self.T, self.Hq, self.Hkv, self.d
+        return e * (B * Hq * d + 2 * B * L * Hkv * d + B * (Hq // 2) * d) + 4 * B * (Hq // 2)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("v1_fp32_B1_H2_T128_d32", "v1", "fp32", B=1, H=2, T=128, d=32, layers=(3,), seed=1),
+        Workload("v1_gpt2small_B8_H6_T1024_d64", "v1", "bf16", B=8, H=6, T=1024, d=64,
+                 layers=tuple(range(12)), seed=2),
+        Workload("v1_3b_B2_H12_T4096_d128", "v1", "bf16", B=2, H=12, T=4096, d=128, layers=(14,), seed=3),
+        Workload("v2_prefill_B1_T8192_Hq64_Hkv8_d128", "v2", "bf16", B=1, T=8192, d=128, Hq=64, Hkv=8, seed=4),
+        Workload("v2_decode_B64_L32768_Hq64_Hkv8_d128", "decode", "bf16", B=64, T=32768, d=128, Hq=64,
+                 Hkv=8, seed=5),
+    ]
+}
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _randn(shape, g, device, dtype, std: float = 1.0, chunk_rows: int = 0) -> torch.Tensor:
+    """fp32 N(0, std^2) draws rounded to ``dtype``.  With ``chunk_rows`` the
+    draw is made in slices of the leading dimension to bound the fp32
+    temporary (used for multi-GB KV caches)."""
+    if chunk_rows <= 0 or shape[0] <= chunk_rows:
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(std)
+        return x.to(dtype)
+    out = torch.empty(shape, device=device, dtype=dtype)
+    for s in range(0, shape[0], chunk_rows):
+        e = min(shape[0], s + chunk_rows)
+        x = torch.randn((e - s,) + tuple(shape[1:]), generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(std)
+        out[s:e].copy_(x)
+        del x
+    return out
+
+
+def v1_inputs(B: int, H: int, T: int, d: int, dtype=torch.bfloat16, seed: int = 0,
+              device="cpu") -> Dict[str, torch.Tensor]:
+    """q1, q2, k1, k2 ``[B, H, T, d]``; v ``[B, H, T, 2d]`` (dtype);
+    lq1, lk1, lq2, lk2 ``[d]`` fp32 ~ N(0, 0.1)."""
+    g = _gen(seed, device)
+    out = {}
+    for name in ("q1", "q2", "k1", "k2"):
+        out[name] = _randn((B, H, T, d), g, device, dtype)
+    out["v"] = _randn((B, H, T, 2 * d), g, device, dtype)
+    for name in ("lq1", "lk1", "lq2", "lk2"):
+        out[name] = _randn((d,), g, device, torch.float32, std=0.1)
+    return out
+
+
+def v2_inputs(B: int, T: int, Hq: int, Hkv: int, d: int, dtype=torch.bfloat16, seed: int = 0,
+              device="cpu") -> Dict[str, torch.Tensor]:
+    """q ``[B, T, Hq, d]``; k, v ``[B, T, Hkv, d]`` (dtype); lam ``[B, T, Hq/2]``
+    fp32 logits ~ N(0, 1)."""
+    g = _gen(seed, device)
+    return {
+        "q": _randn((B, T, Hq, d), g, device, dtype),
+        "k": _randn((B, T, Hkv, d), g, device, dtype),
+        "v": _randn((B, T, Hkv, d), g, device, dtype),
+        "lam": _randn((B, T, Hq // 2), g, device, torch.float32),
+    }
+
+
+def decode_inputs(B: int, L: int, Hq: int, Hkv: int, d: int, dtype=torch.bfloat16, seed: int = 0,
+                  device="cpu") -> Dict[str, torch.Tensor]:
+    """q ``[B, Hq, d]``; k_cache, v_cache ``[B, L, Hkv, d]`` (dtype, contiguous);
+    lam ``[B, Hq/2]`` fp32 logits ~ N(0, 1)."""
+    g = _gen(seed, device)
+    return {
+        "q": _randn((B, Hq, d), g, device, dtype),
+        "k": _randn((B, L, Hkv, d), g, device, dtype, chunk_rows=4),
+        "v": _randn((B, L, Hkv, d), g, device, dtype, chunk_rows=4),
+        "lam": _randn((B, Hq // 2), g, device, torch.float32),
+    }
+
+
+def inputs_for(w: Workload, device="cpu") -> Dict[str, torch.Tensor]:
+    if w.kind == "v1":
+        return v1_inputs(w.B, w.H, w.T, w.d, w.torch_dtype, w.seed, device)
+    if w.kind == "v2":
+        return v2_inputs(w.B, w.T, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)
+    return decode_inputs(w.B, w.T, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)

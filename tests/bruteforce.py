@@ -1,0 +1,77 @@
+"""Brute-force fp64 differential attention with explicit T x T maps (numpy).
+
+A second, independent formulation used only to pin the oracle on tiny
+inputs.  It follows the matrix form of notlober's module in the nanoGPT issue
+"How best to implement a differential transformer?": whole score maps,
+masked with -inf above the diagonal, softmax along keys, the two maps
+combined as A1 - lambda*A2 BEFORE multiplying by V, then the per-head norm
+and the (1 - lambda_init) scale.  Two deviations of that module are not
+followed, because the "Differential Transformer V2" article (DiffAttnV1
+pseudo-code) is the authority: the norm is RMSNorm (not LayerNorm with
+affine), and lambda_init uses the layer's own index (not the layer count).
+
+This shares no code with ``oracle/`` (which computes one softmax row at a
+time, maps separately, and combines after P.V).
+"""
+import math
+
+import numpy as np
+from scipy.special import expit
+
+
+def _causal_softmax(s: np.ndarray) -> np.ndarray:
+    """Row softmax of ``s[..., T, T]`` with keys j > i masked to -inf."""
+    T = s.shape[-1]
+    mask = np.triu(np.ones((T, T), dtype=bool), k=1)
+    s = np.where(mask, -np.inf, s)
+    s = s - s.max(axis=-1, keepdims=True)
+    e = np.exp(s)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def v1(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer):
+    """q*, k* [B,H,T,d]; v [B,H,T,2d]; returns [B,T,H,2d]."""
+    d = q1.shape[-1]
+    a1 = _causal_softmax(q1 @ np.swapaxes(k1, -1, -2) / math.sqrt(d))
+    a2 = _causal_softmax(q2 @ np.swapaxes(k2, -1, -2) / math.sqrt(d))
+    li = 0.8 - 0.6 * math.exp(-0.3 * layer)
+    lam = math.exp(float(np.sum(lq1 * lk1))) - math.exp(float(np.sum(lq2 * lk2))) + li
+    w = a1 - lam * a2  # [B,H,T,T]
+    o = w @ v  # [B,H,T,2d]
+    o = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + 1e-5)
+    o = o * (1.0 - li)
+    return np.transpose(o, (0, 2, 1, 3))
+
+
+def _gqa_attention(q, k, v, causal=True):
+    """q [B,Tq,Hq,d], k/v [B,Tk,Hkv,d] -> [B,Tq,Hq,d]; head h uses kv head
+    h // (Hq/Hkv).  causal masks j > i (Tq == Tk); otherwise all keys."""
+    B, Tq, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    kr = np.repeat(k, G, axis=2)  # [B,Tk,Hq,d]
+    vr = np.repeat(v, G, axis=2)
+    qh = np.transpose(q, (0, 2, 1, 3))
+    kh = np.transpose(kr, (0, 2, 1, 3))
+    vh = np.transpose(vr, (0, 2, 1, 3))
+    s = qh @ np.swapaxes(kh, -1, -2) / math.sqrt(d)
+    if causal:
+        a = _causal_softmax(s)
+    else:
+        s = s - s.max(axis=-1, keepdims=True)
+        e = np.exp(s)
+        a = e / e.sum(axis=-1, keepdims=True)
+    return np.transpose(a @ vh, (0, 2, 1, 3))
+
+
+def v2(q, k, v, lam):
+    """q [B,T,Hq,d], k/v [B,T,Hkv,d], lam [B,T,Hq/2] -> [B,T,Hq/2,d]."""
+    a = _gqa_attention(q, k, v, causal=True)
+    return a[:, :, 0::2] - expit(lam)[..., None] * a[:, :, 1::2]
+
+
+def v2_decode(q, k, v, lam):
+    """q [B,Hq,d], k/v [B,L,Hkv,d], lam [B,Hq/2] -> [B,Hq/2,d]; the query
+    sees every cache entry."""
+    a = _gqa_attention(q[:, None], k, v, causal=False)[:, 0]
+    return a[:, 0::2] - expit(lam)[..., None] * a[:, 1::2]

@@ -1,0 +1,350 @@
+"""Pins for the fp64 oracle: checks against things other than the oracle itself.
+
+The pages print no worked numerical example for this method, so every pin is
+constructed from what the pages and the mathematics fix:
+
+* brute force: an independent explicit-map formulation (tests/bruteforce.py)
+  on tiny hypothesis-drawn shapes;
+* library routines: torch's scaled_dot_product_attention and rms_norm (fp64,
+  CPU) where the method reduces to plain causal attention (lambda = 0,
+  sigmoid = 0, identical branches);
+* closed forms: T = 1, uniform attention (Q = 0 gives prefix means), needle
+  keys on and just past the diagonal, lambda_init special values;
+* invariants: odd symmetry in V, linearity of V2 in V, batch permutation,
+  GQA group mapping.
+"""
+import math
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from hypothesis import given, settings, strategies as st
+
+import bruteforce
+import oracle
+
+RTOL = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _v1_case(rng, B, H, T, d, lam_std=0.1):
+    q1, q2, k1, k2 = (rng.standard_normal((B, H, T, d)) for _ in range(4))
+    v = rng.standard_normal((B, H, T, 2 * d))
+    lams = [lam_std * rng.standard_normal(d) for _ in range(4)]
+    return q1, q2, k1, k2, v, lams
+
+
+def _v2_case(rng, B, T, Hq, Hkv, d):
+    q = rng.standard_normal((B, T, Hq, d))
+    k = rng.standard_normal((B, T, Hkv, d))
+    v = rng.standard_normal((B, T, Hkv, d))
+    lam = rng.standard_normal((B, T, Hq // 2))
+    return q, k, v, lam
+
+
+def _close(a, b, rtol=RTOL, atol=1e-13):
+    np.testing.assert_allclose(a, b, rtol=rtol, atol=atol)
+
+
+# --------------------------------------------------------------------------
+# lambda_init = 0.8 - 0.6 exp(-0.3 layer)  ("Differential Transformer V2",
+# DiffAttnV1; Hacker News item 41780844, the quoted constant)
+# --------------------------------------------------------------------------
+
+def test_lambda_init_special_values():
+    assert abs(oracle.lambda_init(0) - 0.2) < 1e-15  # 0.8 - 0.6 * e^0
+    assert abs(oracle.lambda_init(400) - 0.8) < 1e-15  # decays to 0.8
+    vals = [oracle.lambda_init(l) for l in range(40)]
+    assert all(a < b for a, b in zip(vals, vals[1:]))  # increasing in depth
+    assert all(0.2 <= x < 0.8 for x in vals)
+
+
+def test_lambda_init_geometric_gap_decimal():
+    """The gap to 0.8 shrinks by e^-0.3 per layer; e^-0.3 comes from Python's
+    decimal module, an exp implementation independent of libm."""
+    getcontext().prec = 40
+    ratio = float(Decimal("-0.3").exp())
+    for l in range(30):
+        g0 = 0.8 - oracle.lambda_init(l)
+        g1 = 0.8 - oracle.lambda_init(l + 1)
+        assert abs(g1 / g0 - ratio) < 1e-12
+    for l in range(16):
+        ref = Decimal("0.8") - Decimal("0.6") * (Decimal(-3 * l) / Decimal(10)).exp()
+        assert abs(oracle.lambda_init(l) - float(ref)) < 1e-15
+
+
+def test_v1_lambda_special_cases():
+    rng = _rng(0)
+    d = 8
+    z = np.zeros(d)
+    for layer in (0, 3, 11):
+        li = oracle.lambda_init(layer)
+        # all-zero vectors: exp(0) - exp(0) + li
+        assert abs(oracle.v1_lambda(z, z, z, z, layer) - li) < 1e-15
+        # identical pairs cancel
+        a, b = rng.standard_normal(d), rng.standard_normal(d)
+        assert abs(oracle.v1_lambda(a, b, a, b, layer) - li) < 1e-14
+    # one active coordinate: exp(2*3) - exp(0) + li(2)
+    a = np.zeros(d); a[5] = 2.0
+    b = np.zeros(d); b[5] = 3.0
+    assert abs(oracle.v1_lambda(a, b, z, z, 2) - (math.exp(6.0) - 1.0 + oracle.lambda_init(2))) < 1e-11
+    # sign: the second exponential is subtracted
+    assert abs(oracle.v1_lambda(z, z, a, b, 2) - (1.0 - math.exp(6.0) + oracle.lambda_init(2))) < 1e-11
+
+
+# --------------------------------------------------------------------------
+# brute force on tiny shapes
+# --------------------------------------------------------------------------
+
+@settings(max_examples=40, deadline=None)
+@given(B=st.integers(1, 2), H=st.integers(1, 3), T=st.sampled_from([1, 2, 3, 7, 16, 33]),
+       d=st.sampled_from([4, 8, 32]), layer=st.integers(0, 20), seed=st.integers(0, 10**6))
+def test_v1_matches_bruteforce(B, H, T, d, layer, seed):
+    q1, q2, k1, k2, v, lams = _v1_case(_rng(seed), B, H, T, d, lam_std=0.3)
+    got = oracle.v1_fwd(q1, q2, k1, k2, v, *lams, layer)
+    ref = bruteforce.v1(q1, q2, k1, k2, v, *lams, layer)
+    _close(got, ref, rtol=1e-10, atol=1e-11)
+
+
+@settings(max_examples=40, deadline=None)
+@given(B=st.integers(1, 2), T=st.sampled_from([1, 2, 5, 16, 33]), Hkv=st.integers(1, 3),
+       G=st.sampled_from([2, 4]), d=st.sampled_from([4, 8, 16]), seed=st.integers(0, 10**6))
+def test_v2_matches_bruteforce(B, T, Hkv, G, d, seed):
+    q, k, v, lam = _v2_case(_rng(seed), B, T, G * Hkv, Hkv, d)
+    _close(oracle.v2_fwd(q, k, v, lam), bruteforce.v2(q, k, v, lam))
+
+
+@settings(max_examples=30, deadline=None)
+@given(B=st.integers(1, 3), L=st.sampled_from([1, 2, 9, 64, 100]), Hkv=st.integers(1, 3),
+       G=st.sampled_from([2, 4, 8]), d=st.sampled_from([4, 16]), seed=st.integers(0, 10**6))
+def test_decode_matches_bruteforce(B, L, Hkv, G, d, seed):
+    rng = _rng(seed)
+    Hq = G * Hkv
+    q = rng.standard_normal((B, Hq, d))
+    k = rng.standard_normal((B, L, Hkv, d))
+    v = rng.standard_normal((B, L, Hkv, d))
+    lam = rng.standard_normal((B, Hq // 2))
+    _close(oracle.v2_decode(q, k, v, lam), bruteforce.v2_decode(q, k, v, lam))
+
+
+# --------------------------------------------------------------------------
+# reductions to plain causal attention (torch SDPA + rms_norm, fp64, CPU)
+# --------------------------------------------------------------------------
+
+def _sdpa(q, k, v):
+    """Causal SDPA with torch's default 1/sqrt(E) scale; q,k [.., T, E], v [.., T, Ev]."""
+    t = [torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v)]
+    return F.scaled_dot_product_attention(*t, is_causal=True).numpy()
+
+
+def _rmsnorm(x):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return F.rms_norm(t, (t.shape[-1],), eps=1e-5).numpy()
+
+
+@pytest.mark.parametrize("layer", [0, 3, 14])
+def test_v1_lambda_zero_is_plain_attention(layer):
+    """lambda = 0 (lq1 = 0, lq2 = lk2 = c*1 with d c^2 = ln(1 + li)): the
+    output is (1 - li) * RMSNorm(SDPA(Q1, K1, V))."""
+    rng = _rng(1 + layer)
+    B, H, T, d = 2, 3, 29, 16
+    q1, q2, k1, k2, v, lams = _v1_case(rng, B, H, T, d)
+    li = oracle.lambda_init(layer)
+    c = math.sqrt(math.log(1.0 + li) / d)
+    lq1, lk1 = np.zeros(d), rng.standard_normal(d)
+    lq2 = lk2 = np.full(d, c)
+    assert abs(oracle.v1_lambda(lq1, lk1, lq2, lk2, layer)) < 1e-14
+    got = oracle.v1_fwd(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer)
+    ref = (1.0 - li) * _rmsnorm(_sdpa(q1, k1, v))  # [B,H,T,2d]
+    _close(got, np.transpose(ref, (0, 2, 1, 3)), rtol=1e-10, atol=1e-12)
+
+
+def test_v1_identical_branches():
+    """Q2 = Q1, K2 = K1: the two maps coincide and A - lambda*A = (1 - lambda)*A
+    (Hacker News "Differential Transformer" board, post #131), so the output is
+    (1 - li) * RMSNorm((1 - lambda) * SDPA(Q1, K1, V))."""
+    rng = _rng(7)
+    B, H, T, d, layer = 1, 2, 40, 8, 5
+    q1, _, k1, _, v, lams = _v1_case(rng, B, H, T, d, lam_std=0.4)
+    lam = oracle.v1_lambda(*lams, layer)
+    assert abs(1.0 - lam) > 0.05
+    li = oracle.lambda_init(layer)
+    got = oracle.v1_fwd(q1, q1, k1, k1, v, *lams, layer)
+    ref = (1.0 - li) * _rmsnorm((1.0 - lam) * _sdpa(q1, k1, v))
+    _close(got, np.transpose(ref, (0, 2, 1, 3)), rtol=1e-10, atol=1e-12)
+
+
+def test_v2_sigmoid_zero_is_plain_gqa_attention():
+    """lam = -inf gives sigmoid = 0 exactly: out[:, :, p] = SDPA(q_{2p}, K_g, V_g)
+    with g = 2p // (Hq/Hkv)."""
+    rng = _rng(3)
+    B, T, Hq, Hkv, d = 2, 23, 8, 2, 16
+    q, k, v, _ = _v2_case(rng, B, T, Hq, Hkv, d)
+    lam = np.full((B, T, Hq // 2), -np.inf)
+    got = oracle.v2_fwd(q, k, v, lam)
+    G = Hq // Hkv
+    for p in range(Hq // 2):
+        h, g = 2 * p, (2 * p) // G
+        ref = _sdpa(q[:, :, h].transpose(0, 1, 2)[:, None], k[:, :, g][:, None], v[:, :, g][:, None])[:, 0]
+        _close(got[:, :, p], ref)
+
+
+def test_v2_identical_heads_and_full_gate():
+    """q_{2p+1} = q_{2p}: out = (1 - sigmoid(lam)) * a_{2p}; with lam = +inf the
+    pair cancels to exactly zero."""
+    rng = _rng(4)
+    B, T, Hq, Hkv, d = 1, 17, 4, 1, 8
+    q, k, v, lam = _v2_case(rng, B, T, Hq, Hkv, d)
+    q[:, :, 1::2] = q[:, :, 0::2]
+    got = oracle.v2_fwd(q, k, v, lam)
+    a = np.stack([_sdpa(q[:, None, :, 2 * p], k[:, None, :, 0], v[:, None, :, 0])[:, 0]
+                  for p in range(Hq // 2)], axis=2)
+    sig = 1.0 / (1.0 + np.exp(-lam))
+    _close(got, (1.0 - sig)[..., None] * a)
+    zero = oracle.v2_fwd(q, k, v, np.full_like(lam, np.inf))
+    assert np.array_equal(zero, np.zeros_like(zero))
+
+
+# --------------------------------------------------------------------------
+# closed forms
+# --------------------------------------------------------------------------
+
+def test_t1_closed_forms():
+    """T = 1: each map returns v_0, so V1 gives (1-li)(1-lam)v0 /
+    sqrt((1-lam)^2 mean(v0^2) + 1e-5) and V2 gives (1 - sigmoid) v0."""
+    rng = _rng(5)
+    d, layer = 16, 9
+    q1, q2, k1, k2, v, lams = _v1_case(rng, 2, 3, 1, d, lam_std=0.5)
+    lam = oracle.v1_lambda(*lams, layer)
+    li = oracle.lambda_init(layer)
+    got = oracle.v1_fwd(q1, q2, k1, k2, v, *lams, layer)[:, 0]  # [B,H,2d]
+    v0 = v[:, :, 0]
+    ref = (1 - li) * (1 - lam) * v0 / np.sqrt((1 - lam) ** 2 * np.mean(v0 * v0, -1, keepdims=True) + 1e-5)
+    _close(got, ref)
+    q, k, vv, lg = _v2_case(rng, 2, 1, 8, 2, d)
+    got2 = oracle.v2_fwd(q, k, vv, lg)[:, 0]  # [B,P,d]
+    sig = 1.0 / (1.0 + np.exp(-lg[:, 0]))
+    ref2 = (1 - sig)[..., None] * np.repeat(vv[:, 0], 2, axis=1)  # pairs 0,1 -> group 0; 2,3 -> 1
+    _close(got2, ref2)
+
+
+def test_uniform_attention_prefix_mean():
+    """Q = 0: every visible score is 0, each row is uniform over j <= i and A.V
+    is the prefix mean of V."""
+    rng = _rng(6)
+    B, H, T, d, layer = 1, 2, 50, 8, 4
+    _, _, k1, k2, v, lams = _v1_case(rng, B, H, T, d, lam_std=0.3)
+    z = np.zeros((B, H, T, d))
+    lam = oracle.v1_lambda(*lams, layer)
+    li = oracle.lambda_init(layer)
+    pm = np.cumsum(v, axis=2) / np.arange(1, T + 1)[None, None, :, None]
+    D = (1 - lam) * pm
+    ref = (1 - li) * D / np.sqrt(np.mean(D * D, -1, keepdims=True) + 1e-5)
+    _close(oracle.v1_fwd(z, z, k1, k2, v, *lams, layer), np.transpose(ref, (0, 2, 1, 3)))
+    q, k, vv, lg = _v2_case(rng, 2, 37, 8, 2, d)
+    pm2 = np.cumsum(vv, axis=1) / np.arange(1, 38)[None, :, None, None]  # [B,T,Hkv,d]
+    sig = 1.0 / (1.0 + np.exp(-lg))
+    ref2 = (1 - sig)[..., None] * np.repeat(pm2, 2, axis=2)
+    _close(oracle.v2_fwd(np.zeros_like(q), k, vv, lg), ref2)
+
+
+@pytest.mark.parametrize("offset,visible", [(0, True), (1, False)])
+def test_needle_on_and_past_the_diagonal(offset, visible):
+    """Query i = a*e0, key i+offset = e0, every other key has coordinate 0 = 0.
+    On the diagonal (offset 0) the map is one-hot at key i (error ~e^-40);
+    one past it (offset 1) the key is masked and the row is uniform."""
+    d, T = 8, 24
+    rng = _rng(10 + offset)
+    alpha = 40.0 * math.sqrt(d)
+    q = np.zeros((1, 1, T, d)); k = rng.standard_normal((1, 1, T, d)); k[..., 0] = 0.0
+    v = rng.standard_normal((1, 1, T, 2 * d))
+    i = 11
+    q[0, 0, i, 0] = alpha
+    k[0, 0, i + offset] = 0.0
+    k[0, 0, i + offset, 0] = 1.0
+    z = np.zeros(d)
+    li = oracle.lambda_init(0)
+    # lambda = li with zero vectors; second map uses q2 = 0 (uniform)
+    out = oracle.v1_fwd(q, np.zeros_like(q), k, k, v, z, z, z, z, 0)[0, i, 0]
+    a1 = v[0, 0, i] if visible else v[0, 0, : i + 1].mean(axis=0)
+    D = a1 - li * v[0, 0, : i + 1].mean(axis=0)
+    ref = (1 - li) * D / math.sqrt(np.mean(D * D) + 1e-5)
+    _close(out, ref, rtol=1e-9, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# invariants
+# --------------------------------------------------------------------------
+
+def test_v1_odd_symmetry_and_scale():
+    rng = _rng(8)
+    q1, q2, k1, k2, v, lams = _v1_case(rng, 1, 2, 20, 8)
+    a = oracle.v1_fwd(q1, q2, k1, k2, v, *lams, 2)
+    b = oracle.v1_fwd(q1, q2, k1, k2, -v, *lams, 2)
+    assert np.array_equal(a, -b)  # exact: every step is odd in V
+    # RMSNorm removes the scale of V up to eps: at x1000 and x2000 the eps
+    # term is ~1e-11 of mean(D^2), so the two agree to ~1e-11.
+    c = oracle.v1_fwd(q1, q2, k1, k2, 1000.0 * v, *lams, 2)
+    e = oracle.v1_fwd(q1, q2, k1, k2, 2000.0 * v, *lams, 2)
+    _close(c, e, rtol=1e-9, atol=1e-10)
+    assert np.max(np.abs(c - a)) > 1e-7  # while at scale 1 eps is visible
+
+
+def test_v2_linear_in_v():
+    rng = _rng(9)
+    q, k, v, lam = _v2_case(rng, 1, 19, 4, 2, 8)
+    w = rng.standard_normal(v.shape)
+    lhs = oracle.v2_fwd(q, k, 2.0 * v - 3.0 * w, lam)
+    rhs = 2.0 * oracle.v2_fwd(q, k, v, lam) - 3.0 * oracle.v2_fwd(q, k, w, lam)
+    _close(lhs, rhs, rtol=1e-10, atol=1e-12)
+
+
+def test_v2_gqa_group_mapping():
+    """Heads of one GQA group are contiguous: with V_g = (g+1) everywhere and
+    sigmoid = 0, pair p reads group (2p) // (Hq/Hkv)."""
+    rng = _rng(11)
+    B, T, Hq, Hkv, d = 1, 9, 12, 3, 4
+    q, k, _, _ = _v2_case(rng, B, T, Hq, Hkv, d)
+    v = np.ones((B, T, Hkv, d)) * (np.arange(Hkv) + 1.0)[None, None, :, None]
+    out = oracle.v2_fwd(q, k, v, np.full((B, T, Hq // 2), -np.inf))
+    G = Hq // Hkv
+    for p in range(Hq // 2):
+        _close(out[:, :, p], np.full((B, T, d), (2 * p) // G + 1.0))
+
+
+def test_batch_permutation():
+    rng = _rng(12)
+    q1, q2, k1, k2, v, lams = _v1_case(rng, 3, 2, 12, 8)
+    perm = [2, 0, 1]
+    a = oracle.v1_fwd(q1, q2, k1, k2, v, *lams, 1)
+    b = oracle.v1_fwd(q1[perm], q2[perm], k1[perm], k2[perm], v[perm], *lams, 1)
+    assert np.array_equal(a[perm], b)
+
+
+def test_decode_equals_last_prefill_row():
+    rng = _rng(13)
+    q, k, v, lam = _v2_case(rng, 2, 31, 8, 2, 8)
+    full = oracle.v2_fwd(q, k, v, lam)
+    dec = oracle.v2_decode(q[:, -1], k, v, lam[:, -1])
+    _close(dec, full[:, -1])
+
+
+def test_row_variants_match_full():
+    rng = _rng(14)
+    q1, q2, k1, k2, v, lams = _v1_case(rng, 2, 3, 21, 8)
+    full = oracle.v1_fwd(q1, q2, k1, k2, v, *lams, 6)
+    idx = np.array([[0, 0, 0], [1, 2, 20], [0, 1, 7], [1, 0, 13]])
+    rows = oracle.v1_rows(q1, q2, k1, k2, v, *lams, 6, idx)
+    for r, (b, h, i) in enumerate(idx):
+        assert np.array_equal(rows[r], full[b, i, h])
+    q, k, vv, lam = _v2_case(rng, 2, 15, 8, 2, 8)
+    full2 = oracle.v2_fwd(q, k, vv, lam)
+    idx2 = np.array([[0, 0, 0], [1, 14, 3], [0, 7, 2]])
+    rows2 = oracle.v2_rows(q, k, vv, lam, idx2)
+    for r, (b, t, p) in enumerate(idx2):
+        assert np.array_equal(rows2[r], full2[b, t, p])
