@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Benchmark of the differential-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
+
+Headline workload (the `value`): the DIFF V1 causal forward at the GPT-2-small
+shape, B=8, T=1024, 6 differential heads, q/k head_dim 64, V width 128, bf16.
+One step = the 12 layer calls of a 12-layer model (layer index 0..11; only
+lambda_init differs between them).  value = algorithmic TFLOP/s over the K
+timed steps (only unmasked (i, j<=i) pairs are counted: 6*B*H*d*T(T+1) per
+call).  Inputs are seeded synthetic N(0,1) tensors already resident in HBM.
+
+The JSON line also carries:
+  roofline      the V1 kernel's per-launch duration (HIP events on the stream
+                the library launches on) against the bf16 dense MFMA peak;
+  cpu_baseline  the fp64 oracle timed on a bounded sample of the same
+                workload on this host's cores;
+  secondary     the other full-size workloads (3B-class V1, V2 GQA prefill,
+                V2 decode), each with its own roofline.
+Logs go to stderr; stdout holds exactly one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "diff-attn causal fwd TFLOP/s (bf16, % MFMA peak); V2 decode HBM GB/s (% peak)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+HEADLINE = "v1_gpt2small_B8_H6_T1024_d64"
+SECONDARY = ["v1_3b_B2_H12_T4096_d128", "v2_prefill_B1_T8192_Hq64_Hkv8_d128", "v2_decode_B64_L32768_Hq64_Hkv8_d128"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _caller(w, x, binding, torch):
+    """Return (fn(layer) -> None) that enqueues one call of workload w."""
+    if w.kind == "v1":
+        out = torch.empty((w.B, w.T, w.H, 2 * w.d), dtype=w.torch_dtype, device=x["v"].device)
+        args = [x[n] for n in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")]
+        return lambda layer: binding.v1_fwd(*args, layer, out=out)
+    if w.kind == "v2":
+        out = torch.empty((w.B, w.T, w.Hq // 2, w.d), dtype=w.torch_dtype, device=x["v"].device)
+        return lambda layer: binding.v2_fwd(x["q"], x["k"], x["v"], x["lam"], out=out)
+    out = torch.empty((w.B, w.Hq // 2, w.d), dtype=w.torch_dtype, device=x["v"].device)
+    ws = torch.empty(binding.v2_decode_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.d), dtype=torch.uint8,
+                     device=x["v"].device)
+    return lambda layer: binding.v2_decode(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws)
+
+
+def _timed(torch, call, layers, steps, warmup):
+    """Run `warmup` untimed steps, then exactly `steps` timed steps (one step
+    = one call per layer).  Returns (elapsed_s, per-launch ms list)."""
+    for _ in range(warmup):
+        for l in layers:
+            call(l)
+    torch.cuda.synchronize()
+    n = steps * len(layers)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    k = 0
+    for _ in range(steps):
+        for l in layers:
+            ev[k][0].record()
+            call(l)
+            ev[k][1].record()
+            k += 1
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    return elapsed, [a.elapsed_time(b) for a, b in ev]
+
+
+def _roofline(w, launch_ms):
+    avg_s = sum(launch_ms) / len(launch_ms) / 1e3
+    if w.kind == "decode":
+        a = w.compulsory_bytes() / avg_s / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(a / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel_ms": round(avg_s * 1e3, 5)}
+    a = w.flops() / avg_s / 1e12
+    return {"bound": "mfma", "achieved": round(a, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(a / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel_ms": round(avg_s * 1e3, 5)}
+
+
+def _cpu_baseline(w, x):
+    """Time the fp64 oracle on a bounded sample (leading batch entries of
+    layer 0) of the headline workload."""
+    import numpy as np
+
+    import oracle
+
+    cores = oracle.set_threads(len(os.sched_getaffinity(0)))
+    host = {n: x[n].detach().to("cpu").double().numpy() for n in x}
+    lam = [host[n] for n in ("lq1", "lk1", "lq2", "lk2")]
+
+    def run(nb):
+        args = [np.ascontiguousarray(host[n][:nb]) for n in ("q1", "q2", "k1", "k2", "v")]
+        t0 = time.perf_counter()
+        oracle.v1_fwd(*args, *lam, 0)
+        return time.perf_counter() - t0
+
+    nb, t = 1, run(1)
+    if t < 10.0 and w.B > 1:
+        nb = max(1, min(w.B, int(round(15.0 / max(t, 1e-3)))))
+        if nb > 1:
+            t = run(nb)
+    flops = w.flops() * nb / w.B
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(t, 3),
+            "sample": f"layer 0 of {w.name}, batch entries 0..{nb - 1} ({nb * w.H * w.T} rows), fp64 C + OpenMP"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default=None, help="time a single workload by name (no cpu baseline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); the kernels shard "
+              "by head/group with no exchange, so the 1-GPU figure is the per-GPU figure.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from differential_attention_diffattn_amd import binding, workloads
+
+    if not binding.library_path().exists():
+        import __graft_entry__
+
+        __graft_entry__.build()
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def measure(name, steps, warmup):
+        w = workloads.WORKLOADS[name]
+        x = workloads.inputs_for(w, dev)
+        call = _caller(w, x, binding, torch)
+        layers = list(w.layers) if w.layers else [0]
+        elapsed, launch_ms = _timed(torch, call, layers, steps, warmup)
+        per_call_s = elapsed / (steps * len(layers))
+        res = {"workload": name, "steps": steps, "warmup": warmup, "calls_per_step": len(layers),
+               "ms_per_step": round(elapsed / steps * 1e3, 5), "roofline": _roofline(w, launch_ms)}
+        if w.kind == "decode":
+            res.update(metric="V2 decode HBM GB/s", unit="GB/s",
+                       value=round(w.compulsory_bytes() / per_call_s / 1e9, 1))
+        else:
+            res.update(metric="causal fwd TFLOP/s", unit="TFLOP/s", value=round(w.flops() / per_call_s / 1e12, 3))
+        log(json.dumps(res))
+        return w, x, res
+
+    if args.only:
+        _, _, res = measure(args.only, args.steps, args.warmup)
+        print(json.dumps(res))
+        return
+
+    w, x, head = measure(HEADLINE, args.steps, args.warmup)
+    secondary = []
+    if not args.no_secondary:
+        for name in SECONDARY:
+            _, xs, r = measure(name, max(5, args.steps // 2), 3)
+            secondary.append(r)
+            del xs
+            torch.cuda.empty_cache()
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = _cpu_baseline(w, x)
+        log(json.dumps({"cpu_baseline": cpu}))
+
+    line = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) q/k/v, lambda vectors N(0,0.1) fp32; resident in HBM",
+        "config": {"workload": HEADLINE, "kind": "DIFF V1 causal forward", "B": w.B, "T": w.T, "H": w.H,
+                   "d": w.d, "dv": 2 * w.d, "layers": "0..11 (one step = 12 calls)", "parallelism": "none"},
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+"""ctypes binding over libdiffattn.so (include/diffattn.h).
+
+Argument marshalling only: tensors are passed as (data_ptr, role strides);
+every step of the computation runs in the library's HIP kernels.  torch is
+used for device memory, strides and the current stream.  If the library is
+not built the calls raise -- there is no fallback path.
+
+Logical layouts (any strided view with a unit-stride last axis is accepted):
+  v1_fwd     q1, q2, k1, k2 [B,H,T,d]; v [B,H,T,2d]; lambda vectors [d] fp32;
+             returns / writes out [B,T,H,2d]
+  v2_fwd     q [B,T,Hq,d]; k, v [B,T,Hkv,d]; lam [B,T,Hq/2] fp32 logits;
+             returns / writes out [B,T,Hq/2,d]
+  v2_decode  q [B,Hq,d]; k_cache, v_cache [B,L,Hkv,d]; lam [B,Hq/2] fp32;
+             returns / writes out [B,Hq/2,d]
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from pathlib import Path
+
+import torch
+
+_LIB_PATH = Path(__file__).resolve().parent / "libdiffattn.so"
+_lib = None
+
+DA_FP32, DA_BF16 = 0, 1
+_STATUS = {0: "DA_OK", 1: "DA_E_NULL", 2: "DA_E_DTYPE", 3: "DA_E_SHAPE", 4: "DA_E_LAYOUT",
+           5: "DA_E_UNSUPPORTED", 6: "DA_E_WORKSPACE", 7: "DA_E_LAUNCH"}
+
+
+class DiffAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = _STATUS.get(status, str(status))
+        msg = load_library().diffattn_status_string(status).decode()
+        super().__init__(f"{where}: {self.name} ({msg})")
+
+
+class DaIn(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("sb", ctypes.c_int64), ("sh", ctypes.c_int64), ("st", ctypes.c_int64)]
+
+
+class DaOut(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("sb", ctypes.c_int64), ("sh", ctypes.c_int64), ("st", ctypes.c_int64)]
+
+
+def library_path() -> Path:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libdiffattn.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists():
+        raise RuntimeError(f"{_LIB_PATH} is not built: run `python -m differential_attention_diffattn_amd.build` "
+                           "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    i, vp, fp = ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
+    lib.diffattn_v1_fwd.argtypes = [i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaIn, fp, fp, fp, fp, i, DaOut, vp]
+    lib.diffattn_v1_fwd.restype = i
+    lib.diffattn_v2_fwd.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaOut, vp]
+    lib.diffattn_v2_fwd.restype = i
+    lib.diffattn_v2_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.diffattn_v2_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.diffattn_v2_decode.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaOut, vp, ctypes.c_size_t, vp]
+    lib.diffattn_v2_decode.restype = i
+    lib.diffattn_lambda_init.argtypes = [i]
+    lib.diffattn_lambda_init.restype = ctypes.c_double
+    lib.diffattn_status_string.argtypes = [i]
+    lib.diffattn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DA_BF16
+    if t.dtype == torch.float32:
+        return DA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _in(t: torch.Tensor, b, h, tok) -> DaIn:
+    """Role strides of a tensor whose axes b/h/tok (None = absent) are given."""
+    s = t.stride()
+    return DaIn(t.data_ptr(), s[b] if b is not None else 0, s[h] if h is not None else 0,
+                s[tok] if tok is not None else 0)
+
+
+def _out(t: torch.Tensor, b, h, tok) -> DaOut:
+    s = t.stride()
+    return DaOut(t.data_ptr(), s[b] if b is not None else 0, s[h] if h is not None else 0,
+                 s[tok] if tok is not None else 0)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_device(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if t.device.type != "cuda" or t.device != dev:
+            raise ValueError("all tensors must be on the same CUDA (HIP) device")
+        if t.stride(-1) != 1 and t.shape[-1] > 1:
+            raise ValueError("the last (head_dim) axis must be unit-stride")
+
+
+def lambda_init(layer: int) -> float:
+    return load_library().diffattn_lambda_init(int(layer))
+
+
+def v1_fwd(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, out: torch.Tensor | None = None):
+    """DIFF V1 forward; q*/k* [B,H,T,d], v [B,H,T,2d]; returns out [B,T,H,2d]."""
+    lib = load_library()
+    B, H, T, d = q1.shape
+    for x in (q2, k1, k2):
+        if tuple(x.shape) != (B, H, T, d):
+            raise ValueError(f"q/k shape mismatch: {tuple(x.shape)} vs {(B, H, T, d)}")
+    if tuple(v.shape) != (B, H, T, 2 * d):
+        raise ValueError(f"v must be {(B, H, T, 2 * d)}, got {tuple(v.shape)}")
+    for x in (q2, k1, k2, v):
+        if x.dtype != q1.dtype:
+            raise TypeError("q1, q2, k1, k2, v must share one dtype")
+    lams = [x.contiguous() for x in (lq1, lk1, lq2, lk2)]
+    for x in lams:
+        if x.dtype != torch.float32 or tuple(x.shape) != (d,):
+            raise ValueError("lambda vectors must be fp32 of shape [d]")
+    if out is None:
+        out = torch.empty((B, T, H, 2 * d), dtype=q1.dtype, device=q1.device)
+    _check_device(q1, q2, k1, k2, v, out, *lams)
+    st = lib.diffattn_v1_fwd(_dtype_code(q1), B, H, T, d,
+                             _in(q1, 0, 1, 2), _in(q2, 0, 1, 2), _in(k1, 0, 1, 2), _in(k2, 0, 1, 2),
+                             _in(v, 0, 1, 2), *[x.data_ptr() for x in lams], int(layer),
+                             _out(out, 0, 2, 1), _stream(q1))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_v1_fwd")
+    return out
+
+
+def v2_fwd(q, k, v, lam, out: torch.Tensor | None = None):
+    """DIFF V2 prefill; q [B,T,Hq,d], k/v [B,T,Hkv,d], lam [B,T,Hq/2]; returns [B,T,Hq/2,d]."""
+    lib = load_library()
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, T, Hkv, d) or tuple(v.shape) != (B, T, Hkv, d):
+        raise ValueError("k, v must be [B,T,Hkv,d]")
+    if tuple(lam.shape) != (B, T, Hq // 2) or lam.dtype != torch.float32:
+        raise ValueError("lam must be fp32 [B,T,Hq/2]")
+    if out is None:
+        out = torch.empty((B, T, Hq // 2, d), dtype=q.dtype, device=q.device)
+    _check_device(q, k, v, out)
+    st = lib.diffattn_v2_fwd(_dtype_code(q), B, T, Hq, Hkv, d, _in(q, 0, 2, 1), _in(k, 0, 2, 1),
+                             _in(v, 0, 2, 1), _in(lam, 0, 2, 1), _out(out, 0, 2, 1), _stream(q))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_v2_fwd")
+    return out
+
+
+def v2_decode_workspace_bytes(B: int, L: int, Hq: int, Hkv: int, d: int) -> int:
+    return int(load_library().diffattn_v2_decode_workspace_bytes(B, L, Hq, Hkv, d))
+
+
+def v2_decode(q, k_cache, v_cache, lam, out: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None):
+    """DIFF V2 decode; q [B,Hq,d], caches [B,L,Hkv,d], lam [B,Hq/2]; returns [B,Hq/2,d]."""
+    lib = load_library()
+    B, Hq, d = q.shape
+    L, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, L, Hkv, d) or tuple(v_cache.shape) != (B, L, Hkv, d):
+        raise ValueError("caches must be [B,L,Hkv,d]")
+    if tuple(lam.shape) != (B, Hq // 2) or lam.dtype != torch.float32:
+        raise ValueError("lam must be fp32 [B,Hq/2]")
+    if out is None:
+        out = torch.empty((B, Hq // 2, d), dtype=q.dtype, device=q.device)
+    need = v2_decode_workspace_bytes(B, L, Hq, Hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_device(q, k_cache, v_cache, out)
+    st = lib.diffattn_v2_decode(_dtype_code(q), B, L, Hq, Hkv, d, _in(q, 0, 1, None),
+                                _in(k_cache, 0, 2, 1), _in(v_cache, 0, 2, 1), _in(lam, 0, 1, None),
+                                _out(out, 0, 1, None), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream(q))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_v2_decode")
+    return out

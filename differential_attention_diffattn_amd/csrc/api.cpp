@@ -1,0 +1,197 @@
+// api.cpp -- the C ABI declared in include/diffattn.h: argument validation on
+// the host, then dispatch to the gfx950 kernels.
+//
+// Validation makes no HIP call, so every error status is reachable (and
+// tested) on a machine without a GPU; a call that fails validation enqueues
+// nothing and leaves `out` untouched.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/diffattn.h"
+#include "kernels.hpp"
+
+namespace {
+
+using da::TIn;
+using da::TOut;
+
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+// A dense-row tensor (unit-stride head_dim, 128-bit rows): non-null, 16-byte
+// aligned base, non-negative role strides that are multiples of `mult`
+// elements.
+da_status check_rows(const void* p, int64_t sb, int64_t sh, int64_t st, int64_t mult) {
+  if (!p) return DA_E_NULL;
+  if (!aligned(p, 16)) return DA_E_LAYOUT;
+  const int64_t s[3] = {sb, sh, st};
+  for (int64_t x : s)
+    if (x < 0 || x % mult != 0) return DA_E_LAYOUT;
+  return DA_OK;
+}
+da_status check_in(const da_in& t, int64_t mult) { return check_rows(t.ptr, t.sb, t.sh, t.st, mult); }
+da_status check_out(const da_out& t, int64_t mult) { return check_rows(t.ptr, t.sb, t.sh, t.st, mult); }
+
+// fp32 logits without a head_dim axis: only element alignment is needed.
+da_status check_logits(const da_in& t) {
+  if (!t.ptr) return DA_E_NULL;
+  if (!aligned(t.ptr, 4)) return DA_E_LAYOUT;
+  if (t.sb < 0 || t.sh < 0 || t.st < 0) return DA_E_LAYOUT;
+  return DA_OK;
+}
+
+#define DA_TRY(x)                   \
+  do {                              \
+    const da_status _s = (x);       \
+    if (_s != DA_OK) return _s;     \
+  } while (0)
+
+TIn tin(const da_in& t) { return TIn{t.ptr, t.sb, t.sh, t.st}; }
+TOut tout(const da_out& t) { return TOut{t.ptr, t.sb, t.sh, t.st}; }
+
+float log2e_over_sqrt(int d) { return (float)(1.4426950408889634 / sqrt((double)d)); }
+
+da_status launch_status(hipError_t e) { return e == hipSuccess ? DA_OK : DA_E_LAUNCH; }
+
+// Largest grid the launchers build, for the overflow check.
+bool grid_fits(long long n) { return n >= 1 && n <= 0x7fffffffLL; }
+
+da_status validate_v2_common(da_dtype dtype, int B, int T, int Hq, int Hkv, int d) {
+  if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1) return DA_E_SHAPE;
+  if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return DA_E_SHAPE;
+  if (dtype != DA_BF16) return DA_E_UNSUPPORTED;
+  if (d != 64 && d != 128) return DA_E_UNSUPPORTED;
+  return DA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+double diffattn_lambda_init(int layer_index) { return 0.8 - 0.6 * exp(-0.3 * (double)layer_index); }
+
+const char* diffattn_status_string(da_status s) {
+  switch (s) {
+    case DA_OK: return "ok";
+    case DA_E_NULL: return "a required pointer is NULL";
+    case DA_E_DTYPE: return "unknown dtype";
+    case DA_E_SHAPE: return "a size is < 1 or sizes are inconsistent";
+    case DA_E_LAYOUT: return "misaligned pointer or invalid stride";
+    case DA_E_UNSUPPORTED: return "no kernel for these (valid) arguments";
+    case DA_E_WORKSPACE: return "decode workspace missing, misaligned or too small";
+    case DA_E_LAUNCH: return "the HIP runtime rejected a kernel launch";
+  }
+  return "unknown status";
+}
+
+da_status diffattn_v1_fwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+                          da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
+                          const float* lam_k2, int layer_index, da_out out, void* stream) {
+  if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
+  if (B < 1 || H < 1 || T < 1 || d < 1 || layer_index < 0) return DA_E_SHAPE;
+  const int64_t mult = dtype == DA_BF16 ? 8 : 4;
+  DA_TRY(check_in(q1, mult));
+  DA_TRY(check_in(q2, mult));
+  DA_TRY(check_in(k1, mult));
+  DA_TRY(check_in(k2, mult));
+  DA_TRY(check_in(v, mult));
+  DA_TRY(check_out(out, mult));
+  if (!lam_q1 || !lam_k1 || !lam_q2 || !lam_k2) return DA_E_NULL;
+  if (!aligned(lam_q1, 4) || !aligned(lam_k1, 4) || !aligned(lam_q2, 4) || !aligned(lam_k2, 4))
+    return DA_E_LAYOUT;
+  if (dtype == DA_BF16 && d != 64 && d != 128) return DA_E_UNSUPPORTED;
+  if (dtype == DA_FP32 && d != 32 && d != 64 && d != 128) return DA_E_UNSUPPORTED;
+  if (!grid_fits((long long)B * H * ((T + 31) / 32))) return DA_E_SHAPE;
+
+  const float li = (float)diffattn_lambda_init(layer_index);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == DA_BF16) {
+    da::PrefillArgs a{};
+    a.q1 = tin(q1), a.q2 = tin(q2), a.k1 = tin(k1), a.k2 = tin(k2), a.v = tin(v);
+    a.out = tout(out);
+    a.lq1 = lam_q1, a.lk1 = lam_k1, a.lq2 = lam_q2, a.lk2 = lam_k2;
+    a.lam_init = li;
+    a.sl2 = log2e_over_sqrt(d);
+    a.B = B, a.T = T, a.H = H;
+    return launch_status(da::launch_prefill_v1_bf16(d, a, s));
+  }
+  da::V1F32Args a{};
+  a.q1 = tin(q1), a.q2 = tin(q2), a.k1 = tin(k1), a.k2 = tin(k2), a.v = tin(v);
+  a.out = tout(out);
+  a.lq1 = lam_q1, a.lk1 = lam_k1, a.lq2 = lam_q2, a.lk2 = lam_k2;
+  a.lam_init = li;
+  a.sl2 = log2e_over_sqrt(d);
+  a.B = B, a.H = H, a.T = T;
+  return launch_status(da::launch_v1_fp32(d, a, s));
+}
+
+da_status diffattn_v2_fwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
+                          da_in lam, da_out out, void* stream) {
+  if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1) return DA_E_SHAPE;
+  if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return DA_E_SHAPE;
+  const int64_t mult = dtype == DA_BF16 ? 8 : 4;
+  DA_TRY(check_in(q, mult));
+  DA_TRY(check_in(k, mult));
+  DA_TRY(check_in(v, mult));
+  DA_TRY(check_logits(lam));
+  DA_TRY(check_out(out, mult));
+  DA_TRY(validate_v2_common(dtype, B, T, Hq, Hkv, d));
+  if (!grid_fits((long long)B * (Hq / 2) * ((T + 31) / 32))) return DA_E_SHAPE;
+
+  da::PrefillArgs a{};
+  a.q1 = a.q2 = tin(q);
+  a.k1 = a.k2 = tin(k);
+  a.v = tin(v);
+  a.lam = tin(lam);
+  a.out = tout(out);
+  a.sl2 = log2e_over_sqrt(d);
+  a.B = B, a.T = T, a.H = Hkv, a.G = Hq / Hkv;
+  return launch_status(da::launch_prefill_v2_bf16(d, a, (hipStream_t)stream));
+}
+
+size_t diffattn_v2_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int d) {
+  if (B < 1 || L < 1 || Hq < 1 || Hkv < 1 || d < 1) return 0;
+  if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return 0;
+  const da::DecodeSplit sp = da::decode_split(B, L, Hkv);
+  return (size_t)B * Hkv * sp.nsplit * (size_t)(Hq / Hkv) * (size_t)(d + 2) * sizeof(float);
+}
+
+da_status diffattn_v2_decode(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
+                             da_in v_cache, da_in lam, da_out out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
+  if (B < 1 || L < 1 || Hq < 1 || Hkv < 1 || d < 1) return DA_E_SHAPE;
+  if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return DA_E_SHAPE;
+  const int64_t mult = dtype == DA_BF16 ? 8 : 4;
+  // q, lam and out have no token axis: their st is ignored.
+  DA_TRY(check_rows(q.ptr, q.sb, q.sh, 0, mult));
+  DA_TRY(check_in(k_cache, mult));
+  DA_TRY(check_in(v_cache, mult));
+  da_in lam2 = lam;
+  lam2.st = 0;
+  DA_TRY(check_logits(lam2));
+  DA_TRY(check_rows(out.ptr, out.sb, out.sh, 0, mult));
+  DA_TRY(validate_v2_common(dtype, B, L, Hq, Hkv, d));
+  if (Hq / Hkv > 16) return DA_E_UNSUPPORTED;  // one 16-wide MFMA column block per group
+  const size_t need = diffattn_v2_decode_workspace_bytes(B, L, Hq, Hkv, d);
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return DA_E_WORKSPACE;
+  const da::DecodeSplit sp = da::decode_split(B, L, Hkv);
+  if (!grid_fits((long long)B * Hkv * sp.nsplit) || !grid_fits((long long)B * (Hq / 2))) return DA_E_SHAPE;
+
+  da::DecodeArgs a{};
+  a.q = TIn{q.ptr, q.sb, q.sh, 0};
+  a.k = tin(k_cache);
+  a.v = tin(v_cache);
+  a.lam = TIn{lam.ptr, lam.sb, lam.sh, 0};
+  a.out = TOut{out.ptr, out.sb, out.sh, 0};
+  a.ws = (float*)workspace;
+  a.sl2 = log2e_over_sqrt(d);
+  a.B = B, a.L = L, a.Hq = Hq, a.Hkv = Hkv, a.G = Hq / Hkv;
+  a.chunk = sp.chunk;
+  a.nsplit = sp.nsplit;
+  return launch_status(da::launch_decode_bf16(d, a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// kernels.hpp -- internal interface between the C-ABI front end (api.cpp) and
+// the kernel translation units.  Every function here enqueues work on
+// `stream` and returns the hipError_t of the launch; arguments have already
+// been validated by the front end.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace da {
+
+// Two causal softmax maps per wave over one shared V (V1), or one GQA
+// attention whose adjacent query heads are paired (V2).
+struct PrefillArgs {
+  TIn q1, q2, k1, k2, v;  // V2: q1 == q2 == q (heads selected by pair), k1 == k2 == k
+  TIn lam;                // V2: fp32 logits [B,T,Hq/2] (roles b, pair, t)
+  TOut out;
+  const float* lq1;  // V1 lambda vectors (device, [d])
+  const float* lk1;
+  const float* lq2;
+  const float* lk2;
+  float lam_init;  // V1: 0.8 - 0.6 exp(-0.3 layer)
+  float sl2;       // log2(e) / sqrt(d)
+  int B, T;
+  int H;           // V1: differential heads; V2: kv heads
+  int G;           // V2: query heads per kv head (even)
+  int pc;          // V2: pairs per workgroup (1, 2 or 4)
+  int units_per_b; // work units per batch entry
+  int tiles;       // token tiles per unit
+  int nwg;         // workgroups in the grid
+};
+
+hipError_t launch_prefill_v1_bf16(int d, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_v2_bf16(int d, const PrefillArgs& a, hipStream_t s);
+
+// Plain fp32 V1 forward (VALU, LDS tiled).
+struct V1F32Args {
+  TIn q1, q2, k1, k2, v;
+  TOut out;
+  const float* lq1;
+  const float* lk1;
+  const float* lq2;
+  const float* lk2;
+  float lam_init;
+  float sl2;
+  int B, H, T;
+  int tiles;
+};
+hipError_t launch_v1_fp32(int d, const V1F32Args& a, hipStream_t s);
+
+// Split-K decode over a KV cache, then a deterministic merge.
+struct DecodeArgs {
+  TIn q, k, v, lam;
+  TOut out;
+  float* ws;  // [B][Hkv][nsplit][G][d + 2] fp32 partials (m, l, O)
+  float sl2;
+  int B, L, Hq, Hkv, G;
+  int chunk;   // tokens per split (multiple of 128)
+  int nsplit;
+};
+hipError_t launch_decode_bf16(int d, const DecodeArgs& a, hipStream_t s);
+
+// Decode split geometry, shared by the workspace query and the launcher.
+struct DecodeSplit {
+  int chunk, nsplit;
+};
+DecodeSplit decode_split(int B, int L, int Hkv);
+
+}  // namespace da

@@ -1,0 +1,174 @@
+/*
+ * diffattn.h -- C ABI of libdiffattn.so: differential-attention forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the pages this follows):
+ *   "Differential Transformer V2" article -- the DiffAttnV1 and DiffAttnV2
+ *     pseudo-code, the note that heads of one GQA group are contiguous and
+ *     that the two heads subtracted share key and value, and the paragraph
+ *     on memory-bound decoding.
+ *   nanoGPT issue "How best to implement a differential transformer?" --
+ *     Wilsontomass's module: causal attention with the default 1/sqrt(d)
+ *     scale, one V of width 2*head_dim shared by both maps, the lambda
+ *     vectors, subln = RMSNorm(2*head_dim, eps 1e-5, no affine) and the
+ *     (1 - lambda_init) output scale.
+ *   Hacker News item 41780844 -- lambda_init = 0.8 - 0.6*exp(-0.3*depth).
+ *
+ * Conventions shared by every entry point
+ *   Memory    Every tensor pointer is DEVICE memory, allocated and owned by
+ *             the caller; the library allocates nothing, keeps no state
+ *             between calls and never frees caller memory.
+ *   Layout    A tensor is described by da_in / da_out: a base pointer and
+ *             element strides for its batch, head and token axes (the
+ *             "role" strides).  The head_dim axis is always unit-stride.
+ *             Any permutation of those axes (e.g. [B,T,H,d] or [B,H,T,d])
+ *             is accepted without a copy.  Base pointers must be 16-byte
+ *             aligned and every role stride a multiple of 8 elements (bf16)
+ *             or 4 elements (fp32), so rows can be moved with 128-bit loads.
+ *             Lambda tensors (fp32, no head_dim axis) only need 4-byte
+ *             alignment and have no stride-multiple rule.
+ *   Stream    Work is enqueued on `stream` (a hipStream_t; NULL = the
+ *             default stream) and the call returns without synchronising.
+ *   Errors    Status codes only; nothing is thrown, nothing aborts.  All
+ *             arguments are validated on the host before anything is
+ *             enqueued: on any error other than DA_E_LAUNCH nothing has been
+ *             enqueued and `out` is untouched.  DA_E_LAUNCH reports a launch
+ *             failure from the HIP runtime.  Faults during execution surface
+ *             at the caller's next synchronisation, as for any HIP kernel.
+ *   Threads   Entry points are reentrant and may be called concurrently
+ *             from several host threads (on different or the same stream).
+ *   Numerics  bf16 inputs, fp32 accumulation and softmax, fp32 lambda,
+ *             combine and norm; one round-to-nearest-even store to the
+ *             output dtype.  Results are bitwise reproducible run to run.
+ */
+#ifndef DIFFATTN_H
+#define DIFFATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DA_OK = 0,
+    DA_E_NULL = 1,        /* a required pointer is NULL                         */
+    DA_E_DTYPE = 2,       /* unknown dtype value                                */
+    DA_E_SHAPE = 3,       /* a size is < 1, or sizes are inconsistent           */
+    DA_E_LAYOUT = 4,      /* misaligned pointer or a stride breaks the rules    */
+    DA_E_UNSUPPORTED = 5, /* valid arguments this build has no kernel for       */
+    DA_E_WORKSPACE = 6,   /* decode workspace missing or too small              */
+    DA_E_LAUNCH = 7       /* the HIP runtime rejected a kernel launch           */
+} da_status;
+
+typedef enum { DA_FP32 = 0, DA_BF16 = 1 } da_dtype;
+
+/* Read-only device tensor: base pointer + element strides by role. */
+typedef struct {
+    const void* ptr;
+    int64_t sb; /* stride between batch entries   */
+    int64_t sh; /* stride between heads (or pairs) */
+    int64_t st; /* stride between tokens           */
+} da_in;
+
+/* Writable device tensor: same meaning as da_in. */
+typedef struct {
+    void* ptr;
+    int64_t sb;
+    int64_t sh;
+    int64_t st;
+} da_out;
+
+/*
+ * DIFF V1 forward ("Differential Transformer V2" article, DiffAttnV1;
+ * nanoGPT issue, Wilsontomass's module).  For every batch b, differential
+ * head h and token i:
+ *   A_m     = causal softmax_j( q_m[b,h,i] . k_m[b,h,j] / sqrt(d) ),  j <= i
+ *   lam     = exp(sum_c lam_q1[c]*lam_k1[c]) - exp(sum_c lam_q2[c]*lam_k2[c])
+ *             + lambda_init,  lambda_init = 0.8 - 0.6*exp(-0.3*layer_index)
+ *   D       = (A_1 - lam*A_2) V[b,h]                (width 2d)
+ *   out[b,i,h,:] = D / sqrt(mean_c D^2 + 1e-5) * (1 - lambda_init)
+ *
+ *   dtype        DA_BF16 (d in {64, 128}) or DA_FP32 (d in {32, 64, 128}).
+ *   B, H, T, d   batch, differential heads, tokens, q/k head_dim; >= 1.
+ *   q1,q2,k1,k2  logical [B,H,T,d] of `dtype` (roles b, h, t).
+ *   v            logical [B,H,T,2d] of `dtype`; one V shared by both maps.
+ *   lam_q1..lam_k2  device fp32 vectors of length d, contiguous.
+ *   layer_index  0-based depth of the layer (any int >= 0).
+ *   out          logical [B,T,H,2d] of `dtype` (roles b, h, t).
+ * lam is one scalar per call shared by every head, computed on the device
+ * in fp32; it may take any real value (no clamp).
+ */
+da_status diffattn_v1_fwd(da_dtype dtype, int B, int H, int T, int d,
+                          da_in q1, da_in q2, da_in k1, da_in k2, da_in v,
+                          const float* lam_q1, const float* lam_k1,
+                          const float* lam_q2, const float* lam_k2,
+                          int layer_index, da_out out, void* stream);
+
+/*
+ * DIFF V2 prefill ("Differential Transformer V2" article, DiffAttnV2 and
+ * the GQA-layout note).  Query heads of one GQA group are contiguous, so
+ * query head h reads kv head g = h / (Hq/Hkv); the two heads of a pair
+ * (2p, 2p+1) always fall in one group.  For every b, token t, pair p:
+ *   a_h = causal softmax_j( q[b,t,h] . k[b,j,g] / sqrt(d) ) v[b,:,g],  j <= t
+ *   out[b,t,p,:] = a_{2p} - sigmoid(lam[b,t,p]) * a_{2p+1}
+ * No norm, no scale.
+ *
+ *   dtype   DA_BF16 only (DA_FP32 -> DA_E_UNSUPPORTED).
+ *   d       128 or 64.   Hq % Hkv == 0 and (Hq/Hkv) even.
+ *   q       logical [B,T,Hq,d]   (roles b, h, t)
+ *   k, v    logical [B,T,Hkv,d]  (roles b, h, t)
+ *   lam     logical [B,T,Hq/2] fp32 logits (roles b, h = pair, t); +-inf allowed.
+ *   out     logical [B,T,Hq/2,d] bf16 (roles b, h = pair, t).
+ */
+da_status diffattn_v2_fwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d,
+                          da_in q, da_in k, da_in v, da_in lam,
+                          da_out out, void* stream);
+
+/*
+ * Bytes of device workspace diffattn_v2_decode needs for these sizes
+ * (0 if the sizes are invalid).  The split of the cache length, and hence
+ * the size, depends only on (B, L, Hq, Hkv, d).
+ */
+size_t diffattn_v2_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int d);
+
+/*
+ * DIFF V2 decode ("Differential Transformer V2" article: DiffAttnV2 at the
+ * newest position; decoding is memory-bound).  One new query token per
+ * sequence against a KV cache of L entries that already holds that token at
+ * position L-1; the query attends to all L entries:
+ *   a_h = softmax_j( q[b,h] . k[b,j,g] / sqrt(d) ) v[b,:,g],  j < L
+ *   out[b,p,:] = a_{2p} - sigmoid(lam[b,p]) * a_{2p+1}
+ * The cache is split along L; each piece is reduced to a partial (max, sum,
+ * weighted V) per head and the pieces are merged in a fixed order (no
+ * atomics, so results are deterministic).
+ *
+ *   dtype      DA_BF16 only.   d in {64, 128}.  Hq % Hkv == 0, (Hq/Hkv) even.
+ *   q          logical [B,Hq,d]      (roles b, h; st ignored)
+ *   k_cache    logical [B,L,Hkv,d]   (roles b, h, t)
+ *   v_cache    logical [B,L,Hkv,d]   (roles b, h, t)
+ *   lam        logical [B,Hq/2] fp32 logits (roles b, h = pair; st ignored)
+ *   out        logical [B,Hq/2,d] bf16 (roles b, h = pair; st ignored)
+ *   workspace  device scratch of at least
+ *              diffattn_v2_decode_workspace_bytes(B,L,Hq,Hkv,d) bytes,
+ *              16-byte aligned, owned by the caller; its contents on entry
+ *              do not matter and on return are unspecified.
+ * Two kernels are enqueued on `stream` (split, then merge).
+ */
+da_status diffattn_v2_decode(da_dtype dtype, int B, int L, int Hq, int Hkv, int d,
+                             da_in q, da_in k_cache, da_in v_cache, da_in lam,
+                             da_out out, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* lambda_init = 0.8 - 0.6*exp(-0.3*layer_index), as the V1 kernels use it
+ * (computed on the host in double, handed to the device as float). */
+double diffattn_lambda_init(int layer_index);
+
+/* Static, NUL-terminated description of a status code. */
+const char* diffattn_status_string(da_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DIFFATTN_H */

@@ -1,0 +1,129 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and every validation error is returned before anything is
+enqueued (no HIP call happens on these paths, so they run on any host)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "diffattn.h"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from differential_attention_diffattn_amd import binding
+
+    if not binding.library_path().exists():
+        from differential_attention_diffattn_amd.build import build_library
+
+        build_library()
+    return binding.load_library()
+
+
+def _declared_symbols():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(diffattn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    syms = _declared_symbols()
+    for need in ("diffattn_v1_fwd", "diffattn_v2_fwd", "diffattn_v2_decode",
+                 "diffattn_v2_decode_workspace_bytes", "diffattn_status_string"):
+        assert need in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lib.diffattn_status_string(code)
+        assert s and len(s) > 1
+    assert lib.diffattn_status_string(0) == b"ok"
+
+
+def test_lambda_init_matches_oracle(lib):
+    import oracle
+
+    for layer in range(20):
+        assert abs(lib.diffattn_lambda_init(layer) - oracle.lambda_init(layer)) < 1e-15
+
+
+# ----- validation -----------------------------------------------------------
+from differential_attention_diffattn_amd.binding import DaIn, DaOut  # noqa: E402
+
+OK = 0
+E_NULL, E_DTYPE, E_SHAPE, E_LAYOUT, E_UNSUP, E_WS = 1, 2, 3, 4, 5, 6
+FAKE = 0x10000  # aligned, never dereferenced: validation fails before any launch
+
+
+def _t(ptr=FAKE, sb=8 * 1024, sh=8 * 64, st=64, out=False):
+    return (DaOut if out else DaIn)(ptr, sb, sh, st)
+
+
+def _v1(lib, dtype=1, B=1, H=2, T=16, d=64, q1=None, v=None, out=None, lam=FAKE, layer=0):
+    q = q1 or _t()
+    return lib.diffattn_v1_fwd(dtype, B, H, T, d, q, _t(), _t(), _t(), v or _t(), lam, FAKE, FAKE, FAKE,
+                               layer, out or _t(out=True), None)
+
+
+def test_v1_validation(lib):
+    assert _v1(lib, dtype=7) == E_DTYPE
+    assert _v1(lib, T=0) == E_SHAPE
+    assert _v1(lib, B=0) == E_SHAPE
+    assert _v1(lib, layer=-1) == E_SHAPE
+    assert _v1(lib, q1=_t(ptr=0)) == E_NULL
+    assert _v1(lib, lam=0) == E_NULL
+    assert _v1(lib, out=_t(ptr=0, out=True)) == E_NULL
+    assert _v1(lib, q1=_t(ptr=FAKE + 2)) == E_LAYOUT        # not 16-byte aligned
+    assert _v1(lib, v=_t(st=68)) == E_LAYOUT                # stride not a multiple of 8 bf16
+    assert _v1(lib, q1=_t(sh=-64)) == E_LAYOUT              # negative stride
+    assert _v1(lib, lam=FAKE + 2) == E_LAYOUT
+    assert _v1(lib, d=96) == E_UNSUP                        # bf16 d in {64, 128}
+    assert _v1(lib, dtype=0, d=16) == E_UNSUP               # fp32 d in {32, 64, 128}
+    assert _v1(lib, dtype=0, v=_t(st=66)) == E_LAYOUT       # fp32: multiples of 4
+
+
+def _v2(lib, dtype=1, B=1, T=16, Hq=8, Hkv=2, d=128, lam=None, q=None):
+    return lib.diffattn_v2_fwd(dtype, B, T, Hq, Hkv, d, q or _t(), _t(), _t(), lam or _t(), _t(out=True), None)
+
+
+def test_v2_validation(lib):
+    assert _v2(lib, dtype=3) == E_DTYPE
+    assert _v2(lib, T=0) == E_SHAPE
+    assert _v2(lib, Hq=8, Hkv=3) == E_SHAPE                  # not a multiple
+    assert _v2(lib, Hq=6, Hkv=2) == E_SHAPE                  # odd group: a pair would straddle groups
+    assert _v2(lib, q=_t(ptr=0)) == E_NULL
+    assert _v2(lib, lam=_t(ptr=FAKE + 2)) == E_LAYOUT        # logits need 4-byte alignment
+    assert _v2(lib, dtype=0) == E_UNSUP                      # fp32 V2 has no kernel
+    assert _v2(lib, d=96) == E_UNSUP
+
+
+def test_decode_workspace_query(lib):
+    n = lib.diffattn_v2_decode_workspace_bytes(64, 32768, 64, 8, 128)
+    # 64 batch x 8 groups x 16 splits x 8 heads x (128 + 2) floats
+    assert n == 64 * 8 * 16 * 8 * 130 * 4
+    assert lib.diffattn_v2_decode_workspace_bytes(1, 1, 2, 1, 128) > 0
+    assert lib.diffattn_v2_decode_workspace_bytes(0, 10, 8, 2, 128) == 0
+    assert lib.diffattn_v2_decode_workspace_bytes(1, 10, 6, 2, 128) == 0
+
+
+def _dec(lib, B=2, L=100, Hq=8, Hkv=2, d=128, ws=FAKE, wsb=None, dtype=1):
+    need = lib.diffattn_v2_decode_workspace_bytes(B, L, Hq, Hkv, d)
+    return lib.diffattn_v2_decode(dtype, B, L, Hq, Hkv, d, _t(), _t(), _t(), _t(), _t(out=True), ws,
+                                  need if wsb is None else wsb, None)
+
+
+def test_decode_validation(lib):
+    assert _dec(lib, L=0) == E_SHAPE
+    assert _dec(lib, Hq=10, Hkv=2) == E_SHAPE
+    assert _dec(lib, dtype=0) == E_UNSUP
+    assert _dec(lib, Hq=64, Hkv=2) == E_UNSUP                # 32 heads per group > one 16-wide block
+    assert _dec(lib, ws=0) == E_WS
+    assert _dec(lib, ws=FAKE + 4) == E_WS
+    assert _dec(lib, wsb=100) == E_WS
