@@ -1,35 +1,43 @@
 // prefill_bf16.hip -- fused causal differential-attention prefill, bf16 MFMA.
 //
-// What one wave computes ("Differential Transformer V2" article, DiffAttnV1
-// and DiffAttnV2 pseudo-code):
-//   V1: for 32 query rows of one differential head, the two causal softmax
-//       maps softmax(Q1 K1^T / sqrt d) and softmax(Q2 K2^T / sqrt d) applied to
-//       the one shared V (width 2d), then A1 V - lam A2 V, RMSNorm over the 2d
+// What is computed ("Differential Transformer V2" article, DiffAttnV1 and
+// DiffAttnV2 pseudo-code):
+//   V1: per differential head, the two causal softmax maps
+//       softmax(Q1 K1^T / sqrt d) and softmax(Q2 K2^T / sqrt d) applied to the
+//       one shared V (width 2d), then A1 V - lam A2 V, RMSNorm over the 2d
 //       channels (eps 1e-5, no weight) and the (1 - lambda_init) scale
 //       (nanoGPT issue "How best to implement a differential transformer?",
 //       Wilsontomass's module).
-//   V2: for 32 tokens of one adjacent head pair (2p, 2p+1) of a GQA group,
-//       the two maps over the group's shared K and V, then
-//       O_2p - sigmoid(lam[t, p]) O_2p+1 (no norm, no scale).
+//   V2: per adjacent head pair (2p, 2p+1) of a GQA group, the two maps over
+//       the group's shared K and V, then O_2p - sigmoid(lam[t, p]) O_2p+1
+//       (no norm, no scale).
 //
 // Structure (designed for gfx950, not taken from any listing):
-//   * A workgroup of 4 waves streams 64-key tiles of K (two K tensors for
-//     V1, one for V2) and V through LDS, double-buffered, so each tile is read
-//     from HBM/L2 once per workgroup.  For V2 the 4 waves are the 4 pairs of
-//     one 8-head GQA group, so a K/V tile is loaded once for the whole group.
+//   * K and V tiles of 64 keys go HBM -> LDS with global_load_lds_dwordx4
+//     (no registers, no VALU), double-buffered: the next tile streams in
+//     while the current one is consumed; one barrier per tile.  In LDS both
+//     stay row-major with an XOR swizzle of their 16-byte chunks, so the
+//     MFMA operand reads are bank-conflict-free.
 //   * Scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_bf16: the Q fragments stay in registers for the
-//     whole key loop and each lane then holds 16 scores of ONE query row, so
-//     the softmax row state (running max and sum) is per lane, and the fp32
-//     score registers convert in place to the bf16 B operand of the P.V
-//     product O^T = V^T P^T.  V is transposed once on its way into LDS.
+//     v_mfma_f32_32x32x16_bf16: Q fragments stay in registers for the whole
+//     key loop, each lane holds 16 scores of ONE query row (softmax state is
+//     per lane), and the fp32 score registers convert in place to the bf16 B
+//     operand of O^T = V^T P^T.  The V^T A operand comes straight from the
+//     row-major V tile through ds_read_b64_tr_b16 (the LDS transpose read).
 //   * Online softmax in the log2 domain with a lazily updated reference max:
-//     the running reference only moves (and O, l are rescaled) when a row's
-//     max exceeds it by more than 2^8, which keeps every exponent <= 2^8 and
-//     leaves the result exact up to rounding.
-//   * Causal work skipping at 32-key granularity; the mask is only evaluated
-//     on diagonal sub-blocks.  Workgroups run heaviest tiles first and map
-//     onto XCDs so the tiles of one head share an L2.
+//     O and l are only rescaled when a row's max grows by more than 2^8,
+//     which keeps every exponent <= 2^8 and the result exact up to rounding.
+//   * Work split.  A wave owns 32 query rows.  MPW = 2: the wave carries
+//     both maps (V1: map 1 and map 2 of one differential head; V2: the two
+//     heads of a pair), so a V fragment read once feeds two MFMAs.  MPW = 1:
+//     the two maps of the same rows sit in two partner waves (halving the
+//     accumulator registers, so two waves fit per SIMD) and are combined
+//     through LDS at the end.  For V2 the waves of a workgroup cover the
+//     heads of one GQA group, so each K/V tile is loaded once for the whole
+//     group.
+//   * Causal skipping at 32-key granularity (mask only on diagonal
+//     sub-blocks); heaviest tiles first; workgroups mapped onto XCDs so the
+//     tiles of one head share an L2.
 #include <math.h>
 
 #include "kernels.hpp"
@@ -37,90 +45,53 @@
 namespace da {
 namespace {
 
-constexpr int kBN = 64;          // keys per LDS stage
-constexpr int kKPad = 8;         // bf16 padding per K row  -> conflict-free 16 B reads
-constexpr int kVPad = 4;         // bf16 padding per V^T row -> conflict-free 8 B reads/writes
-constexpr float kLazyLog2 = 8.f; // rescale only when the max grows by > 2^8
+constexpr int kBN = 64;           // keys per LDS stage
+constexpr float kLazyLog2 = 8.f;  // rescale only when the max grows by > 2^8
 
-template <int D, int DV, bool V2>
-struct Layout {
-  static constexpr int KROW = D + kKPad;
-  static constexpr int VROW = kBN + kVPad;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// 16 bytes per lane, HBM -> LDS; lane l's bytes land at lds + 16 l.  `lds`
+// must be the same for every lane of the wave.
+__device__ __forceinline__ void dma16(const void* g, unsigned char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+}
+
+// LDS transpose read: in each group of 16 lanes, lane j receives element
+// (j & 3) of the 4-element rows addressed by lanes 4k + (j >> 2), k = 0..3.
+__device__ __forceinline__ uint2 tr_read(const unsigned char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
+template <int D, int DV, bool V2, int NW, int MPW>
+struct Cfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int KS = D / 16;   // k-steps of the score MFMA
+  static constexpr int CB = DV / 32;  // 32-wide column blocks of O^T
   static constexpr int NK = V2 ? 1 : 2;
-  static constexpr int KSZ = kBN * KROW;
-  static constexpr int VSZ = DV * VROW;
-  static constexpr int STAGE = NK * KSZ + VSZ;  // bf16 elements per stage
+  static constexpr int K_BYTES = kBN * D * 2;
+  static constexpr int V_BYTES = kBN * DV * 2;
+  static constexpr int STAGE = NK * K_BYTES + V_BYTES;
+  static constexpr int KCH = K_BYTES / 1024;  // 1 KB DMA instructions per K tensor
+  static constexpr int VCH = V_BYTES / 1024;
+  static constexpr int NCH = NK * KCH + VCH;
+  static constexpr int CPW = NCH / NW;        // DMA instructions per wave per tile
+  static_assert(NCH % NW == 0, "tile DMA split");
+  static_assert(D >= 64 && DV >= 64, "swizzles assume >= 8 chunks per row");
+  // MPW == 1: one exchange slot per partner-wave pair (fp32, lane-native order)
+  static constexpr int XBYTES = MPW == 1 ? (NW / 2) * CB * 16 * 64 * 4 : 0;
+  static constexpr int SMEM = 2 * STAGE > XBYTES ? 2 * STAGE : XBYTES;
+  static constexpr int MIN_BLOCKS = NW == 4 ? 2 : 1;  // two waves per SIMD
 };
 
-// Cooperative staging of one key tile: global -> registers -> LDS.
-template <int D, int DV, bool V2, int NT>
-struct Stage {
-  using L = Layout<D, DV, V2>;
-  static constexpr int KTOT = kBN * (D / 8);         // 16 B chunks per K tensor
-  static constexpr int VTOT = (kBN / 4) * (DV / 8);  // 4-row x 8-col units of V
-  static constexpr int KCH = (KTOT + NT - 1) / NT;
-  static constexpr int VU = (VTOT + NT - 1) / NT;
-  uint4 k[L::NK][KCH];
-  uint4 v[VU][4];
-
-  __device__ __forceinline__ void load(const uint16_t* const kp[2], const int64_t kst[2], const uint16_t* vp,
-                                       int64_t vst, int j0, int T, int tid) {
-#pragma unroll
-    for (int n = 0; n < L::NK; ++n) {
-#pragma unroll
-      for (int u = 0; u < KCH; ++u) {
-        const int c = tid + NT * u;
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        const int key = j0 + row;
-        k[n][u] = (KTOT % NT == 0 || c < KTOT) && key < T
-                      ? *(const uint4*)(kp[n] + (int64_t)key * kst[n] + col)
-                      : make_uint4(0, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      const int c = tid + NT * u;
-      const int rg = c % (kBN / 4), cc = c / (kBN / 4);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int key = j0 + 4 * rg + q;
-        v[u][q] = (VTOT % NT == 0 || c < VTOT) && key < T ? *(const uint4*)(vp + (int64_t)key * vst + cc * 8)
-                                                          : make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(uint16_t* st, int tid) const {
-#pragma unroll
-    for (int n = 0; n < L::NK; ++n) {
-#pragma unroll
-      for (int u = 0; u < KCH; ++u) {
-        const int c = tid + NT * u;
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        if (KTOT % NT == 0 || c < KTOT) *(uint4*)(st + n * L::KSZ + row * L::KROW + col) = k[n][u];
-      }
-    }
-    uint16_t* vt = st + L::NK * L::KSZ;
-#pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      const int c = tid + NT * u;
-      const int rg = c % (kBN / 4), cc = c / (kBN / 4);
-      if (VTOT % NT == 0 || c < VTOT) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *(uint2*)(vt + (cc * 8 + e) * L::VROW + 4 * rg) = column4(v[u][0], v[u][1], v[u][2], v[u][3], e);
-      }
-    }
-  }
-};
-
-template <int D, int DV, bool V2, int NW>
-__global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(const PrefillArgs a) {
-  using L = Layout<D, DV, V2>;
-  constexpr int NT = NW * 64;
-  constexpr int KS = D / 16;   // k-steps of the score MFMA
-  constexpr int CB = DV / 32;  // 32-wide column blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
+template <int D, int DV, bool V2, int NW, int MPW>
+__global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW>::MIN_BLOCKS))
+    prefill_kernel(const PrefillArgs a) {
+  using C = Cfg<D, DV, V2, NW, MPW>;
+  constexpr int KS = C::KS, CB = C::CB;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::SMEM];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 31, hg = lane >> 5;
@@ -130,19 +101,33 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(const PrefillArgs a
   const int tile = a.tiles - 1 - logical % a.tiles;  // heaviest tiles first
   const int b = unit / a.units_per_b;
   const int u = unit % a.units_per_b;
+  const int T = a.T;
 
-  // --- this wave's two maps and its 32 rows --------------------------------
-  int RB, rb, h = 0, pair = 0;
-  const uint16_t *qA, *qB, *kp[2], *vp;
-  int64_t qstA, qstB, kst[2], vst;
+  // ---- roles: which rows and maps this wave owns ----------------------------
+  int RB, rb, m0 = 0, h = 0, pair = 0;
+  const uint16_t* qp[2];
+  int64_t qst[2];
+  const uint16_t* kp[2];
+  int64_t kst[2];
+  const uint16_t* vp;
+  int64_t vst;
   if constexpr (!V2) {
-    RB = NW;
-    rb = wave;
     h = u;
-    qA = (const uint16_t*)a.q1.p + b * a.q1.sb + h * a.q1.sh;
-    qB = (const uint16_t*)a.q2.p + b * a.q2.sb + h * a.q2.sh;
-    qstA = a.q1.st;
-    qstB = a.q2.st;
+    if constexpr (MPW == 2) {
+      RB = NW;
+      rb = wave;
+    } else {
+      RB = NW / 2;
+      rb = wave >> 1;
+      m0 = wave & 1;  // this wave's map
+    }
+    const TIn* qs[2] = {&a.q1, &a.q2};
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) {
+      const TIn& t = *qs[m0 + m];
+      qp[m] = (const uint16_t*)t.p + b * t.sb + h * t.sh;
+      qst[m] = t.st;
+    }
     kp[0] = (const uint16_t*)a.k1.p + b * a.k1.sb + h * a.k1.sh;
     kp[1] = (const uint16_t*)a.k2.p + b * a.k2.sb + h * a.k2.sh;
     kst[0] = a.k1.st;
@@ -152,18 +137,22 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(const PrefillArgs a
   } else {
     const int npc = (a.G / 2) / a.pc;  // pair chunks per group
     const int g = u / npc, pcix = u % npc;
-    RB = NW / a.pc;
-    rb = wave / a.pc;
-    pair = g * (a.G / 2) + pcix * a.pc + wave % a.pc;
-    qA = (const uint16_t*)a.q1.p + b * a.q1.sb + (2 * pair) * a.q1.sh;
-    qB = (const uint16_t*)a.q1.p + b * a.q1.sb + (2 * pair + 1) * a.q1.sh;
-    qstA = qstB = a.q1.st;
+    // MPW == 2: wave w -> pair w % pc, row block w / pc.
+    // MPW == 1: waves 2k (even head) and 2k+1 (odd head) share pair k % pc and
+    //           row block k / pc.
+    const int pw = MPW == 2 ? wave : wave >> 1;
+    if constexpr (MPW == 1) m0 = wave & 1;
+    RB = (NW / (3 - MPW)) / a.pc;
+    rb = pw / a.pc;
+    pair = g * (a.G / 2) + pcix * a.pc + pw % a.pc;
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) qp[m] = (const uint16_t*)a.q1.p + b * a.q1.sb + (2 * pair + m0 + m) * a.q1.sh;
+    qst[0] = qst[1] = a.q1.st;
     kp[0] = kp[1] = (const uint16_t*)a.k1.p + b * a.k1.sb + g * a.k1.sh;
     kst[0] = kst[1] = a.k1.st;
     vp = (const uint16_t*)a.v.p + b * a.v.sb + g * a.v.sh;
     vst = a.v.st;
   }
-  const int T = a.T;
   const int BMT = 32 * RB;
   const int I0 = tile * BMT;
   const int i0w = I0 + 32 * rb;
@@ -171,19 +160,68 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(const PrefillArgs a
   const int kend = min(T, I0 + BMT);
   const int nkt = (kend + kBN - 1) / kBN;
 
-  // --- Q fragments (B operand of S^T = K Q^T): row i0w+li, cols 16ks+8hg.. --
-  bf16x8 qf[2][KS];
+  // ---- tile DMA: wave issues CPW 1 KB chunks; rows >= T are clamped to T-1
+  // (finite data; those keys are always masked for every valid query) ----
+  auto issue_tile = [&](int kt, int stage) {
+    const int j0 = kt * kBN;
+    unsigned char* sbase = smem + stage * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) {
+      const int ci = wave + NW * i;  // chunk of this stage (wave-uniform)
+      const uint16_t* g;
+      unsigned char* dst;
+      if (ci < C::NK * C::KCH) {
+        const int n = ci / C::KCH, cix = ci % C::KCH;
+        const int pos = cix * 64 + lane;  // 16 B chunk index inside the K tile
+        const int r = pos / (D / 8), sc = pos % (D / 8);
+        const int c = sc ^ (r & 7);
+        g = kp[n] + (int64_t)min(j0 + r, T - 1) * kst[n] + c * 8;
+        dst = sbase + n * C::K_BYTES + cix * 1024;
+      } else {
+        const int cix = ci - C::NK * C::KCH;
+        const int pos = cix * 64 + lane;
+        const int r = pos / (DV / 8), sc = pos % (DV / 8);
+        const int c = sc ^ (2 * (r & 3));
+        g = vp + (int64_t)min(j0 + r, T - 1) * vst + c * 8;
+        dst = sbase + C::NK * C::K_BYTES + cix * 1024;
+      }
+      dma16(g, dst);
+    }
+  };
+
+  // ---- Q fragments (B operand of S^T = K Q^T): row i0w+li, cols 16ks+8hg ----
+  bf16x8 qf[MPW][KS];
   {
     const int row = i0w + li;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      qf[0][ks] = as_bf16x8(row < T ? *(const uint4*)(qA + (int64_t)row * qstA + 16 * ks + 8 * hg) : z);
-      qf[1][ks] = as_bf16x8(row < T ? *(const uint4*)(qB + (int64_t)row * qstB + 16 * ks + 8 * hg) : z);
+    for (int m = 0; m < MPW; ++m)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[m][ks] = as_bf16x8(row < T ? *(const uint4*)(qp[m] + (int64_t)row * qst[m] + 16 * ks + 8 * hg)
+                                      : make_uint4(0, 0, 0, 0));
+  }
+
+  // ---- per-lane LDS offsets ----
+  // K chunk (2ks + hg) of row li lives at chunk (2ks + hg) ^ (li & 7).
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = li * (D * 2) + (((2 * ks + hg) ^ (li & 7)) << 4);
+  // V^T operand via transpose reads: lane (G16 = lane>>4, l16 = lane&15) points at
+  // row 4*(G16>>1) + (l16>>2) (+ sub-block, k-step), columns 32cb + 16(G16&1) + 4(l16&3).
+  int voff[2];  // for even / odd column blocks (the swizzle flips bit 2 of the chunk)
+  {
+    const int l16 = lane & 15, g16 = lane >> 4;
+    const int vr = 4 * (g16 >> 1) + (l16 >> 2);
+    const int cl = 2 * (g16 & 1) + ((l16 & 3) >> 1);  // chunk within a 4-chunk block
+    const int x = 2 * (l16 >> 2);                     // swizzle of rows with (r & 3) = l16 >> 2
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int c = ((4 * par + cl) ^ x) - 4 * par;  // chunk offset relative to 4*cb
+      voff[par] = vr * (DV * 2) + c * 16 + (l16 & 1) * 8;
     }
   }
 
-  // --- V1 lambda: one scalar per call, fp32 ---------------------------------
+  // ---- V1 lambda (one fp32 scalar per call) ----
   float lam = 0.f;
   if constexpr (!V2) {
     float pa = 0.f, pb = 0.f;
@@ -197,160 +235,196 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(const PrefillArgs a
   }
 
   const float sl2 = a.sl2;
-  float mref[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
-  f32x16 o[2][CB];
+  float mref[MPW], lsum[MPW];
+  f32x16 o[MPW][CB];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int m = 0; m < MPW; ++m) {
+    mref[m] = -INFINITY;
+    lsum[m] = 0.f;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[m][cb][r] = 0.f;
+  }
+  // K tensor of each map inside a stage
+  int kbyte[MPW];
+#pragma unroll
+  for (int m = 0; m < MPW; ++m) kbyte[m] = V2 ? 0 : (m0 + m) * C::K_BYTES;
 
-  Stage<D, DV, V2, NT> stg;
-  stg.load(kp, kst, vp, vst, 0, T, tid);
-  stg.store(smem, tid);
-  __syncthreads();
-
+  issue_tile(0, 0);
   for (int kt = 0; kt < nkt; ++kt) {
-    const uint16_t* cur = smem + (kt & 1) * L::STAGE;
-    const bool has_next = kt + 1 < nkt;
-    if (has_next) stg.load(kp, kst, vp, vst, (kt + 1) * kBN, T, tid);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile kt landed
+    __syncthreads();                                  // all parts landed; other stage free
+    if (kt + 1 < nkt) issue_tile(kt + 1, (kt + 1) & 1);
+    if (!active) continue;
+    const unsigned char* st = smem + (kt & 1) * C::STAGE;
+    const unsigned char* vt = st + C::NK * C::K_BYTES;
 
-    if (active) {
 #pragma unroll
-      for (int sb = 0; sb < kBN / 32; ++sb) {
-        const int jb = kt * kBN + 32 * sb;
-        if (jb > i0w) break;  // sub-block entirely above this wave's diagonal
-        const bool diag = jb == i0w;
-        const int kb0 = 32 * sb;
+    for (int sb = 0; sb < kBN / 32; ++sb) {
+      const int jb = kt * kBN + 32 * sb;
+      if (jb > i0w) break;  // sub-block entirely above this wave's diagonal
+      const bool diag = jb == i0w;
 
-        // ---- scores, both maps: S^T[j][i] for 32 keys x 32 rows ----
-        f32x16 s[2];
+      // ---- scores S^T[j][i]: 32 keys x 32 rows per map ----
+      f32x16 s[MPW];
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < MPW; ++m)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[m][r] = 0.f;
-        const uint16_t* krow0 = cur + (kb0 + li) * L::KROW + 8 * hg;
+        for (int r = 0; r < 16; ++r) s[m][r] = 0.f;
+      const unsigned char* kr = st + sb * 32 * (D * 2);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 ka = *(const bf16x8*)(krow0 + 16 * ks);
-          s[0] = mfma32x32x16(ka, qf[0][ks], s[0]);
-          if constexpr (V2) {
-            s[1] = mfma32x32x16(ka, qf[1][ks], s[1]);
-          } else {
-            const bf16x8 kb = *(const bf16x8*)(krow0 + L::KSZ + 16 * ks);
-            s[1] = mfma32x32x16(kb, qf[1][ks], s[1]);
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (V2) {  // one K fragment feeds every map of the wave
+          const bf16x8 ka = *(const bf16x8*)(kr + koff[ks]);
+#pragma unroll
+          for (int m = 0; m < MPW; ++m) s[m] = mfma32x32x16(ka, qf[m][ks], s[m]);
+        } else {
+#pragma unroll
+          for (int m = 0; m < MPW; ++m)
+            s[m] = mfma32x32x16(*(const bf16x8*)(kr + kbyte[m] + koff[ks]), qf[m][ks], s[m]);
+        }
+      }
+
+      // ---- causal mask (diagonal sub-block only) and row maxima ----
+      float mb[MPW];
+      bool need[MPW];
+      bool any = false;
+#pragma unroll
+      for (int m = 0; m < MPW; ++m) {
+        if (diag) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = 8 * (r >> 2) + 4 * hg + (r & 3);
+            if (key > li) s[m][r] = -INFINITY;
           }
         }
+        float mx = s[m][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[m][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mb[m] = mx * sl2;
+        need[m] = mb[m] > mref[m] + kLazyLog2;
+        any |= need[m];
+      }
 
-        // ---- causal mask (diagonal sub-block only) and row maxima ----
-        float mb[2];
+      // ---- lazy rescale: only when some row's max outgrew its reference ----
+      if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          if (diag) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = 8 * (r >> 2) + 4 * hg + (r & 3);
-              if (key > li) s[m][r] = -INFINITY;
-            }
-          }
-          float mx = s[m][0];
-#pragma unroll
-          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[m][r]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          mb[m] = mx * sl2;
-        }
-
-        // ---- lazy rescale: only when some row's max outgrew its reference ----
-        const bool need0 = mb[0] > mref[0] + kLazyLog2;
-        const bool need1 = mb[1] > mref[1] + kLazyLog2;
-        if (__builtin_amdgcn_ballot_w64(need0 || need1)) {
-          const float al0 = need0 ? exp2f(mref[0] - mb[0]) : 1.f;
-          const float al1 = need1 ? exp2f(mref[1] - mb[1]) : 1.f;
-          if (need0) mref[0] = mb[0];
-          if (need1) mref[1] = mb[1];
-          lsum[0] *= al0;
-          lsum[1] *= al1;
+        for (int m = 0; m < MPW; ++m) {
+          const float al = need[m] ? exp2f(mref[m] - mb[m]) : 1.f;
+          if (need[m]) mref[m] = mb[m];
+          lsum[m] *= al;
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              o[0][cb][r] *= al0;
-              o[1][cb][r] *= al1;
-            }
+            for (int r = 0; r < 16; ++r) o[m][cb][r] *= al;
         }
+      }
 
-        // ---- probabilities -> bf16 B operand of O^T = V^T P^T ----
-        bf16x8 pk[2][2];
+      // ---- probabilities -> bf16 B operand of O^T = V^T P^T ----
+      bf16x8 pk[MPW][2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          f32x8 p0, p1;
-          float acc = 0.f;
+      for (int m = 0; m < MPW; ++m) {
+        f32x8 p0, p1;
+        float acc = 0.f;
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            p0[r] = __builtin_amdgcn_exp2f(fmaf(s[m][r], sl2, -mref[m]));
-            p1[r] = __builtin_amdgcn_exp2f(fmaf(s[m][r + 8], sl2, -mref[m]));
-            acc += p0[r] + p1[r];
-          }
-          lsum[m] += acc;
-          pk[m][0] = cvt_bf16x8(p0);
-          pk[m][1] = cvt_bf16x8(p1);
+        for (int r = 0; r < 8; ++r) {
+          p0[r] = __builtin_amdgcn_exp2f(fmaf(s[m][r], sl2, -mref[m]));
+          p1[r] = __builtin_amdgcn_exp2f(fmaf(s[m][r + 8], sl2, -mref[m]));
+          acc += p0[r] + p1[r];
         }
+        lsum[m] += acc;
+        pk[m][0] = cvt_bf16x8(p0);
+        pk[m][1] = cvt_bf16x8(p1);
+      }
 
-        // ---- O^T[c][i] += V^T[c][j] P^T[j][i]; V^T fragment shared by both maps ----
-        const uint16_t* vt = cur + L::NK * L::KSZ + li * L::VROW + kb0 + 4 * hg;
+      // ---- O^T[c][i] += V^T[c][j] P^T[j][i] ----
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
+      for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const uint16_t* vr = vt + 32 * cb * L::VROW + 16 * kk;
-            const bf16x8 va = join_bf16x8(*(const uint2*)vr, *(const uint2*)(vr + 8));
-            o[0][cb] = mfma32x32x16(va, pk[0][kk], o[0][cb]);
-            o[1][cb] = mfma32x32x16(va, pk[1][kk], o[1][cb]);
-          }
+        for (int kk = 0; kk < 2; ++kk) {
+          const unsigned char* p = vt + (sb * 32 + 16 * kk) * (DV * 2) + cb * 64 + voff[cb & 1];
+          const bf16x8 va = join_bf16x8(tr_read(p), tr_read(p + 8 * (DV * 2)));
+#pragma unroll
+          for (int m = 0; m < MPW; ++m) o[m][cb] = mfma32x32x16(va, pk[m][kk], o[m][cb]);
         }
       }
     }
-
-    if (has_next) stg.store(smem + ((kt + 1) & 1) * L::STAGE, tid);
-    __syncthreads();
   }
 
-  if (!active) return;
-
-  // --- epilogue: normalise each map, combine, (V1) RMSNorm and scale ---------
-  const float l0 = lsum[0] + __shfl_xor(lsum[0], 32, 64);
-  const float l1 = lsum[1] + __shfl_xor(lsum[1], 32, 64);
-  const float inv0 = 1.f / l0, inv1 = 1.f / l1;
+  // ---- epilogue ----------------------------------------------------------------
   const int row = i0w + li;
+  float inv[MPW];
+#pragma unroll
+  for (int m = 0; m < MPW; ++m) inv[m] = 1.f / (lsum[m] + __shfl_xor(lsum[m], 32, 64));
 
-  float w1;  // weight of map 2 in the combine
-  float post = 1.f;
   uint16_t* dst;
-  if constexpr (!V2) {
-    w1 = lam * inv1;
+  float post = 1.f;
+  if constexpr (MPW == 1) {
+    // map 2's wave hands lam * O2 / l2 to map 1's wave through LDS
+    __syncthreads();  // every wave is done with the K/V stages
+    float* xch = (float*)smem + (wave >> 1) * (CB * 16 * 64);  // one slot per partner pair
+    if (m0 == 1) {
+      if (active) {
+        float w = lam * inv[0];
+        if constexpr (V2) {
+          float lg = 0.f;
+          if (row < T) lg = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)row * a.lam.st + pair * a.lam.sh];
+          w = sigmoid_f32(lg) * inv[0];
+        }
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xch[(cb * 16 + r) * 64 + lane] = o[0][cb][r] * w;
+      }
+      __syncthreads();
+      return;
+    }
+    __syncthreads();
+    if (!active) return;
     float ss = 0.f;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float dv = o[0][cb][r] * inv0 - w1 * o[1][cb][r];
+        const float dv = o[0][cb][r] * inv[0] - xch[(cb * 16 + r) * 64 + lane];
         o[0][cb][r] = dv;
         ss += dv * dv;
       }
-    ss += __shfl_xor(ss, 32, 64);
-    post = (1.f - a.lam_init) / sqrtf(ss * (1.f / DV) + 1e-5f);
-    dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)row * a.out.st + h * a.out.sh;
+    if constexpr (!V2) {
+      ss += __shfl_xor(ss, 32, 64);
+      post = (1.f - a.lam_init) / sqrtf(ss * (1.f / DV) + 1e-5f);
+      dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)row * a.out.st + h * a.out.sh;
+    } else {
+      dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)row * a.out.st + pair * a.out.sh;
+    }
   } else {
-    float lg = 0.f;
-    if (row < T) lg = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)row * a.lam.st + pair * a.lam.sh];
-    w1 = sigmoid_f32(lg) * inv1;
+    if (!active) return;
+    if constexpr (!V2) {
+      const float w1 = lam * inv[1];
+      float ss = 0.f;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[0][cb][r] = o[0][cb][r] * inv0 - w1 * o[1][cb][r];
-    dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)row * a.out.st + pair * a.out.sh;
+        for (int r = 0; r < 16; ++r) {
+          const float dv = o[0][cb][r] * inv[0] - w1 * o[1][cb][r];
+          o[0][cb][r] = dv;
+          ss += dv * dv;
+        }
+      ss += __shfl_xor(ss, 32, 64);
+      post = (1.f - a.lam_init) / sqrtf(ss * (1.f / DV) + 1e-5f);
+      dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)row * a.out.st + h * a.out.sh;
+    } else {
+      float lg = 0.f;
+      if (row < T) lg = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)row * a.lam.st + pair * a.lam.sh];
+      const float w1 = sigmoid_f32(lg) * inv[1];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[0][cb][r] = o[0][cb][r] * inv[0] - w1 * o[1][cb][r];
+      dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)row * a.out.st + pair * a.out.sh;
+    }
   }
   if (row < T) {
 #pragma unroll
@@ -366,22 +440,34 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_kernel(const PrefillArgs a
   }
 }
 
-template <int D, int DV, bool V2>
+template <int D, int DV, bool V2, int NW, int MPW>
 hipError_t launch(const PrefillArgs& a, hipStream_t s) {
   const void* args[] = {&a};
-  return hipLaunchKernel((const void*)prefill_kernel<D, DV, V2, 4>, dim3(a.nwg), dim3(256), (void**)args, 0, s);
+  return hipLaunchKernel((const void*)prefill_kernel<D, DV, V2, NW, MPW>, dim3(a.nwg), dim3(NW * 64),
+                         (void**)args, 0, s);
 }
 
 }  // namespace
 
+// Per-shape kernel variant: waves per workgroup and maps per wave.
+#ifndef DA_V1_D64_MPW
+#define DA_V1_D64_MPW 2
+#endif
+#ifndef DA_V1_D128_MPW
+#define DA_V1_D128_MPW 1
+#endif
+#ifndef DA_V2_MPW
+#define DA_V2_MPW 1
+#endif
+
 hipError_t launch_prefill_v1_bf16(int d, const PrefillArgs& a0, hipStream_t s) {
   PrefillArgs a = a0;
-  const int BMT = 32 * 4;
+  const int BMT = 32 * 4;  // 4 row blocks of 32 per workgroup in both modes
   a.tiles = (a.T + BMT - 1) / BMT;
   a.units_per_b = a.H;
   a.nwg = a.B * a.H * a.tiles;
-  if (d == 64) return launch<64, 128, false>(a, s);
-  if (d == 128) return launch<128, 256, false>(a, s);
+  if (d == 64) return launch<64, 128, false, 4 * (3 - DA_V1_D64_MPW), DA_V1_D64_MPW>(a, s);
+  if (d == 128) return launch<128, 256, false, 4 * (3 - DA_V1_D128_MPW), DA_V1_D128_MPW>(a, s);
   return hipErrorInvalidValue;
 }
 
@@ -389,12 +475,12 @@ hipError_t launch_prefill_v2_bf16(int d, const PrefillArgs& a0, hipStream_t s) {
   PrefillArgs a = a0;
   const int np = a.G / 2;
   a.pc = np % 4 == 0 ? 4 : np % 2 == 0 ? 2 : 1;
-  const int BMT = 32 * (4 / a.pc);
+  const int BMT = 32 * (4 / a.pc);  // 4 pair-row units per workgroup
   a.tiles = (a.T + BMT - 1) / BMT;
   a.units_per_b = a.H * (np / a.pc);
   a.nwg = a.B * a.units_per_b * a.tiles;
-  if (d == 64) return launch<64, 64, true>(a, s);
-  if (d == 128) return launch<128, 128, true>(a, s);
+  if (d == 64) return launch<64, 64, true, 4 * (3 - DA_V2_MPW), DA_V2_MPW>(a, s);
+  if (d == 128) return launch<128, 128, true, 4 * (3 - DA_V2_MPW), DA_V2_MPW>(a, s);
   return hipErrorInvalidValue;
 }
 
