@@ -17,7 +17,7 @@
 //     (no registers, no VALU), double-buffered: the next tile streams in
 //     while the current one is consumed; one barrier per tile.  In LDS both
 //     stay row-major with an XOR swizzle of their 16-byte chunks, so the
-//     MFMA operand reads are bank-conflict-free.
+//     MFMA operand reads are bank-conflict-free (256 B per clock).
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: Q fragments stay in registers for the whole
 //     key loop, each lane holds 16 scores of ONE query row (softmax state is
@@ -40,6 +40,8 @@
 //     tiles of one head share an L2.
 #include <math.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace da {
@@ -52,10 +54,18 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-// 16 bytes per lane, HBM -> LDS; lane l's bytes land at lds + 16 l.  `lds`
-// must be the same for every lane of the wave.
-__device__ __forceinline__ void dma16(const void* g, unsigned char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+// 16 bytes per lane, HBM -> LDS (global_load_lds_dwordx4): lane l's bytes
+// land at LDS byte address lds_addr + 16 l; lds_addr must be wave-uniform.
+// Issued as inline asm so the compiler does not track it: it would otherwise
+// make every LDS read wait for the copy in flight, although that copy only
+// ever targets the other LDS stage.  The kernel waits for it explicitly
+// (vmcnt(0) + barrier) before the stage is read.  M0 is used by nothing else
+// in these kernels.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
 }
 
 // LDS transpose read: in each group of 16 lanes, lane j receives element
@@ -63,6 +73,29 @@ __device__ __forceinline__ void dma16(const void* g, unsigned char* lds) {
 __device__ __forceinline__ uint2 tr_read(const unsigned char* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
   return __builtin_bit_cast(uint2, v);
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// XOR swizzles of 16-byte chunks inside a tile row (measured conflict-free on
+// gfx950, whose LDS serves 256 B per clock from 64 banks):
+//   K rows (read by ds_read_b128, 16 rows per pass): rows of 256 B use
+//   chunk ^ (r & 15); rows of 128 B use chunk ^ ((r & 7) ^ ((r >> 3) & 1)).
+//   V rows (read by ds_read_b64_tr_b16, 4 rows x 32 B per 16 lanes):
+//   chunk ^ 4 (r & 3) when a row has >= 16 chunks, else chunk ^ 2 (r & 3).
+template <int D>
+__device__ __forceinline__ int k_swizzle(int r) {
+  return D >= 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
+}
+template <int DV>
+__device__ __forceinline__ int v_swizzle(int r) {
+  return (DV >= 128 ? 4 : 2) * (r & 3);
 }
 
 template <int D, int DV, bool V2, int NW, int MPW>
@@ -121,12 +154,12 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW>::MIN_BLOCKS)
       rb = wave >> 1;
       m0 = wave & 1;  // this wave's map
     }
-    const TIn* qs[2] = {&a.q1, &a.q2};
 #pragma unroll
-    for (int m = 0; m < MPW; ++m) {
-      const TIn& t = *qs[m0 + m];
-      qp[m] = (const uint16_t*)t.p + b * t.sb + h * t.sh;
-      qst[m] = t.st;
+    for (int m = 0; m < MPW; ++m) {  // selects, not an indexed array: keeps args out of scratch
+      const bool second = m0 + m == 1;
+      qp[m] = second ? (const uint16_t*)a.q2.p + b * a.q2.sb + h * a.q2.sh
+                     : (const uint16_t*)a.q1.p + b * a.q1.sb + h * a.q1.sh;
+      qst[m] = second ? a.q2.st : a.q1.st;
     }
     kp[0] = (const uint16_t*)a.k1.p + b * a.k1.sb + h * a.k1.sh;
     kp[1] = (const uint16_t*)a.k2.p + b * a.k2.sb + h * a.k2.sh;
@@ -142,7 +175,7 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW>::MIN_BLOCKS)
     //           row block k / pc.
     const int pw = MPW == 2 ? wave : wave >> 1;
     if constexpr (MPW == 1) m0 = wave & 1;
-    RB = (NW / (3 - MPW)) / a.pc;
+    RB = (MPW == 2 ? NW : NW / 2) / a.pc;
     rb = pw / a.pc;
     pair = g * (a.G / 2) + pcix * a.pc + pw % a.pc;
 #pragma unroll
@@ -160,28 +193,30 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW>::MIN_BLOCKS)
   const int kend = min(T, I0 + BMT);
   const int nkt = (kend + kBN - 1) / kBN;
 
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+
   // ---- tile DMA: wave issues CPW 1 KB chunks; rows >= T are clamped to T-1
   // (finite data; those keys are always masked for every valid query) ----
   auto issue_tile = [&](int kt, int stage) {
     const int j0 = kt * kBN;
-    unsigned char* sbase = smem + stage * C::STAGE;
+    const uint32_t sbase = smem_lds + stage * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::CPW; ++i) {
       const int ci = wave + NW * i;  // chunk of this stage (wave-uniform)
       const uint16_t* g;
-      unsigned char* dst;
+      uint32_t dst;
       if (ci < C::NK * C::KCH) {
         const int n = ci / C::KCH, cix = ci % C::KCH;
         const int pos = cix * 64 + lane;  // 16 B chunk index inside the K tile
         const int r = pos / (D / 8), sc = pos % (D / 8);
-        const int c = sc ^ (r & 7);
-        g = kp[n] + (int64_t)min(j0 + r, T - 1) * kst[n] + c * 8;
+        const int c = sc ^ k_swizzle<D>(r);
+        g = (n ? kp[1] : kp[0]) + (int64_t)min(j0 + r, T - 1) * (n ? kst[1] : kst[0]) + c * 8;
         dst = sbase + n * C::K_BYTES + cix * 1024;
       } else {
         const int cix = ci - C::NK * C::KCH;
         const int pos = cix * 64 + lane;
         const int r = pos / (DV / 8), sc = pos % (DV / 8);
-        const int c = sc ^ (2 * (r & 3));
+        const int c = sc ^ v_swizzle<DV>(r);
         g = vp + (int64_t)min(j0 + r, T - 1) * vst + c * 8;
         dst = sbase + C::NK * C::K_BYTES + cix * 1024;
       }
@@ -201,24 +236,33 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW>::MIN_BLOCKS)
                                       : make_uint4(0, 0, 0, 0));
   }
 
+  // Retire the Q loads here.  The compiler cannot see the tile DMA, but the
+  // hardware counter counts it: a compiler-placed vmcnt wait for Q inside the
+  // key loop would also wait for the next tile's copy.
+#pragma unroll
+  for (int m = 0; m < MPW; ++m)
+#pragma unroll
+    for (int ks = 0; ks < KS; ks += 2)
+      asm volatile("s_waitcnt vmcnt(0)" : "+v"(qf[m][ks]), "+v"(qf[m][ks + 1]));
+
   // ---- per-lane LDS offsets ----
-  // K chunk (2ks + hg) of row li lives at chunk (2ks + hg) ^ (li & 7).
+  // K chunk (2ks + hg) of tile row r = 32 sb + li sits at chunk (2ks + hg) ^ k_swizzle(li).
   int koff[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = li * (D * 2) + (((2 * ks + hg) ^ (li & 7)) << 4);
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = li * (D * 2) + (((2 * ks + hg) ^ k_swizzle<D>(li)) << 4);
   // V^T operand via transpose reads: lane (G16 = lane>>4, l16 = lane&15) points at
-  // row 4*(G16>>1) + (l16>>2) (+ sub-block, k-step), columns 32cb + 16(G16&1) + 4(l16&3).
-  int voff[2];  // for even / odd column blocks (the swizzle flips bit 2 of the chunk)
+  // row 4*(G16>>1) + (l16>>2) (+ sub-block, k-step), columns 32cb + 16(G16&1) + 4(l16&3),
+  // i.e. chunk 4cb + cl.  The swizzle only permutes chunks within aligned groups of
+  // 4*NV, so the per-lane offset depends on cb only through cb % NV.
+  constexpr int NV = DV >= 128 ? 4 : 2;
+  int voff[NV];
   {
     const int l16 = lane & 15, g16 = lane >> 4;
     const int vr = 4 * (g16 >> 1) + (l16 >> 2);
-    const int cl = 2 * (g16 & 1) + ((l16 & 3) >> 1);  // chunk within a 4-chunk block
-    const int x = 2 * (l16 >> 2);                     // swizzle of rows with (r & 3) = l16 >> 2
+    const int cl = 2 * (g16 & 1) + ((l16 & 3) >> 1);
+    const int x = v_swizzle<DV>(vr);  // rows of one read share r & 3 = l16 >> 2
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int c = ((4 * par + cl) ^ x) - 4 * par;  // chunk offset relative to 4*cb
-      voff[par] = vr * (DV * 2) + c * 16 + (l16 & 1) * 8;
-    }
+    for (int v = 0; v < NV; ++v) voff[v] = vr * (DV * 2) + (((4 * v + cl) ^ x) - 4 * v) * 16 + (l16 & 1) * 8;
   }
 
   // ---- V1 lambda (one fp32 scalar per call) ----
@@ -260,10 +304,10 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW>::MIN_BLOCKS)
     const unsigned char* st = smem + (kt & 1) * C::STAGE;
     const unsigned char* vt = st + C::NK * C::K_BYTES;
 
-#pragma unroll
-    for (int sb = 0; sb < kBN / 32; ++sb) {
+    static_for<0, kBN / 32>([&](auto sbc) {
+      constexpr int sb = decltype(sbc)::value;
       const int jb = kt * kBN + 32 * sb;
-      if (jb > i0w) break;  // sub-block entirely above this wave's diagonal
+      if (jb > i0w) return;  // sub-block entirely above this wave's diagonal
       const bool diag = jb == i0w;
 
       // ---- scores S^T[j][i]: 32 keys x 32 rows per map ----
@@ -341,16 +385,16 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW>::MIN_BLOCKS)
 
       // ---- O^T[c][i] += V^T[c][j] P^T[j][i] ----
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
+      for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const unsigned char* p = vt + (sb * 32 + 16 * kk) * (DV * 2) + cb * 64 + voff[cb & 1];
+        for (int cb = 0; cb < CB; ++cb) {
+          const unsigned char* p = vt + (sb * 32 + 16 * kk) * (DV * 2) + cb * 64 + voff[cb % NV];
           const bf16x8 va = join_bf16x8(tr_read(p), tr_read(p + 8 * (DV * 2)));
 #pragma unroll
           for (int m = 0; m < MPW; ++m) o[m][cb] = mfma32x32x16(va, pk[m][kk], o[m][cb]);
         }
       }
-    }
+    });
   }
 
   // ---- epilogue ----------------------------------------------------------------
@@ -449,9 +493,12 @@ hipError_t launch(const PrefillArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Per-shape kernel variant: waves per workgroup and maps per wave.
+// Per-shape kernel variant: maps per wave (MPW) and waves per workgroup (NW).
 #ifndef DA_V1_D64_MPW
-#define DA_V1_D64_MPW 2
+#define DA_V1_D64_MPW 1
+#endif
+#ifndef DA_V1_D64_NW
+#define DA_V1_D64_NW 4
 #endif
 #ifndef DA_V1_D128_MPW
 #define DA_V1_D128_MPW 1
@@ -459,28 +506,41 @@ hipError_t launch(const PrefillArgs& a, hipStream_t s) {
 #ifndef DA_V2_MPW
 #define DA_V2_MPW 1
 #endif
+#ifndef DA_V2_NW
+#define DA_V2_NW 8
+#endif
 
 hipError_t launch_prefill_v1_bf16(int d, const PrefillArgs& a0, hipStream_t s) {
   PrefillArgs a = a0;
-  const int BMT = 32 * 4;  // 4 row blocks of 32 per workgroup in both modes
-  a.tiles = (a.T + BMT - 1) / BMT;
   a.units_per_b = a.H;
-  a.nwg = a.B * a.H * a.tiles;
-  if (d == 64) return launch<64, 128, false, 4 * (3 - DA_V1_D64_MPW), DA_V1_D64_MPW>(a, s);
-  if (d == 128) return launch<128, 256, false, 4 * (3 - DA_V1_D128_MPW), DA_V1_D128_MPW>(a, s);
+  auto geom = [&](int nw, int mpw) {
+    const int BMT = 32 * (mpw == 2 ? nw : nw / 2);  // rows per workgroup
+    a.tiles = (a.T + BMT - 1) / BMT;
+    a.nwg = a.B * a.H * a.tiles;
+  };
+  if (d == 64) {
+    geom(DA_V1_D64_NW, DA_V1_D64_MPW);
+    return launch<64, 128, false, DA_V1_D64_NW, DA_V1_D64_MPW>(a, s);
+  }
+  if (d == 128) {
+    geom(4 * (3 - DA_V1_D128_MPW), DA_V1_D128_MPW);
+    return launch<128, 256, false, 4 * (3 - DA_V1_D128_MPW), DA_V1_D128_MPW>(a, s);
+  }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_v2_bf16(int d, const PrefillArgs& a0, hipStream_t s) {
   PrefillArgs a = a0;
   const int np = a.G / 2;
-  a.pc = np % 4 == 0 ? 4 : np % 2 == 0 ? 2 : 1;
-  const int BMT = 32 * (4 / a.pc);  // 4 pair-row units per workgroup
+  const int units = DA_V2_MPW == 2 ? DA_V2_NW : DA_V2_NW / 2;  // (pair, row block) slots per workgroup
+  a.pc = np % units == 0 ? units : np % 2 == 0 && units % 2 == 0 ? 2 : 1;
+  if (a.pc > units) a.pc = 1;
+  const int BMT = 32 * (units / a.pc);
   a.tiles = (a.T + BMT - 1) / BMT;
   a.units_per_b = a.H * (np / a.pc);
   a.nwg = a.B * a.units_per_b * a.tiles;
-  if (d == 64) return launch<64, 64, true, 4 * (3 - DA_V2_MPW), DA_V2_MPW>(a, s);
-  if (d == 128) return launch<128, 128, true, 4 * (3 - DA_V2_MPW), DA_V2_MPW>(a, s);
+  if (d == 64) return launch<64, 64, true, DA_V2_NW, DA_V2_MPW>(a, s);
+  if (d == 128) return launch<128, 128, true, DA_V2_NW, DA_V2_MPW>(a, s);
   return hipErrorInvalidValue;
 }
 
