@@ -92,32 +92,143 @@ def _roofline(w, launch_ms):
             "frac": round(a / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel_ms": round(avg_s * 1e3, 5)}
 
 
-def _cpu_baseline(w, x):
-    """Time the fp64 oracle on a bounded sample (leading batch entries of
-    layer 0) of the headline workload."""
+def _cpu_baseline(w, x, min_seconds=10.0, max_seconds=30.0):
+    """Time the fp64 oracle on a bounded sample of the headline workload: whole
+    layer calls (all rows of all heads) in the step's layer order, repeated
+    until at least `min_seconds` of CPU work (stopping before `max_seconds`)."""
     import numpy as np
 
     import oracle
 
     cores = oracle.set_threads(len(os.sched_getaffinity(0)))
-    host = {n: x[n].detach().to("cpu").double().numpy() for n in x}
-    lam = [host[n] for n in ("lq1", "lk1", "lq2", "lk2")]
-
-    def run(nb):
-        args = [np.ascontiguousarray(host[n][:nb]) for n in ("q1", "q2", "k1", "k2", "v")]
+    host = {n: np.ascontiguousarray(x[n].detach().to("cpu").double().numpy()) for n in x}
+    args = [host[n] for n in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")]
+    layers = list(w.layers) or [0]
+    calls, t = 0, 0.0
+    while t < min_seconds:
+        layer = layers[calls % len(layers)]
         t0 = time.perf_counter()
-        oracle.v1_fwd(*args, *lam, 0)
-        return time.perf_counter() - t0
-
-    nb, t = 1, run(1)
-    if t < 10.0 and w.B > 1:
-        nb = max(1, min(w.B, int(round(15.0 / max(t, 1e-3)))))
-        if nb > 1:
-            t = run(nb)
-    flops = w.flops() * nb / w.B
-    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        oracle.v1_fwd(*args, layer)
+        dt = time.perf_counter() - t0
+        t += dt
+        calls += 1
+        if t + dt > max_seconds:
+            break
+    return {"value": round(w.flops() * calls / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": round(t, 3),
-            "sample": f"layer 0 of {w.name}, batch entries 0..{nb - 1} ({nb * w.H * w.T} rows), fp64 C + OpenMP"}
+            "sample": f"{calls} whole layer calls of {w.name} (layers {layers[0]}.. in order), fp64 C + OpenMP"}
+
+
+def _source_sha(kind):
+    """sha256 of the HIP source a kernel is built from; a traffic figure taken
+    from hardware counters only applies to the kernel it was measured on."""
+    import hashlib
+
+    src = {"v1": "prefill_bf16.hip", "v2": "prefill_bf16.hip", "decode": "decode_bf16.hip"}[kind]
+    path = os.path.join(ROOT, "differential_attention_diffattn_amd", "csrc", src)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def _traffic(w):
+    """HBM bytes per launch of the workload's dominant kernel from the committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the same
+    counters read for a plain copy of known size), or None when absent or
+    taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(w.name)
+    if not rec or rec.get("kernel_source_sha256") != _source_sha(w.kind):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def _copy_calibration(torch, steps):
+    """A plain device copy of known size (reads and writes 1 GiB), the reference
+    for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    n = 1 << 29  # bf16 elements = 1 GiB
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": "copy_1GiB", "bytes_read": 2 * n, "bytes_written": 2 * n, "ms": round(ms, 4),
+            "GB_per_s": round(4 * n / ms / 1e6, 1)}
+
+
+def write_traffic(pmc_dir):
+    """Turn FETCH_SIZE / WRITE_SIZE counter runs into profiles/traffic.json.
+
+    Expects rocprofv3 CSV output in <pmc_dir>/pmc_<workload>_<COUNTER>/ for the
+    'copy' calibration and each workload (bench.py --only <workload>).  Each
+    counter is scaled by bytes_moved / counter_reading of the 1 GiB copy."""
+    import csv
+    from collections import defaultdict
+
+    from differential_attention_diffattn_amd import workloads
+
+    def per_dispatch(work, counter, match):
+        f = os.path.join(pmc_dir, f"pmc_{work}_{counter}", "run_counter_collection.csv")
+        acc = defaultdict(float)
+        for r in csv.DictReader(open(f)):
+            if match in r["Kernel_Name"]:
+                acc[r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return sum(acc.values()) / len(acc)
+
+    copy_bytes = 1 << 30
+    f_scale = copy_bytes / (1024 * per_dispatch("copy", "FETCH_SIZE", "copyBuffer"))
+    w_scale = copy_bytes / (1024 * per_dispatch("copy", "WRITE_SIZE", "copyBuffer"))
+    out = {"_calibration": {"copy_bytes_each_way": copy_bytes, "fetch_scale": round(f_scale, 4),
+                            "write_scale": round(w_scale, 4)}}
+    for name, match in [("v1_gpt2small_B8_H6_T1024_d64", "prefill_kernel"), ("v1_3b_B2_H12_T4096_d128", "prefill_kernel"),
+                        ("v2_prefill_B1_T8192_Hq64_Hkv8_d128", "prefill_kernel"),
+                        ("v2_decode_B64_L32768_Hq64_Hkv8_d128", "decode_split_kernel")]:
+        w = workloads.WORKLOADS[name]
+        fk = per_dispatch(name, "FETCH_SIZE", match)
+        wk = per_dispatch(name, "WRITE_SIZE", match)
+        traffic = fk * 1024 * f_scale + wk * 1024 * w_scale
+        out[name] = {"kernel": match, "kernel_source_sha256": _source_sha(w.kind),
+                     "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+                     "traffic_bytes_per_launch": int(traffic), "algorithmic_bytes_per_launch": w.compulsory_bytes(),
+                     "traffic_over_algorithmic": round(traffic / w.compulsory_bytes(), 3)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    return out
+
+
+def summarize(path, match):
+    """Summarise rocprofv3 CSV output under `path` for kernels whose name
+    contains `match`: kernel-trace durations and/or per-dispatch counters."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    out = {}
+    for f in sorted(glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True)):
+        durs = defaultdict(list)
+        for r in csv.DictReader(open(f)):
+            if match in r["Kernel_Name"]:
+                durs[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        for k, v in durs.items():
+            out.setdefault("kernels", {})[k] = {"dispatches": len(v), "avg_us": round(sum(v) / len(v), 3),
+                                                 "min_us": round(min(v), 3), "max_us": round(max(v), 3)}
+    acc = defaultdict(lambda: defaultdict(float))
+    for f in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            if match in r["Kernel_Name"]:
+                acc[r["Counter_Name"]][(f, r["Dispatch_Id"])] += float(r["Counter_Value"])
+    for k, v in acc.items():
+        out.setdefault("counters_per_dispatch", {})[k] = sum(v.values()) / len(v)
+    return out
 
 
 def main():
@@ -125,10 +236,22 @@ def main():
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default=None, help="time a single workload by name (no cpu baseline)")
+    ap.add_argument("--only", default=None,
+                    help="time a single workload by name, or 'copy' for the 1 GiB copy calibration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--summarize", default=None, metavar="DIR",
+                    help="summarise rocprofv3 CSV output in DIR (kernels matching --kernel) and exit")
+    ap.add_argument("--kernel", default="", help="kernel-name substring for --summarize")
+    ap.add_argument("--write-traffic", default=None, metavar="DIR",
+                    help="turn FETCH_SIZE/WRITE_SIZE runs in DIR into profiles/traffic.json and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        print(json.dumps(write_traffic(args.write_traffic), indent=1))
+        return
+    if args.summarize:
+        print(json.dumps(summarize(args.summarize, args.kernel), indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); the kernels shard "
               "by head/group with no exchange, so the 1-GPU figure is the per-GPU figure.", file=sys.stderr)
@@ -153,8 +276,10 @@ def main():
         layers = list(w.layers) if w.layers else [0]
         elapsed, launch_ms = _timed(torch, call, layers, steps, warmup)
         per_call_s = elapsed / (steps * len(layers))
+        roof = _roofline(w, launch_ms)
+        roof["traffic"] = _traffic(w)
         res = {"workload": name, "steps": steps, "warmup": warmup, "calls_per_step": len(layers),
-               "ms_per_step": round(elapsed / steps * 1e3, 5), "roofline": _roofline(w, launch_ms)}
+               "ms_per_step": round(elapsed / steps * 1e3, 5), "roofline": roof}
         if w.kind == "decode":
             res.update(metric="V2 decode HBM GB/s", unit="GB/s",
                        value=round(w.compulsory_bytes() / per_call_s / 1e9, 1))
@@ -163,6 +288,9 @@ def main():
         log(json.dumps(res))
         return w, x, res
 
+    if args.only == "copy":
+        print(json.dumps(_copy_calibration(torch, args.steps)))
+        return
     if args.only:
         _, _, res = measure(args.only, args.steps, args.warmup)
         print(json.dumps(res))
