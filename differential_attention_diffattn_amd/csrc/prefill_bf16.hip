@@ -47,8 +47,13 @@
 namespace da {
 namespace {
 
-constexpr int kBN = 64;           // keys per LDS stage
 constexpr float kLazyLog2 = 8.f;  // rescale only when the max grows by > 2^8
+#ifndef DA_V2_BN
+#define DA_V2_BN 128  // keys per LDS stage of the V2 kernel (64 or 128)
+#endif
+#ifndef DA_SETPRIO
+#define DA_SETPRIO 1  // raise wave priority while issuing MFMA sections
+#endif
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -98,14 +103,18 @@ __device__ __forceinline__ int v_swizzle(int r) {
   return (DV >= 128 ? 4 : 2) * (r & 3);
 }
 
-template <int D, int DV, bool V2, int NW, int MPW>
+template <int D, int DV, bool V2, int NW, int MPW, bool PIPE>
 struct Cfg {
   static constexpr int NT = NW * 64;
   static constexpr int KS = D / 16;   // k-steps of the score MFMA
   static constexpr int CB = DV / 32;  // 32-wide column blocks of O^T
   static constexpr int NK = V2 ? 1 : 2;
-  static constexpr int K_BYTES = kBN * D * 2;
-  static constexpr int V_BYTES = kBN * DV * 2;
+  // PIPE: 32-key tiles in a 4-stage ring (software-pipelined key loop);
+  // otherwise 64-key tiles, double-buffered.
+  static constexpr int BN = PIPE ? 32 : (V2 ? DA_V2_BN : 64);
+  static constexpr int NST = PIPE ? 4 : 2;
+  static constexpr int K_BYTES = BN * D * 2;
+  static constexpr int V_BYTES = BN * DV * 2;
   static constexpr int STAGE = NK * K_BYTES + V_BYTES;
   static constexpr int KCH = K_BYTES / 1024;  // 1 KB DMA instructions per K tensor
   static constexpr int VCH = V_BYTES / 1024;
@@ -115,23 +124,50 @@ struct Cfg {
   static_assert(D >= 64 && DV >= 64, "swizzles assume >= 8 chunks per row");
   // MPW == 1: one exchange slot per partner-wave pair (fp32, lane-native order)
   static constexpr int XBYTES = MPW == 1 ? (NW / 2) * CB * 16 * 64 * 4 : 0;
-  static constexpr int SMEM = 2 * STAGE > XBYTES ? 2 * STAGE : XBYTES;
+  static constexpr int SMEM = NST * STAGE > XBYTES ? NST * STAGE : XBYTES;
   static constexpr int MIN_BLOCKS = NW == 4 ? 2 : 1;  // two waves per SIMD
 };
 
-template <int D, int DV, bool V2, int NW, int MPW>
-__global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW>::MIN_BLOCKS))
+template <int MPW>
+struct Scores {
+  f32x16 s[MPW];
+};
+template <int MPW>
+struct Probs {
+  bf16x8 p[MPW][2];
+};
+
+template <int D, int DV, bool V2, int NW, int MPW, bool PIPE>
+__global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_BLOCKS))
     prefill_kernel(const PrefillArgs a) {
-  using C = Cfg<D, DV, V2, NW, MPW>;
+  using C = Cfg<D, DV, V2, NW, MPW, PIPE>;
+  constexpr int kBN = C::BN;
   constexpr int KS = C::KS, CB = C::CB;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::SMEM];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // wave index in a scalar register: every per-wave condition derived from it
+  // is then a uniform (scalar) branch and does not split basic blocks
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, hg = lane >> 5;
 
-  const int logical = xcd_logical_id(blockIdx.x, a.nwg);
-  const int unit = logical / a.tiles;
-  const int tile = a.tiles - 1 - logical % a.tiles;  // heaviest tiles first
+  // Work order.  Units (a head / group of one batch entry) are dealt to XCDs
+  // round-robin; when every XCD gets the same number of units, each XCD runs
+  // its units' tiles heaviest-first across all of them (longest causal rows
+  // start first, the L2 still only holds those units' K/V).  Otherwise each
+  // XCD gets a contiguous run of (unit, tile) pairs, heaviest tile first.
+  int unit, tile;
+  {
+    const int units = a.nwg / a.tiles;
+    if (units % kXcds == 0) {
+      const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, nu = units / kXcds;
+      tile = a.tiles - 1 - slot / nu;
+      unit = xcd + kXcds * (slot % nu);
+    } else {
+      const int logical = xcd_logical_id(blockIdx.x, a.nwg);
+      unit = logical / a.tiles;
+      tile = a.tiles - 1 - logical % a.tiles;
+    }
+  }
   const int b = unit / a.units_per_b;
   const int u = unit % a.units_per_b;
   const int T = a.T;
@@ -295,106 +331,176 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW>::MIN_BLOCKS)
 #pragma unroll
   for (int m = 0; m < MPW; ++m) kbyte[m] = V2 ? 0 : (m0 + m) * C::K_BYTES;
 
-  issue_tile(0, 0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile kt landed
-    __syncthreads();                                  // all parts landed; other stage free
-    if (kt + 1 < nkt) issue_tile(kt + 1, (kt + 1) & 1);
-    if (!active) continue;
-    const unsigned char* st = smem + (kt & 1) * C::STAGE;
+  // ---- the arithmetic of one 32-key sub-block, shared by both loop forms ----
+  // scores S^T[j][i] (32 keys x 32 rows per map) from K rows row0.. of a stage
+  auto qk = [&](const unsigned char* st, int row0) {
+    Scores<MPW> r;
+#pragma unroll
+    for (int m = 0; m < MPW; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r.s[m][i] = 0.f;
+    const unsigned char* kr = st + row0 * (D * 2);
+    if (DA_SETPRIO) __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (V2) {  // one K fragment feeds every map of the wave
+        const bf16x8 ka = *(const bf16x8*)(kr + koff[ks]);
+#pragma unroll
+        for (int m = 0; m < MPW; ++m) r.s[m] = mfma32x32x16(ka, qf[m][ks], r.s[m]);
+      } else {
+#pragma unroll
+        for (int m = 0; m < MPW; ++m)
+          r.s[m] = mfma32x32x16(*(const bf16x8*)(kr + kbyte[m] + koff[ks]), qf[m][ks], r.s[m]);
+      }
+    }
+    if (DA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    return r;
+  };
+  // causal mask (diagonal sub-block only), row maxima, and whether any row's max
+  // outgrew its reference by more than 2^8
+  float mb[MPW];
+  bool need[MPW];
+  auto softmax_head = [&](Scores<MPW>& S, bool diag) {
+    bool any = false;
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) {
+      if (diag) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 8 * (r >> 2) + 4 * hg + (r & 3);
+          if (key > li) S.s[m][r] = -INFINITY;
+        }
+      }
+      float mx = S.s[m][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S.s[m][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mb[m] = mx * sl2;
+      need[m] = mb[m] > mref[m] + kLazyLog2;
+      any |= need[m];
+    }
+    return any;
+  };
+  auto rescale = [&]() {
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) {
+      const float al = need[m] ? exp2f(mref[m] - mb[m]) : 1.f;
+      if (need[m]) mref[m] = mb[m];
+      lsum[m] *= al;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[m][cb][r] *= al;
+    }
+  };
+  // probabilities -> bf16 B operand of O^T = V^T P^T
+  auto softmax_exp = [&](const Scores<MPW>& S) {
+    Probs<MPW> P;
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) {
+      f32x8 p0, p1;
+      float acc = 0.f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        p0[r] = __builtin_amdgcn_exp2f(fmaf(S.s[m][r], sl2, -mref[m]));
+        p1[r] = __builtin_amdgcn_exp2f(fmaf(S.s[m][r + 8], sl2, -mref[m]));
+        acc += p0[r] + p1[r];
+      }
+      lsum[m] += acc;
+      P.p[m][0] = cvt_bf16x8(p0);
+      P.p[m][1] = cvt_bf16x8(p1);
+    }
+    return P;
+  };
+  // O^T[c][i] += V^T[c][j] P^T[j][i] over V rows row0..row0+31 of a stage
+  auto pv = [&](const unsigned char* st, int row0, const Probs<MPW>& P) {
     const unsigned char* vt = st + C::NK * C::K_BYTES;
+    if (DA_SETPRIO) __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const unsigned char* q = vt + (row0 + 16 * kk) * (DV * 2) + cb * 64 + voff[cb % NV];
+        const bf16x8 va = join_bf16x8(tr_read(q), tr_read(q + 8 * (DV * 2)));
+#pragma unroll
+        for (int m = 0; m < MPW; ++m) o[m][cb] = mfma32x32x16(va, P.p[m][kk], o[m][cb]);
+      }
+    }
+    if (DA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+  };
 
-    static_for<0, kBN / 32>([&](auto sbc) {
-      constexpr int sb = decltype(sbc)::value;
-      const int jb = kt * kBN + 32 * sb;
-      if (jb > i0w) return;  // sub-block entirely above this wave's diagonal
-      const bool diag = jb == i0w;
-
-      // ---- scores S^T[j][i]: 32 keys x 32 rows per map ----
-      f32x16 s[MPW];
+  if constexpr (!PIPE) {
+    // ---- 64-key tiles, double-buffered; sub-blocks processed in order ----
+    issue_tile(0, 0);
+    for (int kt = 0; kt < nkt; ++kt) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile kt landed
+      __syncthreads();                                  // all parts landed; other stage free
+      if (kt + 1 < nkt) issue_tile(kt + 1, (kt + 1) & 1);
+      if (!active) continue;
+      const unsigned char* st = smem + (kt & 1) * C::STAGE;
 #pragma unroll
-      for (int m = 0; m < MPW; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[m][r] = 0.f;
-      const unsigned char* kr = st + sb * 32 * (D * 2);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (V2) {  // one K fragment feeds every map of the wave
-          const bf16x8 ka = *(const bf16x8*)(kr + koff[ks]);
-#pragma unroll
-          for (int m = 0; m < MPW; ++m) s[m] = mfma32x32x16(ka, qf[m][ks], s[m]);
+      for (int sb = 0; sb < kBN / 32; ++sb) {
+        const int jb = kt * kBN + 32 * sb;
+        if (jb > i0w) break;  // sub-block entirely above this wave's diagonal
+        Scores<MPW> S = qk(st, 32 * sb);
+        if (__builtin_amdgcn_ballot_w64(softmax_head(S, jb == i0w))) rescale();
+        pv(st, 32 * sb, softmax_exp(S));
+      }
+    }
+  } else {
+    // ---- 32-key tiles in a 4-stage ring, software-pipelined ----
+    // Step n (tile n) issues the MFMAs of P.V for tile n-1 and of the scores
+    // for tile n+1 in the same basic block as the exponentials of tile n, so
+    // matrix and vector work overlap inside the wave.  Tile n+1 is waited for
+    // (and made visible by a barrier) at step n; the copy of tile n+2 then
+    // goes to stage (n+2)%4, whose last reader was step n-1.  A rescale (rare)
+    // first flushes the pending P.V of tile n-1.
+    const int dw = active ? i0w / 32 : -1;  // last tile this wave needs
+    auto stage = [&](int n) { return smem + (n & 3) * C::STAGE; };
+    issue_tile(0, 0);
+    if (nkt > 1) issue_tile(1, 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    Scores<MPW> S;
+    Probs<MPW> P;
+    if (dw >= 0) S = qk(stage(0), 0);
+    bool pending = false;  // P holds tile n-1's probabilities, its P.V not issued yet
+    for (int n = 0; n < nkt; ++n) {
+      const bool mine = n <= dw;
+      if (mine && __builtin_amdgcn_ballot_w64(softmax_head(S, n == dw))) {
+        if (pending) {
+          pv(stage(n - 1), 0, P);
+          pending = false;
+        }
+        rescale();
+      }
+      if (n + 1 < nkt) {
+        if (n >= 1) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile n+1 landed (this wave's part)
+          __syncthreads();
+        }
+        if (n + 2 < nkt) issue_tile(n + 2, (n + 2) & 3);
+      }
+      if (!mine) continue;
+      if (n < dw) {
+        if (pending) {  // steady state
+          const Scores<MPW> Sn = qk(stage(n + 1), 0);
+          const Probs<MPW> Pn = softmax_exp(S);
+          pv(stage(n - 1), 0, P);
+          S = Sn;
+          P = Pn;
         } else {
-#pragma unroll
-          for (int m = 0; m < MPW; ++m)
-            s[m] = mfma32x32x16(*(const bf16x8*)(kr + kbyte[m] + koff[ks]), qf[m][ks], s[m]);
+          const Scores<MPW> Sn = qk(stage(n + 1), 0);
+          P = softmax_exp(S);
+          S = Sn;
         }
+        pending = true;
+      } else {  // n == dw: this wave's last tile
+        if (pending) pv(stage(n - 1), 0, P);
+        pv(stage(n), 0, softmax_exp(S));
+        pending = false;
       }
-
-      // ---- causal mask (diagonal sub-block only) and row maxima ----
-      float mb[MPW];
-      bool need[MPW];
-      bool any = false;
-#pragma unroll
-      for (int m = 0; m < MPW; ++m) {
-        if (diag) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 8 * (r >> 2) + 4 * hg + (r & 3);
-            if (key > li) s[m][r] = -INFINITY;
-          }
-        }
-        float mx = s[m][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[m][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        mb[m] = mx * sl2;
-        need[m] = mb[m] > mref[m] + kLazyLog2;
-        any |= need[m];
-      }
-
-      // ---- lazy rescale: only when some row's max outgrew its reference ----
-      if (__builtin_amdgcn_ballot_w64(any)) {
-#pragma unroll
-        for (int m = 0; m < MPW; ++m) {
-          const float al = need[m] ? exp2f(mref[m] - mb[m]) : 1.f;
-          if (need[m]) mref[m] = mb[m];
-          lsum[m] *= al;
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[m][cb][r] *= al;
-        }
-      }
-
-      // ---- probabilities -> bf16 B operand of O^T = V^T P^T ----
-      bf16x8 pk[MPW][2];
-#pragma unroll
-      for (int m = 0; m < MPW; ++m) {
-        f32x8 p0, p1;
-        float acc = 0.f;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          p0[r] = __builtin_amdgcn_exp2f(fmaf(s[m][r], sl2, -mref[m]));
-          p1[r] = __builtin_amdgcn_exp2f(fmaf(s[m][r + 8], sl2, -mref[m]));
-          acc += p0[r] + p1[r];
-        }
-        lsum[m] += acc;
-        pk[m][0] = cvt_bf16x8(p0);
-        pk[m][1] = cvt_bf16x8(p1);
-      }
-
-      // ---- O^T[c][i] += V^T[c][j] P^T[j][i] ----
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const unsigned char* p = vt + (sb * 32 + 16 * kk) * (DV * 2) + cb * 64 + voff[cb % NV];
-          const bf16x8 va = join_bf16x8(tr_read(p), tr_read(p + 8 * (DV * 2)));
-#pragma unroll
-          for (int m = 0; m < MPW; ++m) o[m][cb] = mfma32x32x16(va, pk[m][kk], o[m][cb]);
-        }
-      }
-    });
+    }
   }
 
   // ---- epilogue ----------------------------------------------------------------
@@ -484,10 +590,10 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW>::MIN_BLOCKS)
   }
 }
 
-template <int D, int DV, bool V2, int NW, int MPW>
+template <int D, int DV, bool V2, int NW, int MPW, bool PIPE>
 hipError_t launch(const PrefillArgs& a, hipStream_t s) {
   const void* args[] = {&a};
-  return hipLaunchKernel((const void*)prefill_kernel<D, DV, V2, NW, MPW>, dim3(a.nwg), dim3(NW * 64),
+  return hipLaunchKernel((const void*)prefill_kernel<D, DV, V2, NW, MPW, PIPE>, dim3(a.nwg), dim3(NW * 64),
                          (void**)args, 0, s);
 }
 
@@ -509,6 +615,12 @@ hipError_t launch(const PrefillArgs& a, hipStream_t s) {
 #ifndef DA_V2_NW
 #define DA_V2_NW 8
 #endif
+#ifndef DA_V1_D64_PIPE
+#define DA_V1_D64_PIPE false
+#endif
+#ifndef DA_V2_PIPE
+#define DA_V2_PIPE false
+#endif
 
 hipError_t launch_prefill_v1_bf16(int d, const PrefillArgs& a0, hipStream_t s) {
   PrefillArgs a = a0;
@@ -520,11 +632,11 @@ hipError_t launch_prefill_v1_bf16(int d, const PrefillArgs& a0, hipStream_t s) {
   };
   if (d == 64) {
     geom(DA_V1_D64_NW, DA_V1_D64_MPW);
-    return launch<64, 128, false, DA_V1_D64_NW, DA_V1_D64_MPW>(a, s);
+    return launch<64, 128, false, DA_V1_D64_NW, DA_V1_D64_MPW, DA_V1_D64_PIPE>(a, s);
   }
   if (d == 128) {
     geom(4 * (3 - DA_V1_D128_MPW), DA_V1_D128_MPW);
-    return launch<128, 256, false, 4 * (3 - DA_V1_D128_MPW), DA_V1_D128_MPW>(a, s);
+    return launch<128, 256, false, 4 * (3 - DA_V1_D128_MPW), DA_V1_D128_MPW, false>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -539,8 +651,8 @@ hipError_t launch_prefill_v2_bf16(int d, const PrefillArgs& a0, hipStream_t s) {
   a.tiles = (a.T + BMT - 1) / BMT;
   a.units_per_b = a.H * (np / a.pc);
   a.nwg = a.B * a.units_per_b * a.tiles;
-  if (d == 64) return launch<64, 64, true, DA_V2_NW, DA_V2_MPW>(a, s);
-  if (d == 128) return launch<128, 128, true, DA_V2_NW, DA_V2_MPW>(a, s);
+  if (d == 64) return launch<64, 64, true, DA_V2_NW, DA_V2_MPW, DA_V2_PIPE>(a, s);
+  if (d == 128) return launch<128, 128, true, DA_V2_NW, DA_V2_MPW, DA_V2_PIPE>(a, s);
   return hipErrorInvalidValue;
 }
 
