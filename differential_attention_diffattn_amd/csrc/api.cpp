@@ -56,6 +56,10 @@ da_status launch_status(hipError_t e) { return e == hipSuccess ? DA_OK : DA_E_LA
 // Largest grid the launchers build, for the overflow check.
 bool grid_fits(long long n) { return n >= 1 && n <= 0x7fffffffLL; }
 
+// The prefill kernels address a 128-key tile with 32-bit byte offsets from a
+// per-tile base, which bounds the key/value token stride.
+constexpr int64_t kMaxTokenStride = int64_t(1) << 24;  // elements
+
 da_status validate_v2_common(da_dtype dtype, int B, int T, int Hq, int Hkv, int d) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1) return DA_E_SHAPE;
@@ -102,6 +106,8 @@ da_status diffattn_v1_fwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, 
     return DA_E_LAYOUT;
   if (dtype == DA_BF16 && d != 64 && d != 128) return DA_E_UNSUPPORTED;
   if (dtype == DA_FP32 && d != 32 && d != 64 && d != 128) return DA_E_UNSUPPORTED;
+  if (dtype == DA_BF16 && (k1.st >= kMaxTokenStride || k2.st >= kMaxTokenStride || v.st >= kMaxTokenStride))
+    return DA_E_UNSUPPORTED;
   if (!grid_fits((long long)B * H * ((T + 31) / 32))) return DA_E_SHAPE;
 
   const float li = (float)diffattn_lambda_init(layer_index);
@@ -138,6 +144,7 @@ da_status diffattn_v2_fwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, 
   DA_TRY(check_logits(lam));
   DA_TRY(check_out(out, mult));
   DA_TRY(validate_v2_common(dtype, B, T, Hq, Hkv, d));
+  if (k.st >= kMaxTokenStride || v.st >= kMaxTokenStride) return DA_E_UNSUPPORTED;
   if (!grid_fits((long long)B * (Hq / 2) * ((T + 31) / 32))) return DA_E_SHAPE;
 
   da::PrefillArgs a{};

@@ -73,6 +73,15 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
                : "memory");
 }
 
+// Same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit
+// byte offset (the global_load "saddr" form): no per-lane address arithmetic.
+__device__ __forceinline__ void dma16_sbase(const void* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+
 // LDS transpose read: in each group of 16 lanes, lane j receives element
 // (j & 3) of the 4-element rows addressed by lanes 4k + (j >> 2), k = 0..3.
 __device__ __forceinline__ uint2 tr_read(const unsigned char* p) {
@@ -233,30 +242,49 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
 
   // ---- tile DMA: wave issues CPW 1 KB chunks; rows >= T are clamped to T-1
   // (finite data; those keys are always masked for every valid query) ----
+  // Each wave copies CPW 1 KB chunks per tile.  A chunk slot always covers the
+  // same (tensor, rows, swizzled columns) relative to the tile start, so the
+  // lane's byte offset is computed once; per tile only the scalar base moves.
+  // Rows >= T (last tile only) are clamped to T-1: finite data for keys that
+  // every valid query masks.
+  uint32_t dma_off[C::CPW];
+#pragma unroll
+  for (int i = 0; i < C::CPW; ++i) {
+    const int ci = wave + NW * i;  // chunk of the stage (wave-uniform)
+    if (ci < C::NK * C::KCH) {
+      const int n = ci / C::KCH, cix = ci % C::KCH;
+      const int pos = cix * 64 + lane;  // 16 B chunk index inside the K tile
+      const int r = pos / (D / 8), sc = pos % (D / 8);
+      dma_off[i] = (uint32_t)((r * (n ? kst[1] : kst[0]) + (sc ^ k_swizzle<D>(r)) * 8) * 2);
+    } else {
+      const int cix = ci - C::NK * C::KCH;
+      const int pos = cix * 64 + lane;
+      const int r = pos / (DV / 8), sc = pos % (DV / 8);
+      dma_off[i] = (uint32_t)((r * vst + (sc ^ v_swizzle<DV>(r)) * 8) * 2);
+    }
+  }
   auto issue_tile = [&](int kt, int stage) {
     const int j0 = kt * kBN;
     const uint32_t sbase = smem_lds + stage * C::STAGE;
+    const bool tail = j0 + kBN > T;  // uniform: rows past the end need clamping
 #pragma unroll
     for (int i = 0; i < C::CPW; ++i) {
-      const int ci = wave + NW * i;  // chunk of this stage (wave-uniform)
-      const uint16_t* g;
-      uint32_t dst;
-      if (ci < C::NK * C::KCH) {
-        const int n = ci / C::KCH, cix = ci % C::KCH;
-        const int pos = cix * 64 + lane;  // 16 B chunk index inside the K tile
-        const int r = pos / (D / 8), sc = pos % (D / 8);
-        const int c = sc ^ k_swizzle<D>(r);
-        g = (n ? kp[1] : kp[0]) + (int64_t)min(j0 + r, T - 1) * (n ? kst[1] : kst[0]) + c * 8;
-        dst = sbase + n * C::K_BYTES + cix * 1024;
+      const int ci = wave + NW * i;
+      const bool isk = ci < C::NK * C::KCH;
+      const int n = isk ? ci / C::KCH : 0;
+      const int cix = isk ? ci % C::KCH : ci - C::NK * C::KCH;
+      const uint16_t* tp = isk ? (n ? kp[1] : kp[0]) : vp;
+      const int64_t tst = isk ? (n ? kst[1] : kst[0]) : vst;
+      const uint32_t dst = sbase + (isk ? n * C::K_BYTES : C::NK * C::K_BYTES) + cix * 1024;
+      if (!tail) {
+        dma16_sbase(tp + (int64_t)j0 * tst, dma_off[i], dst);
       } else {
-        const int cix = ci - C::NK * C::KCH;
+        const int cols = isk ? D / 8 : DV / 8;
         const int pos = cix * 64 + lane;
-        const int r = pos / (DV / 8), sc = pos % (DV / 8);
-        const int c = sc ^ v_swizzle<DV>(r);
-        g = vp + (int64_t)min(j0 + r, T - 1) * vst + c * 8;
-        dst = sbase + C::NK * C::K_BYTES + cix * 1024;
+        const int r = pos / cols, sc = pos % cols;
+        const int c = sc ^ (isk ? k_swizzle<D>(r) : v_swizzle<DV>(r));
+        dma16(tp + (int64_t)min(j0 + r, T - 1) * tst + c * 8, dst);
       }
-      dma16(g, dst);
     }
   };
 

@@ -87,6 +87,7 @@ def test_v1_validation(lib):
     assert _v1(lib, d=96) == E_UNSUP                        # bf16 d in {64, 128}
     assert _v1(lib, dtype=0, d=16) == E_UNSUP               # fp32 d in {32, 64, 128}
     assert _v1(lib, dtype=0, v=_t(st=66)) == E_LAYOUT       # fp32: multiples of 4
+    assert _v1(lib, v=_t(st=1 << 24)) == E_UNSUP            # token stride beyond 32-bit tile offsets
 
 
 def _v2(lib, dtype=1, B=1, T=16, Hq=8, Hkv=2, d=128, lam=None, q=None):
