@@ -57,27 +57,53 @@ def _caller(w, x, binding, torch):
     return lambda layer: binding.v2_decode(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws)
 
 
-def _timed(torch, call, layers, steps, warmup):
+def _timed(torch, call, layers, steps, warmup, graph=True):
     """Run `warmup` untimed steps, then exactly `steps` timed steps (one step
-    = one call per layer).  Returns (elapsed_s, per-launch ms list)."""
-    for _ in range(warmup):
-        for l in layers:
-            call(l)
+    = one call per layer).  With `graph`, one step (its len(layers) calls) is
+    captured once as a HIP graph and each step is a replay, so host launch
+    overhead does not gap the GPU.  Returns (elapsed_s, per-call ms list) where
+    a call's time is its step's event-timed duration / calls per step (graph)
+    or the events around that one call (eager)."""
+    for l in layers:  # eager first: any lazy initialisation happens outside capture
+        call(l)
     torch.cuda.synchronize()
-    n = steps * len(layers)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in layers:
+                call(l)
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        if g is not None:
+            g.replay()
+        else:
+            for l in layers:
+                call(l)
+    torch.cuda.synchronize()
+    per = 1 if g is not None else len(layers)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps * per)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     k = 0
     for _ in range(steps):
-        for l in layers:
+        if g is not None:
             ev[k][0].record()
-            call(l)
+            g.replay()
             ev[k][1].record()
             k += 1
+        else:
+            for l in layers:
+                ev[k][0].record()
+                call(l)
+                ev[k][1].record()
+                k += 1
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    return elapsed, [a.elapsed_time(b) for a, b in ev]
+    ms = [a.elapsed_time(b) for a, b in ev]
+    if g is not None:
+        ms = [m / len(layers) for m in ms for _ in range(len(layers))]
+    return elapsed, ms
 
 
 def _roofline(w, launch_ms):
@@ -240,6 +266,8 @@ def main():
                     help="time a single workload by name, or 'copy' for the 1 GiB copy calibration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of replaying "
+                    "a captured HIP graph of one step")
     ap.add_argument("--summarize", default=None, metavar="DIR",
                     help="summarise rocprofv3 CSV output in DIR (kernels matching --kernel) and exit")
     ap.add_argument("--kernel", default="", help="kernel-name substring for --summarize")
@@ -274,11 +302,12 @@ def main():
         x = workloads.inputs_for(w, dev)
         call = _caller(w, x, binding, torch)
         layers = list(w.layers) if w.layers else [0]
-        elapsed, launch_ms = _timed(torch, call, layers, steps, warmup)
+        elapsed, launch_ms = _timed(torch, call, layers, steps, warmup, graph=not args.eager)
         per_call_s = elapsed / (steps * len(layers))
         roof = _roofline(w, launch_ms)
         roof["traffic"] = _traffic(w)
         res = {"workload": name, "steps": steps, "warmup": warmup, "calls_per_step": len(layers),
+               "launch": "eager" if args.eager else "hip_graph",
                "ms_per_step": round(elapsed / steps * 1e3, 5), "roofline": roof}
         if w.kind == "decode":
             res.update(metric="V2 decode HBM GB/s", unit="GB/s",

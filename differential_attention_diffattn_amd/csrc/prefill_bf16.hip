@@ -51,6 +51,9 @@ constexpr float kLazyLog2 = 8.f;  // rescale only when the max grows by > 2^8
 #ifndef DA_V2_BN
 #define DA_V2_BN 128  // keys per LDS stage of the V2 kernel (64 or 128)
 #endif
+#ifndef DA_TILE_SOFTMAX
+#define DA_TILE_SOFTMAX 0  // one max/rescale decision per two visible sub-blocks (slower on MI355X)
+#endif
 #ifndef DA_SETPRIO
 #define DA_SETPRIO 1  // raise wave priority while issuing MFMA sections
 #endif
@@ -135,6 +138,8 @@ struct Cfg {
   static constexpr int XBYTES = MPW == 1 ? (NW / 2) * CB * 16 * 64 * 4 : 0;
   static constexpr int SMEM = NST * STAGE > XBYTES ? NST * STAGE : XBYTES;
   static constexpr int MIN_BLOCKS = NW == 4 ? 2 : 1;  // two waves per SIMD
+  // sub-blocks per softmax group (registers permitting: two score tiles per wave)
+  static constexpr int SMG = (DA_TILE_SOFTMAX && !PIPE && DV <= 128 && BN >= 64) ? 2 : 1;
 };
 
 template <int MPW>
@@ -466,13 +471,58 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
       if (kt + 1 < nkt) issue_tile(kt + 1, (kt + 1) & 1);
       if (!active) continue;
       const unsigned char* st = smem + (kt & 1) * C::STAGE;
+      constexpr int NSB = kBN / 32;
+      constexpr int GS = C::SMG;  // sub-blocks sharing one max / rescale decision
 #pragma unroll
-      for (int sb = 0; sb < kBN / 32; ++sb) {
-        const int jb = kt * kBN + 32 * sb;
-        if (jb > i0w) break;  // sub-block entirely above this wave's diagonal
-        Scores<MPW> S = qk(st, 32 * sb);
-        if (__builtin_amdgcn_ballot_w64(softmax_head(S, jb == i0w))) rescale();
-        pv(st, 32 * sb, softmax_exp(S));
+      for (int g0 = 0; g0 < NSB; g0 += GS) {
+        if (kt * kBN + 32 * g0 > i0w) break;  // group entirely above this wave's diagonal
+        if (GS > 1 && kt * kBN + 32 * (g0 + GS - 1) <= i0w) {
+          // The whole group is visible: its score MFMAs back to back, one max /
+          // rescale decision, then the exponentials of sub-block s+1 alongside
+          // the P.V MFMAs of sub-block s.
+          Scores<MPW> S[GS];
+#pragma unroll
+          for (int j = 0; j < GS; ++j) S[j] = qk(st, 32 * (g0 + j));
+          const bool diag_last = kt * kBN + 32 * (g0 + GS - 1) == i0w;
+          bool any = false;
+#pragma unroll
+          for (int m = 0; m < MPW; ++m) {
+            if (diag_last) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int key = 8 * (r >> 2) + 4 * hg + (r & 3);
+                if (key > li) S[GS - 1].s[m][r] = -INFINITY;
+              }
+            }
+            float mx = S[0].s[m][0];
+#pragma unroll
+            for (int j = 0; j < GS; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[j].s[m][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            mb[m] = mx * sl2;
+            need[m] = mb[m] > mref[m] + kLazyLog2;
+            any |= need[m];
+          }
+          if (__builtin_amdgcn_ballot_w64(any)) rescale();
+          Probs<MPW> P = softmax_exp(S[0]);
+#pragma unroll
+          for (int j = 0; j < GS; ++j) {
+            Probs<MPW> Pn;
+            if (j + 1 < GS) Pn = softmax_exp(S[j + 1]);
+            pv(st, 32 * (g0 + j), P);
+            if (j + 1 < GS) P = Pn;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < GS; ++j) {
+            const int jb = kt * kBN + 32 * (g0 + j);
+            if (jb > i0w) break;  // sub-block entirely above this wave's diagonal
+            Scores<MPW> S = qk(st, 32 * (g0 + j));
+            if (__builtin_amdgcn_ballot_w64(softmax_head(S, jb == i0w))) rescale();
+            pv(st, 32 * (g0 + j), softmax_exp(S));
+          }
+        }
       }
     }
   } else {

@@ -308,3 +308,42 @@ def test_decode_prefix_mean_closed_form_full_size():
     assert_bf16_close(out, ref, "decode mean")
     del z
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ HIP graphs
+
+def test_graph_replay_matches_eager():
+    """The benchmark replays one step captured as a HIP graph (12 V1 layer
+    calls, a V2 prefill and a decode).  Every replay, with eager work and a
+    clearing of the outputs in between, must equal the eager results bit for
+    bit."""
+    w = WORKLOADS["v1_gpt2small_B8_H6_T1024_d64"]
+    x = workloads.inputs_for(w, DEV)
+    y = workloads.v2_inputs(1, 300, 16, 2, 128, torch.bfloat16, seed=41, device=DEV)
+    z = workloads.decode_inputs(4, 3000, 16, 2, 128, torch.bfloat16, seed=42, device=DEV)
+    outs = [torch.empty((w.B, w.T, w.H, 2 * w.d), device=DEV, dtype=torch.bfloat16) for _ in w.layers]
+    out2 = torch.empty((1, 300, 8, 128), device=DEV, dtype=torch.bfloat16)
+    out3 = torch.empty((4, 8, 128), device=DEV, dtype=torch.bfloat16)
+    ws = torch.empty(binding.v2_decode_workspace_bytes(4, 3000, 16, 2, 128), device=DEV, dtype=torch.uint8)
+
+    def step():
+        for layer, o in zip(w.layers, outs):
+            binding.v1_fwd(*[x[n] for n in V1_NAMES], layer, out=o)
+        binding.v2_fwd(y["q"], y["k"], y["v"], y["lam"], out=out2)
+        binding.v2_decode(z["q"], z["k"], z["v"], z["lam"], out=out3, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs] + [out2.clone(), out3.clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs + [out2, out3]:
+            o.zero_()
+        _v1_run(workloads.v1_inputs(1, 2, 64, 64, torch.bfloat16, seed=rep, device=DEV), rep)  # eager work
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs + [out2, out3], ref):
+            assert torch.equal(got, want), f"replay {rep} differs"
