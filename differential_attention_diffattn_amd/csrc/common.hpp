@@ -99,6 +99,15 @@ __device__ __forceinline__ float sigmoid_f32(float x) {
   return e / (1.f + e);
 }
 
+// max(x[l % 32], x[l % 32 + 32]) in every lane l, without an LDS round trip:
+// v_permlane32_swap exchanges the upper half of one copy of x with the lower
+// half of another, leaving each lane with x of both lane halves.
+__device__ __forceinline__ float max_across_halves(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -407,7 +407,7 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
       float mx = S.s[m][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S.s[m][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = max_across_halves(mx);
       mb[m] = mx * sl2;
       need[m] = mb[m] > mref[m] + kLazyLog2;
       any |= need[m];
@@ -499,7 +499,7 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
             for (int j = 0; j < GS; ++j)
 #pragma unroll
               for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[j].s[m][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            mx = max_across_halves(mx);
             mb[m] = mx * sl2;
             need[m] = mb[m] > mref[m] + kLazyLog2;
             any |= need[m];
