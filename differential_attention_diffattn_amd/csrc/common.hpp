@@ -101,11 +101,15 @@ __device__ __forceinline__ float sigmoid_f32(float x) {
 
 // max(x[l % 32], x[l % 32 + 32]) in every lane l, without an LDS round trip:
 // v_permlane32_swap exchanges the upper half of one copy of x with the lower
-// half of another, leaving each lane with x of both lane halves.
+// half of another, leaving each lane with x of both lane halves.  Written as
+// inline asm: with both operands equal, the compiler's model of the builtin
+// folds the two results into one and drops the upper half.  The s_nop covers
+// the VALU-write -> permlane-read hazards on both sides of the swap.
 __device__ __forceinline__ float max_across_halves(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
+               : "+v"(a), "+v"(b));
+  return a;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -66,6 +66,26 @@ def test_v1_bf16_ragged(d, T):
     assert_bf16_close(out, oracle.v1_fwd(*_v1_cpu(x), 4), f"bf16 d{d} T{T}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_v1_bf16_peaked_scores(d):
+    """Scores spread over hundreds of log2 units: every row's maximum must be
+    taken over all of its keys (both lane halves of a score tile), or the
+    exponentials overflow."""
+    x = workloads.v1_inputs(2, 3, 300, d, torch.bfloat16, seed=250 + d, device=DEV)
+    for n in ("q1", "q2", "k1", "k2"):
+        x[n].mul_(6)
+    out = _v1_run(x, 2)
+    assert_bf16_close(out, oracle.v1_fwd(*_v1_cpu(x), 2), f"peaked d{d}")
+
+
+def test_v1_fp32_peaked_scores():
+    x = workloads.v1_inputs(1, 2, 200, 64, torch.float32, seed=260, device=DEV)
+    for n in ("q1", "q2", "k1", "k2"):
+        x[n].mul_(6)
+    out = _v1_run(x, 2)
+    assert_fp32_close(out, oracle.v1_fwd(*_v1_cpu(x), 2), "fp32 peaked")
+
+
 def test_v1_bf16_gpt2small_full():
     """GPT-2-small shape, every element of layer 0, then sampled rows of
     every layer of the 0..11 sweep (only lambda_init changes)."""
@@ -207,6 +227,15 @@ def test_v2_ragged(G, d, T):
     assert_bf16_close(out, oracle.v2_fwd(*_v2_cpu(y)), f"v2 G{G} d{d} T{T}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_v2_peaked_scores(d):
+    y = workloads.v2_inputs(1, 300, 8, 1, d, torch.bfloat16, seed=350 + d, device=DEV)
+    y["q"].mul_(6)
+    y["k"].mul_(6)
+    out = _v2_run(y)
+    assert_bf16_close(out, oracle.v2_fwd(*_v2_cpu(y)), f"v2 peaked d{d}")
+
+
 def test_v2_gate_limits():
     """Logits -inf / +inf give sigmoid 0 / 1 exactly."""
     y = workloads.v2_inputs(1, 80, 8, 1, 128, torch.bfloat16, seed=31, device=DEV)
@@ -264,6 +293,15 @@ def test_decode_ragged(L, G, d):
     z = workloads.decode_inputs(3, L, G * Hkv, Hkv, d, torch.bfloat16, seed=400 + L + G + d, device=DEV)
     out = _dec_run(z)
     assert_bf16_close(out, oracle.v2_decode(*_dec_cpu(z)), f"decode L{L} G{G} d{d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_peaked_scores(d):
+    z = workloads.decode_inputs(2, 1000, 16, 2, d, torch.bfloat16, seed=450 + d, device=DEV)
+    z["q"].mul_(6)
+    z["k"].mul_(6)
+    out = _dec_run(z)
+    assert_bf16_close(out, oracle.v2_decode(*_dec_cpu(z)), f"decode peaked d{d}")
 
 
 def test_decode_equals_last_prefill_row():
