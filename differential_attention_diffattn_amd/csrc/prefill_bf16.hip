@@ -13,28 +13,35 @@
 //       (no norm, no scale).
 //
 // Structure (designed for gfx950, not taken from any listing):
-//   * K and V tiles of 64 keys go HBM -> LDS with global_load_lds_dwordx4
-//     (no registers, no VALU), double-buffered: the next tile streams in
-//     while the current one is consumed; one barrier per tile.  In LDS both
-//     stay row-major with an XOR swizzle of their 16-byte chunks, so the
-//     MFMA operand reads are bank-conflict-free (256 B per clock).
+//   * A wave owns 32 query rows of ONE map (V1: map 1 or map 2 of a
+//     differential head; V2: the even or the odd head of a pair).  Partner
+//     waves (2k, 2k+1) hold the two maps of the same rows and are combined
+//     through LDS in the epilogue.  For V2 the waves of a workgroup cover the
+//     heads of one GQA group, so each K/V tile is loaded once for the group.
+//   * K and V tiles go HBM -> LDS with global_load_lds_dwordx4 (no registers,
+//     no VALU), double-buffered: the next tile streams in while the current
+//     one is consumed; one barrier per tile.  In LDS both stay row-major with
+//     an XOR swizzle of their 16-byte chunks, so the MFMA operand reads are
+//     bank-conflict-free.  The LDS holds [K stage 0 | K stage 1 | V stage 0 |
+//     V stage 1] and the key loop is unrolled by stage, so every operand
+//     read is a per-lane base register plus an immediate offset.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: Q fragments stay in registers for the whole
 //     key loop, each lane holds 16 scores of ONE query row (softmax state is
-//     per lane), and the fp32 score registers convert in place to the bf16 B
-//     operand of O^T = V^T P^T.  The V^T A operand comes straight from the
-//     row-major V tile through ds_read_b64_tr_b16 (the LDS transpose read).
-//   * Online softmax in the log2 domain with a lazily updated reference max:
-//     O and l are only rescaled when a row's max grows by more than 2^8,
-//     which keeps every exponent <= 2^8 and the result exact up to rounding.
-//   * Work split.  A wave owns 32 query rows.  MPW = 2: the wave carries
-//     both maps (V1: map 1 and map 2 of one differential head; V2: the two
-//     heads of a pair), so a V fragment read once feeds two MFMAs.  MPW = 1:
-//     the two maps of the same rows sit in two partner waves (halving the
-//     accumulator registers, so two waves fit per SIMD) and are combined
-//     through LDS at the end.  For V2 the waves of a workgroup cover the
-//     heads of one GQA group, so each K/V tile is loaded once for the whole
-//     group.
+//     per lane), and the probabilities convert in place to the bf16 B operand
+//     of O^T = V^T P^T.  The V^T A operand comes straight from the row-major
+//     V tile through ds_read_b64_tr_b16 (the LDS transpose read).
+//   * Online softmax in the log2 domain against a per-row reference m that
+//     only moves when it must.  The common path per 32-key sub-block is one
+//     fma + one exp2 per score, a bf16 conversion, and the row sum taken with
+//     v_dot2_f32_bf16 over the converted probabilities (so the sum is exactly
+//     that of the P fed to the MFMA).  No row maximum is computed there: if
+//     a lane's 16 probabilities sum past 2^10 (a score rose more than ~10
+//     log2 units above m, or m is still unset), the wave takes the exact
+//     path -- the row maximum over both lane halves, a rescale of O and l,
+//     and the sub-block's exponentials again against the new m.  Every
+//     probability fed to the MFMA is therefore <= 2^10, and the result is the
+//     same softmax up to rounding.
 //   * Causal skipping at 32-key granularity (mask only on diagonal
 //     sub-blocks); heaviest tiles first; workgroups mapped onto XCDs so the
 //     tiles of one head share an L2.
@@ -47,37 +54,36 @@
 namespace da {
 namespace {
 
-constexpr float kLazyLog2 = 8.f;  // rescale only when the max grows by > 2^8
 #ifndef DA_V2_BN
 #define DA_V2_BN 128  // keys per LDS stage of the V2 kernel (64 or 128)
 #endif
-#ifndef DA_TILE_SOFTMAX
-#define DA_TILE_SOFTMAX 0  // one max/rescale decision per two visible sub-blocks (slower on MI355X)
+#ifndef DA_NO_HINTS
+#define DA_NO_HINTS 0
 #endif
 #ifndef DA_SETPRIO
 #define DA_SETPRIO 1  // raise wave priority while issuing MFMA sections
 #endif
 
+// A lane whose 16 probabilities of a sub-block sum past this takes the exact
+// (row maximum + rescale) path.
+constexpr float kSumCap = 1024.f;
+// Reference before any key is seen: finite, so masked scores (-inf) still
+// give fma(-inf, c, kMInit) = -inf rather than NaN, and every visible score
+// overflows the cap on the first sub-block.
+constexpr float kMInit = -1e30f;
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-// 16 bytes per lane, HBM -> LDS (global_load_lds_dwordx4): lane l's bytes
-// land at LDS byte address lds_addr + 16 l; lds_addr must be wave-uniform.
-// Issued as inline asm so the compiler does not track it: it would otherwise
-// make every LDS read wait for the copy in flight, although that copy only
-// ever targets the other LDS stage.  The kernel waits for it explicitly
-// (vmcnt(0) + barrier) before the stage is read.  M0 is used by nothing else
-// in these kernels.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory");
-}
-
-// Same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit
-// byte offset (the global_load "saddr" form): no per-lane address arithmetic.
+// 16 bytes per lane, HBM -> LDS (global_load_lds_dwordx4, "saddr" form: a
+// wave-uniform 64-bit base in SGPRs plus a per-lane 32-bit byte offset):
+// lane l's bytes land at LDS byte address lds_addr + 16 l; lds_addr must be
+// wave-uniform.  Issued as inline asm so the compiler does not track it: it
+// would otherwise make every LDS read wait for the copy in flight, although
+// that copy only ever targets another LDS stage.  The kernel waits for it
+// explicitly (vmcnt(0) + barrier) before the stage is read.  M0 is used by
+// nothing else in these kernels.
 __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t off, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
@@ -87,9 +93,14 @@ __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t off, uint
 
 // LDS transpose read: in each group of 16 lanes, lane j receives element
 // (j & 3) of the 4-element rows addressed by lanes 4k + (j >> 2), k = 0..3.
-__device__ __forceinline__ uint2 tr_read(const unsigned char* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+__device__ __forceinline__ uint2 tr_read(uint32_t lds_addr) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)lds_addr);
   return __builtin_bit_cast(uint2, v);
+}
+
+// 16-byte LDS read (ds_read_b128) at an LDS byte address.
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t lds_addr) {
+  return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)lds_addr;
 }
 
 template <int I, int N, typename F>
@@ -98,6 +109,18 @@ __device__ __forceinline__ void static_for(F&& f) {
     f(std::integral_constant<int, I>{});
     static_for<I + 1, N>(f);
   }
+}
+
+// Sum of the eight bf16 values of x, accumulated onto acc in fp32
+// (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 x, float acc) {
+  const uint4 u = as_u4(x);
+  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.x), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.y), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.z), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.w), one, acc, false);
+  return acc;
 }
 
 // XOR swizzles of 16-byte chunks inside a tile row (measured conflict-free on
@@ -117,44 +140,58 @@ __device__ __forceinline__ int v_swizzle(int r) {
 
 template <int D, int DV, bool V2, int NW, int MPW, bool PIPE>
 struct Cfg {
-  static constexpr int NT = NW * 64;
   static constexpr int KS = D / 16;   // k-steps of the score MFMA
   static constexpr int CB = DV / 32;  // 32-wide column blocks of O^T
   static constexpr int NK = V2 ? 1 : 2;
-  // PIPE: 32-key tiles in a 4-stage ring (software-pipelined key loop);
-  // otherwise 64-key tiles, double-buffered.
-  static constexpr int BN = PIPE ? 32 : (V2 ? DA_V2_BN : 64);
-  static constexpr int NST = PIPE ? 4 : 2;
-  static constexpr int K_BYTES = BN * D * 2;
+  // PIPE: 64-key tiles in a 3-stage ring (software-pipelined key loop);
+  // otherwise BN-key tiles double-buffered.
+  static constexpr int NST = PIPE ? 3 : 2;
+  static constexpr int BN = PIPE ? 64 : (V2 ? DA_V2_BN : 64);  // keys per tile
+  static constexpr int NSB = BN / 32;            // 32-key sub-blocks per tile
+  static constexpr int K_BYTES = BN * D * 2;     // one K tensor of one tile
   static constexpr int V_BYTES = BN * DV * 2;
-  static constexpr int STAGE = NK * K_BYTES + V_BYTES;
-  static constexpr int KCH = K_BYTES / 1024;  // 1 KB DMA instructions per K tensor
+  static constexpr int KREG = NK * K_BYTES;      // K tensors of one stage
+  static constexpr int VBASE = NST * KREG;       // V stages follow all K stages
+  static constexpr int TILE_SMEM = NST * (KREG + V_BYTES);
+  static constexpr int KCH = K_BYTES / 1024;     // 1 KB DMA instructions per K tensor
   static constexpr int VCH = V_BYTES / 1024;
   static constexpr int NCH = NK * KCH + VCH;
-  static constexpr int CPW = NCH / NW;        // DMA instructions per wave per tile
+  static constexpr int CPW = NCH / NW;           // DMA instructions per wave per tile
   static_assert(NCH % NW == 0, "tile DMA split");
   static_assert(D >= 64 && DV >= 64, "swizzles assume >= 8 chunks per row");
-  // MPW == 1: one exchange slot per partner-wave pair (fp32, lane-native order)
+  static_assert(MPW == 1 || MPW == 2, "maps per wave");
+  static_assert(!PIPE || NSB >= 2, "the pipelined ring frees a stage one sub-block before the tile ends");
+  // Operand reads use 16-bit immediate offsets from a per-lane base.
+  static_assert((NST - 1) * KREG + (NK - 1) * K_BYTES * (MPW - 1) + (BN - 32) * D * 2 < 65536, "K read offset range");
+  static_assert((NST - 1) * V_BYTES + (BN - 8) * DV * 2 + (CB - 1) * 64 < 65536, "V read offset range");
+  // MPW == 1 epilogue: one exchange slot per partner-wave pair (fp32, lane-native order)
   static constexpr int XBYTES = MPW == 1 ? (NW / 2) * CB * 16 * 64 * 4 : 0;
-  static constexpr int SMEM = NST * STAGE > XBYTES ? NST * STAGE : XBYTES;
-  static constexpr int MIN_BLOCKS = NW == 4 ? 2 : 1;  // two waves per SIMD
-  // sub-blocks per softmax group (registers permitting: two score tiles per wave)
-  static constexpr int SMG = (DA_TILE_SOFTMAX && !PIPE && DV <= 128 && BN >= 64) ? 2 : 1;
+  static constexpr int SMEM = TILE_SMEM > XBYTES ? TILE_SMEM : XBYTES;
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  // MPW == 1 with 4 waves: two workgroups (two waves per SIMD) per CU
+  static constexpr int MIN_BLOCKS = (MPW == 1 && NW == 4) ? 2 : 1;
 };
 
+// (clang tries to constant-evaluate a lambda call whose value initialises a
+// variable or is returned, and that evaluation crashes on the vector element
+// stores inside; the score lambda therefore starts with an empty asm
+// statement, which ends any such evaluation at once.)
 template <int MPW>
 struct Scores {
   f32x16 s[MPW];
 };
 template <int MPW>
 struct Probs {
-  bf16x8 p[MPW][2];
+  bf16x8 p[MPW][2];  // bf16 B operand of P.V, two 16-key halves
+  float bs[MPW];     // this lane's sum of the block's probabilities
 };
 
 template <int D, int DV, bool V2, int NW, int MPW, bool PIPE>
 __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_BLOCKS))
     prefill_kernel(const PrefillArgs a) {
   using C = Cfg<D, DV, V2, NW, MPW, PIPE>;
+  using Sc = Scores<MPW>;
+  using Pr = Probs<MPW>;
   constexpr int kBN = C::BN;
   constexpr int KS = C::KS, CB = C::CB;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::SMEM];
@@ -186,24 +223,23 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
   const int u = unit % a.units_per_b;
   const int T = a.T;
 
-  // ---- roles: which rows and maps this wave owns ----------------------------
-  int RB, rb, m0 = 0, h = 0, pair = 0;
-  const uint16_t* qp[2];
-  int64_t qst[2];
+  // ---- roles: which rows and which maps this wave owns ----------------------
+  // MPW == 2: the wave holds both maps (V1) / both heads of a pair (V2).
+  // MPW == 1: waves 2k (map 1 / even head) and 2k+1 (map 2 / odd head) are
+  // partners holding the two maps of the same rows.
+  constexpr int WPU = 2 / MPW;           // waves per (rows, map pair) unit
+  const int m0 = MPW == 1 ? wave & 1 : 0;  // first map of this wave
+  const int slot = wave / WPU;           // (rows, map pair) unit of the workgroup
+  int rb, h = 0, pair = 0;
+  const uint16_t* qp[MPW];
+  int64_t qst[MPW];
   const uint16_t* kp[2];
   int64_t kst[2];
   const uint16_t* vp;
   int64_t vst;
   if constexpr (!V2) {
     h = u;
-    if constexpr (MPW == 2) {
-      RB = NW;
-      rb = wave;
-    } else {
-      RB = NW / 2;
-      rb = wave >> 1;
-      m0 = wave & 1;  // this wave's map
-    }
+    rb = slot;
 #pragma unroll
     for (int m = 0; m < MPW; ++m) {  // selects, not an indexed array: keeps args out of scratch
       const bool second = m0 + m == 1;
@@ -218,24 +254,22 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
     vp = (const uint16_t*)a.v.p + b * a.v.sb + h * a.v.sh;
     vst = a.v.st;
   } else {
+    // unit slot -> pair slot % pc of this chunk of the group, row block slot / pc
     const int npc = (a.G / 2) / a.pc;  // pair chunks per group
     const int g = u / npc, pcix = u % npc;
-    // MPW == 2: wave w -> pair w % pc, row block w / pc.
-    // MPW == 1: waves 2k (even head) and 2k+1 (odd head) share pair k % pc and
-    //           row block k / pc.
-    const int pw = MPW == 2 ? wave : wave >> 1;
-    if constexpr (MPW == 1) m0 = wave & 1;
-    RB = (MPW == 2 ? NW : NW / 2) / a.pc;
-    rb = pw / a.pc;
-    pair = g * (a.G / 2) + pcix * a.pc + pw % a.pc;
+    rb = slot / a.pc;
+    pair = g * (a.G / 2) + pcix * a.pc + slot % a.pc;
 #pragma unroll
-    for (int m = 0; m < MPW; ++m) qp[m] = (const uint16_t*)a.q1.p + b * a.q1.sb + (2 * pair + m0 + m) * a.q1.sh;
-    qst[0] = qst[1] = a.q1.st;
+    for (int m = 0; m < MPW; ++m) {
+      qp[m] = (const uint16_t*)a.q1.p + b * a.q1.sb + (2 * pair + m0 + m) * a.q1.sh;
+      qst[m] = a.q1.st;
+    }
     kp[0] = kp[1] = (const uint16_t*)a.k1.p + b * a.k1.sb + g * a.k1.sh;
     kst[0] = kst[1] = a.k1.st;
     vp = (const uint16_t*)a.v.p + b * a.v.sb + g * a.v.sh;
     vst = a.v.st;
   }
+  const int RB = V2 ? (NW / WPU) / a.pc : NW / WPU;  // row blocks per workgroup
   const int BMT = 32 * RB;
   const int I0 = tile * BMT;
   const int i0w = I0 + 32 * rb;
@@ -245,8 +279,7 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
 
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
-  // ---- tile DMA: wave issues CPW 1 KB chunks; rows >= T are clamped to T-1
-  // (finite data; those keys are always masked for every valid query) ----
+  // ---- tile DMA ----------------------------------------------------------------
   // Each wave copies CPW 1 KB chunks per tile.  A chunk slot always covers the
   // same (tensor, rows, swizzled columns) relative to the tile start, so the
   // lane's byte offset is computed once; per tile only the scalar base moves.
@@ -268,9 +301,9 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
       dma_off[i] = (uint32_t)((r * vst + (sc ^ v_swizzle<DV>(r)) * 8) * 2);
     }
   }
-  auto issue_tile = [&](int kt, int stage) {
+  auto issue_tile = [&](int kt, auto stage_c) {
+    constexpr int S = decltype(stage_c)::value;
     const int j0 = kt * kBN;
-    const uint32_t sbase = smem_lds + stage * C::STAGE;
     const bool tail = j0 + kBN > T;  // uniform: rows past the end need clamping
 #pragma unroll
     for (int i = 0; i < C::CPW; ++i) {
@@ -280,16 +313,16 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
       const int cix = isk ? ci % C::KCH : ci - C::NK * C::KCH;
       const uint16_t* tp = isk ? (n ? kp[1] : kp[0]) : vp;
       const int64_t tst = isk ? (n ? kst[1] : kst[0]) : vst;
-      const uint32_t dst = sbase + (isk ? n * C::K_BYTES : C::NK * C::K_BYTES) + cix * 1024;
-      if (!tail) {
-        dma16_sbase(tp + (int64_t)j0 * tst, dma_off[i], dst);
-      } else {
+      const uint32_t dst = smem_lds + (isk ? S * C::KREG + n * C::K_BYTES : C::VBASE + S * C::V_BYTES) + cix * 1024;
+      uint32_t off = dma_off[i];
+      if (tail) {  // same chunk, row clamped to T-1 (offsets < 2^31: token stride < 2^24)
         const int cols = isk ? D / 8 : DV / 8;
         const int pos = cix * 64 + lane;
         const int r = pos / cols, sc = pos % cols;
         const int c = sc ^ (isk ? k_swizzle<D>(r) : v_swizzle<DV>(r));
-        dma16(tp + (int64_t)min(j0 + r, T - 1) * tst + c * 8, dst);
+        off = ((uint32_t)min(r, T - 1 - j0) * (uint32_t)tst + (uint32_t)(c * 8)) * 2u;
       }
+      dma16_sbase(tp + (int64_t)j0 * tst, off, dst);
     }
   };
 
@@ -304,34 +337,41 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
         qf[m][ks] = as_bf16x8(row < T ? *(const uint4*)(qp[m] + (int64_t)row * qst[m] + 16 * ks + 8 * hg)
                                       : make_uint4(0, 0, 0, 0));
   }
-
   // Retire the Q loads here.  The compiler cannot see the tile DMA, but the
   // hardware counter counts it: a compiler-placed vmcnt wait for Q inside the
   // key loop would also wait for the next tile's copy.
 #pragma unroll
   for (int m = 0; m < MPW; ++m)
 #pragma unroll
-    for (int ks = 0; ks < KS; ks += 2)
-      asm volatile("s_waitcnt vmcnt(0)" : "+v"(qf[m][ks]), "+v"(qf[m][ks + 1]));
+    for (int ks = 0; ks < KS; ks += 2) asm volatile("s_waitcnt vmcnt(0)" : "+v"(qf[m][ks]), "+v"(qf[m][ks + 1]));
 
-  // ---- per-lane LDS offsets ----
-  // K chunk (2ks + hg) of tile row r = 32 sb + li sits at chunk (2ks + hg) ^ k_swizzle(li).
-  int koff[KS];
+  // ---- per-lane LDS bases (every stage / sub-block / map offset is an immediate) ----
+  // K chunk (2ks + hg) of tile row r = 32 sb + li sits at chunk (2ks + hg) ^ k_swizzle(li)
+  // of the map's K tensor (V1: K2 follows K1 in a stage).
+  uint32_t kbase[KS];  // LDS byte addresses
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = li * (D * 2) + (((2 * ks + hg) ^ k_swizzle<D>(li)) << 4);
+  for (int ks = 0; ks < KS; ++ks)
+    kbase[ks] = smem_lds + (V2 ? 0 : m0 * C::K_BYTES) + li * (D * 2) + (((2 * ks + hg) ^ k_swizzle<D>(li)) << 4);
+  // Opaque to the compiler: it would otherwise rebuild each base from shared
+  // parts inside the key loop (one VALU add per operand read).
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(kbase[ks]));
   // V^T operand via transpose reads: lane (G16 = lane>>4, l16 = lane&15) points at
   // row 4*(G16>>1) + (l16>>2) (+ sub-block, k-step), columns 32cb + 16(G16&1) + 4(l16&3),
   // i.e. chunk 4cb + cl.  The swizzle only permutes chunks within aligned groups of
   // 4*NV, so the per-lane offset depends on cb only through cb % NV.
   constexpr int NV = DV >= 128 ? 4 : 2;
-  int voff[NV];
+  uint32_t vbase[NV];
   {
     const int l16 = lane & 15, g16 = lane >> 4;
     const int vr = 4 * (g16 >> 1) + (l16 >> 2);
     const int cl = 2 * (g16 & 1) + ((l16 & 3) >> 1);
     const int x = v_swizzle<DV>(vr);  // rows of one read share r & 3 = l16 >> 2
 #pragma unroll
-    for (int v = 0; v < NV; ++v) voff[v] = vr * (DV * 2) + (((4 * v + cl) ^ x) - 4 * v) * 16 + (l16 & 1) * 8;
+    for (int v = 0; v < NV; ++v)
+      vbase[v] = smem_lds + C::VBASE + vr * (DV * 2) + (((4 * v + cl) ^ x) - 4 * v) * 16 + (l16 & 1) * 8;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) asm volatile("" : "+v"(vbase[v]));
   }
 
   // ---- V1 lambda (one fp32 scalar per call) ----
@@ -347,237 +387,251 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
     lam = expf(pa) - expf(pb) + a.lam_init;
   }
 
+  if constexpr (MPW == 2) {
+    // With two maps per wave the working set exceeds 256 VGPRs.  An inline
+    // asm operand in an AGPR makes the backend select the MFMA forms whose
+    // accumulators live in AGPRs (O stays there between MFMAs) instead of
+    // VGPR forms with AGPRs used as spill space.
+    asm volatile("" ::"a"(0.f));
+  }
   const float sl2 = a.sl2;
-  float mref[MPW], lsum[MPW];
+  float nm[MPW], lsum[MPW];  // minus the reference m of this lane's row (log2 units); row sum
   f32x16 o[MPW][CB];
 #pragma unroll
   for (int m = 0; m < MPW; ++m) {
-    mref[m] = -INFINITY;
+    nm[m] = -kMInit;
     lsum[m] = 0.f;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[m][cb][r] = 0.f;
   }
-  // K tensor of each map inside a stage
-  int kbyte[MPW];
-#pragma unroll
-  for (int m = 0; m < MPW; ++m) kbyte[m] = V2 ? 0 : (m0 + m) * C::K_BYTES;
 
-  // ---- the arithmetic of one 32-key sub-block, shared by both loop forms ----
-  // scores S^T[j][i] (32 keys x 32 rows per map) from K rows row0.. of a stage
-  auto qk = [&](const unsigned char* st, int row0) {
-    Scores<MPW> r;
+  // ---- building blocks of one 32-key sub-block --------------------------------
+  // (s_setprio around the MFMA sections only in the unpipelined loop: it
+  // bounds the compiler's scheduling regions.)
+  constexpr bool kPrio = DA_SETPRIO && !PIPE;
+  // S^T (32 keys x 32 rows per map) of the sub-block at K offset KO.  V2: one
+  // K fragment feeds every map of the wave.
+  auto qk = [&](auto koffc) {
+    constexpr int KO = decltype(koffc)::value;
+    asm volatile("");  // not a constant expression (see the note above Scores)
+    Sc r;
 #pragma unroll
     for (int m = 0; m < MPW; ++m)
 #pragma unroll
       for (int i = 0; i < 16; ++i) r.s[m][i] = 0.f;
-    const unsigned char* kr = st + row0 * (D * 2);
-    if (DA_SETPRIO) __builtin_amdgcn_s_setprio(2);
+    if (kPrio) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if constexpr (V2) {  // one K fragment feeds every map of the wave
-        const bf16x8 ka = *(const bf16x8*)(kr + koff[ks]);
+      if constexpr (V2) {
+        const bf16x8 ka = lds_read16(kbase[ks] + KO);
 #pragma unroll
         for (int m = 0; m < MPW; ++m) r.s[m] = mfma32x32x16(ka, qf[m][ks], r.s[m]);
       } else {
 #pragma unroll
         for (int m = 0; m < MPW; ++m)
-          r.s[m] = mfma32x32x16(*(const bf16x8*)(kr + kbyte[m] + koff[ks]), qf[m][ks], r.s[m]);
+          r.s[m] = mfma32x32x16(lds_read16(kbase[ks] + KO + m * C::K_BYTES), qf[m][ks], r.s[m]);
       }
     }
-    if (DA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    if (kPrio) __builtin_amdgcn_s_setprio(0);
     return r;
   };
-  // causal mask (diagonal sub-block only), row maxima, and whether any row's max
-  // outgrew its reference by more than 2^8
-  float mb[MPW];
-  bool need[MPW];
-  auto softmax_head = [&](Scores<MPW>& S, bool diag) {
-    bool any = false;
-#pragma unroll
-    for (int m = 0; m < MPW; ++m) {
-      if (diag) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 8 * (r >> 2) + 4 * hg + (r & 3);
-          if (key > li) S.s[m][r] = -INFINITY;
-        }
-      }
-      float mx = S.s[m][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S.s[m][r]);
-      mx = max_across_halves(mx);
-      mb[m] = mx * sl2;
-      need[m] = mb[m] > mref[m] + kLazyLog2;
-      any |= need[m];
-    }
-    return any;
-  };
-  auto rescale = [&]() {
-#pragma unroll
-    for (int m = 0; m < MPW; ++m) {
-      const float al = need[m] ? exp2f(mref[m] - mb[m]) : 1.f;
-      if (need[m]) mref[m] = mb[m];
-      lsum[m] *= al;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[m][cb][r] *= al;
-    }
-  };
-  // probabilities -> bf16 B operand of O^T = V^T P^T
-  auto softmax_exp = [&](const Scores<MPW>& S) {
-    Probs<MPW> P;
-#pragma unroll
-    for (int m = 0; m < MPW; ++m) {
-      f32x8 p0, p1;
-      float acc = 0.f;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        p0[r] = __builtin_amdgcn_exp2f(fmaf(S.s[m][r], sl2, -mref[m]));
-        p1[r] = __builtin_amdgcn_exp2f(fmaf(S.s[m][r + 8], sl2, -mref[m]));
-        acc += p0[r] + p1[r];
-      }
-      lsum[m] += acc;
-      P.p[m][0] = cvt_bf16x8(p0);
-      P.p[m][1] = cvt_bf16x8(p1);
-    }
-    return P;
-  };
-  // O^T[c][i] += V^T[c][j] P^T[j][i] over V rows row0..row0+31 of a stage
-  auto pv = [&](const unsigned char* st, int row0, const Probs<MPW>& P) {
-    const unsigned char* vt = st + C::NK * C::K_BYTES;
-    if (DA_SETPRIO) __builtin_amdgcn_s_setprio(2);
+  // O^T += V^T P^T over the sub-block at V offset VO; one V fragment feeds
+  // every map of the wave.
+  auto pv = [&](auto voffc, const Pr& P) {
+    constexpr int VO = decltype(voffc)::value;
+    if (kPrio) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const unsigned char* q = vt + (row0 + 16 * kk) * (DV * 2) + cb * 64 + voff[cb % NV];
+        const uint32_t q = vbase[cb % NV] + VO + 16 * kk * (DV * 2) + cb * 64;
         const bf16x8 va = join_bf16x8(tr_read(q), tr_read(q + 8 * (DV * 2)));
 #pragma unroll
         for (int m = 0; m < MPW; ++m) o[m][cb] = mfma32x32x16(va, P.p[m][kk], o[m][cb]);
       }
     }
-    if (DA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    if (kPrio) __builtin_amdgcn_s_setprio(0);
   };
+  // Causal mask of the diagonal sub-block: key 8(r>>2) + 4hg + (r&3) is
+  // masked for row li when 8(r>>2) + (r&3) > li - 4hg.  The threshold is
+  // opaque so the 16 compares stay here instead of being hoisted into 32
+  // live SGPRs.
+  auto mask_diag = [&](Sc& S) {
+    int t = li - 4 * hg;
+    asm volatile("" : "+v"(t));
+#pragma unroll
+    for (int m = 0; m < MPW; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > t) S.s[m][r] = -INFINITY;
+  };
+  // Probabilities as the bf16 B operand of P.V and the lane's block sums bs,
+  // computed in place over the scores (no branch: part of the steady-state
+  // scheduling region).
+  auto softmax_exps = [&](Sc& S, Pr& P) {
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S.s[m][r] = __builtin_amdgcn_exp2f(fmaf(S.s[m][r], sl2, nm[m]));
+      f32x8 e0, e1;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        e0[r] = S.s[m][r];
+        e1[r] = S.s[m][r + 8];
+      }
+      P.p[m][0] = cvt_bf16x8(e0);
+      P.p[m][1] = cvt_bf16x8(e1);
+      P.bs[m] = sum_bf16x8(P.p[m][1], sum_bf16x8(P.p[m][0], 0.f));
+    }
+  };
+  // The rare exact path, taken when some lane's block sum is above the cap:
+  // the sub-block's scores again (rescore(): its K is still in LDS), each
+  // map's m moved to its row maximum over both lane halves, O and l rescaled,
+  // the exponentials redone.  Then the running sums.
+  auto softmax_finish = [&](auto rescore, bool diag, Pr& P) {
+    bool any = false;
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) any |= !(P.bs[m] <= kSumCap);
+    if (__builtin_amdgcn_ballot_w64(any)) {
+      Sc S;
+      S = rescore();
+      if (diag) mask_diag(S);
+#pragma unroll
+      for (int m = 0; m < MPW; ++m) {
+        float mx = S.s[m][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S.s[m][r]);
+        const float mnew = fmaxf(-nm[m], max_across_halves(mx) * sl2);
+        const float al = __builtin_amdgcn_exp2f(-nm[m] - mnew);
+        nm[m] = -mnew;
+        lsum[m] *= al;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[m][cb][r] *= al;
+      }
+      softmax_exps(S, P);
+    }
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) lsum[m] += P.bs[m];
+  };
+  using std::integral_constant;
 
   if constexpr (!PIPE) {
-    // ---- 64-key tiles, double-buffered; sub-blocks processed in order ----
-    issue_tile(0, 0);
-    for (int kt = 0; kt < nkt; ++kt) {
+    // ---- key loop: 2-stage ring, unrolled by stage; each sub-block in order --
+    auto tile_step = [&](int kt, auto stage_c) {
+      constexpr int S = decltype(stage_c)::value;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile kt landed
       __syncthreads();                                  // all parts landed; other stage free
-      if (kt + 1 < nkt) issue_tile(kt + 1, (kt + 1) & 1);
-      if (!active) continue;
-      const unsigned char* st = smem + (kt & 1) * C::STAGE;
-      constexpr int NSB = kBN / 32;
-      constexpr int GS = C::SMG;  // sub-blocks sharing one max / rescale decision
-#pragma unroll
-      for (int g0 = 0; g0 < NSB; g0 += GS) {
-        if (kt * kBN + 32 * g0 > i0w) break;  // group entirely above this wave's diagonal
-        if (GS > 1 && kt * kBN + 32 * (g0 + GS - 1) <= i0w) {
-          // The whole group is visible: its score MFMAs back to back, one max /
-          // rescale decision, then the exponentials of sub-block s+1 alongside
-          // the P.V MFMAs of sub-block s.
-          Scores<MPW> S[GS];
-#pragma unroll
-          for (int j = 0; j < GS; ++j) S[j] = qk(st, 32 * (g0 + j));
-          const bool diag_last = kt * kBN + 32 * (g0 + GS - 1) == i0w;
-          bool any = false;
-#pragma unroll
-          for (int m = 0; m < MPW; ++m) {
-            if (diag_last) {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int key = 8 * (r >> 2) + 4 * hg + (r & 3);
-                if (key > li) S[GS - 1].s[m][r] = -INFINITY;
-              }
-            }
-            float mx = S[0].s[m][0];
-#pragma unroll
-            for (int j = 0; j < GS; ++j)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[j].s[m][r]);
-            mx = max_across_halves(mx);
-            mb[m] = mx * sl2;
-            need[m] = mb[m] > mref[m] + kLazyLog2;
-            any |= need[m];
-          }
-          if (__builtin_amdgcn_ballot_w64(any)) rescale();
-          Probs<MPW> P = softmax_exp(S[0]);
-#pragma unroll
-          for (int j = 0; j < GS; ++j) {
-            Probs<MPW> Pn;
-            if (j + 1 < GS) Pn = softmax_exp(S[j + 1]);
-            pv(st, 32 * (g0 + j), P);
-            if (j + 1 < GS) P = Pn;
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < GS; ++j) {
-            const int jb = kt * kBN + 32 * (g0 + j);
-            if (jb > i0w) break;  // sub-block entirely above this wave's diagonal
-            Scores<MPW> S = qk(st, 32 * (g0 + j));
-            if (__builtin_amdgcn_ballot_w64(softmax_head(S, jb == i0w))) rescale();
-            pv(st, 32 * (g0 + j), softmax_exp(S));
-          }
-        }
-      }
+      if (kt + 1 < nkt) issue_tile(kt + 1, integral_constant<int, 1 - S>{});
+      if (!active) return;
+      const int j0 = kt * kBN;
+      static_for<0, C::NSB>([&](auto sbc) {
+        constexpr int SB = decltype(sbc)::value;
+        const int jb = j0 + 32 * SB;
+        if (jb > i0w) return;  // sub-block entirely above this wave's diagonal
+        using cur_k = integral_constant<int, S * C::KREG + 32 * SB * D * 2>;
+        using cur_v = integral_constant<int, S * C::V_BYTES + 32 * SB * DV * 2>;
+        const bool diag = jb == i0w;
+        Sc Sb;
+        Sb = qk(cur_k{});
+        if (diag) mask_diag(Sb);
+        Pr P;
+        softmax_exps(Sb, P);
+        softmax_finish([&]() { return qk(cur_k{}); }, diag, P);
+        pv(cur_v{}, P);
+      });
+    };
+    issue_tile(0, integral_constant<int, 0>{});
+    for (int kt = 0; kt < nkt; kt += 2) {
+      tile_step(kt, integral_constant<int, 0>{});
+      if (kt + 1 >= nkt) break;
+      tile_step(kt + 1, integral_constant<int, 1>{});
     }
   } else {
-    // ---- 32-key tiles in a 4-stage ring, software-pipelined ----
-    // Step n (tile n) issues the MFMAs of P.V for tile n-1 and of the scores
-    // for tile n+1 in the same basic block as the exponentials of tile n, so
-    // matrix and vector work overlap inside the wave.  Tile n+1 is waited for
-    // (and made visible by a barrier) at step n; the copy of tile n+2 then
-    // goes to stage (n+2)%4, whose last reader was step n-1.  A rescale (rare)
-    // first flushes the pending P.V of tile n-1.
-    const int dw = active ? i0w / 32 : -1;  // last tile this wave needs
-    auto stage = [&](int n) { return smem + (n & 3) * C::STAGE; };
-    issue_tile(0, 0);
-    if (nkt > 1) issue_tile(1, 1);
+    // ---- key loop: 3-stage ring, software-pipelined over sub-blocks ---------
+    // Step n (this wave's n-th sub-block) issues, in one basic block, the P.V
+    // MFMAs of sub-block n-1 and the score MFMAs of sub-block n+1 alongside the
+    // exponentials of sub-block n, so matrix and vector work of one wave
+    // overlap.  The tile after the current one must be visible before the
+    // last sub-block of the current tile (its scores are computed there): the
+    // wait + barrier sits before that sub-block, and right after it the copy
+    // of the tile two ahead goes to the stage whose last reader (the P.V of
+    // the previous tile's last sub-block, issued at this tile's first step)
+    // every wave has passed.
+    const int nsub = active ? i0w / 32 + 1 : 0;  // sub-blocks up to the diagonal
+    // Scheduling of the steady-state step: NMF MFMAs (P.V of the previous
+    // sub-block, scores of the next), NRD LDS operand reads and the
+    // exponentials of this sub-block (~52 VALU instructions per map) dealt
+    // out in turn, a few reads ahead of the MFMAs that consume them.
+    auto interleave_hints = [&]() {
+      constexpr int NMF = MPW * (2 * CB + KS);
+      constexpr int NRD = 4 * CB + (V2 ? 1 : MPW) * KS;
+      constexpr int VPER = (52 * MPW + NMF - 1) / NMF;
+      constexpr int RPER = (NRD + NMF - 1) / NMF;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * RPER, 0);  // DS reads
+      static_for<0, NMF>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, RPER, 0);  // DS reads
+      });
+    };
+    Sc Scur;
+    Pr pp;  // probabilities of the previous sub-block, P.V pending
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) pp.p[m][0] = pp.p[m][1] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    issue_tile(0, integral_constant<int, 0>{});
+    {  // zero the V slot read as "the previous sub-block" at n = 0 (stage 2, last sub-block)
+      constexpr int ZB = 32 * DV * 2, Z0 = C::VBASE + 2 * C::V_BYTES + 32 * (C::NSB - 1) * DV * 2;
+      for (int i = tid * 16; i < ZB; i += NW * 64 * 16) *(uint4*)(smem + Z0 + i) = make_uint4(0, 0, 0, 0);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    Scores<MPW> S;
-    Probs<MPW> P;
-    if (dw >= 0) S = qk(stage(0), 0);
-    bool pending = false;  // P holds tile n-1's probabilities, its P.V not issued yet
-    for (int n = 0; n < nkt; ++n) {
-      const bool mine = n <= dw;
-      if (mine && __builtin_amdgcn_ballot_w64(softmax_head(S, n == dw))) {
-        if (pending) {
-          pv(stage(n - 1), 0, P);
-          pending = false;
+    if (nkt > 1) issue_tile(1, integral_constant<int, 1>{});
+    if (nsub > 0) Scur = qk(integral_constant<int, 0>{});
+    auto tile_step = [&](int kt, auto stage_c) {
+      constexpr int S = decltype(stage_c)::value;
+      static_for<0, C::NSB>([&](auto sbc) {
+        constexpr int SB = decltype(sbc)::value;
+        if constexpr (SB == C::NSB - 1) {
+          if (kt + 1 < nkt) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile kt+1 landed
+            __syncthreads();
+            if (kt + 2 < nkt) issue_tile(kt + 2, integral_constant<int, (S + 2) % 3>{});
+          }
         }
-        rescale();
-      }
-      if (n + 1 < nkt) {
-        if (n >= 1) {
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile n+1 landed (this wave's part)
-          __syncthreads();
-        }
-        if (n + 2 < nkt) issue_tile(n + 2, (n + 2) & 3);
-      }
-      if (!mine) continue;
-      if (n < dw) {
-        if (pending) {  // steady state
-          const Scores<MPW> Sn = qk(stage(n + 1), 0);
-          const Probs<MPW> Pn = softmax_exp(S);
-          pv(stage(n - 1), 0, P);
-          S = Sn;
-          P = Pn;
-        } else {
-          const Scores<MPW> Sn = qk(stage(n + 1), 0);
-          P = softmax_exp(S);
-          S = Sn;
-        }
-        pending = true;
-      } else {  // n == dw: this wave's last tile
-        if (pending) pv(stage(n - 1), 0, P);
-        pv(stage(n), 0, softmax_exp(S));
-        pending = false;
-      }
+        const int n = kt * C::NSB + SB;
+        if (n >= nsub) return;
+        constexpr int PS = SB > 0 ? S : (S + 2) % 3, PSB = SB > 0 ? SB - 1 : C::NSB - 1;  // previous
+        constexpr int NS = SB + 1 < C::NSB ? S : (S + 1) % 3, NSBI = SB + 1 < C::NSB ? SB + 1 : 0;  // next
+        using prev_v = integral_constant<int, PS * C::V_BYTES + 32 * PSB * DV * 2>;
+        using next_k = integral_constant<int, NS * C::KREG + 32 * NSBI * D * 2>;
+        using cur_v = integral_constant<int, S * C::V_BYTES + 32 * SB * DV * 2>;
+        using cur_k = integral_constant<int, S * C::KREG + 32 * SB * D * 2>;
+        // One straight-line step for every n.  At n = 0 the P.V of "the
+        // previous sub-block" multiplies zero probabilities with a zeroed V
+        // slot; at the last step the score MFMAs of "the next sub-block" read
+        // whatever that LDS holds and their result is dropped.
+        const bool last = n + 1 == nsub;
+        if (last) mask_diag(Scur);  // the diagonal is this wave's last sub-block
+        pv(prev_v{}, pp);
+        Sc Snext;
+        Snext = qk(next_k{});
+        softmax_exps(Scur, pp);
+        if (!DA_NO_HINTS) interleave_hints();
+        softmax_finish([&]() { return qk(cur_k{}); }, last, pp);
+        if (last) pv(cur_v{}, pp);  // drain
+        Scur = Snext;
+      });
+    };
+    for (int kt = 0; kt < nkt; kt += 3) {
+      tile_step(kt, integral_constant<int, 0>{});
+      if (kt + 1 >= nkt) break;
+      tile_step(kt + 1, integral_constant<int, 1>{});
+      if (kt + 2 >= nkt) break;
+      tile_step(kt + 2, integral_constant<int, 2>{});
     }
   }
 
@@ -586,21 +640,24 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
   float inv[MPW];
 #pragma unroll
   for (int m = 0; m < MPW; ++m) inv[m] = 1.f / (lsum[m] + __shfl_xor(lsum[m], 32, 64));
-
-  uint16_t* dst;
-  float post = 1.f;
+  // weight of the second map: lam / l2 (V1) or sigmoid(lam[t, p]) / l_odd (V2)
+  auto second_weight = [&](float inv2) {
+    if constexpr (V2) {
+      float lg = 0.f;
+      if (row < T) lg = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)row * a.lam.st + pair * a.lam.sh];
+      return sigmoid_f32(lg) * inv2;
+    } else {
+      return lam * inv2;
+    }
+  };
+  float ss = 0.f;
   if constexpr (MPW == 1) {
-    // map 2's wave hands lam * O2 / l2 to map 1's wave through LDS
+    // map 2's wave hands its weighted O to its partner through LDS
     __syncthreads();  // every wave is done with the K/V stages
-    float* xch = (float*)smem + (wave >> 1) * (CB * 16 * 64);  // one slot per partner pair
+    float* xch = (float*)smem + slot * (CB * 16 * 64);
     if (m0 == 1) {
       if (active) {
-        float w = lam * inv[0];
-        if constexpr (V2) {
-          float lg = 0.f;
-          if (row < T) lg = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)row * a.lam.st + pair * a.lam.sh];
-          w = sigmoid_f32(lg) * inv[0];
-        }
+        const float w = second_weight(inv[0]);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -611,7 +668,6 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
     }
     __syncthreads();
     if (!active) return;
-    float ss = 0.f;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -620,39 +676,26 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
         o[0][cb][r] = dv;
         ss += dv * dv;
       }
-    if constexpr (!V2) {
-      ss += __shfl_xor(ss, 32, 64);
-      post = (1.f - a.lam_init) / sqrtf(ss * (1.f / DV) + 1e-5f);
-      dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)row * a.out.st + h * a.out.sh;
-    } else {
-      dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)row * a.out.st + pair * a.out.sh;
-    }
   } else {
     if (!active) return;
-    if constexpr (!V2) {
-      const float w1 = lam * inv[1];
-      float ss = 0.f;
+    const float w = second_weight(inv[1]);
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float dv = o[0][cb][r] * inv[0] - w1 * o[1][cb][r];
-          o[0][cb][r] = dv;
-          ss += dv * dv;
-        }
-      ss += __shfl_xor(ss, 32, 64);
-      post = (1.f - a.lam_init) / sqrtf(ss * (1.f / DV) + 1e-5f);
-      dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)row * a.out.st + h * a.out.sh;
-    } else {
-      float lg = 0.f;
-      if (row < T) lg = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)row * a.lam.st + pair * a.lam.sh];
-      const float w1 = sigmoid_f32(lg) * inv[1];
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[0][cb][r] = o[0][cb][r] * inv[0] - w1 * o[1][cb][r];
-      dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)row * a.out.st + pair * a.out.sh;
-    }
+      for (int r = 0; r < 16; ++r) {
+        const float dv = o[0][cb][r] * inv[0] - w * o[1][cb][r];
+        o[0][cb][r] = dv;
+        ss += dv * dv;
+      }
+  }
+  uint16_t* dst;
+  float post = 1.f;
+  if constexpr (!V2) {
+    ss += __shfl_xor(ss, 32, 64);
+    post = (1.f - a.lam_init) / sqrtf(ss * (1.f / DV) + 1e-5f);
+    dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)row * a.out.st + h * a.out.sh;
+  } else {
+    dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)row * a.out.st + pair * a.out.sh;
   }
   if (row < T) {
 #pragma unroll
@@ -677,34 +720,41 @@ hipError_t launch(const PrefillArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Per-shape kernel variant: maps per wave (MPW) and waves per workgroup (NW).
+// Kernel shape by workload: waves per workgroup (NW), maps per wave (MPW),
+// pipelined key loop (PIPE).  Rows per workgroup = 32 * NW * MPW / 2 (V1).
+#ifndef DA_V1_D64_NW
+#define DA_V1_D64_NW 8
+#endif
 #ifndef DA_V1_D64_MPW
 #define DA_V1_D64_MPW 1
 #endif
-#ifndef DA_V1_D64_NW
-#define DA_V1_D64_NW 4
+#ifndef DA_V1_D64_PIPE
+#define DA_V1_D64_PIPE true
+#endif
+#ifndef DA_V1_D128_NW
+#define DA_V1_D128_NW 8
 #endif
 #ifndef DA_V1_D128_MPW
 #define DA_V1_D128_MPW 1
 #endif
-#ifndef DA_V2_MPW
-#define DA_V2_MPW 1
+#ifndef DA_V1_D128_PIPE
+#define DA_V1_D128_PIPE false
 #endif
 #ifndef DA_V2_NW
 #define DA_V2_NW 8
 #endif
-#ifndef DA_V1_D64_PIPE
-#define DA_V1_D64_PIPE false
+#ifndef DA_V2_MPW
+#define DA_V2_MPW 1
 #endif
 #ifndef DA_V2_PIPE
-#define DA_V2_PIPE false
+#define DA_V2_PIPE true
 #endif
 
 hipError_t launch_prefill_v1_bf16(int d, const PrefillArgs& a0, hipStream_t s) {
   PrefillArgs a = a0;
   a.units_per_b = a.H;
   auto geom = [&](int nw, int mpw) {
-    const int BMT = 32 * (mpw == 2 ? nw : nw / 2);  // rows per workgroup
+    const int BMT = 32 * (nw * mpw / 2);  // rows per workgroup
     a.tiles = (a.T + BMT - 1) / BMT;
     a.nwg = a.B * a.H * a.tiles;
   };
@@ -713,8 +763,8 @@ hipError_t launch_prefill_v1_bf16(int d, const PrefillArgs& a0, hipStream_t s) {
     return launch<64, 128, false, DA_V1_D64_NW, DA_V1_D64_MPW, DA_V1_D64_PIPE>(a, s);
   }
   if (d == 128) {
-    geom(4 * (3 - DA_V1_D128_MPW), DA_V1_D128_MPW);
-    return launch<128, 256, false, 4 * (3 - DA_V1_D128_MPW), DA_V1_D128_MPW, false>(a, s);
+    geom(DA_V1_D128_NW, DA_V1_D128_MPW);
+    return launch<128, 256, false, DA_V1_D128_NW, DA_V1_D128_MPW, DA_V1_D128_PIPE>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -722,7 +772,7 @@ hipError_t launch_prefill_v1_bf16(int d, const PrefillArgs& a0, hipStream_t s) {
 hipError_t launch_prefill_v2_bf16(int d, const PrefillArgs& a0, hipStream_t s) {
   PrefillArgs a = a0;
   const int np = a.G / 2;
-  const int units = DA_V2_MPW == 2 ? DA_V2_NW : DA_V2_NW / 2;  // (pair, row block) slots per workgroup
+  const int units = DA_V2_NW * DA_V2_MPW / 2;  // (pair, row block) slots per workgroup
   a.pc = np % units == 0 ? units : np % 2 == 0 && units % 2 == 0 ? 2 : 1;
   if (a.pc > units) a.pc = 1;
   const int BMT = 32 * (units / a.pc);
