@@ -57,6 +57,9 @@ namespace {
 #ifndef DA_V2_BN
 #define DA_V2_BN 128  // keys per LDS stage of the V2 kernel (64 or 128)
 #endif
+#ifndef DA_PIPE_VSTAGES
+#define DA_PIPE_VSTAGES 3  // V stages of the pipelined loop (2: 80 KB of LDS at d = 64 / 128)
+#endif
 #ifndef DA_NO_HINTS
 #define DA_NO_HINTS 0
 #endif
@@ -143,33 +146,37 @@ struct Cfg {
   static constexpr int KS = D / 16;   // k-steps of the score MFMA
   static constexpr int CB = DV / 32;  // 32-wide column blocks of O^T
   static constexpr int NK = V2 ? 1 : 2;
-  // PIPE: 64-key tiles in a 3-stage ring (software-pipelined key loop);
-  // otherwise BN-key tiles double-buffered.
-  static constexpr int NST = PIPE ? 3 : 2;
+  // PIPE: 64-key tiles, K in a 3-stage ring and V in a DA_PIPE_VSTAGES-stage
+  // ring (software-pipelined key loop: the scores of a tile's first
+  // sub-block are computed one step before its V is needed, so V needs one
+  // stage less); otherwise BN-key tiles with K and V double-buffered.
+  static constexpr int NSTK = PIPE ? 3 : 2;
+  static constexpr int NSTV = PIPE ? DA_PIPE_VSTAGES : 2;
+  static_assert(NSTV == 2 || NSTV == 3, "V ring depth");
   static constexpr int BN = PIPE ? 64 : (V2 ? DA_V2_BN : 64);  // keys per tile
   static constexpr int NSB = BN / 32;            // 32-key sub-blocks per tile
   static constexpr int K_BYTES = BN * D * 2;     // one K tensor of one tile
   static constexpr int V_BYTES = BN * DV * 2;
   static constexpr int KREG = NK * K_BYTES;      // K tensors of one stage
-  static constexpr int VBASE = NST * KREG;       // V stages follow all K stages
-  static constexpr int TILE_SMEM = NST * (KREG + V_BYTES);
-  static constexpr int KCH = K_BYTES / 1024;     // 1 KB DMA instructions per K tensor
-  static constexpr int VCH = V_BYTES / 1024;
-  static constexpr int NCH = NK * KCH + VCH;
-  static constexpr int CPW = NCH / NW;           // DMA instructions per wave per tile
-  static_assert(NCH % NW == 0, "tile DMA split");
+  static constexpr int VBASE = NSTK * KREG;      // V stages follow all K stages
+  static constexpr int TILE_SMEM = NSTK * KREG + NSTV * V_BYTES;
+  static constexpr int KCH = NK * K_BYTES / 1024;  // 1 KB DMA instructions per tile: K
+  static constexpr int VCH = V_BYTES / 1024;       // and V
+  static constexpr int KPW = KCH / NW, VPW = VCH / NW;  // per wave
+  static_assert(KCH % NW == 0 && VCH % NW == 0, "tile DMA split");
   static_assert(D >= 64 && DV >= 64, "swizzles assume >= 8 chunks per row");
   static_assert(MPW == 1 || MPW == 2, "maps per wave");
-  static_assert(!PIPE || NSB >= 2, "the pipelined ring frees a stage one sub-block before the tile ends");
+  static_assert(!PIPE || NSB >= 2, "the pipelined rings free a stage one sub-block before the tile ends");
   // Operand reads use 16-bit immediate offsets from a per-lane base.
-  static_assert((NST - 1) * KREG + (NK - 1) * K_BYTES * (MPW - 1) + (BN - 32) * D * 2 < 65536, "K read offset range");
-  static_assert((NST - 1) * V_BYTES + (BN - 8) * DV * 2 + (CB - 1) * 64 < 65536, "V read offset range");
+  static_assert((NSTK - 1) * KREG + (NK - 1) * K_BYTES * (MPW - 1) + (BN - 32) * D * 2 < 65536, "K read offset range");
+  static_assert((NSTV - 1) * V_BYTES + (BN - 8) * DV * 2 + (CB - 1) * 64 < 65536, "V read offset range");
   // MPW == 1 epilogue: one exchange slot per partner-wave pair (fp32, lane-native order)
   static constexpr int XBYTES = MPW == 1 ? (NW / 2) * CB * 16 * 64 * 4 : 0;
   static constexpr int SMEM = TILE_SMEM > XBYTES ? TILE_SMEM : XBYTES;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   // MPW == 1 with 4 waves: two workgroups (two waves per SIMD) per CU
   static constexpr int MIN_BLOCKS = (MPW == 1 && NW == 4) ? 2 : 1;
+  static_assert(MIN_BLOCKS * SMEM <= 160 * 1024, "LDS budget for the intended occupancy");
 };
 
 // (clang tries to constant-evaluate a lambda call whose value initialises a
@@ -285,48 +292,74 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
   // lane's byte offset is computed once; per tile only the scalar base moves.
   // Rows >= T (last tile only) are clamped to T-1: finite data for keys that
   // every valid query masks.
-  uint32_t dma_off[C::CPW];
+  uint32_t koff[C::KPW], voff[C::VPW];
 #pragma unroll
-  for (int i = 0; i < C::CPW; ++i) {
-    const int ci = wave + NW * i;  // chunk of the stage (wave-uniform)
-    if (ci < C::NK * C::KCH) {
-      const int n = ci / C::KCH, cix = ci % C::KCH;
-      const int pos = cix * 64 + lane;  // 16 B chunk index inside the K tile
-      const int r = pos / (D / 8), sc = pos % (D / 8);
-      dma_off[i] = (uint32_t)((r * (n ? kst[1] : kst[0]) + (sc ^ k_swizzle<D>(r)) * 8) * 2);
-    } else {
-      const int cix = ci - C::NK * C::KCH;
-      const int pos = cix * 64 + lane;
-      const int r = pos / (DV / 8), sc = pos % (DV / 8);
-      dma_off[i] = (uint32_t)((r * vst + (sc ^ v_swizzle<DV>(r)) * 8) * 2);
-    }
+  for (int i = 0; i < C::KPW; ++i) {
+    const int ci = wave + NW * i;  // K chunk of the tile (wave-uniform)
+    const int n = ci / (C::KCH / C::NK), cix = ci % (C::KCH / C::NK);
+    const int pos = cix * 64 + lane;  // 16 B chunk index inside the K tensor's tile
+    const int r = pos / (D / 8), sc = pos % (D / 8);
+    koff[i] = (uint32_t)((r * (n ? kst[1] : kst[0]) + (sc ^ k_swizzle<D>(r)) * 8) * 2);
   }
-  auto issue_tile = [&](int kt, auto stage_c) {
+#pragma unroll
+  for (int i = 0; i < C::VPW; ++i) {
+    const int cix = wave + NW * i;
+    const int pos = cix * 64 + lane;
+    const int r = pos / (DV / 8), sc = pos % (DV / 8);
+    voff[i] = (uint32_t)((r * vst + (sc ^ v_swizzle<DV>(r)) * 8) * 2);
+  }
+  // K tensors of tile kt into K stage S.
+  auto issue_k = [&](int kt, auto stage_c) {
     constexpr int S = decltype(stage_c)::value;
     const int j0 = kt * kBN;
     const bool tail = j0 + kBN > T;  // uniform: rows past the end need clamping
 #pragma unroll
-    for (int i = 0; i < C::CPW; ++i) {
+    for (int i = 0; i < C::KPW; ++i) {
       const int ci = wave + NW * i;
-      const bool isk = ci < C::NK * C::KCH;
-      const int n = isk ? ci / C::KCH : 0;
-      const int cix = isk ? ci % C::KCH : ci - C::NK * C::KCH;
-      const uint16_t* tp = isk ? (n ? kp[1] : kp[0]) : vp;
-      const int64_t tst = isk ? (n ? kst[1] : kst[0]) : vst;
-      const uint32_t dst = smem_lds + (isk ? S * C::KREG + n * C::K_BYTES : C::VBASE + S * C::V_BYTES) + cix * 1024;
-      uint32_t off = dma_off[i];
+      const int n = ci / (C::KCH / C::NK), cix = ci % (C::KCH / C::NK);
+      const int64_t tst = n ? kst[1] : kst[0];
+      uint32_t off = koff[i];
       if (tail) {  // same chunk, row clamped to T-1 (offsets < 2^31: token stride < 2^24)
-        const int cols = isk ? D / 8 : DV / 8;
         const int pos = cix * 64 + lane;
-        const int r = pos / cols, sc = pos % cols;
-        const int c = sc ^ (isk ? k_swizzle<D>(r) : v_swizzle<DV>(r));
-        off = ((uint32_t)min(r, T - 1 - j0) * (uint32_t)tst + (uint32_t)(c * 8)) * 2u;
+        const int r = pos / (D / 8), sc = pos % (D / 8);
+        off = ((uint32_t)min(r, T - 1 - j0) * (uint32_t)tst + (uint32_t)((sc ^ k_swizzle<D>(r)) * 8)) * 2u;
       }
-      dma16_sbase(tp + (int64_t)j0 * tst, off, dst);
+      dma16_sbase((n ? kp[1] : kp[0]) + (int64_t)j0 * tst, off,
+                  smem_lds + S * C::KREG + n * C::K_BYTES + cix * 1024);
+    }
+  };
+  // V of tile kt into V stage S.
+  auto issue_v = [&](int kt, auto stage_c) {
+    constexpr int S = decltype(stage_c)::value;
+    const int j0 = kt * kBN;
+    const bool tail = j0 + kBN > T;
+#pragma unroll
+    for (int i = 0; i < C::VPW; ++i) {
+      const int cix = wave + NW * i;
+      uint32_t off = voff[i];
+      if (tail) {
+        const int pos = cix * 64 + lane;
+        const int r = pos / (DV / 8), sc = pos % (DV / 8);
+        off = ((uint32_t)min(r, T - 1 - j0) * (uint32_t)vst + (uint32_t)((sc ^ v_swizzle<DV>(r)) * 8)) * 2u;
+      }
+      dma16_sbase(vp + (int64_t)j0 * vst, off, smem_lds + C::VBASE + S * C::V_BYTES + cix * 1024);
     }
   };
 
-  // ---- Q fragments (B operand of S^T = K Q^T): row i0w+li, cols 16ks+8hg ----
+  // ---- prologue loads, overlapped: the first K/V tile(s), Q, the V1 lambda
+  // vectors.  One wait below retires them all, so a compiler-placed wait for
+  // Q inside the key loop (which would also wait for a tile copy in flight)
+  // never happens, and the latencies of the three are paid once.
+  using std::integral_constant;
+  issue_k(0, integral_constant<int, 0>{});
+  issue_v(0, integral_constant<int, 0>{});
+  if constexpr (PIPE) {
+    if (nkt > 1) {
+      issue_k(1, integral_constant<int, 1>{});
+      if constexpr (C::NSTV == 3) issue_v(1, integral_constant<int, 1>{});
+    }
+  }
+  // Q fragments (B operand of S^T = K Q^T): row i0w+li, cols 16ks+8hg
   bf16x8 qf[MPW][KS];
   {
     const int row = i0w + li;
@@ -337,13 +370,27 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
         qf[m][ks] = as_bf16x8(row < T ? *(const uint4*)(qp[m] + (int64_t)row * qst[m] + 16 * ks + 8 * hg)
                                       : make_uint4(0, 0, 0, 0));
   }
-  // Retire the Q loads here.  The compiler cannot see the tile DMA, but the
-  // hardware counter counts it: a compiler-placed vmcnt wait for Q inside the
-  // key loop would also wait for the next tile's copy.
+  // V2: this row's lambda logit for the pair (used by the wave holding the odd head)
+  float lgit = 0.f;
+  if constexpr (V2) {
+    const int row = i0w + li;
+    if ((MPW == 2 || m0 == 1) && row < T)
+      lgit = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)row * a.lam.st + pair * a.lam.sh];
+  }
+  constexpr int LPL = (D + 63) / 64;  // lambda vector elements per lane
+  float lv[4][LPL];
+  if constexpr (!V2) {
+    const float* lp[4] = {a.lq1, a.lk1, a.lq2, a.lk2};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < LPL; ++i) lv[j][i] = lane + 64 * i < D ? lp[j][lane + 64 * i] : 0.f;
+  }
 #pragma unroll
   for (int m = 0; m < MPW; ++m)
 #pragma unroll
     for (int ks = 0; ks < KS; ks += 2) asm volatile("s_waitcnt vmcnt(0)" : "+v"(qf[m][ks]), "+v"(qf[m][ks + 1]));
+  asm volatile("" : "+v"(lgit));  // (retired by the wait above)
 
   // ---- per-lane LDS bases (every stage / sub-block / map offset is an immediate) ----
   // K chunk (2ks + hg) of tile row r = 32 sb + li sits at chunk (2ks + hg) ^ k_swizzle(li)
@@ -378,9 +425,10 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
   float lam = 0.f;
   if constexpr (!V2) {
     float pa = 0.f, pb = 0.f;
-    for (int c = lane; c < D; c += 64) {
-      pa += a.lq1[c] * a.lk1[c];
-      pb += a.lq2[c] * a.lk2[c];
+#pragma unroll
+    for (int i = 0; i < LPL; ++i) {
+      pa += lv[0][i] * lv[1][i];
+      pb += lv[2][i] * lv[3][i];
     }
     pa = wave_sum(pa);
     pb = wave_sum(pb);
@@ -517,7 +565,6 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
 #pragma unroll
     for (int m = 0; m < MPW; ++m) lsum[m] += P.bs[m];
   };
-  using std::integral_constant;
 
   if constexpr (!PIPE) {
     // ---- key loop: 2-stage ring, unrolled by stage; each sub-block in order --
@@ -525,7 +572,10 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
       constexpr int S = decltype(stage_c)::value;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile kt landed
       __syncthreads();                                  // all parts landed; other stage free
-      if (kt + 1 < nkt) issue_tile(kt + 1, integral_constant<int, 1 - S>{});
+      if (kt + 1 < nkt) {
+        issue_k(kt + 1, integral_constant<int, 1 - S>{});
+        issue_v(kt + 1, integral_constant<int, 1 - S>{});
+      }
       if (!active) return;
       const int j0 = kt * kBN;
       static_for<0, C::NSB>([&](auto sbc) {
@@ -544,23 +594,26 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
         pv(cur_v{}, P);
       });
     };
-    issue_tile(0, integral_constant<int, 0>{});
-    for (int kt = 0; kt < nkt; kt += 2) {
+    for (int kt = 0; kt < nkt; kt += 2) {  // (tile 0 was issued in the prologue)
       tile_step(kt, integral_constant<int, 0>{});
       if (kt + 1 >= nkt) break;
       tile_step(kt + 1, integral_constant<int, 1>{});
     }
   } else {
-    // ---- key loop: 3-stage ring, software-pipelined over sub-blocks ---------
-    // Step n (this wave's n-th sub-block) issues, in one basic block, the P.V
-    // MFMAs of sub-block n-1 and the score MFMAs of sub-block n+1 alongside the
-    // exponentials of sub-block n, so matrix and vector work of one wave
-    // overlap.  The tile after the current one must be visible before the
-    // last sub-block of the current tile (its scores are computed there): the
-    // wait + barrier sits before that sub-block, and right after it the copy
-    // of the tile two ahead goes to the stage whose last reader (the P.V of
-    // the previous tile's last sub-block, issued at this tile's first step)
-    // every wave has passed.
+    // ---- key loop: K in a 3-stage ring, V in an NSTV-stage ring, software-
+    // pipelined over sub-blocks.  Step n (this wave's n-th sub-block) issues,
+    // in one basic block, the P.V MFMAs of sub-block n-1 and the score MFMAs
+    // of sub-block n+1 alongside the exponentials of sub-block n, so matrix
+    // and vector work of one wave overlap.
+    // Tile kt's K sits in K stage kt % 3 and its V in V stage kt % NSTV.
+    // Before the last sub-block of tile kt (whose step computes the scores of
+    // tile kt+1) every wave waits for its copies and meets at a barrier; then:
+    //   * K of tile kt+2 goes to K stage (kt+2) % 3, last read by the scores
+    //     of tile kt-1's last sub-block (step (kt-1, NSB-2));
+    //   * V of tile kt+NSTV-1 goes to V stage (kt-1) % NSTV, last read by the
+    //     P.V of tile kt-1's last sub-block (step (kt, 0)).
+    // Every wave has passed both steps at that barrier.  K lands two steps
+    // before its first reader, V 2 (NSTV - 1) steps before.
     const int nsub = active ? i0w / 32 + 1 : 0;  // sub-blocks up to the diagonal
     // Scheduling of the steady-state step: NMF MFMAs (P.V of the previous
     // sub-block, scores of the next), NRD LDS operand reads and the
@@ -582,34 +635,33 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
     Pr pp;  // probabilities of the previous sub-block, P.V pending
 #pragma unroll
     for (int m = 0; m < MPW; ++m) pp.p[m][0] = pp.p[m][1] = as_bf16x8(make_uint4(0, 0, 0, 0));
-    issue_tile(0, integral_constant<int, 0>{});
-    {  // zero the V slot read as "the previous sub-block" at n = 0 (stage 2, last sub-block)
-      constexpr int ZB = 32 * DV * 2, Z0 = C::VBASE + 2 * C::V_BYTES + 32 * (C::NSB - 1) * DV * 2;
+    {  // zero the V slot read as "the previous sub-block" at n = 0 (last V stage, last sub-block)
+      constexpr int ZB = 32 * DV * 2, Z0 = C::VBASE + (C::NSTV - 1) * C::V_BYTES + 32 * (C::NSB - 1) * DV * 2;
       for (int i = tid * 16; i < ZB; i += NW * 64 * 16) *(uint4*)(smem + Z0 + i) = make_uint4(0, 0, 0, 0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (nkt > 1) issue_tile(1, integral_constant<int, 1>{});
+    __syncthreads();  // K of tiles 0, 1 and V of tiles 0..NSTV-2 (issued, retired in the prologue) visible
     if (nsub > 0) Scur = qk(integral_constant<int, 0>{});
-    auto tile_step = [&](int kt, auto stage_c) {
-      constexpr int S = decltype(stage_c)::value;
+    auto tile_step = [&](int kt, auto kstage_c, auto vstage_c) {
+      constexpr int SK = decltype(kstage_c)::value, SV = decltype(vstage_c)::value;
       static_for<0, C::NSB>([&](auto sbc) {
         constexpr int SB = decltype(sbc)::value;
         if constexpr (SB == C::NSB - 1) {
           if (kt + 1 < nkt) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile kt+1 landed
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies landed
             __syncthreads();
-            if (kt + 2 < nkt) issue_tile(kt + 2, integral_constant<int, (S + 2) % 3>{});
+            if (kt + 2 < nkt) issue_k(kt + 2, integral_constant<int, (SK + 2) % 3>{});
+            if (kt + C::NSTV - 1 < nkt)
+              issue_v(kt + C::NSTV - 1, integral_constant<int, (SV + C::NSTV - 1) % C::NSTV>{});
           }
         }
         const int n = kt * C::NSB + SB;
         if (n >= nsub) return;
-        constexpr int PS = SB > 0 ? S : (S + 2) % 3, PSB = SB > 0 ? SB - 1 : C::NSB - 1;  // previous
-        constexpr int NS = SB + 1 < C::NSB ? S : (S + 1) % 3, NSBI = SB + 1 < C::NSB ? SB + 1 : 0;  // next
-        using prev_v = integral_constant<int, PS * C::V_BYTES + 32 * PSB * DV * 2>;
-        using next_k = integral_constant<int, NS * C::KREG + 32 * NSBI * D * 2>;
-        using cur_v = integral_constant<int, S * C::V_BYTES + 32 * SB * DV * 2>;
-        using cur_k = integral_constant<int, S * C::KREG + 32 * SB * D * 2>;
+        constexpr int PSV = SB > 0 ? SV : (SV + C::NSTV - 1) % C::NSTV, PSB = SB > 0 ? SB - 1 : C::NSB - 1;  // prev
+        constexpr int NSK = SB + 1 < C::NSB ? SK : (SK + 1) % 3, NSBI = SB + 1 < C::NSB ? SB + 1 : 0;  // next
+        using prev_v = integral_constant<int, PSV * C::V_BYTES + 32 * PSB * DV * 2>;
+        using next_k = integral_constant<int, NSK * C::KREG + 32 * NSBI * D * 2>;
+        using cur_v = integral_constant<int, SV * C::V_BYTES + 32 * SB * DV * 2>;
+        using cur_k = integral_constant<int, SK * C::KREG + 32 * SB * D * 2>;
         // One straight-line step for every n.  At n = 0 the P.V of "the
         // previous sub-block" multiplies zero probabilities with a zeroed V
         // slot; at the last step the score MFMAs of "the next sub-block" read
@@ -626,12 +678,18 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
         Scur = Snext;
       });
     };
-    for (int kt = 0; kt < nkt; kt += 3) {
-      tile_step(kt, integral_constant<int, 0>{});
-      if (kt + 1 >= nkt) break;
-      tile_step(kt + 1, integral_constant<int, 1>{});
-      if (kt + 2 >= nkt) break;
-      tile_step(kt + 2, integral_constant<int, 2>{});
+    // unrolled over the period of the two rings
+    constexpr int PER = C::NSTV == 3 ? 3 : 6;
+    for (int kt0 = 0; kt0 < nkt; kt0 += PER) {
+      bool done = false;
+      static_for<0, PER>([&](auto ic) {
+        constexpr int I = decltype(ic)::value;
+        if (done || kt0 + I >= nkt) {
+          done = true;
+          return;
+        }
+        tile_step(kt0 + I, integral_constant<int, I % 3>{}, integral_constant<int, I % C::NSTV>{});
+      });
     }
   }
 
@@ -643,9 +701,7 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
   // weight of the second map: lam / l2 (V1) or sigmoid(lam[t, p]) / l_odd (V2)
   auto second_weight = [&](float inv2) {
     if constexpr (V2) {
-      float lg = 0.f;
-      if (row < T) lg = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)row * a.lam.st + pair * a.lam.sh];
-      return sigmoid_f32(lg) * inv2;
+      return sigmoid_f32(lgit) * inv2;
     } else {
       return lam * inv2;
     }
