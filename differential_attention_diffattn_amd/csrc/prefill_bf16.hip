@@ -710,14 +710,20 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
   if constexpr (MPW == 1) {
     // map 2's wave hands its weighted O to its partner through LDS
     __syncthreads();  // every wave is done with the K/V stages
-    float* xch = (float*)smem + slot * (CB * 16 * 64);
+    // 16-byte chunks (four accumulator registers) in lane order: conflict-free
+    f32x4* xch = (f32x4*)smem + slot * (CB * 4 * 64);
     if (m0 == 1) {
       if (active) {
         const float w = second_weight(inv[0]);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) xch[(cb * 16 + r) * 64 + lane] = o[0][cb][r] * w;
+          for (int g = 0; g < 4; ++g) {
+            f32x4 x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = o[0][cb][4 * g + j] * w;
+            xch[(cb * 4 + g) * 64 + lane] = x;
+          }
       }
       __syncthreads();
       return;
@@ -727,10 +733,14 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float dv = o[0][cb][r] * inv[0] - xch[(cb * 16 + r) * 64 + lane];
-        o[0][cb][r] = dv;
-        ss += dv * dv;
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = xch[(cb * 4 + g) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float dv = o[0][cb][4 * g + j] * inv[0] - x[j];
+          o[0][cb][4 * g + j] = dv;
+          ss += dv * dv;
+        }
       }
   } else {
     if (!active) return;
