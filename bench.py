@@ -16,7 +16,8 @@ The JSON line also carries:
   cpu_baseline  the fp64 oracle timed on a bounded sample of the same
                 workload on this host's cores;
   secondary     the other full-size workloads (3B-class V1, V2 GQA prefill,
-                V2 decode), each with its own roofline.
+                V2 decode), each with its own roofline; a secondary step is
+                8 launches of the workload (warm-up ~0.3 s of its own calls).
 Logs go to stderr; stdout holds exactly one JSON line.
 """
 from __future__ import annotations
@@ -261,7 +262,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--only", default=None,
                     help="time a single workload by name, or 'copy' for the 1 GiB copy calibration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -297,11 +298,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    def measure(name, steps, warmup):
+    def measure(name, steps, warmup, calls_per_step=None):
         w = workloads.WORKLOADS[name]
         x = workloads.inputs_for(w, dev)
         call = _caller(w, x, binding, torch)
         layers = list(w.layers) if w.layers else [0]
+        if calls_per_step:  # repeat the layer list so one step holds several launches
+            layers = (layers * calls_per_step)[:max(calls_per_step, len(layers))]
         elapsed, launch_ms = _timed(torch, call, layers, steps, warmup, graph=not args.eager)
         per_call_s = elapsed / (steps * len(layers))
         roof = _roofline(w, launch_ms)
@@ -329,7 +332,13 @@ def main():
     secondary = []
     if not args.no_secondary:
         for name in SECONDARY:
-            _, xs, r = measure(name, max(5, args.steps // 2), 3)
+            # warm-up sized to ~0.3 s of this workload's own calls, so the
+            # GPU clock has settled under its load before the timed steps
+            ws = workloads.WORKLOADS[name]
+            est_s = ws.flops() / 1e15 if ws.kind != "decode" else ws.compulsory_bytes() / 5.5e12
+            # 8 launches per step: the events around a graph replay then time
+            # the kernels, not the replay's launch
+            _, xs, r = measure(name, max(10, args.steps), max(3, int(0.3 / (8 * est_s))), calls_per_step=8)
             secondary.append(r)
             del xs
             torch.cuda.empty_cache()
