@@ -170,8 +170,10 @@ struct Cfg {
   // Operand reads use 16-bit immediate offsets from a per-lane base.
   static_assert((NSTK - 1) * KREG + (NK - 1) * K_BYTES * (MPW - 1) + (BN - 32) * D * 2 < 65536, "K read offset range");
   static_assert((NSTV - 1) * V_BYTES + (BN - 8) * DV * 2 + (CB - 1) * 64 < 65536, "V read offset range");
-  // MPW == 1 epilogue: one exchange slot per partner-wave pair (fp32, lane-native order)
-  static constexpr int XBYTES = MPW == 1 ? (NW / 2) * CB * 16 * 64 * 4 : 0;
+  // MPW == 1 epilogue: one exchange slot per partner-wave pair (fp32, lane-native
+  // order), then each pair's two 64-lane partial sums of squares
+  static constexpr int XBYTES_DATA = MPW == 1 ? (NW / 2) * CB * 16 * 64 * 4 : 0;
+  static constexpr int XBYTES = MPW == 1 ? XBYTES_DATA + (NW / 2) * 128 * 4 : 0;
   static constexpr int SMEM = TILE_SMEM > XBYTES ? TILE_SMEM : XBYTES;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   // MPW == 1 with 4 waves: two workgroups (two waves per SIMD) per CU
@@ -346,19 +348,15 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
     }
   };
 
-  // ---- prologue loads, overlapped: the first K/V tile(s), Q, the V1 lambda
-  // vectors.  One wait below retires them all, so a compiler-placed wait for
-  // Q inside the key loop (which would also wait for a tile copy in flight)
-  // never happens, and the latencies of the three are paid once.
+  // ---- prologue loads, overlapped: the first K/V tile, Q, the V1 lambda
+  // vectors / the V2 logit, then (pipelined loop) the second tile.  One wait
+  // below retires all but the second tile's copies, so a compiler-placed wait
+  // for Q inside the key loop (which would also wait for a tile copy in
+  // flight) never happens, the latencies are paid once, and the second tile
+  // keeps streaming until the first tile barrier.
   using std::integral_constant;
   issue_k(0, integral_constant<int, 0>{});
   issue_v(0, integral_constant<int, 0>{});
-  if constexpr (PIPE) {
-    if (nkt > 1) {
-      issue_k(1, integral_constant<int, 1>{});
-      if constexpr (C::NSTV == 3) issue_v(1, integral_constant<int, 1>{});
-    }
-  }
   // Q fragments (B operand of S^T = K Q^T): row i0w+li, cols 16ks+8hg
   bf16x8 qf[MPW][KS];
   {
@@ -386,11 +384,35 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
 #pragma unroll
       for (int i = 0; i < LPL; ++i) lv[j][i] = lane + 64 * i < D ? lp[j][lane + 64 * i] : 0.f;
   }
+  // copies of tile 1 (pipelined loop), issued last: the waits below leave them in flight
+  constexpr int kT1 = PIPE ? C::KPW + (C::NSTV == 3 ? C::VPW : 0) : 0;
+  if constexpr (PIPE) {
+    if (nkt > 1) {
+      issue_k(1, integral_constant<int, 1>{});
+      if constexpr (C::NSTV == 3) issue_v(1, integral_constant<int, 1>{});
+    }
+  }
+  // Every value loaded above passes through one of these waits, so the
+  // compiler sees it as available from here on and places no wait of its own
+  // later (such a wait would also hold up tile 1's copies).
+  auto retire = [&](auto& v) {
+    if (PIPE && nkt > 1)
+      asm volatile("s_waitcnt vmcnt(%1)" : "+v"(v) : "n"(kT1));
+    else
+      asm volatile("s_waitcnt vmcnt(0)" : "+v"(v));
+  };
 #pragma unroll
   for (int m = 0; m < MPW; ++m)
 #pragma unroll
-    for (int ks = 0; ks < KS; ks += 2) asm volatile("s_waitcnt vmcnt(0)" : "+v"(qf[m][ks]), "+v"(qf[m][ks + 1]));
-  asm volatile("" : "+v"(lgit));  // (retired by the wait above)
+    for (int ks = 0; ks < KS; ++ks) retire(qf[m][ks]);
+  if constexpr (V2) {
+    retire(lgit);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < LPL; ++i) retire(lv[j][i]);
+  }
 
   // ---- per-lane LDS bases (every stage / sub-block / map offset is an immediate) ----
   // K chunk (2ks + hg) of tile row r = 32 sb + li sits at chunk (2ks + hg) ^ k_swizzle(li)
@@ -639,7 +661,7 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
       constexpr int ZB = 32 * DV * 2, Z0 = C::VBASE + (C::NSTV - 1) * C::V_BYTES + 32 * (C::NSB - 1) * DV * 2;
       for (int i = tid * 16; i < ZB; i += NW * 64 * 16) *(uint4*)(smem + Z0 + i) = make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();  // K of tiles 0, 1 and V of tiles 0..NSTV-2 (issued, retired in the prologue) visible
+    __syncthreads();  // K and V of tile 0 visible (tile 1 is waited for at the first tile barrier)
     if (nsub > 0) Scur = qk(integral_constant<int, 0>{});
     auto tile_step = [&](int kt, auto kstage_c, auto vstage_c) {
       constexpr int SK = decltype(kstage_c)::value, SV = decltype(vstage_c)::value;
