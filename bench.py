@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the differential-attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline] [--softmax1]
 
 Headline workload (the `value`): the DIFF V1 causal forward at the GPT-2-small
 shape, B=8, T=1024, 6 differential heads, q/k head_dim 64, V width 128, bf16.
@@ -43,19 +43,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _caller(w, x, binding, torch):
-    """Return (fn(layer) -> None) that enqueues one call of workload w."""
+def _caller(w, x, binding, torch, softmax1=False):
+    """Return (fn(layer) -> None) that enqueues one call of workload w
+    (softmax1: the off-by-one softmax entry points)."""
     if w.kind == "v1":
         out = torch.empty((w.B, w.T, w.H, 2 * w.d), dtype=w.torch_dtype, device=x["v"].device)
         args = [x[n] for n in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")]
-        return lambda layer: binding.v1_fwd(*args, layer, out=out)
+        return lambda layer: binding.v1_fwd(*args, layer, out=out, softmax1=softmax1)
     if w.kind == "v2":
         out = torch.empty((w.B, w.T, w.Hq // 2, w.d), dtype=w.torch_dtype, device=x["v"].device)
-        return lambda layer: binding.v2_fwd(x["q"], x["k"], x["v"], x["lam"], out=out)
+        return lambda layer: binding.v2_fwd(x["q"], x["k"], x["v"], x["lam"], out=out, softmax1=softmax1)
     out = torch.empty((w.B, w.Hq // 2, w.d), dtype=w.torch_dtype, device=x["v"].device)
     ws = torch.empty(binding.v2_decode_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.d), dtype=torch.uint8,
                      device=x["v"].device)
-    return lambda layer: binding.v2_decode(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws)
+    return lambda layer: binding.v2_decode(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws,
+                                           softmax1=softmax1)
 
 
 def _timed(torch, call, layers, steps, warmup, graph=True):
@@ -119,7 +121,7 @@ def _roofline(w, launch_ms):
             "frac": round(a / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel_ms": round(avg_s * 1e3, 5)}
 
 
-def _cpu_baseline(w, x, min_seconds=10.0, max_seconds=30.0):
+def _cpu_baseline(w, x, min_seconds=10.0, max_seconds=30.0, softmax1=False):
     """Time the fp64 oracle on a bounded sample of the headline workload: whole
     layer calls (all rows of all heads) in the step's layer order, repeated
     until at least `min_seconds` of CPU work (stopping before `max_seconds`)."""
@@ -135,7 +137,7 @@ def _cpu_baseline(w, x, min_seconds=10.0, max_seconds=30.0):
     while t < min_seconds:
         layer = layers[calls % len(layers)]
         t0 = time.perf_counter()
-        oracle.v1_fwd(*args, layer)
+        oracle.v1_fwd(*args, layer, softmax1=softmax1)
         dt = time.perf_counter() - t0
         t += dt
         calls += 1
@@ -269,6 +271,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of replaying "
                     "a captured HIP graph of one step")
+    ap.add_argument("--softmax1", action="store_true",
+                    help="time the off-by-one softmax entry points (diffattn_*_softmax1) instead")
     ap.add_argument("--summarize", default=None, metavar="DIR",
                     help="summarise rocprofv3 CSV output in DIR (kernels matching --kernel) and exit")
     ap.add_argument("--kernel", default="", help="kernel-name substring for --summarize")
@@ -301,7 +305,7 @@ def main():
     def measure(name, steps, warmup, calls_per_step=None):
         w = workloads.WORKLOADS[name]
         x = workloads.inputs_for(w, dev)
-        call = _caller(w, x, binding, torch)
+        call = _caller(w, x, binding, torch, softmax1=args.softmax1)
         layers = list(w.layers) if w.layers else [0]
         if calls_per_step:  # repeat the layer list so one step holds several launches
             layers = (layers * calls_per_step)[:max(calls_per_step, len(layers))]
@@ -344,7 +348,7 @@ def main():
             torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = _cpu_baseline(w, x)
+        cpu = _cpu_baseline(w, x, softmax1=args.softmax1)
         log(json.dumps({"cpu_baseline": cpu}))
 
     line = {
@@ -361,7 +365,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) q/k/v, lambda vectors N(0,0.1) fp32; resident in HBM",
         "config": {"workload": HEADLINE, "kind": "DIFF V1 causal forward", "B": w.B, "T": w.T, "H": w.H,
-                   "d": w.d, "dv": 2 * w.d, "layers": "0..11 (one step = 12 calls)", "parallelism": "none"},
+                   "d": w.d, "dv": 2 * w.d, "layers": "0..11 (one step = 12 calls)", "parallelism": "none",
+                   "softmax": "off_by_one" if args.softmax1 else "standard"},
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "secondary": secondary,

@@ -12,6 +12,8 @@ Logical layouts (any strided view with a unit-stride last axis is accepted):
              returns / writes out [B,T,Hq/2,d]
   v2_decode  q [B,Hq,d]; k_cache, v_cache [B,L,Hkv,d]; lam [B,Hq/2] fp32;
              returns / writes out [B,Hq/2,d]
+Each takes ``softmax1=True`` for the off-by-one softmax entry points
+(``diffattn_*_softmax1``: every map's denominator gains exp(0)).
 """
 from __future__ import annotations
 
@@ -59,14 +61,18 @@ def load_library():
                            "(or __graft_entry__.build())")
     lib = ctypes.CDLL(str(_LIB_PATH))
     i, vp, fp = ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
-    lib.diffattn_v1_fwd.argtypes = [i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaIn, fp, fp, fp, fp, i, DaOut, vp]
-    lib.diffattn_v1_fwd.restype = i
-    lib.diffattn_v2_fwd.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaOut, vp]
-    lib.diffattn_v2_fwd.restype = i
+    for sfx in ("", "_softmax1"):
+        f = getattr(lib, "diffattn_v1_fwd" + sfx)
+        f.argtypes = [i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaIn, fp, fp, fp, fp, i, DaOut, vp]
+        f.restype = i
+        f = getattr(lib, "diffattn_v2_fwd" + sfx)
+        f.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaOut, vp]
+        f.restype = i
+        f = getattr(lib, "diffattn_v2_decode" + sfx)
+        f.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaOut, vp, ctypes.c_size_t, vp]
+        f.restype = i
     lib.diffattn_v2_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.diffattn_v2_decode_workspace_bytes.restype = ctypes.c_size_t
-    lib.diffattn_v2_decode.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaOut, vp, ctypes.c_size_t, vp]
-    lib.diffattn_v2_decode.restype = i
     lib.diffattn_lambda_init.argtypes = [i]
     lib.diffattn_lambda_init.restype = ctypes.c_double
     lib.diffattn_status_string.argtypes = [i]
@@ -113,7 +119,8 @@ def lambda_init(layer: int) -> float:
     return load_library().diffattn_lambda_init(int(layer))
 
 
-def v1_fwd(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, out: torch.Tensor | None = None):
+def v1_fwd(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, out: torch.Tensor | None = None,
+           softmax1: bool = False):
     """DIFF V1 forward; q*/k* [B,H,T,d], v [B,H,T,2d]; returns out [B,T,H,2d]."""
     lib = load_library()
     B, H, T, d = q1.shape
@@ -132,16 +139,17 @@ def v1_fwd(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, out: torch.Tensor 
     if out is None:
         out = torch.empty((B, T, H, 2 * d), dtype=q1.dtype, device=q1.device)
     _check_device(q1, q2, k1, k2, v, out, *lams)
-    st = lib.diffattn_v1_fwd(_dtype_code(q1), B, H, T, d,
+    name = "diffattn_v1_fwd" + ("_softmax1" if softmax1 else "")
+    st = getattr(lib, name)(_dtype_code(q1), B, H, T, d,
                              _in(q1, 0, 1, 2), _in(q2, 0, 1, 2), _in(k1, 0, 1, 2), _in(k2, 0, 1, 2),
                              _in(v, 0, 1, 2), *[x.data_ptr() for x in lams], int(layer),
                              _out(out, 0, 2, 1), _stream(q1))
     if st != 0:
-        raise DiffAttnError(st, "diffattn_v1_fwd")
+        raise DiffAttnError(st, name)
     return out
 
 
-def v2_fwd(q, k, v, lam, out: torch.Tensor | None = None):
+def v2_fwd(q, k, v, lam, out: torch.Tensor | None = None, softmax1: bool = False):
     """DIFF V2 prefill; q [B,T,Hq,d], k/v [B,T,Hkv,d], lam [B,T,Hq/2]; returns [B,T,Hq/2,d]."""
     lib = load_library()
     B, T, Hq, d = q.shape
@@ -153,10 +161,11 @@ def v2_fwd(q, k, v, lam, out: torch.Tensor | None = None):
     if out is None:
         out = torch.empty((B, T, Hq // 2, d), dtype=q.dtype, device=q.device)
     _check_device(q, k, v, out)
-    st = lib.diffattn_v2_fwd(_dtype_code(q), B, T, Hq, Hkv, d, _in(q, 0, 2, 1), _in(k, 0, 2, 1),
-                             _in(v, 0, 2, 1), _in(lam, 0, 2, 1), _out(out, 0, 2, 1), _stream(q))
+    name = "diffattn_v2_fwd" + ("_softmax1" if softmax1 else "")
+    st = getattr(lib, name)(_dtype_code(q), B, T, Hq, Hkv, d, _in(q, 0, 2, 1), _in(k, 0, 2, 1),
+                            _in(v, 0, 2, 1), _in(lam, 0, 2, 1), _out(out, 0, 2, 1), _stream(q))
     if st != 0:
-        raise DiffAttnError(st, "diffattn_v2_fwd")
+        raise DiffAttnError(st, name)
     return out
 
 
@@ -165,7 +174,7 @@ def v2_decode_workspace_bytes(B: int, L: int, Hq: int, Hkv: int, d: int) -> int:
 
 
 def v2_decode(q, k_cache, v_cache, lam, out: torch.Tensor | None = None,
-              workspace: torch.Tensor | None = None):
+              workspace: torch.Tensor | None = None, softmax1: bool = False):
     """DIFF V2 decode; q [B,Hq,d], caches [B,L,Hkv,d], lam [B,Hq/2]; returns [B,Hq/2,d]."""
     lib = load_library()
     B, Hq, d = q.shape
@@ -180,10 +189,11 @@ def v2_decode(q, k_cache, v_cache, lam, out: torch.Tensor | None = None,
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check_device(q, k_cache, v_cache, out)
-    st = lib.diffattn_v2_decode(_dtype_code(q), B, L, Hq, Hkv, d, _in(q, 0, 1, None),
-                                _in(k_cache, 0, 2, 1), _in(v_cache, 0, 2, 1), _in(lam, 0, 1, None),
-                                _out(out, 0, 1, None), workspace.data_ptr(),
-                                workspace.numel() * workspace.element_size(), _stream(q))
+    name = "diffattn_v2_decode" + ("_softmax1" if softmax1 else "")
+    st = getattr(lib, name)(_dtype_code(q), B, L, Hq, Hkv, d, _in(q, 0, 1, None),
+                            _in(k_cache, 0, 2, 1), _in(v_cache, 0, 2, 1), _in(lam, 0, 1, None),
+                            _out(out, 0, 1, None), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), _stream(q))
     if st != 0:
-        raise DiffAttnError(st, "diffattn_v2_decode")
+        raise DiffAttnError(st, name)
     return out

@@ -89,7 +89,8 @@ const char* diffattn_status_string(da_status s) {
   return "unknown status";
 }
 
-da_status diffattn_v1_fwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+static da_status v1_fwd_impl(int softmax1, da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2,
+                             da_in k1, da_in k2,
                           da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
                           const float* lam_k2, int layer_index, da_out out, void* stream) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
@@ -120,6 +121,7 @@ da_status diffattn_v1_fwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, 
     a.lam_init = li;
     a.sl2 = log2e_over_sqrt(d);
     a.B = B, a.T = T, a.H = H;
+    a.softmax1 = softmax1;
     return launch_status(da::launch_prefill_v1_bf16(d, a, s));
   }
   da::V1F32Args a{};
@@ -129,10 +131,12 @@ da_status diffattn_v1_fwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, 
   a.lam_init = li;
   a.sl2 = log2e_over_sqrt(d);
   a.B = B, a.H = H, a.T = T;
+  a.softmax1 = softmax1;
   return launch_status(da::launch_v1_fp32(d, a, s));
 }
 
-da_status diffattn_v2_fwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
+static da_status v2_fwd_impl(int softmax1, da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
+                             da_in v,
                           da_in lam, da_out out, void* stream) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1) return DA_E_SHAPE;
@@ -155,6 +159,7 @@ da_status diffattn_v2_fwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, 
   a.out = tout(out);
   a.sl2 = log2e_over_sqrt(d);
   a.B = B, a.T = T, a.H = Hkv, a.G = Hq / Hkv;
+  a.softmax1 = softmax1;
   return launch_status(da::launch_prefill_v2_bf16(d, a, (hipStream_t)stream));
 }
 
@@ -165,7 +170,8 @@ size_t diffattn_v2_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int d) 
   return (size_t)B * Hkv * sp.nsplit * (size_t)(Hq / Hkv) * (size_t)(d + 2) * sizeof(float);
 }
 
-da_status diffattn_v2_decode(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
+static da_status v2_decode_impl(int softmax1, da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
+                                da_in k_cache,
                              da_in v_cache, da_in lam, da_out out, void* workspace, size_t workspace_bytes,
                              void* stream) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
@@ -198,7 +204,47 @@ da_status diffattn_v2_decode(da_dtype dtype, int B, int L, int Hq, int Hkv, int 
   a.B = B, a.L = L, a.Hq = Hq, a.Hkv = Hkv, a.G = Hq / Hkv;
   a.chunk = sp.chunk;
   a.nsplit = sp.nsplit;
+  a.softmax1 = softmax1;
   return launch_status(da::launch_decode_bf16(d, a, (hipStream_t)stream));
+}
+
+da_status diffattn_v1_fwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+                          da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
+                          const float* lam_k2, int layer_index, da_out out, void* stream) {
+  return v1_fwd_impl(0, dtype, B, H, T, d, q1, q2, k1, k2, v, lam_q1, lam_k1, lam_q2, lam_k2, layer_index, out,
+                     stream);
+}
+
+da_status diffattn_v1_fwd_softmax1(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1,
+                                   da_in k2, da_in v, const float* lam_q1, const float* lam_k1,
+                                   const float* lam_q2, const float* lam_k2, int layer_index, da_out out,
+                                   void* stream) {
+  return v1_fwd_impl(1, dtype, B, H, T, d, q1, q2, k1, k2, v, lam_q1, lam_k1, lam_q2, lam_k2, layer_index, out,
+                     stream);
+}
+
+da_status diffattn_v2_fwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
+                          da_in lam, da_out out, void* stream) {
+  return v2_fwd_impl(0, dtype, B, T, Hq, Hkv, d, q, k, v, lam, out, stream);
+}
+
+da_status diffattn_v2_fwd_softmax1(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
+                                   da_in v, da_in lam, da_out out, void* stream) {
+  return v2_fwd_impl(1, dtype, B, T, Hq, Hkv, d, q, k, v, lam, out, stream);
+}
+
+da_status diffattn_v2_decode(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
+                             da_in v_cache, da_in lam, da_out out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return v2_decode_impl(0, dtype, B, L, Hq, Hkv, d, q, k_cache, v_cache, lam, out, workspace, workspace_bytes,
+                        stream);
+}
+
+da_status diffattn_v2_decode_softmax1(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
+                                      da_in k_cache, da_in v_cache, da_in lam, da_out out, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return v2_decode_impl(1, dtype, B, L, Hq, Hkv, d, q, k_cache, v_cache, lam, out, workspace, workspace_bytes,
+                        stream);
 }
 
 }  // extern "C"

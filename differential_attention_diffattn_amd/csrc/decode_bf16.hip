@@ -217,7 +217,8 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(const DecodeArgs a) {
       l += base[s * sstride + 1] * f;
       acc += base[s * sstride + 2 + c] * f;
     }
-    res[k] = acc / l;
+    // off-by-one softmax: one more logit 0, i.e. 2^(0 - M) against the merged max
+    res[k] = acc / (l + (a.softmax1 ? exp2f(-M) : 0.f));
   }
   const float lg = ((const float*)a.lam.p)[b * a.lam.sb + p * a.lam.sh];
   const float val = res[0] - sigmoid_f32(lg) * res[1];

@@ -30,6 +30,7 @@ struct PrefillArgs {
   int units_per_b; // work units per batch entry
   int tiles;       // token tiles per unit
   int nwg;         // workgroups in the grid
+  int softmax1;    // 1: off-by-one softmax (each map's denominator + exp(0))
 };
 
 hipError_t launch_prefill_v1_bf16(int d, const PrefillArgs& a, hipStream_t s);
@@ -47,6 +48,7 @@ struct V1F32Args {
   float sl2;
   int B, H, T;
   int tiles;
+  int softmax1;  // 1: off-by-one softmax (each map's denominator + exp(0))
 };
 hipError_t launch_v1_fp32(int d, const V1F32Args& a, hipStream_t s);
 
@@ -59,6 +61,7 @@ struct DecodeArgs {
   int B, L, Hq, Hkv, G;
   int chunk;   // tokens per split (multiple of 128)
   int nsplit;
+  int softmax1;  // 1: off-by-one softmax (each head's denominator + exp(0))
 };
 hipError_t launch_decode_bf16(int d, const DecodeArgs& a, hipStream_t s);
 

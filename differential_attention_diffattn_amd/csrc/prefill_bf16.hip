@@ -719,7 +719,11 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
   const int row = i0w + li;
   float inv[MPW];
 #pragma unroll
-  for (int m = 0; m < MPW; ++m) inv[m] = 1.f / (lsum[m] + __shfl_xor(lsum[m], 32, 64));
+  for (int m = 0; m < MPW; ++m) {
+    // off-by-one softmax: one more logit 0, i.e. 2^(0 - m) against the row's reference m
+    const float extra = a.softmax1 ? __builtin_amdgcn_exp2f(nm[m]) : 0.f;
+    inv[m] = 1.f / (lsum[m] + __shfl_xor(lsum[m], 32, 64) + extra);
+  }
   // weight of the second map: lam / l2 (V1) or sigmoid(lam[t, p]) / l_odd (V2)
   auto second_weight = [&](float inv2) {
     if constexpr (V2) {

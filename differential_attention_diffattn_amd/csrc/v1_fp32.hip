@@ -163,7 +163,8 @@ __global__ void __launch_bounds__(256) v1_fp32_kernel(const V1F32Args a) {
     }
   }
 
-  if (sm_kg == 0) sm.l[sm_m][sm_r] = l_run;
+  // off-by-one softmax: one more logit 0, i.e. 2^(0 - m) against the running max
+  if (sm_kg == 0) sm.l[sm_m][sm_r] = l_run + (a.softmax1 ? exp2f(-m_run) : 0.f);
   __syncthreads();
 
   const int row = i0 + pv_r;

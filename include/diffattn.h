@@ -163,6 +163,32 @@ da_status diffattn_v2_decode(da_dtype dtype, int B, int L, int Hq, int Hkv, int 
                              da_out out, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * Off-by-one softmax variants (Hacker News item 41780844: the comment that
+ * softmax "should be exp()/1+sum exp()", with 1 added to the denominator,
+ * and that adding an extra zero value to the logits does the same).  Each
+ * entry point computes exactly what its namesake above computes, with every
+ * softmax map replaced by
+ *     softmax1_j(x) = exp(x_j) / (1 + sum_k exp(x_k))
+ * over the same visible keys -- the same as one more key whose logit is 0
+ * for every query and whose value row is 0.  A row's attention weights then
+ * sum to less than 1 and tend to 0 when every logit is very negative.
+ * Arguments, layouts, validation, workspace and errors are those of the
+ * namesake.
+ */
+da_status diffattn_v1_fwd_softmax1(da_dtype dtype, int B, int H, int T, int d,
+                                   da_in q1, da_in q2, da_in k1, da_in k2, da_in v,
+                                   const float* lam_q1, const float* lam_k1,
+                                   const float* lam_q2, const float* lam_k2,
+                                   int layer_index, da_out out, void* stream);
+da_status diffattn_v2_fwd_softmax1(da_dtype dtype, int B, int T, int Hq, int Hkv, int d,
+                                   da_in q, da_in k, da_in v, da_in lam,
+                                   da_out out, void* stream);
+da_status diffattn_v2_decode_softmax1(da_dtype dtype, int B, int L, int Hq, int Hkv, int d,
+                                      da_in q, da_in k_cache, da_in v_cache, da_in lam,
+                                      da_out out, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
 /* lambda_init = 0.8 - 0.6*exp(-0.3*layer_index), as the V1 kernels use it
  * (computed on the host in double, handed to the device as float). */
 double diffattn_lambda_init(int layer_index);

@@ -65,15 +65,15 @@ def _configure(lib):
     lib.da_oracle_lambda_init.restype = ctypes.c_double
     lib.da_oracle_v1_lambda.argtypes = [i, dp, dp, dp, dp, i]
     lib.da_oracle_v1_lambda.restype = ctypes.c_double
-    lib.da_oracle_v1_fwd.argtypes = [i, i, i, i] + [dp] * 9 + [i, dp]
+    lib.da_oracle_v1_fwd.argtypes = [i, i, i, i] + [dp] * 9 + [i, i, dp]
     lib.da_oracle_v1_fwd.restype = None
-    lib.da_oracle_v1_rows.argtypes = [i, i, i, i] + [dp] * 9 + [i, ctypes.c_int64, ip, dp]
+    lib.da_oracle_v1_rows.argtypes = [i, i, i, i] + [dp] * 9 + [i, i, ctypes.c_int64, ip, dp]
     lib.da_oracle_v1_rows.restype = None
-    lib.da_oracle_v2_fwd.argtypes = [i, i, i, i, i] + [dp] * 5
+    lib.da_oracle_v2_fwd.argtypes = [i, i, i, i, i] + [dp] * 4 + [i, dp]
     lib.da_oracle_v2_fwd.restype = None
-    lib.da_oracle_v2_rows.argtypes = [i, i, i, i, i] + [dp] * 4 + [ctypes.c_int64, ip, dp]
+    lib.da_oracle_v2_rows.argtypes = [i, i, i, i, i] + [dp] * 4 + [i, ctypes.c_int64, ip, dp]
     lib.da_oracle_v2_rows.restype = None
-    lib.da_oracle_v2_decode.argtypes = [i, i, i, i, i] + [dp] * 5
+    lib.da_oracle_v2_decode.argtypes = [i, i, i, i, i] + [dp] * 4 + [i, dp]
     lib.da_oracle_v2_decode.restype = None
     lib.da_oracle_set_threads.argtypes = [i]
     lib.da_oracle_set_threads.restype = i
@@ -115,16 +115,17 @@ def _v1_check(q1, q2, k1, k2, v, lams):
     return B, H, T, d
 
 
-def v1_fwd(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int) -> np.ndarray:
-    """DIFF V1 forward, all rows; returns ``[B, T, H, 2d]`` float64."""
+def v1_fwd(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, softmax1: bool = False) -> np.ndarray:
+    """DIFF V1 forward, all rows; returns ``[B, T, H, 2d]`` float64.
+    ``softmax1``: the off-by-one softmax (denominator + exp(0)) in both maps."""
     t = [_f64(x) for x in (q1, q2, k1, k2, v, lq1, lk1, lq2, lk2)]
     B, H, T, d = _v1_check(*t[:5], t[5:])
     out = np.zeros((B, T, H, 2 * d), dtype=np.float64)
-    _load().da_oracle_v1_fwd(B, H, T, d, *[_p(x) for x in t], int(layer), _p(out))
+    _load().da_oracle_v1_fwd(B, H, T, d, *[_p(x) for x in t], int(layer), int(bool(softmax1)), _p(out))
     return out
 
 
-def v1_rows(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, bhi) -> np.ndarray:
+def v1_rows(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, bhi, softmax1: bool = False) -> np.ndarray:
     """DIFF V1 forward for rows ``bhi`` (an ``[n, 3]`` array of (b, h, i));
     returns ``[n, 2d]`` float64."""
     t = [_f64(x) for x in (q1, q2, k1, k2, v, lq1, lk1, lq2, lk2)]
@@ -132,7 +133,7 @@ def v1_rows(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, bhi) -> np.ndarra
     idx = np.ascontiguousarray(np.asarray(bhi, dtype=np.int64).reshape(-1, 3))
     assert (idx[:, 0] < B).all() and (idx[:, 1] < H).all() and (idx[:, 2] < T).all()
     out = np.zeros((idx.shape[0], 2 * d), dtype=np.float64)
-    _load().da_oracle_v1_rows(B, H, T, d, *[_p(x) for x in t], int(layer), idx.shape[0],
+    _load().da_oracle_v1_rows(B, H, T, d, *[_p(x) for x in t], int(layer), int(bool(softmax1)), idx.shape[0],
                               idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _p(out))
     return out
 
@@ -153,31 +154,31 @@ def _v2_check(q, k, v, lam, decode: bool):
     return B, T, Hq, Hkv, d
 
 
-def v2_fwd(q, k, v, lam) -> np.ndarray:
+def v2_fwd(q, k, v, lam, softmax1: bool = False) -> np.ndarray:
     """DIFF V2 prefill, all rows; returns ``[B, T, Hq/2, d]`` float64."""
     t = [_f64(x) for x in (q, k, v, lam)]
     B, T, Hq, Hkv, d = _v2_check(*t, decode=False)
     out = np.zeros((B, T, Hq // 2, d), dtype=np.float64)
-    _load().da_oracle_v2_fwd(B, T, Hq, Hkv, d, *[_p(x) for x in t], _p(out))
+    _load().da_oracle_v2_fwd(B, T, Hq, Hkv, d, *[_p(x) for x in t], int(bool(softmax1)), _p(out))
     return out
 
 
-def v2_rows(q, k, v, lam, btp) -> np.ndarray:
+def v2_rows(q, k, v, lam, btp, softmax1: bool = False) -> np.ndarray:
     """DIFF V2 prefill for rows ``btp`` (``[n, 3]`` of (b, t, pair))."""
     t = [_f64(x) for x in (q, k, v, lam)]
     B, T, Hq, Hkv, d = _v2_check(*t, decode=False)
     idx = np.ascontiguousarray(np.asarray(btp, dtype=np.int64).reshape(-1, 3))
     assert (idx[:, 0] < B).all() and (idx[:, 1] < T).all() and (idx[:, 2] < Hq // 2).all()
     out = np.zeros((idx.shape[0], d), dtype=np.float64)
-    _load().da_oracle_v2_rows(B, T, Hq, Hkv, d, *[_p(x) for x in t], idx.shape[0],
+    _load().da_oracle_v2_rows(B, T, Hq, Hkv, d, *[_p(x) for x in t], int(bool(softmax1)), idx.shape[0],
                               idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _p(out))
     return out
 
 
-def v2_decode(q, k, v, lam) -> np.ndarray:
+def v2_decode(q, k, v, lam, softmax1: bool = False) -> np.ndarray:
     """DIFF V2 decode; returns ``[B, Hq/2, d]`` float64."""
     t = [_f64(x) for x in (q, k, v, lam)]
     B, L, Hq, Hkv, d = _v2_check(*t, decode=True)
     out = np.zeros((B, Hq // 2, d), dtype=np.float64)
-    _load().da_oracle_v2_decode(B, L, Hq, Hkv, d, *[_p(x) for x in t], _p(out))
+    _load().da_oracle_v2_decode(B, L, Hq, Hkv, d, *[_p(x) for x in t], int(bool(softmax1)), _p(out))
     return out

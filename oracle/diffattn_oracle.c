@@ -47,22 +47,26 @@ static double sigmoid(double x) {
  * of [V2A] and [NGI], written out):
  *   s_j = q . k_j / sqrt(d)          for j = 0 .. nkeys-1 (the caller passes
  *                                    only the keys the query may see)
- *   w_j = exp(s_j - max_j s_j),  Z = sum_j w_j
+ *   w_j = exp(s_j - M),  Z = sum_j w_j,  M = max_j s_j
  *   out[c] = sum_j w_j v_j[c] / Z    for c < dv
+ * With softmax1 set, the off-by-one softmax of the [HN] comment "softmax
+ * should be exp()/(1+sum exp())": the denominator gains exp(0), the same as
+ * one more logit 0 whose value row is 0.  M then also covers that logit,
+ * M = max(0, max_j s_j), and Z gains exp(0 - M).
  * k_j is at k + j*kstride, v_j at v + j*vstride.  w is caller scratch of
  * nkeys doubles.
  */
 static void softmax_attention_row(int d, int dv, int nkeys, const double* q,
                                   const double* k, int64_t kstride,
                                   const double* v, int64_t vstride,
-                                  double* w, double* out) {
+                                  int softmax1, double* w, double* out) {
     const double scale = 1.0 / sqrt((double)d);
-    double m = -INFINITY;
+    double m = softmax1 ? 0.0 : -INFINITY;
     for (int j = 0; j < nkeys; ++j) {
         w[j] = dot(d, q, k + (int64_t)j * kstride) * scale;
         if (w[j] > m) m = w[j];
     }
-    double z = 0.0;
+    double z = softmax1 ? exp(0.0 - m) : 0.0;
     for (int j = 0; j < nkeys; ++j) {
         w[j] = exp(w[j] - m);
         z += w[j];
@@ -76,7 +80,7 @@ static void softmax_attention_row(int d, int dv, int nkeys, const double* q,
 }
 
 /*
- * One V1 output row (b, h, i), following [V2A] DiffAttnV1 line by line:
+ * One V1 output row (b, h, i), the steps of [V2A] DiffAttnV1 in their order:
  *   attn1 = attention(q1, k1, v), attn2 = attention(q2, k2, v)   (causal)
  *   attn  = attn1 - lam * attn2
  *   attn  = rmsnorm(attn)     -- over the 2d channels, eps 1e-5 inside the
@@ -85,7 +89,7 @@ static void softmax_attention_row(int d, int dv, int nkeys, const double* q,
  */
 static void v1_row(int H, int T, int d, const double* q1, const double* q2,
                    const double* k1, const double* k2, const double* v,
-                   double lam, double lam_init, int b, int h, int i,
+                   double lam, double lam_init, int softmax1, int b, int h, int i,
                    double* w, double* a1, double* a2, double* dst) {
     const int dv = 2 * d;
     const int64_t bh = (int64_t)b * H + h;
@@ -94,8 +98,8 @@ static void v1_row(int H, int T, int d, const double* q1, const double* q2,
     const double* k1h = k1 + bh * T * d;
     const double* k2h = k2 + bh * T * d;
     const double* vh = v + bh * T * dv;
-    softmax_attention_row(d, dv, i + 1, q1i, k1h, d, vh, dv, w, a1);
-    softmax_attention_row(d, dv, i + 1, q2i, k2h, d, vh, dv, w, a2);
+    softmax_attention_row(d, dv, i + 1, q1i, k1h, d, vh, dv, softmax1, w, a1);
+    softmax_attention_row(d, dv, i + 1, q2i, k2h, d, vh, dv, softmax1, w, a2);
     double ms = 0.0;
     for (int c = 0; c < dv; ++c) {
         a1[c] = a1[c] - lam * a2[c];
@@ -110,7 +114,7 @@ void da_oracle_v1_fwd(int B, int H, int T, int d, const double* q1,
                       const double* q2, const double* k1, const double* k2,
                       const double* v, const double* lq1, const double* lk1,
                       const double* lq2, const double* lk2, int layer,
-                      double* out) {
+                      int softmax1, double* out) {
     const double lam = da_oracle_v1_lambda(d, lq1, lk1, lq2, lk2, layer);
     const double li = da_oracle_lambda_init(layer);
     const int dv = 2 * d;
@@ -126,7 +130,7 @@ void da_oracle_v1_fwd(int B, int H, int T, int d, const double* q1,
             const int h = (int)((r / T) % H);
             const int b = (int)(r / ((int64_t)T * H));
             double* dst = out + (((int64_t)b * T + i) * H + h) * dv;
-            v1_row(H, T, d, q1, q2, k1, k2, v, lam, li, b, h, i, w, a1, a2, dst);
+            v1_row(H, T, d, q1, q2, k1, k2, v, lam, li, softmax1, b, h, i, w, a1, a2, dst);
         }
         free(w);
         free(a1);
@@ -138,7 +142,7 @@ void da_oracle_v1_rows(int B, int H, int T, int d, const double* q1,
                        const double* q2, const double* k1, const double* k2,
                        const double* v, const double* lq1, const double* lk1,
                        const double* lq2, const double* lk2, int layer,
-                       int64_t n, const int64_t* bhi, double* out_rows) {
+                       int softmax1, int64_t n, const int64_t* bhi, double* out_rows) {
     (void)B;
     const double lam = da_oracle_v1_lambda(d, lq1, lk1, lq2, lk2, layer);
     const double li = da_oracle_lambda_init(layer);
@@ -150,7 +154,7 @@ void da_oracle_v1_rows(int B, int H, int T, int d, const double* q1,
         double* a2 = (double*)malloc(sizeof(double) * (size_t)dv);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t r = 0; r < n; ++r) {
-            v1_row(H, T, d, q1, q2, k1, k2, v, lam, li, (int)bhi[3 * r],
+            v1_row(H, T, d, q1, q2, k1, k2, v, lam, li, softmax1, (int)bhi[3 * r],
                    (int)bhi[3 * r + 1], (int)bhi[3 * r + 2], w, a1, a2,
                    out_rows + r * dv);
         }
@@ -161,7 +165,7 @@ void da_oracle_v1_rows(int B, int H, int T, int d, const double* q1,
 }
 
 /*
- * One V2 output row (b, t, p), following [V2A] DiffAttnV2: one attention
+ * One V2 output row (b, t, p), the steps of [V2A] DiffAttnV2: one attention
  * over all Hq query heads, heads of a GQA group contiguous so head h reads
  * kv head g = h / (Hq/Hkv); the output pairs adjacent heads,
  *   attn1 = attn[:, 0::2], attn2 = attn[:, 1::2]
@@ -171,23 +175,23 @@ void da_oracle_v1_rows(int B, int H, int T, int d, const double* q1,
  */
 static void v2_row(int Hq, int Hkv, int d, int nkeys, const double* qrow,
                    const double* kb, const double* vb, double lam_logit,
-                   int p, double* w, double* a_even, double* a_odd,
+                   int p, int softmax1, double* w, double* a_even, double* a_odd,
                    double* dst) {
     const int group = Hq / Hkv;
     const int he = 2 * p, ho = 2 * p + 1;
     const int ge = he / group, go = ho / group;
     const int64_t kvstride = (int64_t)Hkv * d; /* token stride in k, v */
     softmax_attention_row(d, d, nkeys, qrow + (int64_t)he * d, kb + (int64_t)ge * d,
-                          kvstride, vb + (int64_t)ge * d, kvstride, w, a_even);
+                          kvstride, vb + (int64_t)ge * d, kvstride, softmax1, w, a_even);
     softmax_attention_row(d, d, nkeys, qrow + (int64_t)ho * d, kb + (int64_t)go * d,
-                          kvstride, vb + (int64_t)go * d, kvstride, w, a_odd);
+                          kvstride, vb + (int64_t)go * d, kvstride, softmax1, w, a_odd);
     const double s = sigmoid(lam_logit);
     for (int c = 0; c < d; ++c) dst[c] = a_even[c] - s * a_odd[c];
 }
 
 void da_oracle_v2_fwd(int B, int T, int Hq, int Hkv, int d, const double* q,
                       const double* k, const double* v, const double* lam,
-                      double* out) {
+                      int softmax1, double* out) {
     const int P = Hq / 2;
     const int64_t nrows = (int64_t)B * T * P;
 #pragma omp parallel
@@ -204,7 +208,7 @@ void da_oracle_v2_fwd(int B, int T, int Hq, int Hkv, int d, const double* q,
             const double* kb = k + (int64_t)b * T * Hkv * d;
             const double* vb = v + (int64_t)b * T * Hkv * d;
             const double lg = lam[((int64_t)b * T + t) * P + p];
-            v2_row(Hq, Hkv, d, t + 1, qrow, kb, vb, lg, p, w, ae, ao,
+            v2_row(Hq, Hkv, d, t + 1, qrow, kb, vb, lg, p, softmax1, w, ae, ao,
                    out + (((int64_t)b * T + t) * P + p) * d);
         }
         free(w);
@@ -215,7 +219,7 @@ void da_oracle_v2_fwd(int B, int T, int Hq, int Hkv, int d, const double* q,
 
 void da_oracle_v2_rows(int B, int T, int Hq, int Hkv, int d, const double* q,
                        const double* k, const double* v, const double* lam,
-                       int64_t n, const int64_t* btp, double* out_rows) {
+                       int softmax1, int64_t n, const int64_t* btp, double* out_rows) {
     (void)B;
     const int P = Hq / 2;
 #pragma omp parallel
@@ -231,7 +235,7 @@ void da_oracle_v2_rows(int B, int T, int Hq, int Hkv, int d, const double* q,
             const double* kb = k + (int64_t)b * T * Hkv * d;
             const double* vb = v + (int64_t)b * T * Hkv * d;
             const double lg = lam[((int64_t)b * T + t) * P + p];
-            v2_row(Hq, Hkv, d, t + 1, qrow, kb, vb, lg, p, w, ae, ao,
+            v2_row(Hq, Hkv, d, t + 1, qrow, kb, vb, lg, p, softmax1, w, ae, ao,
                    out_rows + r * d);
         }
         free(w);
@@ -242,7 +246,7 @@ void da_oracle_v2_rows(int B, int T, int Hq, int Hkv, int d, const double* q,
 
 void da_oracle_v2_decode(int B, int L, int Hq, int Hkv, int d,
                          const double* q, const double* k, const double* v,
-                         const double* lam, double* out) {
+                         const double* lam, int softmax1, double* out) {
     const int P = Hq / 2;
     const int64_t nrows = (int64_t)B * P;
 #pragma omp parallel
@@ -257,7 +261,7 @@ void da_oracle_v2_decode(int B, int L, int Hq, int Hkv, int d,
             const double* qrow = q + (int64_t)b * Hq * d;
             const double* kb = k + (int64_t)b * L * Hkv * d;
             const double* vb = v + (int64_t)b * L * Hkv * d;
-            v2_row(Hq, Hkv, d, L, qrow, kb, vb, lam[(int64_t)b * P + p], p, w,
+            v2_row(Hq, Hkv, d, L, qrow, kb, vb, lam[(int64_t)b * P + p], p, softmax1, w,
                    ae, ao, out + ((int64_t)b * P + p) * d);
         }
         free(w);

@@ -23,7 +23,13 @@
  *          notlober's module (explicit masked score maps, adjacent heads
  *          paired, one V of width 2*head_dim per differential head).
  *   [HN]   Hacker News item 41780844 comments: the lambda_init expression
- *          0.8 - 0.6*exp(-0.3*depth).
+ *          0.8 - 0.6*exp(-0.3*depth), and the comment that softmax should be
+ *          exp()/(1 + sum exp()) ("off-by-one" softmax, the same as one extra
+ *          logit 0).
+ *
+ * softmax1 (every attention function): 0 = the standard softmax; 1 = the
+ * off-by-one softmax, each map's denominator gaining exp(0) -- equivalently
+ * one more key at logit 0 whose value row is 0.
  */
 #ifndef DIFFATTN_ORACLE_H
 #define DIFFATTN_ORACLE_H
@@ -57,7 +63,7 @@ void da_oracle_v1_fwd(int B, int H, int T, int d,
                       const double* k1, const double* k2, const double* v,
                       const double* lq1, const double* lk1,
                       const double* lq2, const double* lk2,
-                      int layer, double* out);
+                      int layer, int softmax1, double* out);
 
 /* DIFF V1 forward for selected rows only: row r is (b, h, i) =
  * (bhi[3r], bhi[3r+1], bhi[3r+2]); out_rows is [n][2d].  Same layouts as
@@ -67,7 +73,7 @@ void da_oracle_v1_rows(int B, int H, int T, int d,
                        const double* k1, const double* k2, const double* v,
                        const double* lq1, const double* lk1,
                        const double* lq2, const double* lk2,
-                       int layer, int64_t n, const int64_t* bhi,
+                       int layer, int softmax1, int64_t n, const int64_t* bhi,
                        double* out_rows);
 
 /* DIFF V2 prefill, every row.
@@ -80,13 +86,13 @@ void da_oracle_v1_rows(int B, int H, int T, int d,
  * [V2A] DiffAttnV2 and the GQA-layout note. */
 void da_oracle_v2_fwd(int B, int T, int Hq, int Hkv, int d,
                       const double* q, const double* k, const double* v,
-                      const double* lam, double* out);
+                      const double* lam, int softmax1, double* out);
 
 /* DIFF V2 prefill for selected rows: row r is (b, t, p) = btp[3r..3r+2];
  * out_rows is [n][d]. */
 void da_oracle_v2_rows(int B, int T, int Hq, int Hkv, int d,
                        const double* q, const double* k, const double* v,
-                       const double* lam, int64_t n, const int64_t* btp,
+                       const double* lam, int softmax1, int64_t n, const int64_t* btp,
                        double* out_rows);
 
 /* DIFF V2 decode: one new query token per sequence against a cache that
@@ -98,7 +104,7 @@ void da_oracle_v2_rows(int B, int T, int Hq, int Hkv, int d,
  * [V2A] DiffAttnV2 applied to the last position (the decoding paragraph). */
 void da_oracle_v2_decode(int B, int L, int Hq, int Hkv, int d,
                          const double* q, const double* k, const double* v,
-                         const double* lam, double* out);
+                         const double* lam, int softmax1, double* out);
 
 /* Threads the library's OpenMP loops may use (0 = OpenMP default).  Returns
  * the count that will be used. */

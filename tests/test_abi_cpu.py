@@ -31,6 +31,7 @@ def _declared_symbols():
 def test_header_declares_the_entry_points():
     syms = _declared_symbols()
     for need in ("diffattn_v1_fwd", "diffattn_v2_fwd", "diffattn_v2_decode",
+                 "diffattn_v1_fwd_softmax1", "diffattn_v2_fwd_softmax1", "diffattn_v2_decode_softmax1",
                  "diffattn_v2_decode_workspace_bytes", "diffattn_status_string"):
         assert need in syms
 
@@ -128,3 +129,19 @@ def test_decode_validation(lib):
     assert _dec(lib, ws=0) == E_WS
     assert _dec(lib, ws=FAKE + 4) == E_WS
     assert _dec(lib, wsb=100) == E_WS
+
+
+def test_softmax1_entry_points_validate_like_their_namesakes(lib):
+    """The off-by-one softmax entry points share their namesakes' argument
+    checks: the same invalid calls return the same status, before any launch."""
+    v1 = lambda f, **kw: f(kw.get("dtype", 1), 1, 2, kw.get("T", 16), kw.get("d", 64), _t(), _t(), _t(), _t(),
+                           _t(), kw.get("lam", FAKE), FAKE, FAKE, FAKE, 0, _t(out=True), None)
+    for kw in ({"dtype": 7}, {"T": 0}, {"lam": 0}, {"d": 96}):
+        assert v1(lib.diffattn_v1_fwd_softmax1, **kw) == v1(lib.diffattn_v1_fwd, **kw) != OK
+    v2 = lambda f, **kw: f(kw.get("dtype", 1), 1, 16, kw.get("Hq", 8), 2, 128, _t(), _t(), _t(), _t(),
+                           _t(out=True), None)
+    for kw in ({"dtype": 3}, {"Hq": 6}, {"dtype": 0}):
+        assert v2(lib.diffattn_v2_fwd_softmax1, **kw) == v2(lib.diffattn_v2_fwd, **kw) != OK
+    need = lib.diffattn_v2_decode_workspace_bytes(2, 100, 8, 2, 128)
+    dec = lambda f, ws: f(1, 2, 100, 8, 2, 128, _t(), _t(), _t(), _t(), _t(out=True), ws, need, None)
+    assert dec(lib.diffattn_v2_decode_softmax1, 0) == dec(lib.diffattn_v2_decode, 0) == E_WS

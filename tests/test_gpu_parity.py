@@ -28,8 +28,8 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _v1_run(x, layer, out=None):
-    o = binding.v1_fwd(*[x[n] for n in V1_NAMES], layer, out=out)
+def _v1_run(x, layer, out=None, softmax1=False):
+    o = binding.v1_fwd(*[x[n] for n in V1_NAMES], layer, out=out, softmax1=softmax1)
     torch.cuda.synchronize()
     return o
 
@@ -84,6 +84,27 @@ def test_v1_fp32_peaked_scores():
         x[n].mul_(6)
     out = _v1_run(x, 2)
     assert_fp32_close(out, oracle.v1_fwd(*_v1_cpu(x), 2), "fp32 peaked")
+
+
+def _rising(k, slope):
+    """k[..., j, 0] = slope * j along the token axis (axis -2 of [.., T, d])."""
+    T = k.shape[-2]
+    k[..., 0] = (slope * torch.arange(T, device=k.device, dtype=torch.float32)).to(k.dtype)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_v1_rising_scores_rescale_every_block(d):
+    """Scores that grow with the key index: every 32-key block raises each
+    row's maximum by ~12 log2 units, so the exact rescale path runs on
+    nearly every block (and on both lane halves)."""
+    x = workloads.v1_inputs(2, 2, 300, d, torch.bfloat16, seed=270 + d, device=DEV)
+    s = math.sqrt(d) / 8.0
+    for n in ("q1", "q2"):
+        x[n][..., 0] = 8.0 * s
+    for n in ("k1", "k2"):
+        _rising(x[n], 0.26)
+    out = _v1_run(x, 5)
+    assert_bf16_close(out, oracle.v1_fwd(*_v1_cpu(x), 5), f"rising d{d}")
 
 
 def test_v1_bf16_gpt2small_full():
@@ -207,8 +228,8 @@ def test_v1_error_leaves_output_untouched():
 
 # ------------------------------------------------------------------ V2 prefill
 
-def _v2_run(y, out=None):
-    o = binding.v2_fwd(y["q"], y["k"], y["v"], y["lam"], out=out)
+def _v2_run(y, out=None, softmax1=False):
+    o = binding.v2_fwd(y["q"], y["k"], y["v"], y["lam"], out=out, softmax1=softmax1)
     torch.cuda.synchronize()
     return o
 
@@ -234,6 +255,16 @@ def test_v2_peaked_scores(d):
     y["k"].mul_(6)
     out = _v2_run(y)
     assert_bf16_close(out, oracle.v2_fwd(*_v2_cpu(y)), f"v2 peaked d{d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_v2_rising_scores_rescale_every_block(d):
+    y = workloads.v2_inputs(1, 300, 8, 2, d, torch.bfloat16, seed=370 + d, device=DEV)
+    y["q"][..., 0] = 12.0 * math.sqrt(d) / math.sqrt(128)
+    k = y["k"].transpose(1, 2)  # [B, Hkv, T, d] view
+    _rising(k, 0.26)
+    out = _v2_run(y)
+    assert_bf16_close(out, oracle.v2_fwd(*_v2_cpu(y)), f"v2 rising d{d}")
 
 
 def test_v2_gate_limits():
@@ -276,8 +307,8 @@ def test_v2_prefix_mean_closed_form_full_size():
 
 # ------------------------------------------------------------------ V2 decode
 
-def _dec_run(z, out=None, ws=None):
-    o = binding.v2_decode(z["q"], z["k"], z["v"], z["lam"], out=out, workspace=ws)
+def _dec_run(z, out=None, ws=None, softmax1=False):
+    o = binding.v2_decode(z["q"], z["k"], z["v"], z["lam"], out=out, workspace=ws, softmax1=softmax1)
     torch.cuda.synchronize()
     return o
 
@@ -302,6 +333,15 @@ def test_decode_peaked_scores(d):
     z["k"].mul_(6)
     out = _dec_run(z)
     assert_bf16_close(out, oracle.v2_decode(*_dec_cpu(z)), f"decode peaked d{d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_rising_scores_rescale_every_block(d):
+    z = workloads.decode_inputs(2, 1000, 16, 2, d, torch.bfloat16, seed=470 + d, device=DEV)
+    z["q"][..., 0] = 12.0 * math.sqrt(d) / math.sqrt(128)
+    _rising(z["k"].transpose(1, 2), 0.26)
+    out = _dec_run(z)
+    assert_bf16_close(out, oracle.v2_decode(*_dec_cpu(z)), f"decode rising d{d}")
 
 
 def test_decode_equals_last_prefill_row():
@@ -349,6 +389,94 @@ def test_decode_prefix_mean_closed_form_full_size():
 
 
 # ------------------------------------------------------------------ HIP graphs
+
+# ------------------------------------------------------- off-by-one softmax
+# (every map's denominator + exp(0); Hacker News item 41780844)
+
+@pytest.mark.parametrize("d,T", [(64, 1), (64, 33), (64, 300), (128, 33), (128, 300)])
+def test_softmax1_v1_bf16(d, T):
+    """(Layer 0: lambda ~ 0.2.  With lambda near 1 a row whose two maps agree
+    -- e.g. row 1, two visible keys -- has D = A1 V - lambda A2 V cancel, and
+    the RMSNorm magnifies the 2^-9 rounding of the bf16 probabilities by
+    |A1 V| / |D|; at this seed at layer 4 one such row (lambda = 1.006,
+    factor 51) exceeds the tolerance for the standard and the off-by-one
+    softmax alike.)"""
+    x = workloads.v1_inputs(2, 3, T, d, torch.bfloat16, seed=500 + d + T, device=DEV)
+    out = _v1_run(x, 0, softmax1=True)
+    assert_bf16_close(out, oracle.v1_fwd(*_v1_cpu(x), 0, softmax1=True), f"softmax1 v1 d{d} T{T}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_softmax1_v1_bf16_peaked_and_rising(d):
+    x = workloads.v1_inputs(2, 2, 300, d, torch.bfloat16, seed=520 + d, device=DEV)
+    for n in ("q1", "q2", "k1", "k2"):
+        x[n].mul_(6)
+    assert_bf16_close(_v1_run(x, 2, softmax1=True), oracle.v1_fwd(*_v1_cpu(x), 2, softmax1=True), "peaked")
+    x = workloads.v1_inputs(2, 2, 300, d, torch.bfloat16, seed=530 + d, device=DEV)
+    for n in ("q1", "q2"):
+        x[n][..., 0] = math.sqrt(d)
+    for n in ("k1", "k2"):
+        _rising(x[n], 0.26)
+    assert_bf16_close(_v1_run(x, 5, softmax1=True), oracle.v1_fwd(*_v1_cpu(x), 5, softmax1=True), "rising")
+
+
+@pytest.mark.parametrize("d,T", [(32, 33), (64, 200), (128, 33)])
+def test_softmax1_v1_fp32(d, T):
+    x = workloads.v1_inputs(2, 2, T, d, torch.float32, seed=540 + d + T, device=DEV)
+    out = _v1_run(x, 7, softmax1=True)
+    assert_fp32_close(out, oracle.v1_fwd(*_v1_cpu(x), 7, softmax1=True), f"softmax1 fp32 d{d} T{T}")
+
+
+@pytest.mark.parametrize("G,d,T", [(2, 128, 1), (8, 128, 150), (8, 64, 150), (4, 128, 33)])
+def test_softmax1_v2(G, d, T):
+    y = workloads.v2_inputs(2, T, 2 * G, 2, d, torch.bfloat16, seed=550 + G + d + T, device=DEV)
+    out = _v2_run(y, softmax1=True)
+    assert_bf16_close(out, oracle.v2_fwd(*_v2_cpu(y), softmax1=True), f"softmax1 v2 G{G} d{d} T{T}")
+
+
+def test_softmax1_v2_very_negative_logits():
+    """Every visible score strongly negative: the off-by-one weights (and the
+    output) shrink towards 0 while the standard softmax still averages V."""
+    y = workloads.v2_inputs(1, 150, 8, 1, 128, torch.bfloat16, seed=560, device=DEV)
+    y["k"].zero_()
+    y["k"][..., 0] = 1.0
+    y["q"].zero_()
+    y["q"][..., 0] = -6.0 * math.sqrt(128)  # score -6 everywhere
+    out = _v2_run(y, softmax1=True)
+    ref = oracle.v2_fwd(*_v2_cpu(y), softmax1=True)
+    assert_bf16_close(out, ref, "softmax1 negative logits")
+    assert np.abs(ref[:, :8]).max() < 0.05  # first rows: n e^-6 / (1 + n e^-6) is small
+
+
+def test_softmax1_v2_full_sampled():
+    w = WORKLOADS["v2_prefill_B1_T8192_Hq64_Hkv8_d128"]
+    y = workloads.inputs_for(w, DEV)
+    out = _v2_run(y, softmax1=True)
+    rng = np.random.default_rng(3)
+    n = 64
+    btp = np.stack([np.zeros(n, dtype=np.int64), rng.integers(0, w.T, n), rng.integers(0, w.Hq // 2, n)], 1)
+    btp[:4, 1] = [0, 1, 32, w.T - 1]
+    ref = oracle.v2_rows(*_v2_cpu(y), btp, softmax1=True)
+    got = host64(out)[btp[:, 0], btp[:, 1], btp[:, 2]]
+    assert_bf16_close(got, ref, "softmax1 " + w.name)
+    assert rel_l2(got, ref, axis=-1).max() < 3e-2
+
+
+@pytest.mark.parametrize("L,G,d", [(1, 8, 128), (33, 2, 128), (1000, 8, 64), (5000, 16, 128)])
+def test_softmax1_decode(L, G, d):
+    z = workloads.decode_inputs(2, L, G * 2, 2, d, torch.bfloat16, seed=570 + L + G + d, device=DEV)
+    out = _dec_run(z, softmax1=True)
+    assert_bf16_close(out, oracle.v2_decode(*_dec_cpu(z), softmax1=True), f"softmax1 decode L{L}")
+
+
+def test_softmax1_decode_equals_last_prefill_row():
+    B, L, Hq, Hkv, d = 1, 600, 16, 2, 128
+    y = workloads.v2_inputs(B, L, Hq, Hkv, d, torch.bfloat16, seed=580, device=DEV)
+    pre = _v2_run(y, softmax1=True)
+    z = {"q": y["q"][:, -1].contiguous(), "k": y["k"], "v": y["v"], "lam": y["lam"][:, -1].contiguous()}
+    dec = _dec_run(z, softmax1=True)
+    assert_bf16_close(dec, host64(pre[:, -1]), "softmax1 decode vs prefill last row")
+
 
 def test_graph_replay_matches_eager():
     """The benchmark replays one step captured as a HIP graph (12 V1 layer

@@ -48,6 +48,10 @@ MUTATIONS = {
     "gqa_mod": ("const int ge = he / group, go = ho / group;", "const int ge = he % Hkv, go = ho % Hkv;"),
     # decode: the newest cache entry is not seen
     "decode_drops_last": ("v2_row(Hq, Hkv, d, L, qrow", "v2_row(Hq, Hkv, d, L - 1, qrow"),
+    # off-by-one softmax: the extra exp(0) term dropped
+    "softmax1_ignored": ("double z = softmax1 ? exp(0.0 - m) : 0.0;", "double z = 0.0;"),
+    # off-by-one softmax: the extra term added without the max shift
+    "softmax1_unshifted": ("double z = softmax1 ? exp(0.0 - m) : 0.0;", "double z = softmax1 ? 1.0 : 0.0;"),
 }
 
 PINS = [
@@ -67,6 +71,8 @@ PINS = [
     lambda: pins.test_v1_matches_bruteforce.hypothesis.inner_test(B=2, H=2, T=16, d=8, layer=5, seed=1),
     lambda: pins.test_v2_matches_bruteforce.hypothesis.inner_test(B=1, T=16, Hkv=2, G=4, d=8, seed=2),
     lambda: pins.test_decode_matches_bruteforce.hypothesis.inner_test(B=2, L=9, Hkv=2, G=4, d=4, seed=3),
+    lambda: pins.test_softmax1_is_an_extra_zero_key(0),
+    lambda: [pins.test_softmax1_equal_scores_closed_form(s) for s in (-2.0, 1.5)],
 ]
 
 

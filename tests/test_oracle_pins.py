@@ -348,3 +348,71 @@ def test_row_variants_match_full():
     rows2 = oracle.v2_rows(q, k, vv, lam, idx2)
     for r, (b, t, p) in enumerate(idx2):
         assert np.array_equal(rows2[r], full2[b, t, p])
+
+
+# --------------------------------------------------------------------------
+# Off-by-one softmax exp(x_j) / (1 + sum_j exp(x_j)) (Hacker News item
+# 41780844, the comment that softmax "should be exp()/1+sum exp()" and that
+# adding an extra zero value in x does the same)
+# --------------------------------------------------------------------------
+
+def _prepend_zero_token(x, axis):
+    """x with one all-zero entry inserted at index 0 of the token axis."""
+    shape = list(x.shape)
+    shape[axis] = 1
+    return np.concatenate([np.zeros(shape), x], axis=axis)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_softmax1_is_an_extra_zero_key(seed):
+    """Off-by-one attention over T keys equals standard attention over T+1
+    keys whose first key is the zero vector (logit exactly 0 for every
+    query) with a zero value row: prepend that token, drop its output row."""
+    rng = _rng(200 + seed)
+    B, H, T, d, layer = 2, 2, 19, 8, 3
+    q1, q2, k1, k2, v, lams = _v1_case(rng, B, H, T, d, lam_std=0.4)
+    got = oracle.v1_fwd(q1, q2, k1, k2, v, *lams, layer, softmax1=True)
+    aug = [_prepend_zero_token(x, 2) for x in (q1, q2, k1, k2, v)]
+    ref = oracle.v1_fwd(*aug, *lams, layer)[:, 1:]
+    _close(got, ref, rtol=1e-11, atol=1e-12)
+    q, k, vv, lg = _v2_case(rng, 2, 23, 8, 2, d)
+    got2 = oracle.v2_fwd(q, k, vv, lg, softmax1=True)
+    ref2 = oracle.v2_fwd(*[_prepend_zero_token(x, 1) for x in (q, k, vv, lg)])[:, 1:]
+    _close(got2, ref2, rtol=1e-11, atol=1e-12)
+    qd = rng.standard_normal((2, 8, d))
+    kd, vd = rng.standard_normal((2, 30, 2, d)), rng.standard_normal((2, 30, 2, d))
+    lgd = rng.standard_normal((2, 4))
+    got3 = oracle.v2_decode(qd, kd, vd, lgd, softmax1=True)
+    ref3 = oracle.v2_decode(qd, _prepend_zero_token(kd, 1), _prepend_zero_token(vd, 1), lgd)
+    _close(got3, ref3, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("s", [-2.0, 1.5])
+def test_softmax1_equal_scores_closed_form(s):
+    """Every visible score equal to s: each of the n = i+1 keys gets weight
+    e^s / (1 + n e^s), so A.V = n e^s / (1 + n e^s) * prefix-mean(V)."""
+    rng = _rng(210)
+    B, T, Hq, Hkv, d = 1, 40, 4, 2, 8
+    u = np.zeros(d)
+    u[0] = 1.0
+    q = np.broadcast_to(s * math.sqrt(d) * u, (B, T, Hq, d)).copy()
+    k = np.broadcast_to(u, (B, T, Hkv, d)).copy()
+    v = rng.standard_normal((B, T, Hkv, d))
+    lg = rng.standard_normal((B, T, Hq // 2))
+    n = np.arange(1, T + 1)[None, :, None, None]
+    frac = n * math.exp(s) / (1.0 + n * math.exp(s))
+    pm = np.cumsum(v, axis=1) / n  # [B,T,Hkv,d]
+    a = np.repeat(frac * pm, 2, axis=2)  # heads 2p, 2p+1 share the group's K/V here (G = 2)
+    sig = 1.0 / (1.0 + np.exp(-lg))
+    _close(oracle.v2_fwd(q, k, v, lg, softmax1=True), (1 - sig)[..., None] * a[:, :, 0::2])
+    # V1 with both maps on the same scores: D = (1 - lam) frac * prefix-mean(V)
+    H, layer = 1, 6
+    q1 = np.broadcast_to(s * math.sqrt(d) * u, (B, H, T, d)).copy()
+    k1 = np.broadcast_to(u, (B, H, T, d)).copy()
+    v1 = rng.standard_normal((B, H, T, 2 * d))
+    lams = [0.3 * rng.standard_normal(d) for _ in range(4)]
+    lam, li = oracle.v1_lambda(*lams, layer), oracle.lambda_init(layer)
+    n1 = np.arange(1, T + 1)[None, None, :, None]
+    D = (1 - lam) * (n1 * math.exp(s) / (1 + n1 * math.exp(s))) * np.cumsum(v1, axis=2) / n1
+    ref = (1 - li) * D / np.sqrt(np.mean(D * D, -1, keepdims=True) + 1e-5)
+    _close(oracle.v1_fwd(q1, q1, k1, k1, v1, *lams, layer, softmax1=True), np.transpose(ref, (0, 2, 1, 3)))
