@@ -16,7 +16,8 @@ The JSON line also carries:
   cpu_baseline  the fp64 oracle timed on a bounded sample of the same
                 workload on this host's cores;
   secondary     the other full-size workloads (3B-class V1, V2 GQA prefill,
-                V2 decode), each with its own roofline; a secondary step is
+                V2 decode, V2 decode of a ragged batch over a paged cache),
+                each with its own roofline; a secondary step is
                 8 launches of the workload (warm-up ~0.3 s of its own calls).
 Logs go to stderr; stdout holds exactly one JSON line.
 """
@@ -36,7 +37,8 @@ METRIC = "diff-attn causal fwd TFLOP/s (bf16, % MFMA peak); V2 decode HBM GB/s (
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 HEADLINE = "v1_gpt2small_B8_H6_T1024_d64"
-SECONDARY = ["v1_3b_B2_H12_T4096_d128", "v2_prefill_B1_T8192_Hq64_Hkv8_d128", "v2_decode_B64_L32768_Hq64_Hkv8_d128"]
+SECONDARY = ["v1_3b_B2_H12_T4096_d128", "v2_prefill_B1_T8192_Hq64_Hkv8_d128", "v2_decode_B64_L32768_Hq64_Hkv8_d128",
+             "v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128"]
 
 
 def log(*a):
@@ -53,9 +55,15 @@ def _caller(w, x, binding, torch, softmax1=False):
     if w.kind == "v2":
         out = torch.empty((w.B, w.T, w.Hq // 2, w.d), dtype=w.torch_dtype, device=x["v"].device)
         return lambda layer: binding.v2_fwd(x["q"], x["k"], x["v"], x["lam"], out=out, softmax1=softmax1)
-    out = torch.empty((w.B, w.Hq // 2, w.d), dtype=w.torch_dtype, device=x["v"].device)
-    ws = torch.empty(binding.v2_decode_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.d), dtype=torch.uint8,
-                     device=x["v"].device)
+    dev = x["q"].device
+    out = torch.empty((w.B, w.Hq // 2, w.d), dtype=w.torch_dtype, device=dev)
+    if w.kind == "decode_paged":
+        ws = torch.empty(binding.v2_decode_paged_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.d), dtype=torch.uint8,
+                         device=dev)
+        return lambda layer: binding.v2_decode_paged(x["q"], x["k_pages"], x["v_pages"], x["block_table"],
+                                                     x["seq_lens"], x["lam"], w.T, out=out, workspace=ws,
+                                                     softmax1=softmax1)
+    ws = torch.empty(binding.v2_decode_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.d), dtype=torch.uint8, device=dev)
     return lambda layer: binding.v2_decode(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws,
                                            softmax1=softmax1)
 
@@ -111,7 +119,7 @@ def _timed(torch, call, layers, steps, warmup, graph=True):
 
 def _roofline(w, launch_ms):
     avg_s = sum(launch_ms) / len(launch_ms) / 1e3
-    if w.kind == "decode":
+    if w.kind in ("decode", "decode_paged"):
         a = w.compulsory_bytes() / avg_s / 1e9
         return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(a / PEAK_HBM_GBS, 4), "traffic": None,
@@ -153,7 +161,8 @@ def _source_sha(kind):
     from hardware counters only applies to the kernel it was measured on."""
     import hashlib
 
-    src = {"v1": "prefill_bf16.hip", "v2": "prefill_bf16.hip", "decode": "decode_bf16.hip"}[kind]
+    src = {"v1": "prefill_bf16.hip", "v2": "prefill_bf16.hip", "decode": "decode_bf16.hip",
+           "decode_paged": "decode_bf16.hip"}[kind]
     path = os.path.join(ROOT, "differential_attention_diffattn_amd", "csrc", src)
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
@@ -218,7 +227,8 @@ def write_traffic(pmc_dir):
                             "write_scale": round(w_scale, 4)}}
     for name, match in [("v1_gpt2small_B8_H6_T1024_d64", "prefill_kernel"), ("v1_3b_B2_H12_T4096_d128", "prefill_kernel"),
                         ("v2_prefill_B1_T8192_Hq64_Hkv8_d128", "prefill_kernel"),
-                        ("v2_decode_B64_L32768_Hq64_Hkv8_d128", "decode_split_kernel")]:
+                        ("v2_decode_B64_L32768_Hq64_Hkv8_d128", "decode_split_kernel"),
+                        ("v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128", "decode_split_kernel")]:
         w = workloads.WORKLOADS[name]
         fk = per_dispatch(name, "FETCH_SIZE", match)
         wk = per_dispatch(name, "WRITE_SIZE", match)
@@ -319,6 +329,9 @@ def main():
         if w.kind == "decode":
             res.update(metric="V2 decode HBM GB/s", unit="GB/s",
                        value=round(w.compulsory_bytes() / per_call_s / 1e9, 1))
+        elif w.kind == "decode_paged":
+            res.update(metric="V2 paged ragged decode HBM GB/s (bytes of the sequences' own lengths)",
+                       unit="GB/s", value=round(w.compulsory_bytes() / per_call_s / 1e9, 1))
         else:
             res.update(metric="causal fwd TFLOP/s", unit="TFLOP/s", value=round(w.flops() / per_call_s / 1e12, 3))
         log(json.dumps(res))
@@ -339,7 +352,7 @@ def main():
             # warm-up sized to ~0.3 s of this workload's own calls, so the
             # GPU clock has settled under its load before the timed steps
             ws = workloads.WORKLOADS[name]
-            est_s = ws.flops() / 1e15 if ws.kind != "decode" else ws.compulsory_bytes() / 5.5e12
+            est_s = ws.flops() / 1e15 if ws.kind in ("v1", "v2") else ws.compulsory_bytes() / 5.5e12
             # 8 launches per step: the events around a graph replay then time
             # the kernels, not the replay's launch
             _, xs, r = measure(name, max(10, args.steps), max(3, int(0.3 / (8 * est_s))), calls_per_step=8)

@@ -170,6 +170,13 @@ size_t diffattn_v2_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int d) 
   return (size_t)B * Hkv * sp.nsplit * (size_t)(Hq / Hkv) * (size_t)(d + 2) * sizeof(float);
 }
 
+size_t diffattn_v2_decode_paged_workspace_bytes(int B, int max_len, int Hq, int Hkv, int d) {
+  if (B < 1 || max_len < 1 || Hq < 1 || Hkv < 1 || d < 1) return 0;
+  if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return 0;
+  const da::DecodeSplit sp = da::decode_split(B, max_len, Hkv, da::kPagedMaxChunk);
+  return (size_t)B * Hkv * sp.nsplit * (size_t)(Hq / Hkv) * (size_t)(d + 2) * sizeof(float);
+}
+
 static da_status v2_decode_impl(int softmax1, da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
                                 da_in k_cache,
                              da_in v_cache, da_in lam, da_out out, void* workspace, size_t workspace_bytes,
@@ -191,7 +198,7 @@ static da_status v2_decode_impl(int softmax1, da_dtype dtype, int B, int L, int 
   const size_t need = diffattn_v2_decode_workspace_bytes(B, L, Hq, Hkv, d);
   if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return DA_E_WORKSPACE;
   const da::DecodeSplit sp = da::decode_split(B, L, Hkv);
-  if (!grid_fits((long long)B * Hkv * sp.nsplit) || !grid_fits((long long)B * (Hq / 2))) return DA_E_SHAPE;
+  if (!grid_fits(da::decode_split_grid(B, Hkv, sp.nsplit)) || !grid_fits((long long)B * (Hq / 2))) return DA_E_SHAPE;
 
   da::DecodeArgs a{};
   a.q = TIn{q.ptr, q.sb, q.sh, 0};
@@ -205,6 +212,62 @@ static da_status v2_decode_impl(int softmax1, da_dtype dtype, int B, int L, int 
   a.chunk = sp.chunk;
   a.nsplit = sp.nsplit;
   a.softmax1 = softmax1;
+  return launch_status(da::launch_decode_bf16(d, a, (hipStream_t)stream));
+}
+
+// Paged, ragged cache: k_pages / v_pages are [num_pages, page_size, Hkv, d]
+// with roles (b = page, h = kv head, t = row in the page).
+static da_status v2_decode_paged_impl(int softmax1, da_dtype dtype, int B, int max_len, int Hq, int Hkv, int d,
+                                      da_in q, da_in k_pages, da_in v_pages, int num_pages, int page_size,
+                                      const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                                      da_in lam, da_out out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
+  if (B < 1 || max_len < 1 || Hq < 1 || Hkv < 1 || d < 1 || num_pages < 1) return DA_E_SHAPE;
+  if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return DA_E_SHAPE;
+  if (page_size < 16 || page_size > (1 << 30) || (page_size & (page_size - 1)) != 0) return DA_E_SHAPE;
+  const int64_t pages_per_seq = ((int64_t)max_len + page_size - 1) / page_size;
+  if (bt_stride < pages_per_seq) return DA_E_SHAPE;
+  const int64_t mult = dtype == DA_BF16 ? 8 : 4;
+  DA_TRY(check_rows(q.ptr, q.sb, q.sh, 0, mult));
+  DA_TRY(check_in(k_pages, mult));
+  DA_TRY(check_in(v_pages, mult));
+  if (!block_table || !seq_lens) return DA_E_NULL;
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4)) return DA_E_LAYOUT;
+  da_in lam2 = lam;
+  lam2.st = 0;
+  DA_TRY(check_logits(lam2));
+  DA_TRY(check_rows(out.ptr, out.sb, out.sh, 0, mult));
+  DA_TRY(validate_v2_common(dtype, B, max_len, Hq, Hkv, d));
+  if (Hq / Hkv > 16) return DA_E_UNSUPPORTED;  // one 16-wide MFMA column block per group
+  // the kernel addresses a row within a page with a 32-bit element offset
+  if ((int64_t)page_size * k_pages.st >= (int64_t(1) << 31) || (int64_t)page_size * v_pages.st >= (int64_t(1) << 31))
+    return DA_E_UNSUPPORTED;
+  const size_t need = diffattn_v2_decode_paged_workspace_bytes(B, max_len, Hq, Hkv, d);
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return DA_E_WORKSPACE;
+  const da::DecodeSplit sp = da::decode_split(B, max_len, Hkv, da::kPagedMaxChunk);
+  if (!grid_fits(da::decode_split_grid(B, Hkv, sp.nsplit)) || !grid_fits((long long)B * (Hq / 2))) return DA_E_SHAPE;
+
+  da::DecodeArgs a{};
+  a.q = TIn{q.ptr, q.sb, q.sh, 0};
+  a.k = tin(k_pages);
+  a.v = tin(v_pages);
+  a.lam = TIn{lam.ptr, lam.sb, lam.sh, 0};
+  a.out = TOut{out.ptr, out.sb, out.sh, 0};
+  a.ws = (float*)workspace;
+  a.sl2 = log2e_over_sqrt(d);
+  a.B = B, a.L = max_len, a.Hq = Hq, a.Hkv = Hkv, a.G = Hq / Hkv;
+  a.chunk = sp.chunk;
+  a.nsplit = sp.nsplit;
+  a.softmax1 = softmax1;
+  a.block_table = block_table;
+  a.bt_stride = bt_stride;
+  a.seq_lens = seq_lens;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  a.page_shift = shift;
+  a.page_mask = page_size - 1;
+  a.num_pages = num_pages;
   return launch_status(da::launch_decode_bf16(d, a, (hipStream_t)stream));
 }
 
@@ -245,6 +308,24 @@ da_status diffattn_v2_decode_softmax1(da_dtype dtype, int B, int L, int Hq, int 
                                       size_t workspace_bytes, void* stream) {
   return v2_decode_impl(1, dtype, B, L, Hq, Hkv, d, q, k_cache, v_cache, lam, out, workspace, workspace_bytes,
                         stream);
+}
+
+da_status diffattn_v2_decode_paged(da_dtype dtype, int B, int max_len, int Hq, int Hkv, int d, da_in q,
+                                   da_in k_pages, da_in v_pages, int num_pages, int page_size,
+                                   const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                                   da_in lam, da_out out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return v2_decode_paged_impl(0, dtype, B, max_len, Hq, Hkv, d, q, k_pages, v_pages, num_pages, page_size,
+                              block_table, bt_stride, seq_lens, lam, out, workspace, workspace_bytes, stream);
+}
+
+da_status diffattn_v2_decode_paged_softmax1(da_dtype dtype, int B, int max_len, int Hq, int Hkv, int d, da_in q,
+                                            da_in k_pages, da_in v_pages, int num_pages, int page_size,
+                                            const int32_t* block_table, int64_t bt_stride,
+                                            const int32_t* seq_lens, da_in lam, da_out out, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  return v2_decode_paged_impl(1, dtype, B, max_len, Hq, Hkv, d, q, k_pages, v_pages, num_pages, page_size,
+                              block_table, bt_stride, seq_lens, lam, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

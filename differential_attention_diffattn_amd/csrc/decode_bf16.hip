@@ -18,6 +18,9 @@
 //   * merge kernel: per (b, pair), the partials of both heads are merged in
 //     split order (fixed, no atomics: deterministic), normalised and combined
 //     as a_2p - sigmoid(lam[b, p]) a_2p+1.
+// The paged variant (PAGED) reads the cache through a per-sequence page table
+// and stops at each sequence's own length; splits past that length leave an
+// empty partial (max -inf), which the merges skip.
 #include <math.h>
 
 #include "kernels.hpp"
@@ -37,7 +40,7 @@ __device__ __forceinline__ void lds_fence() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ void __launch_bounds__(kWaves * 64) decode_split_kernel(const DecodeArgs a) {
   constexpr int KS = D / 32;   // k-steps of the score MFMA
   constexpr int CB = D / 16;   // 16-wide column blocks of O^T
@@ -45,6 +48,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_split_kernel(const DecodeA
   constexpr int VT_ELEMS = D * VROW;               // one wave's V^T slice
   constexpr int VU = (kBlk / 4) * (D / 8) / 64;    // 4x8 V units per lane
   static_assert(VU >= 1 && (kBlk / 4) * (D / 8) % 64 == 0, "V block split");
+  static_assert(kBlk == 32, "a step is two 16-token sub-blocks");
   constexpr int LDS_VT = kWaves * VT_ELEMS * 2;            // bytes
   constexpr int LDS_RED = kWaves * 16 * (D + 2) * 4;       // bytes
   constexpr int LDS_BYTES = LDS_VT > LDS_RED ? LDS_VT : LDS_RED;
@@ -53,11 +57,39 @@ __global__ void __launch_bounds__(kWaves * 64) decode_split_kernel(const DecodeA
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, kg = lane >> 4;
 
+  // Workgroup -> (sequence b, kv head g, split s).  The hardware deals
+  // consecutive workgroups to the 8 XCDs in turn (XCD = id mod 8).
+  //  * dense (every sequence L long, uniform work): split fastest, then kv
+  //    head, then sequence (with nsplit a multiple of 8, XCD x takes the
+  //    splits s = x mod 8 of every (b, g)).
+  //  * paged (ragged lengths: the late splits of short sequences are empty):
+  //    the dense order would give the XCDs holding the early splits most of
+  //    the work.  A "unit" is one split of one sequence; units are numbered
+  //    split-major with the sequence index rotated by the split, all kv heads
+  //    of a unit go to one XCD, and XCD x takes every 8th unit, so each XCD
+  //    gets every split of a spread of sequences.  The grid is padded to a
+  //    multiple of 8 units.
+  // Measured on MI355X: the paged order is 1.46x the dense order's rate on a
+  // ragged batch (lengths uniform in [1, 32768]); the dense order is 1.06x
+  // the paged order's on uniform lengths.
   const int bid = blockIdx.x;
-  const int s = bid % a.nsplit;
-  const int g = (bid / a.nsplit) % a.Hkv;
-  const int b = bid / (a.nsplit * a.Hkv);
-  const int G = a.G, L = a.L;
+  int b, g, s;
+  if constexpr (PAGED) {
+    const int xcd = bid & 7, j = bid >> 3;
+    g = j % a.Hkv;
+    const int unit = (j / a.Hkv) * 8 + xcd;
+    if (unit >= a.B * a.nsplit) return;  // padding (uniform over the workgroup)
+    s = unit / a.B;
+    b = (unit % a.B + s) % a.B;
+  } else {
+    if (bid >= a.B * a.Hkv * a.nsplit) return;  // padding
+    s = bid % a.nsplit;
+    g = (bid / a.nsplit) % a.Hkv;
+    b = bid / (a.nsplit * a.Hkv);
+  }
+  const int G = a.G;
+  // tokens of this sequence (paged: its own length, at most the longest)
+  const int L = PAGED ? min(max(a.seq_lens[b], 0), a.L) : a.L;
 
   // q fragments: B operand of S = K q^T.  Lane column = head (c16 < G).
   bf16x8 qf[KS];
@@ -67,9 +99,22 @@ __global__ void __launch_bounds__(kWaves * 64) decode_split_kernel(const DecodeA
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = as_bf16x8(c16 < G ? *(const uint4*)(qrow + 32 * ks + 8 * kg) : make_uint4(0, 0, 0, 0));
   }
-  const uint16_t* kbase = (const uint16_t*)a.k.p + b * a.k.sb + g * a.k.sh;
-  const uint16_t* vbase = (const uint16_t*)a.v.p + b * a.v.sb + g * a.v.sh;
+  const uint16_t* kbase = (const uint16_t*)a.k.p + (PAGED ? 0 : b * a.k.sb) + g * a.k.sh;
+  const uint16_t* vbase = (const uint16_t*)a.v.p + (PAGED ? 0 : b * a.v.sb) + g * a.v.sh;
   const int64_t kst = a.k.st, vst = a.v.st;
+  // Paged cache: pages hold a power of two >= 16 tokens, so each 16-token
+  // sub-block of a step lies in one page and one table entry per sub-block
+  // locates it.  The entries of a wave's next step are loaded one step ahead
+  // (their latency hides behind the current step); a sub-block past the
+  // sequence's end reads the entry of its last token instead (its rows are
+  // masked).  Entries outside [0, num_pages) are clamped.
+  const int32_t* bt_row = PAGED ? a.block_table + (int64_t)b * a.bt_stride : nullptr;
+  auto table_entry = [&](int tok) -> int { return bt_row[min(tok, L - 1) >> a.page_shift]; };
+  auto page_base = [&](int raw, int64_t page_stride) -> int64_t {
+    const int pg = min(max(__builtin_amdgcn_readfirstlane(raw), 0), a.num_pages - 1);
+    return (int64_t)pg * page_stride;
+  };
+  const int pmask = PAGED ? a.page_mask : 0;
 
   uint16_t* vt = (uint16_t*)smem + wave * VT_ELEMS;
   const float sl2 = a.sl2;
@@ -79,28 +124,53 @@ __global__ void __launch_bounds__(kWaves * 64) decode_split_kernel(const DecodeA
   for (int cb = 0; cb < CB; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int t0 = s * a.chunk, t1 = min(L, t0 + a.chunk);
-  for (int blk = t0 + kBlk * wave; blk < t1; blk += kBlk * kWaves) {
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int blk0 = t0 + kBlk * wv;
+  int raw[2] = {0, 0};  // table entries of the step's two sub-blocks
+  if constexpr (PAGED) {
+    if (L > 0) raw[0] = table_entry(blk0), raw[1] = table_entry(blk0 + 16);
+  }
+  for (int blk = blk0; blk < t1; blk += kBlk * kWaves) {
     // ---- issue the block's K (A operand) and V (transpose units) loads ----
+    // kp/vp: element offset of each sub-block's page (paged) or 0; a token's
+    // row offset within it is 32-bit (the host bounds page_size * stride)
+    int64_t kp[2] = {0, 0}, vp[2] = {0, 0};
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        kp[sub] = page_base(raw[sub], a.k.sb);
+        vp[sub] = page_base(raw[sub], a.v.sb);
+      }
+    }
+    // Tokens past the end load the last token's row instead (no branches, so
+    // the loads stay in flight together): their scores are masked to -inf
+    // below, so their probabilities are 0 and the (finite) rows add nothing.
+    // A sub-block that starts past the end was given the last token's page.
     uint4 kr[2][KS];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      const int tok = blk + 16 * sub + c16;
+      const int tok = min(blk + 16 * sub + c16, L - 1);
+      const int64_t off = PAGED ? kp[sub] + (uint32_t)((tok & pmask) * (int)kst) : (int64_t)tok * kst;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kr[sub][ks] = tok < L ? load_nt16(kbase + (int64_t)tok * kst + 32 * ks + 8 * kg)
-                              : make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) kr[sub][ks] = load_nt16(kbase + off + 32 * ks + 8 * kg);
     }
     uint4 vr[VU][4];
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
       const int unit = lane + 64 * u;
       const int rg = unit % (kBlk / 4), cc = unit / (kBlk / 4);
+      // the group's 4 tokens lie in sub-block 4*rg/16 (and in one page)
+      const int64_t vpage = PAGED ? (rg < 4 ? vp[0] : vp[1]) : 0;
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const int tok = blk + 4 * rg + qq;
-        vr[u][qq] = tok < L ? load_nt16(vbase + (int64_t)tok * vst + cc * 8)
-                            : make_uint4(0, 0, 0, 0);
+        const int tok = min(blk + 4 * rg + qq, L - 1);
+        const int64_t off = PAGED ? vpage + (uint32_t)((tok & pmask) * (int)vst) : (int64_t)tok * vst;
+        vr[u][qq] = load_nt16(vbase + off + cc * 8);
       }
+    }
+    if constexpr (PAGED) {  // the next step's table entries (in bounds even past the end)
+      const int nb = blk + kBlk * kWaves;
+      raw[0] = table_entry(nb), raw[1] = table_entry(nb + 16);
     }
 
     // ---- scores: S[tok][head], two 16-token sub-blocks ----
@@ -122,7 +192,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_split_kernel(const DecodeA
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mb = mx * sl2;  // finite: token blk < L is in every block
+    const float mb = mx * sl2;  // finite: token blk < L is in every block (blk < t1 <= L)
     const bool need = mb > mref + kLazyLog2;
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float al = need ? exp2f(mref - mb) : 1.f;
@@ -211,6 +281,10 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(const DecodeArgs a) {
     const int64_t sstride = (int64_t)G * (D + 2);
     float M = -INFINITY;
     for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, base[s * sstride]);
+    if (M == -INFINITY) {  // no token at all (a paged sequence of length 0): no contribution
+      res[k] = 0.f;
+      continue;
+    }
     float l = 0.f, acc = 0.f;
     for (int s = 0; s < a.nsplit; ++s) {
       const float f = exp2f(base[s * sstride] - M);
@@ -230,8 +304,9 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(const DecodeArgs a) {
 template <int D>
 hipError_t launch(const DecodeArgs& a, hipStream_t st) {
   const void* args[] = {&a};
-  hipError_t e = hipLaunchKernel((const void*)decode_split_kernel<D>, dim3(a.B * a.Hkv * a.nsplit),
-                                 dim3(kWaves * 64), (void**)args, 0, st);
+  const void* split = a.block_table ? (const void*)decode_split_kernel<D, true> : (const void*)decode_split_kernel<D, false>;
+  hipError_t e = hipLaunchKernel(split, dim3(decode_split_grid(a.B, a.Hkv, a.nsplit)), dim3(kWaves * 64),
+                                 (void**)args, 0, st);
   if (e != hipSuccess) return e;
   return hipLaunchKernel((const void*)decode_merge_kernel<D>, dim3(a.B * (a.Hq / 2)), dim3(D), (void**)args, 0,
                          st);
@@ -239,12 +314,12 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
-DecodeSplit decode_split(int B, int L, int Hkv) {
-  // Aim for >= 2048 workgroups (8 per CU) and chunks of <= 2048 tokens; a
-  // chunk is a multiple of the 4 waves x 32 tokens one step consumes.
+DecodeSplit decode_split(int B, int L, int Hkv, int max_chunk) {
+  // Aim for >= 2048 workgroups (8 per CU) and chunks of <= max_chunk tokens;
+  // a chunk is a multiple of the 4 waves x 32 tokens one step consumes.
   const int step = kWaves * kBlk;
   const long units = (long)B * Hkv;
-  long ns = (L + 2047) / 2048;
+  long ns = (L + max_chunk - 1) / max_chunk;
   const long want = (2048 + units - 1) / units;
   if (ns < want) ns = want;
   const long maxns = (L + step - 1) / step;
@@ -256,6 +331,11 @@ DecodeSplit decode_split(int B, int L, int Hkv) {
   r.chunk = (int)chunk;
   r.nsplit = (int)((L + chunk - 1) / chunk);
   return r;
+}
+
+long long decode_split_grid(int B, int Hkv, int nsplit) {
+  const long long units = (long long)B * nsplit;
+  return (units + 7) / 8 * 8 * Hkv;
 }
 
 hipError_t launch_decode_bf16(int d, const DecodeArgs& a, hipStream_t s) {

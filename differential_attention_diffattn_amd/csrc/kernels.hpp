@@ -62,13 +62,28 @@ struct DecodeArgs {
   int chunk;   // tokens per split (multiple of 128)
   int nsplit;
   int softmax1;  // 1: off-by-one softmax (each head's denominator + exp(0))
+  // Paged cache (null block_table: the dense [B, L, Hkv, d] cache of k / v):
+  // token t of sequence b is row (t & page_mask) of page
+  // block_table[b * bt_stride + (t >> page_shift)] (clamped to [0, num_pages)),
+  // with k.sb / v.sb the stride between pages; the sequence has seq_lens[b]
+  // tokens (clamped to [0, L]; L is the longest).
+  const int32_t* block_table;
+  int64_t bt_stride;
+  const int32_t* seq_lens;
+  int page_shift, page_mask, num_pages;
 };
 hipError_t launch_decode_bf16(int d, const DecodeArgs& a, hipStream_t s);
+// workgroups of the decode split kernel (B * nsplit units padded to a multiple of 8, times Hkv)
+long long decode_split_grid(int B, int Hkv, int nsplit);
 
 // Decode split geometry, shared by the workspace query and the launcher.
 struct DecodeSplit {
   int chunk, nsplit;
 };
-DecodeSplit decode_split(int B, int L, int Hkv);
+DecodeSplit decode_split(int B, int L, int Hkv, int max_chunk = 2048);
+#ifndef DA_PAGED_CHUNK
+#define DA_PAGED_CHUNK 2048
+#endif
+constexpr int kPagedMaxChunk = DA_PAGED_CHUNK;  // paged decode: tokens per split at most
 
 }  // namespace da

@@ -11,7 +11,12 @@ initialisation); V2 lambda logits N(0, 1) in fp32.  Values are drawn in fp32
 with a seeded ``torch.Generator`` and then rounded (RNE) to the working dtype;
 the order of draws is fixed per workload.
 
-Shapes: the five workloads below.  The GPT-2-small and 3B-class shapes stand
+Paged decode: sequence lengths uniform in [1, max_len] and the page table a
+seeded random permutation of the page pool (a pool shared by a ragged batch,
+pages handed out in no particular order), both drawn on the CPU so the sizes
+are known without touching the device.
+
+Shapes: the workloads below.  The GPT-2-small and 3B-class shapes stand
 in for the models the pages name (a GPT-2 124M nanoGPT run; a 3B model with
 28 layers, hidden 3072, 12 heads); no dataset, checkpoint or real activation
 is available, so seeded N(0, 1) tensors stand in for them.
@@ -27,7 +32,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "v1", "v2", "decode"
+    kind: str  # "v1", "v2", "decode", "decode_paged"
     dtype: str  # "fp32" or "bf16"
     B: int
     H: int = 0  # V1: differential heads
@@ -37,6 +42,11 @@ class Workload:
     Hkv: int = 0
     layers: Tuple[int, ...] = ()
     seed: int = 0
+    page: int = 0  # decode_paged: tokens per cache page (T is then the longest length)
+
+    def seq_lens(self) -> torch.Tensor:
+        """decode_paged: the seeded sequence lengths (CPU int32 [B])."""
+        return draw_seq_lens(self.B, self.T, self.seed)
 
     @property
     def torch_dtype(self):
@@ -45,11 +55,14 @@ class Workload:
     def flops(self) -> float:
         """Algorithmic flops of one call, counting only unmasked (i, j<=i)
         pairs: V1 = 2 maps x (QK^T over d + PV over 2d) = 6*B*H*d*T(T+1);
-        V2 prefill = 2*B*Hq*d*T(T+1); decode = 4*B*Hq*d*L."""
+        V2 prefill = 2*B*Hq*d*T(T+1); decode = 4*B*Hq*d*L (paged: the sum of
+        the sequences' lengths in place of B*L)."""
         if self.kind == "v1":
             return 6.0 * self.B * self.H * self.d * self.T * (self.T + 1)
         if self.kind == "v2":
             return 2.0 * self.B * self.Hq * self.d * self.T * (self.T + 1)
+        if self.kind == "decode_paged":
+            return 4.0 * self.Hq * self.d * int(self.seq_lens().sum())
         return 4.0 * self.B * self.Hq * self.d * self.T
 
     def compulsory_bytes(self) -> int:
@@ -63,6 +76,12 @@ class Workload:
             B, T, Hq, Hkv, d = self.B, self.T, self.Hq, self.Hkv, self.d
             return e * (B * T * Hq * d + 2 * B * T * Hkv * d + B * T * (Hq // 2) * d) + 4 * B * T * (Hq // 2)
         B, L, Hq, Hkv, d = self.B, self.T, self.Hq, self.Hkv, self.d
+        if self.kind == "decode_paged":
+            lens = self.seq_lens().long()
+            tokens = int(lens.sum())
+            table = 4 * int(((lens + self.page - 1) // self.page).sum())  # the entries a call reads
+            return (e * (B * Hq * d + 2 * tokens * Hkv * d + B * (Hq // 2) * d) + 4 * B * (Hq // 2) + table
+                    + 4 * B)
         return e * (B * Hq * d + 2 * B * L * Hkv * d + B * (Hq // 2) * d) + 4 * B * (Hq // 2)
 
 
@@ -76,6 +95,8 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("v2_prefill_B1_T8192_Hq64_Hkv8_d128", "v2", "bf16", B=1, T=8192, d=128, Hq=64, Hkv=8, seed=4),
         Workload("v2_decode_B64_L32768_Hq64_Hkv8_d128", "decode", "bf16", B=64, T=32768, d=128, Hq=64,
                  Hkv=8, seed=5),
+        Workload("v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128", "decode_paged", "bf16", B=64, T=32768,
+                 d=128, Hq=64, Hkv=8, seed=6, page=64),
     ]
 }
 
@@ -146,9 +167,48 @@ def decode_inputs(B: int, L: int, Hq: int, Hkv: int, d: int, dtype=torch.bfloat1
     }
 
 
+def draw_seq_lens(B: int, max_len: int, seed: int) -> torch.Tensor:
+    """Lengths uniform in [1, max_len], CPU int32 [B]."""
+    g = torch.Generator().manual_seed(int(seed) + 7919)
+    return torch.randint(1, max_len + 1, (B,), generator=g, dtype=torch.int32)
+
+
+def paged_decode_inputs(B: int, max_len: int, page: int, Hq: int, Hkv: int, d: int, dtype=torch.bfloat16,
+                        seed: int = 0, device="cpu", lens=None, spare_pages: int = 3) -> Dict[str, torch.Tensor]:
+    """Decode over a paged cache.  lens: the sequence lengths (default: uniform
+    in [1, max_len]); q ``[B, Hq, d]``; k_pages, v_pages ``[num_pages, page,
+    Hkv, d]`` (dtype) with num_pages = the pages the sequences need +
+    ``spare_pages``; block_table int32 ``[B, ceil(max_len / page)]``: the
+    sequences' pages in a seeded random order of the pool, -1 past each
+    sequence's last page; seq_lens int32 ``[B]``; lam ``[B, Hq/2]`` fp32."""
+    lens = draw_seq_lens(B, max_len, seed) if lens is None else torch.tensor(list(lens), dtype=torch.int32)
+    width = (max_len + page - 1) // page
+    need = [(int(L) + page - 1) // page for L in lens]
+    num_pages = sum(need) + spare_pages
+    gc = torch.Generator().manual_seed(int(seed) + 104729)
+    order = torch.randperm(num_pages, generator=gc).to(torch.int32)
+    table = torch.full((B, width), -1, dtype=torch.int32)
+    at = 0
+    for b, n in enumerate(need):
+        table[b, :n] = order[at:at + n]
+        at += n
+    g = _gen(seed, device)
+    rows = max(1, (64 << 20) // (page * Hkv * d * 4))  # bound the fp32 temporary to ~64 MB
+    return {
+        "q": _randn((B, Hq, d), g, device, dtype),
+        "k_pages": _randn((num_pages, page, Hkv, d), g, device, dtype, chunk_rows=rows),
+        "v_pages": _randn((num_pages, page, Hkv, d), g, device, dtype, chunk_rows=rows),
+        "block_table": table.to(device),
+        "seq_lens": lens.to(device),
+        "lam": _randn((B, Hq // 2), g, device, torch.float32),
+    }
+
+
 def inputs_for(w: Workload, device="cpu") -> Dict[str, torch.Tensor]:
     if w.kind == "v1":
         return v1_inputs(w.B, w.H, w.T, w.d, w.torch_dtype, w.seed, device)
     if w.kind == "v2":
         return v2_inputs(w.B, w.T, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)
+    if w.kind == "decode_paged":
+        return paged_decode_inputs(w.B, w.T, w.page, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)
     return decode_inputs(w.B, w.T, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)

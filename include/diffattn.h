@@ -189,6 +189,67 @@ da_status diffattn_v2_decode_softmax1(da_dtype dtype, int B, int L, int Hq, int 
                                       da_out out, void* workspace, size_t workspace_bytes,
                                       void* stream);
 
+/*
+ * Bytes of device workspace diffattn_v2_decode_paged (and its _softmax1
+ * variant) needs for these sizes (0 if the sizes are invalid); it depends
+ * only on (B, max_len, Hq, Hkv, d).
+ */
+size_t diffattn_v2_decode_paged_workspace_bytes(int B, int max_len, int Hq, int Hkv, int d);
+
+/*
+ * DIFF V2 decode over a paged, ragged KV cache.  Per sequence b it computes
+ * exactly what diffattn_v2_decode computes ("Differential Transformer V2"
+ * article: DiffAttnV2 at the newest position) with L = seq_lens[b]; only the
+ * storage of the cache differs.  The pages define the attention, not this
+ * layout: it is the serving layout in which sequences of different lengths
+ * share one pool of fixed-size cache pages.
+ *
+ *   dtype        DA_BF16 only.   d in {64, 128}.  Hq % Hkv == 0, (Hq/Hkv)
+ *                even and <= 16.
+ *   max_len      the longest sequence allowed (>= 1); sets the split of the
+ *                cache and the workspace size.
+ *   q, lam, out  as for diffattn_v2_decode.
+ *   k_pages      logical [num_pages, page_size, Hkv, d] bf16 with roles
+ *   v_pages      b = page, h = kv head, t = row within the page.
+ *   num_pages    pages in the pool (>= 1).
+ *   page_size    tokens per page: a power of two, >= 16.
+ *   block_table  DEVICE int32 [B][bt_stride], bt_stride >=
+ *                ceil(max_len / page_size): token t of sequence b is row
+ *                t % page_size of page block_table[b*bt_stride + t/page_size].
+ *                Only the entries that cover t < seq_lens[b] are read.  An
+ *                entry outside [0, num_pages) is clamped into it (wrong
+ *                values, never an access outside the pool).
+ *   seq_lens     DEVICE int32 [B]: cache entries of each sequence, the new
+ *                token's included (the query attends to all of them).
+ *                Values are clamped to [0, max_len]; a sequence of length 0
+ *                gets an output of 0.
+ *   workspace    at least diffattn_v2_decode_paged_workspace_bytes(B,
+ *                max_len, Hq, Hkv, d) bytes, 16-byte aligned, owned by the
+ *                caller; contents on entry do not matter.
+ * Errors: DA_E_SHAPE also for a page_size that is not a power of two >= 16,
+ * num_pages < 1 or a bt_stride too small; DA_E_UNSUPPORTED if page_size times
+ * a token stride of k_pages / v_pages reaches 2^31 elements (rows within a
+ * page are addressed with 32-bit offsets); DA_E_NULL for a NULL block_table or
+ * seq_lens; DA_E_LAYOUT if either is not 4-byte aligned.  The table and the
+ * lengths live on the device and are not checked on the host.
+ * Two kernels are enqueued on `stream` (split, then merge).
+ */
+da_status diffattn_v2_decode_paged(da_dtype dtype, int B, int max_len, int Hq, int Hkv, int d,
+                                   da_in q, da_in k_pages, da_in v_pages,
+                                   int num_pages, int page_size,
+                                   const int32_t* block_table, int64_t bt_stride,
+                                   const int32_t* seq_lens, da_in lam, da_out out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+/* Off-by-one softmax variant of diffattn_v2_decode_paged (see the
+ * *_softmax1 entry points above); a sequence of length 0 also gets 0. */
+da_status diffattn_v2_decode_paged_softmax1(da_dtype dtype, int B, int max_len, int Hq, int Hkv,
+                                            int d, da_in q, da_in k_pages, da_in v_pages,
+                                            int num_pages, int page_size,
+                                            const int32_t* block_table, int64_t bt_stride,
+                                            const int32_t* seq_lens, da_in lam, da_out out,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream);
+
 /* lambda_init = 0.8 - 0.6*exp(-0.3*layer_index), as the V1 kernels use it
  * (computed on the host in double, handed to the device as float). */
 double diffattn_lambda_init(int layer_index);

@@ -15,6 +15,8 @@ numpy float64 arrays through ctypes.  Layouts are dense, as documented in
   out ``[B, T, Hq/2, d]``.
 * V2 decode: q ``[B, Hq, d]``; k, v ``[B, L, Hkv, d]``; lam ``[B, Hq/2]``;
   out ``[B, Hq/2, d]``.
+* V2 decode over a paged cache: k, v pages ``[num_pages, page_size, Hkv, d]``,
+  an int page table ``[B, >= ceil(L_b / page_size)]`` and lengths ``[B]``.
 """
 from __future__ import annotations
 
@@ -181,4 +183,38 @@ def v2_decode(q, k, v, lam, softmax1: bool = False) -> np.ndarray:
     B, L, Hq, Hkv, d = _v2_check(*t, decode=True)
     out = np.zeros((B, Hq // 2, d), dtype=np.float64)
     _load().da_oracle_v2_decode(B, L, Hq, Hkv, d, *[_p(x) for x in t], int(bool(softmax1)), _p(out))
+    return out
+
+
+def v2_decode_paged(q, k_pages, v_pages, block_table, seq_lens, lam, softmax1: bool = False) -> np.ndarray:
+    """DIFF V2 decode over a paged, ragged cache; returns ``[B, Hq/2, d]`` float64.
+
+    A page table only says where the cache entries are stored: token t of
+    sequence b is row ``t % page_size`` of page ``block_table[b, t // page_size]``
+    and the sequence holds ``seq_lens[b]`` entries.  Each sequence's entries
+    are gathered into a dense ``[L_b, Hkv, d]`` cache and decoded by
+    :func:`v2_decode` ("Differential Transformer V2" article, DiffAttnV2 at
+    the newest position).  The pages define no attention over an empty set:
+    a sequence of length 0 is given the output 0 (with the off-by-one softmax
+    that is also the limit, an extra zero key with a zero value).
+    """
+    q, kp, vp, lam = [_f64(x) for x in (q, k_pages, v_pages, lam)]
+    table = np.asarray(block_table, dtype=np.int64)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    B, Hq, d = q.shape
+    num_pages, page, Hkv, _ = kp.shape
+    assert vp.shape == kp.shape and kp.shape[3] == d
+    assert table.ndim == 2 and table.shape[0] == B and lens.shape == (B,)
+    assert lam.shape == (B, Hq // 2)
+    out = np.zeros((B, Hq // 2, d), dtype=np.float64)
+    for b in range(B):
+        L = int(lens[b])
+        if L == 0:
+            continue
+        t = np.arange(L)
+        pg = table[b, t // page]
+        assert ((pg >= 0) & (pg < num_pages)).all(), "page index outside the pool"
+        k = kp[pg, t % page]  # [L, Hkv, d]
+        v = vp[pg, t % page]
+        out[b] = v2_decode(q[b:b + 1], k[None], v[None], lam[b:b + 1], softmax1=softmax1)[0]
     return out

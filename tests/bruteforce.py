@@ -75,3 +75,28 @@ def v2_decode(q, k, v, lam):
     sees every cache entry."""
     a = _gqa_attention(q[:, None], k, v, causal=False)[:, 0]
     return a[:, 0::2] - expit(lam)[..., None] * a[:, 1::2]
+
+
+def v2_decode_paged(q, k_pages, v_pages, block_table, seq_lens, lam):
+    """Paged decode, one sequence and one token at a time: walk the page
+    table entry by entry (page j holds tokens j*P .. j*P + P - 1), copy each
+    stored row out, then decode the dense copy with :func:`v2_decode`.
+    A sequence of length 0 gives 0."""
+    B, Hq, d = q.shape
+    P, Hkv = k_pages.shape[1], k_pages.shape[2]
+    out = np.zeros((B, Hq // 2, d))
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        k = np.zeros((L, Hkv, d))
+        v = np.zeros((L, Hkv, d))
+        for j in range((L + P - 1) // P):
+            page = int(block_table[b][j])
+            for r in range(P):
+                t = j * P + r
+                if t < L:
+                    k[t] = k_pages[page][r]
+                    v[t] = v_pages[page][r]
+        out[b] = v2_decode(q[b:b + 1], k[None], v[None], lam[b:b + 1])[0]
+    return out

@@ -32,6 +32,8 @@ def test_header_declares_the_entry_points():
     syms = _declared_symbols()
     for need in ("diffattn_v1_fwd", "diffattn_v2_fwd", "diffattn_v2_decode",
                  "diffattn_v1_fwd_softmax1", "diffattn_v2_fwd_softmax1", "diffattn_v2_decode_softmax1",
+                 "diffattn_v2_decode_paged", "diffattn_v2_decode_paged_softmax1",
+                 "diffattn_v2_decode_paged_workspace_bytes",
                  "diffattn_v2_decode_workspace_bytes", "diffattn_status_string"):
         assert need in syms
 
@@ -145,3 +147,35 @@ def test_softmax1_entry_points_validate_like_their_namesakes(lib):
     need = lib.diffattn_v2_decode_workspace_bytes(2, 100, 8, 2, 128)
     dec = lambda f, ws: f(1, 2, 100, 8, 2, 128, _t(), _t(), _t(), _t(), _t(out=True), ws, need, None)
     assert dec(lib.diffattn_v2_decode_softmax1, 0) == dec(lib.diffattn_v2_decode, 0) == E_WS
+
+
+def _paged(lib, f=None, B=2, max_len=100, Hq=8, Hkv=2, d=128, num_pages=20, page=16, table=FAKE,
+           bt_stride=None, lens=FAKE, ws=FAKE, wsb=None, dtype=1, kst=None):
+    need = lib.diffattn_v2_decode_paged_workspace_bytes(B, max_len, Hq, Hkv, d)
+    bt = (max_len + page - 1) // page if bt_stride is None else bt_stride
+    kp = _t(sb=page * Hkv * d, sh=d, st=Hkv * d if kst is None else kst)
+    return (f or lib.diffattn_v2_decode_paged)(dtype, B, max_len, Hq, Hkv, d, _t(), kp, _t(sb=page * Hkv * d),
+                                               num_pages, page, table, bt, lens, _t(), _t(out=True), ws,
+                                               need if wsb is None else wsb, None)
+
+
+def test_paged_decode_validation(lib):
+    assert _paged(lib, max_len=0) == E_SHAPE
+    assert _paged(lib, num_pages=0) == E_SHAPE
+    assert _paged(lib, page=8) == E_SHAPE                    # below 16
+    assert _paged(lib, page=48) == E_SHAPE                   # not a power of two
+    assert _paged(lib, bt_stride=6) == E_SHAPE               # 100 tokens need 7 pages of 16
+    assert _paged(lib, Hq=10, Hkv=2) == E_SHAPE
+    assert _paged(lib, table=0) == E_NULL
+    assert _paged(lib, lens=0) == E_NULL
+    assert _paged(lib, table=FAKE + 2) == E_LAYOUT
+    assert _paged(lib, lens=FAKE + 1) == E_LAYOUT
+    assert _paged(lib, dtype=0) == E_UNSUP
+    assert _paged(lib, d=96) == E_UNSUP
+    assert _paged(lib, Hq=64, Hkv=2) == E_UNSUP
+    assert _paged(lib, page=1 << 16, kst=1 << 15) == E_UNSUP  # rows within a page need 32-bit offsets
+    assert _paged(lib, ws=0) == E_WS
+    assert _paged(lib, wsb=100) == E_WS
+    for kw in ({"page": 8}, {"table": 0}, {"dtype": 0}, {"ws": 0}):
+        assert _paged(lib, lib.diffattn_v2_decode_paged_softmax1, **kw) == _paged(lib, **kw) != OK
+

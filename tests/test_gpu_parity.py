@@ -388,6 +388,126 @@ def test_decode_prefix_mean_closed_form_full_size():
     torch.cuda.empty_cache()
 
 
+# ------------------------------------------------- V2 decode, paged and ragged
+
+def _paged_run(z, max_len, out=None, ws=None, softmax1=False):
+    o = binding.v2_decode_paged(z["q"], z["k_pages"], z["v_pages"], z["block_table"], z["seq_lens"], z["lam"],
+                                max_len, out=out, workspace=ws, softmax1=softmax1)
+    torch.cuda.synchronize()
+    return o
+
+
+def _paged_ref(z, softmax1=False):
+    c = {n: z[n].cpu() for n in z}
+    return oracle.v2_decode_paged(c["q"], c["k_pages"], c["v_pages"], c["block_table"].numpy(),
+                                  c["seq_lens"].numpy(), c["lam"], softmax1=softmax1)
+
+
+PAGED_LENS = [1, 15, 16, 17, 127, 128, 129, 640, 2047, 3001]
+
+
+@pytest.mark.parametrize("page", [16, 32, 64, 256])
+@pytest.mark.parametrize("G,d", [(2, 128), (8, 128), (8, 64), (16, 64)])
+def test_paged_decode_ragged(page, G, d):
+    Hkv = 2
+    z = workloads.paged_decode_inputs(len(PAGED_LENS), 3072, page, G * Hkv, Hkv, d, torch.bfloat16,
+                                      seed=500 + page + G + d, device=DEV, lens=PAGED_LENS)
+    out = _paged_run(z, 3072)
+    assert_bf16_close(out, _paged_ref(z), f"paged P{page} G{G} d{d}")
+
+
+def test_paged_identity_table_matches_dense_decode_bitwise():
+    """Pages laid end to end in sequence order and every length = L: the
+    paged kernel visits the same rows in the same order as the dense one, so
+    the outputs are bit-identical."""
+    B, L, Hq, Hkv, d, page = 3, 1000, 16, 2, 128, 16
+    z = workloads.decode_inputs(B, L, Hq, Hkv, d, torch.bfloat16, seed=520, device=DEV)
+    Lp = (L + page - 1) // page * page
+    pad = torch.zeros((B, Lp - L, Hkv, d), dtype=torch.bfloat16, device=DEV)
+    kp = torch.cat([z["k"], pad], 1).reshape(B * Lp // page, page, Hkv, d)
+    vp = torch.cat([z["v"], pad], 1).reshape(B * Lp // page, page, Hkv, d)
+    table = torch.arange(B * Lp // page, dtype=torch.int32, device=DEV).reshape(B, Lp // page)
+    lens = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    pz = {"q": z["q"], "k_pages": kp, "v_pages": vp, "block_table": table, "seq_lens": lens, "lam": z["lam"]}
+    assert torch.equal(_paged_run(pz, L), _dec_run(z))
+
+
+def test_paged_max_len_beyond_every_sequence():
+    """A max_len far above the lengths only adds empty splits."""
+    lens = [3, 200, 1]
+    z = workloads.paged_decode_inputs(3, 20000, 32, 16, 2, 128, torch.bfloat16, seed=530, device=DEV, lens=lens)
+    ref = _paged_ref(z)
+    assert_bf16_close(_paged_run(z, 20000), ref, "paged, long max_len")
+    z2 = dict(z, block_table=z["block_table"][:, :7].contiguous())  # 7 pages of 32 cover max_len 224
+    assert_bf16_close(_paged_run(z2, 224), ref, "paged, tight max_len")
+
+
+def test_paged_strided_pool_and_table():
+    """Pages stored head-major ([num_pages, Hkv, page, d], viewed as
+    [num_pages, page, Hkv, d]) and a table that is a column slice of a wider
+    one: the kernel follows the role strides."""
+    lens = [77, 500, 16, 1]
+    z = workloads.paged_decode_inputs(4, 512, 16, 8, 2, 64, torch.bfloat16, seed=540, device=DEV, lens=lens)
+    kp = z["k_pages"].transpose(1, 2).contiguous().transpose(1, 2)
+    vp = z["v_pages"].transpose(1, 2).contiguous().transpose(1, 2)
+    wide = torch.full((4, 64), -1, dtype=torch.int32, device=DEV)
+    wide[:, 5:5 + z["block_table"].shape[1]] = z["block_table"]
+    zs = dict(z, k_pages=kp, v_pages=vp, block_table=wide[:, 5:5 + z["block_table"].shape[1]])
+    assert zs["block_table"].stride(0) == 64 and kp.stride(1) == 64
+    assert_bf16_close(_paged_run(zs, 512), _paged_ref(z), "paged strided")
+
+
+def test_paged_length_zero_and_clamping():
+    """Documented edge cases: a length of 0 (or below) gives 0, a length
+    above max_len counts as max_len, a table entry outside the pool reads
+    the nearest page of the pool."""
+    lens = [0, 40, 64, 33]
+    z = workloads.paged_decode_inputs(4, 64, 16, 8, 2, 128, torch.bfloat16, seed=550, device=DEV, lens=lens)
+    n = z["k_pages"].shape[0]
+    bad = z["block_table"].clone()
+    bad[1, 0] = -5          # clamps to page 0
+    bad[2, 3] = n + 3       # clamps to page n-1
+    # sequence 3 (33 tokens, 3 pages) is given length 90: it reads 64 tokens,
+    # its fourth table entry (-1) included, which clamps to page 0
+    zc = dict(z, block_table=bad, seq_lens=torch.tensor([-4, 40, 64, 90], dtype=torch.int32, device=DEV))
+    out = _paged_run(zc, 64)
+    ref = _paged_ref(dict(z, block_table=bad.clamp(0, n - 1),
+                          seq_lens=torch.tensor([0, 40, 64, 64], dtype=torch.int32)))
+    assert torch.all(out[0] == 0)
+    assert_bf16_close(out, ref, "paged clamping")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_paged_softmax1(d):
+    z = workloads.paged_decode_inputs(len(PAGED_LENS), 3072, 64, 16, 2, d, torch.bfloat16, seed=560 + d,
+                                      device=DEV, lens=PAGED_LENS)
+    out = _paged_run(z, 3072, softmax1=True)
+    assert_bf16_close(out, _paged_ref(z, softmax1=True), f"paged softmax1 d{d}")
+
+
+def test_paged_full_sampled():
+    """The benchmarked ragged batch (64 sequences, lengths uniform in
+    [1, 32768], 64-token pages in a shuffled pool): sampled sequences against
+    the oracle, and bitwise determinism."""
+    w = WORKLOADS["v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128"]
+    z = workloads.inputs_for(w, DEV)
+    out = _paged_run(z, w.T)
+    assert torch.equal(out, _paged_run(z, w.T))
+    lens = z["seq_lens"].cpu()
+    picks = [int(lens.argmin()), int(lens.argmax()), 5, 40]
+    for b in picks:
+        L = int(lens[b])
+        pages = z["block_table"][b, :(L + w.page - 1) // w.page].long()
+        zb = {"q": z["q"][b:b + 1].cpu(), "k_pages": z["k_pages"][pages].cpu(), "v_pages": z["v_pages"][pages].cpu(),
+              "lam": z["lam"][b:b + 1].cpu()}
+        table = np.arange(len(pages))[None]
+        ref = oracle.v2_decode_paged(zb["q"], zb["k_pages"], zb["v_pages"], table, np.array([L]), zb["lam"])
+        got = host64(out[b:b + 1])
+        assert_bf16_close(got, ref, f"{w.name} b{b} L{L}")
+    del z
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ HIP graphs
 
 # ------------------------------------------------------- off-by-one softmax

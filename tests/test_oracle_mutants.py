@@ -115,3 +115,60 @@ def test_mutant_is_caught(name, tmp_path, restore_oracle):
     finally:
         oracle._lib = saved
     assert failed >= 1, f"no pin catches mutation {name}"
+
+
+# --------------------------------------------------------------------------
+# The paged decode's gather is Python (oracle.v2_decode_paged): its mutants
+# are textual replacements in that function's source, re-executed in the
+# oracle module's namespace.
+# --------------------------------------------------------------------------
+
+import inspect  # noqa: E402
+
+PAGED_SRC = inspect.getsource(oracle.v2_decode_paged)
+
+PAGED_MUTATIONS = {
+    # page and row swapped
+    "paged_page_row_swap": ("k = kp[pg, t % page]", "k = kp[t % page, pg % page]"),
+    # every sequence read through the first sequence's table row
+    "paged_first_row_only": ("pg = table[b, t // page]", "pg = table[0, t // page]"),
+    # the sequence's own length ignored (the table's full width used)
+    "paged_full_width": ("L = int(lens[b])", "L = int(lens.max())"),
+    # the newest entry of each sequence dropped
+    "paged_drops_last": ("t = np.arange(L)", "t = np.arange(max(L - 1, 1))"),
+    # V read from the K pool
+    "paged_v_from_k": ("v = vp[pg, t % page]", "v = kp[pg, t % page]"),
+}
+
+PAGED_PINS = [
+    lambda: pins.test_paged_decode_matches_bruteforce.hypothesis.inner_test(
+        lens=[5, 33, 1], page=4, Hkv=2, G=2, d=4, seed=4),
+    pins.test_paged_identity_table_is_the_dense_cache,
+    pins.test_paged_pool_permutation_invariance,
+    pins.test_paged_ragged_lengths_are_dense_prefixes,
+]
+
+
+def _failing_paged_pins():
+    failed = 0
+    for pin in PAGED_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, IndexError, ValueError):
+            failed += 1
+    return failed
+
+
+def test_paged_pins_pass_on_the_real_oracle():
+    assert _failing_paged_pins() == 0
+
+
+@pytest.mark.parametrize("name", sorted(PAGED_MUTATIONS))
+def test_paged_mutant_is_caught(name, monkeypatch):
+    old, new = PAGED_MUTATIONS[name]
+    assert PAGED_SRC.count(old) == 1, f"mutation {name} no longer matches the oracle source"
+    ns = dict(vars(oracle))
+    exec(compile(PAGED_SRC.replace(old, new), "<mutant>", "exec"), ns)
+    monkeypatch.setattr(oracle, "v2_decode_paged", ns["v2_decode_paged"])
+    assert _failing_paged_pins() >= 1, f"no pin catches mutation {name}"

@@ -416,3 +416,90 @@ def test_softmax1_equal_scores_closed_form(s):
     D = (1 - lam) * (n1 * math.exp(s) / (1 + n1 * math.exp(s))) * np.cumsum(v1, axis=2) / n1
     ref = (1 - li) * D / np.sqrt(np.mean(D * D, -1, keepdims=True) + 1e-5)
     _close(oracle.v1_fwd(q1, q1, k1, k1, v1, *lams, layer, softmax1=True), np.transpose(ref, (0, 2, 1, 3)))
+
+
+# --------------------------------------------------------------------------
+# V2 decode over a paged, ragged cache: a storage layout of the same decode
+# ("Differential Transformer V2" article, DiffAttnV2 at the newest position)
+# --------------------------------------------------------------------------
+
+def _paged_case(rng, lens, page, Hkv, G, d, spare=3):
+    """Random pages for sequences of lengths ``lens``: every page a sequence
+    uses is drawn without replacement from a shuffled pool with ``spare``
+    unused pages; returns (q, k_pages, v_pages, table, lens, lam)."""
+    B = len(lens)
+    npp = [max(1, (L + page - 1) // page) for L in lens]
+    width = max(npp)
+    pool = sum(npp) + spare
+    order = rng.permutation(pool)
+    table = np.full((B, width), -1, dtype=np.int64)
+    at = 0
+    for b in range(B):
+        table[b, :npp[b]] = order[at:at + npp[b]]
+        at += npp[b]
+    Hq = G * Hkv
+    q = rng.standard_normal((B, Hq, d))
+    kp = rng.standard_normal((pool, page, Hkv, d))
+    vp = rng.standard_normal((pool, page, Hkv, d))
+    lam = rng.standard_normal((B, Hq // 2))
+    return q, kp, vp, table, np.array(lens, dtype=np.int64), lam
+
+
+@settings(max_examples=30, deadline=None)
+@given(lens=st.lists(st.integers(0, 40), min_size=1, max_size=4), page=st.sampled_from([1, 2, 4, 16]),
+       Hkv=st.integers(1, 2), G=st.sampled_from([2, 4]), d=st.sampled_from([4, 8]), seed=st.integers(0, 10**6))
+def test_paged_decode_matches_bruteforce(lens, page, Hkv, G, d, seed):
+    q, kp, vp, table, ln, lam = _paged_case(_rng(seed), lens, page, Hkv, G, d)
+    got = oracle.v2_decode_paged(q, kp, vp, table, ln, lam)
+    _close(got, bruteforce.v2_decode_paged(q, kp, vp, table, ln, lam))
+
+
+def test_paged_identity_table_is_the_dense_cache():
+    """Pages laid end to end in sequence order (table[b, j] = b*n + j) are a
+    reshaped dense cache: the result is the dense decode's."""
+    rng = _rng(220)
+    B, L, Hkv, G, d, page = 3, 48, 2, 4, 8, 16
+    q = rng.standard_normal((B, G * Hkv, d))
+    k = rng.standard_normal((B, L, Hkv, d))
+    v = rng.standard_normal((B, L, Hkv, d))
+    lam = rng.standard_normal((B, G * Hkv // 2))
+    n = L // page
+    table = np.arange(B * n).reshape(B, n)
+    kp, vp = k.reshape(B * n, page, Hkv, d), v.reshape(B * n, page, Hkv, d)
+    got = oracle.v2_decode_paged(q, kp, vp, table, np.full(B, L), lam)
+    assert np.array_equal(got, oracle.v2_decode(q, k, v, lam))
+
+
+def test_paged_pool_permutation_invariance():
+    """Moving pages around the pool and rewriting the table to match leaves
+    every result bit-identical."""
+    rng = _rng(221)
+    q, kp, vp, table, ln, lam = _paged_case(rng, [37, 1, 64, 0, 16], 16, 2, 4, 8)
+    perm = rng.permutation(kp.shape[0])  # new slot of old page i is perm[i]
+    kq, vq = np.empty_like(kp), np.empty_like(vp)
+    kq[perm], vq[perm] = kp, vp
+    t2 = np.where(table >= 0, perm[np.maximum(table, 0)], -1)
+    a = oracle.v2_decode_paged(q, kp, vp, table, ln, lam)
+    assert np.array_equal(a, oracle.v2_decode_paged(q, kq, vq, t2, ln, lam))
+
+
+def test_paged_ragged_lengths_are_dense_prefixes():
+    """A sequence of length L_b decodes exactly the first L_b cache entries
+    (dense decode of the prefix); length 0 gives 0."""
+    rng = _rng(222)
+    lens = [1, 17, 32, 0, 45]
+    B, Lmax, Hkv, G, d, page = len(lens), 48, 2, 2, 8, 16
+    q = rng.standard_normal((B, G * Hkv, d))
+    k = rng.standard_normal((B, Lmax, Hkv, d))
+    v = rng.standard_normal((B, Lmax, Hkv, d))
+    lam = rng.standard_normal((B, G * Hkv // 2))
+    n = Lmax // page
+    table = np.arange(B * n).reshape(B, n)
+    got = oracle.v2_decode_paged(q, k.reshape(B * n, page, Hkv, d), v.reshape(B * n, page, Hkv, d),
+                                 table, np.array(lens), lam)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.array_equal(got[b], np.zeros_like(got[b]))
+        else:
+            ref = oracle.v2_decode(q[b:b + 1], k[b:b + 1, :L], v[b:b + 1, :L], lam[b:b + 1])[0]
+            assert np.array_equal(got[b], ref)
