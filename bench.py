@@ -16,7 +16,8 @@ The JSON line also carries:
   cpu_baseline  the fp64 oracle timed on a bounded sample of the same
                 workload on this host's cores;
   secondary     the other full-size workloads (3B-class V1, V2 GQA prefill,
-                V2 decode, V2 decode of a ragged batch over a paged cache),
+                V2 decode, V2 decode of a ragged batch over a paged cache, V2
+                decode of 4 new tokens per sequence),
                 each with its own roofline; a secondary step is
                 8 launches of the workload (warm-up ~0.3 s of its own calls).
 Logs go to stderr; stdout holds exactly one JSON line.
@@ -38,7 +39,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 HEADLINE = "v1_gpt2small_B8_H6_T1024_d64"
 SECONDARY = ["v1_3b_B2_H12_T4096_d128", "v2_prefill_B1_T8192_Hq64_Hkv8_d128", "v2_decode_B64_L32768_Hq64_Hkv8_d128",
-             "v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128"]
+             "v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128", "v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128"]
 
 
 def log(*a):
@@ -58,10 +59,16 @@ def _caller(w, x, binding, torch, softmax1=False):
     dev = x["q"].device
     out = torch.empty((w.B, w.Hq // 2, w.d), dtype=w.torch_dtype, device=dev)
     if w.kind == "decode_paged":
-        ws = torch.empty(binding.v2_decode_paged_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.d), dtype=torch.uint8,
+        ws = torch.empty(binding.v2_decode_paged_workspace_bytes(w.B, w.T, 1, w.Hq, w.Hkv, w.d), dtype=torch.uint8,
                          device=dev)
         return lambda layer: binding.v2_decode_paged(x["q"], x["k_pages"], x["v_pages"], x["block_table"],
                                                      x["seq_lens"], x["lam"], w.T, out=out, workspace=ws,
+                                                     softmax1=softmax1)
+    if w.kind == "decode_multi":
+        out = torch.empty((w.B, w.nq, w.Hq // 2, w.d), dtype=w.torch_dtype, device=dev)
+        ws = torch.empty(binding.v2_decode_multi_workspace_bytes(w.B, w.T, w.nq, w.Hq, w.Hkv, w.d), dtype=torch.uint8,
+                         device=dev)
+        return lambda layer: binding.v2_decode_multi(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws,
                                                      softmax1=softmax1)
     ws = torch.empty(binding.v2_decode_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.d), dtype=torch.uint8, device=dev)
     return lambda layer: binding.v2_decode(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws,
@@ -119,7 +126,7 @@ def _timed(torch, call, layers, steps, warmup, graph=True):
 
 def _roofline(w, launch_ms):
     avg_s = sum(launch_ms) / len(launch_ms) / 1e3
-    if w.kind in ("decode", "decode_paged"):
+    if w.kind in ("decode", "decode_paged", "decode_multi"):
         a = w.compulsory_bytes() / avg_s / 1e9
         return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(a / PEAK_HBM_GBS, 4), "traffic": None,
@@ -162,7 +169,7 @@ def _source_sha(kind):
     import hashlib
 
     src = {"v1": "prefill_bf16.hip", "v2": "prefill_bf16.hip", "decode": "decode_bf16.hip",
-           "decode_paged": "decode_bf16.hip"}[kind]
+           "decode_paged": "decode_bf16.hip", "decode_multi": "decode_bf16.hip"}[kind]
     path = os.path.join(ROOT, "differential_attention_diffattn_amd", "csrc", src)
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
@@ -332,6 +339,9 @@ def main():
         elif w.kind == "decode_paged":
             res.update(metric="V2 paged ragged decode HBM GB/s (bytes of the sequences' own lengths)",
                        unit="GB/s", value=round(w.compulsory_bytes() / per_call_s / 1e9, 1))
+        elif w.kind == "decode_multi":
+            res.update(metric=f"V2 decode of {w.nq} new tokens per sequence, HBM GB/s", unit="GB/s",
+                       value=round(w.compulsory_bytes() / per_call_s / 1e9, 1))
         else:
             res.update(metric="causal fwd TFLOP/s", unit="TFLOP/s", value=round(w.flops() / per_call_s / 1e12, 3))
         log(json.dumps(res))

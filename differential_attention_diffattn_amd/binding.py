@@ -12,8 +12,11 @@ Logical layouts (any strided view with a unit-stride last axis is accepted):
              returns / writes out [B,T,Hq/2,d]
   v2_decode  q [B,Hq,d]; k_cache, v_cache [B,L,Hkv,d]; lam [B,Hq/2] fp32;
              returns / writes out [B,Hq/2,d]
+  v2_decode_multi
+             q [B,nq,Hq,d]; k_cache, v_cache [B,L,Hkv,d] holding the nq new tokens
+             last; lam [B,nq,Hq/2] fp32; returns / writes out [B,nq,Hq/2,d]
   v2_decode_paged
-             q [B,Hq,d]; k_pages, v_pages [num_pages,page_size,Hkv,d];
+             q [B,Hq,d] or [B,nq,Hq,d]; k_pages, v_pages [num_pages,page_size,Hkv,d];
              block_table int32 [B, >= ceil(max_len/page_size)]; seq_lens
              int32 [B]; lam [B,Hq/2] fp32; returns / writes out [B,Hq/2,d]
 Each takes ``softmax1=True`` for the off-by-one softmax entry points
@@ -75,12 +78,17 @@ def load_library():
         f = getattr(lib, "diffattn_v2_decode" + sfx)
         f.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaOut, vp, ctypes.c_size_t, vp]
         f.restype = i
+        f = getattr(lib, "diffattn_v2_decode_multi" + sfx)
+        f.argtypes = [i, i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaOut, vp, ctypes.c_size_t, vp]
+        f.restype = i
         f = getattr(lib, "diffattn_v2_decode_paged" + sfx)
-        f.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, i, i, vp, ctypes.c_int64, vp, DaIn, DaOut, vp,
+        f.argtypes = [i, i, i, i, i, i, i, DaIn, DaIn, DaIn, i, i, vp, ctypes.c_int64, vp, DaIn, DaOut, vp,
                       ctypes.c_size_t, vp]
         f.restype = i
-    for f in (lib.diffattn_v2_decode_workspace_bytes, lib.diffattn_v2_decode_paged_workspace_bytes):
-        f.argtypes = [i, i, i, i, i]
+    lib.diffattn_v2_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.diffattn_v2_decode_workspace_bytes.restype = ctypes.c_size_t
+    for f in (lib.diffattn_v2_decode_multi_workspace_bytes, lib.diffattn_v2_decode_paged_workspace_bytes):
+        f.argtypes = [i, i, i, i, i, i]
         f.restype = ctypes.c_size_t
     lib.diffattn_lambda_init.argtypes = [i]
     lib.diffattn_lambda_init.restype = ctypes.c_double
@@ -182,8 +190,12 @@ def v2_decode_workspace_bytes(B: int, L: int, Hq: int, Hkv: int, d: int) -> int:
     return int(load_library().diffattn_v2_decode_workspace_bytes(B, L, Hq, Hkv, d))
 
 
-def v2_decode_paged_workspace_bytes(B: int, max_len: int, Hq: int, Hkv: int, d: int) -> int:
-    return int(load_library().diffattn_v2_decode_paged_workspace_bytes(B, max_len, Hq, Hkv, d))
+def v2_decode_multi_workspace_bytes(B: int, L: int, nq: int, Hq: int, Hkv: int, d: int) -> int:
+    return int(load_library().diffattn_v2_decode_multi_workspace_bytes(B, L, nq, Hq, Hkv, d))
+
+
+def v2_decode_paged_workspace_bytes(B: int, max_len: int, nq: int, Hq: int, Hkv: int, d: int) -> int:
+    return int(load_library().diffattn_v2_decode_paged_workspace_bytes(B, max_len, nq, Hq, Hkv, d))
 
 
 def v2_decode(q, k_cache, v_cache, lam, out: torch.Tensor | None = None,
@@ -212,13 +224,45 @@ def v2_decode(q, k_cache, v_cache, lam, out: torch.Tensor | None = None,
     return out
 
 
+def v2_decode_multi(q, k_cache, v_cache, lam, out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None, softmax1: bool = False):
+    """DIFF V2 decode of nq new tokens; q [B,nq,Hq,d], caches [B,L,Hkv,d] (the new tokens are the
+    last nq entries), lam [B,nq,Hq/2]; returns [B,nq,Hq/2,d]."""
+    lib = load_library()
+    B, nq, Hq, d = q.shape
+    L, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, L, Hkv, d) or tuple(v_cache.shape) != (B, L, Hkv, d):
+        raise ValueError("caches must be [B,L,Hkv,d]")
+    if tuple(lam.shape) != (B, nq, Hq // 2) or lam.dtype != torch.float32:
+        raise ValueError("lam must be fp32 [B,nq,Hq/2]")
+    if out is None:
+        out = torch.empty((B, nq, Hq // 2, d), dtype=q.dtype, device=q.device)
+    need = v2_decode_multi_workspace_bytes(B, L, nq, Hq, Hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_device(q, k_cache, v_cache, out)
+    name = "diffattn_v2_decode_multi" + ("_softmax1" if softmax1 else "")
+    st = getattr(lib, name)(_dtype_code(q), B, L, nq, Hq, Hkv, d, _in(q, 0, 2, 1), _in(k_cache, 0, 2, 1),
+                            _in(v_cache, 0, 2, 1), _in(lam, 0, 2, 1), _out(out, 0, 2, 1), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), _stream(q))
+    if st != 0:
+        raise DiffAttnError(st, name)
+    return out
+
+
 def v2_decode_paged(q, k_pages, v_pages, block_table, seq_lens, lam, max_len: int,
                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                     softmax1: bool = False):
-    """DIFF V2 decode over a paged cache; q [B,Hq,d], pages [num_pages,page_size,Hkv,d],
-    block_table int32 [B, >= ceil(max_len/page_size)], seq_lens int32 [B]; returns [B,Hq/2,d]."""
+    """DIFF V2 decode over a paged cache; q [B,Hq,d] (one new token, returns [B,Hq/2,d]) or
+    [B,nq,Hq,d] (nq new tokens, the last nq entries of each sequence; lam [B,nq,Hq/2]; returns
+    [B,nq,Hq/2,d]); pages [num_pages,page_size,Hkv,d], block_table int32
+    [B, >= ceil(max_len/page_size)], seq_lens int32 [B]."""
     lib = load_library()
-    B, Hq, d = q.shape
+    multi = q.dim() == 4
+    if multi:
+        B, nq, Hq, d = q.shape
+    else:
+        (B, Hq, d), nq = q.shape, 1
     num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
     if tuple(k_pages.shape) != (num_pages, page_size, Hkv, d) or tuple(v_pages.shape) != tuple(k_pages.shape):
         raise ValueError("k_pages, v_pages must be [num_pages,page_size,Hkv,d]")
@@ -230,19 +274,21 @@ def v2_decode_paged(q, k_pages, v_pages, block_table, seq_lens, lam, max_len: in
         raise ValueError("seq_lens must be a contiguous int32 [B]")
     if block_table.shape[1] * page_size < max_len:
         raise ValueError("block_table has too few columns for max_len")
-    if tuple(lam.shape) != (B, Hq // 2) or lam.dtype != torch.float32:
-        raise ValueError("lam must be fp32 [B,Hq/2]")
+    lam_shape = (B, nq, Hq // 2) if multi else (B, Hq // 2)
+    if tuple(lam.shape) != lam_shape or lam.dtype != torch.float32:
+        raise ValueError(f"lam must be fp32 {list(lam_shape)}")
     if out is None:
-        out = torch.empty((B, Hq // 2, d), dtype=q.dtype, device=q.device)
-    need = v2_decode_paged_workspace_bytes(B, max_len, Hq, Hkv, d)
+        out = torch.empty(((B, nq) if multi else (B,)) + (Hq // 2, d), dtype=q.dtype, device=q.device)
+    need = v2_decode_paged_workspace_bytes(B, max_len, nq, Hq, Hkv, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check_device(q, k_pages, v_pages, out, block_table, seq_lens)
     name = "diffattn_v2_decode_paged" + ("_softmax1" if softmax1 else "")
-    st = getattr(lib, name)(_dtype_code(q), B, int(max_len), Hq, Hkv, d, _in(q, 0, 1, None),
+    ax = (0, 2, 1) if multi else (0, 1, None)  # (b, h, t) axes of q / lam / out
+    st = getattr(lib, name)(_dtype_code(q), B, int(max_len), nq, Hq, Hkv, d, _in(q, *ax),
                             _in(k_pages, 0, 2, 1), _in(v_pages, 0, 2, 1), num_pages, page_size,
                             block_table.data_ptr(), block_table.stride(0), seq_lens.data_ptr(),
-                            _in(lam, 0, 1, None), _out(out, 0, 1, None), workspace.data_ptr(),
+                            _in(lam, *ax), _out(out, *ax), workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), _stream(q))
     if st != 0:
         raise DiffAttnError(st, name)

@@ -69,6 +69,104 @@ da_status validate_v2_common(da_dtype dtype, int B, int T, int Hq, int Hkv, int 
   return DA_OK;
 }
 
+// Split geometry of a decode call: nq query tokens x G heads form the
+// columns a workgroup scores 16 or 32 at a time (column groups); the cache is
+// split along its length for B x column groups x Hkv units.
+struct DecodeGeom {
+  int ncg;
+  da::DecodeSplit sp;
+};
+DecodeGeom decode_geom(int B, int L, int nq, int Hq, int Hkv, int max_chunk) {
+  DecodeGeom r;
+  r.ncg = da::decode_column_groups(nq, Hq / Hkv);
+  r.sp = da::decode_split(B * r.ncg, L, Hkv, max_chunk);
+  return r;
+}
+bool decode_sizes_ok(int B, int L, int nq, int Hq, int Hkv, int d) {
+  if (B < 1 || L < 1 || nq < 1 || Hq < 1 || Hkv < 1 || d < 1) return false;
+  if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return false;
+  return (long long)B * nq <= 0x7fffffffLL && (long long)nq * Hq <= 0x7fffffffLL;
+}
+size_t decode_ws_bytes(int B, int L, int nq, int Hq, int Hkv, int d, int max_chunk) {
+  if (!decode_sizes_ok(B, L, nq, Hq, Hkv, d)) return 0;
+  const DecodeGeom gm = decode_geom(B, L, nq, Hq, Hkv, max_chunk);
+  return (size_t)B * Hkv * gm.sp.nsplit * (size_t)nq * (size_t)(Hq / Hkv) * (size_t)(d + 2) * sizeof(float);
+}
+
+// Shared by the dense and paged decode entry points.  q, lam and out carry a
+// token axis (stride st) only when nq > 1.  Paged: k / v are page pools and
+// `pg` describes the table; dense: pg.block_table is null.
+struct PagedArgs {
+  int num_pages, page_size;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  const int32_t* seq_lens;
+};
+da_status decode_impl(int softmax1, da_dtype dtype, int B, int L, int nq, int Hq, int Hkv, int d, da_in q,
+                      da_in kc, da_in vc, const PagedArgs* pg, da_in lam, da_out out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
+  if (!decode_sizes_ok(B, L, nq, Hq, Hkv, d)) return DA_E_SHAPE;
+  if (!pg && nq > L) return DA_E_SHAPE;  // the new tokens are the last nq cache entries
+  const int page_size = pg ? pg->page_size : 0;
+  if (pg) {
+    if (pg->num_pages < 1) return DA_E_SHAPE;
+    if (page_size < 16 || page_size > (1 << 30) || (page_size & (page_size - 1)) != 0) return DA_E_SHAPE;
+    if (pg->bt_stride < ((int64_t)L + page_size - 1) / page_size) return DA_E_SHAPE;
+  }
+  const int64_t mult = dtype == DA_BF16 ? 8 : 4;
+  const int64_t qst = nq > 1 ? q.st : 0, ost = nq > 1 ? out.st : 0;
+  DA_TRY(check_rows(q.ptr, q.sb, q.sh, qst, mult));
+  DA_TRY(check_in(kc, mult));
+  DA_TRY(check_in(vc, mult));
+  if (pg) {
+    if (!pg->block_table || !pg->seq_lens) return DA_E_NULL;
+    if (!aligned(pg->block_table, 4) || !aligned(pg->seq_lens, 4)) return DA_E_LAYOUT;
+  }
+  da_in lam2 = lam;
+  lam2.st = nq > 1 ? lam.st : 0;
+  DA_TRY(check_logits(lam2));
+  DA_TRY(check_rows(out.ptr, out.sb, out.sh, ost, mult));
+  DA_TRY(validate_v2_common(dtype, B, L, Hq, Hkv, d));
+  if (Hq / Hkv > 16) return DA_E_UNSUPPORTED;  // one 16-wide MFMA column block per head group
+  if (pg) {  // the kernel addresses a row within a page with a 32-bit element offset
+    if ((int64_t)page_size * kc.st >= (int64_t(1) << 31) || (int64_t)page_size * vc.st >= (int64_t(1) << 31))
+      return DA_E_UNSUPPORTED;
+  }
+  const int max_chunk = pg ? da::kPagedMaxChunk : 2048;
+  const size_t need = decode_ws_bytes(B, L, nq, Hq, Hkv, d, max_chunk);
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return DA_E_WORKSPACE;
+  const DecodeGeom gm = decode_geom(B, L, nq, Hq, Hkv, max_chunk);
+  if (!grid_fits(da::decode_split_grid(B * gm.ncg, Hkv, gm.sp.nsplit)) || !grid_fits((long long)B * nq * (Hq / 2)))
+    return DA_E_SHAPE;
+
+  da::DecodeArgs a{};
+  a.q = TIn{q.ptr, q.sb, q.sh, qst};
+  a.k = tin(kc);
+  a.v = tin(vc);
+  a.lam = TIn{lam.ptr, lam.sb, lam.sh, lam2.st};
+  a.out = TOut{out.ptr, out.sb, out.sh, ost};
+  a.ws = (float*)workspace;
+  a.sl2 = log2e_over_sqrt(d);
+  a.B = B, a.L = L, a.Hq = Hq, a.Hkv = Hkv, a.G = Hq / Hkv;
+  a.chunk = gm.sp.chunk;
+  a.nsplit = gm.sp.nsplit;
+  a.nq = nq;
+  a.ncg = gm.ncg;
+  a.softmax1 = softmax1;
+  if (pg) {
+    a.block_table = pg->block_table;
+    a.bt_stride = pg->bt_stride;
+    a.seq_lens = pg->seq_lens;
+    int shift = 0;
+    while ((1 << shift) < page_size) ++shift;
+    a.page_shift = shift;
+    a.page_mask = page_size - 1;
+    a.num_pages = pg->num_pages;
+  }
+  return launch_status(da::launch_decode_bf16(d, a, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -163,112 +261,17 @@ static da_status v2_fwd_impl(int softmax1, da_dtype dtype, int B, int T, int Hq,
   return launch_status(da::launch_prefill_v2_bf16(d, a, (hipStream_t)stream));
 }
 
+
 size_t diffattn_v2_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int d) {
-  if (B < 1 || L < 1 || Hq < 1 || Hkv < 1 || d < 1) return 0;
-  if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return 0;
-  const da::DecodeSplit sp = da::decode_split(B, L, Hkv);
-  return (size_t)B * Hkv * sp.nsplit * (size_t)(Hq / Hkv) * (size_t)(d + 2) * sizeof(float);
+  return decode_ws_bytes(B, L, 1, Hq, Hkv, d, 2048);
 }
 
-size_t diffattn_v2_decode_paged_workspace_bytes(int B, int max_len, int Hq, int Hkv, int d) {
-  if (B < 1 || max_len < 1 || Hq < 1 || Hkv < 1 || d < 1) return 0;
-  if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return 0;
-  const da::DecodeSplit sp = da::decode_split(B, max_len, Hkv, da::kPagedMaxChunk);
-  return (size_t)B * Hkv * sp.nsplit * (size_t)(Hq / Hkv) * (size_t)(d + 2) * sizeof(float);
+size_t diffattn_v2_decode_multi_workspace_bytes(int B, int L, int nq, int Hq, int Hkv, int d) {
+  return decode_ws_bytes(B, L, nq, Hq, Hkv, d, 2048);
 }
 
-static da_status v2_decode_impl(int softmax1, da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
-                                da_in k_cache,
-                             da_in v_cache, da_in lam, da_out out, void* workspace, size_t workspace_bytes,
-                             void* stream) {
-  if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
-  if (B < 1 || L < 1 || Hq < 1 || Hkv < 1 || d < 1) return DA_E_SHAPE;
-  if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return DA_E_SHAPE;
-  const int64_t mult = dtype == DA_BF16 ? 8 : 4;
-  // q, lam and out have no token axis: their st is ignored.
-  DA_TRY(check_rows(q.ptr, q.sb, q.sh, 0, mult));
-  DA_TRY(check_in(k_cache, mult));
-  DA_TRY(check_in(v_cache, mult));
-  da_in lam2 = lam;
-  lam2.st = 0;
-  DA_TRY(check_logits(lam2));
-  DA_TRY(check_rows(out.ptr, out.sb, out.sh, 0, mult));
-  DA_TRY(validate_v2_common(dtype, B, L, Hq, Hkv, d));
-  if (Hq / Hkv > 16) return DA_E_UNSUPPORTED;  // one 16-wide MFMA column block per group
-  const size_t need = diffattn_v2_decode_workspace_bytes(B, L, Hq, Hkv, d);
-  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return DA_E_WORKSPACE;
-  const da::DecodeSplit sp = da::decode_split(B, L, Hkv);
-  if (!grid_fits(da::decode_split_grid(B, Hkv, sp.nsplit)) || !grid_fits((long long)B * (Hq / 2))) return DA_E_SHAPE;
-
-  da::DecodeArgs a{};
-  a.q = TIn{q.ptr, q.sb, q.sh, 0};
-  a.k = tin(k_cache);
-  a.v = tin(v_cache);
-  a.lam = TIn{lam.ptr, lam.sb, lam.sh, 0};
-  a.out = TOut{out.ptr, out.sb, out.sh, 0};
-  a.ws = (float*)workspace;
-  a.sl2 = log2e_over_sqrt(d);
-  a.B = B, a.L = L, a.Hq = Hq, a.Hkv = Hkv, a.G = Hq / Hkv;
-  a.chunk = sp.chunk;
-  a.nsplit = sp.nsplit;
-  a.softmax1 = softmax1;
-  return launch_status(da::launch_decode_bf16(d, a, (hipStream_t)stream));
-}
-
-// Paged, ragged cache: k_pages / v_pages are [num_pages, page_size, Hkv, d]
-// with roles (b = page, h = kv head, t = row in the page).
-static da_status v2_decode_paged_impl(int softmax1, da_dtype dtype, int B, int max_len, int Hq, int Hkv, int d,
-                                      da_in q, da_in k_pages, da_in v_pages, int num_pages, int page_size,
-                                      const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
-                                      da_in lam, da_out out, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
-  if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
-  if (B < 1 || max_len < 1 || Hq < 1 || Hkv < 1 || d < 1 || num_pages < 1) return DA_E_SHAPE;
-  if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return DA_E_SHAPE;
-  if (page_size < 16 || page_size > (1 << 30) || (page_size & (page_size - 1)) != 0) return DA_E_SHAPE;
-  const int64_t pages_per_seq = ((int64_t)max_len + page_size - 1) / page_size;
-  if (bt_stride < pages_per_seq) return DA_E_SHAPE;
-  const int64_t mult = dtype == DA_BF16 ? 8 : 4;
-  DA_TRY(check_rows(q.ptr, q.sb, q.sh, 0, mult));
-  DA_TRY(check_in(k_pages, mult));
-  DA_TRY(check_in(v_pages, mult));
-  if (!block_table || !seq_lens) return DA_E_NULL;
-  if (!aligned(block_table, 4) || !aligned(seq_lens, 4)) return DA_E_LAYOUT;
-  da_in lam2 = lam;
-  lam2.st = 0;
-  DA_TRY(check_logits(lam2));
-  DA_TRY(check_rows(out.ptr, out.sb, out.sh, 0, mult));
-  DA_TRY(validate_v2_common(dtype, B, max_len, Hq, Hkv, d));
-  if (Hq / Hkv > 16) return DA_E_UNSUPPORTED;  // one 16-wide MFMA column block per group
-  // the kernel addresses a row within a page with a 32-bit element offset
-  if ((int64_t)page_size * k_pages.st >= (int64_t(1) << 31) || (int64_t)page_size * v_pages.st >= (int64_t(1) << 31))
-    return DA_E_UNSUPPORTED;
-  const size_t need = diffattn_v2_decode_paged_workspace_bytes(B, max_len, Hq, Hkv, d);
-  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return DA_E_WORKSPACE;
-  const da::DecodeSplit sp = da::decode_split(B, max_len, Hkv, da::kPagedMaxChunk);
-  if (!grid_fits(da::decode_split_grid(B, Hkv, sp.nsplit)) || !grid_fits((long long)B * (Hq / 2))) return DA_E_SHAPE;
-
-  da::DecodeArgs a{};
-  a.q = TIn{q.ptr, q.sb, q.sh, 0};
-  a.k = tin(k_pages);
-  a.v = tin(v_pages);
-  a.lam = TIn{lam.ptr, lam.sb, lam.sh, 0};
-  a.out = TOut{out.ptr, out.sb, out.sh, 0};
-  a.ws = (float*)workspace;
-  a.sl2 = log2e_over_sqrt(d);
-  a.B = B, a.L = max_len, a.Hq = Hq, a.Hkv = Hkv, a.G = Hq / Hkv;
-  a.chunk = sp.chunk;
-  a.nsplit = sp.nsplit;
-  a.softmax1 = softmax1;
-  a.block_table = block_table;
-  a.bt_stride = bt_stride;
-  a.seq_lens = seq_lens;
-  int shift = 0;
-  while ((1 << shift) < page_size) ++shift;
-  a.page_shift = shift;
-  a.page_mask = page_size - 1;
-  a.num_pages = num_pages;
-  return launch_status(da::launch_decode_bf16(d, a, (hipStream_t)stream));
+size_t diffattn_v2_decode_paged_workspace_bytes(int B, int max_len, int nq, int Hq, int Hkv, int d) {
+  return decode_ws_bytes(B, max_len, nq, Hq, Hkv, d, da::kPagedMaxChunk);
 }
 
 da_status diffattn_v1_fwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
@@ -299,33 +302,49 @@ da_status diffattn_v2_fwd_softmax1(da_dtype dtype, int B, int T, int Hq, int Hkv
 da_status diffattn_v2_decode(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
                              da_in v_cache, da_in lam, da_out out, void* workspace, size_t workspace_bytes,
                              void* stream) {
-  return v2_decode_impl(0, dtype, B, L, Hq, Hkv, d, q, k_cache, v_cache, lam, out, workspace, workspace_bytes,
-                        stream);
+  return decode_impl(0, dtype, B, L, 1, Hq, Hkv, d, q, k_cache, v_cache, nullptr, lam, out, workspace,
+                     workspace_bytes, stream);
 }
 
 da_status diffattn_v2_decode_softmax1(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
                                       da_in k_cache, da_in v_cache, da_in lam, da_out out, void* workspace,
                                       size_t workspace_bytes, void* stream) {
-  return v2_decode_impl(1, dtype, B, L, Hq, Hkv, d, q, k_cache, v_cache, lam, out, workspace, workspace_bytes,
-                        stream);
+  return decode_impl(1, dtype, B, L, 1, Hq, Hkv, d, q, k_cache, v_cache, nullptr, lam, out, workspace,
+                     workspace_bytes, stream);
 }
 
-da_status diffattn_v2_decode_paged(da_dtype dtype, int B, int max_len, int Hq, int Hkv, int d, da_in q,
+da_status diffattn_v2_decode_multi(da_dtype dtype, int B, int L, int nq, int Hq, int Hkv, int d, da_in q,
+                                   da_in k_cache, da_in v_cache, da_in lam, da_out out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return decode_impl(0, dtype, B, L, nq, Hq, Hkv, d, q, k_cache, v_cache, nullptr, lam, out, workspace,
+                     workspace_bytes, stream);
+}
+
+da_status diffattn_v2_decode_multi_softmax1(da_dtype dtype, int B, int L, int nq, int Hq, int Hkv, int d,
+                                            da_in q, da_in k_cache, da_in v_cache, da_in lam, da_out out,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(1, dtype, B, L, nq, Hq, Hkv, d, q, k_cache, v_cache, nullptr, lam, out, workspace,
+                     workspace_bytes, stream);
+}
+
+da_status diffattn_v2_decode_paged(da_dtype dtype, int B, int max_len, int nq, int Hq, int Hkv, int d, da_in q,
                                    da_in k_pages, da_in v_pages, int num_pages, int page_size,
                                    const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                                    da_in lam, da_out out, void* workspace, size_t workspace_bytes,
                                    void* stream) {
-  return v2_decode_paged_impl(0, dtype, B, max_len, Hq, Hkv, d, q, k_pages, v_pages, num_pages, page_size,
-                              block_table, bt_stride, seq_lens, lam, out, workspace, workspace_bytes, stream);
+  const PagedArgs pg{num_pages, page_size, block_table, bt_stride, seq_lens};
+  return decode_impl(0, dtype, B, max_len, nq, Hq, Hkv, d, q, k_pages, v_pages, &pg, lam, out, workspace,
+                     workspace_bytes, stream);
 }
 
-da_status diffattn_v2_decode_paged_softmax1(da_dtype dtype, int B, int max_len, int Hq, int Hkv, int d, da_in q,
-                                            da_in k_pages, da_in v_pages, int num_pages, int page_size,
+da_status diffattn_v2_decode_paged_softmax1(da_dtype dtype, int B, int max_len, int nq, int Hq, int Hkv, int d,
+                                            da_in q, da_in k_pages, da_in v_pages, int num_pages, int page_size,
                                             const int32_t* block_table, int64_t bt_stride,
                                             const int32_t* seq_lens, da_in lam, da_out out, void* workspace,
                                             size_t workspace_bytes, void* stream) {
-  return v2_decode_paged_impl(1, dtype, B, max_len, Hq, Hkv, d, q, k_pages, v_pages, num_pages, page_size,
-                              block_table, bt_stride, seq_lens, lam, out, workspace, workspace_bytes, stream);
+  const PagedArgs pg{num_pages, page_size, block_table, bt_stride, seq_lens};
+  return decode_impl(1, dtype, B, max_len, nq, Hq, Hkv, d, q, k_pages, v_pages, &pg, lam, out, workspace,
+                     workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -1,7 +1,8 @@
-// decode_bf16.hip -- DIFF V2 decode: one new query token per sequence against
-// a long KV cache ("Differential Transformer V2" article: DiffAttnV2 at the
-// newest position; the remark that decoding is memory-bound and that the
-// paired heads of one GQA group share key and value).
+// decode_bf16.hip -- DIFF V2 decode: one (or nq) new query tokens per
+// sequence against a long KV cache ("Differential Transformer V2" article:
+// DiffAttnV2 at the newest positions; the remark that decoding is
+// memory-bound and that the paired heads of one GQA group share key and
+// value).
 //
 // The cache is the only large operand (B*L*Hkv*d*2 bf16), so the kernel is
 // built to stream it from HBM exactly once:
@@ -21,6 +22,10 @@
 // The paged variant (PAGED) reads the cache through a per-sequence page table
 // and stops at each sequence's own length; splits past that length leave an
 // empty partial (max -inf), which the merges skip.
+// Several new tokens (nq > 1, the last nq cache entries): the MFMA columns
+// are (query token, head) pairs instead of heads, 16 per column block and
+// NCB = 1 or 2 blocks per workgroup, so one pass over the cache serves up to
+// 32 of them; new token i masks the entries after its own position.
 #include <math.h>
 
 #include "kernels.hpp"
@@ -40,8 +45,8 @@ __device__ __forceinline__ void lds_fence() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-template <int D, bool PAGED>
-__global__ void __launch_bounds__(kWaves * 64) decode_split_kernel(const DecodeArgs a) {
+template <int D, bool PAGED, int NCB>
+__global__ void __launch_bounds__(kWaves * 64, NCB == 1 ? 1 : 2) decode_split_kernel(const DecodeArgs a) {
   constexpr int KS = D / 32;   // k-steps of the score MFMA
   constexpr int CB = D / 16;   // 16-wide column blocks of O^T
   constexpr int VROW = kBlk + kVtPad;
@@ -50,54 +55,68 @@ __global__ void __launch_bounds__(kWaves * 64) decode_split_kernel(const DecodeA
   static_assert(VU >= 1 && (kBlk / 4) * (D / 8) % 64 == 0, "V block split");
   static_assert(kBlk == 32, "a step is two 16-token sub-blocks");
   constexpr int LDS_VT = kWaves * VT_ELEMS * 2;            // bytes
-  constexpr int LDS_RED = kWaves * 16 * (D + 2) * 4;       // bytes
+  constexpr int LDS_RED = kWaves * 16 * (D + 2) * 4;       // bytes (one column block at a time)
   constexpr int LDS_BYTES = LDS_VT > LDS_RED ? LDS_VT : LDS_RED;
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, kg = lane >> 4;
 
-  // Workgroup -> (sequence b, kv head g, split s).  The hardware deals
-  // consecutive workgroups to the 8 XCDs in turn (XCD = id mod 8).
+  // Workgroup -> (sequence b, column group cg, kv head g, split s).  A
+  // "column" is one (query token, head of the group) pair; a workgroup scores
+  // 16 NCB of them (column group cg), the pair (b, cg) acting as one virtual
+  // sequence vb.  The hardware deals consecutive workgroups to the 8 XCDs in
+  // turn (XCD = id mod 8).
   //  * dense (every sequence L long, uniform work): split fastest, then kv
-  //    head, then sequence (with nsplit a multiple of 8, XCD x takes the
-  //    splits s = x mod 8 of every (b, g)).
+  //    head, then virtual sequence (with nsplit a multiple of 8, XCD x takes
+  //    the splits s = x mod 8 of every (vb, g)).
   //  * paged (ragged lengths: the late splits of short sequences are empty):
   //    the dense order would give the XCDs holding the early splits most of
-  //    the work.  A "unit" is one split of one sequence; units are numbered
-  //    split-major with the sequence index rotated by the split, all kv heads
-  //    of a unit go to one XCD, and XCD x takes every 8th unit, so each XCD
-  //    gets every split of a spread of sequences.  The grid is padded to a
-  //    multiple of 8 units.
+  //    the work.  A "unit" is one split of one virtual sequence; units are
+  //    numbered split-major with the sequence index rotated by the split, all
+  //    kv heads of a unit go to one XCD, and XCD x takes every 8th unit, so
+  //    each XCD gets every split of a spread of sequences.  The grid is
+  //    padded to a multiple of 8 units.
   // Measured on MI355X: the paged order is 1.46x the dense order's rate on a
   // ragged batch (lengths uniform in [1, 32768]); the dense order is 1.06x
   // the paged order's on uniform lengths.
   const int bid = blockIdx.x;
-  int b, g, s;
+  const int VB = a.B * a.ncg;
+  int vb, g, s;
   if constexpr (PAGED) {
     const int xcd = bid & 7, j = bid >> 3;
     g = j % a.Hkv;
     const int unit = (j / a.Hkv) * 8 + xcd;
-    if (unit >= a.B * a.nsplit) return;  // padding (uniform over the workgroup)
-    s = unit / a.B;
-    b = (unit % a.B + s) % a.B;
+    if (unit >= VB * a.nsplit) return;  // padding (uniform over the workgroup)
+    s = unit / VB;
+    vb = (unit % VB + s) % VB;
   } else {
-    if (bid >= a.B * a.Hkv * a.nsplit) return;  // padding
+    if (bid >= VB * a.Hkv * a.nsplit) return;  // padding
     s = bid % a.nsplit;
     g = (bid / a.nsplit) % a.Hkv;
-    b = bid / (a.nsplit * a.Hkv);
+    vb = bid / (a.nsplit * a.Hkv);
   }
-  const int G = a.G;
+  const int b = vb / a.ncg, cg = vb % a.ncg;
+  const int G = a.G, NQ = a.nq, NC = NQ * G;
   // tokens of this sequence (paged: its own length, at most the longest)
   const int L = PAGED ? min(max(a.seq_lens[b], 0), a.L) : a.L;
 
-  // q fragments: B operand of S = K q^T.  Lane column = head (c16 < G).
-  bf16x8 qf[KS];
-  {
-    const uint16_t* qrow = (const uint16_t*)a.q.p + b * a.q.sb + (int64_t)(g * G + c16) * a.q.sh;
+  // q fragments: B operand of S = K q^T.  Column n*16 + c16 of the group is
+  // query token qi, head hh; it sees cache entries t < lim (the new tokens
+  // are the last NQ entries, each seeing itself and what precedes it).
+  bf16x8 qf[NCB][KS];
+  int lim[NCB];
+#pragma unroll
+  for (int n = 0; n < NCB; ++n) {
+    const int col = (cg * NCB + n) * 16 + c16;
+    const bool valid = col < NC;
+    const int qi = valid ? col / G : 0, hh = valid ? col % G : 0;
+    lim[n] = valid ? L - NQ + 1 + qi : L;
+    const uint16_t* qrow =
+        (const uint16_t*)a.q.p + b * a.q.sb + (int64_t)qi * a.q.st + (int64_t)(g * G + hh) * a.q.sh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = as_bf16x8(c16 < G ? *(const uint4*)(qrow + 32 * ks + 8 * kg) : make_uint4(0, 0, 0, 0));
+      qf[n][ks] = as_bf16x8(valid ? *(const uint4*)(qrow + 32 * ks + 8 * kg) : make_uint4(0, 0, 0, 0));
   }
   const uint16_t* kbase = (const uint16_t*)a.k.p + (PAGED ? 0 : b * a.k.sb) + g * a.k.sh;
   const uint16_t* vbase = (const uint16_t*)a.v.p + (PAGED ? 0 : b * a.v.sb) + g * a.v.sh;
@@ -118,10 +137,15 @@ __global__ void __launch_bounds__(kWaves * 64) decode_split_kernel(const DecodeA
 
   uint16_t* vt = (uint16_t*)smem + wave * VT_ELEMS;
   const float sl2 = a.sl2;
-  float mref = -INFINITY, lsum = 0.f;
-  f32x4 o[CB];
+  float mref[NCB], lsum[NCB];
+  f32x4 o[NCB][CB];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < NCB; ++n) {
+    mref[n] = -INFINITY;
+    lsum[n] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) o[n][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int t0 = s * a.chunk, t1 = min(L, t0 + a.chunk);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -173,44 +197,53 @@ __global__ void __launch_bounds__(kWaves * 64) decode_split_kernel(const DecodeA
       raw[0] = table_entry(nb), raw[1] = table_entry(nb + 16);
     }
 
-    // ---- scores: S[tok][head], two 16-token sub-blocks ----
-    f32x4 sc[2];
+    // ---- scores S[tok][col], softmax state per column ----
+    bf16x8 pk[NCB];  // slot t: token 4kg+t (t<4), 16+4kg+t-4 (t>=4)
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      sc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NCB; ++n) {
+      f32x4 sc[2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sc[sub] = mfma16x16x32(as_bf16x8(kr[sub][ks]), qf[ks], sc[sub]);
-    }
-    // lane (head c16, kg) holds tokens blk + 16*sub + 4*kg + r
-    float mx = -INFINITY;
+      for (int sub = 0; sub < 2; ++sub) {
+        sc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+        for (int ks = 0; ks < KS; ++ks) sc[sub] = mfma16x16x32(as_bf16x8(kr[sub][ks]), qf[n][ks], sc[sub]);
+      }
+      // lane (column c16, kg) holds tokens blk + 16*sub + 4*kg + r
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (blk + 16 * sub + 4 * kg + r >= lim[n]) sc[sub][r] = -INFINITY;
+          mx = fmaxf(mx, sc[sub][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // -inf when the whole block is masked for this column (a later query
+      // token's entries only); then nothing changes below
+      const float mb = mx * sl2;
+      const bool need = mb > mref[n] + kLazyLog2;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float al = need ? exp2f(mref[n] - mb) : 1.f;
+        if (need) mref[n] = mb;
+        lsum[n] *= al;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) o[n][cb] *= al;
+      }
+      // a column that has seen no visible entry yet has every score -inf:
+      // use 0 for its reference so the probabilities are 0, not NaN
+      const float nm = mref[n] == -INFINITY ? 0.f : -mref[n];
+      f32x8 p;
+      float ps = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (blk + 16 * sub + 4 * kg + r >= L) sc[sub][r] = -INFINITY;
-        mx = fmaxf(mx, sc[sub][r]);
+        p[r] = __builtin_amdgcn_exp2f(fmaf(sc[0][r], sl2, nm));
+        p[r + 4] = __builtin_amdgcn_exp2f(fmaf(sc[1][r], sl2, nm));
+        ps += p[r] + p[r + 4];
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mb = mx * sl2;  // finite: token blk < L is in every block (blk < t1 <= L)
-    const bool need = mb > mref + kLazyLog2;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float al = need ? exp2f(mref - mb) : 1.f;
-      if (need) mref = mb;
-      lsum *= al;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) o[cb] *= al;
+      lsum[n] += ps;
+      pk[n] = cvt_bf16x8(p);
     }
-    f32x8 p;
-    float ps = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(fmaf(sc[0][r], sl2, -mref));
-      p[r + 4] = __builtin_amdgcn_exp2f(fmaf(sc[1][r], sl2, -mref));
-      ps += p[r] + p[r + 4];
-    }
-    lsum += ps;
-    const bf16x8 pk = cvt_bf16x8(p);  // slot t: token 4kg+t (t<4), 16+4kg+t-4 (t>=4)
 
     // ---- V block -> V^T in this wave's LDS slice ----
 #pragma unroll
@@ -222,66 +255,77 @@ __global__ void __launch_bounds__(kWaves * 64) decode_split_kernel(const DecodeA
         *(uint2*)(vt + (cc * 8 + e) * VROW + 4 * rg) = column4(vr[u][0], vr[u][1], vr[u][2], vr[u][3], e);
     }
     lds_fence();
-    // ---- O^T[c][head] += V^T[c][tok] P^T[tok][head] ----
+    // ---- O^T[c][col] += V^T[c][tok] P^T[tok][col] ----
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const uint16_t* row = vt + (16 * cb + c16) * VROW + 4 * kg;
       const bf16x8 va = join_bf16x8(*(const uint2*)row, *(const uint2*)(row + 16));
-      o[cb] = mfma16x16x32(va, pk, o[cb]);
+#pragma unroll
+      for (int n = 0; n < NCB; ++n) o[n][cb] = mfma16x16x32(va, pk[n], o[n][cb]);
     }
     lds_fence();
   }
 
-  // ---- per-wave state -> LDS, then a log-sum-exp merge across the 4 waves ----
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  __syncthreads();  // all waves are done with their V^T slices
-  float* red = (float*)smem;  // [wave][head 16][D + 2]: m, l, O[D]
-  {
-    float* mine = red + (wave * 16 + c16) * (D + 2);
-    if (kg == 0) {
-      mine[0] = mref;
-      mine[1] = lsum;
+  // ---- per column block: per-wave state -> LDS, then a log-sum-exp merge
+  // across the 4 waves; one partial per (b, g, split, column) ----
+  float* red = (float*)smem;  // [wave][column 16][D + 2]: m, l, O[D]
+  float* out = a.ws + (((int64_t)b * a.Hkv + g) * a.nsplit + s) * (int64_t)NC * (D + 2);
+#pragma unroll
+  for (int n = 0; n < NCB; ++n) {
+    float l = lsum[n];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    __syncthreads();  // all waves are done with their V^T slices / the previous block's reads
+    {
+      float* mine = red + (wave * 16 + c16) * (D + 2);
+      if (kg == 0) {
+        mine[0] = mref[n];
+        mine[1] = l;
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mine[2 + 16 * cb + 4 * kg + r] = o[n][cb][r];
     }
+    __syncthreads();
+    const int col0 = (cg * NCB + n) * 16;
+    const int ncols = min(16, NC - col0);
+    for (int e = tid; e < ncols * (D + 2); e += kWaves * 64) {
+      const int hh = e / (D + 2), c = e % (D + 2);
+      float M = -INFINITY;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[(w * 16 + hh) * (D + 2)]);
+      float acc = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mine[2 + 16 * cb + 4 * kg + r] = o[cb][r];
-  }
-  __syncthreads();
-  float* out = a.ws + (((int64_t)b * a.Hkv + g) * a.nsplit + s) * (int64_t)G * (D + 2);
-  for (int e = tid; e < G * (D + 2); e += kWaves * 64) {
-    const int hh = e / (D + 2), c = e % (D + 2);
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[(w * 16 + hh) * (D + 2)]);
-    float acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = red[(w * 16 + hh) * (D + 2)];
-      const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-      acc += (c == 0 ? 0.f : red[(w * 16 + hh) * (D + 2) + c]) * f;
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = red[(w * 16 + hh) * (D + 2)];
+        const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+        acc += (c == 0 ? 0.f : red[(w * 16 + hh) * (D + 2) + c]) * f;
+      }
+      out[(int64_t)(col0 + hh) * (D + 2) + c] = c == 0 ? M : acc;
     }
-    out[hh * (D + 2) + c] = c == 0 ? M : acc;
   }
 }
 
 template <int D>
 __global__ void __launch_bounds__(D) decode_merge_kernel(const DecodeArgs a) {
+  // workgroup -> (sequence b, query token qi, pair p)
   const int P = a.Hq / 2;
-  const int b = blockIdx.x / P, p = blockIdx.x % P;
+  const int p = blockIdx.x % P;
+  const int qi = (blockIdx.x / P) % a.nq;
+  const int b = blockIdx.x / (P * a.nq);
   const int c = threadIdx.x;
-  const int G = a.G;
+  const int G = a.G, NC = a.nq * G;
   float res[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int head = 2 * p + k;
-    const int g = head / G, hh = head % G;
-    const float* base = a.ws + ((int64_t)b * a.Hkv + g) * a.nsplit * (int64_t)G * (D + 2) + hh * (D + 2);
-    const int64_t sstride = (int64_t)G * (D + 2);
+    const int g = head / G, col = qi * G + head % G;
+    const float* base = a.ws + ((int64_t)b * a.Hkv + g) * a.nsplit * (int64_t)NC * (D + 2) + (int64_t)col * (D + 2);
+    const int64_t sstride = (int64_t)NC * (D + 2);
     float M = -INFINITY;
     for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, base[s * sstride]);
-    if (M == -INFINITY) {  // no token at all (a paged sequence of length 0): no contribution
+    if (M == -INFINITY) {  // no visible entry at all (e.g. a paged sequence of length 0): no contribution
       res[k] = 0.f;
       continue;
     }
@@ -294,22 +338,23 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(const DecodeArgs a) {
     // off-by-one softmax: one more logit 0, i.e. 2^(0 - M) against the merged max
     res[k] = acc / (l + (a.softmax1 ? exp2f(-M) : 0.f));
   }
-  const float lg = ((const float*)a.lam.p)[b * a.lam.sb + p * a.lam.sh];
+  const float lg = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)qi * a.lam.st + p * a.lam.sh];
   const float val = res[0] - sigmoid_f32(lg) * res[1];
-  uint16_t* dst = (uint16_t*)a.out.p + b * a.out.sb + p * a.out.sh;
+  uint16_t* dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)qi * a.out.st + p * a.out.sh;
   const uint32_t w = pack_bf16x2(val, 0.f);
   dst[c] = (uint16_t)(w & 0xffffu);
 }
 
-template <int D>
+template <int D, int NCB>
 hipError_t launch(const DecodeArgs& a, hipStream_t st) {
   const void* args[] = {&a};
-  const void* split = a.block_table ? (const void*)decode_split_kernel<D, true> : (const void*)decode_split_kernel<D, false>;
-  hipError_t e = hipLaunchKernel(split, dim3(decode_split_grid(a.B, a.Hkv, a.nsplit)), dim3(kWaves * 64),
+  const void* split = a.block_table ? (const void*)decode_split_kernel<D, true, NCB>
+                                    : (const void*)decode_split_kernel<D, false, NCB>;
+  hipError_t e = hipLaunchKernel(split, dim3(decode_split_grid(a.B * a.ncg, a.Hkv, a.nsplit)), dim3(kWaves * 64),
                                  (void**)args, 0, st);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel((const void*)decode_merge_kernel<D>, dim3(a.B * (a.Hq / 2)), dim3(D), (void**)args, 0,
-                         st);
+  return hipLaunchKernel((const void*)decode_merge_kernel<D>, dim3(a.B * a.nq * (a.Hq / 2)), dim3(D), (void**)args,
+                         0, st);
 }
 
 }  // namespace
@@ -338,9 +383,18 @@ long long decode_split_grid(int B, int Hkv, int nsplit) {
   return (units + 7) / 8 * 8 * Hkv;
 }
 
+int decode_column_blocks(int nq, int G) { return nq * G <= 16 ? 1 : 2; }
+
+int decode_column_groups(int nq, int G) {
+  const int per = 16 * decode_column_blocks(nq, G);
+  return (nq * G + per - 1) / per;
+}
+
 hipError_t launch_decode_bf16(int d, const DecodeArgs& a, hipStream_t s) {
-  if (d == 64) return launch<64>(a, s);
-  if (d == 128) return launch<128>(a, s);
+  const int ncb = decode_column_blocks(a.nq, a.G);
+  if (a.ncg != decode_column_groups(a.nq, a.G)) return hipErrorInvalidValue;
+  if (d == 64) return ncb == 1 ? launch<64, 1>(a, s) : launch<64, 2>(a, s);
+  if (d == 128) return ncb == 1 ? launch<128, 1>(a, s) : launch<128, 2>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -61,6 +61,8 @@ struct DecodeArgs {
   int B, L, Hq, Hkv, G;
   int chunk;   // tokens per split (multiple of 128)
   int nsplit;
+  int nq;      // query tokens per sequence (the last nq cache entries; q/lam/out token stride st)
+  int ncg;     // column groups: (query token, head) columns are scored 16 or 32 per workgroup
   int softmax1;  // 1: off-by-one softmax (each head's denominator + exp(0))
   // Paged cache (null block_table: the dense [B, L, Hkv, d] cache of k / v):
   // token t of sequence b is row (t & page_mask) of page
@@ -75,6 +77,9 @@ struct DecodeArgs {
 hipError_t launch_decode_bf16(int d, const DecodeArgs& a, hipStream_t s);
 // workgroups of the decode split kernel (B * nsplit units padded to a multiple of 8, times Hkv)
 long long decode_split_grid(int B, int Hkv, int nsplit);
+// 16-wide column blocks per workgroup (1 or 2) and column groups for nq query tokens x G heads
+int decode_column_blocks(int nq, int G);
+int decode_column_groups(int nq, int G);
 
 // Decode split geometry, shared by the workspace query and the launcher.
 struct DecodeSplit {

@@ -32,7 +32,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "v1", "v2", "decode", "decode_paged"
+    kind: str  # "v1", "v2", "decode", "decode_paged", "decode_multi"
     dtype: str  # "fp32" or "bf16"
     B: int
     H: int = 0  # V1: differential heads
@@ -43,6 +43,7 @@ class Workload:
     layers: Tuple[int, ...] = ()
     seed: int = 0
     page: int = 0  # decode_paged: tokens per cache page (T is then the longest length)
+    nq: int = 0    # decode_multi: new tokens per sequence (the last nq of the T cache entries)
 
     def seq_lens(self) -> torch.Tensor:
         """decode_paged: the seeded sequence lengths (CPU int32 [B])."""
@@ -63,6 +64,8 @@ class Workload:
             return 2.0 * self.B * self.Hq * self.d * self.T * (self.T + 1)
         if self.kind == "decode_paged":
             return 4.0 * self.Hq * self.d * int(self.seq_lens().sum())
+        if self.kind == "decode_multi":  # new token i sees T - nq + i + 1 entries
+            return 4.0 * self.B * self.Hq * self.d * sum(self.T - self.nq + i + 1 for i in range(self.nq))
         return 4.0 * self.B * self.Hq * self.d * self.T
 
     def compulsory_bytes(self) -> int:
@@ -82,6 +85,9 @@ class Workload:
             table = 4 * int(((lens + self.page - 1) // self.page).sum())  # the entries a call reads
             return (e * (B * Hq * d + 2 * tokens * Hkv * d + B * (Hq // 2) * d) + 4 * B * (Hq // 2) + table
                     + 4 * B)
+        if self.kind == "decode_multi":
+            nq = self.nq
+            return e * (B * nq * Hq * d + 2 * B * L * Hkv * d + B * nq * (Hq // 2) * d) + 4 * B * nq * (Hq // 2)
         return e * (B * Hq * d + 2 * B * L * Hkv * d + B * (Hq // 2) * d) + 4 * B * (Hq // 2)
 
 
@@ -97,6 +103,8 @@ WORKLOADS: Dict[str, Workload] = {
                  Hkv=8, seed=5),
         Workload("v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128", "decode_paged", "bf16", B=64, T=32768,
                  d=128, Hq=64, Hkv=8, seed=6, page=64),
+        Workload("v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128", "decode_multi", "bf16", B=64, T=32768, d=128,
+                 Hq=64, Hkv=8, seed=7, nq=4),
     ]
 }
 
@@ -167,6 +175,19 @@ def decode_inputs(B: int, L: int, Hq: int, Hkv: int, d: int, dtype=torch.bfloat1
     }
 
 
+def decode_multi_inputs(B: int, L: int, nq: int, Hq: int, Hkv: int, d: int, dtype=torch.bfloat16, seed: int = 0,
+                        device="cpu") -> Dict[str, torch.Tensor]:
+    """Multi-token decode: q ``[B, nq, Hq, d]``; k_cache, v_cache ``[B, L, Hkv, d]``
+    (the nq new tokens are the last nq entries); lam ``[B, nq, Hq/2]`` fp32."""
+    g = _gen(seed, device)
+    return {
+        "q": _randn((B, nq, Hq, d), g, device, dtype),
+        "k": _randn((B, L, Hkv, d), g, device, dtype, chunk_rows=4),
+        "v": _randn((B, L, Hkv, d), g, device, dtype, chunk_rows=4),
+        "lam": _randn((B, nq, Hq // 2), g, device, torch.float32),
+    }
+
+
 def draw_seq_lens(B: int, max_len: int, seed: int) -> torch.Tensor:
     """Lengths uniform in [1, max_len], CPU int32 [B]."""
     g = torch.Generator().manual_seed(int(seed) + 7919)
@@ -174,13 +195,15 @@ def draw_seq_lens(B: int, max_len: int, seed: int) -> torch.Tensor:
 
 
 def paged_decode_inputs(B: int, max_len: int, page: int, Hq: int, Hkv: int, d: int, dtype=torch.bfloat16,
-                        seed: int = 0, device="cpu", lens=None, spare_pages: int = 3) -> Dict[str, torch.Tensor]:
+                        seed: int = 0, device="cpu", lens=None, spare_pages: int = 3,
+                        nq: int = 0) -> Dict[str, torch.Tensor]:
     """Decode over a paged cache.  lens: the sequence lengths (default: uniform
     in [1, max_len]); q ``[B, Hq, d]``; k_pages, v_pages ``[num_pages, page,
     Hkv, d]`` (dtype) with num_pages = the pages the sequences need +
     ``spare_pages``; block_table int32 ``[B, ceil(max_len / page)]``: the
     sequences' pages in a seeded random order of the pool, -1 past each
-    sequence's last page; seq_lens int32 ``[B]``; lam ``[B, Hq/2]`` fp32."""
+    sequence's last page; seq_lens int32 ``[B]``; lam ``[B, Hq/2]`` fp32.
+    nq > 0: q ``[B, nq, Hq, d]`` and lam ``[B, nq, Hq/2]`` (nq new tokens)."""
     lens = draw_seq_lens(B, max_len, seed) if lens is None else torch.tensor(list(lens), dtype=torch.int32)
     width = (max_len + page - 1) // page
     need = [(int(L) + page - 1) // page for L in lens]
@@ -194,13 +217,14 @@ def paged_decode_inputs(B: int, max_len: int, page: int, Hq: int, Hkv: int, d: i
         at += n
     g = _gen(seed, device)
     rows = max(1, (64 << 20) // (page * Hkv * d * 4))  # bound the fp32 temporary to ~64 MB
+    tok = (nq,) if nq > 0 else ()
     return {
-        "q": _randn((B, Hq, d), g, device, dtype),
+        "q": _randn((B,) + tok + (Hq, d), g, device, dtype),
         "k_pages": _randn((num_pages, page, Hkv, d), g, device, dtype, chunk_rows=rows),
         "v_pages": _randn((num_pages, page, Hkv, d), g, device, dtype, chunk_rows=rows),
         "block_table": table.to(device),
         "seq_lens": lens.to(device),
-        "lam": _randn((B, Hq // 2), g, device, torch.float32),
+        "lam": _randn((B,) + tok + (Hq // 2,), g, device, torch.float32),
     }
 
 
@@ -211,4 +235,6 @@ def inputs_for(w: Workload, device="cpu") -> Dict[str, torch.Tensor]:
         return v2_inputs(w.B, w.T, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)
     if w.kind == "decode_paged":
         return paged_decode_inputs(w.B, w.T, w.page, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)
+    if w.kind == "decode_multi":
+        return decode_multi_inputs(w.B, w.T, w.nq, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)
     return decode_inputs(w.B, w.T, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)

@@ -190,17 +190,50 @@ da_status diffattn_v2_decode_softmax1(da_dtype dtype, int B, int L, int Hq, int 
                                       void* stream);
 
 /*
+ * DIFF V2 decode of nq new tokens per sequence at once (multi-token, e.g.
+ * speculative, decoding).  The cache of L entries already holds the nq new
+ * tokens at positions L-nq .. L-1; new token i (0-based) attends, causally,
+ * to entries j <= L-nq+i -- the last nq rows of DiffAttnV2 over the cache
+ * ("Differential Transformer V2" article, DiffAttnV2 pseudo-code; decoding
+ * is memory-bound, so the cache is streamed once for all nq tokens):
+ *   a_{i,h} = softmax_{j <= L-nq+i}( q[b,i,h] . k[b,j,g] / sqrt(d) ) v[b,:,g]
+ *   out[b,i,p,:] = a_{i,2p} - sigmoid(lam[b,i,p]) * a_{i,2p+1}
+ * With nq = 1 this is diffattn_v2_decode.
+ *
+ *   dtype, d, Hq, Hkv   as for diffattn_v2_decode.   1 <= nq <= L.
+ *   q          logical [B,nq,Hq,d]   (roles b, h, t = new token)
+ *   k_cache    logical [B,L,Hkv,d]   (roles b, h, t)
+ *   v_cache    logical [B,L,Hkv,d]   (roles b, h, t)
+ *   lam        logical [B,nq,Hq/2] fp32 logits (roles b, h = pair, t)
+ *   out        logical [B,nq,Hq/2,d] bf16 (roles b, h = pair, t)
+ *   workspace  at least diffattn_v2_decode_multi_workspace_bytes(B, L, nq,
+ *              Hq, Hkv, d) bytes, 16-byte aligned, owned by the caller.
+ * The cache is read once per group of 16 (Hq/Hkv*nq <= 16) or 32 (query
+ * token, head) pairs of a kv head.  Two kernels are enqueued on `stream`.
+ */
+size_t diffattn_v2_decode_multi_workspace_bytes(int B, int L, int nq, int Hq, int Hkv, int d);
+da_status diffattn_v2_decode_multi(da_dtype dtype, int B, int L, int nq, int Hq, int Hkv, int d,
+                                   da_in q, da_in k_cache, da_in v_cache, da_in lam,
+                                   da_out out, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+/* Off-by-one softmax variant of diffattn_v2_decode_multi. */
+da_status diffattn_v2_decode_multi_softmax1(da_dtype dtype, int B, int L, int nq, int Hq, int Hkv,
+                                            int d, da_in q, da_in k_cache, da_in v_cache,
+                                            da_in lam, da_out out, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace diffattn_v2_decode_paged (and its _softmax1
  * variant) needs for these sizes (0 if the sizes are invalid); it depends
- * only on (B, max_len, Hq, Hkv, d).
+ * only on (B, max_len, nq, Hq, Hkv, d).
  */
-size_t diffattn_v2_decode_paged_workspace_bytes(int B, int max_len, int Hq, int Hkv, int d);
+size_t diffattn_v2_decode_paged_workspace_bytes(int B, int max_len, int nq, int Hq, int Hkv, int d);
 
 /*
  * DIFF V2 decode over a paged, ragged KV cache.  Per sequence b it computes
- * exactly what diffattn_v2_decode computes ("Differential Transformer V2"
- * article: DiffAttnV2 at the newest position) with L = seq_lens[b]; only the
- * storage of the cache differs.  The pages define the attention, not this
+ * exactly what diffattn_v2_decode_multi computes ("Differential Transformer
+ * V2" article: DiffAttnV2 at the newest positions) with L = seq_lens[b]; only
+ * the storage of the cache differs (nq = 1: one new token per sequence).  The pages define the attention, not this
  * layout: it is the serving layout in which sequences of different lengths
  * share one pool of fixed-size cache pages.
  *
@@ -208,7 +241,9 @@ size_t diffattn_v2_decode_paged_workspace_bytes(int B, int max_len, int Hq, int 
  *                even and <= 16.
  *   max_len      the longest sequence allowed (>= 1); sets the split of the
  *                cache and the workspace size.
- *   q, lam, out  as for diffattn_v2_decode.
+ *   nq           new tokens per sequence (>= 1), the last nq of its entries.
+ *   q, lam, out  as for diffattn_v2_decode_multi (token axis used when
+ *                nq > 1).
  *   k_pages      logical [num_pages, page_size, Hkv, d] bf16 with roles
  *   v_pages      b = page, h = kv head, t = row within the page.
  *   num_pages    pages in the pool (>= 1).
@@ -221,11 +256,12 @@ size_t diffattn_v2_decode_paged_workspace_bytes(int B, int max_len, int Hq, int 
  *                values, never an access outside the pool).
  *   seq_lens     DEVICE int32 [B]: cache entries of each sequence, the new
  *                token's included (the query attends to all of them).
- *                Values are clamped to [0, max_len]; a sequence of length 0
- *                gets an output of 0.
+ *                Values are clamped to [0, max_len]; a new token that sees
+ *                no entry (a sequence shorter than nq, or of length 0) gets
+ *                an output of 0.
  *   workspace    at least diffattn_v2_decode_paged_workspace_bytes(B,
- *                max_len, Hq, Hkv, d) bytes, 16-byte aligned, owned by the
- *                caller; contents on entry do not matter.
+ *                max_len, nq, Hq, Hkv, d) bytes, 16-byte aligned, owned by
+ *                the caller; contents on entry do not matter.
  * Errors: DA_E_SHAPE also for a page_size that is not a power of two >= 16,
  * num_pages < 1 or a bt_stride too small; DA_E_UNSUPPORTED if page_size times
  * a token stride of k_pages / v_pages reaches 2^31 elements (rows within a
@@ -234,7 +270,7 @@ size_t diffattn_v2_decode_paged_workspace_bytes(int B, int max_len, int Hq, int 
  * lengths live on the device and are not checked on the host.
  * Two kernels are enqueued on `stream` (split, then merge).
  */
-da_status diffattn_v2_decode_paged(da_dtype dtype, int B, int max_len, int Hq, int Hkv, int d,
+da_status diffattn_v2_decode_paged(da_dtype dtype, int B, int max_len, int nq, int Hq, int Hkv, int d,
                                    da_in q, da_in k_pages, da_in v_pages,
                                    int num_pages, int page_size,
                                    const int32_t* block_table, int64_t bt_stride,
@@ -242,8 +278,8 @@ da_status diffattn_v2_decode_paged(da_dtype dtype, int B, int max_len, int Hq, i
                                    void* workspace, size_t workspace_bytes, void* stream);
 /* Off-by-one softmax variant of diffattn_v2_decode_paged (see the
  * *_softmax1 entry points above); a sequence of length 0 also gets 0. */
-da_status diffattn_v2_decode_paged_softmax1(da_dtype dtype, int B, int max_len, int Hq, int Hkv,
-                                            int d, da_in q, da_in k_pages, da_in v_pages,
+da_status diffattn_v2_decode_paged_softmax1(da_dtype dtype, int B, int max_len, int nq, int Hq,
+                                            int Hkv, int d, da_in q, da_in k_pages, da_in v_pages,
                                             int num_pages, int page_size,
                                             const int32_t* block_table, int64_t bt_stride,
                                             const int32_t* seq_lens, da_in lam, da_out out,

@@ -186,6 +186,27 @@ def v2_decode(q, k, v, lam, softmax1: bool = False) -> np.ndarray:
     return out
 
 
+def v2_decode_multi(q, k, v, lam, softmax1: bool = False) -> np.ndarray:
+    """DIFF V2 decode of nq new tokens per sequence; q ``[B, nq, Hq, d]``, k, v
+    ``[B, L, Hkv, d]`` (the new tokens are the last nq entries), lam
+    ``[B, nq, Hq/2]``; returns ``[B, nq, Hq/2, d]`` float64.
+
+    New token i sits at cache position L - nq + i and, as a row of causal
+    DiffAttnV2 ("Differential Transformer V2" article, DiffAttnV2
+    pseudo-code), attends to positions 0 .. L - nq + i: it is the single-token
+    decode over that prefix of the cache.
+    """
+    q, k, v, lam = [_f64(x) for x in (q, k, v, lam)]
+    B, nq, Hq, d = q.shape
+    L = k.shape[1]
+    assert 1 <= nq <= L and lam.shape == (B, nq, Hq // 2)
+    out = np.zeros((B, nq, Hq // 2, d), dtype=np.float64)
+    for i in range(nq):
+        n = L - nq + i + 1  # visible entries of new token i
+        out[:, i] = v2_decode(q[:, i], k[:, :n], v[:, :n], lam[:, i], softmax1=softmax1)
+    return out
+
+
 def v2_decode_paged(q, k_pages, v_pages, block_table, seq_lens, lam, softmax1: bool = False) -> np.ndarray:
     """DIFF V2 decode over a paged, ragged cache; returns ``[B, Hq/2, d]`` float64.
 
@@ -194,13 +215,18 @@ def v2_decode_paged(q, k_pages, v_pages, block_table, seq_lens, lam, softmax1: b
     and the sequence holds ``seq_lens[b]`` entries.  Each sequence's entries
     are gathered into a dense ``[L_b, Hkv, d]`` cache and decoded by
     :func:`v2_decode` ("Differential Transformer V2" article, DiffAttnV2 at
-    the newest position).  The pages define no attention over an empty set:
-    a sequence of length 0 is given the output 0 (with the off-by-one softmax
-    that is also the limit, an extra zero key with a zero value).
+    the newest position), or by :func:`v2_decode_multi` when q is
+    ``[B, nq, Hq, d]`` (lam ``[B, nq, Hq/2]``, result ``[B, nq, Hq/2, d]``).
+    The pages define no attention over an empty set: a new token that sees
+    no entry (a sequence of length 0, or new token i of a sequence shorter
+    than nq with L_b - nq + i < 0) is given the output 0 (with the off-by-one
+    softmax that is also the limit, an extra zero key with a zero value).
     """
     q, kp, vp, lam = [_f64(x) for x in (q, k_pages, v_pages, lam)]
     table = np.asarray(block_table, dtype=np.int64)
     lens = np.asarray(seq_lens, dtype=np.int64)
+    if q.ndim == 4:
+        return _paged_multi(q, kp, vp, table, lens, lam, softmax1)
     B, Hq, d = q.shape
     num_pages, page, Hkv, _ = kp.shape
     assert vp.shape == kp.shape and kp.shape[3] == d
@@ -218,3 +244,25 @@ def v2_decode_paged(q, k_pages, v_pages, block_table, seq_lens, lam, softmax1: b
         v = vp[pg, t % page]
         out[b] = v2_decode(q[b:b + 1], k[None], v[None], lam[b:b + 1], softmax1=softmax1)[0]
     return out
+
+
+def _paged_multi(q, kp, vp, table, lens, lam, softmax1):
+    B, nq, Hq, d = q.shape
+    page = kp.shape[1]
+    assert lam.shape == (B, nq, Hq // 2)
+    out = np.zeros((B, nq, Hq // 2, d), dtype=np.float64)
+    for b in range(B):
+        L = int(lens[b])
+        if L == 0:
+            continue
+        t = np.arange(L)
+        pg = table[b, t // page]
+        assert ((pg >= 0) & (pg < kp.shape[0])).all(), "page index outside the pool"
+        k, v = kp[pg, t % page], vp[pg, t % page]
+        for i in range(nq):
+            n = L - nq + i + 1  # visible entries of new token i
+            if n > 0:
+                out[b, i] = v2_decode(q[b:b + 1, i], k[None, :n], v[None, :n], lam[b:b + 1, i],
+                                      softmax1=softmax1)[0]
+    return out
+

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     for need in ("diffattn_v1_fwd", "diffattn_v2_fwd", "diffattn_v2_decode",
                  "diffattn_v1_fwd_softmax1", "diffattn_v2_fwd_softmax1", "diffattn_v2_decode_softmax1",
                  "diffattn_v2_decode_paged", "diffattn_v2_decode_paged_softmax1",
-                 "diffattn_v2_decode_paged_workspace_bytes",
+                 "diffattn_v2_decode_paged_workspace_bytes", "diffattn_v2_decode_multi",
+                 "diffattn_v2_decode_multi_softmax1", "diffattn_v2_decode_multi_workspace_bytes",
                  "diffattn_v2_decode_workspace_bytes", "diffattn_status_string"):
         assert need in syms
 
@@ -150,11 +151,11 @@ def test_softmax1_entry_points_validate_like_their_namesakes(lib):
 
 
 def _paged(lib, f=None, B=2, max_len=100, Hq=8, Hkv=2, d=128, num_pages=20, page=16, table=FAKE,
-           bt_stride=None, lens=FAKE, ws=FAKE, wsb=None, dtype=1, kst=None):
-    need = lib.diffattn_v2_decode_paged_workspace_bytes(B, max_len, Hq, Hkv, d)
+           bt_stride=None, lens=FAKE, ws=FAKE, wsb=None, dtype=1, kst=None, nq=1):
+    need = lib.diffattn_v2_decode_paged_workspace_bytes(B, max_len, nq, Hq, Hkv, d)
     bt = (max_len + page - 1) // page if bt_stride is None else bt_stride
     kp = _t(sb=page * Hkv * d, sh=d, st=Hkv * d if kst is None else kst)
-    return (f or lib.diffattn_v2_decode_paged)(dtype, B, max_len, Hq, Hkv, d, _t(), kp, _t(sb=page * Hkv * d),
+    return (f or lib.diffattn_v2_decode_paged)(dtype, B, max_len, nq, Hq, Hkv, d, _t(), kp, _t(sb=page * Hkv * d),
                                                num_pages, page, table, bt, lens, _t(), _t(out=True), ws,
                                                need if wsb is None else wsb, None)
 
@@ -176,6 +177,29 @@ def test_paged_decode_validation(lib):
     assert _paged(lib, page=1 << 16, kst=1 << 15) == E_UNSUP  # rows within a page need 32-bit offsets
     assert _paged(lib, ws=0) == E_WS
     assert _paged(lib, wsb=100) == E_WS
+    assert _paged(lib, nq=0) == E_SHAPE
+    assert _paged(lib, nq=3, wsb=lib.diffattn_v2_decode_paged_workspace_bytes(2, 100, 2, 8, 2, 128)) == E_WS
     for kw in ({"page": 8}, {"table": 0}, {"dtype": 0}, {"ws": 0}):
         assert _paged(lib, lib.diffattn_v2_decode_paged_softmax1, **kw) == _paged(lib, **kw) != OK
+
+
+def _multi(lib, f=None, B=2, L=100, nq=4, Hq=8, Hkv=2, d=128, ws=FAKE, wsb=None, dtype=1, q=None):
+    need = lib.diffattn_v2_decode_multi_workspace_bytes(B, L, nq, Hq, Hkv, d)
+    return (f or lib.diffattn_v2_decode_multi)(dtype, B, L, nq, Hq, Hkv, d, q or _t(), _t(), _t(), _t(),
+                                               _t(out=True), ws, need if wsb is None else wsb, None)
+
+
+def test_multi_decode_workspace_and_validation(lib):
+    one = lib.diffattn_v2_decode_workspace_bytes(64, 32768, 64, 8, 128)
+    assert lib.diffattn_v2_decode_multi_workspace_bytes(64, 32768, 1, 64, 8, 128) == one
+    # 4 tokens x 8 heads = 32 columns: one workgroup column group, 4x the partial columns
+    assert lib.diffattn_v2_decode_multi_workspace_bytes(64, 32768, 4, 64, 8, 128) == 4 * one
+    assert lib.diffattn_v2_decode_multi_workspace_bytes(2, 10, 0, 8, 2, 128) == 0
+    assert _multi(lib, nq=0) == E_SHAPE
+    assert _multi(lib, nq=101) == E_SHAPE                    # more new tokens than cache entries
+    assert _multi(lib, q=_t(st=68)) == E_LAYOUT              # token stride of q checked when nq > 1
+    assert _multi(lib, wsb=100) == E_WS
+    assert _multi(lib, dtype=0) == E_UNSUP
+    for kw in ({"nq": 0}, {"ws": 0}, {"dtype": 0}):
+        assert _multi(lib, lib.diffattn_v2_decode_multi_softmax1, **kw) == _multi(lib, **kw) != OK
 

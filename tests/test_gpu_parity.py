@@ -508,6 +508,82 @@ def test_paged_full_sampled():
     torch.cuda.empty_cache()
 
 
+# ------------------------------------------------- V2 decode, several new tokens
+
+def _multi_cpu(z):
+    return [z[n].cpu() for n in ("q", "k", "v", "lam")]
+
+
+@pytest.mark.parametrize("L,nq", [(4, 4), (33, 3), (300, 2), (1000, 4), (2100, 8), (5000, 5)])
+@pytest.mark.parametrize("G,d", [(2, 128), (8, 128), (8, 64), (16, 64)])
+def test_multi_decode(L, nq, G, d):
+    """nq x G columns: 16 or fewer (one column block), up to 32 (two), more
+    (several column groups, each streaming the cache)."""
+    Hkv = 2
+    z = workloads.decode_multi_inputs(2, L, nq, G * Hkv, Hkv, d, torch.bfloat16, seed=600 + L + nq + G + d,
+                                      device=DEV)
+    out = binding.v2_decode_multi(z["q"], z["k"], z["v"], z["lam"])
+    torch.cuda.synchronize()
+    assert_bf16_close(out, oracle.v2_decode_multi(*_multi_cpu(z)), f"multi L{L} nq{nq} G{G} d{d}")
+
+
+def test_multi_decode_one_token_is_the_single_token_path():
+    z = workloads.decode_inputs(3, 777, 16, 2, 128, torch.bfloat16, seed=620, device=DEV)
+    single = _dec_run(z)
+    multi = binding.v2_decode_multi(z["q"][:, None], z["k"], z["v"], z["lam"][:, None])
+    torch.cuda.synchronize()
+    assert torch.equal(multi[:, 0], single)
+
+
+def test_multi_decode_equals_prefill_last_rows():
+    """The new tokens' outputs are the last nq rows of the prefill over the
+    cache (both kernels against each other, and against the oracle)."""
+    B, L, nq, Hq, Hkv, d = 2, 600, 4, 16, 2, 128
+    y = workloads.v2_inputs(B, L, Hq, Hkv, d, torch.bfloat16, seed=630, device=DEV)
+    pre = _v2_run(y)
+    dec = binding.v2_decode_multi(y["q"][:, L - nq:], y["k"], y["v"], y["lam"][:, L - nq:])
+    torch.cuda.synchronize()
+    ref = oracle.v2_decode_multi(y["q"][:, L - nq:].cpu(), y["k"].cpu(), y["v"].cpu(), y["lam"][:, L - nq:].cpu())
+    assert_bf16_close(dec, ref, "multi decode vs oracle")
+    assert_bf16_close(pre[:, L - nq:], ref, "prefill last rows vs oracle")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_multi_decode_softmax1(d):
+    z = workloads.decode_multi_inputs(2, 1500, 4, 16, 2, d, torch.bfloat16, seed=640 + d, device=DEV)
+    out = binding.v2_decode_multi(z["q"], z["k"], z["v"], z["lam"], softmax1=True)
+    torch.cuda.synchronize()
+    assert_bf16_close(out, oracle.v2_decode_multi(*_multi_cpu(z), softmax1=True), f"multi softmax1 d{d}")
+
+
+@pytest.mark.parametrize("nq", [2, 4, 7])
+def test_paged_multi_decode(nq):
+    """Ragged lengths, some shorter than nq (their first new tokens see no
+    entry and give 0), shuffled pages."""
+    lens = [1, 3, 16, 17, 200, 2047, 3001]
+    z = workloads.paged_decode_inputs(len(lens), 3072, 32, 16, 2, 128, torch.bfloat16, seed=650 + nq,
+                                      device=DEV, lens=lens, nq=nq)
+    out = _paged_run(z, 3072)
+    assert out.shape == (len(lens), nq, 8, 128)
+    assert_bf16_close(out, _paged_ref(z), f"paged multi nq{nq}")
+
+
+def test_multi_decode_full_sampled():
+    """The speculative-decoding shape: 64 sequences of 32768 entries, 4 new
+    tokens each; sampled sequences against the oracle, and determinism."""
+    w = WORKLOADS["v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128"]
+    z = workloads.inputs_for(w, DEV)
+    out = binding.v2_decode_multi(z["q"], z["k"], z["v"], z["lam"])
+    again = binding.v2_decode_multi(z["q"], z["k"], z["v"], z["lam"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+    for b in (0, 41):
+        ref = oracle.v2_decode_multi(*[z[n][b:b + 1].cpu() for n in ("q", "k", "v", "lam")])
+        assert_bf16_close(out[b:b + 1], ref, f"{w.name} b{b}")
+    del z
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ HIP graphs
 
 # ------------------------------------------------------- off-by-one softmax

@@ -172,3 +172,43 @@ def test_paged_mutant_is_caught(name, monkeypatch):
     exec(compile(PAGED_SRC.replace(old, new), "<mutant>", "exec"), ns)
     monkeypatch.setattr(oracle, "v2_decode_paged", ns["v2_decode_paged"])
     assert _failing_paged_pins() >= 1, f"no pin catches mutation {name}"
+
+
+MULTI_SRC = inspect.getsource(oracle.v2_decode_multi)
+
+MULTI_MUTATIONS = {
+    # every new token sees the whole cache (no causality among the new tokens)
+    "multi_sees_all": ("n = L - nq + i + 1  # visible entries of new token i", "n = L"),
+    # each new token also sees the next one
+    "multi_one_ahead": ("n = L - nq + i + 1  # visible entries of new token i", "n = min(L, L - nq + i + 2)"),
+    # queries matched to the wrong positions
+    "multi_reversed": ("out[:, i] = v2_decode(q[:, i],", "out[:, i] = v2_decode(q[:, nq - 1 - i],"),
+}
+
+MULTI_PINS = [
+    lambda: pins.test_multi_decode_is_the_last_prefill_rows_bruteforce.hypothesis.inner_test(
+        B=1, L=17, nq=4, Hkv=1, G=2, d=4, seed=5),
+    pins.test_multi_decode_matches_prefill_oracle_and_single_token,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MULTI_MUTATIONS))
+def test_multi_mutant_is_caught(name, monkeypatch):
+    old, new = MULTI_MUTATIONS[name]
+    assert MULTI_SRC.count(old) == 1, f"mutation {name} no longer matches the oracle source"
+    ns = dict(vars(oracle))
+    exec(compile(MULTI_SRC.replace(old, new), "<mutant>", "exec"), ns)
+    monkeypatch.setattr(oracle, "v2_decode_multi", ns["v2_decode_multi"])
+    failed = 0
+    for pin in MULTI_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, IndexError, ValueError):
+            failed += 1
+    assert failed >= 1, f"no pin catches mutation {name}"
+
+
+def test_multi_pins_pass_on_the_real_oracle():
+    for pin in MULTI_PINS:
+        pin()

@@ -503,3 +503,66 @@ def test_paged_ragged_lengths_are_dense_prefixes():
         else:
             ref = oracle.v2_decode(q[b:b + 1], k[b:b + 1, :L], v[b:b + 1, :L], lam[b:b + 1])[0]
             assert np.array_equal(got[b], ref)
+
+
+# --------------------------------------------------------------------------
+# Multi-token decode: the last nq rows of causal DiffAttnV2 over the cache
+# --------------------------------------------------------------------------
+
+def _as_prefill(rng, q_new, lam_new, L):
+    """Embed the nq decode queries as the last nq rows of a length-L prefill
+    (random queries and logits for the rows before them)."""
+    B, nq, Hq, d = q_new.shape
+    q = rng.standard_normal((B, L, Hq, d))
+    lam = rng.standard_normal((B, L, Hq // 2))
+    q[:, L - nq:] = q_new
+    lam[:, L - nq:] = lam_new
+    return q, lam
+
+
+@settings(max_examples=25, deadline=None)
+@given(B=st.integers(1, 2), L=st.sampled_from([1, 2, 5, 17, 40]), nq=st.integers(1, 6), Hkv=st.integers(1, 2),
+       G=st.sampled_from([2, 4]), d=st.sampled_from([4, 8]), seed=st.integers(0, 10**6))
+def test_multi_decode_is_the_last_prefill_rows_bruteforce(B, L, nq, Hkv, G, d, seed):
+    """Brute force (explicit masked maps over the whole sequence): the nq new
+    tokens' outputs are the last nq rows of causal DiffAttnV2."""
+    nq = min(nq, L)
+    rng = _rng(seed)
+    Hq = G * Hkv
+    qn, ln = rng.standard_normal((B, nq, Hq, d)), rng.standard_normal((B, nq, Hq // 2))
+    k, v = rng.standard_normal((B, L, Hkv, d)), rng.standard_normal((B, L, Hkv, d))
+    q, lam = _as_prefill(rng, qn, ln, L)
+    _close(oracle.v2_decode_multi(qn, k, v, ln), bruteforce.v2(q, k, v, lam)[:, L - nq:])
+
+
+def test_multi_decode_matches_prefill_oracle_and_single_token():
+    rng = _rng(230)
+    B, L, nq, Hq, Hkv, d = 2, 50, 5, 16, 2, 16
+    qn, ln = rng.standard_normal((B, nq, Hq, d)), rng.standard_normal((B, nq, Hq // 2))
+    k, v = rng.standard_normal((B, L, Hkv, d)), rng.standard_normal((B, L, Hkv, d))
+    q, lam = _as_prefill(rng, qn, ln, L)
+    got = oracle.v2_decode_multi(qn, k, v, ln)
+    _close(got, oracle.v2_fwd(q, k, v, lam)[:, L - nq:])
+    # the newest token sees the whole cache: the single-token decode
+    assert np.array_equal(got[:, -1], oracle.v2_decode(qn[:, -1], k, v, ln[:, -1]))
+    # off-by-one softmax: the same rows of the off-by-one prefill
+    _close(oracle.v2_decode_multi(qn, k, v, ln, softmax1=True),
+           oracle.v2_fwd(q, k, v, lam, softmax1=True)[:, L - nq:])
+
+
+def test_paged_multi_decode_matches_dense_multi():
+    rng = _rng(231)
+    lens, nq, page, Hkv, G, d = [30, 5, 64, 17], 4, 16, 2, 4, 8
+    q, kp, vp, table, ln, lam = _paged_case(rng, lens, page, Hkv, G, d)
+    B, Hq = len(lens), G * Hkv
+    qn, lmn = rng.standard_normal((B, nq, Hq, d)), rng.standard_normal((B, nq, Hq // 2))
+    got = oracle.v2_decode_paged(qn, kp, vp, table, ln, lmn)
+    for b, L in enumerate(lens):
+        t = np.arange(L)
+        k, v = kp[table[b, t // page], t % page], vp[table[b, t // page], t % page]
+        ref = oracle.v2_decode_multi(qn[b:b + 1], k[None], v[None], lmn[b:b + 1])[0]
+        assert np.array_equal(got[b], ref)
+    # a sequence shorter than nq: its first new tokens see nothing and give 0
+    short = oracle.v2_decode_paged(qn[:1], kp, vp, table[:1], np.array([2]), lmn[:1])
+    assert np.array_equal(short[0, :2], np.zeros_like(short[0, :2]))
+    assert np.abs(short[0, 2:]).max() > 0
