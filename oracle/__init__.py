@@ -17,6 +17,10 @@ numpy float64 arrays through ctypes.  Layouts are dense, as documented in
   out ``[B, Hq/2, d]``.
 * V2 decode over a paged cache: k, v pages ``[num_pages, page_size, Hkv, d]``,
   an int page table ``[B, >= ceil(L_b / page_size)]`` and lengths ``[B]``.
+
+``oracle.backward`` (numpy, fp64) holds the V2 training step: the forward
+with what a backward pass keeps (per-head attention outputs, log-sum-exp)
+and the gradients.
 """
 from __future__ import annotations
 

@@ -1,0 +1,144 @@
+"""Pins of the DIFF V2 backward oracle (oracle/backward.py), on the CPU.
+
+The gradient oracle is pinned to things other than itself: central finite
+differences of the (pinned) forward in random directions, torch autograd
+through an independently written fp64 forward, and an exact invariant of
+the softmax (each row of P sums to one).  The mutants at the end plant one
+plausible mistake at a time in the oracle's source and check a pin fails.
+"""
+import inspect
+import math
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from oracle import backward as ob
+
+
+def _case(seed, B, T, Hkv, G, d):
+    rng = np.random.default_rng(seed)
+    Hq = G * Hkv
+    return (rng.standard_normal((B, T, Hq, d)), rng.standard_normal((B, T, Hkv, d)),
+            rng.standard_normal((B, T, Hkv, d)), rng.standard_normal((B, T, Hq // 2)),
+            rng.standard_normal((B, T, Hq // 2, d)), rng)
+
+
+def test_fwd_train_matches_the_forward_oracle():
+    q, k, v, lam, _, _ = _case(1, 2, 13, 2, 4, 8)
+    for s1 in (False, True):
+        out, attn, lse2 = ob.v2_fwd_train(q, k, v, lam, softmax1=s1)
+        assert np.abs(out - oracle.v2_fwd(q, k, v, lam, softmax1=s1)).max() < 1e-12
+        sig = 1.0 / (1.0 + np.exp(-lam))
+        assert np.abs(out - (attn[:, :, 0::2] - sig[..., None] * attn[:, :, 1::2])).max() < 1e-12
+        # lse2 rebuilds the row's probabilities: they sum to 1 (standard) or
+        # to 1 - 2^(-lse2) (off-by-one: the extra logit 0 takes the rest)
+        B, T, Hq, d = q.shape
+        G = Hq // k.shape[2]
+        for h in (0, Hq - 1):
+            S = q[0][:, h] @ k[0][:, h // G].T / math.sqrt(d) * math.log2(math.e)
+            S = np.where(np.triu(np.ones((T, T), bool), 1), -np.inf, S)
+            rows = np.exp2(S - lse2[0, h][:, None]).sum(axis=1)
+            want = 1.0 - (np.exp2(-lse2[0, h]) if s1 else 0.0)
+            assert np.abs(rows - want).max() < 1e-12
+
+
+@settings(max_examples=20, deadline=None)
+@given(B=st.integers(1, 2), T=st.sampled_from([1, 2, 5, 12]), Hkv=st.integers(1, 2), G=st.sampled_from([2, 4]),
+       d=st.sampled_from([4, 8]), s1=st.booleans(), seed=st.integers(0, 10**6))
+def test_bwd_matches_central_differences(B, T, Hkv, G, d, s1, seed):
+    """<grad, u> equals the central difference of sum(dout * out) along a
+    random direction u, for each input."""
+    q, k, v, lam, dout, rng = _case(seed, B, T, Hkv, G, d)
+    grads = dict(zip(("q", "k", "v", "lam"), ob.v2_bwd(q, k, v, lam, dout, softmax1=s1)))
+    args = dict(q=q, k=k, v=v, lam=lam)
+    f = lambda **a: float((ob.v2_fwd_train(**a, softmax1=s1)[0] * dout).sum())
+    eps = 1e-5
+    for name, x in args.items():
+        u = rng.standard_normal(x.shape)
+        fd = (f(**{**args, name: x + eps * u}) - f(**{**args, name: x - eps * u})) / (2 * eps)
+        an = float((grads[name] * u).sum())
+        assert abs(fd - an) <= 1e-6 * (1.0 + abs(an)), (name, fd, an)
+
+
+def _torch_forward(q, k, v, lam, softmax1):
+    """An independent fp64 forward in torch ops (explicit masked maps per
+    kv group, heads repeated), differentiated by autograd."""
+    B, T, Hq, d = q.shape
+    G = Hq // k.shape[2]
+    kr, vr = k.repeat_interleave(G, dim=2), v.repeat_interleave(G, dim=2)
+    s = torch.einsum("bthc,bjhc->bhtj", q, kr) / math.sqrt(d)
+    s = s.masked_fill(torch.ones(T, T, dtype=torch.bool).triu(1), -math.inf)
+    if softmax1:
+        s = torch.cat([s, torch.zeros(B, Hq, T, 1, dtype=s.dtype)], dim=-1)
+        p = torch.softmax(s, dim=-1)[..., :T]
+    else:
+        p = torch.softmax(s, dim=-1)
+    a = torch.einsum("bhtj,bjhc->bthc", p, vr)
+    return a[:, :, 0::2] - torch.sigmoid(lam)[..., None] * a[:, :, 1::2]
+
+
+@pytest.mark.parametrize("s1", [False, True])
+def test_bwd_matches_torch_autograd(s1):
+    q, k, v, lam, dout, _ = _case(7, 2, 17, 2, 4, 8)
+    ts = [torch.tensor(x, requires_grad=True) for x in (q, k, v, lam)]
+    (_torch_forward(*ts, s1) * torch.tensor(dout)).sum().backward()
+    for got, t in zip(ob.v2_bwd(q, k, v, lam, dout, softmax1=s1), ts):
+        assert np.abs(got - t.grad.numpy()).max() < 1e-10
+
+
+def test_bwd_dv_column_sums():
+    """Rows of P sum to one, so summing dv over the keys gives the sum over
+    rows and over the group's heads of d attn (dout for even heads,
+    -sigmoid(lam) dout for odd heads)."""
+    q, k, v, lam, dout, _ = _case(8, 2, 11, 2, 4, 8)
+    dv = ob.v2_bwd(q, k, v, lam, dout)[2]
+    sig = 1.0 / (1.0 + np.exp(-lam))
+    da = np.zeros(q.shape)
+    da[:, :, 0::2] = dout
+    da[:, :, 1::2] = -sig[..., None] * dout
+    G = q.shape[2] // k.shape[2]
+    for g in range(k.shape[2]):
+        want = da[:, :, g * G:(g + 1) * G].sum(axis=(1, 2))
+        assert np.abs(dv[:, :, g].sum(axis=1) - want).max() < 1e-12
+
+
+BWD_SRC = inspect.getsource(ob)
+
+BWD_MUTATIONS = {
+    "odd_head_sign": ("da[:, 1::2] = -sig[..., None] * dout[b]", "da[:, 1::2] = sig[..., None] * dout[b]"),
+    "dlam_no_derivative": ("dlam[b] = -sig * (1.0 - sig) *", "dlam[b] = -sig *"),
+    "dlam_even_head": ('np.einsum("tpc,tpc->tp", dout[b], attn[:, 1::2])',
+                       'np.einsum("tpc,tpc->tp", dout[b], attn[:, 0::2])'),
+    "softmax_jacobian_no_rowsum": ("dS = P[h] * (dP - (P[h] * dP).sum(axis=1, keepdims=True))", "dS = P[h] * dP"),
+    "dk_unscaled": ("dk[b][:, g] += dS.T @ q[b][:, h] / math.sqrt(d)", "dk[b][:, g] += dS.T @ q[b][:, h]"),
+    "dv_untransposed": ("dv[b][:, g] += P[h].T @ da[:, h]", "dv[b][:, g] += P[h] @ da[:, h]"),
+    "dq_wrong_group": ("dq[b][:, h] = dS @ k[b][:, g] / math.sqrt(d)",
+                       "dq[b][:, h] = dS @ k[b][:, (g + 1) % Hkv] / math.sqrt(d)"),
+}
+
+BWD_PINS = [
+    lambda: test_bwd_matches_central_differences.hypothesis.inner_test(
+        B=1, T=6, Hkv=2, G=2, d=4, s1=False, seed=11),
+    lambda: test_bwd_matches_torch_autograd(False),
+    test_bwd_dv_column_sums,
+]
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTATIONS))
+def test_backward_mutant_is_caught(name, monkeypatch):
+    old, new = BWD_MUTATIONS[name]
+    assert BWD_SRC.count(old) == 1, f"mutation {name} no longer matches the oracle source"
+    ns = {"__name__": "oracle.backward_mutant", "__package__": "oracle"}
+    exec(compile(BWD_SRC.replace(old, new), "<mutant>", "exec"), ns)
+    monkeypatch.setattr(ob, "v2_bwd", ns["v2_bwd"])
+    failed = 0
+    for pin in BWD_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, f"no pin catches mutation {name}"
