@@ -38,7 +38,7 @@ METRIC = "diff-attn causal fwd TFLOP/s (bf16, % MFMA peak); V2 decode HBM GB/s (
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 HEADLINE = "v1_gpt2small_B8_H6_T1024_d64"
-SECONDARY = ["v1_3b_B2_H12_T4096_d128", "v2_prefill_B1_T8192_Hq64_Hkv8_d128", "v2_decode_B64_L32768_Hq64_Hkv8_d128",
+SECONDARY = ["v1_3b_B2_H12_T4096_d128", "v2_prefill_B1_T8192_Hq64_Hkv8_d128", "v2_backward_B1_T8192_Hq64_Hkv8_d128", "v2_decode_B64_L32768_Hq64_Hkv8_d128",
              "v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128", "v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128"]
 
 
@@ -56,6 +56,13 @@ def _caller(w, x, binding, torch, softmax1=False):
     if w.kind == "v2":
         out = torch.empty((w.B, w.T, w.Hq // 2, w.d), dtype=w.torch_dtype, device=x["v"].device)
         return lambda layer: binding.v2_fwd(x["q"], x["k"], x["v"], x["lam"], out=out, softmax1=softmax1)
+    if w.kind == "v2_bwd":  # the timed call is the backward; the training forward runs once, untimed
+        _, attn, lse = binding.v2_fwd_train(x["q"], x["k"], x["v"], x["lam"], softmax1=softmax1)
+        grads = [torch.empty_like(x[n]) for n in ("q", "k", "v", "lam")]
+        ws = torch.empty(binding.v2_bwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.d), dtype=torch.uint8,
+                         device=x["v"].device)
+        return lambda layer: binding.v2_bwd(x["q"], x["k"], x["v"], x["lam"], attn, lse, x["dout"], *grads,
+                                            workspace=ws)
     dev = x["q"].device
     out = torch.empty((w.B, w.Hq // 2, w.d), dtype=w.torch_dtype, device=dev)
     if w.kind == "decode_paged":
@@ -168,7 +175,7 @@ def _source_sha(kind):
     from hardware counters only applies to the kernel it was measured on."""
     import hashlib
 
-    src = {"v1": "prefill_bf16.hip", "v2": "prefill_bf16.hip", "decode": "decode_bf16.hip",
+    src = {"v1": "prefill_bf16.hip", "v2": "prefill_bf16.hip", "v2_bwd": "backward_bf16.hip", "decode": "decode_bf16.hip",
            "decode_paged": "decode_bf16.hip", "decode_multi": "decode_bf16.hip"}[kind]
     path = os.path.join(ROOT, "differential_attention_diffattn_amd", "csrc", src)
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
@@ -342,6 +349,9 @@ def main():
         elif w.kind == "decode_multi":
             res.update(metric=f"V2 decode of {w.nq} new tokens per sequence, HBM GB/s", unit="GB/s",
                        value=round(w.compulsory_bytes() / per_call_s / 1e9, 1))
+        elif w.kind == "v2_bwd":
+            res.update(metric="causal bwd TFLOP/s (5 products over unmasked pairs)", unit="TFLOP/s",
+                       value=round(w.flops() / per_call_s / 1e12, 3))
         else:
             res.update(metric="causal fwd TFLOP/s", unit="TFLOP/s", value=round(w.flops() / per_call_s / 1e12, 3))
         log(json.dumps(res))
@@ -362,7 +372,7 @@ def main():
             # warm-up sized to ~0.3 s of this workload's own calls, so the
             # GPU clock has settled under its load before the timed steps
             ws = workloads.WORKLOADS[name]
-            est_s = ws.flops() / 1e15 if ws.kind in ("v1", "v2") else ws.compulsory_bytes() / 5.5e12
+            est_s = ws.flops() / 1e15 if ws.kind in ("v1", "v2", "v2_bwd") else ws.compulsory_bytes() / 5.5e12
             # 8 launches per step: the events around a graph replay then time
             # the kernels, not the replay's launch
             _, xs, r = measure(name, max(10, args.steps), max(3, int(0.3 / (8 * est_s))), calls_per_step=8)

@@ -19,6 +19,9 @@ Logical layouts (any strided view with a unit-stride last axis is accepted):
              q [B,Hq,d] or [B,nq,Hq,d]; k_pages, v_pages [num_pages,page_size,Hkv,d];
              block_table int32 [B, >= ceil(max_len/page_size)]; seq_lens
              int32 [B]; lam [B,Hq/2] fp32; returns / writes out [B,Hq/2,d]
+  v2_fwd_train  as v2_fwd, also returning attn [B,T,Hq,d] and lse fp32 [B,Hq,T]
+  v2_bwd     gradients dq [B,T,Hq,d], dk, dv [B,T,Hkv,d], dlam fp32 [B,T,Hq/2]
+             from dout [B,T,Hq/2,d] and the training forward's attn, lse
 Each takes ``softmax1=True`` for the off-by-one softmax entry points
 (``diffattn_*_softmax1``: every map's denominator gains exp(0)).
 """
@@ -85,6 +88,15 @@ def load_library():
         f.argtypes = [i, i, i, i, i, i, i, DaIn, DaIn, DaIn, i, i, vp, ctypes.c_int64, vp, DaIn, DaOut, vp,
                       ctypes.c_size_t, vp]
         f.restype = i
+    for sfx in ("", "_softmax1"):
+        f = getattr(lib, "diffattn_v2_fwd_train" + sfx)
+        f.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaOut, DaOut, vp, vp]
+        f.restype = i
+    lib.diffattn_v2_bwd.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaIn, vp, DaIn, DaOut, DaOut, DaOut,
+                                    DaOut, vp, ctypes.c_size_t, vp]
+    lib.diffattn_v2_bwd.restype = i
+    lib.diffattn_v2_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.diffattn_v2_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.diffattn_v2_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.diffattn_v2_decode_workspace_bytes.restype = ctypes.c_size_t
     for f in (lib.diffattn_v2_decode_multi_workspace_bytes, lib.diffattn_v2_decode_paged_workspace_bytes):
@@ -184,6 +196,60 @@ def v2_fwd(q, k, v, lam, out: torch.Tensor | None = None, softmax1: bool = False
     if st != 0:
         raise DiffAttnError(st, name)
     return out
+
+
+def v2_fwd_train(q, k, v, lam, out=None, attn=None, lse=None, softmax1: bool = False):
+    """DIFF V2 training forward; returns (out [B,T,Hq/2,d], attn [B,T,Hq,d], lse fp32 [B,Hq,T])."""
+    lib = load_library()
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, T, Hkv, d) or tuple(v.shape) != (B, T, Hkv, d):
+        raise ValueError("k, v must be [B,T,Hkv,d]")
+    if tuple(lam.shape) != (B, T, Hq // 2) or lam.dtype != torch.float32:
+        raise ValueError("lam must be fp32 [B,T,Hq/2]")
+    out = torch.empty((B, T, Hq // 2, d), dtype=q.dtype, device=q.device) if out is None else out
+    attn = torch.empty((B, T, Hq, d), dtype=q.dtype, device=q.device) if attn is None else attn
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, T) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B,Hq,T]")
+    _check_device(q, k, v, out, attn)
+    name = "diffattn_v2_fwd_train" + ("_softmax1" if softmax1 else "")
+    st = getattr(lib, name)(_dtype_code(q), B, T, Hq, Hkv, d, _in(q, 0, 2, 1), _in(k, 0, 2, 1), _in(v, 0, 2, 1),
+                            _in(lam, 0, 2, 1), _out(out, 0, 2, 1), _out(attn, 0, 2, 1), lse.data_ptr(), _stream(q))
+    if st != 0:
+        raise DiffAttnError(st, name)
+    return out, attn, lse
+
+
+def v2_bwd_workspace_bytes(B: int, T: int, Hq: int, Hkv: int, d: int) -> int:
+    return int(load_library().diffattn_v2_bwd_workspace_bytes(B, T, Hq, Hkv, d))
+
+
+def v2_bwd(q, k, v, lam, attn, lse, dout, dq=None, dk=None, dv=None, dlam=None,
+           workspace: torch.Tensor | None = None):
+    """DIFF V2 backward; returns (dq [B,T,Hq,d], dk, dv [B,T,Hkv,d], dlam fp32 [B,T,Hq/2])."""
+    lib = load_library()
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if tuple(attn.shape) != (B, T, Hq, d) or tuple(dout.shape) != (B, T, Hq // 2, d):
+        raise ValueError("attn must be [B,T,Hq,d] and dout [B,T,Hq/2,d]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, T) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B,Hq,T]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dlam = torch.empty_like(lam) if dlam is None else dlam
+    need = v2_bwd_workspace_bytes(B, T, Hq, Hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_device(q, k, v, attn, dout, dq, dk, dv)
+    st = lib.diffattn_v2_bwd(_dtype_code(q), B, T, Hq, Hkv, d, _in(q, 0, 2, 1), _in(k, 0, 2, 1), _in(v, 0, 2, 1),
+                             _in(lam, 0, 2, 1), _in(attn, 0, 2, 1), lse.data_ptr(), _in(dout, 0, 2, 1),
+                             _out(dq, 0, 2, 1), _out(dk, 0, 2, 1), _out(dv, 0, 2, 1), _out(dlam, 0, 2, 1),
+                             workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_v2_bwd")
+    return dq, dk, dv, dlam
 
 
 def v2_decode_workspace_bytes(B: int, L: int, Hq: int, Hkv: int, d: int) -> int:

@@ -235,7 +235,8 @@ static da_status v1_fwd_impl(int softmax1, da_dtype dtype, int B, int H, int T, 
 
 static da_status v2_fwd_impl(int softmax1, da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
                              da_in v,
-                          da_in lam, da_out out, void* stream) {
+                          da_in lam, da_out out, void* stream, const da_out* attn = nullptr,
+                          float* lse = nullptr) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1) return DA_E_SHAPE;
   if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return DA_E_SHAPE;
@@ -248,6 +249,11 @@ static da_status v2_fwd_impl(int softmax1, da_dtype dtype, int B, int T, int Hq,
   DA_TRY(validate_v2_common(dtype, B, T, Hq, Hkv, d));
   if (k.st >= kMaxTokenStride || v.st >= kMaxTokenStride) return DA_E_UNSUPPORTED;
   if (!grid_fits((long long)B * (Hq / 2) * ((T + 31) / 32))) return DA_E_SHAPE;
+  if (attn) {  // training forward
+    DA_TRY(check_out(*attn, 8));
+    if (!lse) return DA_E_NULL;
+    if (!aligned(lse, 4)) return DA_E_LAYOUT;
+  }
 
   da::PrefillArgs a{};
   a.q1 = a.q2 = tin(q);
@@ -258,7 +264,59 @@ static da_status v2_fwd_impl(int softmax1, da_dtype dtype, int B, int T, int Hq,
   a.sl2 = log2e_over_sqrt(d);
   a.B = B, a.T = T, a.H = Hkv, a.G = Hq / Hkv;
   a.softmax1 = softmax1;
+  if (attn) {
+    a.attn = tout(*attn);
+    a.lse = lse;
+  }
   return launch_status(da::launch_prefill_v2_bf16(d, a, (hipStream_t)stream));
+}
+
+// DIFF V2 backward: sizes of the three workspace regions.
+struct BwdWs {
+  size_t dA, rows;  // bytes of d attn; bytes of each [B][Hq][Tp] fp32 array
+};
+static BwdWs bwd_ws(int B, int T, int Hq, int d) {
+  BwdWs w;
+  w.dA = ((size_t)B * T * Hq * d * 2 + 255) / 256 * 256;
+  w.rows = ((size_t)B * Hq * da::backward_padded_rows(T) * 4 + 255) / 256 * 256;
+  return w;
+}
+
+static da_status v2_bwd_impl(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
+                             da_in lam, da_in attn, const float* lse, da_in dout, da_out dq, da_out dk, da_out dv,
+                             da_out dlam, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1) return DA_E_SHAPE;
+  if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return DA_E_SHAPE;
+  for (const da_in* t : {&q, &k, &v, &attn, &dout}) DA_TRY(check_in(*t, 8));
+  for (const da_out* t : {&dq, &dk, &dv}) DA_TRY(check_out(*t, 8));
+  DA_TRY(check_logits(lam));
+  da_in dl{dlam.ptr, dlam.sb, dlam.sh, dlam.st};
+  DA_TRY(check_logits(dl));
+  if (!lse) return DA_E_NULL;
+  if (!aligned(lse, 4)) return DA_E_LAYOUT;
+  DA_TRY(validate_v2_common(dtype, B, T, Hq, Hkv, d));
+  if (q.st >= kMaxTokenStride || k.st >= kMaxTokenStride || v.st >= kMaxTokenStride ||
+      (int64_t)Hq * d >= kMaxTokenStride)
+    return DA_E_UNSUPPORTED;
+  const BwdWs w = bwd_ws(B, T, Hq, d);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.dA + 2 * w.rows) return DA_E_WORKSPACE;
+  const int qt = (T + 127) / 128;
+  if (!grid_fits((long long)B * Hq * qt) || !grid_fits(((long long)B * da::backward_padded_rows(T) * (Hq / 2) + 3) / 4))
+    return DA_E_SHAPE;
+
+  da::BwdArgs a{};
+  a.q = tin(q), a.k = tin(k), a.v = tin(v), a.lam = tin(lam), a.attn = tin(attn), a.dout = tin(dout);
+  a.lse = lse;
+  a.dq = tout(dq), a.dk = tout(dk), a.dv = tout(dv), a.dlam = tout(dlam);
+  a.dA = (uint16_t*)workspace;
+  a.Dw = (float*)((char*)workspace + w.dA);
+  a.lsew = (float*)((char*)workspace + w.dA + w.rows);
+  a.sl2 = log2e_over_sqrt(d);
+  a.scale = (float)(1.0 / sqrt((double)d));
+  a.B = B, a.T = T, a.Hq = Hq, a.Hkv = Hkv, a.G = Hq / Hkv;
+  a.Tp = da::backward_padded_rows(T);
+  return launch_status(da::launch_backward_v2_bf16(d, a, (hipStream_t)stream));
 }
 
 
@@ -344,6 +402,30 @@ da_status diffattn_v2_decode_paged_softmax1(da_dtype dtype, int B, int max_len, 
                                             size_t workspace_bytes, void* stream) {
   const PagedArgs pg{num_pages, page_size, block_table, bt_stride, seq_lens};
   return decode_impl(1, dtype, B, max_len, nq, Hq, Hkv, d, q, k_pages, v_pages, &pg, lam, out, workspace,
+                     workspace_bytes, stream);
+}
+
+da_status diffattn_v2_fwd_train(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
+                                da_in lam, da_out out, da_out attn, float* lse, void* stream) {
+  return v2_fwd_impl(0, dtype, B, T, Hq, Hkv, d, q, k, v, lam, out, stream, &attn, lse);
+}
+
+da_status diffattn_v2_fwd_train_softmax1(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
+                                         da_in v, da_in lam, da_out out, da_out attn, float* lse, void* stream) {
+  return v2_fwd_impl(1, dtype, B, T, Hq, Hkv, d, q, k, v, lam, out, stream, &attn, lse);
+}
+
+size_t diffattn_v2_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1) return 0;
+  if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return 0;
+  const BwdWs w = bwd_ws(B, T, Hq, d);
+  return w.dA + 2 * w.rows;
+}
+
+da_status diffattn_v2_bwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
+                          da_in lam, da_in attn, const float* lse, da_in dout, da_out dq, da_out dk, da_out dv,
+                          da_out dlam, void* workspace, size_t workspace_bytes, void* stream) {
+  return v2_bwd_impl(dtype, B, T, Hq, Hkv, d, q, k, v, lam, attn, lse, dout, dq, dk, dv, dlam, workspace,
                      workspace_bytes, stream);
 }
 

@@ -1,0 +1,425 @@
+// backward_bf16.hip -- DIFF V2 backward (gradients of the prefill), bf16 MFMA.
+//
+// What is differentiated ("Differential Transformer V2" article, DiffAttnV2
+// pseudo-code): attn_h = causal softmax(q_h k_g^T / sqrt d) v_g for every
+// query head h of kv group g, out_p = attn_2p - sigmoid(lam_p) attn_2p+1.
+// Chain rule, in the forward's order reversed:
+//   d attn_2p = dout_p, d attn_2p+1 = -sigmoid(lam_p) dout_p,
+//   d lam_p = -sigmoid(lam_p)(1 - sigmoid(lam_p)) <dout_p, attn_2p+1>,
+//   per head: P = exp2(s log2(e)/sqrt(d) - lse) (rebuilt from the forward's
+//   log-sum-exp), dP = d attn_h v^T, dS = P o (dP - D) with
+//   D = rowsum(d attn_h o attn_h), dq = dS k / sqrt d, dk += dS^T q / sqrt d,
+//   dv += P^T d attn_h.  (With the off-by-one softmax P carries the extra
+//   term in lse, and the same steps hold.)
+//
+// Three kernels (designed for gfx950):
+//   * bwd_pre: one wave per (b, token, pair): d attn of both heads (bf16, to
+//     the workspace), D of both heads, d lam, and a copy of lse padded to a
+//     multiple of 128 rows (so row blocks read whole float4 groups).
+//   * bwd_dq: the forward's structure with the key loop kept: a wave owns 32
+//     query rows of one head, K/V tiles of 32 keys stream through LDS
+//     (global_load_lds), S^T = K Q^T and dP^T = V dA^T come from
+//     v_mfma_f32_32x32x16_bf16 with Q / dA fragments held in registers, and
+//     dQ^T += K^T dS^T takes K^T through ds_read_b64_tr_b16 (K is copied to
+//     LDS twice, once swizzled for row reads and once for transpose reads).
+//   * bwd_dkdv: the mirror image: a wave owns 32 keys of one kv head and
+//     loops over the group's heads and the query rows at or after its keys;
+//     S = Q K^T and dP = dA V^T with K / V fragments in registers, then
+//     dV^T += dA^T P and dK^T += Q^T dS with transpose reads of the Q and
+//     dA tiles.  The gradients of a kv head are summed over its query heads
+//     inside the wave, so nothing is reduced across workgroups (no atomics:
+//     deterministic).
+#include <math.h>
+
+#include "kernels.hpp"
+#include "tile_ops.hpp"
+
+namespace da {
+namespace {
+
+constexpr int kNW = 4;   // waves per workgroup (bwd_dq, bwd_dkdv)
+constexpr int kBT = 32;  // rows / keys per streamed tile
+
+// ---- pre-pass -----------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdArgs a) {
+  constexpr int PL = D / 64;  // elements per lane
+  const int lane = threadIdx.x & 63;
+  const int P = a.Hq / 2;
+  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, t, p), t < Tp
+  if (item >= (long long)a.B * a.Tp * P) return;
+  const int p = (int)(item % P);
+  const int t = (int)((item / P) % a.Tp);
+  const int b = (int)(item / ((long long)P * a.Tp));
+  const int64_t r0 = ((int64_t)b * a.Hq + 2 * p) * a.Tp + t, r1 = r0 + a.Tp;  // rows of heads 2p, 2p+1
+  if (t >= a.T) {  // padding rows: zero D and lse (masked where read)
+    if (lane == 0) a.Dw[r0] = a.Dw[r1] = a.lsew[r0] = a.lsew[r1] = 0.f;
+    return;
+  }
+  const uint16_t* dop = (const uint16_t*)a.dout.p + b * a.dout.sb + (int64_t)t * a.dout.st + p * a.dout.sh;
+  const uint16_t* a0 = (const uint16_t*)a.attn.p + b * a.attn.sb + (int64_t)t * a.attn.st + (2 * p) * a.attn.sh;
+  const uint16_t* a1 = a0 + a.attn.sh;
+  float go[PL], x = 0.f, y = 0.f;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int c = lane + 64 * i;
+    go[i] = bf16_to_f32(dop[c]);
+    x += go[i] * bf16_to_f32(a0[c]);
+    y += go[i] * bf16_to_f32(a1[c]);
+  }
+  x = wave_sum(x);
+  y = wave_sum(y);
+  const float lg = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)t * a.lam.st + p * a.lam.sh];
+  const float s = sigmoid_f32(lg);
+  uint16_t* d0 = a.dA + (((int64_t)b * a.T + t) * a.Hq + 2 * p) * D;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int c = lane + 64 * i;
+    d0[c] = dop[c];
+    d0[D + c] = (uint16_t)(pack_bf16x2(-s * go[i], 0.f) & 0xffffu);
+  }
+  if (lane == 0) {
+    a.Dw[r0] = x;
+    a.Dw[r1] = -s * y;
+    a.lsew[r0] = a.lse[((int64_t)b * a.Hq + 2 * p) * a.T + t];
+    a.lsew[r1] = a.lse[((int64_t)b * a.Hq + 2 * p + 1) * a.T + t];
+    ((float*)a.dlam.p)[b * a.dlam.sb + (int64_t)t * a.dlam.st + p * a.dlam.sh] = -s * (1.f - s) * y;
+  }
+}
+
+// ---- shared tile machinery -------------------------------------------------
+// A streamed tile is kBT rows of D bf16 of one tensor (row stride `st`
+// elements), copied HBM -> LDS in 1 KB chunks.  Layout "k": 16-byte chunks
+// XOR-swizzled for ds_read_b128 row reads; layout "v": swizzled for
+// ds_read_b64_tr_b16 transpose reads.  Rows past the end are clamped to the
+// last row (finite data; masked where used).
+template <int D>
+struct TileDma {
+  static constexpr int BYTES = kBT * D * 2;
+  static constexpr int CH = BYTES / 1024;  // 1 KB copies per tensor tile
+  // issue this wave's copies of chunks wave, wave + kNW, ... of one tensor tile
+  __device__ static void issue(const uint16_t* base, int64_t st, int row0, int T, bool vlayout, uint32_t lds,
+                               int wave, int lane) {
+    const bool tail = row0 + kBT > T;
+    for (int ci = wave; ci < CH; ci += kNW) {
+      const int pos = ci * 64 + lane;
+      const int r = pos / (D / 8), sc = pos % (D / 8);
+      const int sw = vlayout ? v_swizzle<D>(r) : k_swizzle<D>(r);
+      const int rr = tail ? min(r, T - 1 - row0) : r;
+      const uint32_t off = ((uint32_t)rr * (uint32_t)st + (uint32_t)((sc ^ sw) * 8)) * 2u;
+      dma16_sbase(base + (int64_t)row0 * st, off, lds + ci * 1024);
+    }
+  }
+};
+
+// Per-lane LDS byte offsets (from a tile's start) of the row reads of A
+// operands X[row = li][16 ks + 8 hg .. +8] from a "k" layout tile.
+template <int D>
+__device__ __forceinline__ void row_read_bases(int li, int hg, uint32_t* base) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) base[ks] = li * (D * 2) + (((2 * ks + hg) ^ k_swizzle<D>(li)) << 4);
+}
+
+// Per-lane LDS byte offsets of the transpose reads giving A operands
+// X^T[c][rows of k-chunk kk] from a "v" layout tile (rows in the order the
+// P-like B operands hold them: 16kk + 4hg + 0..3, then + 8).
+template <int D>
+struct TrBases {
+  static constexpr int NV = D >= 128 ? 4 : 2;
+  uint32_t b[NV];
+  __device__ void init(int lane) {
+    const int l16 = lane & 15, g16 = lane >> 4;
+    const int vr = 4 * (g16 >> 1) + (l16 >> 2);
+    const int cl = 2 * (g16 & 1) + ((l16 & 3) >> 1);
+    const int x = v_swizzle<D>(vr);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) b[v] = vr * (D * 2) + (((4 * v + cl) ^ x) - 4 * v) * 16 + (l16 & 1) * 8;
+  }
+  __device__ bf16x8 read(uint32_t tile, int kk, int cb) const {
+    const uint32_t q = tile + b[cb % NV] + 16 * kk * (D * 2) + cb * 64;
+    return join_bf16x8(tr_read(q), tr_read(q + 8 * (D * 2)));
+  }
+};
+
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---- dQ ------------------------------------------------------------------------
+// Workgroup: (b, head h, 32 kNW query rows); wave w owns rows i0 + 32 w.
+template <int D>
+__global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
+  constexpr int KS = D / 16, CB = D / 32;
+  using Dma = TileDma<D>;
+  constexpr int TB = Dma::BYTES;
+  constexpr int STAGE = 3 * TB;  // [K "k" | K "v" | V "k"]
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int li = lane & 31, hg = lane >> 5;
+  const int T = a.T, BM = 32 * kNW;
+  const int tiles = (T + BM - 1) / BM;
+  const int units = a.B * a.Hq;
+  const int unit = blockIdx.x % units, tile = tiles - 1 - blockIdx.x / units;  // heaviest row tiles first
+  const int b = unit / a.Hq, h = unit % a.Hq, g = h / a.G;
+  const int i0w = tile * BM + 32 * wave;
+  const bool active = i0w < T;
+  const int kend = min(T, tile * BM + BM);
+  const int nkt = (kend + kBT - 1) / kBT;
+  const int row = i0w + li;
+
+  const uint16_t* kp = (const uint16_t*)a.k.p + b * a.k.sb + g * a.k.sh;
+  const uint16_t* vp = (const uint16_t*)a.v.p + b * a.v.sb + g * a.v.sh;
+  auto issue = [&](int kt, int stage) {
+    const uint32_t st = lds0 + stage * STAGE;
+    Dma::issue(kp, a.k.st, kt * kBT, T, false, st, wave, lane);
+    Dma::issue(kp, a.k.st, kt * kBT, T, true, st + TB, wave, lane);
+    Dma::issue(vp, a.v.st, kt * kBT, T, false, st + 2 * TB, wave, lane);
+  };
+  issue(0, 0);
+
+  // B operands: Q^T and dA^T of this wave's rows; the row's lse and D
+  bf16x8 qf[KS], af[KS];
+  {
+    const uint16_t* qr = (const uint16_t*)a.q.p + b * a.q.sb + (int64_t)row * a.q.st + h * a.q.sh;
+    const uint16_t* ar = a.dA + (((int64_t)b * T + row) * a.Hq + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = as_bf16x8(row < T ? *(const uint4*)(qr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+      af[ks] = as_bf16x8(row < T ? *(const uint4*)(ar + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+    }
+  }
+  const int64_t rr = ((int64_t)b * a.Hq + h) * a.Tp + min(row, a.Tp - 1);
+  const float lse_r = a.lsew[rr], D_r = a.Dw[rr];
+  uint32_t rb[KS];
+  row_read_bases<D>(li, hg, rb);
+  TrBases<D> tb;
+  tb.init(lane);
+  const float sl2 = a.sl2;
+  f32x16 acc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int stage = kt & 1;
+    wait_copies();
+    __syncthreads();  // tile kt visible; the other stage is free
+    if (kt + 1 < nkt) issue(kt + 1, stage ^ 1);
+    const int j0 = kt * kBT;
+    if (!active || j0 > i0w) continue;  // keys after every row of this wave
+    const bool diag = j0 == i0w;
+    const uint32_t st = lds0 + stage * STAGE;
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma32x32x16(lds_read16(st + rb[ks]), qf[ks], s);             // S^T = K Q^T
+      dp = mfma32x32x16(lds_read16(st + 2 * TB + rb[ks]), af[ks], dp);  // dP^T = V dA^T
+    }
+    // lane: row li; register r: key j0 + 8(r>>2) + 4hg + (r&3)
+    f32x8 e0, e1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * hg + (r & 3);
+      float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse_r));
+      if (diag && key > li) pr = 0.f;
+      const float ds = pr * (dp[r] - D_r);
+      if (r < 8) e0[r] = ds; else e1[r - 8] = ds;
+    }
+    const bf16x8 dsk[2] = {cvt_bf16x8(e0), cvt_bf16x8(e1)};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) acc[cb] = mfma32x32x16(tb.read(st + TB, kk, cb), dsk[kk], acc[cb]);
+  }
+  if (!active || row >= T) return;
+  // dQ^T[c][row]: c = 32 cb + 8 (r>>2) + 4 hg + (r&3); dq = dS k / sqrt d
+  uint16_t* dst = (uint16_t*)a.dq.p + b * a.dq.sb + (int64_t)row * a.dq.st + h * a.dq.sh;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      uint2 w;
+      w.x = pack_bf16x2(acc[cb][4 * g4 + 0] * a.scale, acc[cb][4 * g4 + 1] * a.scale);
+      w.y = pack_bf16x2(acc[cb][4 * g4 + 2] * a.scale, acc[cb][4 * g4 + 3] * a.scale);
+      *(uint2*)(dst + 32 * cb + 8 * g4 + 4 * hg) = w;
+    }
+}
+
+// ---- dK, dV ------------------------------------------------------------------
+// Workgroup: (b, kv head g, 32 kNW keys); wave w owns keys j0 + 32 w and
+// loops over the group's query heads and the row tiles at or after its keys.
+template <int D>
+__global__ void __launch_bounds__(kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs a) {
+  constexpr int KS = D / 16, CB = D / 32;
+  using Dma = TileDma<D>;
+  constexpr int TB = Dma::BYTES;
+  constexpr int STAGE = 4 * TB;  // [Q "k" | Q "v" | dA "k" | dA "v"]
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int li = lane & 31, hg = lane >> 5;
+  const int T = a.T, BK = 32 * kNW;
+  const int ktiles = (T + BK - 1) / BK;
+  const int units = a.B * a.Hkv;
+  const int unit = blockIdx.x % units, kt = blockIdx.x / units;  // low key tiles (most rows) first
+  const int b = unit / a.Hkv, g = unit % a.Hkv;
+  const int J0 = kt * BK, j0w = J0 + 32 * wave;
+  const bool active = j0w < T;
+  const int key = j0w + li;
+  const int nrt = (T + kBT - 1) / kBT;  // row tiles of 32
+  const int rt0 = J0 / kBT;
+  const int nit = a.G * (nrt - rt0);    // (head, row tile) iterations
+
+  // B operands: K^T and V^T of this wave's keys
+  bf16x8 kf[KS], vf[KS];
+  {
+    const uint16_t* kr = (const uint16_t*)a.k.p + b * a.k.sb + (int64_t)key * a.k.st + g * a.k.sh;
+    const uint16_t* vr = (const uint16_t*)a.v.p + b * a.v.sb + (int64_t)key * a.v.st + g * a.v.sh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = as_bf16x8(key < T ? *(const uint4*)(kr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+      vf[ks] = as_bf16x8(key < T ? *(const uint4*)(vr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+    }
+  }
+  // lse and D of an iteration's 32 rows, as the four 4-row groups a lane's
+  // registers hold (rows i0 + 8 q4 + 4 hg + 0..3); loaded one iteration ahead
+  float4 lnx[4], dnx[4];
+  auto load_rows = [&](int it) {
+    const int hh = g * a.G + it / (nrt - rt0), i0 = (rt0 + it % (nrt - rt0)) * kBT;
+    const int64_t rbase = ((int64_t)b * a.Hq + hh) * a.Tp + i0 + 4 * hg;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      lnx[q4] = *(const float4*)(a.lsew + rbase + 8 * q4);
+      dnx[q4] = *(const float4*)(a.Dw + rbase + 8 * q4);
+    }
+  };
+  auto issue = [&](int it, int stage) {
+    const int hh = g * a.G + it / (nrt - rt0), i0 = (rt0 + it % (nrt - rt0)) * kBT;
+    const uint16_t* qp = (const uint16_t*)a.q.p + b * a.q.sb + hh * a.q.sh;
+    const uint16_t* ap = a.dA + ((int64_t)b * T * a.Hq + hh) * D;
+    const uint32_t st = lds0 + stage * STAGE;
+    Dma::issue(qp, a.q.st, i0, T, false, st, wave, lane);
+    Dma::issue(qp, a.q.st, i0, T, true, st + TB, wave, lane);
+    Dma::issue(ap, (int64_t)a.Hq * D, i0, T, false, st + 2 * TB, wave, lane);
+    Dma::issue(ap, (int64_t)a.Hq * D, i0, T, true, st + 3 * TB, wave, lane);
+  };
+  issue(0, 0);
+  load_rows(0);
+
+  uint32_t rb[KS];
+  row_read_bases<D>(li, hg, rb);
+  TrBases<D> tb;
+  tb.init(lane);
+  const float sl2 = a.sl2;
+  asm volatile("" ::"a"(0.f));  // accumulators in AGPRs (the working set exceeds 256 VGPRs)
+  f32x16 dk[CB], dv[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[cb][r] = dv[cb][r] = 0.f;
+
+  for (int it = 0; it < nit; ++it) {
+    const int stage = it & 1;
+    wait_copies();  // this iteration's tiles and rows have landed
+    // the wait above covers the row loads too: pass them through an empty asm
+    // so the compiler sees them available and places no wait of its own
+    // (which would also hold up the next tile's copies issued below)
+    float4 lcu[4], dcu[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      asm volatile("" : "+v"(lnx[q4].x), "+v"(lnx[q4].y), "+v"(lnx[q4].z), "+v"(lnx[q4].w));
+      asm volatile("" : "+v"(dnx[q4].x), "+v"(dnx[q4].y), "+v"(dnx[q4].z), "+v"(dnx[q4].w));
+      lcu[q4] = lnx[q4];
+      dcu[q4] = dnx[q4];
+    }
+    __syncthreads();
+    if (it + 1 < nit) {
+      issue(it + 1, stage ^ 1);
+      load_rows(it + 1);
+    }
+    const int hh = g * a.G + it / (nrt - rt0), i0 = (rt0 + it % (nrt - rt0)) * kBT;
+    if (!active || i0 < j0w) continue;  // rows before this wave's keys
+    const bool diag = i0 == j0w;
+    const uint32_t st = lds0 + stage * STAGE;
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma32x32x16(lds_read16(st + rb[ks]), kf[ks], s);             // S = Q K^T
+      dp = mfma32x32x16(lds_read16(st + 2 * TB + rb[ks]), vf[ks], dp);  // dP = dA V^T
+    }
+    (void)hh;
+    // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
+    f32x8 p0, p1, d0, d1;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float lv[4] = {lcu[q4].x, lcu[q4].y, lcu[q4].z, lcu[q4].w};
+      const float Dv[4] = {dcu[q4].x, dcu[q4].y, dcu[q4].z, dcu[q4].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * q4 + j;
+        const int rw = i0 + 8 * q4 + 4 * hg + j;
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lv[j]));
+        if (rw >= T || (diag && li > rw - i0)) pr = 0.f;
+        const float ds = pr * (dp[r] - Dv[j]);
+        if (r < 8) p0[r] = pr, d0[r] = ds; else p1[r - 8] = pr, d1[r - 8] = ds;
+      }
+    }
+    const bf16x8 pk[2] = {cvt_bf16x8(p0), cvt_bf16x8(p1)};
+    const bf16x8 dsk[2] = {cvt_bf16x8(d0), cvt_bf16x8(d1)};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        dv[cb] = mfma32x32x16(tb.read(st + 3 * TB, kk, cb), pk[kk], dv[cb]);   // dV^T += dA^T P
+        dk[cb] = mfma32x32x16(tb.read(st + TB, kk, cb), dsk[kk], dk[cb]);      // dK^T += Q^T dS
+      }
+  }
+  if (!active || key >= T) return;
+  uint16_t* dkp = (uint16_t*)a.dk.p + b * a.dk.sb + (int64_t)key * a.dk.st + g * a.dk.sh;
+  uint16_t* dvp = (uint16_t*)a.dv.p + b * a.dv.sb + (int64_t)key * a.dv.st + g * a.dv.sh;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int c = 32 * cb + 8 * g4 + 4 * hg;
+      uint2 w;
+      w.x = pack_bf16x2(dk[cb][4 * g4 + 0] * a.scale, dk[cb][4 * g4 + 1] * a.scale);
+      w.y = pack_bf16x2(dk[cb][4 * g4 + 2] * a.scale, dk[cb][4 * g4 + 3] * a.scale);
+      *(uint2*)(dkp + c) = w;
+      w.x = pack_bf16x2(dv[cb][4 * g4 + 0], dv[cb][4 * g4 + 1]);
+      w.y = pack_bf16x2(dv[cb][4 * g4 + 2], dv[cb][4 * g4 + 3]);
+      *(uint2*)(dvp + c) = w;
+    }
+}
+
+template <int D>
+hipError_t launch(const BwdArgs& a, hipStream_t st) {
+  const void* args[] = {&a};
+  const long long items = (long long)a.B * a.Tp * (a.Hq / 2);
+  hipError_t e = hipLaunchKernel((const void*)bwd_pre_kernel<D>, dim3((unsigned)((items + 3) / 4)), dim3(256),
+                                 (void**)args, 0, st);
+  if (e != hipSuccess) return e;
+  const int qt = (a.T + 32 * kNW - 1) / (32 * kNW);
+  e = hipLaunchKernel((const void*)bwd_dq_kernel<D>, dim3(a.B * a.Hq * qt), dim3(kNW * 64), (void**)args, 0, st);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel((const void*)bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * qt), dim3(kNW * 64), (void**)args, 0,
+                         st);
+}
+
+}  // namespace
+
+int backward_padded_rows(int T) { return (T + 127) / 128 * 128; }
+
+hipError_t launch_backward_v2_bf16(int d, const BwdArgs& a, hipStream_t s) {
+  if (d == 64) return launch<64>(a, s);
+  if (d == 128) return launch<128>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace da

@@ -31,6 +31,11 @@ struct PrefillArgs {
   int tiles;       // token tiles per unit
   int nwg;         // workgroups in the grid
   int softmax1;    // 1: off-by-one softmax (each map's denominator + exp(0))
+  // V2 training forward (lse non-null): each head's normalised output
+  // attn [B,T,Hq,d] (roles b, head, t) and the log2 of each row's softmax
+  // denominator of the log2(e)/sqrt(d)-scaled scores, lse [B][Hq][T].
+  TOut attn;
+  float* lse;
 };
 
 hipError_t launch_prefill_v1_bf16(int d, const PrefillArgs& a, hipStream_t s);
@@ -51,6 +56,25 @@ struct V1F32Args {
   int softmax1;  // 1: off-by-one softmax (each map's denominator + exp(0))
 };
 hipError_t launch_v1_fp32(int d, const V1F32Args& a, hipStream_t s);
+
+// DIFF V2 backward: pre-pass, dQ kernel, dK/dV kernel.
+struct BwdArgs {
+  TIn q, k, v;     // [B,T,Hq,d] / [B,T,Hkv,d] bf16
+  TIn lam;         // [B,T,Hq/2] fp32 logits (roles b, pair, t)
+  TIn attn;        // [B,T,Hq,d] bf16 per-head forward outputs
+  TIn dout;        // [B,T,Hq/2,d] bf16
+  const float* lse;  // [B][Hq][T] log2 softmax denominators (training forward)
+  TOut dq, dk, dv;   // bf16, layouts of q / k / v
+  TOut dlam;         // [B,T,Hq/2] fp32
+  uint16_t* dA;      // workspace [B][T][Hq][d] bf16: d attn per head
+  float* Dw;         // workspace [B][Hq][Tp]: rowsum(d attn * attn)
+  float* lsew;       // workspace [B][Hq][Tp]: lse, padded with zeros
+  float sl2;         // log2(e) / sqrt(d)
+  float scale;       // 1 / sqrt(d)
+  int B, T, Hq, Hkv, G, Tp;
+};
+int backward_padded_rows(int T);
+hipError_t launch_backward_v2_bf16(int d, const BwdArgs& a, hipStream_t s);
 
 // Split-K decode over a KV cache, then a deterministic merge.
 struct DecodeArgs {

@@ -50,6 +50,7 @@
 #include <type_traits>
 
 #include "kernels.hpp"
+#include "tile_ops.hpp"
 
 namespace da {
 namespace {
@@ -74,72 +75,6 @@ constexpr float kSumCap = 1024.f;
 // give fma(-inf, c, kMInit) = -inf rather than NaN, and every visible score
 // overflows the cap on the first sub-block.
 constexpr float kMInit = -1e30f;
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
-
-// 16 bytes per lane, HBM -> LDS (global_load_lds_dwordx4, "saddr" form: a
-// wave-uniform 64-bit base in SGPRs plus a per-lane 32-bit byte offset):
-// lane l's bytes land at LDS byte address lds_addr + 16 l; lds_addr must be
-// wave-uniform.  Issued as inline asm so the compiler does not track it: it
-// would otherwise make every LDS read wait for the copy in flight, although
-// that copy only ever targets another LDS stage.  The kernel waits for it
-// explicitly (vmcnt(0) + barrier) before the stage is read.  M0 is used by
-// nothing else in these kernels.
-__device__ __forceinline__ void dma16_sbase(const void* base, uint32_t off, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory");
-}
-
-// LDS transpose read: in each group of 16 lanes, lane j receives element
-// (j & 3) of the 4-element rows addressed by lanes 4k + (j >> 2), k = 0..3.
-__device__ __forceinline__ uint2 tr_read(uint32_t lds_addr) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)lds_addr);
-  return __builtin_bit_cast(uint2, v);
-}
-
-// 16-byte LDS read (ds_read_b128) at an LDS byte address.
-__device__ __forceinline__ bf16x8 lds_read16(uint32_t lds_addr) {
-  return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)lds_addr;
-}
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
-// Sum of the eight bf16 values of x, accumulated onto acc in fp32
-// (v_dot2_f32_bf16 against (1, 1)).
-__device__ __forceinline__ float sum_bf16x8(bf16x8 x, float acc) {
-  const uint4 u = as_u4(x);
-  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.x), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.y), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.z), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.w), one, acc, false);
-  return acc;
-}
-
-// XOR swizzles of 16-byte chunks inside a tile row (measured conflict-free on
-// gfx950, whose LDS serves 256 B per clock from 64 banks):
-//   K rows (read by ds_read_b128, 16 rows per pass): rows of 256 B use
-//   chunk ^ (r & 15); rows of 128 B use chunk ^ ((r & 7) ^ ((r >> 3) & 1)).
-//   V rows (read by ds_read_b64_tr_b16, 4 rows x 32 B per 16 lanes):
-//   chunk ^ 4 (r & 3) when a row has >= 16 chunks, else chunk ^ 2 (r & 3).
-template <int D>
-__device__ __forceinline__ int k_swizzle(int r) {
-  return D >= 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
-}
-template <int DV>
-__device__ __forceinline__ int v_swizzle(int r) {
-  return (DV >= 128 ? 4 : 2) * (r & 3);
-}
 
 template <int D, int DV, bool V2, int NW, int MPW, bool PIPE>
 struct Cfg {
@@ -723,6 +658,27 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
     // off-by-one softmax: one more logit 0, i.e. 2^(0 - m) against the row's reference m
     const float extra = a.softmax1 ? __builtin_amdgcn_exp2f(nm[m]) : 0.f;
     inv[m] = 1.f / (lsum[m] + __shfl_xor(lsum[m], 32, 64) + extra);
+  }
+  // V2 training forward: this wave's head output (normalised) and the row's
+  // log2-sum-exp2, lse = m + log2(denominator) = -nm - log2(inv)
+  if constexpr (V2) {
+    if (a.lse != nullptr && active && row < T) {
+#pragma unroll
+      for (int m = 0; m < MPW; ++m) {
+        const int head = 2 * pair + m0 + m;
+        if (hg == 0) a.lse[((int64_t)b * (a.H * a.G) + head) * T + row] = -nm[m] - log2f(inv[m]);
+        uint16_t* ad = (uint16_t*)a.attn.p + b * a.attn.sb + (int64_t)row * a.attn.st + (int64_t)head * a.attn.sh;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            uint2 w;
+            w.x = pack_bf16x2(o[m][cb][4 * g4 + 0] * inv[m], o[m][cb][4 * g4 + 1] * inv[m]);
+            w.y = pack_bf16x2(o[m][cb][4 * g4 + 2] * inv[m], o[m][cb][4 * g4 + 3] * inv[m]);
+            *(uint2*)(ad + 32 * cb + 8 * g4 + 4 * hg) = w;
+          }
+      }
+    }
   }
   // weight of the second map: lam / l2 (V1) or sigmoid(lam[t, p]) / l_odd (V2)
   auto second_weight = [&](float inv2) {

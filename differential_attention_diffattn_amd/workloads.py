@@ -32,7 +32,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "v1", "v2", "decode", "decode_paged", "decode_multi"
+    kind: str  # "v1", "v2", "v2_bwd", "decode", "decode_paged", "decode_multi"
     dtype: str  # "fp32" or "bf16"
     B: int
     H: int = 0  # V1: differential heads
@@ -62,6 +62,8 @@ class Workload:
             return 6.0 * self.B * self.H * self.d * self.T * (self.T + 1)
         if self.kind == "v2":
             return 2.0 * self.B * self.Hq * self.d * self.T * (self.T + 1)
+        if self.kind == "v2_bwd":  # 5 products (S, dP, dV, dK, dQ) over the unmasked pairs
+            return 5.0 * self.B * self.Hq * self.d * self.T * (self.T + 1)
         if self.kind == "decode_paged":
             return 4.0 * self.Hq * self.d * int(self.seq_lens().sum())
         if self.kind == "decode_multi":  # new token i sees T - nq + i + 1 entries
@@ -78,6 +80,10 @@ class Workload:
         if self.kind == "v2":
             B, T, Hq, Hkv, d = self.B, self.T, self.Hq, self.Hkv, self.d
             return e * (B * T * Hq * d + 2 * B * T * Hkv * d + B * T * (Hq // 2) * d) + 4 * B * T * (Hq // 2)
+        if self.kind == "v2_bwd":  # q, k, v, attn, dout, lam, lse in; dq, dk, dv, dlam out
+            B, T, Hq, Hkv, d = self.B, self.T, self.Hq, self.Hkv, self.d
+            return (e * (2 * B * T * Hq * d + 4 * B * T * Hkv * d + 2 * B * T * Hq * d + B * T * (Hq // 2) * d)
+                    + 4 * (2 * B * T * (Hq // 2) + B * Hq * T))
         B, L, Hq, Hkv, d = self.B, self.T, self.Hq, self.Hkv, self.d
         if self.kind == "decode_paged":
             lens = self.seq_lens().long()
@@ -101,6 +107,7 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("v2_prefill_B1_T8192_Hq64_Hkv8_d128", "v2", "bf16", B=1, T=8192, d=128, Hq=64, Hkv=8, seed=4),
         Workload("v2_decode_B64_L32768_Hq64_Hkv8_d128", "decode", "bf16", B=64, T=32768, d=128, Hq=64,
                  Hkv=8, seed=5),
+        Workload("v2_backward_B1_T8192_Hq64_Hkv8_d128", "v2_bwd", "bf16", B=1, T=8192, d=128, Hq=64, Hkv=8, seed=4),
         Workload("v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128", "decode_paged", "bf16", B=64, T=32768,
                  d=128, Hq=64, Hkv=8, seed=6, page=64),
         Workload("v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128", "decode_multi", "bf16", B=64, T=32768, d=128,
@@ -233,6 +240,10 @@ def inputs_for(w: Workload, device="cpu") -> Dict[str, torch.Tensor]:
         return v1_inputs(w.B, w.H, w.T, w.d, w.torch_dtype, w.seed, device)
     if w.kind == "v2":
         return v2_inputs(w.B, w.T, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)
+    if w.kind == "v2_bwd":  # the prefill's inputs plus an output gradient dout ~ N(0, 1)
+        x = v2_inputs(w.B, w.T, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)
+        x["dout"] = _randn((w.B, w.T, w.Hq // 2, w.d), _gen(w.seed + 99, device), device, w.torch_dtype)
+        return x
     if w.kind == "decode_paged":
         return paged_decode_inputs(w.B, w.T, w.page, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)
     if w.kind == "decode_multi":

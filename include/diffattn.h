@@ -286,6 +286,59 @@ da_status diffattn_v2_decode_paged_softmax1(da_dtype dtype, int B, int max_len, 
                                             void* workspace, size_t workspace_bytes,
                                             void* stream);
 
+/*
+ * DIFF V2 training forward: diffattn_v2_fwd (or its off-by-one softmax
+ * variant) that also keeps what diffattn_v2_bwd needs.
+ *   attn   logical [B,T,Hq,d] bf16 (roles b, h = query head, t): each head's
+ *          attention output before the pair combine (the pseudo-code's attn
+ *          of "Differential Transformer V2", DiffAttnV2, before the 0::2 /
+ *          1::2 split), normalised, rounded once to bf16.
+ *   lse    DEVICE fp32 [B][Hq][T], contiguous: for each row, log2 of the
+ *          softmax denominator of the scores scaled by log2(e)/sqrt(d), so a
+ *          probability is exp2(q.k log2(e)/sqrt(d) - lse) (with the
+ *          off-by-one softmax the denominator holds its extra term).
+ * Other arguments, layouts and errors as for diffattn_v2_fwd; DA_E_NULL for
+ * a NULL lse, DA_E_LAYOUT for a misaligned one.
+ */
+da_status diffattn_v2_fwd_train(da_dtype dtype, int B, int T, int Hq, int Hkv, int d,
+                                da_in q, da_in k, da_in v, da_in lam,
+                                da_out out, da_out attn, float* lse, void* stream);
+da_status diffattn_v2_fwd_train_softmax1(da_dtype dtype, int B, int T, int Hq, int Hkv, int d,
+                                         da_in q, da_in k, da_in v, da_in lam,
+                                         da_out out, da_out attn, float* lse, void* stream);
+
+/*
+ * Bytes of device workspace diffattn_v2_bwd needs (0 if the sizes are
+ * invalid): d attn per head in bf16 plus two fp32 arrays of B*Hq rows padded
+ * to a multiple of 128 tokens.
+ */
+size_t diffattn_v2_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d);
+
+/*
+ * DIFF V2 backward ("Differential Transformer V2" article, DiffAttnV2
+ * pseudo-code, differentiated): given dout = dL/dout, the gradients of the
+ * prefill's inputs, from the training forward's attn and lse:
+ *   d attn_2p = dout_p,   d attn_2p+1 = -sigmoid(lam_p) dout_p,
+ *   dlam_p    = -sigmoid(lam_p) (1 - sigmoid(lam_p)) <dout_p, attn_2p+1>,
+ *   and for every head the softmax-attention gradients dq, dk, dv (dk and
+ *   dv of a kv head summed over the query heads of its group).
+ *   dtype      DA_BF16 only; d in {64, 128}; Hq % Hkv == 0, (Hq/Hkv) even.
+ *   q, k, v, lam   the forward's inputs (layouts as for diffattn_v2_fwd).
+ *   attn, lse      the training forward's outputs for the same inputs.
+ *   dout       logical [B,T,Hq/2,d] bf16.
+ *   dq         logical [B,T,Hq,d] bf16;  dk, dv  logical [B,T,Hkv,d] bf16.
+ *   dlam       logical [B,T,Hq/2] fp32 (roles b, h = pair, t).
+ *   workspace  at least diffattn_v2_bwd_workspace_bytes(B,T,Hq,Hkv,d) bytes,
+ *              256-byte aligned, owned by the caller.
+ * Three kernels are enqueued on `stream` (a pre-pass, dq, then dk/dv); the
+ * sums over heads and keys are taken in a fixed order (deterministic).
+ * Token strides of q, k, v must be below 2^24 elements (DA_E_UNSUPPORTED).
+ */
+da_status diffattn_v2_bwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d,
+                          da_in q, da_in k, da_in v, da_in lam, da_in attn,
+                          const float* lse, da_in dout, da_out dq, da_out dk, da_out dv,
+                          da_out dlam, void* workspace, size_t workspace_bytes, void* stream);
+
 /* lambda_init = 0.8 - 0.6*exp(-0.3*layer_index), as the V1 kernels use it
  * (computed on the host in double, handed to the device as float). */
 double diffattn_lambda_init(int layer_index);

@@ -109,3 +109,42 @@ def v2_bwd(q, k, v, lam, dout, softmax1: bool = False):
             dk[b][:, g] += dS.T @ q[b][:, h] / math.sqrt(d)
             dv[b][:, g] += P[h].T @ da[:, h]
     return dq, dk, dv, dlam
+
+
+def v2_bwd_rounding_bounds(q, k, v, lam, dout, softmax1: bool = False):
+    """Per-element scale of what bf16 rounding can move in each gradient of
+    :func:`v2_bwd`, for a path that holds P, dS, d attn and attn in bf16
+    (relative rounding u = 2^-9 each) and accumulates in fp32.
+
+    Each bound is u times the sum of the absolute values of the terms that a
+    rounded factor enters, following the same steps as :func:`v2_bwd`:
+      E_i     = sum_c |d attn_ic| |attn_ic|     (what rounding attn moves in D_i)
+      dq_ic  <- sum_j (P_ij E_i + |dS_ij|) |k_jc| / sqrt d
+      dk_jc  <- sum_{h,i} (P_ij E_i + |dS_ij|) |q_ic| / sqrt d
+      dv_jc  <- 2 sum_{h,i} P_ij |d attn_ic|
+      dlam   <- 2 s (1 - s) sum_c |dout_c| |attn_odd,c|
+    Returns (bq, bk, bv, blam) shaped like the gradients.
+    """
+    q, k, v, lam, dout = [_f64(x) for x in (q, k, v, lam, dout)]
+    u = 2.0 ** -9
+    B, T, Hq, d = q.shape
+    G = Hq // k.shape[2]
+    bq, bk, bv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    blam = np.zeros_like(lam)
+    for b in range(B):
+        P, attn, _ = _rows(q[b], k[b], v[b], softmax1)
+        sig = 1.0 / (1.0 + np.exp(-lam[b]))
+        da = np.zeros((T, Hq, d))
+        da[:, 0::2] = dout[b]
+        da[:, 1::2] = -sig[..., None] * dout[b]
+        blam[b] = 2 * u * sig * (1.0 - sig) * np.einsum("tpc,tpc->tp", np.abs(dout[b]), np.abs(attn[:, 1::2]))
+        for h in range(Hq):
+            g = h // G
+            dP = da[:, h] @ v[b][:, g].T
+            dS = P[h] * (dP - (P[h] * dP).sum(axis=1, keepdims=True))
+            E = (np.abs(da[:, h]) * np.abs(attn[:, h])).sum(axis=1, keepdims=True)
+            W = P[h] * E + np.abs(dS)
+            bq[b][:, h] = u * (W @ np.abs(k[b][:, g])) / math.sqrt(d)
+            bk[b][:, g] += u * (W.T @ np.abs(q[b][:, h])) / math.sqrt(d)
+            bv[b][:, g] += 2 * u * (P[h].T @ np.abs(da[:, h]))
+    return bq, bk, bv, blam

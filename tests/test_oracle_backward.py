@@ -105,7 +105,7 @@ def test_bwd_dv_column_sums():
         assert np.abs(dv[:, :, g].sum(axis=1) - want).max() < 1e-12
 
 
-BWD_SRC = inspect.getsource(ob)
+BWD_SRC = inspect.getsource(ob.v2_bwd)
 
 BWD_MUTATIONS = {
     "odd_head_sign": ("da[:, 1::2] = -sig[..., None] * dout[b]", "da[:, 1::2] = sig[..., None] * dout[b]"),
@@ -131,7 +131,7 @@ BWD_PINS = [
 def test_backward_mutant_is_caught(name, monkeypatch):
     old, new = BWD_MUTATIONS[name]
     assert BWD_SRC.count(old) == 1, f"mutation {name} no longer matches the oracle source"
-    ns = {"__name__": "oracle.backward_mutant", "__package__": "oracle"}
+    ns = dict(vars(ob))
     exec(compile(BWD_SRC.replace(old, new), "<mutant>", "exec"), ns)
     monkeypatch.setattr(ob, "v2_bwd", ns["v2_bwd"])
     failed = 0
