@@ -22,13 +22,13 @@
 //     v_mfma_f32_32x32x16_bf16 with Q / dA fragments held in registers, and
 //     dQ^T += K^T dS^T takes K^T through ds_read_b64_tr_b16 (K is copied to
 //     LDS twice, once swizzled for row reads and once for transpose reads).
-//   * bwd_dkdv: the mirror image: a wave owns 32 keys of one kv head and
-//     loops over the group's heads and the query rows at or after its keys;
-//     S = Q K^T and dP = dA V^T with K / V fragments in registers, then
-//     dV^T += dA^T P and dK^T += Q^T dS with transpose reads of the Q and
-//     dA tiles.  The gradients of a kv head are summed over its query heads
-//     inside the wave, so nothing is reduced across workgroups (no atomics:
-//     deterministic).
+//   * bwd_dkdv: the mirror image: two waves own 32 keys of one kv head (one
+//     accumulates dV, the other dK) and loop over the group's heads and the
+//     query rows at or after their keys; S = Q K^T and dP = dA V^T with K / V
+//     fragments in registers, then dV^T += dA^T P and dK^T += Q^T dS with
+//     transpose reads of the Q and dA tiles.  The gradients of a kv head are
+//     summed over its query heads inside a wave, so nothing is reduced
+//     across workgroups (no atomics: deterministic).
 #include <math.h>
 
 #include "kernels.hpp"
@@ -37,7 +37,7 @@
 namespace da {
 namespace {
 
-constexpr int kNW = 4;   // waves per workgroup (bwd_dq, bwd_dkdv)
+constexpr int kNW = 4;   // waves per workgroup of bwd_dq; bwd_dkdv has 2 kNW (two per key block)
 constexpr int kBT = 32;  // rows / keys per streamed tile
 
 // ---- pre-pass -----------------------------------------------------------------
@@ -93,15 +93,15 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdArgs a) {
 // XOR-swizzled for ds_read_b128 row reads; layout "v": swizzled for
 // ds_read_b64_tr_b16 transpose reads.  Rows past the end are clamped to the
 // last row (finite data; masked where used).
-template <int D>
+template <int D, int NW = kNW>
 struct TileDma {
   static constexpr int BYTES = kBT * D * 2;
   static constexpr int CH = BYTES / 1024;  // 1 KB copies per tensor tile
-  // issue this wave's copies of chunks wave, wave + kNW, ... of one tensor tile
+  // issue this wave's copies of chunks wave, wave + NW, ... of one tensor tile
   __device__ static void issue(const uint16_t* base, int64_t st, int row0, int T, bool vlayout, uint32_t lds,
                                int wave, int lane) {
     const bool tail = row0 + kBT > T;
-    for (int ci = wave; ci < CH; ci += kNW) {
+    for (int ci = wave; ci < CH; ci += NW) {
       const int pos = ci * 64 + lane;
       const int r = pos / (D / 8), sc = pos % (D / 8);
       const int sw = vlayout ? v_swizzle<D>(r) : k_swizzle<D>(r);
@@ -142,6 +142,16 @@ struct TrBases {
 };
 
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 31] (the count is an
+// instruction immediate): wait until at most n of this wave's memory reads
+// are in flight.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  static_for<0, 32>([&](auto c) {
+    constexpr int C = decltype(c)::value;
+    if (n == C) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C) : "memory");
+  });
+}
 
 // ---- dQ ------------------------------------------------------------------------
 // Workgroup: (b, head h, 32 kNW query rows); wave w owns rows i0 + 32 w.
@@ -249,32 +259,43 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
 }
 
 // ---- dK, dV ------------------------------------------------------------------
-// Workgroup: (b, kv head g, 32 kNW keys); wave w owns keys j0 + 32 w and
-// loops over the group's query heads and the row tiles at or after its keys.
+// Workgroup: (b, kv head g, 32 kNW keys), 2 kNW waves: waves m and m + kNW
+// own keys j0 + 32 m, the first accumulating dV, the second dK, and both loop
+// over the group's query heads and the row tiles at or after their keys.
+// (Splitting dV and dK over two waves keeps each under 256 registers, so two
+// waves share a SIMD; both rebuild P, only the dK wave needs dP.)
 template <int D>
-__global__ void __launch_bounds__(kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs a) {
+  constexpr int NW = 2 * kNW;
   constexpr int KS = D / 16, CB = D / 32;
-  using Dma = TileDma<D>;
+  using Dma = TileDma<D, NW>;
   constexpr int TB = Dma::BYTES;
-  constexpr int STAGE = 4 * TB;  // [Q "k" | Q "v" | dA "k" | dA "v"]
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  constexpr int STAGE = 4 * TB + 256;  // [Q "k" | Q "v" | dA "k" | dA "v" | lse, D of the 32 rows]
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * STAGE];  // two pairs of stages
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, hg = lane >> 5;
+  // waves m and m + kNW own keys j0 + 32 m: the dV and the dK wave of a key
+  // block sit on the same SIMD (wave w runs on SIMD w mod 4), so every SIMD
+  // carries one of each and the per-iteration barrier waits for no SIMD
+  // holding two dK waves
+  const int kb = wave % kNW;
+  const bool kwave = wave >= kNW;  // accumulates dK (else dV)
   const int T = a.T, BK = 32 * kNW;
   const int ktiles = (T + BK - 1) / BK;
   const int units = a.B * a.Hkv;
   const int unit = blockIdx.x % units, kt = blockIdx.x / units;  // low key tiles (most rows) first
   const int b = unit / a.Hkv, g = unit % a.Hkv;
-  const int J0 = kt * BK, j0w = J0 + 32 * wave;
+  const int J0 = kt * BK, j0w = J0 + 32 * kb;
+  (void)ktiles;
   const bool active = j0w < T;
   const int key = j0w + li;
   const int nrt = (T + kBT - 1) / kBT;  // row tiles of 32
   const int rt0 = J0 / kBT;
   const int nit = a.G * (nrt - rt0);    // (head, row tile) iterations
 
-  // B operands: K^T and V^T of this wave's keys
+  // B operands: K^T (both waves) and V^T (the dK wave) of this wave's keys
   bf16x8 kf[KS], vf[KS];
   {
     const uint16_t* kr = (const uint16_t*)a.k.p + b * a.k.sb + (int64_t)key * a.k.st + g * a.k.sh;
@@ -282,21 +303,9 @@ __global__ void __launch_bounds__(kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs a) 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       kf[ks] = as_bf16x8(key < T ? *(const uint4*)(kr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
-      vf[ks] = as_bf16x8(key < T ? *(const uint4*)(vr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+      vf[ks] = as_bf16x8(key < T && kwave ? *(const uint4*)(vr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
     }
   }
-  // lse and D of an iteration's 32 rows, as the four 4-row groups a lane's
-  // registers hold (rows i0 + 8 q4 + 4 hg + 0..3); loaded one iteration ahead
-  float4 lnx[4], dnx[4];
-  auto load_rows = [&](int it) {
-    const int hh = g * a.G + it / (nrt - rt0), i0 = (rt0 + it % (nrt - rt0)) * kBT;
-    const int64_t rbase = ((int64_t)b * a.Hq + hh) * a.Tp + i0 + 4 * hg;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      lnx[q4] = *(const float4*)(a.lsew + rbase + 8 * q4);
-      dnx[q4] = *(const float4*)(a.Dw + rbase + 8 * q4);
-    }
-  };
   auto issue = [&](int it, int stage) {
     const int hh = g * a.G + it / (nrt - rt0), i0 = (rt0 + it % (nrt - rt0)) * kBT;
     const uint16_t* qp = (const uint16_t*)a.q.p + b * a.q.sb + hh * a.q.sh;
@@ -306,95 +315,87 @@ __global__ void __launch_bounds__(kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs a) 
     Dma::issue(qp, a.q.st, i0, T, true, st + TB, wave, lane);
     Dma::issue(ap, (int64_t)a.Hq * D, i0, T, false, st + 2 * TB, wave, lane);
     Dma::issue(ap, (int64_t)a.Hq * D, i0, T, true, st + 3 * TB, wave, lane);
+    // the 32 rows' lse and D (padded arrays: always in bounds), 8 lanes x 16 B each
+    const int64_t rbase = ((int64_t)b * a.Hq + hh) * a.Tp + i0;
+    if (wave == NW - 2 && lane < 8) dma16_sbase(a.lsew + rbase, lane * 16, st + 4 * TB);
+    if (wave == NW - 1 && lane < 8) dma16_sbase(a.Dw + rbase, lane * 16, st + 4 * TB + 128);
   };
+  // Two row tiles per barrier: the pair (it, it+1) uses stages 2(it/2 mod 2),
+  // +1, and the next pair streams into the other two stages meanwhile.
   issue(0, 0);
-  load_rows(0);
+  if (nit > 1) issue(1, 1);
 
   uint32_t rb[KS];
   row_read_bases<D>(li, hg, rb);
   TrBases<D> tb;
   tb.init(lane);
   const float sl2 = a.sl2;
-  asm volatile("" ::"a"(0.f));  // accumulators in AGPRs (the working set exceeds 256 VGPRs)
-  f32x16 dk[CB], dv[CB];
+  f32x16 acc[CB];  // dV^T or dK^T [c][key]
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dk[cb][r] = dv[cb][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
-  for (int it = 0; it < nit; ++it) {
-    const int stage = it & 1;
-    wait_copies();  // this iteration's tiles and rows have landed
-    // the wait above covers the row loads too: pass them through an empty asm
-    // so the compiler sees them available and places no wait of its own
-    // (which would also hold up the next tile's copies issued below)
-    float4 lcu[4], dcu[4];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      asm volatile("" : "+v"(lnx[q4].x), "+v"(lnx[q4].y), "+v"(lnx[q4].z), "+v"(lnx[q4].w));
-      asm volatile("" : "+v"(dnx[q4].x), "+v"(dnx[q4].y), "+v"(dnx[q4].z), "+v"(dnx[q4].w));
-      lcu[q4] = lnx[q4];
-      dcu[q4] = dnx[q4];
-    }
-    __syncthreads();
-    if (it + 1 < nit) {
-      issue(it + 1, stage ^ 1);
-      load_rows(it + 1);
-    }
-    const int hh = g * a.G + it / (nrt - rt0), i0 = (rt0 + it % (nrt - rt0)) * kBT;
-    if (!active || i0 < j0w) continue;  // rows before this wave's keys
+  auto tile_step = [&](int it, int stage) {
+    const int i0 = (rt0 + it % (nrt - rt0)) * kBT;
+    if (!active || i0 < j0w) return;  // rows before this wave's keys
     const bool diag = i0 == j0w;
     const uint32_t st = lds0 + stage * STAGE;
     f32x16 s, dp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = mfma32x32x16(lds_read16(st + rb[ks]), kf[ks], s);             // S = Q K^T
-      dp = mfma32x32x16(lds_read16(st + 2 * TB + rb[ks]), vf[ks], dp);  // dP = dA V^T
+    for (int ks = 0; ks < KS; ++ks) s = mfma32x32x16(lds_read16(st + rb[ks]), kf[ks], s);  // S = Q K^T
+    if (kwave) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) dp = mfma32x32x16(lds_read16(st + 2 * TB + rb[ks]), vf[ks], dp);  // dP = dA V^T
     }
-    (void)hh;
     // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
-    f32x8 p0, p1, d0, d1;
+    f32x8 e0, e1;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const float lv[4] = {lcu[q4].x, lcu[q4].y, lcu[q4].z, lcu[q4].w};
-      const float Dv[4] = {dcu[q4].x, dcu[q4].y, dcu[q4].z, dcu[q4].w};
+      const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(st + 4 * TB + (8 * q4 + 4 * hg) * 4);
+      const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(st + 4 * TB + 128 + (8 * q4 + 4 * hg) * 4);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * q4 + j;
         const int rw = i0 + 8 * q4 + 4 * hg + j;
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lv[j]));
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[j]));
         if (rw >= T || (diag && li > rw - i0)) pr = 0.f;
-        const float ds = pr * (dp[r] - Dv[j]);
-        if (r < 8) p0[r] = pr, d0[r] = ds; else p1[r - 8] = pr, d1[r - 8] = ds;
+        const float x = kwave ? pr * (dp[r] - d4[j]) : pr;  // dS (dK wave) or P (dV wave)
+        if (r < 8) e0[r] = x; else e1[r - 8] = x;
       }
     }
-    const bf16x8 pk[2] = {cvt_bf16x8(p0), cvt_bf16x8(p1)};
-    const bf16x8 dsk[2] = {cvt_bf16x8(d0), cvt_bf16x8(d1)};
+    const bf16x8 xk[2] = {cvt_bf16x8(e0), cvt_bf16x8(e1)};
+    // dV^T += dA^T P (dV wave), dK^T += Q^T dS (dK wave)
+    const uint32_t src = st + (kwave ? TB : 3 * TB);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        dv[cb] = mfma32x32x16(tb.read(st + 3 * TB, kk, cb), pk[kk], dv[cb]);   // dV^T += dA^T P
-        dk[cb] = mfma32x32x16(tb.read(st + TB, kk, cb), dsk[kk], dk[cb]);      // dK^T += Q^T dS
-      }
+      for (int cb = 0; cb < CB; ++cb) acc[cb] = mfma32x32x16(tb.read(src, kk, cb), xk[kk], acc[cb]);
+  };
+
+  for (int it = 0; it < nit; it += 2) {
+    const int sp = (it >> 1) & 1;  // stage pair of tiles it, it+1
+    wait_copies();
+    __syncthreads();  // tiles it, it+1 visible; the other stage pair is free
+    if (it + 2 < nit) issue(it + 2, 2 * (sp ^ 1));
+    if (it + 3 < nit) issue(it + 3, 2 * (sp ^ 1) + 1);
+    tile_step(it, 2 * sp);
+    if (it + 1 < nit) tile_step(it + 1, 2 * sp + 1);
   }
   if (!active || key >= T) return;
-  uint16_t* dkp = (uint16_t*)a.dk.p + b * a.dk.sb + (int64_t)key * a.dk.st + g * a.dk.sh;
-  uint16_t* dvp = (uint16_t*)a.dv.p + b * a.dv.sb + (int64_t)key * a.dv.st + g * a.dv.sh;
+  const TOut& o = kwave ? a.dk : a.dv;
+  const float sc = kwave ? a.scale : 1.f;
+  uint16_t* dst = (uint16_t*)o.p + b * o.sb + (int64_t)key * o.st + g * o.sh;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const int c = 32 * cb + 8 * g4 + 4 * hg;
       uint2 w;
-      w.x = pack_bf16x2(dk[cb][4 * g4 + 0] * a.scale, dk[cb][4 * g4 + 1] * a.scale);
-      w.y = pack_bf16x2(dk[cb][4 * g4 + 2] * a.scale, dk[cb][4 * g4 + 3] * a.scale);
-      *(uint2*)(dkp + c) = w;
-      w.x = pack_bf16x2(dv[cb][4 * g4 + 0], dv[cb][4 * g4 + 1]);
-      w.y = pack_bf16x2(dv[cb][4 * g4 + 2], dv[cb][4 * g4 + 3]);
-      *(uint2*)(dvp + c) = w;
+      w.x = pack_bf16x2(acc[cb][4 * g4 + 0] * sc, acc[cb][4 * g4 + 1] * sc);
+      w.y = pack_bf16x2(acc[cb][4 * g4 + 2] * sc, acc[cb][4 * g4 + 3] * sc);
+      *(uint2*)(dst + 32 * cb + 8 * g4 + 4 * hg) = w;
     }
 }
 
@@ -408,8 +409,8 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
   const int qt = (a.T + 32 * kNW - 1) / (32 * kNW);
   e = hipLaunchKernel((const void*)bwd_dq_kernel<D>, dim3(a.B * a.Hq * qt), dim3(kNW * 64), (void**)args, 0, st);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel((const void*)bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * qt), dim3(kNW * 64), (void**)args, 0,
-                         st);
+  return hipLaunchKernel((const void*)bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * qt), dim3(2 * kNW * 64), (void**)args,
+                         0, st);
 }
 
 }  // namespace
