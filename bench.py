@@ -227,12 +227,17 @@ def write_traffic(pmc_dir):
     from differential_attention_diffattn_amd import workloads
 
     def per_dispatch(work, counter, match):
+        """Counter per call: mean over dispatches of each kernel matching one of
+        the `|`-separated names, summed over those kernels."""
         f = os.path.join(pmc_dir, f"pmc_{work}_{counter}", "run_counter_collection.csv")
-        acc = defaultdict(float)
-        for r in csv.DictReader(open(f)):
-            if match in r["Kernel_Name"]:
-                acc[r["Dispatch_Id"]] += float(r["Counter_Value"])
-        return sum(acc.values()) / len(acc)
+        total = 0.0
+        for m in match.split("|"):
+            acc = defaultdict(float)
+            for r in csv.DictReader(open(f)):
+                if m in r["Kernel_Name"]:
+                    acc[r["Dispatch_Id"]] += float(r["Counter_Value"])
+            total += sum(acc.values()) / len(acc)
+        return total
 
     copy_bytes = 1 << 30
     f_scale = copy_bytes / (1024 * per_dispatch("copy", "FETCH_SIZE", "copyBuffer"))
@@ -241,8 +246,10 @@ def write_traffic(pmc_dir):
                             "write_scale": round(w_scale, 4)}}
     for name, match in [("v1_gpt2small_B8_H6_T1024_d64", "prefill_kernel"), ("v1_3b_B2_H12_T4096_d128", "prefill_kernel"),
                         ("v2_prefill_B1_T8192_Hq64_Hkv8_d128", "prefill_kernel"),
+                        ("v2_backward_B1_T8192_Hq64_Hkv8_d128", "bwd_pre_kernel|bwd_dq_kernel|bwd_dkdv_kernel"),
                         ("v2_decode_B64_L32768_Hq64_Hkv8_d128", "decode_split_kernel"),
-                        ("v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128", "decode_split_kernel")]:
+                        ("v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128", "decode_split_kernel"),
+                        ("v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128", "decode_split_kernel")]:
         w = workloads.WORKLOADS[name]
         fk = per_dispatch(name, "FETCH_SIZE", match)
         wk = per_dispatch(name, "WRITE_SIZE", match)

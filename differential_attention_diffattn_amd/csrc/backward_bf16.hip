@@ -143,6 +143,17 @@ struct TrBases {
 
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait for every read in flight and pass a loaded register through the
+// wait: the compiler then sees the value as available from here on and puts
+// no wait of its own before a later use (such a wait, vmcnt(0) inside the
+// loop, would also hold up the tile copies issued ahead of their use).
+__device__ __forceinline__ void retire(bf16x8& x) {
+  uint4 u = as_u4(x);
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+  x = as_bf16x8(u);
+}
+__device__ __forceinline__ void retire(float& x) { asm volatile("s_waitcnt vmcnt(0)" : "+v"(x)); }
+
 // s_waitcnt vmcnt(n) for a wave-uniform n in [0, 31] (the count is an
 // instruction immediate): wait until at most n of this wave's memory reads
 // are in flight.
@@ -168,9 +179,13 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
   const int li = lane & 31, hg = lane >> 5;
   const int T = a.T, BM = 32 * kNW;
   const int tiles = (T + BM - 1) / BM;
+  // heaviest row tiles first; within a tile index the kv group varies
+  // fastest, so the workgroups on one XCD (id mod 8) share kv groups and
+  // stream the same K/V tiles through its L2
   const int units = a.B * a.Hq;
-  const int unit = blockIdx.x % units, tile = tiles - 1 - blockIdx.x / units;  // heaviest row tiles first
-  const int b = unit / a.Hq, h = unit % a.Hq, g = h / a.G;
+  const int unit = blockIdx.x % units, tile = tiles - 1 - blockIdx.x / units;
+  const int g = unit % a.Hkv, jq = unit / a.Hkv;
+  const int b = jq / a.G, h = g * a.G + jq % a.G;
   const int i0w = tile * BM + 32 * wave;
   const bool active = i0w < T;
   const int kend = min(T, tile * BM + BM);
@@ -199,7 +214,14 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
     }
   }
   const int64_t rr = ((int64_t)b * a.Hq + h) * a.Tp + min(row, a.Tp - 1);
-  const float lse_r = a.lsew[rr], D_r = a.Dw[rr];
+  float lse_r = a.lsew[rr], D_r = a.Dw[rr];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    retire(qf[ks]);
+    retire(af[ks]);
+  }
+  retire(lse_r);
+  retire(D_r);
   uint32_t rb[KS];
   row_read_bases<D>(li, hg, rb);
   TrBases<D> tb;
@@ -293,7 +315,14 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   const int key = j0w + li;
   const int nrt = (T + kBT - 1) / kBT;  // row tiles of 32
   const int rt0 = J0 / kBT;
-  const int nit = a.G * (nrt - rt0);    // (head, row tile) iterations
+  const int nit = a.G * (nrt - rt0);    // (row tile, head) iterations
+  // Iteration it: row tile nrt-1 - it/G (rows descending), head g*G + it%G.
+  // Every workgroup starts at the last row tile and they step down in
+  // lockstep, so the workgroups of one kv group (one XCD: the group varies
+  // fastest in the grid order) read the same Q / dA tiles at about the same
+  // time, from that XCD's L2; a workgroup stops at its own first keys.
+  auto it_row0 = [&](int it) { return (nrt - 1 - it / a.G) * kBT; };
+  auto it_head = [&](int it) { return g * a.G + it % a.G; };
 
   // B operands: K^T (both waves) and V^T (the dK wave) of this wave's keys
   bf16x8 kf[KS], vf[KS];
@@ -305,9 +334,14 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
       kf[ks] = as_bf16x8(key < T ? *(const uint4*)(kr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
       vf[ks] = as_bf16x8(key < T && kwave ? *(const uint4*)(vr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
     }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      retire(kf[ks]);
+      retire(vf[ks]);
+    }
   }
   auto issue = [&](int it, int stage) {
-    const int hh = g * a.G + it / (nrt - rt0), i0 = (rt0 + it % (nrt - rt0)) * kBT;
+    const int hh = it_head(it), i0 = it_row0(it);
     const uint16_t* qp = (const uint16_t*)a.q.p + b * a.q.sb + hh * a.q.sh;
     const uint16_t* ap = a.dA + ((int64_t)b * T * a.Hq + hh) * D;
     const uint32_t st = lds0 + stage * STAGE;
@@ -337,7 +371,7 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
   auto tile_step = [&](int it, int stage) {
-    const int i0 = (rt0 + it % (nrt - rt0)) * kBT;
+    const int i0 = it_row0(it);
     if (!active || i0 < j0w) return;  // rows before this wave's keys
     const bool diag = i0 == j0w;
     const uint32_t st = lds0 + stage * STAGE;
