@@ -18,9 +18,9 @@ numpy float64 arrays through ctypes.  Layouts are dense, as documented in
 * V2 decode over a paged cache: k, v pages ``[num_pages, page_size, Hkv, d]``,
   an int page table ``[B, >= ceil(L_b / page_size)]`` and lengths ``[B]``.
 
-``oracle.backward`` (numpy, fp64) holds the V2 training step: the forward
-with what a backward pass keeps (per-head attention outputs, log-sum-exp)
-and the gradients.
+``oracle.backward`` (numpy, fp64) holds the V2 and V1 training steps: the
+forward with what a backward pass keeps (per-head or per-map attention
+outputs, log-sum-exp) and the gradients.
 """
 from __future__ import annotations
 

@@ -142,3 +142,139 @@ def test_backward_mutant_is_caught(name, monkeypatch):
         except AssertionError:
             failed += 1
     assert failed >= 1, f"no pin catches mutation {name}"
+
+
+# ---- DIFF V1 ---------------------------------------------------------------------
+
+def _v1_case(seed, B, H, T, d):
+    rng = np.random.default_rng(seed)
+    qk = [rng.standard_normal((B, H, T, d)) for _ in range(4)]
+    v = rng.standard_normal((B, H, T, 2 * d))
+    lams = [0.1 * rng.standard_normal(d) for _ in range(4)]
+    dout = rng.standard_normal((B, T, H, 2 * d))
+    return qk, v, lams, dout, rng
+
+
+V1_NAMES = ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")
+
+
+def test_v1_fwd_train_matches_the_forward_oracle():
+    (q1, q2, k1, k2), v, lams, _, _ = _v1_case(3, 2, 2, 11, 8)
+    layer = 5
+    lam = oracle.v1_lambda(*lams, layer)
+    li = oracle.lambda_init(layer)
+    for s1 in (False, True):
+        out, a1, a2, lse2 = ob.v1_fwd_train(q1, q2, k1, k2, v, *lams, layer, softmax1=s1)
+        assert np.abs(out - oracle.v1_fwd(q1, q2, k1, k2, v, *lams, layer, softmax1=s1)).max() < 1e-12
+        D = a1 - lam * a2
+        assert np.abs(out - (1 - li) * D / np.sqrt((D * D).mean(-1, keepdims=True) + 1e-5)).max() < 1e-12
+        T, d = q1.shape[2], q1.shape[3]
+        for m, (q, k, a) in enumerate(((q1, k1, a1), (q2, k2, a2))):
+            S = q[1, 0] @ k[1, 0].T / math.sqrt(d) * math.log2(math.e)
+            S = np.where(np.triu(np.ones((T, T), bool), 1), -np.inf, S)
+            P = np.exp2(S - lse2[m, 1, 0][:, None])
+            want = 1.0 - (np.exp2(-lse2[m, 1, 0]) if s1 else 0.0)
+            assert np.abs(P.sum(axis=1) - want).max() < 1e-12
+            assert np.abs(P @ v[1, 0] - a[1, :, 0]).max() < 1e-12
+
+
+@settings(max_examples=15, deadline=None)
+@given(B=st.integers(1, 2), H=st.integers(1, 2), T=st.sampled_from([1, 2, 5, 12]), d=st.sampled_from([2, 4, 8]),
+       layer=st.integers(0, 14), s1=st.booleans(), seed=st.integers(0, 10**6))
+def test_v1_bwd_matches_central_differences(B, H, T, d, layer, s1, seed):
+    """<grad, u> equals the central difference of sum(dout * out) along a
+    random direction u, for each of the nine inputs."""
+    qk, v, lams, dout, rng = _v1_case(seed, B, H, T, d)
+    args = dict(zip(V1_NAMES, qk + [v] + lams))
+    grads = dict(zip(V1_NAMES, ob.v1_bwd(**args, layer=layer, dout=dout, softmax1=s1)))
+    f = lambda **a: float((ob.v1_fwd_train(**a, layer=layer, softmax1=s1)[0] * dout).sum())
+    eps = 1e-5
+    for name, x in args.items():
+        u = rng.standard_normal(x.shape)
+        fd = (f(**{**args, name: x + eps * u}) - f(**{**args, name: x - eps * u})) / (2 * eps)
+        an = float((grads[name] * u).sum())
+        assert abs(fd - an) <= 1e-6 * (1.0 + abs(an)), (name, fd, an)
+
+
+def _torch_v1_forward(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer, softmax1):
+    """An independent fp64 forward from torch library routines: causal
+    scaled_dot_product_attention per map (the off-by-one softmax as one extra
+    zero key and zero value row in front, unmasked) and rms_norm."""
+    import torch.nn.functional as F
+    li = 0.8 - 0.6 * math.exp(-0.3 * layer)
+    lam = torch.exp((lq1 * lk1).sum()) - torch.exp((lq2 * lk2).sum()) + li
+    B, H, T, d = q1.shape
+
+    def attend(q, k):
+        if not softmax1:
+            return F.scaled_dot_product_attention(q, k, v, is_causal=True)
+        z = lambda x: torch.cat([torch.zeros(B, H, 1, x.shape[-1], dtype=x.dtype), x], dim=2)
+        mask = torch.ones(T, T + 1, dtype=torch.bool).tril(1)
+        return F.scaled_dot_product_attention(q, z(k), z(v), attn_mask=mask)
+
+    D = attend(q1, k1) - lam * attend(q2, k2)                     # [B, H, T, 2d]
+    y = F.rms_norm(D, (2 * d,), eps=1e-5) * (1 - li)
+    return y.transpose(1, 2)                                       # [B, T, H, 2d]
+
+
+@pytest.mark.parametrize("s1", [False, True])
+def test_v1_bwd_matches_torch_autograd(s1):
+    qk, v, lams, dout, _ = _v1_case(9, 2, 2, 13, 8)
+    ts = [torch.tensor(x, requires_grad=True) for x in qk + [v] + lams]
+    (_torch_v1_forward(*ts, 7, s1) * torch.tensor(dout)).sum().backward()
+    for name, got, t in zip(V1_NAMES, ob.v1_bwd(*qk, v, *lams, 7, dout, softmax1=s1), ts):
+        assert np.abs(got - t.grad.numpy()).max() < 1e-10, name
+
+
+def test_v1_bwd_lambda_vector_structure():
+    """d lam / d lq1 = e1 lk1 and d lam / d lk1 = e1 lq1 (same for map 2 with
+    a minus sign): the four vector gradients share one scalar, so
+    dlq1 / lk1 = dlk1 / lq1 = -(dlq2 / lk2) e1 / e2 elementwise."""
+    qk, v, lams, dout, _ = _v1_case(10, 1, 2, 9, 4)
+    g = ob.v1_bwd(*qk, v, *lams, 2, dout)
+    lq1, lk1, lq2, lk2 = lams
+    e1, e2 = math.exp(lq1 @ lk1), math.exp(lq2 @ lk2)
+    s = g[5] / lk1
+    assert np.abs(s - s[0]).max() < 1e-12 * abs(s[0])
+    assert np.abs(g[6] / lq1 - s[0]).max() < 1e-12 * abs(s[0])
+    assert np.abs(-g[7] / lk2 * e1 / e2 - s[0]).max() < 1e-12 * abs(s[0])
+    assert np.abs(-g[8] / lq2 * e1 / e2 - s[0]).max() < 1e-12 * abs(s[0])
+
+
+V1_BWD_SRC = inspect.getsource(ob.v1_bwd)
+
+V1_BWD_MUTATIONS = {
+    "second_map_sign": ("for m, da in enumerate((dD, -lam * dD)):", "for m, da in enumerate((dD, lam * dD)):"),
+    "norm_no_projection": ("dD = (1.0 - li) * r * (g - r * r * D * (g * D).mean(axis=1, keepdims=True))",
+                           "dD = (1.0 - li) * r * g"),
+    "norm_missing_r2": ("(g - r * r * D * (g * D).mean(axis=1, keepdims=True))",
+                        "(g - D * (g * D).mean(axis=1, keepdims=True))"),
+    "no_output_scale": ("dD = (1.0 - li) * r *", "dD = r *"),
+    "dlam_from_first_map": ("dlam -= float((dD * a[1]).sum())", "dlam -= float((dD * a[0]).sum())"),
+    "dv_one_map": ("dv[b, h] += P[m].T @ da", "dv[b, h] = P[m].T @ da"),
+    "swapped_lambda_pair": ("-dlam * e2 * lk2, -dlam * e2 * lq2", "-dlam * e2 * lq2, -dlam * e2 * lk2"),
+    "dk_unscaled": ("dk[m][b, h] = dS.T @ qs[m][b, h] / math.sqrt(d)", "dk[m][b, h] = dS.T @ qs[m][b, h]"),
+}
+
+V1_BWD_PINS = [
+    lambda: test_v1_bwd_matches_central_differences.hypothesis.inner_test(
+        B=1, H=2, T=6, d=4, layer=3, s1=False, seed=12),
+    lambda: test_v1_bwd_matches_torch_autograd(False),
+]
+
+
+@pytest.mark.parametrize("name", sorted(V1_BWD_MUTATIONS))
+def test_v1_backward_mutant_is_caught(name, monkeypatch):
+    old, new = V1_BWD_MUTATIONS[name]
+    assert V1_BWD_SRC.count(old) == 1, f"mutation {name} no longer matches the oracle source"
+    ns = dict(vars(ob))
+    exec(compile(V1_BWD_SRC.replace(old, new), "<mutant>", "exec"), ns)
+    monkeypatch.setattr(ob, "v1_bwd", ns["v1_bwd"])
+    failed = 0
+    for pin in V1_BWD_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, f"no pin catches mutation {name}"
