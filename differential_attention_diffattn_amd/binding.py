@@ -19,6 +19,10 @@ Logical layouts (any strided view with a unit-stride last axis is accepted):
              q [B,Hq,d] or [B,nq,Hq,d]; k_pages, v_pages [num_pages,page_size,Hkv,d];
              block_table int32 [B, >= ceil(max_len/page_size)]; seq_lens
              int32 [B]; lam [B,Hq/2] fp32; returns / writes out [B,Hq/2,d]
+  v1_fwd_train  as v1_fwd, also returning attn1, attn2 [B,T,H,2d] and lse fp32 [2,B,H,T]
+  v1_bwd     gradients dq1, dq2, dk1, dk2 [B,H,T,d], dv [B,H,T,2d] and the four
+             lambda vectors' gradients fp32 [d] from dout [B,T,H,2d] and the
+             training forward's attn1, attn2, lse
   v2_fwd_train  as v2_fwd, also returning attn [B,T,Hq,d] and lse fp32 [B,Hq,T]
   v2_bwd     gradients dq [B,T,Hq,d], dk, dv [B,T,Hkv,d], dlam fp32 [B,T,Hq/2]
              from dout [B,T,Hq/2,d] and the training forward's attn, lse
@@ -88,6 +92,15 @@ def load_library():
         f.argtypes = [i, i, i, i, i, i, i, DaIn, DaIn, DaIn, i, i, vp, ctypes.c_int64, vp, DaIn, DaOut, vp,
                       ctypes.c_size_t, vp]
         f.restype = i
+    for sfx in ("", "_softmax1"):
+        f = getattr(lib, "diffattn_v1_fwd_train" + sfx)
+        f.argtypes = [i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaIn, fp, fp, fp, fp, i, DaOut, DaOut, DaOut, vp, vp]
+        f.restype = i
+    lib.diffattn_v1_bwd.argtypes = [i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaIn, fp, fp, fp, fp, i, DaIn, DaIn, vp,
+                                    DaIn, DaOut, DaOut, DaOut, DaOut, DaOut, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.diffattn_v1_bwd.restype = i
+    lib.diffattn_v1_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    lib.diffattn_v1_bwd_workspace_bytes.restype = ctypes.c_size_t
     for sfx in ("", "_softmax1"):
         f = getattr(lib, "diffattn_v2_fwd_train" + sfx)
         f.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaOut, DaOut, vp, vp]
@@ -176,6 +189,76 @@ def v1_fwd(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, out: torch.Tensor 
     if st != 0:
         raise DiffAttnError(st, name)
     return out
+
+
+def _v1_shapes(q1, q2, k1, k2, v, lams):
+    B, H, T, d = q1.shape
+    for x in (q2, k1, k2):
+        if tuple(x.shape) != (B, H, T, d):
+            raise ValueError(f"q/k shape mismatch: {tuple(x.shape)} vs {(B, H, T, d)}")
+    if tuple(v.shape) != (B, H, T, 2 * d):
+        raise ValueError(f"v must be {(B, H, T, 2 * d)}, got {tuple(v.shape)}")
+    for x in lams:
+        if x.dtype != torch.float32 or tuple(x.shape) != (d,) or not x.is_contiguous():
+            raise ValueError("lambda vectors must be contiguous fp32 of shape [d]")
+    return B, H, T, d
+
+
+def v1_fwd_train(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, out=None, attn1=None, attn2=None, lse=None,
+                 softmax1: bool = False):
+    """DIFF V1 training forward; returns (out [B,T,H,2d], attn1, attn2 [B,T,H,2d], lse fp32 [2,B,H,T])."""
+    lib = load_library()
+    lams = [x.contiguous() for x in (lq1, lk1, lq2, lk2)]
+    B, H, T, d = _v1_shapes(q1, q2, k1, k2, v, lams)
+    mk = lambda: torch.empty((B, T, H, 2 * d), dtype=q1.dtype, device=q1.device)
+    out = mk() if out is None else out
+    attn1 = mk() if attn1 is None else attn1
+    attn2 = mk() if attn2 is None else attn2
+    lse = torch.empty((2, B, H, T), dtype=torch.float32, device=q1.device) if lse is None else lse
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (2, B, H, T) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [2,B,H,T]")
+    _check_device(q1, q2, k1, k2, v, out, attn1, attn2, *lams)
+    name = "diffattn_v1_fwd_train" + ("_softmax1" if softmax1 else "")
+    st = getattr(lib, name)(_dtype_code(q1), B, H, T, d, _in(q1, 0, 1, 2), _in(q2, 0, 1, 2), _in(k1, 0, 1, 2),
+                            _in(k2, 0, 1, 2), _in(v, 0, 1, 2), *[x.data_ptr() for x in lams], int(layer),
+                            _out(out, 0, 2, 1), _out(attn1, 0, 2, 1), _out(attn2, 0, 2, 1), lse.data_ptr(),
+                            _stream(q1))
+    if st != 0:
+        raise DiffAttnError(st, name)
+    return out, attn1, attn2, lse
+
+
+def v1_bwd_workspace_bytes(B: int, H: int, T: int, d: int) -> int:
+    return int(load_library().diffattn_v1_bwd_workspace_bytes(B, H, T, d))
+
+
+def v1_bwd(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, attn1, attn2, lse, dout, grads=None,
+           workspace: torch.Tensor | None = None):
+    """DIFF V1 backward; returns (dq1, dq2, dk1, dk2 [B,H,T,d], dv [B,H,T,2d],
+    dlq1, dlk1, dlq2, dlk2 fp32 [d]); ``grads`` may supply those nine outputs."""
+    lib = load_library()
+    lams = [x.contiguous() for x in (lq1, lk1, lq2, lk2)]
+    B, H, T, d = _v1_shapes(q1, q2, k1, k2, v, lams)
+    for x in (attn1, attn2, dout):
+        if tuple(x.shape) != (B, T, H, 2 * d):
+            raise ValueError("attn1, attn2 and dout must be [B,T,H,2d]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (2, B, H, T) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [2,B,H,T]")
+    if grads is None:
+        grads = [torch.empty_like(x) for x in (q1, q2, k1, k2, v)] + \
+                [torch.empty(d, dtype=torch.float32, device=q1.device) for _ in range(4)]
+    need = v1_bwd_workspace_bytes(B, H, T, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q1.device)
+    _check_device(q1, q2, k1, k2, v, attn1, attn2, dout, *grads)
+    st = lib.diffattn_v1_bwd(_dtype_code(q1), B, H, T, d, _in(q1, 0, 1, 2), _in(q2, 0, 1, 2), _in(k1, 0, 1, 2),
+                             _in(k2, 0, 1, 2), _in(v, 0, 1, 2), *[x.data_ptr() for x in lams], int(layer),
+                             _in(attn1, 0, 2, 1), _in(attn2, 0, 2, 1), lse.data_ptr(), _in(dout, 0, 2, 1),
+                             *[_out(g, 0, 1, 2) for g in grads[:5]], *[g.data_ptr() for g in grads[5:]],
+                             workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q1))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_v1_bwd")
+    return tuple(grads)
 
 
 def v2_fwd(q, k, v, lam, out: torch.Tensor | None = None, softmax1: bool = False):

@@ -190,7 +190,8 @@ const char* diffattn_status_string(da_status s) {
 static da_status v1_fwd_impl(int softmax1, da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2,
                              da_in k1, da_in k2,
                           da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
-                          const float* lam_k2, int layer_index, da_out out, void* stream) {
+                          const float* lam_k2, int layer_index, da_out out, void* stream,
+                          const da_out* attn1 = nullptr, const da_out* attn2 = nullptr, float* lse = nullptr) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
   if (B < 1 || H < 1 || T < 1 || d < 1 || layer_index < 0) return DA_E_SHAPE;
   const int64_t mult = dtype == DA_BF16 ? 8 : 4;
@@ -208,6 +209,13 @@ static da_status v1_fwd_impl(int softmax1, da_dtype dtype, int B, int H, int T, 
   if (dtype == DA_BF16 && (k1.st >= kMaxTokenStride || k2.st >= kMaxTokenStride || v.st >= kMaxTokenStride))
     return DA_E_UNSUPPORTED;
   if (!grid_fits((long long)B * H * ((T + 31) / 32))) return DA_E_SHAPE;
+  if (attn1) {  // training forward (bf16 only)
+    if (dtype != DA_BF16) return DA_E_UNSUPPORTED;
+    DA_TRY(check_out(*attn1, 8));
+    DA_TRY(check_out(*attn2, 8));
+    if (!lse) return DA_E_NULL;
+    if (!aligned(lse, 4)) return DA_E_LAYOUT;
+  }
 
   const float li = (float)diffattn_lambda_init(layer_index);
   hipStream_t s = (hipStream_t)stream;
@@ -220,6 +228,11 @@ static da_status v1_fwd_impl(int softmax1, da_dtype dtype, int B, int H, int T, 
     a.sl2 = log2e_over_sqrt(d);
     a.B = B, a.T = T, a.H = H;
     a.softmax1 = softmax1;
+    if (attn1) {
+      a.attn = tout(*attn1);
+      a.attn2 = tout(*attn2);
+      a.lse = lse;
+    }
     return launch_status(da::launch_prefill_v1_bf16(d, a, s));
   }
   da::V1F32Args a{};
@@ -319,6 +332,67 @@ static da_status v2_bwd_impl(da_dtype dtype, int B, int T, int Hq, int Hkv, int 
   return launch_status(da::launch_backward_v2_bf16(d, a, (hipStream_t)stream));
 }
 
+// DIFF V1 backward: workspace regions (each 256-byte aligned).
+struct V1BwdWs {
+  size_t dA, rows, lam;  // bytes of one map's d a; of one [B][H][Tp] fp32 array; of the row terms of d lambda
+  size_t total() const { return 2 * dA + 4 * rows + lam; }
+};
+static V1BwdWs v1_bwd_ws(int B, int H, int T, int d) {
+  V1BwdWs w;
+  w.dA = ((size_t)B * T * H * 2 * d * 2 + 255) / 256 * 256;
+  w.rows = ((size_t)B * H * da::backward_padded_rows(T) * 4 + 255) / 256 * 256;
+  w.lam = ((size_t)B * T * H * 4 + 255) / 256 * 256;
+  return w;
+}
+
+static da_status v1_bwd_impl(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+                             da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
+                             const float* lam_k2, int layer_index, da_in attn1, da_in attn2, const float* lse,
+                             da_in dout, da_out dq1, da_out dq2, da_out dk1, da_out dk2, da_out dv, float* dlam_q1,
+                             float* dlam_k1, float* dlam_q2, float* dlam_k2, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
+  if (B < 1 || H < 1 || T < 1 || d < 1 || layer_index < 0) return DA_E_SHAPE;
+  for (const da_in* t : {&q1, &q2, &k1, &k2, &v, &attn1, &attn2, &dout}) DA_TRY(check_in(*t, 8));
+  for (const da_out* t : {&dq1, &dq2, &dk1, &dk2, &dv}) DA_TRY(check_out(*t, 8));
+  for (const float* p : {lam_q1, lam_k1, lam_q2, lam_k2, lse, (const float*)dlam_q1, (const float*)dlam_k1,
+                         (const float*)dlam_q2, (const float*)dlam_k2}) {
+    if (!p) return DA_E_NULL;
+    if (!aligned(p, 4)) return DA_E_LAYOUT;
+  }
+  if (dtype != DA_BF16) return DA_E_UNSUPPORTED;
+  if (d != 64 && d != 128) return DA_E_UNSUPPORTED;
+  for (int64_t st : {q1.st, q2.st, k1.st, k2.st, v.st, (int64_t)H * 2 * d})
+    if (st >= kMaxTokenStride) return DA_E_UNSUPPORTED;
+  const V1BwdWs w = v1_bwd_ws(B, H, T, d);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.total()) return DA_E_WORKSPACE;
+  const int qt = (T + 127) / 128;
+  if (!grid_fits((long long)B * H * 2 * qt) || !grid_fits(((long long)B * da::backward_padded_rows(T) * H + 3) / 4))
+    return DA_E_SHAPE;
+
+  da::V1BwdArgs a{};
+  a.q[0] = tin(q1), a.q[1] = tin(q2), a.k[0] = tin(k1), a.k[1] = tin(k2), a.v = tin(v);
+  a.a[0] = tin(attn1), a.a[1] = tin(attn2), a.dout = tin(dout);
+  a.lse = lse;
+  a.lq1 = lam_q1, a.lk1 = lam_k1, a.lq2 = lam_q2, a.lk2 = lam_k2;
+  a.dq[0] = tout(dq1), a.dq[1] = tout(dq2), a.dk[0] = tout(dk1), a.dk[1] = tout(dk2), a.dv = tout(dv);
+  a.dlq1 = dlam_q1, a.dlk1 = dlam_k1, a.dlq2 = dlam_q2, a.dlk2 = dlam_k2;
+  char* p = (char*)workspace;
+  a.dA[0] = (uint16_t*)p;
+  a.dA[1] = (uint16_t*)(p + w.dA);
+  p += 2 * w.dA;
+  for (int m = 0; m < 2; ++m) {
+    a.Dw[m] = (float*)(p + (2 * m) * w.rows);
+    a.lsew[m] = (float*)(p + (2 * m + 1) * w.rows);
+  }
+  a.lamrow = (float*)(p + 4 * w.rows);
+  a.lam_init = (float)diffattn_lambda_init(layer_index);
+  a.sl2 = log2e_over_sqrt(d);
+  a.scale = (float)(1.0 / sqrt((double)d));
+  a.B = B, a.T = T, a.H = H;
+  a.Tp = da::backward_padded_rows(T);
+  return launch_status(da::launch_backward_v1_bf16(d, a, (hipStream_t)stream));
+}
 
 size_t diffattn_v2_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int d) {
   return decode_ws_bytes(B, L, 1, Hq, Hkv, d, 2048);
@@ -426,6 +500,38 @@ da_status diffattn_v2_bwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, 
                           da_in lam, da_in attn, const float* lse, da_in dout, da_out dq, da_out dk, da_out dv,
                           da_out dlam, void* workspace, size_t workspace_bytes, void* stream) {
   return v2_bwd_impl(dtype, B, T, Hq, Hkv, d, q, k, v, lam, attn, lse, dout, dq, dk, dv, dlam, workspace,
+                     workspace_bytes, stream);
+}
+
+da_status diffattn_v1_fwd_train(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+                                da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
+                                const float* lam_k2, int layer_index, da_out out, da_out attn1, da_out attn2,
+                                float* lse, void* stream) {
+  return v1_fwd_impl(0, dtype, B, H, T, d, q1, q2, k1, k2, v, lam_q1, lam_k1, lam_q2, lam_k2, layer_index, out,
+                     stream, &attn1, &attn2, lse);
+}
+
+da_status diffattn_v1_fwd_train_softmax1(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2,
+                                         da_in k1, da_in k2, da_in v, const float* lam_q1, const float* lam_k1,
+                                         const float* lam_q2, const float* lam_k2, int layer_index, da_out out,
+                                         da_out attn1, da_out attn2, float* lse, void* stream) {
+  return v1_fwd_impl(1, dtype, B, H, T, d, q1, q2, k1, k2, v, lam_q1, lam_k1, lam_q2, lam_k2, layer_index, out,
+                     stream, &attn1, &attn2, lse);
+}
+
+size_t diffattn_v1_bwd_workspace_bytes(int B, int H, int T, int d) {
+  if (B < 1 || H < 1 || T < 1 || d < 1) return 0;
+  return v1_bwd_ws(B, H, T, d).total();
+}
+
+da_status diffattn_v1_bwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+                          da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
+                          const float* lam_k2, int layer_index, da_in attn1, da_in attn2, const float* lse,
+                          da_in dout, da_out dq1, da_out dq2, da_out dk1, da_out dk2, da_out dv, float* dlam_q1,
+                          float* dlam_k1, float* dlam_q2, float* dlam_k2, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return v1_bwd_impl(dtype, B, H, T, d, q1, q2, k1, k2, v, lam_q1, lam_k1, lam_q2, lam_k2, layer_index, attn1,
+                     attn2, lse, dout, dq1, dq2, dk1, dk2, dv, dlam_q1, dlam_k1, dlam_q2, dlam_k2, workspace,
                      workspace_bytes, stream);
 }
 

@@ -165,13 +165,16 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 
 // ---- dQ ------------------------------------------------------------------------
-// Workgroup: (b, head h, 32 kNW query rows); wave w owns rows i0 + 32 w.
-template <int D>
+// Workgroup: (b, head h, 32 kNW query rows); wave w owns rows i0 + 32 w.  D:
+// q/k head dim; DV: v head dim (V2: D; V1: 2D, one launch per map).
+template <int D, int DV>
 __global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
-  constexpr int KS = D / 16, CB = D / 32;
+  constexpr int KS = D / 16, KSV = DV / 16, CB = D / 32;
+  constexpr int KM = KS > KSV ? KS : KSV;
   using Dma = TileDma<D>;
+  using DmaV = TileDma<DV>;
   constexpr int TB = Dma::BYTES;
-  constexpr int STAGE = 3 * TB;  // [K "k" | K "v" | V "k"]
+  constexpr int STAGE = 2 * TB + DmaV::BYTES;  // [K "k" | K "v" | V "k"]
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
@@ -198,32 +201,33 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
     const uint32_t st = lds0 + stage * STAGE;
     Dma::issue(kp, a.k.st, kt * kBT, T, false, st, wave, lane);
     Dma::issue(kp, a.k.st, kt * kBT, T, true, st + TB, wave, lane);
-    Dma::issue(vp, a.v.st, kt * kBT, T, false, st + 2 * TB, wave, lane);
+    DmaV::issue(vp, a.v.st, kt * kBT, T, false, st + 2 * TB, wave, lane);
   };
   issue(0, 0);
 
   // B operands: Q^T and dA^T of this wave's rows; the row's lse and D
-  bf16x8 qf[KS], af[KS];
+  bf16x8 qf[KS], af[KSV];
   {
     const uint16_t* qr = (const uint16_t*)a.q.p + b * a.q.sb + (int64_t)row * a.q.st + h * a.q.sh;
-    const uint16_t* ar = a.dA + (((int64_t)b * T + row) * a.Hq + h) * D;
+    const uint16_t* ar = a.dA + (((int64_t)b * T + row) * a.Hq + h) * DV;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks)
       qf[ks] = as_bf16x8(row < T ? *(const uint4*)(qr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+    for (int ks = 0; ks < KSV; ++ks)
       af[ks] = as_bf16x8(row < T ? *(const uint4*)(ar + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
-    }
   }
   const int64_t rr = ((int64_t)b * a.Hq + h) * a.Tp + min(row, a.Tp - 1);
   float lse_r = a.lsew[rr], D_r = a.Dw[rr];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    retire(qf[ks]);
-    retire(af[ks]);
-  }
+  for (int ks = 0; ks < KS; ++ks) retire(qf[ks]);
+#pragma unroll
+  for (int ks = 0; ks < KSV; ++ks) retire(af[ks]);
   retire(lse_r);
   retire(D_r);
-  uint32_t rb[KS];
+  uint32_t rb[KS], rbv[KSV];
   row_read_bases<D>(li, hg, rb);
+  row_read_bases<DV>(li, hg, rbv);
   TrBases<D> tb;
   tb.init(lane);
   const float sl2 = a.sl2;
@@ -246,9 +250,9 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = mfma32x32x16(lds_read16(st + rb[ks]), qf[ks], s);             // S^T = K Q^T
-      dp = mfma32x32x16(lds_read16(st + 2 * TB + rb[ks]), af[ks], dp);  // dP^T = V dA^T
+    for (int ks = 0; ks < KM; ++ks) {
+      if (ks < KS) s = mfma32x32x16(lds_read16(st + rb[ks]), qf[ks], s);                // S^T = K Q^T
+      if (ks < KSV) dp = mfma32x32x16(lds_read16(st + 2 * TB + rbv[ks]), af[ks], dp);  // dP^T = V dA^T
     }
     // lane: row li; register r: key j0 + 8(r>>2) + 4hg + (r&3)
     f32x8 e0, e1;
@@ -441,10 +445,413 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
                                  (void**)args, 0, st);
   if (e != hipSuccess) return e;
   const int qt = (a.T + 32 * kNW - 1) / (32 * kNW);
-  e = hipLaunchKernel((const void*)bwd_dq_kernel<D>, dim3(a.B * a.Hq * qt), dim3(kNW * 64), (void**)args, 0, st);
+  e = hipLaunchKernel((const void*)bwd_dq_kernel<D, D>, dim3(a.B * a.Hq * qt), dim3(kNW * 64), (void**)args, 0, st);
   if (e != hipSuccess) return e;
   return hipLaunchKernel((const void*)bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * qt), dim3(2 * kNW * 64), (void**)args,
                          0, st);
+}
+
+
+// ==== DIFF V1 =======================================================================
+//
+// ("Differential Transformer V2" article, DiffAttnV1 pseudo-code; the RMSNorm
+// arguments of Wilsontomass's module in the nanoGPT issue "How best to
+// implement a differential transformer?")  Forward: a_m = causal softmax
+// attention of map m over the shared 2d-wide v, D = a_1 - lam a_2,
+// r = (mean D^2 + 1e-5)^(-1/2), out = (1 - lam_init) r D.  Backward:
+//   dD = (1 - lam_init) r (dout - r^2 D mean(dout D)),  da_1 = dD,
+//   da_2 = -lam dD,  dlam = -sum over rows of <dD, a_2>, and per map the
+//   softmax-attention gradients (dv summed over both maps); the lambda
+//   vectors get dlam times the derivative of exp(<lq, lk>).
+// Kernels: a pre-pass per (b, token, head); dQ with the V2 dQ kernel per map
+// (v 2d wide); dK per map; dV over both maps; a one-workgroup reduction of
+// dlam (fixed order) that writes the four vector gradients.
+
+// One wave per (b, t, h), t < Tp.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_v1_pre_kernel(const V1BwdArgs a) {
+  constexpr int DV = 2 * D, PL = DV / 64;
+  const int lane = threadIdx.x & 63;
+  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, t, h)
+  if (item >= (long long)a.B * a.Tp * a.H) return;
+  const int h = (int)(item % a.H);
+  const int t = (int)((item / a.H) % a.Tp);
+  const int b = (int)(item / ((long long)a.H * a.Tp));
+  const int64_t rw = ((int64_t)b * a.H + h) * a.Tp + t;
+  if (t >= a.T) {  // padding rows: zero D and lse (masked where read)
+    if (lane == 0) a.Dw[0][rw] = a.Dw[1][rw] = a.lsew[0][rw] = a.lsew[1][rw] = 0.f;
+    return;
+  }
+  // lambda from the vectors (D / 64 elements per lane)
+  float pa = 0.f, pb = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    const int c = lane + 64 * i;
+    pa += a.lq1[c] * a.lk1[c];
+    pb += a.lq2[c] * a.lk2[c];
+  }
+  const float lam = expf(wave_sum(pa)) - expf(wave_sum(pb)) + a.lam_init;
+  const uint16_t* gp = (const uint16_t*)a.dout.p + b * a.dout.sb + (int64_t)t * a.dout.st + h * a.dout.sh;
+  const uint16_t* a0 = (const uint16_t*)a.a[0].p + b * a.a[0].sb + (int64_t)t * a.a[0].st + h * a.a[0].sh;
+  const uint16_t* a1 = (const uint16_t*)a.a[1].p + b * a.a[1].sb + (int64_t)t * a.a[1].st + h * a.a[1].sh;
+  float g[PL], x0[PL], x1[PL], dd[PL], ss = 0.f, gd = 0.f;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int c = lane + 64 * i;
+    g[i] = bf16_to_f32(gp[c]);
+    x0[i] = bf16_to_f32(a0[c]);
+    x1[i] = bf16_to_f32(a1[c]);
+    dd[i] = x0[i] - lam * x1[i];  // D
+    ss += dd[i] * dd[i];
+    gd += g[i] * dd[i];
+  }
+  const float r = rsqrtf(wave_sum(ss) * (1.f / DV) + 1e-5f);
+  const float pm = r * r * wave_sum(gd) * (1.f / DV);
+  const float cr = (1.f - a.lam_init) * r;
+  uint16_t* d0 = a.dA[0] + (((int64_t)b * a.T + t) * a.H + h) * DV;
+  uint16_t* d1 = a.dA[1] + (((int64_t)b * a.T + t) * a.H + h) * DV;
+  float s0 = 0.f, s1 = 0.f, sl = 0.f;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int c = lane + 64 * i;
+    const float dD = cr * (g[i] - dd[i] * pm);
+    const uint32_t w0 = pack_bf16x2(dD, 0.f) & 0xffffu, w1 = pack_bf16x2(-lam * dD, 0.f) & 0xffffu;
+    d0[c] = (uint16_t)w0;
+    d1[c] = (uint16_t)w1;
+    // D_m from the rounded d a_m the MFMAs see
+    s0 += bf16_to_f32((uint16_t)w0) * x0[i];
+    s1 += bf16_to_f32((uint16_t)w1) * x1[i];
+    sl -= dD * x1[i];
+  }
+  s0 = wave_sum(s0);
+  s1 = wave_sum(s1);
+  sl = wave_sum(sl);
+  if (lane == 0) {
+    a.Dw[0][rw] = s0;
+    a.Dw[1][rw] = s1;
+    a.lsew[0][rw] = a.lse[(((int64_t)0 * a.B + b) * a.H + h) * a.T + t];
+    a.lsew[1][rw] = a.lse[(((int64_t)1 * a.B + b) * a.H + h) * a.T + t];
+    a.lamrow[((int64_t)b * a.T + t) * a.H + h] = sl;
+  }
+}
+
+// One workgroup: dlam = sum of the row terms, in a fixed order (each thread a
+// fixed strided subset, then a fixed tree), then the four vector gradients.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_v1_lam_kernel(const V1BwdArgs a) {
+  __shared__ float part[256];
+  __shared__ float ex[2];
+  const int tid = threadIdx.x;
+  const long long n = (long long)a.B * a.T * a.H;
+  float acc = 0.f;
+  for (long long i = tid; i < n; i += 256) acc += a.lamrow[i];
+  part[tid] = acc;
+  if (tid < 64) {  // e1 = exp(<lq1, lk1>), e2 = exp(<lq2, lk2>)
+    float pa = 0.f, pb = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      const int c = tid + 64 * i;
+      pa += a.lq1[c] * a.lk1[c];
+      pb += a.lq2[c] * a.lk2[c];
+    }
+    pa = wave_sum(pa);
+    pb = wave_sum(pb);
+    if (tid == 0) {
+      ex[0] = expf(pa);
+      ex[1] = expf(pb);
+    }
+  }
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) part[tid] += part[tid + w];
+    __syncthreads();
+  }
+  const float dl = part[0];
+  for (int c = tid; c < D; c += 256) {
+    a.dlq1[c] = dl * ex[0] * a.lk1[c];
+    a.dlk1[c] = dl * ex[0] * a.lq1[c];
+    a.dlq2[c] = -dl * ex[1] * a.lk2[c];
+    a.dlk2[c] = -dl * ex[1] * a.lq2[c];
+  }
+}
+
+// dK of one map: workgroup (b, h, map, 32 kNW keys), wave w owns keys
+// J0 + 32 w and loops over the row tiles at or after them (rows descending).
+// S = Q K^T and dP = dA V^T with K / V fragments of its keys in registers,
+// dS = P (dP - D), dK^T += Q^T dS with transpose reads of the Q tile.
+template <int D>
+__global__ void __launch_bounds__(kNW * 64, 2) bwd_v1_dk_kernel(const V1BwdArgs a) {
+  constexpr int DV = 2 * D;
+  constexpr int KS = D / 16, KSV = DV / 16, CB = D / 32;
+  using Dma = TileDma<D>;
+  using DmaV = TileDma<DV>;
+  constexpr int TB = Dma::BYTES, TBV = DmaV::BYTES;
+  constexpr int STAGE = 2 * TB + TBV + 256;  // [Q "k" | Q "v" | dA "k" | lse, D of the 32 rows]
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int li = lane & 31, hg = lane >> 5;
+  const int T = a.T, BK = 32 * kNW;
+  const int units = a.B * a.H * 2;
+  const int unit = blockIdx.x % units, kt = blockIdx.x / units;  // low key tiles (most rows) first
+  const int m = unit & 1, bh = unit >> 1;
+  const int b = bh / a.H, h = bh % a.H;
+  const int J0 = kt * BK, j0w = J0 + 32 * wave;
+  const bool active = j0w < T;
+  const int key = j0w + li;
+  const int nrt = (T + kBT - 1) / kBT;
+  const int rt0 = J0 / kBT;
+  const int nit = nrt - rt0;
+  auto it_row0 = [&](int it) { return (nrt - 1 - it) * kBT; };
+
+  const TIn& tq = a.q[m];
+  const TIn& tk = a.k[m];
+  bf16x8 kf[KS], vf[KSV];
+  {
+    const uint16_t* kr = (const uint16_t*)tk.p + b * tk.sb + (int64_t)key * tk.st + h * tk.sh;
+    const uint16_t* vr = (const uint16_t*)a.v.p + b * a.v.sb + (int64_t)key * a.v.st + h * a.v.sh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[ks] = as_bf16x8(key < T ? *(const uint4*)(kr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+    for (int ks = 0; ks < KSV; ++ks)
+      vf[ks] = as_bf16x8(key < T ? *(const uint4*)(vr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) retire(kf[ks]);
+#pragma unroll
+    for (int ks = 0; ks < KSV; ++ks) retire(vf[ks]);
+  }
+  const uint16_t* qp = (const uint16_t*)tq.p + b * tq.sb + h * tq.sh;
+  const uint16_t* ap = a.dA[m] + ((int64_t)b * T * a.H + h) * DV;
+  const float* lsw = a.lsew[m] + ((int64_t)b * a.H + h) * a.Tp;
+  const float* dw = a.Dw[m] + ((int64_t)b * a.H + h) * a.Tp;
+  auto issue = [&](int it, int stage) {
+    const int i0 = it_row0(it);
+    const uint32_t st = lds0 + stage * STAGE;
+    Dma::issue(qp, tq.st, i0, T, false, st, wave, lane);
+    Dma::issue(qp, tq.st, i0, T, true, st + TB, wave, lane);
+    DmaV::issue(ap, (int64_t)a.H * DV, i0, T, false, st + 2 * TB, wave, lane);
+    // the 32 rows' lse and D (padded arrays: always in bounds), 8 lanes x 16 B each
+    if (wave == kNW - 2 && lane < 8) dma16_sbase(lsw + i0, lane * 16, st + 2 * TB + TBV);
+    if (wave == kNW - 1 && lane < 8) dma16_sbase(dw + i0, lane * 16, st + 2 * TB + TBV + 128);
+  };
+  issue(0, 0);
+
+  // row reads of the 2d-wide dA tile: chunk (2ks + hg) ^ (li & 15) of a row,
+  // so k-step ks + 8 reads 256 bytes after k-step ks (an immediate offset)
+  static_assert(DV == 128 || DV == 256, "dA row reads");
+  uint32_t rb[KS], rbv[8];
+  row_read_bases<D>(li, hg, rb);
+  row_read_bases<128>(li, hg, rbv);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rbv[i] += li * (DV * 2 - 256);  // row stride DV*2 bytes
+  TrBases<D> tb;
+  tb.init(lane);
+  const float sl2 = a.sl2;
+  f32x16 acc[CB];  // dK^T [c][key]
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+
+  for (int it = 0; it < nit; ++it) {
+    const int stage = it & 1;
+    wait_copies();
+    __syncthreads();  // tile it visible; the other stage is free
+    if (it + 1 < nit) issue(it + 1, stage ^ 1);
+    const int i0 = it_row0(it);
+    if (!active || i0 < j0w) continue;  // rows before this wave's keys
+    const bool diag = i0 == j0w;
+    const uint32_t st = lds0 + stage * STAGE;
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s = mfma32x32x16(lds_read16(st + rb[ks]), kf[ks], s);  // S = Q K^T
+#pragma unroll
+    for (int ks = 0; ks < KSV; ++ks)
+      dp = mfma32x32x16(lds_read16(st + 2 * TB + rbv[ks & 7] + (ks >> 3) * 256), vf[ks], dp);  // dP = dA V^T
+    // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
+    f32x8 e0, e1;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(st + 2 * TB + TBV + (8 * q4 + 4 * hg) * 4);
+      const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(st + 2 * TB + TBV + 128 + (8 * q4 + 4 * hg) * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * q4 + j;
+        const int rw = i0 + 8 * q4 + 4 * hg + j;
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[j]));
+        if (rw >= T || (diag && li > rw - i0)) pr = 0.f;
+        const float x = pr * (dp[r] - d4[j]);
+        if (r < 8) e0[r] = x; else e1[r - 8] = x;
+      }
+    }
+    const bf16x8 xk[2] = {cvt_bf16x8(e0), cvt_bf16x8(e1)};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) acc[cb] = mfma32x32x16(tb.read(st + TB, kk, cb), xk[kk], acc[cb]);
+  }
+  if (!active || key >= T) return;
+  const TOut& o = a.dk[m];
+  uint16_t* dst = (uint16_t*)o.p + b * o.sb + (int64_t)key * o.st + h * o.sh;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      uint2 w;
+      w.x = pack_bf16x2(acc[cb][4 * g4 + 0] * a.scale, acc[cb][4 * g4 + 1] * a.scale);
+      w.y = pack_bf16x2(acc[cb][4 * g4 + 2] * a.scale, acc[cb][4 * g4 + 3] * a.scale);
+      *(uint2*)(dst + 32 * cb + 8 * g4 + 4 * hg) = w;
+    }
+}
+
+// dV over both maps: workgroup (b, h, 32 kNW keys), wave w owns keys
+// J0 + 32 w; iterations (row tile, map), rows descending, map 1 then map 2
+// of each tile (the stage index is the map).  S_m = Q_m K_m^T with K_1 / K_2
+// fragments of its keys in registers, dV^T += dA_m^T P_m with transpose
+// reads of the dA_m tile.
+template <int D>
+__global__ void __launch_bounds__(kNW * 64, 2) bwd_v1_dv_kernel(const V1BwdArgs a) {
+  constexpr int DV = 2 * D;
+  constexpr int KS = D / 16, CBV = DV / 32;
+  using Dma = TileDma<D>;
+  using DmaV = TileDma<DV>;
+  constexpr int TB = Dma::BYTES, TBV = DmaV::BYTES;
+  constexpr int STAGE = TB + TBV + 128;  // [Q_m "k" | dA_m "v" | lse of the 32 rows]
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int li = lane & 31, hg = lane >> 5;
+  const int T = a.T, BK = 32 * kNW;
+  const int units = a.B * a.H;
+  const int unit = blockIdx.x % units, kt = blockIdx.x / units;  // low key tiles (most rows) first
+  const int b = unit / a.H, h = unit % a.H;
+  const int J0 = kt * BK, j0w = J0 + 32 * wave;
+  const bool active = j0w < T;
+  const int key = j0w + li;
+  const int nrt = (T + kBT - 1) / kBT;
+  const int rt0 = J0 / kBT;
+  const int nit = 2 * (nrt - rt0);  // (row tile, map); even
+  auto it_row0 = [&](int it) { return (nrt - 1 - (it >> 1)) * kBT; };
+
+  bf16x8 kf[2][KS];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const uint16_t* kr = (const uint16_t*)a.k[m].p + b * a.k[m].sb + (int64_t)key * a.k[m].st + h * a.k[m].sh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[m][ks] = as_bf16x8(key < T ? *(const uint4*)(kr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) retire(kf[m][ks]);
+  auto issue = [&](int it) {  // stage = map = it & 1
+    const int m = it & 1, i0 = it_row0(it);
+    const uint16_t* qp = (const uint16_t*)a.q[m].p + b * a.q[m].sb + h * a.q[m].sh;
+    const uint16_t* ap = a.dA[m] + ((int64_t)b * T * a.H + h) * DV;
+    const uint32_t st = lds0 + m * STAGE;
+    Dma::issue(qp, a.q[m].st, i0, T, false, st, wave, lane);
+    DmaV::issue(ap, (int64_t)a.H * DV, i0, T, true, st + TB, wave, lane);
+    if (wave == kNW - 1 && lane < 8)
+      dma16_sbase(a.lsew[m] + ((int64_t)b * a.H + h) * a.Tp + i0, lane * 16, st + TB + TBV);
+  };
+  issue(0);
+
+  uint32_t rb[KS];
+  row_read_bases<D>(li, hg, rb);
+  TrBases<DV> tb;
+  tb.init(lane);
+  const float sl2 = a.sl2;
+  f32x16 acc[CBV];  // dV^T [c][key]
+#pragma unroll
+  for (int cb = 0; cb < CBV; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+
+  auto tile_step = [&](int it, auto mc) {
+    constexpr int M = decltype(mc)::value;
+    wait_copies();
+    __syncthreads();  // tile it visible; the other stage is free
+    if (it + 1 < nit) issue(it + 1);
+    const int i0 = it_row0(it);
+    if (!active || i0 < j0w) return;  // rows before this wave's keys
+    const bool diag = i0 == j0w;
+    const uint32_t st = lds0 + M * STAGE;
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s = mfma32x32x16(lds_read16(st + rb[ks]), kf[M][ks], s);  // S = Q K^T
+    f32x8 e0, e1;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(st + TB + TBV + (8 * q4 + 4 * hg) * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * q4 + j;
+        const int rw = i0 + 8 * q4 + 4 * hg + j;
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[j]));
+        if (rw >= T || (diag && li > rw - i0)) pr = 0.f;
+        if (r < 8) e0[r] = pr; else e1[r - 8] = pr;
+      }
+    }
+    const bf16x8 xk[2] = {cvt_bf16x8(e0), cvt_bf16x8(e1)};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int cb = 0; cb < CBV; ++cb) acc[cb] = mfma32x32x16(tb.read(st + TB, kk, cb), xk[kk], acc[cb]);
+  };
+  for (int it = 0; it < nit; it += 2) {
+    tile_step(it, std::integral_constant<int, 0>{});
+    tile_step(it + 1, std::integral_constant<int, 1>{});
+  }
+  if (!active || key >= T) return;
+  uint16_t* dst = (uint16_t*)a.dv.p + b * a.dv.sb + (int64_t)key * a.dv.st + h * a.dv.sh;
+#pragma unroll
+  for (int cb = 0; cb < CBV; ++cb)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      uint2 w;
+      w.x = pack_bf16x2(acc[cb][4 * g4 + 0], acc[cb][4 * g4 + 1]);
+      w.y = pack_bf16x2(acc[cb][4 * g4 + 2], acc[cb][4 * g4 + 3]);
+      *(uint2*)(dst + 32 * cb + 8 * g4 + 4 * hg) = w;
+    }
+}
+
+template <int D>
+hipError_t launch_v1(const V1BwdArgs& a, hipStream_t st) {
+  const void* args[] = {&a};
+  const long long items = (long long)a.B * a.Tp * a.H;
+  hipError_t e = hipLaunchKernel((const void*)bwd_v1_pre_kernel<D>, dim3((unsigned)((items + 3) / 4)), dim3(256),
+                                 (void**)args, 0, st);
+  if (e != hipSuccess) return e;
+  e = hipLaunchKernel((const void*)bwd_v1_lam_kernel<D>, dim3(1), dim3(256), (void**)args, 0, st);
+  if (e != hipSuccess) return e;
+  const int qt = (a.T + 32 * kNW - 1) / (32 * kNW);
+  for (int m = 0; m < 2; ++m) {  // dQ of each map: the dQ kernel with one head per kv head
+    BwdArgs q{};
+    q.q = a.q[m], q.k = a.k[m], q.v = a.v;
+    q.dq = a.dq[m];
+    q.dA = a.dA[m];
+    q.Dw = a.Dw[m];
+    q.lsew = a.lsew[m];
+    q.sl2 = a.sl2, q.scale = a.scale;
+    q.B = a.B, q.T = a.T, q.Hq = a.H, q.Hkv = a.H, q.G = 1, q.Tp = a.Tp;
+    const void* qa[] = {&q};
+    e = hipLaunchKernel((const void*)bwd_dq_kernel<D, 2 * D>, dim3(a.B * a.H * qt), dim3(kNW * 64), (void**)qa, 0,
+                        st);
+    if (e != hipSuccess) return e;
+  }
+  e = hipLaunchKernel((const void*)bwd_v1_dk_kernel<D>, dim3(a.B * a.H * 2 * qt), dim3(kNW * 64), (void**)args, 0,
+                      st);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel((const void*)bwd_v1_dv_kernel<D>, dim3(a.B * a.H * qt), dim3(kNW * 64), (void**)args, 0,
+                         st);
 }
 
 }  // namespace
@@ -454,6 +861,12 @@ int backward_padded_rows(int T) { return (T + 127) / 128 * 128; }
 hipError_t launch_backward_v2_bf16(int d, const BwdArgs& a, hipStream_t s) {
   if (d == 64) return launch<64>(a, s);
   if (d == 128) return launch<128>(a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_backward_v1_bf16(int d, const V1BwdArgs& a, hipStream_t s) {
+  if (d == 64) return launch_v1<64>(a, s);
+  if (d == 128) return launch_v1<128>(a, s);
   return hipErrorInvalidValue;
 }
 

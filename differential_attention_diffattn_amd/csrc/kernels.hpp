@@ -31,10 +31,12 @@ struct PrefillArgs {
   int tiles;       // token tiles per unit
   int nwg;         // workgroups in the grid
   int softmax1;    // 1: off-by-one softmax (each map's denominator + exp(0))
-  // V2 training forward (lse non-null): each head's normalised output
-  // attn [B,T,Hq,d] (roles b, head, t) and the log2 of each row's softmax
-  // denominator of the log2(e)/sqrt(d)-scaled scores, lse [B][Hq][T].
-  TOut attn;
+  // Training forward (lse non-null): the log2 of each row's softmax
+  // denominator of the log2(e)/sqrt(d)-scaled scores and the normalised
+  // attention outputs.  V2: each head's output attn [B,T,Hq,d] (roles b,
+  // head, t), lse [B][Hq][T].  V1: map 1's output in attn and map 2's in
+  // attn2, both [B,T,H,2d] (roles b, differential head, t), lse [2][B][H][T].
+  TOut attn, attn2;
   float* lse;
 };
 
@@ -75,6 +77,24 @@ struct BwdArgs {
 };
 int backward_padded_rows(int T);
 hipError_t launch_backward_v2_bf16(int d, const BwdArgs& a, hipStream_t s);
+
+// DIFF V1 backward (map m = 0, 1 for the pages' maps 1, 2; dv = 2d).
+struct V1BwdArgs {
+  TIn q[2], k[2], v;  // [B,H,T,d] / v [B,H,T,2d] bf16 (roles b, differential head, t)
+  TIn a[2];           // training forward's map outputs [B,T,H,2d] bf16
+  TIn dout;           // [B,T,H,2d] bf16
+  const float* lse;   // [2][B][H][T] (training forward)
+  const float *lq1, *lk1, *lq2, *lk2;  // lambda vectors [d]
+  TOut dq[2], dk[2], dv;               // bf16, layouts of q / k / v
+  float *dlq1, *dlk1, *dlq2, *dlk2;    // [d] fp32
+  uint16_t* dA[2];    // workspace [B][T][H][2d] bf16: d a_m
+  float* Dw[2];       // workspace [B][H][Tp]: rowsum(d a_m * a_m)
+  float* lsew[2];     // workspace [B][H][Tp]: lse of map m, padded with zeros
+  float* lamrow;      // workspace [B][T][H]: each row's term of d lambda
+  float lam_init, sl2, scale;
+  int B, T, H, Tp;
+};
+hipError_t launch_backward_v1_bf16(int d, const V1BwdArgs& a, hipStream_t s);
 
 // Split-K decode over a KV cache, then a deterministic merge.
 struct DecodeArgs {

@@ -659,25 +659,29 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
     const float extra = a.softmax1 ? __builtin_amdgcn_exp2f(nm[m]) : 0.f;
     inv[m] = 1.f / (lsum[m] + __shfl_xor(lsum[m], 32, 64) + extra);
   }
-  // V2 training forward: this wave's head output (normalised) and the row's
-  // log2-sum-exp2, lse = m + log2(denominator) = -nm - log2(inv)
-  if constexpr (V2) {
-    if (a.lse != nullptr && active && row < T) {
+  // Training forward: this wave's map (V1) / head (V2) output, normalised,
+  // and the row's log2-sum-exp2, lse = m + log2(denominator) = -nm - log2(inv).
+  // V1: map outputs in attn (map 1) and attn2 (map 2), lse [2][B][H][T];
+  // V2: head outputs in attn, lse [B][Hq][T].
+  if (a.lse != nullptr && active && row < T) {
 #pragma unroll
-      for (int m = 0; m < MPW; ++m) {
-        const int head = 2 * pair + m0 + m;
-        if (hg == 0) a.lse[((int64_t)b * (a.H * a.G) + head) * T + row] = -nm[m] - log2f(inv[m]);
-        uint16_t* ad = (uint16_t*)a.attn.p + b * a.attn.sb + (int64_t)row * a.attn.st + (int64_t)head * a.attn.sh;
+    for (int m = 0; m < MPW; ++m) {
+      const int mi = m0 + m;
+      const int head = V2 ? 2 * pair + mi : h;
+      const int64_t li_ = V2 ? ((int64_t)b * (a.H * a.G) + head) * T + row
+                             : (((int64_t)mi * a.B + b) * a.H + h) * T + row;
+      if (hg == 0) a.lse[li_] = -nm[m] - log2f(inv[m]);
+      const TOut& at = (!V2 && mi == 1) ? a.attn2 : a.attn;
+      uint16_t* ad = (uint16_t*)at.p + b * at.sb + (int64_t)row * at.st + (int64_t)head * at.sh;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            uint2 w;
-            w.x = pack_bf16x2(o[m][cb][4 * g4 + 0] * inv[m], o[m][cb][4 * g4 + 1] * inv[m]);
-            w.y = pack_bf16x2(o[m][cb][4 * g4 + 2] * inv[m], o[m][cb][4 * g4 + 3] * inv[m]);
-            *(uint2*)(ad + 32 * cb + 8 * g4 + 4 * hg) = w;
-          }
-      }
+        for (int g4 = 0; g4 < 4; ++g4) {
+          uint2 w;
+          w.x = pack_bf16x2(o[m][cb][4 * g4 + 0] * inv[m], o[m][cb][4 * g4 + 1] * inv[m]);
+          w.y = pack_bf16x2(o[m][cb][4 * g4 + 2] * inv[m], o[m][cb][4 * g4 + 3] * inv[m]);
+          *(uint2*)(ad + 32 * cb + 8 * g4 + 4 * hg) = w;
+        }
     }
   }
   // weight of the second map: lam / l2 (V1) or sigmoid(lam[t, p]) / l_odd (V2)

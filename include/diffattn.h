@@ -339,6 +339,73 @@ da_status diffattn_v2_bwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d,
                           const float* lse, da_in dout, da_out dq, da_out dk, da_out dv,
                           da_out dlam, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * DIFF V1 training forward: diffattn_v1_fwd (or its off-by-one softmax
+ * variant) that also keeps what diffattn_v1_bwd needs.
+ *   attn1, attn2  logical [B,T,H,2d] bf16 (roles b, h = differential head,
+ *          t): each map's attention output softmax(q_m k_m^T / sqrt d) v,
+ *          normalised, rounded once to bf16 (the two flash-attention outputs
+ *          that "Differential Transformer V2" article's DiffAttnV1 pseudo-code
+ *          combines).
+ *   lse    DEVICE fp32 [2][B][H][T], contiguous: for map m (0: q1/k1,
+ *          1: q2/k2) and each row, log2 of the softmax denominator of the
+ *          scores scaled by log2(e)/sqrt(d) (with the off-by-one softmax the
+ *          denominator holds its extra term).
+ * Other arguments, layouts and errors as for diffattn_v1_fwd; bf16 only
+ * (DA_E_UNSUPPORTED for fp32); DA_E_NULL for a NULL lse, DA_E_LAYOUT for a
+ * misaligned one.
+ */
+da_status diffattn_v1_fwd_train(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+                                da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
+                                const float* lam_k2, int layer_index, da_out out, da_out attn1, da_out attn2,
+                                float* lse, void* stream);
+da_status diffattn_v1_fwd_train_softmax1(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2,
+                                         da_in k1, da_in k2, da_in v, const float* lam_q1, const float* lam_k1,
+                                         const float* lam_q2, const float* lam_k2, int layer_index, da_out out,
+                                         da_out attn1, da_out attn2, float* lse, void* stream);
+
+/*
+ * Bytes of device workspace diffattn_v1_bwd needs (0 if the sizes are
+ * invalid): d a_m of both maps in bf16, four fp32 arrays of B*H rows padded
+ * to a multiple of 128 tokens, and one fp32 value per (b, t, h).
+ */
+size_t diffattn_v1_bwd_workspace_bytes(int B, int H, int T, int d);
+
+/*
+ * DIFF V1 backward ("Differential Transformer V2" article, DiffAttnV1
+ * pseudo-code, with the RMSNorm of Wilsontomass's module in the nanoGPT
+ * issue "How best to implement a differential transformer?",
+ * differentiated): given dout = dL/dout, the gradients of the forward's
+ * inputs from the training forward's attn1, attn2 and lse.  With
+ * D = a_1 - lam a_2 and r = (mean D^2 + 1e-5)^(-1/2) per (token, head):
+ *   dD = (1 - lam_init) r (dout - r^2 D mean(dout D)),
+ *   d a_1 = dD,  d a_2 = -lam dD,  dlam = -sum over (b, t, h) of <dD, a_2>,
+ *   per map the softmax-attention gradients dq_m, dk_m and dv (dv summed
+ *   over both maps), and the lambda vectors' gradients
+ *   dlam_q1 = dlam e1 lam_k1, dlam_k1 = dlam e1 lam_q1,
+ *   dlam_q2 = -dlam e2 lam_k2, dlam_k2 = -dlam e2 lam_q2,
+ *   e1 = exp(<lam_q1, lam_k1>), e2 = exp(<lam_q2, lam_k2>).
+ *   dtype      DA_BF16 only; d in {64, 128}.
+ *   q1 .. v, lam vectors, layer_index   the forward's inputs (layouts as for
+ *              diffattn_v1_fwd).
+ *   attn1, attn2, lse   the training forward's outputs for the same inputs.
+ *   dout       logical [B,T,H,2d] bf16.
+ *   dq1, dq2, dk1, dk2  logical [B,H,T,d] bf16;  dv  logical [B,H,T,2d] bf16.
+ *   dlam_q1 .. dlam_k2  DEVICE fp32 [d] each.
+ *   workspace  at least diffattn_v1_bwd_workspace_bytes(B,H,T,d) bytes,
+ *              256-byte aligned, owned by the caller.
+ * Seven kernels are enqueued on `stream` (a pre-pass, the dlam reduction,
+ * dq of each map, dk of both maps, dv); every sum is taken in a fixed order
+ * (deterministic).  Token strides of q1 .. v must be below 2^24 elements
+ * (DA_E_UNSUPPORTED).
+ */
+da_status diffattn_v1_bwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+                          da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
+                          const float* lam_k2, int layer_index, da_in attn1, da_in attn2, const float* lse,
+                          da_in dout, da_out dq1, da_out dq2, da_out dk1, da_out dk2, da_out dv, float* dlam_q1,
+                          float* dlam_k1, float* dlam_q2, float* dlam_k2, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* lambda_init = 0.8 - 0.6*exp(-0.3*layer_index), as the V1 kernels use it
  * (computed on the host in double, handed to the device as float). */
 double diffattn_lambda_init(int layer_index);

@@ -203,3 +203,78 @@ def test_multi_decode_workspace_and_validation(lib):
     for kw in ({"nq": 0}, {"ws": 0}, {"dtype": 0}):
         assert _multi(lib, lib.diffattn_v2_decode_multi_softmax1, **kw) == _multi(lib, **kw) != OK
 
+
+
+# ----- training forward and backward ---------------------------------------------
+
+def test_training_entry_points_are_declared():
+    syms = _declared_symbols()
+    for need in ("diffattn_v1_fwd_train", "diffattn_v1_fwd_train_softmax1", "diffattn_v1_bwd",
+                 "diffattn_v1_bwd_workspace_bytes", "diffattn_v2_fwd_train", "diffattn_v2_fwd_train_softmax1",
+                 "diffattn_v2_bwd", "diffattn_v2_bwd_workspace_bytes"):
+        assert need in syms
+
+
+def _v1_train(lib, fn=None, dtype=1, d=64, attn2=None, lse=FAKE):
+    fn = fn or lib.diffattn_v1_fwd_train
+    return fn(dtype, 1, 2, 16, d, _t(), _t(), _t(), _t(), _t(), FAKE, FAKE, FAKE, FAKE, 0, _t(out=True),
+              _t(out=True), attn2 or _t(out=True), lse, None)
+
+
+def test_v1_fwd_train_validation(lib):
+    for fn in (lib.diffattn_v1_fwd_train, lib.diffattn_v1_fwd_train_softmax1):
+        assert _v1_train(lib, fn, lse=0) == E_NULL
+        assert _v1_train(lib, fn, lse=FAKE + 2) == E_LAYOUT
+        assert _v1_train(lib, fn, attn2=_t(ptr=0, out=True)) == E_NULL
+        assert _v1_train(lib, fn, attn2=_t(st=68, out=True)) == E_LAYOUT
+        assert _v1_train(lib, fn, dtype=0, d=64) == E_UNSUP    # the training forward is bf16 only
+        assert _v1_train(lib, fn, d=96) == E_UNSUP
+
+
+def test_v1_bwd_workspace_query(lib):
+    B, H, T, d = 8, 6, 1024, 64
+    Tp = 1024
+    want = 2 * B * T * H * 2 * d * 2 + 4 * B * H * Tp * 4 + B * T * H * 4
+    assert lib.diffattn_v1_bwd_workspace_bytes(B, H, T, d) == want
+    # padded rows and 256-byte aligned regions
+    # B=H=1, T=3, d=64: d a 3*128*2 = 768 B per map, rows padded to 128 (512 B each), 12 B of row terms -> 256
+    assert lib.diffattn_v1_bwd_workspace_bytes(1, 1, 3, 64) == 2 * 768 + 4 * 512 + 256
+    assert lib.diffattn_v1_bwd_workspace_bytes(0, 1, 3, 64) == 0
+
+
+def _v1_bwd(lib, dtype=1, B=1, H=2, T=16, d=64, ws=FAKE, wsb=1 << 30, lse=FAKE, dl=FAKE, q1=None, dv=None):
+    return lib.diffattn_v1_bwd(dtype, B, H, T, d, q1 or _t(), _t(), _t(), _t(), _t(), FAKE, FAKE, FAKE, FAKE, 0,
+                               _t(), _t(), lse, _t(), _t(out=True), _t(out=True), _t(out=True), _t(out=True),
+                               dv or _t(out=True), dl, FAKE, FAKE, FAKE, ws, wsb, None)
+
+
+def test_v1_bwd_validation(lib):
+    assert _v1_bwd(lib, dtype=5) == E_DTYPE
+    assert _v1_bwd(lib, T=0) == E_SHAPE
+    assert _v1_bwd(lib, q1=_t(ptr=0)) == E_NULL
+    assert _v1_bwd(lib, lse=0) == E_NULL
+    assert _v1_bwd(lib, dl=0) == E_NULL
+    assert _v1_bwd(lib, dl=FAKE + 2) == E_LAYOUT
+    assert _v1_bwd(lib, dv=_t(st=68, out=True)) == E_LAYOUT
+    assert _v1_bwd(lib, dtype=0) == E_UNSUP                   # bf16 only
+    assert _v1_bwd(lib, d=32) == E_UNSUP
+    assert _v1_bwd(lib, ws=0) == E_WS
+    assert _v1_bwd(lib, ws=FAKE + 16) == E_WS                 # 256-byte alignment
+    assert _v1_bwd(lib, wsb=lib.diffattn_v1_bwd_workspace_bytes(1, 2, 16, 64) - 1) == E_WS
+
+
+def _v2_bwd(lib, dtype=1, Hq=8, Hkv=2, d=128, ws=FAKE, wsb=1 << 30, lse=FAKE):
+    return lib.diffattn_v2_bwd(dtype, 1, 16, Hq, Hkv, d, _t(), _t(), _t(), _t(), _t(), lse, _t(), _t(out=True),
+                               _t(out=True), _t(out=True), _t(out=True), ws, wsb, None)
+
+
+def test_v2_training_validation(lib):
+    assert lib.diffattn_v2_bwd_workspace_bytes(1, 8192, 64, 8, 128) == 8192 * 64 * 128 * 2 + 2 * 64 * 8192 * 4
+    assert lib.diffattn_v2_bwd_workspace_bytes(1, 16, 6, 2, 128) == 0   # odd group
+    assert _v2_bwd(lib, Hq=6) == E_SHAPE
+    assert _v2_bwd(lib, lse=0) == E_NULL
+    assert _v2_bwd(lib, dtype=0) == E_UNSUP
+    assert _v2_bwd(lib, ws=0) == E_WS
+    assert _v2_bwd(lib, wsb=100) == E_WS
+    for fn in (lib.diffattn_v2_fwd_train, lib.diffattn_v2_fwd_train_softmax1):
+        assert fn(1, 1, 16, 8, 2, 128, _t(), _t(), _t(), _t(), _t(out=True), _t(out=True), 0, None) == E_NULL

@@ -145,3 +145,126 @@ def test_backward_full_size_properties():
         assert np.abs(got_out - ra).max() < 3e-2
     del y, dq, dk, dv, attn
     torch.cuda.empty_cache()
+
+
+# ==== DIFF V1 =======================================================================
+#
+# Tolerance.  Besides the roundings the V2 path has (P, dS and d a_m held in
+# bf16), the V1 backward rebuilds D = a_1 - lam a_2 from the training
+# forward's bf16 map outputs, and the RMSNorm's backward scales that rounding
+# by r = 1/rms(D).  oracle.backward.v1_bwd_rounding_bounds follows every
+# rounded value through the same steps; summed as independent roundings
+# (root of the sum of squares, the typical size) it is ~1% of a typical
+# gradient element.  Each element must satisfy |x - ref| <= 2e-2 |ref| +
+# 8 b + 1e-4.
+
+V1_GRADS = ("dq1", "dq2", "dk1", "dk2", "dv", "dlq1", "dlk1", "dlq2", "dlk2")
+
+
+def _v1_in(B, H, T, d, seed):
+    x = workloads.v1_inputs(B, H, T, d, torch.bfloat16, seed=seed, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(seed + 99)
+    dout = torch.randn((B, T, H, 2 * d), generator=g, device=DEV).to(torch.bfloat16)
+    args = [x[k] for k in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")]
+    return args, dout
+
+
+def _v1_check(grads, args, layer, dout, what, softmax1=False):
+    cpu = [a.cpu() for a in args]
+    ref = ob.v1_bwd(*cpu, layer, dout.cpu(), softmax1=softmax1)
+    bnd = ob.v1_bwd_rounding_bounds(*cpu, layer, dout.cpu(), softmax1=softmax1)
+    for name, got, r, b in zip(V1_GRADS, grads, ref, bnd):
+        g = host64(got)
+        assert g.shape == r.shape, (name, g.shape, r.shape)
+        assert np.all(np.isfinite(g)), f"{name} {what}: non-finite"
+        excess = np.abs(g - r) - (2e-2 * np.abs(r) + 8.0 * b + 1e-4)
+        worst = np.unravel_index(np.argmax(excess), excess.shape)
+        assert excess.max() <= 0, (f"{name} {what}: element {worst} got {g[worst]:.5f} ref {r[worst]:.5f} "
+                                   f"(excess {excess.max():.3e}, bound {b[worst]:.3e})")
+
+
+@pytest.mark.parametrize("s1", [False, True])
+@pytest.mark.parametrize("T,d", [(1, 64), (33, 128), (300, 64), (200, 128)])
+def test_v1_fwd_train(T, d, s1):
+    """out is the inference forward's, bit for bit; attn1, attn2 and lse match the oracle."""
+    args, _ = _v1_in(2, 2, T, d, seed=1000 + T + d)
+    layer = 4
+    out, a1, a2, lse = binding.v1_fwd_train(*args, layer, softmax1=s1)
+    inf = binding.v1_fwd(*args, layer, softmax1=s1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, inf)
+    r_out, r_a1, r_a2, r_lse = ob.v1_fwd_train(*[a.cpu() for a in args], layer, softmax1=s1)
+    assert_bf16_close(a1, r_a1, f"attn1 T{T} d{d}")
+    assert_bf16_close(a2, r_a2, f"attn2 T{T} d{d}")
+    assert np.abs(host64(lse) - r_lse).max() < 1e-2
+
+
+@pytest.mark.parametrize("T", [1, 31, 33, 100, 300])
+@pytest.mark.parametrize("d,layer", [(64, 0), (128, 14), (64, 11)])
+def test_v1_backward(T, d, layer):
+    B = 2 if T < 200 else 1
+    args, dout = _v1_in(B, 2, T, d, seed=1100 + T + d + layer)
+    _, a1, a2, lse = binding.v1_fwd_train(*args, layer)
+    grads = binding.v1_bwd(*args, layer, a1, a2, lse, dout)
+    torch.cuda.synchronize()
+    _v1_check(grads, args, layer, dout, f"T{T} d{d} layer{layer}")
+
+
+def test_v1_backward_softmax1():
+    args, dout = _v1_in(1, 2, 150, 64, seed=1200)
+    _, a1, a2, lse = binding.v1_fwd_train(*args, 2, softmax1=True)
+    grads = binding.v1_bwd(*args, 2, a1, a2, lse, dout)
+    torch.cuda.synchronize()
+    _v1_check(grads, args, 2, dout, "softmax1", softmax1=True)
+
+
+def test_v1_backward_deterministic_and_strided():
+    """Two runs give identical bits; q/k/v given as [B,T,H,d] storage (strided
+    [B,H,T,d] views) give the same gradients as contiguous inputs."""
+    args, dout = _v1_in(2, 3, 160, 64, seed=1300)
+    _, a1, a2, lse = binding.v1_fwd_train(*args, 1)
+    g1 = binding.v1_bwd(*args, 1, a1, a2, lse, dout)
+    g2 = binding.v1_bwd(*args, 1, a1, a2, lse, dout)
+    tr = lambda x: x.transpose(1, 2).contiguous().transpose(1, 2)
+    g3 = binding.v1_bwd(*[tr(a) for a in args[:5]], *args[5:], 1, a1, a2, lse, dout)
+    torch.cuda.synchronize()
+    for a, b, c in zip(g1, g2, g3):
+        assert torch.equal(a, b)
+        assert torch.equal(a, c)
+
+
+def test_v1_backward_headline_shape():
+    """The GPT-2-small V1 shape (B 8, 6 differential heads, T 1024, d 64),
+    every gradient element against the oracle."""
+    w = workloads.WORKLOADS["v1_gpt2small_B8_H6_T1024_d64"]
+    x = workloads.inputs_for(w, DEV)
+    args = [x[k] for k in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")]
+    g = torch.Generator(device=DEV).manual_seed(5555)
+    dout = torch.randn((w.B, w.T, w.H, 2 * w.d), generator=g, device=DEV).to(torch.bfloat16)
+    _, a1, a2, lse = binding.v1_fwd_train(*args, 6)
+    grads = binding.v1_bwd(*args, 6, a1, a2, lse, dout)
+    torch.cuda.synchronize()
+    _v1_check(grads, args, 6, dout, "headline shape")
+
+
+def test_v1_backward_3b_shape_sampled_heads():
+    """The 3B-class V1 shape (B 2, 12 differential heads, T 4096, d 128):
+    dq, dk, dv of two (b, h) heads against the oracle run on those heads
+    alone (each head's gradients depend only on its own inputs and lambda)."""
+    w = workloads.WORKLOADS["v1_3b_B2_H12_T4096_d128"]
+    x = workloads.inputs_for(w, DEV)
+    args = [x[k] for k in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")]
+    g = torch.Generator(device=DEV).manual_seed(5556)
+    dout = torch.randn((w.B, w.T, w.H, 2 * w.d), generator=g, device=DEV).to(torch.bfloat16)
+    _, a1, a2, lse = binding.v1_fwd_train(*args, 14)
+    grads = binding.v1_bwd(*args, 14, a1, a2, lse, dout)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 11)):
+        sub = [a[b:b + 1, h:h + 1].cpu() for a in args[:5]] + [a.cpu() for a in args[5:]]
+        dsub = dout[b:b + 1, :, h:h + 1].cpu()
+        ref = ob.v1_bwd(*sub, 14, dsub)
+        bnd = ob.v1_bwd_rounding_bounds(*sub, 14, dsub)
+        for name, got, r, bd in list(zip(V1_GRADS, grads, ref, bnd))[:5]:
+            gg = host64(got[b:b + 1, h:h + 1])
+            excess = np.abs(gg - r) - (2e-2 * np.abs(r) + 8.0 * bd + 1e-4)
+            assert excess.max() <= 0, (name, b, h, excess.max())
