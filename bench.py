@@ -16,7 +16,9 @@ The JSON line also carries:
   cpu_baseline  the fp64 oracle timed on a bounded sample of the same
                 workload on this host's cores;
   secondary     the other full-size workloads (3B-class V1, V2 GQA prefill,
-                V2 decode, V2 decode of a ragged batch over a paged cache, V2
+                the V1 backward at the GPT-2-small and 3B shapes and the V2
+                backward (each timed without its training forward), V2
+                decode, V2 decode of a ragged batch over a paged cache, V2
                 decode of 4 new tokens per sequence),
                 each with its own roofline; a secondary step is
                 8 launches of the workload (warm-up ~0.3 s of its own calls).
@@ -38,8 +40,10 @@ METRIC = "diff-attn causal fwd TFLOP/s (bf16, % MFMA peak); V2 decode HBM GB/s (
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 HEADLINE = "v1_gpt2small_B8_H6_T1024_d64"
-SECONDARY = ["v1_3b_B2_H12_T4096_d128", "v2_prefill_B1_T8192_Hq64_Hkv8_d128", "v2_backward_B1_T8192_Hq64_Hkv8_d128", "v2_decode_B64_L32768_Hq64_Hkv8_d128",
-             "v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128", "v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128"]
+SECONDARY = ["v1_3b_B2_H12_T4096_d128", "v2_prefill_B1_T8192_Hq64_Hkv8_d128", "v1_backward_B8_H6_T1024_d64",
+             "v1_backward_B2_H12_T4096_d128", "v2_backward_B1_T8192_Hq64_Hkv8_d128",
+             "v2_decode_B64_L32768_Hq64_Hkv8_d128", "v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128",
+             "v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128"]
 
 
 def log(*a):
@@ -56,6 +60,13 @@ def _caller(w, x, binding, torch, softmax1=False):
     if w.kind == "v2":
         out = torch.empty((w.B, w.T, w.Hq // 2, w.d), dtype=w.torch_dtype, device=x["v"].device)
         return lambda layer: binding.v2_fwd(x["q"], x["k"], x["v"], x["lam"], out=out, softmax1=softmax1)
+    if w.kind == "v1_bwd":  # the timed call is the backward; the training forward runs once, untimed
+        args = [x[n] for n in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")]
+        layer0 = w.layers[0]
+        _, a1, a2, lse = binding.v1_fwd_train(*args, layer0, softmax1=softmax1)
+        grads = [torch.empty_like(x[n]) for n in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")]
+        ws = torch.empty(binding.v1_bwd_workspace_bytes(w.B, w.H, w.T, w.d), dtype=torch.uint8, device=x["v"].device)
+        return lambda layer: binding.v1_bwd(*args, layer, a1, a2, lse, x["dout"], grads=grads, workspace=ws)
     if w.kind == "v2_bwd":  # the timed call is the backward; the training forward runs once, untimed
         _, attn, lse = binding.v2_fwd_train(x["q"], x["k"], x["v"], x["lam"], softmax1=softmax1)
         grads = [torch.empty_like(x[n]) for n in ("q", "k", "v", "lam")]
@@ -175,7 +186,8 @@ def _source_sha(kind):
     from hardware counters only applies to the kernel it was measured on."""
     import hashlib
 
-    src = {"v1": "prefill_bf16.hip", "v2": "prefill_bf16.hip", "v2_bwd": "backward_bf16.hip", "decode": "decode_bf16.hip",
+    src = {"v1": "prefill_bf16.hip", "v2": "prefill_bf16.hip", "v1_bwd": "backward_bf16.hip",
+           "v2_bwd": "backward_bf16.hip", "decode": "decode_bf16.hip",
            "decode_paged": "decode_bf16.hip", "decode_multi": "decode_bf16.hip"}[kind]
     path = os.path.join(ROOT, "differential_attention_diffattn_amd", "csrc", src)
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
@@ -215,6 +227,9 @@ def _copy_calibration(torch, steps):
             "GB_per_s": round(4 * n / ms / 1e6, 1)}
 
 
+V1_BWD_KERNELS = "bwd_v1_pre_kernel|bwd_v1_lam_kernel|bwd_dq_kernel*2|bwd_v1_dk_kernel|bwd_v1_dv_kernel"
+
+
 def write_traffic(pmc_dir):
     """Turn FETCH_SIZE / WRITE_SIZE counter runs into profiles/traffic.json.
 
@@ -228,15 +243,17 @@ def write_traffic(pmc_dir):
 
     def per_dispatch(work, counter, match):
         """Counter per call: mean over dispatches of each kernel matching one of
-        the `|`-separated names, summed over those kernels."""
+        the `|`-separated names (`name*n`: launched n times per call), summed
+        over those kernels."""
         f = os.path.join(pmc_dir, f"pmc_{work}_{counter}", "run_counter_collection.csv")
         total = 0.0
         for m in match.split("|"):
+            m, _, times = m.partition("*")
             acc = defaultdict(float)
             for r in csv.DictReader(open(f)):
                 if m in r["Kernel_Name"]:
                     acc[r["Dispatch_Id"]] += float(r["Counter_Value"])
-            total += sum(acc.values()) / len(acc)
+            total += sum(acc.values()) / len(acc) * int(times or 1)
         return total
 
     copy_bytes = 1 << 30
@@ -247,6 +264,7 @@ def write_traffic(pmc_dir):
     for name, match in [("v1_gpt2small_B8_H6_T1024_d64", "prefill_kernel"), ("v1_3b_B2_H12_T4096_d128", "prefill_kernel"),
                         ("v2_prefill_B1_T8192_Hq64_Hkv8_d128", "prefill_kernel"),
                         ("v2_backward_B1_T8192_Hq64_Hkv8_d128", "bwd_pre_kernel|bwd_dq_kernel|bwd_dkdv_kernel"),
+                        ("v1_backward_B8_H6_T1024_d64", V1_BWD_KERNELS), ("v1_backward_B2_H12_T4096_d128", V1_BWD_KERNELS),
                         ("v2_decode_B64_L32768_Hq64_Hkv8_d128", "decode_split_kernel"),
                         ("v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128", "decode_split_kernel"),
                         ("v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128", "decode_split_kernel")]:
@@ -359,6 +377,9 @@ def main():
         elif w.kind == "v2_bwd":
             res.update(metric="causal bwd TFLOP/s (5 products over unmasked pairs)", unit="TFLOP/s",
                        value=round(w.flops() / per_call_s / 1e12, 3))
+        elif w.kind == "v1_bwd":
+            res.update(metric="causal bwd TFLOP/s (5 products per map over unmasked pairs)", unit="TFLOP/s",
+                       value=round(w.flops() / per_call_s / 1e12, 3))
         else:
             res.update(metric="causal fwd TFLOP/s", unit="TFLOP/s", value=round(w.flops() / per_call_s / 1e12, 3))
         log(json.dumps(res))
@@ -379,7 +400,7 @@ def main():
             # warm-up sized to ~0.3 s of this workload's own calls, so the
             # GPU clock has settled under its load before the timed steps
             ws = workloads.WORKLOADS[name]
-            est_s = ws.flops() / 1e15 if ws.kind in ("v1", "v2", "v2_bwd") else ws.compulsory_bytes() / 5.5e12
+            est_s = ws.flops() / 1e15 if ws.kind in ("v1", "v2", "v1_bwd", "v2_bwd") else ws.compulsory_bytes() / 5.5e12
             # 8 launches per step: the events around a graph replay then time
             # the kernels, not the replay's launch
             _, xs, r = measure(name, max(10, args.steps), max(3, int(0.3 / (8 * est_s))), calls_per_step=8)

@@ -32,7 +32,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "v1", "v2", "v2_bwd", "decode", "decode_paged", "decode_multi"
+    kind: str  # "v1", "v2", "v1_bwd", "v2_bwd", "decode", "decode_paged", "decode_multi"
     dtype: str  # "fp32" or "bf16"
     B: int
     H: int = 0  # V1: differential heads
@@ -64,6 +64,8 @@ class Workload:
             return 2.0 * self.B * self.Hq * self.d * self.T * (self.T + 1)
         if self.kind == "v2_bwd":  # 5 products (S, dP, dV, dK, dQ) over the unmasked pairs
             return 5.0 * self.B * self.Hq * self.d * self.T * (self.T + 1)
+        if self.kind == "v1_bwd":  # per map S, dK, dQ over d and dP, dV over 2d: 14 d flops per pair and map
+            return 14.0 * self.B * self.H * self.d * self.T * (self.T + 1)
         if self.kind == "decode_paged":
             return 4.0 * self.Hq * self.d * int(self.seq_lens().sum())
         if self.kind == "decode_multi":  # new token i sees T - nq + i + 1 entries
@@ -80,6 +82,10 @@ class Workload:
         if self.kind == "v2":
             B, T, Hq, Hkv, d = self.B, self.T, self.Hq, self.Hkv, self.d
             return e * (B * T * Hq * d + 2 * B * T * Hkv * d + B * T * (Hq // 2) * d) + 4 * B * T * (Hq // 2)
+        if self.kind == "v1_bwd":  # q1 q2 k1 k2 v, attn1 attn2, dout, lse, 4 lambda vectors in; 5 grads + 4 out
+            B, H, T, d = self.B, self.H, self.T, self.d
+            return (e * (4 * B * H * T * d + B * H * T * 2 * d + 3 * B * T * H * 2 * d + 4 * B * H * T * d
+                         + B * H * T * 2 * d) + 4 * 2 * B * H * T + 4 * 8 * d)
         if self.kind == "v2_bwd":  # q, k, v, attn, dout, lam, lse in; dq, dk, dv, dlam out
             B, T, Hq, Hkv, d = self.B, self.T, self.Hq, self.Hkv, self.d
             return (e * (2 * B * T * Hq * d + 4 * B * T * Hkv * d + 2 * B * T * Hq * d + B * T * (Hq // 2) * d)
@@ -108,6 +114,9 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("v2_decode_B64_L32768_Hq64_Hkv8_d128", "decode", "bf16", B=64, T=32768, d=128, Hq=64,
                  Hkv=8, seed=5),
         Workload("v2_backward_B1_T8192_Hq64_Hkv8_d128", "v2_bwd", "bf16", B=1, T=8192, d=128, Hq=64, Hkv=8, seed=4),
+        Workload("v1_backward_B8_H6_T1024_d64", "v1_bwd", "bf16", B=8, H=6, T=1024, d=64, layers=(6,), seed=2),
+        Workload("v1_backward_B2_H12_T4096_d128", "v1_bwd", "bf16", B=2, H=12, T=4096, d=128, layers=(14,),
+                 seed=3),
         Workload("v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128", "decode_paged", "bf16", B=64, T=32768,
                  d=128, Hq=64, Hkv=8, seed=6, page=64),
         Workload("v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128", "decode_multi", "bf16", B=64, T=32768, d=128,
@@ -238,6 +247,10 @@ def paged_decode_inputs(B: int, max_len: int, page: int, Hq: int, Hkv: int, d: i
 def inputs_for(w: Workload, device="cpu") -> Dict[str, torch.Tensor]:
     if w.kind == "v1":
         return v1_inputs(w.B, w.H, w.T, w.d, w.torch_dtype, w.seed, device)
+    if w.kind == "v1_bwd":  # the V1 forward's inputs plus an output gradient dout ~ N(0, 1)
+        x = v1_inputs(w.B, w.H, w.T, w.d, w.torch_dtype, w.seed, device)
+        x["dout"] = _randn((w.B, w.T, w.H, 2 * w.d), _gen(w.seed + 99, device), device, w.torch_dtype)
+        return x
     if w.kind == "v2":
         return v2_inputs(w.B, w.T, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)
     if w.kind == "v2_bwd":  # the prefill's inputs plus an output gradient dout ~ N(0, 1)
