@@ -168,14 +168,20 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // Workgroup: (b, head h, 32 kNW query rows); wave w owns rows i0 + 32 w.  D:
 // q/k head dim; DV: v head dim (V2: D; V1: 2D, one launch per map).
 template <int D, int DV>
-__global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
+struct DqCfg {
+  static constexpr int STAGE = 2 * TileDma<D>::BYTES + TileDma<DV>::BYTES;  // [K "k" | K "v" | V "k"]
+  static constexpr int SMEM = 2 * STAGE;
+};
+// `bid`: the workgroup's index in the dQ grid order; `smem`: DqCfg::SMEM bytes
+// of LDS, 1 KB aligned.
+template <int D, int DV>
+__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned char* smem) {
   constexpr int KS = D / 16, KSV = DV / 16, CB = D / 32;
   constexpr int KM = KS > KSV ? KS : KSV;
   using Dma = TileDma<D>;
   using DmaV = TileDma<DV>;
   constexpr int TB = Dma::BYTES;
-  constexpr int STAGE = 2 * TB + DmaV::BYTES;  // [K "k" | K "v" | V "k"]
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  constexpr int STAGE = DqCfg<D, DV>::STAGE;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -186,7 +192,7 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
   // fastest, so the workgroups on one XCD (id mod 8) share kv groups and
   // stream the same K/V tiles through its L2
   const int units = a.B * a.Hq;
-  const int unit = blockIdx.x % units, tile = tiles - 1 - blockIdx.x / units;
+  const int unit = bid % units, tile = tiles - 1 - bid / units;
   const int g = unit % a.Hkv, jq = unit / a.Hkv;
   const int b = jq / a.G, h = g * a.G + jq % a.G;
   const int i0w = tile * BM + 32 * wave;
@@ -282,6 +288,12 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
       w.y = pack_bf16x2(acc[cb][4 * g4 + 2] * a.scale, acc[cb][4 * g4 + 3] * a.scale);
       *(uint2*)(dst + 32 * cb + 8 * g4 + 4 * hg) = w;
     }
+}
+
+template <int D, int DV>
+__global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[DqCfg<D, DV>::SMEM];
+  bwd_dq_body<D, DV>(a, blockIdx.x, smem);
 }
 
 // ---- dK, dV ------------------------------------------------------------------
@@ -463,9 +475,10 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
 //   da_2 = -lam dD,  dlam = -sum over rows of <dD, a_2>, and per map the
 //   softmax-attention gradients (dv summed over both maps); the lambda
 //   vectors get dlam times the derivative of exp(<lq, lk>).
-// Kernels: a pre-pass per (b, token, head); dQ with the V2 dQ kernel per map
-// (v 2d wide); dK per map; dV over both maps; a one-workgroup reduction of
-// dlam (fixed order) that writes the four vector gradients.
+// Kernels: a pre-pass per (b, token, head); then one grid holding the dlam
+// reduction (one workgroup, fixed order, writes the four vector gradients),
+// dQ of each map (the V2 dQ code with a 2d-wide v), dK of each map and dV
+// over both maps.
 
 // One wave per (b, t, h), t < Tp.
 template <int D>
@@ -535,43 +548,49 @@ __global__ void __launch_bounds__(256) bwd_v1_pre_kernel(const V1BwdArgs a) {
   }
 }
 
-// One workgroup: dlam = sum of the row terms, in a fixed order (each thread a
-// fixed strided subset, then a fixed tree), then the four vector gradients.
-template <int D>
-__global__ void __launch_bounds__(256) bwd_v1_lam_kernel(const V1BwdArgs a) {
-  __shared__ float part[256];
-  __shared__ float ex[2];
+// One workgroup of NT threads: dlam = sum of the row terms, in a fixed order
+// (thread t adds rows t + NT j into accumulator j mod 8, the eight are added
+// in order, then a fixed tree), then the four vector gradients.  `part`: NT
+// floats of LDS.
+template <int D, int NT>
+__device__ __forceinline__ void bwd_v1_lam_body(const V1BwdArgs& a, float* part) {
   const int tid = threadIdx.x;
   const long long n = (long long)a.B * a.T * a.H;
-  float acc = 0.f;
-  for (long long i = tid; i < n; i += 256) acc += a.lamrow[i];
-  part[tid] = acc;
-  if (tid < 64) {  // e1 = exp(<lq1, lk1>), e2 = exp(<lq2, lk2>)
-    float pa = 0.f, pb = 0.f;
+  float acc[8];
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) {
-      const int c = tid + 64 * i;
-      pa += a.lq1[c] * a.lk1[c];
-      pb += a.lq2[c] * a.lk2[c];
-    }
-    pa = wave_sum(pa);
-    pb = wave_sum(pb);
-    if (tid == 0) {
-      ex[0] = expf(pa);
-      ex[1] = expf(pb);
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  for (long long i0 = 0; i0 < n; i0 += 8LL * NT) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const long long i = i0 + (long long)j * NT + tid;
+      acc[j] += i < n ? a.lamrow[i] : 0.f;
     }
   }
+  float tot = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) tot += acc[j];
+  part[tid] = tot;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
+  for (int w = NT / 2; w > 0; w >>= 1) {
     if (tid < w) part[tid] += part[tid + w];
     __syncthreads();
   }
   const float dl = part[0];
-  for (int c = tid; c < D; c += 256) {
-    a.dlq1[c] = dl * ex[0] * a.lk1[c];
-    a.dlk1[c] = dl * ex[0] * a.lq1[c];
-    a.dlq2[c] = -dl * ex[1] * a.lk2[c];
-    a.dlk2[c] = -dl * ex[1] * a.lq2[c];
+  // e1 = exp(<lq1, lk1>), e2 = exp(<lq2, lk2>): every wave computes them
+  float pa = 0.f, pb = 0.f;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    const int c = lane + 64 * i;
+    pa += a.lq1[c] * a.lk1[c];
+    pb += a.lq2[c] * a.lk2[c];
+  }
+  const float e1 = expf(wave_sum(pa)), e2 = expf(wave_sum(pb));
+  for (int c = tid; c < D; c += NT) {
+    a.dlq1[c] = dl * e1 * a.lk1[c];
+    a.dlk1[c] = dl * e1 * a.lq1[c];
+    a.dlq2[c] = -dl * e2 * a.lk2[c];
+    a.dlk2[c] = -dl * e2 * a.lq2[c];
   }
 }
 
@@ -580,21 +599,25 @@ __global__ void __launch_bounds__(256) bwd_v1_lam_kernel(const V1BwdArgs a) {
 // S = Q K^T and dP = dA V^T with K / V fragments of its keys in registers,
 // dS = P (dP - D), dK^T += Q^T dS with transpose reads of the Q tile.
 template <int D>
-__global__ void __launch_bounds__(kNW * 64, 2) bwd_v1_dk_kernel(const V1BwdArgs a) {
+struct V1DkCfg {
+  static constexpr int STAGE = 2 * TileDma<D>::BYTES + TileDma<2 * D>::BYTES + 256;  // [Q "k" | Q "v" | dA "k" | lse, D]
+  static constexpr int SMEM = 2 * STAGE;
+};
+template <int D>
+__device__ __forceinline__ void bwd_v1_dk_body(const V1BwdArgs& a, int bid, unsigned char* smem) {
   constexpr int DV = 2 * D;
   constexpr int KS = D / 16, KSV = DV / 16, CB = D / 32;
   using Dma = TileDma<D>;
   using DmaV = TileDma<DV>;
   constexpr int TB = Dma::BYTES, TBV = DmaV::BYTES;
-  constexpr int STAGE = 2 * TB + TBV + 256;  // [Q "k" | Q "v" | dA "k" | lse, D of the 32 rows]
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  constexpr int STAGE = V1DkCfg<D>::STAGE;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, hg = lane >> 5;
   const int T = a.T, BK = 32 * kNW;
   const int units = a.B * a.H * 2;
-  const int unit = blockIdx.x % units, kt = blockIdx.x / units;  // low key tiles (most rows) first
+  const int unit = bid % units, kt = bid / units;  // low key tiles (most rows) first
   const int m = unit & 1, bh = unit >> 1;
   const int b = bh / a.H, h = bh % a.H;
   const int J0 = kt * BK, j0w = J0 + 32 * wave;
@@ -714,21 +737,25 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_v1_dk_kernel(const V1BwdArgs 
 // fragments of its keys in registers, dV^T += dA_m^T P_m with transpose
 // reads of the dA_m tile.
 template <int D>
-__global__ void __launch_bounds__(kNW * 64, 2) bwd_v1_dv_kernel(const V1BwdArgs a) {
+struct V1DvCfg {
+  static constexpr int STAGE = TileDma<D>::BYTES + TileDma<2 * D>::BYTES + 128;  // [Q_m "k" | dA_m "v" | lse]
+  static constexpr int SMEM = 2 * STAGE;
+};
+template <int D>
+__device__ __forceinline__ void bwd_v1_dv_body(const V1BwdArgs& a, int bid, unsigned char* smem) {
   constexpr int DV = 2 * D;
   constexpr int KS = D / 16, CBV = DV / 32;
   using Dma = TileDma<D>;
   using DmaV = TileDma<DV>;
   constexpr int TB = Dma::BYTES, TBV = DmaV::BYTES;
-  constexpr int STAGE = TB + TBV + 128;  // [Q_m "k" | dA_m "v" | lse of the 32 rows]
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  constexpr int STAGE = V1DvCfg<D>::STAGE;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, hg = lane >> 5;
   const int T = a.T, BK = 32 * kNW;
   const int units = a.B * a.H;
-  const int unit = blockIdx.x % units, kt = blockIdx.x / units;  // low key tiles (most rows) first
+  const int unit = bid % units, kt = bid / units;  // low key tiles (most rows) first
   const int b = unit / a.H, h = unit % a.H;
   const int J0 = kt * BK, j0w = J0 + 32 * wave;
   const bool active = j0w < T;
@@ -823,17 +850,27 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_v1_dv_kernel(const V1BwdArgs 
     }
 }
 
+// The dQ, dK and dV work of the V1 backward in one grid, so no workgroup
+// waits for another kernel's tail: level L = 0, 1, ... (heaviest first) holds
+// the dQ row tile qt-1-L of both maps, the dK key tile L of both maps and the
+// dV key tile L (each a causal trapezoid of about the same size).
 template <int D>
-hipError_t launch_v1(const V1BwdArgs& a, hipStream_t st) {
-  const void* args[] = {&a};
-  const long long items = (long long)a.B * a.Tp * a.H;
-  hipError_t e = hipLaunchKernel((const void*)bwd_v1_pre_kernel<D>, dim3((unsigned)((items + 3) / 4)), dim3(256),
-                                 (void**)args, 0, st);
-  if (e != hipSuccess) return e;
-  e = hipLaunchKernel((const void*)bwd_v1_lam_kernel<D>, dim3(1), dim3(256), (void**)args, 0, st);
-  if (e != hipSuccess) return e;
-  const int qt = (a.T + 32 * kNW - 1) / (32 * kNW);
-  for (int m = 0; m < 2; ++m) {  // dQ of each map: the dQ kernel with one head per kv head
+struct V1MainCfg {
+  static constexpr int a_ = DqCfg<D, 2 * D>::SMEM, b_ = V1DkCfg<D>::SMEM, c_ = V1DvCfg<D>::SMEM;
+  static constexpr int SMEM = a_ > b_ ? (a_ > c_ ? a_ : c_) : (b_ > c_ ? b_ : c_);
+};
+template <int D>
+__global__ void __launch_bounds__(kNW * 64, 2) bwd_v1_main_kernel(const V1BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[V1MainCfg<D>::SMEM];
+  if (blockIdx.x == 0) {  // the dlam reduction, first so that it overlaps the rest
+    bwd_v1_lam_body<D, kNW * 64>(a, (float*)smem);
+    return;
+  }
+  const int bh = a.B * a.H;
+  const int per_level = 5 * bh;
+  const int level = (blockIdx.x - 1) / per_level, r = (blockIdx.x - 1) % per_level;
+  if (r < 2 * bh) {  // dQ of map r / bh, unit r % bh
+    const int m = r / bh;
     BwdArgs q{};
     q.q = a.q[m], q.k = a.k[m], q.v = a.v;
     q.dq = a.dq[m];
@@ -842,16 +879,24 @@ hipError_t launch_v1(const V1BwdArgs& a, hipStream_t st) {
     q.lsew = a.lsew[m];
     q.sl2 = a.sl2, q.scale = a.scale;
     q.B = a.B, q.T = a.T, q.Hq = a.H, q.Hkv = a.H, q.G = 1, q.Tp = a.Tp;
-    const void* qa[] = {&q};
-    e = hipLaunchKernel((const void*)bwd_dq_kernel<D, 2 * D>, dim3(a.B * a.H * qt), dim3(kNW * 64), (void**)qa, 0,
-                        st);
-    if (e != hipSuccess) return e;
+    bwd_dq_body<D, 2 * D>(q, level * bh + r % bh, smem);
+  } else if (r < 4 * bh) {
+    bwd_v1_dk_body<D>(a, level * 2 * bh + (r - 2 * bh), smem);
+  } else {
+    bwd_v1_dv_body<D>(a, level * bh + (r - 4 * bh), smem);
   }
-  e = hipLaunchKernel((const void*)bwd_v1_dk_kernel<D>, dim3(a.B * a.H * 2 * qt), dim3(kNW * 64), (void**)args, 0,
-                      st);
+}
+
+template <int D>
+hipError_t launch_v1(const V1BwdArgs& a, hipStream_t st) {
+  const void* args[] = {&a};
+  const long long items = (long long)a.B * a.Tp * a.H;
+  hipError_t e = hipLaunchKernel((const void*)bwd_v1_pre_kernel<D>, dim3((unsigned)((items + 3) / 4)), dim3(256),
+                                 (void**)args, 0, st);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel((const void*)bwd_v1_dv_kernel<D>, dim3(a.B * a.H * qt), dim3(kNW * 64), (void**)args, 0,
-                         st);
+  const int qt = (a.T + 32 * kNW - 1) / (32 * kNW);
+  return hipLaunchKernel((const void*)bwd_v1_main_kernel<D>, dim3(1 + 5 * a.B * a.H * qt), dim3(kNW * 64),
+                         (void**)args, 0, st);
 }
 
 }  // namespace
