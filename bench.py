@@ -227,7 +227,7 @@ def _copy_calibration(torch, steps):
             "GB_per_s": round(4 * n / ms / 1e6, 1)}
 
 
-V1_BWD_KERNELS = "bwd_v1_pre_kernel|bwd_v1_lam_kernel|bwd_dq_kernel*2|bwd_v1_dk_kernel|bwd_v1_dv_kernel"
+V1_BWD_KERNELS = "bwd_v1_pre_kernel|bwd_v1_main_kernel"
 
 
 def write_traffic(pmc_dir):
