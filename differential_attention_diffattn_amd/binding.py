@@ -26,8 +26,13 @@ Logical layouts (any strided view with a unit-stride last axis is accepted):
   v2_fwd_train  as v2_fwd, also returning attn [B,T,Hq,d] and lse fp32 [B,Hq,T]
   v2_bwd     gradients dq [B,T,Hq,d], dk, dv [B,T,Hkv,d], dlam fp32 [B,T,Hq/2]
              from dout [B,T,Hq/2,d] and the training forward's attn, lse
+  rope       x [B,T,H,d] rotated (rotary embedding, rows at positions pos0 + t)
+  v2_lambda_proj  x [B,T,dm], w [P,dm] -> fp32 logits [B,T,P]
 Each takes ``softmax1=True`` for the off-by-one softmax entry points
-(``diffattn_*_softmax1``: every map's denominator gains exp(0)).
+(``diffattn_*_softmax1``: every map's denominator gains exp(0)).  v1_fwd,
+v2_fwd, v2_decode and v2_decode_paged take ``theta=`` for the rotary-embedding
+entry points (``diffattn_*_rope``: q rotated in the kernel, prefill k rotated
+into a workspace, decode caches holding rotated keys).
 """
 from __future__ import annotations
 
@@ -92,6 +97,25 @@ def load_library():
         f.argtypes = [i, i, i, i, i, i, i, DaIn, DaIn, DaIn, i, i, vp, ctypes.c_int64, vp, DaIn, DaOut, vp,
                       ctypes.c_size_t, vp]
         f.restype = i
+    fl = ctypes.c_float
+    lib.diffattn_rope.argtypes = [i, i, i, i, i, DaIn, DaOut, fl, i, vp]
+    lib.diffattn_rope.restype = i
+    lib.diffattn_v1_fwd_rope.argtypes = [i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaIn, fp, fp, fp, fp, i, fl, DaOut,
+                                         vp, ctypes.c_size_t, vp]
+    lib.diffattn_v1_fwd_rope.restype = i
+    lib.diffattn_v2_fwd_rope.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, fl, DaOut, vp, ctypes.c_size_t, vp]
+    lib.diffattn_v2_fwd_rope.restype = i
+    lib.diffattn_v2_decode_rope.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, fl, DaOut, vp,
+                                            ctypes.c_size_t, vp]
+    lib.diffattn_v2_decode_rope.restype = i
+    lib.diffattn_v2_decode_paged_rope.argtypes = [i, i, i, i, i, i, i, DaIn, DaIn, DaIn, i, i, vp, ctypes.c_int64,
+                                                  vp, DaIn, fl, DaOut, vp, ctypes.c_size_t, vp]
+    lib.diffattn_v2_decode_paged_rope.restype = i
+    for f in (lib.diffattn_v1_fwd_rope_workspace_bytes, lib.diffattn_v2_fwd_rope_workspace_bytes):
+        f.argtypes = [i, i, i, i]
+        f.restype = ctypes.c_size_t
+    lib.diffattn_v2_lambda_proj.argtypes = [i, i, i, i, i, DaIn, DaIn, DaIn, vp]
+    lib.diffattn_v2_lambda_proj.restype = i
     for sfx in ("", "_softmax1"):
         f = getattr(lib, "diffattn_v1_fwd_train" + sfx)
         f.argtypes = [i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaIn, fp, fp, fp, fp, i, DaOut, DaOut, DaOut, vp, vp]
@@ -162,8 +186,9 @@ def lambda_init(layer: int) -> float:
 
 
 def v1_fwd(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, out: torch.Tensor | None = None,
-           softmax1: bool = False):
-    """DIFF V1 forward; q*/k* [B,H,T,d], v [B,H,T,2d]; returns out [B,T,H,2d]."""
+           softmax1: bool = False, theta: float | None = None, workspace: torch.Tensor | None = None):
+    """DIFF V1 forward; q*/k* [B,H,T,d], v [B,H,T,2d]; returns out [B,T,H,2d].
+    ``theta``: rotary embedding of q1, q2, k1, k2 first (positions 0..T-1)."""
     lib = load_library()
     B, H, T, d = q1.shape
     for x in (q2, k1, k2):
@@ -181,6 +206,20 @@ def v1_fwd(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, out: torch.Tensor 
     if out is None:
         out = torch.empty((B, T, H, 2 * d), dtype=q1.dtype, device=q1.device)
     _check_device(q1, q2, k1, k2, v, out, *lams)
+    if theta is not None:
+        if softmax1:
+            raise ValueError("the rotary-embedding entry points use the standard softmax")
+        need = int(lib.diffattn_v1_fwd_rope_workspace_bytes(B, H, T, d))
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q1.device)
+        st = lib.diffattn_v1_fwd_rope(_dtype_code(q1), B, H, T, d, _in(q1, 0, 1, 2), _in(q2, 0, 1, 2),
+                                      _in(k1, 0, 1, 2), _in(k2, 0, 1, 2), _in(v, 0, 1, 2),
+                                      *[x.data_ptr() for x in lams], int(layer), float(theta), _out(out, 0, 2, 1),
+                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                      _stream(q1))
+        if st != 0:
+            raise DiffAttnError(st, "diffattn_v1_fwd_rope")
+        return out
     name = "diffattn_v1_fwd" + ("_softmax1" if softmax1 else "")
     st = getattr(lib, name)(_dtype_code(q1), B, H, T, d,
                              _in(q1, 0, 1, 2), _in(q2, 0, 1, 2), _in(k1, 0, 1, 2), _in(k2, 0, 1, 2),
@@ -261,8 +300,10 @@ def v1_bwd(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, attn1, attn2, lse,
     return tuple(grads)
 
 
-def v2_fwd(q, k, v, lam, out: torch.Tensor | None = None, softmax1: bool = False):
-    """DIFF V2 prefill; q [B,T,Hq,d], k/v [B,T,Hkv,d], lam [B,T,Hq/2]; returns [B,T,Hq/2,d]."""
+def v2_fwd(q, k, v, lam, out: torch.Tensor | None = None, softmax1: bool = False, theta: float | None = None,
+           workspace: torch.Tensor | None = None):
+    """DIFF V2 prefill; q [B,T,Hq,d], k/v [B,T,Hkv,d], lam [B,T,Hq/2]; returns [B,T,Hq/2,d].
+    ``theta``: rotary embedding of q and k first (positions 0..T-1)."""
     lib = load_library()
     B, T, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -273,6 +314,18 @@ def v2_fwd(q, k, v, lam, out: torch.Tensor | None = None, softmax1: bool = False
     if out is None:
         out = torch.empty((B, T, Hq // 2, d), dtype=q.dtype, device=q.device)
     _check_device(q, k, v, out)
+    if theta is not None:
+        if softmax1:
+            raise ValueError("the rotary-embedding entry points use the standard softmax")
+        need = int(lib.diffattn_v2_fwd_rope_workspace_bytes(B, T, Hkv, d))
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        st = lib.diffattn_v2_fwd_rope(_dtype_code(q), B, T, Hq, Hkv, d, _in(q, 0, 2, 1), _in(k, 0, 2, 1),
+                                      _in(v, 0, 2, 1), _in(lam, 0, 2, 1), float(theta), _out(out, 0, 2, 1),
+                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
+        if st != 0:
+            raise DiffAttnError(st, "diffattn_v2_fwd_rope")
+        return out
     name = "diffattn_v2_fwd" + ("_softmax1" if softmax1 else "")
     st = getattr(lib, name)(_dtype_code(q), B, T, Hq, Hkv, d, _in(q, 0, 2, 1), _in(k, 0, 2, 1),
                             _in(v, 0, 2, 1), _in(lam, 0, 2, 1), _out(out, 0, 2, 1), _stream(q))
@@ -348,8 +401,9 @@ def v2_decode_paged_workspace_bytes(B: int, max_len: int, nq: int, Hq: int, Hkv:
 
 
 def v2_decode(q, k_cache, v_cache, lam, out: torch.Tensor | None = None,
-              workspace: torch.Tensor | None = None, softmax1: bool = False):
-    """DIFF V2 decode; q [B,Hq,d], caches [B,L,Hkv,d], lam [B,Hq/2]; returns [B,Hq/2,d]."""
+              workspace: torch.Tensor | None = None, softmax1: bool = False, theta: float | None = None):
+    """DIFF V2 decode; q [B,Hq,d], caches [B,L,Hkv,d], lam [B,Hq/2]; returns [B,Hq/2,d].
+    ``theta``: q rotated to position L-1 in the kernel (the cache holds rotated keys)."""
     lib = load_library()
     B, Hq, d = q.shape
     L, Hkv = k_cache.shape[1], k_cache.shape[2]
@@ -363,9 +417,12 @@ def v2_decode(q, k_cache, v_cache, lam, out: torch.Tensor | None = None,
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check_device(q, k_cache, v_cache, out)
-    name = "diffattn_v2_decode" + ("_softmax1" if softmax1 else "")
+    if theta is not None and softmax1:
+        raise ValueError("the rotary-embedding entry points use the standard softmax")
+    name = "diffattn_v2_decode" + ("_softmax1" if softmax1 else "") + ("_rope" if theta is not None else "")
+    extra = (ctypes.c_float(theta),) if theta is not None else ()
     st = getattr(lib, name)(_dtype_code(q), B, L, Hq, Hkv, d, _in(q, 0, 1, None),
-                            _in(k_cache, 0, 2, 1), _in(v_cache, 0, 2, 1), _in(lam, 0, 1, None),
+                            _in(k_cache, 0, 2, 1), _in(v_cache, 0, 2, 1), _in(lam, 0, 1, None), *extra,
                             _out(out, 0, 1, None), workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), _stream(q))
     if st != 0:
@@ -401,7 +458,7 @@ def v2_decode_multi(q, k_cache, v_cache, lam, out: torch.Tensor | None = None,
 
 def v2_decode_paged(q, k_pages, v_pages, block_table, seq_lens, lam, max_len: int,
                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                    softmax1: bool = False):
+                    softmax1: bool = False, theta: float | None = None):
     """DIFF V2 decode over a paged cache; q [B,Hq,d] (one new token, returns [B,Hq/2,d]) or
     [B,nq,Hq,d] (nq new tokens, the last nq entries of each sequence; lam [B,nq,Hq/2]; returns
     [B,nq,Hq/2,d]); pages [num_pages,page_size,Hkv,d], block_table int32
@@ -432,13 +489,49 @@ def v2_decode_paged(q, k_pages, v_pages, block_table, seq_lens, lam, max_len: in
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check_device(q, k_pages, v_pages, out, block_table, seq_lens)
-    name = "diffattn_v2_decode_paged" + ("_softmax1" if softmax1 else "")
+    if theta is not None and softmax1:
+        raise ValueError("the rotary-embedding entry points use the standard softmax")
+    name = "diffattn_v2_decode_paged" + ("_softmax1" if softmax1 else "") + ("_rope" if theta is not None else "")
+    extra = (ctypes.c_float(theta),) if theta is not None else ()
     ax = (0, 2, 1) if multi else (0, 1, None)  # (b, h, t) axes of q / lam / out
     st = getattr(lib, name)(_dtype_code(q), B, int(max_len), nq, Hq, Hkv, d, _in(q, *ax),
                             _in(k_pages, 0, 2, 1), _in(v_pages, 0, 2, 1), num_pages, page_size,
                             block_table.data_ptr(), block_table.stride(0), seq_lens.data_ptr(),
-                            _in(lam, *ax), _out(out, *ax), workspace.data_ptr(),
+                            _in(lam, *ax), *extra, _out(out, *ax), workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), _stream(q))
     if st != 0:
         raise DiffAttnError(st, name)
+    return out
+
+
+def rope(x, theta: float = 10000.0, pos0: int = 0, out: torch.Tensor | None = None):
+    """Rotary embedding of x [B,T,H,d] bf16, row t at position pos0 + t (out may be x: in place)."""
+    lib = load_library()
+    B, T, H, d = x.shape
+    out = torch.empty_like(x) if out is None else out
+    if tuple(out.shape) != (B, T, H, d):
+        raise ValueError("out must have x's shape")
+    _check_device(x, out)
+    st = lib.diffattn_rope(_dtype_code(x), B, T, H, d, _in(x, 0, 2, 1), _out(out, 0, 2, 1), float(theta),
+                           int(pos0), _stream(x))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_rope")
+    return out
+
+
+def v2_lambda_proj(x, w, out: torch.Tensor | None = None):
+    """V2 lambda logits: x [B,T,dm] bf16, w [P,dm] bf16 (a linear layer's weight) -> fp32 [B,T,P]."""
+    lib = load_library()
+    B, T, dm = x.shape
+    P = w.shape[0]
+    if tuple(w.shape) != (P, dm):
+        raise ValueError("w must be [P, dm]")
+    out = torch.empty((B, T, P), dtype=torch.float32, device=x.device) if out is None else out
+    if tuple(out.shape) != (B, T, P) or out.dtype != torch.float32:
+        raise ValueError("out must be fp32 [B,T,P]")
+    _check_device(x, w)
+    st = lib.diffattn_v2_lambda_proj(_dtype_code(x), B, T, dm, P, DaIn(x.data_ptr(), x.stride(0), 0, x.stride(1)),
+                                     DaIn(w.data_ptr(), 0, w.stride(0), 0), _in(out, 0, 2, 1), _stream(x))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_v2_lambda_proj")
     return out

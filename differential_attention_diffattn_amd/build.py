@@ -18,7 +18,7 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 OUT = PKG / "libdiffattn.so"
 BUILD_DIR = PKG.parent / "_build"
-SOURCES = ["api.cpp", "prefill_bf16.hip", "v1_fp32.hip", "decode_bf16.hip", "backward_bf16.hip"]
+SOURCES = ["api.cpp", "prefill_bf16.hip", "v1_fp32.hip", "decode_bf16.hip", "backward_bf16.hip", "prologue_bf16.hip"]
 ARCH = os.environ.get("DIFFATTN_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

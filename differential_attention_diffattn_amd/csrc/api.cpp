@@ -51,6 +51,21 @@ TOut tout(const da_out& t) { return TOut{t.ptr, t.sb, t.sh, t.st}; }
 
 float log2e_over_sqrt(int d) { return (float)(1.4426950408889634 / sqrt((double)d)); }
 
+// Rotary embedding: theta must be a finite number > 0; positions stay below
+// 2^24 (exact in fp32).
+bool rope_theta_ok(float theta) { return theta > 0.f && theta < INFINITY; }
+float rope_nl2t(float theta, int d) { return (float)(-2.0 * log2((double)theta) / (double)d); }
+constexpr long long kMaxRopePos = 1LL << 24;
+
+// The library's own rotated-k buffer inside a caller workspace: [B,T,H,d]
+// contiguous bf16.
+struct RopeK {
+  float theta;
+  void* ws;
+  size_t ws_bytes;
+};
+size_t rope_k_bytes(int B, int T, int H, int d) { return ((size_t)B * T * H * d * 2 + 255) / 256 * 256; }
+
 da_status launch_status(hipError_t e) { return e == hipSuccess ? DA_OK : DA_E_LAUNCH; }
 
 // Largest grid the launchers build, for the overflow check.
@@ -104,8 +119,9 @@ struct PagedArgs {
 };
 da_status decode_impl(int softmax1, da_dtype dtype, int B, int L, int nq, int Hq, int Hkv, int d, da_in q,
                       da_in kc, da_in vc, const PagedArgs* pg, da_in lam, da_out out, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      size_t workspace_bytes, void* stream, float rope_theta = 0.f) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
+  if (rope_theta != 0.f && (!rope_theta_ok(rope_theta) || (long long)L >= kMaxRopePos)) return DA_E_SHAPE;
   if (!decode_sizes_ok(B, L, nq, Hq, Hkv, d)) return DA_E_SHAPE;
   if (!pg && nq > L) return DA_E_SHAPE;  // the new tokens are the last nq cache entries
   const int page_size = pg ? pg->page_size : 0;
@@ -154,6 +170,10 @@ da_status decode_impl(int softmax1, da_dtype dtype, int B, int L, int nq, int Hq
   a.nq = nq;
   a.ncg = gm.ncg;
   a.softmax1 = softmax1;
+  if (rope_theta != 0.f) {
+    a.rope = 1;
+    a.rope_nl2t = rope_nl2t(rope_theta, d);
+  }
   if (pg) {
     a.block_table = pg->block_table;
     a.bt_stride = pg->bt_stride;
@@ -191,9 +211,11 @@ static da_status v1_fwd_impl(int softmax1, da_dtype dtype, int B, int H, int T, 
                              da_in k1, da_in k2,
                           da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
                           const float* lam_k2, int layer_index, da_out out, void* stream,
-                          const da_out* attn1 = nullptr, const da_out* attn2 = nullptr, float* lse = nullptr) {
+                          const da_out* attn1 = nullptr, const da_out* attn2 = nullptr, float* lse = nullptr,
+                          const RopeK* rope = nullptr) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
   if (B < 1 || H < 1 || T < 1 || d < 1 || layer_index < 0) return DA_E_SHAPE;
+  if (rope && (!rope_theta_ok(rope->theta) || (long long)T >= kMaxRopePos)) return DA_E_SHAPE;
   const int64_t mult = dtype == DA_BF16 ? 8 : 4;
   DA_TRY(check_in(q1, mult));
   DA_TRY(check_in(q2, mult));
@@ -217,11 +239,34 @@ static da_status v1_fwd_impl(int softmax1, da_dtype dtype, int B, int H, int T, 
     if (!aligned(lse, 4)) return DA_E_LAYOUT;
   }
 
+  if (rope) {
+    if (dtype != DA_BF16) return DA_E_UNSUPPORTED;
+    const size_t kb = rope_k_bytes(B, T, H, d);
+    if (!rope->ws || !aligned(rope->ws, 256) || rope->ws_bytes < 2 * kb) return DA_E_WORKSPACE;
+  }
+
   const float li = (float)diffattn_lambda_init(layer_index);
   hipStream_t s = (hipStream_t)stream;
   if (dtype == DA_BF16) {
+    if (rope) {  // k1, k2 rotated into the workspace as [B,H,T,d]; q1, q2 in the kernel's prologue
+      for (int m = 0; m < 2; ++m) {
+        da::RopeArgs r{};
+        r.x = tin(m ? k2 : k1);
+        char* dst = (char*)rope->ws + m * rope_k_bytes(B, T, H, d);
+        r.out = TOut{dst, (int64_t)H * T * d, (int64_t)T * d, (int64_t)d};
+        r.B = B, r.T = T, r.H = H, r.d = d, r.pos0 = 0;
+        r.nl2t = rope_nl2t(rope->theta, d);
+        const da_status st = launch_status(da::launch_rope_bf16(r, s));
+        if (st != DA_OK) return st;
+        (m ? k2 : k1) = da_in{dst, (int64_t)H * T * d, (int64_t)T * d, (int64_t)d};
+      }
+    }
     da::PrefillArgs a{};
     a.q1 = tin(q1), a.q2 = tin(q2), a.k1 = tin(k1), a.k2 = tin(k2), a.v = tin(v);
+    if (rope) {
+      a.rope = 1;
+      a.rope_nl2t = rope_nl2t(rope->theta, d);
+    }
     a.out = tout(out);
     a.lq1 = lam_q1, a.lk1 = lam_k1, a.lq2 = lam_q2, a.lk2 = lam_k2;
     a.lam_init = li;
@@ -249,9 +294,10 @@ static da_status v1_fwd_impl(int softmax1, da_dtype dtype, int B, int H, int T, 
 static da_status v2_fwd_impl(int softmax1, da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
                              da_in v,
                           da_in lam, da_out out, void* stream, const da_out* attn = nullptr,
-                          float* lse = nullptr) {
+                          float* lse = nullptr, const RopeK* rope = nullptr) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1) return DA_E_SHAPE;
+  if (rope && (!rope_theta_ok(rope->theta) || (long long)T >= kMaxRopePos)) return DA_E_SHAPE;
   if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return DA_E_SHAPE;
   const int64_t mult = dtype == DA_BF16 ? 8 : 4;
   DA_TRY(check_in(q, mult));
@@ -267,7 +313,19 @@ static da_status v2_fwd_impl(int softmax1, da_dtype dtype, int B, int T, int Hq,
     if (!lse) return DA_E_NULL;
     if (!aligned(lse, 4)) return DA_E_LAYOUT;
   }
+  if (rope && (!rope->ws || !aligned(rope->ws, 256) || rope->ws_bytes < rope_k_bytes(B, T, Hkv, d)))
+    return DA_E_WORKSPACE;
 
+  if (rope) {  // k rotated into the workspace as [B,T,Hkv,d]; q in the kernel's prologue
+    da::RopeArgs r{};
+    r.x = tin(k);
+    r.out = TOut{rope->ws, (int64_t)T * Hkv * d, (int64_t)d, (int64_t)Hkv * d};
+    r.B = B, r.T = T, r.H = Hkv, r.d = d, r.pos0 = 0;
+    r.nl2t = rope_nl2t(rope->theta, d);
+    const da_status st = launch_status(da::launch_rope_bf16(r, (hipStream_t)stream));
+    if (st != DA_OK) return st;
+    k = da_in{rope->ws, (int64_t)T * Hkv * d, (int64_t)d, (int64_t)Hkv * d};
+  }
   da::PrefillArgs a{};
   a.q1 = a.q2 = tin(q);
   a.k1 = a.k2 = tin(k);
@@ -280,6 +338,10 @@ static da_status v2_fwd_impl(int softmax1, da_dtype dtype, int B, int T, int Hq,
   if (attn) {
     a.attn = tout(*attn);
     a.lse = lse;
+  }
+  if (rope) {
+    a.rope = 1;
+    a.rope_nl2t = rope_nl2t(rope->theta, d);
   }
   return launch_status(da::launch_prefill_v2_bf16(d, a, (hipStream_t)stream));
 }
@@ -533,6 +595,87 @@ da_status diffattn_v1_bwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, 
   return v1_bwd_impl(dtype, B, H, T, d, q1, q2, k1, k2, v, lam_q1, lam_k1, lam_q2, lam_k2, layer_index, attn1,
                      attn2, lse, dout, dq1, dq2, dk1, dk2, dv, dlam_q1, dlam_k1, dlam_q2, dlam_k2, workspace,
                      workspace_bytes, stream);
+}
+
+size_t diffattn_v1_fwd_rope_workspace_bytes(int B, int H, int T, int d) {
+  if (B < 1 || H < 1 || T < 1 || d < 1) return 0;
+  return 2 * rope_k_bytes(B, T, H, d);
+}
+
+da_status diffattn_v1_fwd_rope(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+                               da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
+                               const float* lam_k2, int layer_index, float theta, da_out out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  const RopeK r{theta, workspace, workspace_bytes};
+  return v1_fwd_impl(0, dtype, B, H, T, d, q1, q2, k1, k2, v, lam_q1, lam_k1, lam_q2, lam_k2, layer_index, out,
+                     stream, nullptr, nullptr, nullptr, &r);
+}
+
+size_t diffattn_v2_fwd_rope_workspace_bytes(int B, int T, int Hkv, int d) {
+  if (B < 1 || T < 1 || Hkv < 1 || d < 1) return 0;
+  return rope_k_bytes(B, T, Hkv, d);
+}
+
+da_status diffattn_v2_fwd_rope(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
+                               da_in lam, float theta, da_out out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  const RopeK r{theta, workspace, workspace_bytes};
+  return v2_fwd_impl(0, dtype, B, T, Hq, Hkv, d, q, k, v, lam, out, stream, nullptr, nullptr, &r);
+}
+
+da_status diffattn_v2_decode_rope(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
+                                  da_in v_cache, da_in lam, float theta, da_out out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!rope_theta_ok(theta)) return DA_E_SHAPE;
+  return decode_impl(0, dtype, B, L, 1, Hq, Hkv, d, q, k_cache, v_cache, nullptr, lam, out, workspace,
+                     workspace_bytes, stream, theta);
+}
+
+da_status diffattn_v2_decode_paged_rope(da_dtype dtype, int B, int max_len, int nq, int Hq, int Hkv, int d, da_in q,
+                                        da_in k_pages, da_in v_pages, int num_pages, int page_size,
+                                        const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                                        da_in lam, float theta, da_out out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (!rope_theta_ok(theta)) return DA_E_SHAPE;
+  const PagedArgs pg{num_pages, page_size, block_table, bt_stride, seq_lens};
+  return decode_impl(0, dtype, B, max_len, nq, Hq, Hkv, d, q, k_pages, v_pages, &pg, lam, out, workspace,
+                     workspace_bytes, stream, theta);
+}
+
+da_status diffattn_rope(da_dtype dtype, int B, int T, int H, int d, da_in x, da_out out, float theta, int pos0,
+                        void* stream) {
+  if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
+  if (B < 1 || T < 1 || H < 1 || d < 1 || pos0 < 0) return DA_E_SHAPE;
+  if (!rope_theta_ok(theta) || (long long)pos0 + T >= kMaxRopePos) return DA_E_SHAPE;
+  DA_TRY(check_in(x, 8));
+  DA_TRY(check_out(out, 8));
+  if (dtype != DA_BF16) return DA_E_UNSUPPORTED;
+  if (d % 8 != 0 || d > 4096) return DA_E_UNSUPPORTED;
+  if (!grid_fits(((long long)B * T * H * (d / 4) + 255) / 256)) return DA_E_SHAPE;
+  da::RopeArgs r{};
+  r.x = tin(x);
+  r.out = tout(out);
+  r.B = B, r.T = T, r.H = H, r.d = d, r.pos0 = pos0;
+  r.nl2t = rope_nl2t(theta, d);
+  return launch_status(da::launch_rope_bf16(r, (hipStream_t)stream));
+}
+
+da_status diffattn_v2_lambda_proj(da_dtype dtype, int B, int T, int dm, int P, da_in x, da_in w, da_in out,
+                                  void* stream) {
+  if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
+  if (B < 1 || T < 1 || dm < 1 || P < 1) return DA_E_SHAPE;
+  DA_TRY(check_in(x, 8));
+  DA_TRY(check_in(w, 8));
+  DA_TRY(check_logits(out));
+  if (dtype != DA_BF16) return DA_E_UNSUPPORTED;
+  if (dm % 64 != 0) return DA_E_UNSUPPORTED;
+  if (!grid_fits(((long long)B * T + 31) / 32 * ((P + 31) / 32))) return DA_E_SHAPE;
+  da::LamProjArgs a{};
+  a.x = tin(x);
+  a.w = tin(w);
+  a.out = TOut{(void*)out.ptr, out.sb, out.sh, out.st};
+  a.B = B, a.T = T, a.dm = dm, a.P = P;
+  return launch_status(da::launch_lambda_proj_bf16(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -38,6 +38,10 @@ struct PrefillArgs {
   // attn2, both [B,T,H,2d] (roles b, differential head, t), lse [2][B][H][T].
   TOut attn, attn2;
   float* lse;
+  // rotary embedding of q in the prologue (rope != 0): row t of q turns by
+  // t * theta^(-2c/d); rope_nl2t = -2 log2(theta) / d
+  int rope;
+  float rope_nl2t;
 };
 
 hipError_t launch_prefill_v1_bf16(int d, const PrefillArgs& a, hipStream_t s);
@@ -117,8 +121,30 @@ struct DecodeArgs {
   int64_t bt_stride;
   const int32_t* seq_lens;
   int page_shift, page_mask, num_pages;
+  // rotary embedding of q (rope != 0): new token i sits at cache position
+  // L_b - nq + i; the cache holds its keys rotated
+  int rope;
+  float rope_nl2t;
 };
 hipError_t launch_decode_bf16(int d, const DecodeArgs& a, hipStream_t s);
+
+// Rotary embedding of a [B,T,H,d] bf16 tensor (rows at positions pos0 + t),
+// out-of-place or in place; and the V2 lambda projection
+// logits[b,t,p] = <x[b,t,:], w[p,:]> (x [B,T,dm] bf16, w [P,dm] bf16, fp32 out).
+struct RopeArgs {
+  TIn x;
+  TOut out;
+  int B, T, H, d, pos0;
+  float nl2t;
+};
+hipError_t launch_rope_bf16(const RopeArgs& a, hipStream_t s);
+struct LamProjArgs {
+  TIn x;       // roles b, -, t
+  TIn w;       // roles -, p (sh), -
+  TOut out;    // fp32, roles b, p, t
+  int B, T, dm, P;
+};
+hipError_t launch_lambda_proj_bf16(const LamProjArgs& a, hipStream_t s);
 // workgroups of the decode split kernel (B * nsplit units padded to a multiple of 8, times Hkv)
 long long decode_split_grid(int B, int Hkv, int nsplit);
 // 16-wide column blocks per workgroup (1 or 2) and column groups for nq query tokens x G heads

@@ -1,0 +1,126 @@
+// prologue_bf16.hip -- the steps just upstream of the attention: the rotary
+// embedding of a q or k tensor, and the V2 lambda projection (gfx950).
+//
+// Rotary embedding (rope.hpp: the rotate-half arrangement Wilsontomass's
+// module in the nanoGPT issue "How best to implement a differential
+// transformer?" applies to every q and k head): an HBM-bound pass, one thread
+// per two adjacent pairs (c, c+1) <-> (c + d/2, c + d/2 + 1), 4-byte loads and
+// stores; in place or out of place.  The prefill and decode kernels rotate q
+// themselves (prologue, registers); this pass is for k, whose tiles go from
+// HBM straight to LDS and are read by several workgroups each.
+//
+// Lambda projection ("Differential Transformer V2" article: a projected
+// lambda for each token and head): logits[b,t,p] = <x[b,t,:], w[p,:]>, w laid
+// out like a linear layer's weight [P, dm].  A workgroup owns 32 tokens x 32
+// pairs; its 4 waves split dm in four and each runs v_mfma_f32_32x32x16_bf16
+// over its quarter (A = 32 token rows of x, B = 32 rows of w, both 16-byte
+// loads straight from HBM / L2); the four partial tiles are added in a fixed
+// order through LDS (deterministic).  It reads x once: HBM-bound.
+#include <math.h>
+
+#include "kernels.hpp"
+#include "rope.hpp"
+
+namespace da {
+namespace {
+
+__global__ void __launch_bounds__(256) rope_kernel(const RopeArgs a) {
+  const int tpr = a.d / 4;  // threads per row
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = gid / tpr;
+  if (row >= (long long)a.B * a.T * a.H) return;
+  const int c = 2 * (int)(gid % tpr);  // pairs (c, c + d/2) and (c + 1, c + 1 + d/2)
+  const int h = (int)(row % a.H);
+  const int t = (int)((row / a.H) % a.T);
+  const int b = (int)(row / ((long long)a.H * a.T));
+  const uint16_t* xr = (const uint16_t*)a.x.p + b * a.x.sb + (int64_t)t * a.x.st + (int64_t)h * a.x.sh;
+  uint16_t* orow = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)t * a.out.st + (int64_t)h * a.out.sh;
+  const int half = a.d / 2;
+  const uint32_t lo = *(const uint32_t*)(xr + c), hi = *(const uint32_t*)(xr + c + half);
+  const float x1[2] = {bf16_to_f32((uint16_t)(lo & 0xffffu)), bf16_to_f32((uint16_t)(lo >> 16))};
+  const float x2[2] = {bf16_to_f32((uint16_t)(hi & 0xffffu)), bf16_to_f32((uint16_t)(hi >> 16))};
+  float y1[2], y2[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float sn, cs;
+    rope_sincos(a.pos0 + t, rope_freq(c + j, a.nl2t), &sn, &cs);
+    y1[j] = x1[j] * cs - x2[j] * sn;
+    y2[j] = x2[j] * cs + x1[j] * sn;
+  }
+  *(uint32_t*)(orow + c) = pack_bf16x2(y1[0], y1[1]);
+  *(uint32_t*)(orow + c + half) = pack_bf16x2(y2[0], y2[1]);
+}
+
+constexpr int kProjWaves = 4;
+
+__global__ void __launch_bounds__(kProjWaves * 64) lambda_proj_kernel(const LamProjArgs a) {
+  __shared__ f32x16 part[kProjWaves - 1][64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int li = lane & 31, hg = lane >> 5;
+  const int ptiles = (a.P + 31) / 32;
+  const long long r0 = (long long)(blockIdx.x / ptiles) * 32;  // first token (flattened b * T + t)
+  const int p0 = (blockIdx.x % ptiles) * 32;
+  const long long ntok = (long long)a.B * a.T;
+  // this lane's A row (token) and B row (pair), clamped into range (masked at the store)
+  const long long r = min(r0 + li, ntok - 1);
+  const int rb = (int)(r / a.T), rt = (int)(r % a.T);
+  const uint16_t* xr = (const uint16_t*)a.x.p + rb * a.x.sb + (int64_t)rt * a.x.st;
+  const uint16_t* wr = (const uint16_t*)a.w.p + (int64_t)min(p0 + li, a.P - 1) * a.w.sh;
+  const int kq = a.dm / kProjWaves;  // this wave's quarter of dm (a multiple of 16)
+  const int k0 = wave * kq;
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  int k = k0;
+  for (; k + 64 <= k0 + kq; k += 64) {  // four k-steps per round: eight 16-byte loads in flight
+    bf16x8 xa[4], wb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xa[j] = as_bf16x8(*(const uint4*)(xr + k + 16 * j + 8 * hg));
+      wb[j] = as_bf16x8(*(const uint4*)(wr + k + 16 * j + 8 * hg));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = mfma32x32x16(xa[j], wb[j], acc);
+  }
+  for (; k < k0 + kq; k += 16)
+    acc = mfma32x32x16(as_bf16x8(*(const uint4*)(xr + k + 8 * hg)), as_bf16x8(*(const uint4*)(wr + k + 8 * hg)),
+                       acc);
+  if (wave > 0) part[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kProjWaves - 1; ++w) {
+    const f32x16 x = part[w][lane];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += x[i];
+  }
+  // register i: token r0 + 8(i>>2) + 4hg + (i&3), pair p0 + li
+  const int p = p0 + li;
+  if (p >= a.P) return;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const long long tok = r0 + 8 * (i >> 2) + 4 * hg + (i & 3);
+    if (tok < ntok) {
+      const int ob = (int)(tok / a.T), ot = (int)(tok % a.T);
+      ((float*)a.out.p)[ob * a.out.sb + (int64_t)ot * a.out.st + (int64_t)p * a.out.sh] = acc[i];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope_bf16(const RopeArgs& a, hipStream_t s) {
+  const void* args[] = {&a};
+  const long long threads = (long long)a.B * a.T * a.H * (a.d / 4);
+  return hipLaunchKernel((const void*)rope_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                         (void**)args, 0, s);
+}
+
+hipError_t launch_lambda_proj_bf16(const LamProjArgs& a, hipStream_t s) {
+  const void* args[] = {&a};
+  const long long tiles = ((long long)a.B * a.T + 31) / 32 * ((a.P + 31) / 32);
+  return hipLaunchKernel((const void*)lambda_proj_kernel, dim3((unsigned)tiles), dim3(kProjWaves * 64),
+                         (void**)args, 0, s);
+}
+
+}  // namespace da

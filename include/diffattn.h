@@ -406,6 +406,77 @@ da_status diffattn_v1_bwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, 
                           float* dlam_k1, float* dlam_q2, float* dlam_k2, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * Rotary position embedding (Wilsontomass's module in the nanoGPT issue "How
+ * best to implement a differential transformer?" rotates every q and k head
+ * before the attention; the rotate-half arrangement): element c < d/2 of a
+ * head vector pairs with c + d/2 and the pair turns by t * theta^(-2c/d) at
+ * position t:  x'_c = x_c cos - x_{c+d/2} sin,  x'_{c+d/2} = x_{c+d/2} cos +
+ * x_c sin.  theta: a finite float > 0 (10000 in the usual setting).
+ *
+ * diffattn_rope: rotate x, logical [B,T,H,d] bf16 (roles b, h, t), row t at
+ *   position pos0 + t, into out (same logical shape; out == x rotates in
+ *   place).  d a multiple of 8; pos0 >= 0 and pos0 + T < 2^24.  One
+ *   HBM-bound kernel.  Use it for keys written into a cache, which the
+ *   decode entry points below expect rotated.
+ */
+da_status diffattn_rope(da_dtype dtype, int B, int T, int H, int d, da_in x, da_out out, float theta, int pos0,
+                        void* stream);
+
+/*
+ * DIFF V1 / V2 prefill with the rotary embedding applied to q and k first
+ * (positions 0 .. T-1): q is rotated inside the attention kernel's prologue,
+ * k by diffattn_rope into the caller's workspace (k's tiles are read by
+ * several workgroups each, so it is rotated once), then the attention reads
+ * it.  Arguments, layouts and errors as for diffattn_v1_fwd /
+ * diffattn_v2_fwd, plus theta and a workspace of at least
+ * diffattn_v1_fwd_rope_workspace_bytes(B,H,T,d) /
+ * diffattn_v2_fwd_rope_workspace_bytes(B,T,Hkv,d) bytes, 256-byte aligned
+ * (DA_E_WORKSPACE otherwise).  bf16 only; T < 2^24.
+ */
+size_t diffattn_v1_fwd_rope_workspace_bytes(int B, int H, int T, int d);
+da_status diffattn_v1_fwd_rope(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+                               da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
+                               const float* lam_k2, int layer_index, float theta, da_out out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+size_t diffattn_v2_fwd_rope_workspace_bytes(int B, int T, int Hkv, int d);
+da_status diffattn_v2_fwd_rope(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
+                               da_in lam, float theta, da_out out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * DIFF V2 decode with the new token's q rotated to its cache position inside
+ * the decode kernel: L - 1 (dense), seq_lens[b] - nq + i (paged, new token
+ * i).  The cache must hold its keys already rotated, each at its own
+ * position (as diffattn_rope with pos0 = the first row's position writes
+ * them).  Arguments, workspace and errors as for diffattn_v2_decode /
+ * diffattn_v2_decode_paged, plus theta (DA_E_SHAPE unless finite and > 0).
+ */
+da_status diffattn_v2_decode_rope(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
+                                  da_in v_cache, da_in lam, float theta, da_out out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+da_status diffattn_v2_decode_paged_rope(da_dtype dtype, int B, int max_len, int nq, int Hq, int Hkv, int d, da_in q,
+                                        da_in k_pages, da_in v_pages, int num_pages, int page_size,
+                                        const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                                        da_in lam, float theta, da_out out, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
+ * DIFF V2 lambda projection ("Differential Transformer V2" article: a
+ * projected lambda for each token and each head, read as a linear map
+ * without bias of the token's hidden state):
+ *   out[b,t,p] = sum_c x[b,t,c] w[p,c]   (fp32 logits; the sigmoid stays in
+ *   diffattn_v2_fwd, which takes these logits as lam).
+ *   x    logical [B,T,dm] bf16 (roles b, t; sh unused), 16-byte rows.
+ *   w    logical [P,dm] bf16, a linear layer's weight (the pair stride in sh;
+ *        sb, st unused).
+ *   out  logical [B,T,P] fp32 (roles b, h = pair, t), 4-byte aligned.
+ *   dm a multiple of 64 (DA_E_UNSUPPORTED otherwise).  One kernel, MFMA,
+ *   reads x once; sums over dm in a fixed order (deterministic).
+ */
+da_status diffattn_v2_lambda_proj(da_dtype dtype, int B, int T, int dm, int P, da_in x, da_in w, da_in out,
+                                  void* stream);
+
 /* lambda_init = 0.8 - 0.6*exp(-0.3*layer_index), as the V1 kernels use it
  * (computed on the host in double, handed to the device as float). */
 double diffattn_lambda_init(int layer_index);

@@ -278,3 +278,61 @@ def test_v2_training_validation(lib):
     assert _v2_bwd(lib, wsb=100) == E_WS
     for fn in (lib.diffattn_v2_fwd_train, lib.diffattn_v2_fwd_train_softmax1):
         assert fn(1, 1, 16, 8, 2, 128, _t(), _t(), _t(), _t(), _t(out=True), _t(out=True), 0, None) == E_NULL
+
+
+# ----- rotary embedding and lambda projection ------------------------------------
+
+def test_prologue_entry_points_are_declared(lib):
+    syms = _declared_symbols()
+    for need in ("diffattn_rope", "diffattn_v1_fwd_rope", "diffattn_v1_fwd_rope_workspace_bytes",
+                 "diffattn_v2_fwd_rope", "diffattn_v2_fwd_rope_workspace_bytes", "diffattn_v2_decode_rope",
+                 "diffattn_v2_decode_paged_rope", "diffattn_v2_lambda_proj"):
+        assert need in syms and hasattr(lib, need)
+
+
+def test_rope_validation(lib):
+    f = lambda **k: lib.diffattn_rope(k.get("dtype", 1), 1, k.get("T", 16), 2, k.get("d", 64), _t(),
+                                      k.get("out", _t(out=True)), ctypes.c_float(k.get("theta", 1e4)),
+                                      k.get("pos0", 0), None)
+    assert f(theta=0.0) == E_SHAPE
+    assert f(theta=-1.0) == E_SHAPE
+    assert f(theta=float("inf")) == E_SHAPE
+    assert f(pos0=-1) == E_SHAPE
+    assert f(pos0=(1 << 24) - 8) == E_SHAPE                  # positions must stay exact in fp32
+    assert f(T=0) == E_SHAPE
+    assert f(out=_t(ptr=0, out=True)) == E_NULL
+    assert f(dtype=0) == E_UNSUP
+    assert f(d=12) == E_UNSUP                                 # multiples of 8
+
+
+def test_prefill_rope_validation(lib):
+    assert lib.diffattn_v2_fwd_rope_workspace_bytes(1, 8192, 8, 128) == 8192 * 8 * 128 * 2
+    assert lib.diffattn_v1_fwd_rope_workspace_bytes(8, 6, 1024, 64) == 2 * 8 * 6 * 1024 * 64 * 2
+    v2 = lambda ws=FAKE, wsb=1 << 30, theta=1e4: lib.diffattn_v2_fwd_rope(
+        1, 1, 16, 8, 2, 128, _t(), _t(), _t(), _t(), ctypes.c_float(theta), _t(out=True), ws, wsb, None)
+    assert v2(ws=0) == E_WS
+    assert v2(ws=FAKE + 16) == E_WS
+    assert v2(wsb=100) == E_WS
+    assert v2(theta=0.0) == E_SHAPE
+    v1 = lambda dtype=1, ws=FAKE, wsb=1 << 30: lib.diffattn_v1_fwd_rope(
+        dtype, 1, 2, 16, 64, _t(), _t(), _t(), _t(), _t(), FAKE, FAKE, FAKE, FAKE, 0, ctypes.c_float(1e4),
+        _t(out=True), ws, wsb, None)
+    assert v1(dtype=0) == E_UNSUP
+    assert v1(wsb=lib.diffattn_v1_fwd_rope_workspace_bytes(1, 2, 16, 64) - 1) == E_WS
+
+
+def test_decode_rope_validation(lib):
+    f = lambda theta=1e4, wsb=1 << 30: lib.diffattn_v2_decode_rope(
+        1, 2, 100, 8, 2, 128, _t(), _t(), _t(), _t(), ctypes.c_float(theta), _t(out=True), FAKE, wsb, None)
+    assert f(theta=0.0) == E_SHAPE
+    assert f(theta=float("nan")) == E_SHAPE
+    assert f(wsb=100) == E_WS
+
+
+def test_lambda_proj_validation(lib):
+    f = lambda dtype=1, dm=4096, out=FAKE: lib.diffattn_v2_lambda_proj(dtype, 1, 16, dm, 32, _t(), _t(),
+                                                                        DaIn(out, 0, 4, 128), None)
+    assert f(dm=100) == E_UNSUP                               # multiples of 64
+    assert f(dtype=0) == E_UNSUP
+    assert f(out=0) == E_NULL
+    assert f(out=FAKE + 2) == E_LAYOUT
