@@ -19,7 +19,8 @@ The JSON line also carries:
                 the V1 backward at the GPT-2-small and 3B shapes and the V2
                 backward (each timed without its training forward), V2
                 decode, V2 decode of a ragged batch over a paged cache, V2
-                decode of 4 new tokens per sequence),
+                decode of 4 new tokens per sequence, V2 prefill and decode
+                with the rotary embedding, the V2 lambda projection),
                 each with its own roofline; a secondary step is
                 8 launches of the workload (warm-up ~0.3 s of its own calls).
 Logs go to stderr; stdout holds exactly one JSON line.
@@ -43,7 +44,8 @@ HEADLINE = "v1_gpt2small_B8_H6_T1024_d64"
 SECONDARY = ["v1_3b_B2_H12_T4096_d128", "v2_prefill_B1_T8192_Hq64_Hkv8_d128", "v1_backward_B8_H6_T1024_d64",
              "v1_backward_B2_H12_T4096_d128", "v2_backward_B1_T8192_Hq64_Hkv8_d128",
              "v2_decode_B64_L32768_Hq64_Hkv8_d128", "v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128",
-             "v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128"]
+             "v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128", "v2_prefill_rope_B1_T8192_Hq64_Hkv8_d128",
+             "v2_decode_rope_B64_L32768_Hq64_Hkv8_d128", "v2_lambda_proj_B1_T8192_dm4096_P32"]
 
 
 def log(*a):
@@ -60,6 +62,14 @@ def _caller(w, x, binding, torch, softmax1=False):
     if w.kind == "v2":
         out = torch.empty((w.B, w.T, w.Hq // 2, w.d), dtype=w.torch_dtype, device=x["v"].device)
         return lambda layer: binding.v2_fwd(x["q"], x["k"], x["v"], x["lam"], out=out, softmax1=softmax1)
+    if w.kind == "v2_rope":  # rotary embedding: k rotation pass + prefill with q rotated in its prologue
+        out = torch.empty((w.B, w.T, w.Hq // 2, w.d), dtype=w.torch_dtype, device=x["v"].device)
+        ws = torch.empty(int(binding.load_library().diffattn_v2_fwd_rope_workspace_bytes(w.B, w.T, w.Hkv, w.d)),
+                         dtype=torch.uint8, device=x["v"].device)
+        return lambda layer: binding.v2_fwd(x["q"], x["k"], x["v"], x["lam"], out=out, theta=1e4, workspace=ws)
+    if w.kind == "lam_proj":
+        out = torch.empty((w.B, w.T, w.Hq), dtype=torch.float32, device=x["x"].device)
+        return lambda layer: binding.v2_lambda_proj(x["x"], x["w"], out=out)
     if w.kind == "v1_bwd":  # the timed call is the backward; the training forward runs once, untimed
         args = [x[n] for n in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")]
         layer0 = w.layers[0]
@@ -89,6 +99,8 @@ def _caller(w, x, binding, torch, softmax1=False):
         return lambda layer: binding.v2_decode_multi(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws,
                                                      softmax1=softmax1)
     ws = torch.empty(binding.v2_decode_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.d), dtype=torch.uint8, device=dev)
+    if w.kind == "decode_rope":  # q rotated in the kernel; the cache is read as holding rotated keys
+        return lambda layer: binding.v2_decode(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws, theta=1e4)
     return lambda layer: binding.v2_decode(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws,
                                            softmax1=softmax1)
 
@@ -144,7 +156,7 @@ def _timed(torch, call, layers, steps, warmup, graph=True):
 
 def _roofline(w, launch_ms):
     avg_s = sum(launch_ms) / len(launch_ms) / 1e3
-    if w.kind in ("decode", "decode_paged", "decode_multi"):
+    if w.kind in ("decode", "decode_rope", "decode_paged", "decode_multi", "lam_proj"):
         a = w.compulsory_bytes() / avg_s / 1e9
         return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(a / PEAK_HBM_GBS, 4), "traffic": None,
@@ -186,8 +198,9 @@ def _source_sha(kind):
     from hardware counters only applies to the kernel it was measured on."""
     import hashlib
 
-    src = {"v1": "prefill_bf16.hip", "v2": "prefill_bf16.hip", "v1_bwd": "backward_bf16.hip",
-           "v2_bwd": "backward_bf16.hip", "decode": "decode_bf16.hip",
+    src = {"v1": "prefill_bf16.hip", "v2": "prefill_bf16.hip", "v2_rope": "prefill_bf16.hip",
+           "v1_bwd": "backward_bf16.hip", "v2_bwd": "backward_bf16.hip", "decode": "decode_bf16.hip",
+           "decode_rope": "decode_bf16.hip", "lam_proj": "prologue_bf16.hip",
            "decode_paged": "decode_bf16.hip", "decode_multi": "decode_bf16.hip"}[kind]
     path = os.path.join(ROOT, "differential_attention_diffattn_amd", "csrc", src)
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
@@ -377,6 +390,15 @@ def main():
         elif w.kind == "v2_bwd":
             res.update(metric="causal bwd TFLOP/s (5 products over unmasked pairs)", unit="TFLOP/s",
                        value=round(w.flops() / per_call_s / 1e12, 3))
+        elif w.kind == "decode_rope":
+            res.update(metric="V2 decode HBM GB/s, q rotated (rotary embedding) in the kernel", unit="GB/s",
+                       value=round(w.compulsory_bytes() / per_call_s / 1e9, 1))
+        elif w.kind == "lam_proj":
+            res.update(metric="V2 lambda projection HBM GB/s (x, w read once; logits written once)", unit="GB/s",
+                       value=round(w.compulsory_bytes() / per_call_s / 1e9, 1))
+        elif w.kind == "v2_rope":
+            res.update(metric="causal fwd TFLOP/s with the rotary embedding (k pass + prefill)", unit="TFLOP/s",
+                       value=round(w.flops() / per_call_s / 1e12, 3))
         elif w.kind == "v1_bwd":
             res.update(metric="causal bwd TFLOP/s (5 products per map over unmasked pairs)", unit="TFLOP/s",
                        value=round(w.flops() / per_call_s / 1e12, 3))
@@ -400,7 +422,8 @@ def main():
             # warm-up sized to ~0.3 s of this workload's own calls, so the
             # GPU clock has settled under its load before the timed steps
             ws = workloads.WORKLOADS[name]
-            est_s = ws.flops() / 1e15 if ws.kind in ("v1", "v2", "v1_bwd", "v2_bwd") else ws.compulsory_bytes() / 5.5e12
+            est_s = (ws.flops() / 1e15 if ws.kind in ("v1", "v2", "v2_rope", "v1_bwd", "v2_bwd")
+                     else ws.compulsory_bytes() / 5.5e12)
             # 8 launches per step: the events around a graph replay then time
             # the kernels, not the replay's launch
             _, xs, r = measure(name, max(10, args.steps), max(3, int(0.3 / (8 * est_s))), calls_per_step=8)

@@ -54,7 +54,14 @@ float log2e_over_sqrt(int d) { return (float)(1.4426950408889634 / sqrt((double)
 // Rotary embedding: theta must be a finite number > 0; positions stay below
 // 2^24 (exact in fp32).
 bool rope_theta_ok(float theta) { return theta > 0.f && theta < INFINITY; }
-float rope_nl2t(float theta, int d) { return (float)(-2.0 * log2((double)theta) / (double)d); }
+// w_c = theta^(-2c/d) for c < d/2, as hi + lo floats (d <= 256).
+void rope_tab(float theta, int d, da::RopeTab* t) {
+  for (int c = 0; c < 128; ++c) {
+    const double w = c < d / 2 ? pow((double)theta, -2.0 * c / (double)d) : 0.0;
+    t->hi[c] = (float)w;
+    t->lo[c] = (float)(w - (double)t->hi[c]);
+  }
+}
 constexpr long long kMaxRopePos = 1LL << 24;
 
 // The library's own rotated-k buffer inside a caller workspace: [B,T,H,d]
@@ -172,7 +179,7 @@ da_status decode_impl(int softmax1, da_dtype dtype, int B, int L, int nq, int Hq
   a.softmax1 = softmax1;
   if (rope_theta != 0.f) {
     a.rope = 1;
-    a.rope_nl2t = rope_nl2t(rope_theta, d);
+    rope_tab(rope_theta, d, &a.rope_w);
   }
   if (pg) {
     a.block_table = pg->block_table;
@@ -255,7 +262,7 @@ static da_status v1_fwd_impl(int softmax1, da_dtype dtype, int B, int H, int T, 
         char* dst = (char*)rope->ws + m * rope_k_bytes(B, T, H, d);
         r.out = TOut{dst, (int64_t)H * T * d, (int64_t)T * d, (int64_t)d};
         r.B = B, r.T = T, r.H = H, r.d = d, r.pos0 = 0;
-        r.nl2t = rope_nl2t(rope->theta, d);
+        rope_tab(rope->theta, d, &r.w);
         const da_status st = launch_status(da::launch_rope_bf16(r, s));
         if (st != DA_OK) return st;
         (m ? k2 : k1) = da_in{dst, (int64_t)H * T * d, (int64_t)T * d, (int64_t)d};
@@ -265,7 +272,7 @@ static da_status v1_fwd_impl(int softmax1, da_dtype dtype, int B, int H, int T, 
     a.q1 = tin(q1), a.q2 = tin(q2), a.k1 = tin(k1), a.k2 = tin(k2), a.v = tin(v);
     if (rope) {
       a.rope = 1;
-      a.rope_nl2t = rope_nl2t(rope->theta, d);
+      rope_tab(rope->theta, d, &a.rope_w);
     }
     a.out = tout(out);
     a.lq1 = lam_q1, a.lk1 = lam_k1, a.lq2 = lam_q2, a.lk2 = lam_k2;
@@ -321,7 +328,7 @@ static da_status v2_fwd_impl(int softmax1, da_dtype dtype, int B, int T, int Hq,
     r.x = tin(k);
     r.out = TOut{rope->ws, (int64_t)T * Hkv * d, (int64_t)d, (int64_t)Hkv * d};
     r.B = B, r.T = T, r.H = Hkv, r.d = d, r.pos0 = 0;
-    r.nl2t = rope_nl2t(rope->theta, d);
+    rope_tab(rope->theta, d, &r.w);
     const da_status st = launch_status(da::launch_rope_bf16(r, (hipStream_t)stream));
     if (st != DA_OK) return st;
     k = da_in{rope->ws, (int64_t)T * Hkv * d, (int64_t)d, (int64_t)Hkv * d};
@@ -341,7 +348,7 @@ static da_status v2_fwd_impl(int softmax1, da_dtype dtype, int B, int T, int Hq,
   }
   if (rope) {
     a.rope = 1;
-    a.rope_nl2t = rope_nl2t(rope->theta, d);
+    rope_tab(rope->theta, d, &a.rope_w);
   }
   return launch_status(da::launch_prefill_v2_bf16(d, a, (hipStream_t)stream));
 }
@@ -650,13 +657,13 @@ da_status diffattn_rope(da_dtype dtype, int B, int T, int H, int d, da_in x, da_
   DA_TRY(check_in(x, 8));
   DA_TRY(check_out(out, 8));
   if (dtype != DA_BF16) return DA_E_UNSUPPORTED;
-  if (d % 8 != 0 || d > 4096) return DA_E_UNSUPPORTED;
+  if (d % 8 != 0 || d > 256) return DA_E_UNSUPPORTED;
   if (!grid_fits(((long long)B * T * H * (d / 4) + 255) / 256)) return DA_E_SHAPE;
   da::RopeArgs r{};
   r.x = tin(x);
   r.out = tout(out);
   r.B = B, r.T = T, r.H = H, r.d = d, r.pos0 = pos0;
-  r.nl2t = rope_nl2t(theta, d);
+  rope_tab(theta, d, &r.w);
   return launch_status(da::launch_rope_bf16(r, (hipStream_t)stream));
 }
 

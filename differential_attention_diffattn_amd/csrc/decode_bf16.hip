@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(kWaves * 64, NCB == 1 ? 1 : 2) decode_split_ke
     for (int ks = 0; ks < KS; ++ks)
       qf[n][ks] = as_bf16x8(valid ? *(const uint4*)(qrow + 32 * ks + 8 * kg) : make_uint4(0, 0, 0, 0));
     // rotary embedding of the new token at its cache position (elements 32 ks + 8 kg + e)
-    if (a.rope) rope_rotate_frags<KS, 32>(qf[n], 8 * kg, max(L - NQ + qi, 0), a.rope_nl2t);
+    if (a.rope) rope_rotate_frags<KS, 32>(qf[n], 8 * kg, max(L - NQ + qi, 0), a.rope_w);
   }
   const uint16_t* kbase = (const uint16_t*)a.k.p + (PAGED ? 0 : b * a.k.sb) + g * a.k.sh;
   const uint16_t* vbase = (const uint16_t*)a.v.p + (PAGED ? 0 : b * a.v.sb) + g * a.v.sh;

@@ -11,6 +11,13 @@
 
 namespace da {
 
+// Rotary-embedding frequencies w_c = theta^(-2c/d), c < d/2 (d <= 256), each
+// as an unevaluated sum hi + lo of two floats (computed on the host in
+// double), so a position times w_c keeps ~48 bits.
+struct RopeTab {
+  float hi[128], lo[128];
+};
+
 // Two causal softmax maps per wave over one shared V (V1), or one GQA
 // attention whose adjacent query heads are paired (V2).
 struct PrefillArgs {
@@ -39,9 +46,9 @@ struct PrefillArgs {
   TOut attn, attn2;
   float* lse;
   // rotary embedding of q in the prologue (rope != 0): row t of q turns by
-  // t * theta^(-2c/d); rope_nl2t = -2 log2(theta) / d
+  // t * w_c
   int rope;
-  float rope_nl2t;
+  RopeTab rope_w;
 };
 
 hipError_t launch_prefill_v1_bf16(int d, const PrefillArgs& a, hipStream_t s);
@@ -124,7 +131,7 @@ struct DecodeArgs {
   // rotary embedding of q (rope != 0): new token i sits at cache position
   // L_b - nq + i; the cache holds its keys rotated
   int rope;
-  float rope_nl2t;
+  RopeTab rope_w;
 };
 hipError_t launch_decode_bf16(int d, const DecodeArgs& a, hipStream_t s);
 
@@ -135,7 +142,7 @@ struct RopeArgs {
   TIn x;
   TOut out;
   int B, T, H, d, pos0;
-  float nl2t;
+  RopeTab w;
 };
 hipError_t launch_rope_bf16(const RopeArgs& a, hipStream_t s);
 struct LamProjArgs {

@@ -351,7 +351,7 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
   }
   if (a.rope) {  // rotary embedding of this wave's q rows (row i0w + li, elements 16 ks + 8 hg + e)
 #pragma unroll
-    for (int m = 0; m < MPW; ++m) rope_rotate_frags<KS, 16>(qf[m], 8 * hg, i0w + li, a.rope_nl2t);
+    for (int m = 0; m < MPW; ++m) rope_rotate_frags<KS, 16>(qf[m], 8 * hg, i0w + li, a.rope_w);
   }
 
   // ---- per-lane LDS bases (every stage / sub-block / map offset is an immediate) ----

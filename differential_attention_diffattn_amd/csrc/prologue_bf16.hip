@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(256) rope_kernel(const RopeArgs a) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     float sn, cs;
-    rope_sincos(a.pos0 + t, rope_freq(c + j, a.nl2t), &sn, &cs);
+    rope_sincos(a.pos0 + t, a.w.hi[c + j], a.w.lo[c + j], &sn, &cs);
     y1[j] = x1[j] * cs - x2[j] * sn;
     y2[j] = x2[j] * cs + x1[j] * sn;
   }

@@ -32,7 +32,8 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "v1", "v2", "v1_bwd", "v2_bwd", "decode", "decode_paged", "decode_multi"
+    kind: str  # "v1", "v2", "v2_rope", "v1_bwd", "v2_bwd", "decode", "decode_rope", "decode_paged",
+    #           "decode_multi", "lam_proj"
     dtype: str  # "fp32" or "bf16"
     B: int
     H: int = 0  # V1: differential heads
@@ -60,8 +61,10 @@ class Workload:
         the sequences' lengths in place of B*L)."""
         if self.kind == "v1":
             return 6.0 * self.B * self.H * self.d * self.T * (self.T + 1)
-        if self.kind == "v2":
+        if self.kind in ("v2", "v2_rope"):
             return 2.0 * self.B * self.Hq * self.d * self.T * (self.T + 1)
+        if self.kind == "lam_proj":  # x [B,T,dm] . w [P,dm]; here H holds dm and Hq holds P
+            return 2.0 * self.B * self.T * self.H * self.Hq
         if self.kind == "v2_bwd":  # 5 products (S, dP, dV, dK, dQ) over the unmasked pairs
             return 5.0 * self.B * self.Hq * self.d * self.T * (self.T + 1)
         if self.kind == "v1_bwd":  # per map S, dK, dQ over d and dP, dV over 2d: 14 d flops per pair and map
@@ -79,9 +82,11 @@ class Workload:
         if self.kind == "v1":
             B, H, T, d = self.B, self.H, self.T, self.d
             return e * (4 * B * H * T * d + B * H * T * 2 * d + B * T * H * 2 * d) + 4 * 4 * d
-        if self.kind == "v2":
+        if self.kind in ("v2", "v2_rope"):
             B, T, Hq, Hkv, d = self.B, self.T, self.Hq, self.Hkv, self.d
             return e * (B * T * Hq * d + 2 * B * T * Hkv * d + B * T * (Hq // 2) * d) + 4 * B * T * (Hq // 2)
+        if self.kind == "lam_proj":  # x and w read once, fp32 logits written once
+            return e * (self.B * self.T * self.H + self.Hq * self.H) + 4 * self.B * self.T * self.Hq
         if self.kind == "v1_bwd":  # q1 q2 k1 k2 v, attn1 attn2, dout, lse, 4 lambda vectors in; 5 grads + 4 out
             B, H, T, d = self.B, self.H, self.T, self.d
             return (e * (4 * B * H * T * d + B * H * T * 2 * d + 3 * B * T * H * 2 * d + 4 * B * H * T * d
@@ -121,6 +126,13 @@ WORKLOADS: Dict[str, Workload] = {
                  d=128, Hq=64, Hkv=8, seed=6, page=64),
         Workload("v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128", "decode_multi", "bf16", B=64, T=32768, d=128,
                  Hq=64, Hkv=8, seed=7, nq=4),
+        # rotary embedding fused (q in the kernel's prologue; prefill k rotated by a pass into a workspace)
+        Workload("v2_prefill_rope_B1_T8192_Hq64_Hkv8_d128", "v2_rope", "bf16", B=1, T=8192, d=128, Hq=64, Hkv=8,
+                 seed=4),
+        Workload("v2_decode_rope_B64_L32768_Hq64_Hkv8_d128", "decode_rope", "bf16", B=64, T=32768, d=128, Hq=64,
+                 Hkv=8, seed=5),
+        # V2 lambda projection at the V2 prefill shape: d_model = 32 pairs x 128 = 4096 (H = dm, Hq = pairs)
+        Workload("v2_lambda_proj_B1_T8192_dm4096_P32", "lam_proj", "bf16", B=1, T=8192, H=4096, Hq=32, seed=8),
     ]
 }
 
@@ -204,6 +216,15 @@ def decode_multi_inputs(B: int, L: int, nq: int, Hq: int, Hkv: int, d: int, dtyp
     }
 
 
+def lambda_proj_inputs(B: int, T: int, dm: int, P: int, dtype=torch.bfloat16, seed: int = 0,
+                       device="cpu") -> Dict[str, torch.Tensor]:
+    """x ``[B, T, dm]`` ~ N(0, 1) (a hidden state); w ``[P, dm]`` ~ N(0, 1/dm)
+    (a linear layer's weight at the usual initialisation scale)."""
+    g = _gen(seed, device)
+    return {"x": _randn((B, T, dm), g, device, dtype),
+            "w": _randn((P, dm), g, device, dtype, std=1.0 / dm ** 0.5)}
+
+
 def draw_seq_lens(B: int, max_len: int, seed: int) -> torch.Tensor:
     """Lengths uniform in [1, max_len], CPU int32 [B]."""
     g = torch.Generator().manual_seed(int(seed) + 7919)
@@ -251,8 +272,10 @@ def inputs_for(w: Workload, device="cpu") -> Dict[str, torch.Tensor]:
         x = v1_inputs(w.B, w.H, w.T, w.d, w.torch_dtype, w.seed, device)
         x["dout"] = _randn((w.B, w.T, w.H, 2 * w.d), _gen(w.seed + 99, device), device, w.torch_dtype)
         return x
-    if w.kind == "v2":
+    if w.kind in ("v2", "v2_rope"):
         return v2_inputs(w.B, w.T, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)
+    if w.kind == "lam_proj":
+        return lambda_proj_inputs(w.B, w.T, w.H, w.Hq, w.torch_dtype, w.seed, device)
     if w.kind == "v2_bwd":  # the prefill's inputs plus an output gradient dout ~ N(0, 1)
         x = v2_inputs(w.B, w.T, w.Hq, w.Hkv, w.d, w.torch_dtype, w.seed, device)
         x["dout"] = _randn((w.B, w.T, w.Hq // 2, w.d), _gen(w.seed + 99, device), device, w.torch_dtype)

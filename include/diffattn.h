@@ -416,7 +416,7 @@ da_status diffattn_v1_bwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, 
  *
  * diffattn_rope: rotate x, logical [B,T,H,d] bf16 (roles b, h, t), row t at
  *   position pos0 + t, into out (same logical shape; out == x rotates in
- *   place).  d a multiple of 8; pos0 >= 0 and pos0 + T < 2^24.  One
+ *   place).  d a multiple of 8, at most 256; pos0 >= 0 and pos0 + T < 2^24.  One
  *   HBM-bound kernel.  Use it for keys written into a cache, which the
  *   decode entry points below expect rotated.
  */

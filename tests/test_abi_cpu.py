@@ -303,6 +303,7 @@ def test_rope_validation(lib):
     assert f(out=_t(ptr=0, out=True)) == E_NULL
     assert f(dtype=0) == E_UNSUP
     assert f(d=12) == E_UNSUP                                 # multiples of 8
+    assert f(d=264) == E_UNSUP                                # at most 256 (128 frequencies)
 
 
 def test_prefill_rope_validation(lib):
