@@ -675,7 +675,7 @@ da_status diffattn_v2_lambda_proj(da_dtype dtype, int B, int T, int dm, int P, d
   DA_TRY(check_in(w, 8));
   DA_TRY(check_logits(out));
   if (dtype != DA_BF16) return DA_E_UNSUPPORTED;
-  if (dm % 64 != 0) return DA_E_UNSUPPORTED;
+  if (dm % 128 != 0) return DA_E_UNSUPPORTED;
   if (!grid_fits(((long long)B * T + 31) / 32 * ((P + 31) / 32))) return DA_E_SHAPE;
   da::LamProjArgs a{};
   a.x = tin(x);

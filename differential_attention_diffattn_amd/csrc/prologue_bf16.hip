@@ -12,9 +12,9 @@
 // Lambda projection ("Differential Transformer V2" article: a projected
 // lambda for each token and head): logits[b,t,p] = <x[b,t,:], w[p,:]>, w laid
 // out like a linear layer's weight [P, dm].  A workgroup owns 32 tokens x 32
-// pairs; its 4 waves split dm in four and each runs v_mfma_f32_32x32x16_bf16
-// over its quarter (A = 32 token rows of x, B = 32 rows of w, both 16-byte
-// loads straight from HBM / L2); the four partial tiles are added in a fixed
+// pairs; its 8 waves split dm in eight and each runs v_mfma_f32_32x32x16_bf16
+// over its part (A = 32 token rows of x, B = 32 rows of w, both 16-byte
+// loads straight from HBM / L2); the eight partial tiles are added in a fixed
 // order through LDS (deterministic).  It reads x once: HBM-bound.
 #include <math.h>
 
@@ -51,7 +51,7 @@ __global__ void __launch_bounds__(256) rope_kernel(const RopeArgs a) {
   *(uint32_t*)(orow + c + half) = pack_bf16x2(y2[0], y2[1]);
 }
 
-constexpr int kProjWaves = 4;
+constexpr int kProjWaves = 8;
 
 __global__ void __launch_bounds__(kProjWaves * 64) lambda_proj_kernel(const LamProjArgs a) {
   __shared__ f32x16 part[kProjWaves - 1][64];
@@ -66,21 +66,21 @@ __global__ void __launch_bounds__(kProjWaves * 64) lambda_proj_kernel(const LamP
   const int rb = (int)(r / a.T), rt = (int)(r % a.T);
   const uint16_t* xr = (const uint16_t*)a.x.p + rb * a.x.sb + (int64_t)rt * a.x.st;
   const uint16_t* wr = (const uint16_t*)a.w.p + (int64_t)min(p0 + li, a.P - 1) * a.w.sh;
-  const int kq = a.dm / kProjWaves;  // this wave's quarter of dm (a multiple of 16)
+  const int kq = a.dm / kProjWaves;  // this wave's part of dm (a multiple of 16)
   const int k0 = wave * kq;
   f32x16 acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
   int k = k0;
-  for (; k + 64 <= k0 + kq; k += 64) {  // four k-steps per round: eight 16-byte loads in flight
-    bf16x8 xa[4], wb[4];
+  for (; k + 128 <= k0 + kq; k += 128) {  // eight k-steps per round: sixteen 16-byte loads in flight
+    bf16x8 xa[8], wb[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 8; ++j) {
       xa[j] = as_bf16x8(*(const uint4*)(xr + k + 16 * j + 8 * hg));
       wb[j] = as_bf16x8(*(const uint4*)(wr + k + 16 * j + 8 * hg));
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc = mfma32x32x16(xa[j], wb[j], acc);
+    for (int j = 0; j < 8; ++j) acc = mfma32x32x16(xa[j], wb[j], acc);
   }
   for (; k < k0 + kq; k += 16)
     acc = mfma32x32x16(as_bf16x8(*(const uint4*)(xr + k + 8 * hg)), as_bf16x8(*(const uint4*)(wr + k + 8 * hg)),

@@ -471,7 +471,7 @@ da_status diffattn_v2_decode_paged_rope(da_dtype dtype, int B, int max_len, int 
  *   w    logical [P,dm] bf16, a linear layer's weight (the pair stride in sh;
  *        sb, st unused).
  *   out  logical [B,T,P] fp32 (roles b, h = pair, t), 4-byte aligned.
- *   dm a multiple of 64 (DA_E_UNSUPPORTED otherwise).  One kernel, MFMA,
+ *   dm a multiple of 128 (DA_E_UNSUPPORTED otherwise).  One kernel, MFMA,
  *   reads x once; sums over dm in a fixed order (deterministic).
  */
 da_status diffattn_v2_lambda_proj(da_dtype dtype, int B, int T, int dm, int P, da_in x, da_in w, da_in out,

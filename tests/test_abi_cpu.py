@@ -333,7 +333,8 @@ def test_decode_rope_validation(lib):
 def test_lambda_proj_validation(lib):
     f = lambda dtype=1, dm=4096, out=FAKE: lib.diffattn_v2_lambda_proj(dtype, 1, 16, dm, 32, _t(), _t(),
                                                                         DaIn(out, 0, 4, 128), None)
-    assert f(dm=100) == E_UNSUP                               # multiples of 64
+    assert f(dm=100) == E_UNSUP                               # multiples of 128
+    assert f(dm=192) == E_UNSUP
     assert f(dtype=0) == E_UNSUP
     assert f(out=0) == E_NULL
     assert f(out=FAKE + 2) == E_LAYOUT
