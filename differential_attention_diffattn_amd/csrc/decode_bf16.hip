@@ -72,25 +72,43 @@ __global__ void __launch_bounds__(kWaves * 64, NCB == 1 ? 1 : 2) decode_split_ke
   //    head, then virtual sequence (with nsplit a multiple of 8, XCD x takes
   //    the splits s = x mod 8 of every (vb, g)).
   //  * paged (ragged lengths: the late splits of short sequences are empty):
-  //    the dense order would give the XCDs holding the early splits most of
-  //    the work.  A "unit" is one split of one virtual sequence; units are
-  //    numbered split-major with the sequence index rotated by the split, all
-  //    kv heads of a unit go to one XCD, and XCD x takes every 8th unit, so
-  //    each XCD gets every split of a spread of sequences.  The grid is
-  //    padded to a multiple of 8 units.
-  // Measured on MI355X: the paged order is 1.46x the dense order's rate on a
-  // ragged batch (lengths uniform in [1, 32768]); the dense order is 1.06x
-  // the paged order's on uniform lengths.
+  //    only the non-empty splits get workgroups.  They are numbered in one
+  //    packed list, virtual sequence by virtual sequence (split s of vb is
+  //    unit prefix(vb) + s, prefix = the number of non-empty splits before
+  //    vb, found from the lengths with a wave-wide scan); unit u takes
+  //    workgroups Hkv u .. Hkv u + Hkv - 1, one per kv head, and the
+  //    workgroups past the last unit exit at once.  So the workgroups with
+  //    work are the first ones dispatched, dealt evenly over XCDs and CUs.
   const int bid = blockIdx.x;
   const int VB = a.B * a.ncg;
   int vb, g, s;
   if constexpr (PAGED) {
-    const int xcd = bid & 7, j = bid >> 3;
-    g = j % a.Hkv;
-    const int unit = (j / a.Hkv) * 8 + xcd;
-    if (unit >= VB * a.nsplit) return;  // padding (uniform over the workgroup)
-    s = unit / VB;
-    vb = (unit % VB + s) % VB;
+    const int u = bid / a.Hkv;
+    g = bid % a.Hkv;
+    vb = -1;
+    s = 0;
+    int done = 0;  // units in the virtual sequences before this 64-wide window
+    for (int base = 0; base < VB; base += 64) {
+      const int v = base + lane;
+      int ns = 0;
+      if (v < VB) ns = (min(max(a.seq_lens[v / a.ncg], 0), a.L) + a.chunk - 1) / a.chunk;
+      int inc = ns;  // inclusive scan over the window
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
+      }
+      const int first = done + inc - ns;  // this lane's first unit
+      const unsigned long long hit = __ballot(u >= first && u < first + ns);
+      if (hit) {  // wave-uniform
+        const int l = __ffsll((long long)hit) - 1;
+        vb = base + l;
+        s = u - __shfl(first, l, 64);
+        break;
+      }
+      done += __shfl(inc, 63, 64);
+    }
+    if (vb < 0) return;  // past the last unit (uniform over the workgroup)
   } else {
     if (bid >= VB * a.Hkv * a.nsplit) return;  // padding
     s = bid % a.nsplit;
@@ -326,14 +344,17 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(const DecodeArgs a) {
     const int g = head / G, col = qi * G + head % G;
     const float* base = a.ws + ((int64_t)b * a.Hkv + g) * a.nsplit * (int64_t)NC * (D + 2) + (int64_t)col * (D + 2);
     const int64_t sstride = (int64_t)NC * (D + 2);
+    // splits of this sequence that hold entries (paged: the others have no
+    // workgroup and no partial)
+    const int ns = a.block_table ? (min(max(a.seq_lens[b], 0), a.L) + a.chunk - 1) / a.chunk : a.nsplit;
     float M = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, base[s * sstride]);
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, base[s * sstride]);
     if (M == -INFINITY) {  // no visible entry at all (e.g. a paged sequence of length 0): no contribution
       res[k] = 0.f;
       continue;
     }
     float l = 0.f, acc = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) {
+    for (int s = 0; s < ns; ++s) {
       const float f = exp2f(base[s * sstride] - M);
       l += base[s * sstride + 1] * f;
       acc += base[s * sstride + 2 + c] * f;
