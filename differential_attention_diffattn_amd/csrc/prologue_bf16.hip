@@ -20,6 +20,7 @@
 
 #include "kernels.hpp"
 #include "rope.hpp"
+#include "tile_ops.hpp"
 
 namespace da {
 namespace {
@@ -107,6 +108,113 @@ __global__ void __launch_bounds__(kProjWaves * 64) lambda_proj_kernel(const LamP
   }
 }
 
+// Streaming form for dm a multiple of 256: a workgroup (4 waves) owns 32
+// tokens x 32 pairs and walks dm in 256-wide chunks.  Each chunk's x rows
+// (32 x 512 B) and w rows (32 x 512 B) go HBM -> LDS by global_load_lds, two
+// whole rows per 1 KB instruction (fully coalesced), into a 4-stage ring with
+// three chunks in flight (the stream is latency-bound otherwise); 16-byte
+// chunk c of a row lands at chunk c ^ (row & 15), so the MFMA operand reads
+// (ds_read_b128, 16 rows per pass) hit distinct banks.  Wave w runs k-steps
+// 4w .. 4w+3 of each chunk; the four partial tiles are added in a fixed order
+// at the end.
+constexpr int kPsWaves = 4, kPsChunk = 256, kPsStages = 4;  // dm per chunk
+constexpr int kPsRowBytes = kPsChunk * 2;    // 512 B
+constexpr int kPsTile = 32 * kPsRowBytes;    // 16 KB: one operand tile of a chunk
+constexpr int kPsStage = 2 * kPsTile;        // x tile, w tile
+constexpr int kPsCopies = 2 * 16 / kPsWaves; // 1 KB copies per wave per chunk (8)
+
+__global__ void __launch_bounds__(kPsWaves * 64) lambda_proj_stream_kernel(const LamProjArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kPsStages * kPsStage];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int li = lane & 31, hg = lane >> 5;
+  const int ptiles = (a.P + 31) / 32;
+  const long long r0 = (long long)(blockIdx.x / ptiles) * 32;  // first token (flattened b * T + t)
+  const int p0 = (blockIdx.x % ptiles) * 32;
+  const long long ntok = (long long)a.B * a.T;
+  const int nch = a.dm / kPsChunk;
+  // Copy i of wave w moves rows 2(4w + i) and 2(4w + i) + 1 (lanes 0-31 and
+  // 32-63) of the x tile and of the w tile (rows past the end clamped to the
+  // last token / pair: finite, masked at the store).  The two rows' bases
+  // differ per lane half: a copy takes the lower one as its scalar base and
+  // adds each half's distance to the lane offset (the launcher uses this
+  // kernel only when every distance between rows fits in 31 bits).  Bases and
+  // distances do not depend on the chunk, so they are formed once.
+  const char* xb[kPsCopies / 2];
+  const char* wb[kPsCopies / 2];
+  uint32_t xd[kPsCopies / 2], wd[kPsCopies / 2];
+#pragma unroll
+  for (int i = 0; i < kPsCopies / 2; ++i) {
+    const int rp = 2 * (4 * wave + i);  // first row of the pair (uniform)
+    const long long t0 = min(r0 + rp, ntok - 1), t1 = min(r0 + rp + 1, ntok - 1);
+    const char* x0 = (const char*)((const uint16_t*)a.x.p + (t0 / a.T) * a.x.sb + (int64_t)(t0 % a.T) * a.x.st);
+    const char* x1 = (const char*)((const uint16_t*)a.x.p + (t1 / a.T) * a.x.sb + (int64_t)(t1 % a.T) * a.x.st);
+    xb[i] = x0 < x1 ? x0 : x1;
+    xd[i] = (uint32_t)((hg ? x1 : x0) - xb[i]);
+    wb[i] = (const char*)((const uint16_t*)a.w.p + (int64_t)min(p0 + rp, a.P - 1) * a.w.sh);
+    const char* w1 = (const char*)((const uint16_t*)a.w.p + (int64_t)min(p0 + rp + 1, a.P - 1) * a.w.sh);
+    wd[i] = (uint32_t)((hg ? w1 : wb[i]) - wb[i]);
+  }
+  auto issue = [&](int ch, int stage) {
+    const uint32_t st = lds0 + stage * kPsStage;
+#pragma unroll
+    for (int i = 0; i < kPsCopies / 2; ++i) {
+      const int rp = 2 * (4 * wave + i);
+      const uint32_t off = (uint32_t)ch * kPsRowBytes + (uint32_t)((li ^ ((rp + hg) & 15)) << 4);
+      dma16_sbase(xb[i], off + xd[i], st + rp * kPsRowBytes);
+      dma16_sbase(wb[i], off + wd[i], st + kPsTile + rp * kPsRowBytes);
+    }
+  };
+  for (int c = 0; c < kPsStages - 1 && c < nch; ++c) issue(c, c);
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  const uint32_t rrow = li * kPsRowBytes;
+  for (int ch = 0; ch < nch; ++ch) {
+    const int stage = ch % kPsStages;
+    // this wave's copies of chunk ch landed (later chunks may stay in flight)
+    const int later = min(kPsStages - 2, nch - 1 - ch);
+    if (later >= 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPsCopies) : "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPsCopies) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave's copies of chunk ch landed; stage (ch - 1) % 4 is free
+    if (ch + kPsStages - 1 < nch) issue(ch + kPsStages - 1, (ch + kPsStages - 1) % kPsStages);
+    const uint32_t st = lds0 + stage * kPsStage;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = 2 * (4 * wave + j) + hg;  // 16-byte chunk of the row this lane's half reads
+      const uint32_t o = rrow + (uint32_t)((q ^ (li & 15)) << 4);
+      acc = mfma32x32x16(lds_read16(st + o), lds_read16(st + kPsTile + o), acc);
+    }
+  }
+  // fixed-order reduction of the four partial tiles through LDS
+  __syncthreads();  // every wave is done with the stages
+  f32x16* part = (f32x16*)smem;
+  if (wave > 0) part[(wave - 1) * 64 + lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kPsWaves - 1; ++w) {
+    const f32x16 x = part[w * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += x[i];
+  }
+  // register i: token r0 + 8(i>>2) + 4hg + (i&3), pair p0 + li
+  const int p = p0 + li;
+  if (p >= a.P) return;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const long long tok = r0 + 8 * (i >> 2) + 4 * hg + (i & 3);
+    if (tok < ntok) {
+      const int ob = (int)(tok / a.T), ot = (int)(tok % a.T);
+      ((float*)a.out.p)[ob * a.out.sb + (int64_t)ot * a.out.st + (int64_t)p * a.out.sh] = acc[i];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rope_bf16(const RopeArgs& a, hipStream_t s) {
@@ -119,6 +227,13 @@ hipError_t launch_rope_bf16(const RopeArgs& a, hipStream_t s) {
 hipError_t launch_lambda_proj_bf16(const LamProjArgs& a, hipStream_t s) {
   const void* args[] = {&a};
   const long long tiles = ((long long)a.B * a.T + 31) / 32 * ((a.P + 31) / 32);
+  // the streaming kernel addresses rows of x and of w by 32-bit byte
+  // distances from a per-copy base
+  const long long xspan = ((long long)(a.B - 1) * a.x.sb + (long long)(a.T - 1) * a.x.st + a.dm) * 2;
+  const long long wspan = ((long long)(a.P - 1) * a.w.sh + a.dm) * 2;
+  if (a.dm % kPsChunk == 0 && xspan < (1LL << 31) && wspan < (1LL << 31))
+    return hipLaunchKernel((const void*)lambda_proj_stream_kernel, dim3((unsigned)tiles), dim3(kPsWaves * 64),
+                           (void**)args, 0, s);
   return hipLaunchKernel((const void*)lambda_proj_kernel, dim3((unsigned)tiles), dim3(kProjWaves * 64),
                          (void**)args, 0, s);
 }
