@@ -194,16 +194,20 @@ def _cpu_baseline(w, x, min_seconds=10.0, max_seconds=30.0, softmax1=False):
 
 
 def _source_sha(kind):
-    """sha256 of the HIP source a kernel is built from; a traffic figure taken
-    from hardware counters only applies to the kernel it was measured on."""
+    """sha256 of the HIP source(s) a workload's kernels are built from; a
+    traffic figure taken from hardware counters only applies to the kernels it
+    was measured on."""
     import hashlib
 
-    src = {"v1": "prefill_bf16.hip", "v2": "prefill_bf16.hip", "v2_rope": "prefill_bf16.hip",
-           "v1_bwd": "backward_bf16.hip", "v2_bwd": "backward_bf16.hip", "decode": "decode_bf16.hip",
-           "decode_rope": "decode_bf16.hip", "lam_proj": "prologue_bf16.hip",
-           "decode_paged": "decode_bf16.hip", "decode_multi": "decode_bf16.hip"}[kind]
-    path = os.path.join(ROOT, "differential_attention_diffattn_amd", "csrc", src)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+    src = {"v1": ["prefill_bf16.hip"], "v2": ["prefill_bf16.hip"],
+           "v2_rope": ["prologue_bf16.hip", "rope.hpp", "prefill_bf16.hip"],
+           "v1_bwd": ["backward_bf16.hip"], "v2_bwd": ["backward_bf16.hip"], "decode": ["decode_bf16.hip"],
+           "decode_rope": ["rope.hpp", "decode_bf16.hip"], "lam_proj": ["prologue_bf16.hip"],
+           "decode_paged": ["decode_bf16.hip"], "decode_multi": ["decode_bf16.hip"]}[kind]
+    h = hashlib.sha256()
+    for f in src:
+        h.update(open(os.path.join(ROOT, "differential_attention_diffattn_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
 
 
 def _traffic(w):
@@ -280,7 +284,10 @@ def write_traffic(pmc_dir):
                         ("v1_backward_B8_H6_T1024_d64", V1_BWD_KERNELS), ("v1_backward_B2_H12_T4096_d128", V1_BWD_KERNELS),
                         ("v2_decode_B64_L32768_Hq64_Hkv8_d128", "decode_split_kernel"),
                         ("v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128", "decode_split_kernel"),
-                        ("v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128", "decode_split_kernel")]:
+                        ("v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128", "decode_split_kernel"),
+                        ("v2_prefill_rope_B1_T8192_Hq64_Hkv8_d128", "rope_kernel|prefill_kernel"),
+                        ("v2_decode_rope_B64_L32768_Hq64_Hkv8_d128", "decode_split_kernel"),
+                        ("v2_lambda_proj_B1_T8192_dm4096_P32", "lambda_proj")]:
         w = workloads.WORKLOADS[name]
         fk = per_dispatch(name, "FETCH_SIZE", match)
         wk = per_dispatch(name, "WRITE_SIZE", match)
