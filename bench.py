@@ -417,8 +417,8 @@ def main():
     if args.only == "copy":
         print(json.dumps(_copy_calibration(torch, args.steps)))
         return
-    if args.only:
-        _, _, res = measure(args.only, args.steps, args.warmup)
+    if args.only:  # at least 8 launches per step, as in the default run
+        _, _, res = measure(args.only, args.steps, args.warmup, calls_per_step=8)
         print(json.dumps(res))
         return
 

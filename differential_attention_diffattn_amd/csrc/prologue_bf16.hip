@@ -116,7 +116,10 @@ __global__ void __launch_bounds__(kProjWaves * 64) lambda_proj_kernel(const LamP
 // chunk c of a row lands at chunk c ^ (row & 15), so the MFMA operand reads
 // (ds_read_b128, 16 rows per pass) hit distinct banks.  Wave w runs k-steps
 // 4w .. 4w+3 of each chunk; the four partial tiles are added in a fixed order
-// at the end.
+// at the end.  Workgroups walk the chunks in rotated order (workgroup k of
+// an XCD starts at chunk k mod n): when every workgroup read the same columns
+// at the same time, the rows' 8 KB stride kept the reads on a few memory
+// channels and the kernel ran at two thirds of the rate it reaches rotated.
 constexpr int kPsWaves = 4, kPsChunk = 256, kPsStages = 4;  // dm per chunk
 constexpr int kPsRowBytes = kPsChunk * 2;    // 512 B
 constexpr int kPsTile = 32 * kPsRowBytes;    // 16 KB: one operand tile of a chunk
@@ -133,6 +136,7 @@ __global__ void __launch_bounds__(kPsWaves * 64) lambda_proj_stream_kernel(const
   const int p0 = (blockIdx.x % ptiles) * 32;
   const long long ntok = (long long)a.B * a.T;
   const int nch = a.dm / kPsChunk;
+  const int rot = (int)((blockIdx.x / 8) % (unsigned)nch);  // workgroups of one XCD: consecutive k
   // Copy i of wave w moves rows 2(4w + i) and 2(4w + i) + 1 (lanes 0-31 and
   // 32-63) of the x tile and of the w tile (rows past the end clamped to the
   // last token / pair: finite, masked at the store).  The two rows' bases
@@ -160,7 +164,8 @@ __global__ void __launch_bounds__(kPsWaves * 64) lambda_proj_stream_kernel(const
 #pragma unroll
     for (int i = 0; i < kPsCopies / 2; ++i) {
       const int rp = 2 * (4 * wave + i);
-      const uint32_t off = (uint32_t)ch * kPsRowBytes + (uint32_t)((li ^ ((rp + hg) & 15)) << 4);
+      const int chr = ch + rot < nch ? ch + rot : ch + rot - nch;  // chunk of the rotated order
+      const uint32_t off = (uint32_t)chr * kPsRowBytes + (uint32_t)((li ^ ((rp + hg) & 15)) << 4);
       dma16_sbase(xb[i], off + xd[i], st + rp * kPsRowBytes);
       dma16_sbase(wb[i], off + wd[i], st + kPsTile + rp * kPsRowBytes);
     }
