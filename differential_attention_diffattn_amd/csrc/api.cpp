@@ -436,7 +436,7 @@ static da_status v1_bwd_impl(da_dtype dtype, int B, int H, int T, int d, da_in q
   const V1BwdWs w = v1_bwd_ws(B, H, T, d);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.total()) return DA_E_WORKSPACE;
   const int qt = (T + 127) / 128;
-  if (!grid_fits((long long)B * H * 2 * qt) || !grid_fits(((long long)B * da::backward_padded_rows(T) * H + 3) / 4))
+  if (!grid_fits((long long)B * H * 2 * qt) || !grid_fits(((long long)B * da::backward_padded_rows(T) * H + 15) / 16))
     return DA_E_SHAPE;
 
   da::V1BwdArgs a{};

@@ -480,22 +480,21 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
 // dQ of each map (the V2 dQ code with a 2d-wide v), dK of each map and dV
 // over both maps.
 
-// One wave per (b, t, h), t < Tp.
+// Sum over the 16 lanes of a row (lanes 16k .. 16k + 15).
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 16);
+  return v;
+}
+
+// Sixteen lanes per (b, t, h), t < Tp: each lane holds 2d/16 consecutive
+// channels (16-byte loads and stores), four items per wave with consecutive
+// heads, so a wave reads and writes whole contiguous spans of [B, T, H, 2d].
 template <int D>
 __global__ void __launch_bounds__(256) bwd_v1_pre_kernel(const V1BwdArgs a) {
-  constexpr int DV = 2 * D, PL = DV / 64;
-  const int lane = threadIdx.x & 63;
-  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, t, h)
-  if (item >= (long long)a.B * a.Tp * a.H) return;
-  const int h = (int)(item % a.H);
-  const int t = (int)((item / a.H) % a.Tp);
-  const int b = (int)(item / ((long long)a.H * a.Tp));
-  const int64_t rw = ((int64_t)b * a.H + h) * a.Tp + t;
-  if (t >= a.T) {  // padding rows: zero D and lse (masked where read)
-    if (lane == 0) a.Dw[0][rw] = a.Dw[1][rw] = a.lsew[0][rw] = a.lsew[1][rw] = 0.f;
-    return;
-  }
-  // lambda from the vectors (D / 64 elements per lane)
+  constexpr int DV = 2 * D, NV = DV / 128;  // 16-byte vectors (8 channels) per lane
+  const int lane = threadIdx.x & 63, l16 = lane & 15;
+  // lambda from the vectors (D / 64 elements per lane), once per wave
   float pa = 0.f, pb = 0.f;
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
@@ -504,42 +503,68 @@ __global__ void __launch_bounds__(256) bwd_v1_pre_kernel(const V1BwdArgs a) {
     pb += a.lq2[c] * a.lk2[c];
   }
   const float lam = expf(wave_sum(pa)) - expf(wave_sum(pb)) + a.lam_init;
+  const long long item = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);  // (b, t, h)
+  if (item >= (long long)a.B * a.Tp * a.H) return;  // whole rows of 16 lanes
+  const int h = (int)(item % a.H);
+  const int t = (int)((item / a.H) % a.Tp);
+  const int b = (int)(item / ((long long)a.H * a.Tp));
+  const int64_t rw = ((int64_t)b * a.H + h) * a.Tp + t;
+  if (t >= a.T) {  // padding rows: zero D and lse (masked where read)
+    if (l16 == 0) a.Dw[0][rw] = a.Dw[1][rw] = a.lsew[0][rw] = a.lsew[1][rw] = 0.f;
+    return;
+  }
   const uint16_t* gp = (const uint16_t*)a.dout.p + b * a.dout.sb + (int64_t)t * a.dout.st + h * a.dout.sh;
   const uint16_t* a0 = (const uint16_t*)a.a[0].p + b * a.a[0].sb + (int64_t)t * a.a[0].st + h * a.a[0].sh;
   const uint16_t* a1 = (const uint16_t*)a.a[1].p + b * a.a[1].sb + (int64_t)t * a.a[1].st + h * a.a[1].sh;
-  float g[PL], x0[PL], x1[PL], dd[PL], ss = 0.f, gd = 0.f;
+  uint4 gv[NV], xv0[NV], xv1[NV];
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int c = lane + 64 * i;
-    g[i] = bf16_to_f32(gp[c]);
-    x0[i] = bf16_to_f32(a0[c]);
-    x1[i] = bf16_to_f32(a1[c]);
-    dd[i] = x0[i] - lam * x1[i];  // D
-    ss += dd[i] * dd[i];
-    gd += g[i] * dd[i];
+  for (int v = 0; v < NV; ++v) {  // channels 128 v + 8 l16 .. + 7
+    const int c = 128 * v + 8 * l16;
+    gv[v] = *(const uint4*)(gp + c);
+    xv0[v] = *(const uint4*)(a0 + c);
+    xv1[v] = *(const uint4*)(a1 + c);
   }
-  const float r = rsqrtf(wave_sum(ss) * (1.f / DV) + 1e-5f);
-  const float pm = r * r * wave_sum(gd) * (1.f / DV);
+  auto elem = [](const uint4& u, int e) {  // channel e of a 16-byte vector
+    const uint32_t w = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+    return __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
+  };
+  float dd[NV][8], ss = 0.f, gd = 0.f;
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      dd[v][e] = elem(xv0[v], e) - lam * elem(xv1[v], e);  // D
+      ss += dd[v][e] * dd[v][e];
+      gd += elem(gv[v], e) * dd[v][e];
+    }
+  const float r = rsqrtf(row16_sum(ss) * (1.f / DV) + 1e-5f);
+  const float pm = r * r * row16_sum(gd) * (1.f / DV);
   const float cr = (1.f - a.lam_init) * r;
   uint16_t* d0 = a.dA[0] + (((int64_t)b * a.T + t) * a.H + h) * DV;
   uint16_t* d1 = a.dA[1] + (((int64_t)b * a.T + t) * a.H + h) * DV;
   float s0 = 0.f, s1 = 0.f, sl = 0.f;
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int c = lane + 64 * i;
-    const float dD = cr * (g[i] - dd[i] * pm);
-    const uint32_t w0 = pack_bf16x2(dD, 0.f) & 0xffffu, w1 = pack_bf16x2(-lam * dD, 0.f) & 0xffffu;
-    d0[c] = (uint16_t)w0;
-    d1[c] = (uint16_t)w1;
-    // D_m from the rounded d a_m the MFMAs see
-    s0 += bf16_to_f32((uint16_t)w0) * x0[i];
-    s1 += bf16_to_f32((uint16_t)w1) * x1[i];
-    sl -= dD * x1[i];
+  for (int v = 0; v < NV; ++v) {
+    uint32_t w0[4], w1[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float dA = cr * (elem(gv[v], e) - dd[v][e] * pm), dB = cr * (elem(gv[v], e + 1) - dd[v][e + 1] * pm);
+      w0[e / 2] = pack_bf16x2(dA, dB);
+      w1[e / 2] = pack_bf16x2(-lam * dA, -lam * dB);
+      // D_m from the rounded d a_m the MFMAs see
+      const uint4 r0 = make_uint4(w0[e / 2], 0, 0, 0), r1 = make_uint4(w1[e / 2], 0, 0, 0);
+      s0 += elem(r0, 0) * elem(xv0[v], e) + elem(r0, 1) * elem(xv0[v], e + 1);
+      s1 += elem(r1, 0) * elem(xv1[v], e) + elem(r1, 1) * elem(xv1[v], e + 1);
+      sl -= dA * elem(xv1[v], e) + dB * elem(xv1[v], e + 1);
+    }
+    const int c = 128 * v + 8 * l16;
+    *(uint4*)(d0 + c) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+    *(uint4*)(d1 + c) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
   }
-  s0 = wave_sum(s0);
-  s1 = wave_sum(s1);
-  sl = wave_sum(sl);
-  if (lane == 0) {
+  s0 = row16_sum(s0);
+  s1 = row16_sum(s1);
+  sl = row16_sum(sl);
+  if (l16 == 0) {
     a.Dw[0][rw] = s0;
     a.Dw[1][rw] = s1;
     a.lsew[0][rw] = a.lse[(((int64_t)0 * a.B + b) * a.H + h) * a.T + t];
@@ -891,7 +916,7 @@ template <int D>
 hipError_t launch_v1(const V1BwdArgs& a, hipStream_t st) {
   const void* args[] = {&a};
   const long long items = (long long)a.B * a.Tp * a.H;
-  hipError_t e = hipLaunchKernel((const void*)bwd_v1_pre_kernel<D>, dim3((unsigned)((items + 3) / 4)), dim3(256),
+  hipError_t e = hipLaunchKernel((const void*)bwd_v1_pre_kernel<D>, dim3((unsigned)((items + 15) / 16)), dim3(256),
                                  (void**)args, 0, st);
   if (e != hipSuccess) return e;
   const int qt = (a.T + 32 * kNW - 1) / (32 * kNW);
