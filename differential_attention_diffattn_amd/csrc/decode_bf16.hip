@@ -347,13 +347,17 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(const DecodeArgs a) {
     // splits of this sequence that hold entries (paged: the others have no
     // workgroup and no partial)
     const int ns = a.block_table ? (min(max(a.seq_lens[b], 0), a.L) + a.chunk - 1) / a.chunk : a.nsplit;
+    // (loops unrolled by 8: a batch's loads are in flight together instead of
+    // one memory latency per split)
     float M = -INFINITY;
+#pragma unroll 8
     for (int s = 0; s < ns; ++s) M = fmaxf(M, base[s * sstride]);
     if (M == -INFINITY) {  // no visible entry at all (e.g. a paged sequence of length 0): no contribution
       res[k] = 0.f;
       continue;
     }
     float l = 0.f, acc = 0.f;
+#pragma unroll 8
     for (int s = 0; s < ns; ++s) {
       const float f = exp2f(base[s * sstride] - M);
       l += base[s * sstride + 1] * f;
