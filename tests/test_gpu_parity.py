@@ -674,6 +674,39 @@ def test_softmax1_decode_equals_last_prefill_row():
     assert_bf16_close(dec, host64(pre[:, -1]), "softmax1 decode vs prefill last row")
 
 
+def test_v2_fused_qkv_and_head_major_cache_layouts_are_bitwise_equal():
+    """Layouts callers hand over as views: V2 q, k, v sliced out of one fused
+    projection output [B, T, Hq + 2 Hkv, d] (token stride (Hq + 2 Hkv) d), an
+    output written into a wider buffer, and a decode cache stored head-major
+    [B, Hkv, L, d] passed as a [B, L, Hkv, d] view.  The kernels read the same
+    values in the same order, so the results equal the contiguous ones bit
+    for bit; the contiguous ones are checked against the oracle."""
+    B, T, Hq, Hkv, d = 2, 190, 8, 2, 128
+    g = torch.Generator(device=DEV).manual_seed(4300)
+    qkv = torch.randn((B, T, Hq + 2 * Hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    lam = torch.randn((B, T, Hq // 2), generator=g, device=DEV)
+    q, k, v = qkv[:, :, :Hq], qkv[:, :, Hq:Hq + Hkv], qkv[:, :, Hq + Hkv:]
+    wide = torch.zeros((B, T, Hq // 2 + 3, d), dtype=torch.bfloat16, device=DEV)
+    a = binding.v2_fwd(q, k, v, lam, out=wide[:, :, 1:1 + Hq // 2])
+    torch.cuda.synchronize()
+    c = _v2_run({"q": q.contiguous(), "k": k.contiguous(), "v": v.contiguous(), "lam": lam})
+    assert torch.equal(a, c)
+    assert torch.count_nonzero(wide[:, :, 0]) == 0 and torch.count_nonzero(wide[:, :, 1 + Hq // 2:]) == 0
+    assert_bf16_close(c, oracle.v2_fwd(q.cpu(), k.cpu(), v.cpu(), lam.cpu()), "contiguous V2")
+
+    Bd, L = 3, 2500
+    kh = torch.randn((Bd, Hkv, L, d), generator=g, device=DEV).to(torch.bfloat16)
+    vh = torch.randn((Bd, Hkv, L, d), generator=g, device=DEV).to(torch.bfloat16)
+    z = {"q": torch.randn((Bd, Hq, d), generator=g, device=DEV).to(torch.bfloat16),
+         "k": kh.transpose(1, 2), "v": vh.transpose(1, 2),
+         "lam": torch.randn((Bd, Hq // 2), generator=g, device=DEV)}
+    a = _dec_run(z)
+    zc = dict(z, k=z["k"].contiguous(), v=z["v"].contiguous())
+    c = _dec_run(zc)
+    assert torch.equal(a, c)
+    assert_bf16_close(c, oracle.v2_decode(*[zc[n].cpu() for n in ("q", "k", "v", "lam")]), "contiguous decode")
+
+
 def test_graph_replay_matches_eager():
     """The benchmark replays one step captured as a HIP graph (12 V1 layer
     calls, a V2 prefill and a decode).  Every replay, with eager work and a
