@@ -4,8 +4,9 @@
 // Rotary embedding (rope.hpp: the rotate-half arrangement Wilsontomass's
 // module in the nanoGPT issue "How best to implement a differential
 // transformer?" applies to every q and k head): an HBM-bound pass, one thread
-// per two adjacent pairs (c, c+1) <-> (c + d/2, c + d/2 + 1), 4-byte loads and
-// stores; in place or out of place.  The prefill and decode kernels rotate q
+// per eight consecutive pairs (c .. c+7) <-> (c + d/2 .. c + d/2 + 7) with
+// 16-byte loads and stores (two pairs and 4-byte accesses when d/2 is not a
+// multiple of 8); in place or out of place.  The prefill and decode kernels rotate q
 // themselves (prologue, registers); this pass is for k, whose tiles go from
 // HBM straight to LDS and are read by several workgroups each.
 //
@@ -18,6 +19,8 @@
 // order through LDS (deterministic).  It reads x once: HBM-bound.
 #include <math.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "rope.hpp"
 #include "tile_ops.hpp"
@@ -25,31 +28,43 @@
 namespace da {
 namespace {
 
+// VW consecutive pairs per thread: elements c .. c + VW - 1 and the same
+// span of the second half (16-byte loads and stores when VW = 8).
+template <int VW>
 __global__ void __launch_bounds__(256) rope_kernel(const RopeArgs a) {
-  const int tpr = a.d / 4;  // threads per row
+  using Vec = typename std::conditional<VW == 8, uint4, uint32_t>::type;
+  const int half = a.d / 2;
+  const int tpr = half / VW;  // threads per row
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = gid / tpr;
   if (row >= (long long)a.B * a.T * a.H) return;
-  const int c = 2 * (int)(gid % tpr);  // pairs (c, c + d/2) and (c + 1, c + 1 + d/2)
+  const int c = VW * (int)(gid % tpr);
   const int h = (int)(row % a.H);
   const int t = (int)((row / a.H) % a.T);
   const int b = (int)(row / ((long long)a.H * a.T));
   const uint16_t* xr = (const uint16_t*)a.x.p + b * a.x.sb + (int64_t)t * a.x.st + (int64_t)h * a.x.sh;
   uint16_t* orow = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)t * a.out.st + (int64_t)h * a.out.sh;
-  const int half = a.d / 2;
-  const uint32_t lo = *(const uint32_t*)(xr + c), hi = *(const uint32_t*)(xr + c + half);
-  const float x1[2] = {bf16_to_f32((uint16_t)(lo & 0xffffu)), bf16_to_f32((uint16_t)(lo >> 16))};
-  const float x2[2] = {bf16_to_f32((uint16_t)(hi & 0xffffu)), bf16_to_f32((uint16_t)(hi >> 16))};
-  float y1[2], y2[2];
+  const Vec lo = *(const Vec*)(xr + c), hi = *(const Vec*)(xr + c + half);
+  const uint32_t* lw = (const uint32_t*)&lo;
+  const uint32_t* hw = (const uint32_t*)&hi;
+  uint32_t y1w[VW / 2], y2w[VW / 2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    float sn, cs;
-    rope_sincos(a.pos0 + t, a.w.hi[c + j], a.w.lo[c + j], &sn, &cs);
-    y1[j] = x1[j] * cs - x2[j] * sn;
-    y2[j] = x2[j] * cs + x1[j] * sn;
+  for (int j = 0; j < VW; j += 2) {
+    float y1[2], y2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float x1 = bf16_to_f32((uint16_t)(e ? lw[j / 2] >> 16 : lw[j / 2] & 0xffffu));
+      const float x2 = bf16_to_f32((uint16_t)(e ? hw[j / 2] >> 16 : hw[j / 2] & 0xffffu));
+      float sn, cs;
+      rope_sincos(a.pos0 + t, a.w.hi[c + j + e], a.w.lo[c + j + e], &sn, &cs);
+      y1[e] = x1 * cs - x2 * sn;
+      y2[e] = x2 * cs + x1 * sn;
+    }
+    y1w[j / 2] = pack_bf16x2(y1[0], y1[1]);
+    y2w[j / 2] = pack_bf16x2(y2[0], y2[1]);
   }
-  *(uint32_t*)(orow + c) = pack_bf16x2(y1[0], y1[1]);
-  *(uint32_t*)(orow + c + half) = pack_bf16x2(y2[0], y2[1]);
+  *(Vec*)(orow + c) = *(const Vec*)y1w;
+  *(Vec*)(orow + c + half) = *(const Vec*)y2w;
 }
 
 constexpr int kProjWaves = 8;
@@ -224,9 +239,10 @@ __global__ void __launch_bounds__(kPsWaves * 64) lambda_proj_stream_kernel(const
 
 hipError_t launch_rope_bf16(const RopeArgs& a, hipStream_t s) {
   const void* args[] = {&a};
-  const long long threads = (long long)a.B * a.T * a.H * (a.d / 4);
-  return hipLaunchKernel((const void*)rope_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256),
-                         (void**)args, 0, s);
+  const int vw = a.d % 16 == 0 ? 8 : 2;  // pairs per thread (d % 8 == 0 always)
+  const long long threads = (long long)a.B * a.T * a.H * (a.d / 2 / vw);
+  return hipLaunchKernel(vw == 8 ? (const void*)rope_kernel<8> : (const void*)rope_kernel<2>,
+                         dim3((unsigned)((threads + 255) / 256)), dim3(256), (void**)args, 0, s);
 }
 
 hipError_t launch_lambda_proj_bf16(const LamProjArgs& a, hipStream_t s) {

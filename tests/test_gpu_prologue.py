@@ -37,7 +37,8 @@ def _bf16(shape, seed, std=1.0):
     return (std * torch.randn(shape, generator=g, device=DEV)).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("d,theta,pos0", [(64, 1e4, 0), (128, 1e4, 12345), (128, 5e5, 3), (8, 10.0, 100000)])
+@pytest.mark.parametrize("d,theta,pos0", [(64, 1e4, 0), (128, 1e4, 12345), (128, 5e5, 3), (8, 10.0, 100000),
+                                         (24, 1e4, 7), (256, 1e4, 0)])
 def test_rope_kernel(d, theta, pos0):
     x = _bf16((2, 300, 3, d), seed=2000 + d)
     got = binding.rope(x, theta=theta, pos0=pos0)
