@@ -384,7 +384,7 @@ static da_status v2_bwd_impl(da_dtype dtype, int B, int T, int Hq, int Hkv, int 
   const BwdWs w = bwd_ws(B, T, Hq, d);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.dA + 2 * w.rows) return DA_E_WORKSPACE;
   const int qt = (T + 127) / 128;
-  if (!grid_fits((long long)B * Hq * qt) || !grid_fits(((long long)B * da::backward_padded_rows(T) * (Hq / 2) + 3) / 4))
+  if (!grid_fits((long long)B * Hq * qt) || !grid_fits(((long long)B * da::backward_padded_rows(T) * (Hq / 2) + 15) / 16))
     return DA_E_SHAPE;
 
   da::BwdArgs a{};

@@ -13,7 +13,7 @@
 //   term in lse, and the same steps hold.)
 //
 // Three kernels (designed for gfx950):
-//   * bwd_pre: one wave per (b, token, pair): d attn of both heads (bf16, to
+//   * bwd_pre: 16 lanes per (b, token, pair): d attn of both heads (bf16, to
 //     the workspace), D of both heads, d lam, and a copy of lse padded to a
 //     multiple of 128 rows (so row blocks read whole float4 groups).
 //   * bwd_dq: the forward's structure with the key loop kept: a wave owns 32
@@ -31,6 +31,8 @@
 //     across workgroups (no atomics: deterministic).
 #include <math.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "tile_ops.hpp"
 
@@ -41,44 +43,59 @@ constexpr int kNW = 4;   // waves per workgroup of bwd_dq; bwd_dkdv has 2 kNW (t
 constexpr int kBT = 32;  // rows / keys per streamed tile
 
 // ---- pre-pass -----------------------------------------------------------------
+// Sum over the 16 lanes of a row (lanes 16k .. 16k + 15).
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 16);
+  return v;
+}
+
+// Sixteen lanes per (b, t, p), t < Tp: each lane holds d/16 consecutive
+// channels (16-byte accesses at d = 128, 8-byte at d = 64), four pairs per
+// wave, so a wave reads and writes contiguous spans.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdArgs a) {
-  constexpr int PL = D / 64;  // elements per lane
-  const int lane = threadIdx.x & 63;
+  constexpr int EL = D / 16;  // channels per lane
+  using Vec = typename std::conditional<EL == 8, uint4, uint2>::type;
+  const int lane = threadIdx.x & 63, l16 = lane & 15;
   const int P = a.Hq / 2;
-  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, t, p), t < Tp
-  if (item >= (long long)a.B * a.Tp * P) return;
+  const long long item = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);  // (b, t, p)
+  if (item >= (long long)a.B * a.Tp * P) return;  // whole rows of 16 lanes
   const int p = (int)(item % P);
   const int t = (int)((item / P) % a.Tp);
   const int b = (int)(item / ((long long)P * a.Tp));
   const int64_t r0 = ((int64_t)b * a.Hq + 2 * p) * a.Tp + t, r1 = r0 + a.Tp;  // rows of heads 2p, 2p+1
   if (t >= a.T) {  // padding rows: zero D and lse (masked where read)
-    if (lane == 0) a.Dw[r0] = a.Dw[r1] = a.lsew[r0] = a.lsew[r1] = 0.f;
+    if (l16 == 0) a.Dw[r0] = a.Dw[r1] = a.lsew[r0] = a.lsew[r1] = 0.f;
     return;
   }
+  const int c = EL * l16;
   const uint16_t* dop = (const uint16_t*)a.dout.p + b * a.dout.sb + (int64_t)t * a.dout.st + p * a.dout.sh;
   const uint16_t* a0 = (const uint16_t*)a.attn.p + b * a.attn.sb + (int64_t)t * a.attn.st + (2 * p) * a.attn.sh;
   const uint16_t* a1 = a0 + a.attn.sh;
-  float go[PL], x = 0.f, y = 0.f;
+  const Vec gv = *(const Vec*)(dop + c), x0v = *(const Vec*)(a0 + c), x1v = *(const Vec*)(a1 + c);
+  const uint32_t* gw = (const uint32_t*)&gv;
+  const uint32_t* w0 = (const uint32_t*)&x0v;
+  const uint32_t* w1 = (const uint32_t*)&x1v;
+  auto lo = [](uint32_t w) { return __builtin_bit_cast(float, w << 16); };
+  auto hi = [](uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); };
+  float x = 0.f, y = 0.f;
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int c = lane + 64 * i;
-    go[i] = bf16_to_f32(dop[c]);
-    x += go[i] * bf16_to_f32(a0[c]);
-    y += go[i] * bf16_to_f32(a1[c]);
+  for (int i = 0; i < EL / 2; ++i) {
+    x += lo(gw[i]) * lo(w0[i]) + hi(gw[i]) * hi(w0[i]);
+    y += lo(gw[i]) * lo(w1[i]) + hi(gw[i]) * hi(w1[i]);
   }
-  x = wave_sum(x);
-  y = wave_sum(y);
+  x = row16_sum(x);
+  y = row16_sum(y);
   const float lg = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)t * a.lam.st + p * a.lam.sh];
   const float s = sigmoid_f32(lg);
   uint16_t* d0 = a.dA + (((int64_t)b * a.T + t) * a.Hq + 2 * p) * D;
+  uint32_t n1[EL / 2];
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int c = lane + 64 * i;
-    d0[c] = dop[c];
-    d0[D + c] = (uint16_t)(pack_bf16x2(-s * go[i], 0.f) & 0xffffu);
-  }
-  if (lane == 0) {
+  for (int i = 0; i < EL / 2; ++i) n1[i] = pack_bf16x2(-s * lo(gw[i]), -s * hi(gw[i]));
+  *(Vec*)(d0 + c) = gv;
+  *(Vec*)(d0 + D + c) = *(const Vec*)n1;
+  if (l16 == 0) {
     a.Dw[r0] = x;
     a.Dw[r1] = -s * y;
     a.lsew[r0] = a.lse[((int64_t)b * a.Hq + 2 * p) * a.T + t];
@@ -453,7 +470,7 @@ template <int D>
 hipError_t launch(const BwdArgs& a, hipStream_t st) {
   const void* args[] = {&a};
   const long long items = (long long)a.B * a.Tp * (a.Hq / 2);
-  hipError_t e = hipLaunchKernel((const void*)bwd_pre_kernel<D>, dim3((unsigned)((items + 3) / 4)), dim3(256),
+  hipError_t e = hipLaunchKernel((const void*)bwd_pre_kernel<D>, dim3((unsigned)((items + 15) / 16)), dim3(256),
                                  (void**)args, 0, st);
   if (e != hipSuccess) return e;
   const int qt = (a.T + 32 * kNW - 1) / (32 * kNW);
@@ -479,13 +496,6 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
 // reduction (one workgroup, fixed order, writes the four vector gradients),
 // dQ of each map (the V2 dQ code with a 2d-wide v), dK of each map and dV
 // over both maps.
-
-// Sum over the 16 lanes of a row (lanes 16k .. 16k + 15).
-__device__ __forceinline__ float row16_sum(float v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 16);
-  return v;
-}
 
 // Sixteen lanes per (b, t, h), t < Tp: each lane holds 2d/16 consecutive
 // channels (16-byte loads and stores), four items per wave with consecutive
