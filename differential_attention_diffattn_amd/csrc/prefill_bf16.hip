@@ -292,7 +292,6 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
   // keeps streaming until the first tile barrier.
   using std::integral_constant;
   issue_k(0, integral_constant<int, 0>{});
-  issue_v(0, integral_constant<int, 0>{});
   // Q fragments (B operand of S^T = K Q^T): row i0w+li, cols 16ks+8hg
   bf16x8 qf[MPW][KS];
   {
@@ -320,8 +319,13 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
 #pragma unroll
       for (int i = 0; i < LPL; ++i) lv[j][i] = lane + 64 * i < D ? lp[j][lane + 64 * i] : 0.f;
   }
-  // copies of tile 1 (pipelined loop), issued last: the waits below leave them in flight
+  // V of tile 0 after Q: the pipelined loop's first P.V is the next step's
+  // (after the first tile barrier), so outside the first row tile the wait
+  // below leaves V(0) in flight too; then the copies of tile 1, issued last.
+  issue_v(0, integral_constant<int, 0>{});
   constexpr int kT1 = PIPE ? C::KPW + (C::NSTV == 3 ? C::VPW : 0) : 0;
+  // (in the first row tile a wave with one sub-block drains its P.V at step 0)
+  const bool v0_in_flight = PIPE && nkt > 1 && I0 > 0;
   if constexpr (PIPE) {
     if (nkt > 1) {
       issue_k(1, integral_constant<int, 1>{});
@@ -332,7 +336,9 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
   // compiler sees it as available from here on and places no wait of its own
   // later (such a wait would also hold up tile 1's copies).
   auto retire = [&](auto& v) {
-    if (PIPE && nkt > 1)
+    if (v0_in_flight)
+      asm volatile("s_waitcnt vmcnt(%1)" : "+v"(v) : "n"(kT1 + C::VPW));
+    else if (PIPE && nkt > 1)
       asm volatile("s_waitcnt vmcnt(%1)" : "+v"(v) : "n"(kT1));
     else
       asm volatile("s_waitcnt vmcnt(0)" : "+v"(v));
@@ -601,7 +607,7 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
       constexpr int ZB = 32 * DV * 2, Z0 = C::VBASE + (C::NSTV - 1) * C::V_BYTES + 32 * (C::NSB - 1) * DV * 2;
       for (int i = tid * 16; i < ZB; i += NW * 64 * 16) *(uint4*)(smem + Z0 + i) = make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();  // K and V of tile 0 visible (tile 1 is waited for at the first tile barrier)
+    __syncthreads();  // K (and, in the first row tile, V) of tile 0 visible; the rest is waited for at the first tile barrier
     if (nsub > 0) Scur = qk(integral_constant<int, 0>{});
     auto tile_step = [&](int kt, auto kstage_c, auto vstage_c) {
       constexpr int SK = decltype(kstage_c)::value, SV = decltype(vstage_c)::value;
