@@ -107,10 +107,14 @@ struct Cfg {
   static_assert((NSTK - 1) * KREG + (NK - 1) * K_BYTES * (MPW - 1) + (BN - 32) * D * 2 < 65536, "K read offset range");
   static_assert((NSTV - 1) * V_BYTES + (BN - 8) * DV * 2 + (CB - 1) * 64 < 65536, "V read offset range");
   // MPW == 1 epilogue: one exchange slot per partner-wave pair (fp32, lane-native
-  // order), then each pair's two 64-lane partial sums of squares
-  static constexpr int XBYTES_DATA = MPW == 1 ? (NW / 2) * CB * 16 * 64 * 4 : 0;
-  static constexpr int XBYTES = MPW == 1 ? XBYTES_DATA + (NW / 2) * 128 * 4 : 0;
-  static constexpr int SMEM = TILE_SMEM > XBYTES ? TILE_SMEM : XBYTES;
+  // order).  When the stages already take more than half the LDS (one
+  // workgroup per CU) and the slots fit beside them (SEPX), they get LDS of
+  // their own, so a map-2 wave writes its slot as soon as its own key loop
+  // ends; otherwise they reuse the stages once every wave is done with them.
+  static constexpr int XBYTES = MPW == 1 ? (NW / 2) * CB * 16 * 64 * 4 : 0;
+  static constexpr bool SEPX = MPW == 1 && TILE_SMEM > 80 * 1024 && TILE_SMEM + XBYTES <= 160 * 1024;
+  static constexpr int XBASE = SEPX ? TILE_SMEM : 0;
+  static constexpr int SMEM = SEPX ? TILE_SMEM + XBYTES : (TILE_SMEM > XBYTES ? TILE_SMEM : XBYTES);
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   // MPW == 1 with 4 waves: two workgroups (two waves per SIMD) per CU
   static constexpr int MIN_BLOCKS = (MPW == 1 && NW == 4) ? 2 : 1;
@@ -706,9 +710,9 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
   float ss = 0.f;
   if constexpr (MPW == 1) {
     // map 2's wave hands its weighted O to its partner through LDS
-    __syncthreads();  // every wave is done with the K/V stages
+    if constexpr (!C::SEPX) __syncthreads();  // every wave is done with the K/V stages
     // 16-byte chunks (four accumulator registers) in lane order: conflict-free
-    f32x4* xch = (f32x4*)smem + slot * (CB * 4 * 64);
+    f32x4* xch = (f32x4*)(smem + C::XBASE) + slot * (CB * 4 * 64);
     if (m0 == 1) {
       if (active) {
         const float w = second_weight(inv[0]);
