@@ -355,7 +355,7 @@ def main():
         print(json.dumps(summarize(args.summarize, args.kernel), indent=1))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); the kernels shard "
+        print(f"bench.py: measures one GPU only (--gpus {args.gpus} requested); the kernels shard "
               "by head/group with no exchange, so the 1-GPU figure is the per-GPU figure.", file=sys.stderr)
         sys.exit(2)
 

@@ -59,7 +59,7 @@ typedef enum {
     DA_E_DTYPE = 2,       /* unknown dtype value                                */
     DA_E_SHAPE = 3,       /* a size is < 1, or sizes are inconsistent           */
     DA_E_LAYOUT = 4,      /* misaligned pointer or a stride breaks the rules    */
-    DA_E_UNSUPPORTED = 5, /* valid arguments this build has no kernel for       */
+    DA_E_UNSUPPORTED = 5, /* valid arguments the library has no kernel for     */
     DA_E_WORKSPACE = 6,   /* decode workspace missing or too small              */
     DA_E_LAUNCH = 7       /* the HIP runtime rejected a kernel launch           */
 } da_status;
