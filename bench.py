@@ -437,6 +437,30 @@ def main():
             secondary.append(r)
             del xs
             torch.cuda.empty_cache()
+    # context for the MFMA roofline: the vendor GEMM (torch.matmul, hipBLASLt)
+    # on a large square bf16 product on the same card and clock
+    ref = None
+    if not args.no_secondary:
+        import torch
+        n = 8192
+        g = torch.Generator(device="cuda").manual_seed(7)
+        a_ = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+        b_ = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+        for _ in range(10):
+            c_ = torch.matmul(a_, b_)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            c_ = torch.matmul(a_, b_)
+        e1.record()
+        torch.cuda.synchronize()
+        tf = 2.0 * n ** 3 / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e12
+        ref = {"kind": f"torch.matmul bf16 [{n}x{n}] x [{n}x{n}] (vendor GEMM library)",
+               "tflops": round(tf, 1), "frac_of_peak": round(tf / 2500.0, 4)}
+        del a_, b_, c_
+        torch.cuda.empty_cache()
+        log(json.dumps({"mfma_reference": ref}))
     cpu = None
     if not args.no_cpu_baseline:
         cpu = _cpu_baseline(w, x, softmax1=args.softmax1)
@@ -460,6 +484,7 @@ def main():
                    "softmax": "off_by_one" if args.softmax1 else "standard"},
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        "mfma_reference": ref,
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
