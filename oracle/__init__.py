@@ -81,6 +81,8 @@ def _configure(lib):
     lib.da_oracle_v2_rows.restype = None
     lib.da_oracle_v2_decode.argtypes = [i, i, i, i, i] + [dp] * 4 + [i, dp]
     lib.da_oracle_v2_decode.restype = None
+    lib.da_oracle_v2_heads.argtypes = [i, i, i, i, i] + [dp] * 3 + [i, dp, dp]
+    lib.da_oracle_v2_heads.restype = None
     lib.da_oracle_set_threads.argtypes = [i]
     lib.da_oracle_set_threads.restype = i
     return lib
@@ -179,6 +181,20 @@ def v2_rows(q, k, v, lam, btp, softmax1: bool = False) -> np.ndarray:
     _load().da_oracle_v2_rows(B, T, Hq, Hkv, d, *[_p(x) for x in t], int(bool(softmax1)), idx.shape[0],
                               idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _p(out))
     return out
+
+
+def v2_heads(q, k, v, softmax1: bool = False):
+    """Every query head's causal attention before the pairs combine: q
+    ``[B, T, Hq, d]``, k, v ``[B, T, Hkv, d]`` -> (attn ``[B, T, Hq, d]``, lse
+    ``[B, Hq, T]``, the natural log of each row's softmax denominator)."""
+    q, k, v = [_f64(x) for x in (q, k, v)]
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    assert k.shape == (B, T, Hkv, d) and v.shape == k.shape and Hq % Hkv == 0
+    attn = np.zeros((B, T, Hq, d), dtype=np.float64)
+    lse = np.zeros((B, Hq, T), dtype=np.float64)
+    _load().da_oracle_v2_heads(B, T, Hq, Hkv, d, _p(q), _p(k), _p(v), int(bool(softmax1)), _p(attn), _p(lse))
+    return attn, lse
 
 
 def v2_decode(q, k, v, lam, softmax1: bool = False) -> np.ndarray:

@@ -112,65 +112,58 @@ def v2_bwd(q, k, v, lam, dout, softmax1: bool = False):
     return dq, dk, dv, dlam
 
 
-def v2_bwd_rounding_bounds(q, k, v, lam, dout, softmax1: bool = False):
-    """Per-element scale of what bf16 rounding can move in each gradient of
-    :func:`v2_bwd`, for a path that holds P, dS, d attn and attn in bf16
-    (relative rounding u = 2^-9 each) and accumulates in fp32.
+def v2_bwd_sampled(q, k, v, lam, dout, rows, keys, softmax1: bool = False):
+    """The gradients of :func:`v2_bwd` at chosen places, for sizes where the
+    dense per-head matrices are too slow: dq of the rows ``rows`` (an
+    ``[n, 3]`` array of (b, t, query head)), dk and dv of the keys ``keys``
+    (``[m, 3]`` of (b, j, kv head)), and dlam everywhere.
 
-    Each bound is u times the sum of the absolute values of the terms that a
-    rounded factor enters, following the same steps as :func:`v2_bwd`:
-      E_i     = sum_c |d attn_ic| |attn_ic|     (what rounding attn moves in D_i)
-      dq_ic  <- sum_j (P_ij E_i + |dS_ij|) |k_jc| / sqrt d
-      dk_jc  <- sum_{h,i} (P_ij E_i + |dS_ij|) |q_ic| / sqrt d
-      dv_jc  <- 2 sum_{h,i} P_ij |d attn_ic|
-      dlam   <- 2 s (1 - s) sum_c |dout_c| |attn_odd,c|
-    Returns (bq, bk, bv, blam) shaped like the gradients.
+    The same chain rule, one row or one key at a time.  Each head's rows and
+    log-sum-exp come from :func:`oracle.v2_heads` (the C forward), so that
+    P_tj = exp(q_t . k_j / sqrt d - lse_t) for j <= t, and with
+    d attn as in :func:`v2_bwd` and D_t = <d attn_t, attn_t> (= rowsum(P o dP)):
+        dq_t  = sum_{j <= t} P_tj (d attn_t . v_j - D_t) k_j / sqrt d
+        dk_j  = sum_{h in g} sum_{t >= j} P_tj (d attn_t . v_j - D_t) q_t / sqrt d
+        dv_j  = sum_{h in g} sum_{t >= j} P_tj d attn_t
+    Returns (dq [n, d], dk [m, d], dv [m, d], dlam [B, T, Hq/2]).
     """
+    from . import v2_heads
+
     q, k, v, lam, dout = [_f64(x) for x in (q, k, v, lam, dout)]
-    u = 2.0 ** -9
     B, T, Hq, d = q.shape
     G = Hq // k.shape[2]
-    bq, bk, bv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
-    blam = np.zeros_like(lam)
-    for b in range(B):
-        P, attn, _ = _rows(q[b], k[b], v[b], softmax1)
-        sig = 1.0 / (1.0 + np.exp(-lam[b]))
-        da = np.zeros((T, Hq, d))
-        da[:, 0::2] = dout[b]
-        da[:, 1::2] = -sig[..., None] * dout[b]
-        blam[b] = 2 * u * sig * (1.0 - sig) * np.einsum("tpc,tpc->tp", np.abs(dout[b]), np.abs(attn[:, 1::2]))
-        for h in range(Hq):
-            g = h // G
-            dP = da[:, h] @ v[b][:, g].T
-            dS = P[h] * (dP - (P[h] * dP).sum(axis=1, keepdims=True))
-            E = (np.abs(da[:, h]) * np.abs(attn[:, h])).sum(axis=1, keepdims=True)
-            W = P[h] * E + np.abs(dS)
-            bq[b][:, h] = u * (W @ np.abs(k[b][:, g])) / math.sqrt(d)
-            bk[b][:, g] += u * (W.T @ np.abs(q[b][:, h])) / math.sqrt(d)
-            bv[b][:, g] += 2 * u * (P[h].T @ np.abs(da[:, h]))
-    return bq, bk, bv, blam
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+    keys = np.asarray(keys, dtype=np.int64).reshape(-1, 3)
+    attn, lse = v2_heads(q, k, v, softmax1=softmax1)
+    sig = 1.0 / (1.0 + np.exp(-lam))  # [B, T, Hq/2]
+    dlam = -sig * (1.0 - sig) * np.einsum("btpc,btpc->btp", dout, attn[:, :, 1::2])
 
+    def d_attn(b, t, h):  # d attn of head h at rows t (t: int or array)
+        g = dout[b, t, h // 2]
+        return g if h % 2 == 0 else -sig[b, t, h // 2][..., None] * g
 
-# ---- DIFF V1 ---------------------------------------------------------------------
-#
-# What is differentiated ("Differential Transformer V2" article, DiffAttnV1
-# pseudo-code; nanoGPT issue "How best to implement a differential
-# transformer?", Wilsontomass's module for the RMSNorm arguments):
-#
-#     a_m    = causal softmax(q_m k_m^T / sqrt(d)) v        (m = 1, 2; v is 2d wide)
-#     lam    = exp(<lq1, lk1>) - exp(<lq2, lk2>) + lam_init(layer)
-#     D      = a_1 - lam a_2
-#     r      = (mean_c D_c^2 + 1e-5)^(-1/2)                 (per token and head)
-#     out    = (1 - lam_init) r D
-#
-# Backward, the forward's steps reversed (n = 2d channels per row):
-#
-#     dD     = (1 - lam_init) r (dout - r^2 D mean_c(dout_c D_c))
-#     da_1   = dD,    da_2 = -lam dD,    dlam = -sum_rows <dD, a_2>
-#     per map: the softmax-attention gradients of q_m, k_m and v (dv summed
-#     over the two maps)
-#     dlq1 = dlam e1 lk1,  dlk1 = dlam e1 lq1,  dlq2 = -dlam e2 lk2,
-#     dlk2 = -dlam e2 lq2,   with e1 = exp(<lq1, lk1>), e2 = exp(<lq2, lk2>).
+    sc = 1.0 / math.sqrt(d)
+    dq = np.zeros((rows.shape[0], d))
+    for n, (b, t, h) in enumerate(rows):
+        g = h // G
+        kj, vj = k[b, :t + 1, g], v[b, :t + 1, g]
+        P = np.exp(kj @ q[b, t, h] * sc - lse[b, h, t])
+        da = d_attn(b, t, h)
+        dS = P * (vj @ da - da @ attn[b, t, h])
+        dq[n] = dS @ kj * sc
+    dk = np.zeros((keys.shape[0], d))
+    dv = np.zeros((keys.shape[0], d))
+    for n, (b, j, g) in enumerate(keys):
+        for h in range(g * G, (g + 1) * G):
+            ts = np.arange(j, T)
+            qt = q[b, j:, h]
+            P = np.exp(qt @ k[b, j, g] * sc - lse[b, h, j:])
+            da = d_attn(b, ts, h)
+            D = np.einsum("tc,tc->t", da, attn[b, j:, h])
+            dS = P * (da @ v[b, j, g] - D)
+            dk[n] += dS @ qt * sc
+            dv[n] += P @ da
+    return dq, dk, dv, dlam
 
 
 def _causal_map(q, k, softmax1):
@@ -251,85 +244,3 @@ def v1_bwd(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, dout, softmax1: bo
                 dv[b, h] += P[m].T @ da
     return (dq[0], dq[1], dk[0], dk[1], dv,
             dlam * e1 * lk1, dlam * e1 * lq1, -dlam * e2 * lk2, -dlam * e2 * lq2)
-
-
-def v1_bwd_rounding_bounds(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, dout, softmax1: bool = False,
-                           rss: bool = True):
-    """Per-element scale of what bf16 rounding can move in each gradient of
-    :func:`v1_bwd`, for a path that keeps a_1, a_2 in bf16 (the training
-    forward's outputs), rebuilds D from them, holds da_m, P and dS in bf16
-    and accumulates in fp32 (relative rounding u = 2^-9 per rounded value).
-
-    Followed through the same steps, to first order:
-      dD_e   <- the RMSNorm backward's derivative with respect to D applied
-                to |delta D| = u (|a_1| + |lam| |a_2|), plus u |dD| (rounding)
-      da_m   <- eps_m = (1, |lam|)_m times that
-      D_m,i  <- <eps_m,i, |a_m,i|> + u <|da_m,i|, |a_m,i|>
-      dS_ij  <- P_ij (<eps_m,i, |v_j|> + err D_m,i) + u |dS_ij|
-      dq, dk <- |err dS| times |k| or |q| over sqrt d;  dv <- P^T (eps_m + 2u |da_m|)
-      dlam   <- sum_rows <|err dD|, |a_2|> + u <|dD|, |a_2|>;  the vectors scale by e |lambda vector|
-    With ``rss=False`` every sum over an index adds absolute values (a
-    worst case: all roundings aligned); with ``rss=True`` (default) it takes
-    the root of the sum of squares, the typical size when the roundings are
-    independent (each contraction then grows like sqrt(n), not n).
-    Returns arrays shaped like :func:`v1_bwd`'s results.
-    """
-    t, li, e1, e2, lam = _v1_args(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer)
-    q1, q2, k1, k2, v, lq1, lk1, lq2, lk2 = t
-    dout = _f64(dout)
-    u = 2.0 ** -9
-    B, H, T, d = q1.shape
-    n = 2 * d
-    c = 1.0 - li
-    if rss:
-        agg = lambda x: np.sqrt((x * x).sum(axis=1, keepdims=True))
-        mm = lambda x, y: np.sqrt((x * x) @ (y * y))
-        tot = lambda x: float(np.sqrt((x * x).sum()))
-    else:
-        agg = lambda x: x.sum(axis=1, keepdims=True)
-        mm = lambda x, y: x @ y
-        tot = lambda x: float(x.sum())
-    qs, ks = (q1, q2), (k1, k2)
-    bq = [np.zeros_like(q1), np.zeros_like(q2)]
-    bk = [np.zeros_like(k1), np.zeros_like(k2)]
-    bv = [np.zeros_like(v) for _ in range(B * H)]
-    lam_terms = []
-    for b in range(B):
-        for h in range(H):
-            P, a = [], []
-            for m in range(2):
-                Pm, _ = _causal_map(qs[m][b, h], ks[m][b, h], softmax1)
-                P.append(Pm)
-                a.append(Pm @ v[b, h])
-            D = a[0] - lam * a[1]
-            r = 1.0 / np.sqrt((D * D).mean(axis=1, keepdims=True) + 1e-5)
-            g = dout[b, :, h]
-            gm = (g * D).mean(axis=1, keepdims=True)
-            dD = c * r * (g - r * r * D * gm)
-            dlt = u * (np.abs(a[0]) + abs(lam) * np.abs(a[1]))      # |delta D|
-            S1 = agg(np.abs(D) * dlt)
-            S2 = agg(np.abs(g) * dlt)
-            r3 = r ** 3
-            err_dD = (c * r3 * np.abs(g) * S1 / n + 3 * c * r ** 5 * np.abs(D) * np.abs(gm) * S1 / n
-                      + c * r3 * np.abs(gm) * dlt + c * r3 * np.abs(D) * S2 / n)
-            lam_terms.append(err_dD * np.abs(a[1]) + u * np.abs(dD) * np.abs(a[1]))
-            acc_v = np.zeros_like(v[b, h]) if not rss else None
-            sq_v = np.zeros_like(v[b, h])
-            for m, (wt, da) in enumerate(((1.0, dD), (abs(lam), -lam * dD))):
-                eps = wt * (err_dD + u * np.abs(dD))
-                dP = da @ v[b, h].T
-                dS = P[m] * (dP - (P[m] * dP).sum(axis=1, keepdims=True))
-                errD = agg(eps * np.abs(a[m])) + u * agg(np.abs(da) * np.abs(a[m]))
-                W = P[m] * (mm(eps, np.abs(v[b, h]).T) + errD) + u * np.abs(dS)
-                bq[m][b, h] = mm(W, np.abs(ks[m][b, h])) / math.sqrt(d)
-                bk[m][b, h] = mm(W.T, np.abs(qs[m][b, h])) / math.sqrt(d)
-                x = mm(P[m].T, eps + 2 * u * np.abs(da))
-                if rss:
-                    sq_v += x * x
-                else:
-                    acc_v += x
-            bv[b * H + h] = np.sqrt(sq_v) if rss else acc_v
-    dvb = np.stack(bv).reshape(v.shape)
-    blam = tot(np.stack(lam_terms))
-    return (bq[0], bq[1], bk[0], bk[1], dvb,
-            blam * e1 * np.abs(lk1), blam * e1 * np.abs(lq1), blam * e2 * np.abs(lk2), blam * e2 * np.abs(lq2))

@@ -49,17 +49,18 @@ static double sigmoid(double x) {
  *                                    only the keys the query may see)
  *   w_j = exp(s_j - M),  Z = sum_j w_j,  M = max_j s_j
  *   out[c] = sum_j w_j v_j[c] / Z    for c < dv
- * With softmax1 set, the off-by-one softmax of the [HN] comment "softmax
- * should be exp()/(1+sum exp())": the denominator gains exp(0), the same as
- * one more logit 0 whose value row is 0.  M then also covers that logit,
- * M = max(0, max_j s_j), and Z gains exp(0 - M).
+ * With softmax1 set, the off-by-one softmax proposed in a comment of
+ * Hacker News item 41780844: one is added to the softmax denominator, which
+ * is the same as one more logit 0 whose value row is 0.  M then also covers
+ * that logit, M = max(0, max_j s_j), and Z gains exp(0 - M).
  * k_j is at k + j*kstride, v_j at v + j*vstride.  w is caller scratch of
- * nkeys doubles.
+ * nkeys doubles.  If lse is not NULL it receives M + log(Z), the natural log
+ * of the row's softmax denominator.
  */
 static void softmax_attention_row(int d, int dv, int nkeys, const double* q,
                                   const double* k, int64_t kstride,
                                   const double* v, int64_t vstride,
-                                  int softmax1, double* w, double* out) {
+                                  int softmax1, double* w, double* out, double* lse) {
     const double scale = 1.0 / sqrt((double)d);
     double m = softmax1 ? 0.0 : -INFINITY;
     for (int j = 0; j < nkeys; ++j) {
@@ -77,6 +78,7 @@ static void softmax_attention_row(int d, int dv, int nkeys, const double* q,
         for (int c = 0; c < dv; ++c) out[c] += w[j] * vj[c];
     }
     for (int c = 0; c < dv; ++c) out[c] /= z;
+    if (lse) *lse = m + log(z);
 }
 
 /*
@@ -98,8 +100,8 @@ static void v1_row(int H, int T, int d, const double* q1, const double* q2,
     const double* k1h = k1 + bh * T * d;
     const double* k2h = k2 + bh * T * d;
     const double* vh = v + bh * T * dv;
-    softmax_attention_row(d, dv, i + 1, q1i, k1h, d, vh, dv, softmax1, w, a1);
-    softmax_attention_row(d, dv, i + 1, q2i, k2h, d, vh, dv, softmax1, w, a2);
+    softmax_attention_row(d, dv, i + 1, q1i, k1h, d, vh, dv, softmax1, w, a1, NULL);
+    softmax_attention_row(d, dv, i + 1, q2i, k2h, d, vh, dv, softmax1, w, a2, NULL);
     double ms = 0.0;
     for (int c = 0; c < dv; ++c) {
         a1[c] = a1[c] - lam * a2[c];
@@ -182,9 +184,9 @@ static void v2_row(int Hq, int Hkv, int d, int nkeys, const double* qrow,
     const int ge = he / group, go = ho / group;
     const int64_t kvstride = (int64_t)Hkv * d; /* token stride in k, v */
     softmax_attention_row(d, d, nkeys, qrow + (int64_t)he * d, kb + (int64_t)ge * d,
-                          kvstride, vb + (int64_t)ge * d, kvstride, softmax1, w, a_even);
+                          kvstride, vb + (int64_t)ge * d, kvstride, softmax1, w, a_even, NULL);
     softmax_attention_row(d, d, nkeys, qrow + (int64_t)ho * d, kb + (int64_t)go * d,
-                          kvstride, vb + (int64_t)go * d, kvstride, softmax1, w, a_odd);
+                          kvstride, vb + (int64_t)go * d, kvstride, softmax1, w, a_odd, NULL);
     const double s = sigmoid(lam_logit);
     for (int c = 0; c < d; ++c) dst[c] = a_even[c] - s * a_odd[c];
 }
@@ -267,6 +269,39 @@ void da_oracle_v2_decode(int B, int L, int Hq, int Hkv, int d,
         free(w);
         free(ae);
         free(ao);
+    }
+}
+
+/*
+ * Every query head's own causal attention, before the pairs are combined
+ * ([V2A] DiffAttnV2: the single attention call over all Hq heads, head h
+ * reading kv head h / (Hq/Hkv)):
+ *   attn[b, t, h, :] = softmax_j(q_h . k_g(h),j / sqrt d) v_g(h),j   (j <= t)
+ *   lse[b, h, t]     = natural log of that row's softmax denominator
+ * What a backward pass keeps from the forward; rows computed one at a time.
+ */
+void da_oracle_v2_heads(int B, int T, int Hq, int Hkv, int d, const double* q,
+                        const double* k, const double* v, int softmax1,
+                        double* attn, double* lse) {
+    const int group = Hq / Hkv;
+    const int64_t nrows = (int64_t)B * T * Hq;
+    const int64_t kvstride = (int64_t)Hkv * d;
+#pragma omp parallel
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < nrows; ++r) {
+            const int h = (int)(r % Hq);
+            const int t = (int)((r / Hq) % T);
+            const int b = (int)(r / ((int64_t)Hq * T));
+            const int g = h / group;
+            const double* qrow = q + (((int64_t)b * T + t) * Hq + h) * d;
+            const double* kb = k + (int64_t)b * T * kvstride + (int64_t)g * d;
+            const double* vb = v + (int64_t)b * T * kvstride + (int64_t)g * d;
+            softmax_attention_row(d, d, t + 1, qrow, kb, kvstride, vb, kvstride, softmax1, w,
+                                  attn + r * d, lse + ((int64_t)b * Hq + h) * T + t);
+        }
+        free(w);
     }
 }
 

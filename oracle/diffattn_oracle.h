@@ -23,9 +23,9 @@
  *          notlober's module (explicit masked score maps, adjacent heads
  *          paired, one V of width 2*head_dim per differential head).
  *   [HN]   Hacker News item 41780844 comments: the lambda_init expression
- *          0.8 - 0.6*exp(-0.3*depth), and the comment that softmax should be
- *          exp()/(1 + sum exp()) ("off-by-one" softmax, the same as one extra
- *          logit 0).
+ *          0.8 - 0.6*exp(-0.3*depth), and a comment proposing a softmax
+ *          whose denominator gains an extra 1 (the "off-by-one" softmax,
+ *          the same as one extra logit 0).
  *
  * softmax1 (every attention function): 0 = the standard softmax; 1 = the
  * off-by-one softmax, each map's denominator gaining exp(0) -- equivalently
@@ -105,6 +105,16 @@ void da_oracle_v2_rows(int B, int T, int Hq, int Hkv, int d,
 void da_oracle_v2_decode(int B, int L, int Hq, int Hkv, int d,
                          const double* q, const double* k, const double* v,
                          const double* lam, int softmax1, double* out);
+
+/* Every query head's own causal attention rows, before the pairs combine,
+ * and each row's log-sum-exp (what a training forward keeps):
+ *   q   : [B][T][Hq][d];  k, v: [B][T][Hkv][d]
+ *   attn: [B][T][Hq][d];  lse : [B][Hq][T] (natural log of the row's
+ *         softmax denominator, the off-by-one term included when softmax1)
+ * [V2A] DiffAttnV2: the attention call over all Hq heads. */
+void da_oracle_v2_heads(int B, int T, int Hq, int Hkv, int d, const double* q,
+                        const double* k, const double* v, int softmax1,
+                        double* attn, double* lse);
 
 /* Threads the library's OpenMP loops may use (0 = OpenMP default).  Returns
  * the count that will be used. */

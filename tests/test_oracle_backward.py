@@ -144,6 +144,62 @@ def test_backward_mutant_is_caught(name, monkeypatch):
     assert failed >= 1, f"no pin catches mutation {name}"
 
 
+# ---- sampled V2 backward (rows and keys, for full-size GPU checks) -----------------
+
+@pytest.mark.parametrize("s1", [False, True])
+def test_v2_heads_matches_fwd_train(s1):
+    """The C per-head forward gives the dense numpy training forward's attn and
+    lse (natural log here, log2 there)."""
+    q, k, v, lam, _, _ = _case(21, 2, 19, 2, 4, 8)
+    attn, lse = oracle.v2_heads(q, k, v, softmax1=s1)
+    _, attn2, lse2 = ob.v2_fwd_train(q, k, v, lam, softmax1=s1)
+    assert np.abs(attn - attn2).max() < 1e-12
+    assert np.abs(lse - lse2 * math.log(2.0)).max() < 1e-12
+
+
+@settings(max_examples=15, deadline=None)
+@given(B=st.integers(1, 2), T=st.sampled_from([1, 2, 7, 20]), Hkv=st.integers(1, 2), G=st.sampled_from([2, 4]),
+       d=st.sampled_from([4, 8]), s1=st.booleans(), seed=st.integers(0, 10**6))
+def test_bwd_sampled_matches_dense(B, T, Hkv, G, d, s1, seed):
+    """dq of every row and dk, dv of every key, one at a time, equal the dense
+    per-head gradients."""
+    q, k, v, lam, dout, _ = _case(seed, B, T, Hkv, G, d)
+    dq, dk, dv, dlam = ob.v2_bwd(q, k, v, lam, dout, softmax1=s1)
+    Hq = G * Hkv
+    rows = [(b, t, h) for b in range(B) for t in range(T) for h in range(Hq)]
+    keys = [(b, j, g) for b in range(B) for j in range(T) for g in range(Hkv)]
+    sq, sk, sv, sl = ob.v2_bwd_sampled(q, k, v, lam, dout, rows, keys, softmax1=s1)
+    scale = lambda x: max(1.0, np.abs(x).max())
+    assert np.abs(sq - dq.reshape(-1, d)).max() < 1e-12 * scale(dq)
+    assert np.abs(sk - dk.reshape(-1, d)).max() < 1e-12 * scale(dk)
+    assert np.abs(sv - dv.reshape(-1, d)).max() < 1e-12 * scale(dv)
+    assert np.abs(sl - dlam).max() < 1e-12
+
+
+SAMPLED_SRC = inspect.getsource(ob.v2_bwd_sampled)
+
+SAMPLED_MUTATIONS = {
+    "odd_head_sign": ("return g if h % 2 == 0 else -sig", "return g if h % 2 == 0 else sig"),
+    "no_D_in_dq": ("dS = P * (vj @ da - da @ attn[b, t, h])", "dS = P * (vj @ da)"),
+    "rows_from_next_key": ("ts = np.arange(j, T)", "ts = np.arange(j + 1, T)"),
+    "dk_unscaled": ("dk[n] += dS @ qt * sc", "dk[n] += dS @ qt"),
+    "dq_sees_masked_key": ("kj, vj = k[b, :t + 1, g], v[b, :t + 1, g]", "kj, vj = k[b, :t + 2, g], v[b, :t + 2, g]"),
+    "wrong_group_heads": ("for h in range(g * G, (g + 1) * G):", "for h in range(g, g + G):"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SAMPLED_MUTATIONS))
+def test_sampled_mutant_is_caught(name, monkeypatch):
+    old, new = SAMPLED_MUTATIONS[name]
+    assert SAMPLED_SRC.count(old) == 1, f"mutation {name} no longer matches the oracle source"
+    ns = dict(vars(ob))
+    exec(compile(SAMPLED_SRC.replace(old, new), "<mutant>", "exec"), ns)
+    monkeypatch.setattr(ob, "v2_bwd_sampled", ns["v2_bwd_sampled"])
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        with np.errstate(all="ignore"):
+            test_bwd_sampled_matches_dense.hypothesis.inner_test(B=2, T=9, Hkv=2, G=2, d=4, s1=False, seed=5)
+
+
 # ---- DIFF V1 ---------------------------------------------------------------------
 
 def _v1_case(seed, B, H, T, d):

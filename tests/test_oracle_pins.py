@@ -352,8 +352,8 @@ def test_row_variants_match_full():
 
 # --------------------------------------------------------------------------
 # Off-by-one softmax exp(x_j) / (1 + sum_j exp(x_j)) (Hacker News item
-# 41780844, the comment that softmax "should be exp()/1+sum exp()" and that
-# adding an extra zero value in x does the same)
+# 41780844: a comment proposing an extra 1 in the softmax denominator, which
+# is the same as an extra logit 0 among the inputs)
 # --------------------------------------------------------------------------
 
 def _prepend_zero_token(x, axis):
