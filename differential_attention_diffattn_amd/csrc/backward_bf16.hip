@@ -79,25 +79,32 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdArgs a) {
   const uint32_t* w1 = (const uint32_t*)&x1v;
   auto lo = [](uint32_t w) { return __builtin_bit_cast(float, w << 16); };
   auto hi = [](uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); };
-  float x = 0.f, y = 0.f;
+  const float lg = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)t * a.lam.st + p * a.lam.sh];
+  const float s = sigmoid_f32(lg);
+  // The odd head's d attn goes to the MFMAs rounded to bf16; its row sum D
+  // is taken over those same rounded values, so that rowsum(dS) = 0 holds
+  // for the P the kernels see (a row with one visible key then gets dq = 0
+  // up to fp32 summation order).  y (the unrounded <dout, attn_odd>) feeds
+  // d lam only.
+  uint32_t n1[EL / 2];
+#pragma unroll
+  for (int i = 0; i < EL / 2; ++i) n1[i] = pack_bf16x2(-s * lo(gw[i]), -s * hi(gw[i]));
+  float x = 0.f, y = 0.f, z = 0.f;
 #pragma unroll
   for (int i = 0; i < EL / 2; ++i) {
     x += lo(gw[i]) * lo(w0[i]) + hi(gw[i]) * hi(w0[i]);
     y += lo(gw[i]) * lo(w1[i]) + hi(gw[i]) * hi(w1[i]);
+    z += lo(n1[i]) * lo(w1[i]) + hi(n1[i]) * hi(w1[i]);
   }
   x = row16_sum(x);
   y = row16_sum(y);
-  const float lg = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)t * a.lam.st + p * a.lam.sh];
-  const float s = sigmoid_f32(lg);
+  z = row16_sum(z);
   uint16_t* d0 = a.dA + (((int64_t)b * a.T + t) * a.Hq + 2 * p) * D;
-  uint32_t n1[EL / 2];
-#pragma unroll
-  for (int i = 0; i < EL / 2; ++i) n1[i] = pack_bf16x2(-s * lo(gw[i]), -s * hi(gw[i]));
   *(Vec*)(d0 + c) = gv;
   *(Vec*)(d0 + D + c) = *(const Vec*)n1;
   if (l16 == 0) {
     a.Dw[r0] = x;
-    a.Dw[r1] = -s * y;
+    a.Dw[r1] = z;
     a.lsew[r0] = a.lse[((int64_t)b * a.Hq + 2 * p) * a.T + t];
     a.lsew[r1] = a.lse[((int64_t)b * a.Hq + 2 * p + 1) * a.T + t];
     ((float*)a.dlam.p)[b * a.dlam.sb + (int64_t)t * a.dlam.st + p * a.dlam.sh] = -s * (1.f - s) * y;

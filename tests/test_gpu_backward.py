@@ -1,14 +1,12 @@
-"""DIFF V2 training forward and backward (HIP, through the C ABI) against the
-fp64 oracle in oracle/backward.py.
+"""DIFF V2 and DIFF V1 training forward and backward (HIP, through the C ABI)
+against the fp64 oracle in oracle/backward.py.
 
-Tolerance.  Every gradient is a sum over rows (and heads) of products whose
-factors the kernels hold in bf16 (P and dS as MFMA operands, d attn, attn
-and hence D = rowsum(d attn * attn)), each with a relative rounding of at
-most u = 2^-9, accumulated in fp32.  Where the terms cancel (dq of a row
-that sees one key is exactly 0) the error is set by the terms, not by the
-result, so each element is bounded by 2e-2 |ref| (the forward's bf16 bar)
-plus 4x the sum of |terms| times u that oracle.backward.v2_bwd_rounding_bounds
-follows through the same steps, plus 1e-4.
+Tolerance (gpu_util.assert_grad_close): every element within the forward's
+bf16 bar, 2e-2 + 1e-2 |ref| (+ 1e-4, the fp32 bar, for exact zeros), whose
+absolute part grows with the gradient tensor's RMS once that passes 1 and is
+raised to twice the worst error of the pages' module run in bf16 by PyTorch
+(tests/bf16_module.py) where bf16 arithmetic itself costs more than that;
+and every tensor within a relative L2 error of 1e-2.
 """
 import math
 
@@ -19,7 +17,8 @@ import torch
 import oracle
 from oracle import backward as ob
 from differential_attention_diffattn_amd import binding, workloads
-from gpu_util import assert_bf16_close, host64
+import bf16_module
+from gpu_util import assert_bf16_close, assert_grad_close, host64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -33,21 +32,11 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def assert_grad_close(got, ref, bound, what):
-    g = host64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
-    assert g.shape == ref.shape, (g.shape, ref.shape)
-    assert np.all(np.isfinite(g)), f"{what}: non-finite"
-    excess = np.abs(g - ref) - (2e-2 * np.abs(ref) + 4.0 * bound + 1e-4)
-    worst = np.unravel_index(np.argmax(excess), excess.shape)
-    assert excess.max() <= 0, (f"{what}: element {worst} got {g[worst]:.5f} ref {ref[worst]:.5f} "
-                               f"(excess {excess.max():.3e}, bound {bound[worst]:.3e})")
-
-
 def _check_grads(grads, ins, what, softmax1=False):
     ref = ob.v2_bwd(*ins, softmax1=softmax1)
-    bnd = ob.v2_bwd_rounding_bounds(*ins, softmax1=softmax1)
-    for name, got, r, bd in zip(("dq", "dk", "dv", "dlam"), grads, ref, bnd):
-        assert_grad_close(got, r, bd, f"{name} {what}")
+    yard = bf16_module.v2_grads(*ins, softmax1=softmax1)
+    for name, got, r, y in zip(("dq", "dk", "dv", "dlam"), grads, ref, yard):
+        assert_grad_close(got, r, f"{name} {what}", yard=y)
 
 
 def _inputs(B, T, Hq, Hkv, d, seed):
@@ -149,15 +138,6 @@ def test_backward_full_size_properties():
 
 # ==== DIFF V1 =======================================================================
 #
-# Tolerance.  Besides the roundings the V2 path has (P, dS and d a_m held in
-# bf16), the V1 backward rebuilds D = a_1 - lam a_2 from the training
-# forward's bf16 map outputs, and the RMSNorm's backward scales that rounding
-# by r = 1/rms(D).  oracle.backward.v1_bwd_rounding_bounds follows every
-# rounded value through the same steps; summed as independent roundings
-# (root of the sum of squares, the typical size) it is ~1% of a typical
-# gradient element.  Each element must satisfy |x - ref| <= 2e-2 |ref| +
-# 8 b + 1e-4.
-
 V1_GRADS = ("dq1", "dq2", "dk1", "dk2", "dv", "dlq1", "dlk1", "dlq2", "dlk2")
 
 
@@ -172,15 +152,9 @@ def _v1_in(B, H, T, d, seed):
 def _v1_check(grads, args, layer, dout, what, softmax1=False):
     cpu = [a.cpu() for a in args]
     ref = ob.v1_bwd(*cpu, layer, dout.cpu(), softmax1=softmax1)
-    bnd = ob.v1_bwd_rounding_bounds(*cpu, layer, dout.cpu(), softmax1=softmax1)
-    for name, got, r, b in zip(V1_GRADS, grads, ref, bnd):
-        g = host64(got)
-        assert g.shape == r.shape, (name, g.shape, r.shape)
-        assert np.all(np.isfinite(g)), f"{name} {what}: non-finite"
-        excess = np.abs(g - r) - (2e-2 * np.abs(r) + 8.0 * b + 1e-4)
-        worst = np.unravel_index(np.argmax(excess), excess.shape)
-        assert excess.max() <= 0, (f"{name} {what}: element {worst} got {g[worst]:.5f} ref {r[worst]:.5f} "
-                                   f"(excess {excess.max():.3e}, bound {b[worst]:.3e})")
+    yard = bf16_module.v1_grads(*cpu, layer, dout.cpu(), softmax1=softmax1)
+    for name, got, r, y in zip(V1_GRADS, grads, ref, yard):
+        assert_grad_close(got, r, f"{name} {what}", yard=y)
 
 
 @pytest.mark.parametrize("s1", [False, True])
@@ -263,8 +237,65 @@ def test_v1_backward_3b_shape_sampled_heads():
         sub = [a[b:b + 1, h:h + 1].cpu() for a in args[:5]] + [a.cpu() for a in args[5:]]
         dsub = dout[b:b + 1, :, h:h + 1].cpu()
         ref = ob.v1_bwd(*sub, 14, dsub)
-        bnd = ob.v1_bwd_rounding_bounds(*sub, 14, dsub)
-        for name, got, r, bd in list(zip(V1_GRADS, grads, ref, bnd))[:5]:
-            gg = host64(got[b:b + 1, h:h + 1])
-            excess = np.abs(gg - r) - (2e-2 * np.abs(r) + 8.0 * bd + 1e-4)
-            assert excess.max() <= 0, (name, b, h, excess.max())
+        yard = bf16_module.v1_grads(*sub, 14, dsub)
+        for name, got, r, y in list(zip(V1_GRADS, grads, ref, yard))[:5]:
+            assert_grad_close(got[b:b + 1, h:h + 1], r, f"{name} b{b} h{h}", yard=y)
+
+
+# ==== regressions and full-size checks ==================================================
+
+@pytest.mark.parametrize("G,d", [(2, 64), (8, 128)])
+def test_v2_row0_dq_is_zero(G, d):
+    """Row 0 of every head sees one key, so its P is 1 and dS = dP - D = 0:
+    dq there is exactly 0.  The kernels take D from the same bf16 d attn the
+    dP product sees (the odd head's -sigmoid(lam) dout rounded), so what is
+    left is fp32 summation order."""
+    y, dout = _inputs(2, 300, G * 2, 2, d, seed=930 + G)
+    _, attn, lse = binding.v2_fwd_train(y["q"], y["k"], y["v"], y["lam"])
+    dq = binding.v2_bwd(y["q"], y["k"], y["v"], y["lam"], attn, lse, dout)[0]
+    torch.cuda.synchronize()
+    assert dq[:, 0].abs().max().item() <= 1e-4, dq[:, 0].abs().max().item()
+
+
+def test_v1_row0_dq_is_zero():
+    args, dout = _v1_in(2, 3, 200, 64, seed=940)
+    _, a1, a2, lse = binding.v1_fwd_train(*args, 5)
+    grads = binding.v1_bwd(*args, 5, a1, a2, lse, dout)
+    torch.cuda.synchronize()
+    for g in grads[:2]:
+        assert g[:, :, 0].abs().max().item() <= 1e-4, g[:, :, 0].abs().max().item()
+
+
+def test_backward_full_size_sampled():
+    """The V2 prefill workload (B 1, T 8192, 64 query heads, 8 kv heads):
+    for two kv groups, dq of sampled rows of all 8 heads, dk and dv of
+    sampled keys and every dlam of the group's pairs, against the sampled
+    oracle run on that group's inputs alone (a group's gradients depend only
+    on its own q heads, k, v, lambda logits and dout)."""
+    w = workloads.WORKLOADS["v2_prefill_B1_T8192_Hq64_Hkv8_d128"]
+    y = workloads.inputs_for(w, DEV)
+    g = torch.Generator(device=DEV).manual_seed(4321)
+    dout = torch.randn((w.B, w.T, w.Hq // 2, w.d), generator=g, device=DEV).to(torch.bfloat16)
+    _, attn, lse = binding.v2_fwd_train(y["q"], y["k"], y["v"], y["lam"])
+    dq, dk, dv, dlam = binding.v2_bwd(y["q"], y["k"], y["v"], y["lam"], attn, lse, dout)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    ts = [0, 1, 2, 31, 32, 127, 128, 1000, 4095, 4096, 8190, 8191]
+    js = [0, 1, 31, 32, 2047, 4096, 8000, 8191]
+    for grp in (0, 5):
+        hs, ps = slice(grp * G, (grp + 1) * G), slice(grp * G // 2, (grp + 1) * G // 2)
+        sub = [y["q"][:, :, hs], y["k"][:, :, grp:grp + 1], y["v"][:, :, grp:grp + 1], y["lam"][:, :, ps],
+               dout[:, :, ps]]
+        rows = [(0, t, h) for t in ts for h in range(G)]
+        keys = [(0, j, 0) for j in js]
+        rq, rk, rv, rl = ob.v2_bwd_sampled(*_cpu(*sub), rows, keys)
+        got_q = torch.stack([dq[0, t, grp * G + h] for _, t, h in rows])
+        got_k = torch.stack([dk[0, j, grp] for _, j, _ in keys])
+        got_v = torch.stack([dv[0, j, grp] for _, j, _ in keys])
+        assert_grad_close(got_q, rq, f"dq group {grp}")
+        assert_grad_close(got_k, rk, f"dk group {grp}")
+        assert_grad_close(got_v, rv, f"dv group {grp}")
+        assert_grad_close(dlam[:, :, ps], rl, f"dlam group {grp}")
+        assert dq[0, 0, hs].abs().max().item() <= 1e-4  # row 0: exactly 0
+    del y, dq, dk, dv, attn
+    torch.cuda.empty_cache()
