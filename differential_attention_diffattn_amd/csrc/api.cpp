@@ -255,6 +255,7 @@ static da_status v1_fwd_impl(int softmax1, da_dtype dtype, int B, int H, int T, 
   const float li = (float)diffattn_lambda_init(layer_index);
   hipStream_t s = (hipStream_t)stream;
   if (dtype == DA_BF16) {
+    const da_in k1o = k1, k2o = k2;
     if (rope) {  // k1, k2 rotated into the workspace as [B,H,T,d]; q1, q2 in the kernel's prologue
       for (int m = 0; m < 2; ++m) {
         da::RopeArgs r{};
@@ -270,6 +271,7 @@ static da_status v1_fwd_impl(int softmax1, da_dtype dtype, int B, int H, int T, 
     }
     da::PrefillArgs a{};
     a.q1 = tin(q1), a.q2 = tin(q2), a.k1 = tin(k1), a.k2 = tin(k2), a.v = tin(v);
+    a.k1o = tin(k1o), a.k2o = tin(k2o);
     if (rope) {
       a.rope = 1;
       rope_tab(rope->theta, d, &a.rope_w);

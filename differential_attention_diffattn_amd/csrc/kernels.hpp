@@ -49,6 +49,10 @@ struct PrefillArgs {
   // t * w_c
   int rope;
   RopeTab rope_w;
+  // V1 with rope: the keys before rotation (k1, k2 then hold them rotated
+  // and rounded to bf16); the cancellation guard's exact rows rotate these
+  // in fp32.  Without rope the same as k1, k2.
+  TIn k1o, k2o;
 };
 
 hipError_t launch_prefill_v1_bf16(int d, const PrefillArgs& a, hipStream_t s);

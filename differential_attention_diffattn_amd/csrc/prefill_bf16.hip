@@ -45,6 +45,15 @@
 //   * Causal skipping at 32-key granularity (mask only on diagonal
 //     sub-blocks); heaviest tiles first; workgroups mapped onto XCDs so the
 //     tiles of one head share an L2.
+//   * V1 cancellation guard.  Each map's P enters its P.V product rounded to
+//     bf16 (relative 2^-9), so A1 V and A2 V each carry an error of about
+//     1e-3 of their size.  Where they nearly cancel (lambda near 1 and two
+//     maps that nearly agree, e.g. a row with two visible keys) the RMSNorm
+//     scales D = A1 V - lam A2 V back to O(1) and with it that error, by
+//     the factor kappa = |(A1 V, lam A2 V)| / |D|.  A row with kappa > 8 is
+//     recomputed by its map-1 wave from the definition in fp32 (both maps,
+//     exact softmax, P unrounded): the fast path's error stays below ~1e-2
+//     and a flagged row's below 1e-5.  Random inputs flag no rows.
 #include <math.h>
 
 #include <type_traits>
@@ -134,6 +143,157 @@ struct Probs {
   bf16x8 p[MPW][2];  // bf16 B operand of P.V, two 16-key halves
   float bs[MPW];     // this lane's sum of the block's probabilities
 };
+
+// kappa^2 above which a V1 row is recomputed exactly (kappa > 8).
+constexpr float kCancel2 = 64.f;
+
+// One V1 output row (batch b, differential head h, query row i) from the
+// definition, in fp32 and with the whole wave: both maps' scores
+// q_m . k_m,j / sqrt d for j <= i (lane = key, 64 keys per chunk), an online
+// softmax over the chunks with the exact row maximum and no rounding of P,
+// A_m V over the 2d channels (lane = DV/64 consecutive channels), then
+// D = A1 V - lam A2 V, the RMSNorm and the scale, stored to out.  buf (LDS,
+// 2D floats) holds the two q rows.  With rope, q and the keys as given are
+// turned here in fp32 (the key loop reads keys rotated and rounded to bf16).
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef const __attribute__((address_space(4))) PrefillArgs kargs_t;  // the kernel's argument in its segment
+template <int D, int DV>
+__device__ __forceinline__ void v1_exact_row(int b, int h, int i, float lam, lds_f32* buf, int lane) {
+  constexpr int CPL = DV / 64;  // V channels per lane (2 or 4)
+  // The arguments are read from the kernel argument segment (the kernel's
+  // only argument sits at its start) through a pointer the compiler cannot
+  // see through: none of them is then loaded at kernel entry and kept live
+  // across the key loop for this rarely taken path.
+  kargs_t* ap = (kargs_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(ap));
+  lds_f32* qs = buf;
+  // keys as given (with rope: before rotation, turned below in fp32)
+  const uint16_t* kq0 = (const uint16_t*)ap->k1o.p + b * ap->k1o.sb + h * ap->k1o.sh;
+  const uint16_t* kq1 = (const uint16_t*)ap->k2o.p + b * ap->k2o.sb + h * ap->k2o.sh;
+  const int64_t kst0 = ap->k1o.st, kst1 = ap->k2o.st;
+  const int64_t vst = ap->v.st;
+  const uint16_t* vb = (const uint16_t*)ap->v.p + b * ap->v.sb + h * ap->v.sh + lane * CPL;
+  const int rope = ap->rope, softmax1 = ap->softmax1;
+  const float sl2 = ap->sl2, lam_init = ap->lam_init;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const uint16_t* qr = m ? (const uint16_t*)ap->q2.p + b * ap->q2.sb + h * ap->q2.sh + (int64_t)i * ap->q2.st
+                           : (const uint16_t*)ap->q1.p + b * ap->q1.sb + h * ap->q1.sh + (int64_t)i * ap->q1.st;
+    for (int c = lane; c < D / 2; c += 64) {
+      float x1 = bf16_to_f32(qr[c]), x2 = bf16_to_f32(qr[c + D / 2]);
+      if (rope) {
+        float sn, cs;
+        rope_sincos(i, ap->rope_w.hi[c], ap->rope_w.lo[c], &sn, &cs);
+        const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+        x1 = y1;
+        x2 = y2;
+      }
+      qs[m * D + c] = x1;
+      qs[m * D + c + D / 2] = x2;
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  float M[2], Z[2], O[2][CPL];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    // off-by-one softmax: one more logit 0 with a zero value row
+    M[m] = softmax1 ? 0.f : -INFINITY;
+    Z[m] = softmax1 ? 1.f : 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) O[m][e] = 0.f;
+  }
+  for (int j0 = 0; j0 <= i; j0 += 64) {
+    const int j = min(j0 + lane, i);  // lanes past the row read its last key (masked below)
+    // opaque per chunk: the q reads are re-issued (broadcast LDS reads), not
+    // hoisted out of the loop into 2d registers
+    uint32_t qa = (uint32_t)(uintptr_t)qs;
+    asm volatile("" : "+v"(qa));
+    const lds_f32* qc = (const lds_f32*)(uintptr_t)qa;
+    float p[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint16_t* kr = m ? kq1 + (int64_t)j * kst1 : kq0 + (int64_t)j * kst0;
+      float acc = 0.f;
+      if (rope) {  // key j turned by j * w_c, pairs (c, c + d/2), in fp32
+#pragma unroll 2
+        for (int c = 0; c < D / 2; c += 8) {
+          const uint4 wa = *(const uint4*)(kr + c), wb = *(const uint4*)(kr + c + D / 2);
+          const uint32_t ua[4] = {wa.x, wa.y, wa.z, wa.w}, ub[4] = {wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x1 = __builtin_bit_cast(float, (e & 1) ? ua[e / 2] & 0xffff0000u : ua[e / 2] << 16);
+            const float x2 = __builtin_bit_cast(float, (e & 1) ? ub[e / 2] & 0xffff0000u : ub[e / 2] << 16);
+            float sn, cs;
+            rope_sincos(j, ap->rope_w.hi[c + e], ap->rope_w.lo[c + e], &sn, &cs);
+            acc += qc[m * D + c + e] * (x1 * cs - x2 * sn) + qc[m * D + c + e + D / 2] * (x2 * cs + x1 * sn);
+          }
+        }
+      } else {
+#pragma unroll 4
+        for (int c = 0; c < D; c += 8) {
+          const uint4 w = *(const uint4*)(kr + c);
+          const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc += __builtin_bit_cast(float, u[e] << 16) * qc[m * D + c + 2 * e];
+            acc += __builtin_bit_cast(float, u[e] & 0xffff0000u) * qc[m * D + c + 2 * e + 1];
+          }
+        }
+      }
+      const float sc = j0 + lane <= i ? acc * sl2 : -INFINITY;  // log2 units
+      float cm = sc;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o, 64));
+      const float nM = fmaxf(M[m], cm);
+      const float al = exp2f(M[m] - nM);
+      p[m] = exp2f(sc - nM);
+      Z[m] = Z[m] * al + wave_sum(p[m]);
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) O[m][e] *= al;
+      M[m] = nM;
+    }
+    const int n = min(64, i + 1 - j0);
+#pragma unroll 8
+    for (int jj = 0; jj < n; ++jj) {
+      const float p1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p[0]), jj));
+      const float p2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p[1]), jj));
+      const uint16_t* vr = vb + (int64_t)(j0 + jj) * vst;
+      float x[CPL];
+      if constexpr (CPL == 2) {
+        const uint32_t w = *(const uint32_t*)vr;
+        x[0] = __builtin_bit_cast(float, w << 16);
+        x[1] = __builtin_bit_cast(float, w & 0xffff0000u);
+      } else {
+        const uint2 w = *(const uint2*)vr;
+        x[0] = __builtin_bit_cast(float, w.x << 16);
+        x[1] = __builtin_bit_cast(float, w.x & 0xffff0000u);
+        x[2] = __builtin_bit_cast(float, w.y << 16);
+        x[3] = __builtin_bit_cast(float, w.y & 0xffff0000u);
+      }
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        O[0][e] = fmaf(p1, x[e], O[0][e]);
+        O[1][e] = fmaf(p2, x[e], O[1][e]);
+      }
+    }
+  }
+  // D = A1 V - lam A2 V, RMSNorm over the 2d channels, (1 - lambda_init)
+  const float r1 = 1.f / Z[0], r2 = lam / Z[1];
+  float dd[CPL], ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    dd[e] = O[0][e] * r1 - O[1][e] * r2;
+    ss += dd[e] * dd[e];
+  }
+  const float post = (1.f - lam_init) / sqrtf(wave_sum(ss) * (1.f / DV) + 1e-5f);
+  uint16_t* dst = (uint16_t*)ap->out.p + b * ap->out.sb + (int64_t)i * ap->out.st + h * ap->out.sh + lane * CPL;
+  if constexpr (CPL == 2) {
+    *(uint32_t*)dst = pack_bf16x2(dd[0] * post, dd[1] * post);
+  } else {
+    *(uint2*)dst = make_uint2(pack_bf16x2(dd[0] * post, dd[1] * post), pack_bf16x2(dd[2] * post, dd[3] * post));
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the next row rewrites qs
+}
 
 template <int D, int DV, bool V2, int NW, int MPW, bool PIPE>
 __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_BLOCKS))
@@ -707,7 +867,7 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
       return lam * inv2;
     }
   };
-  float ss = 0.f;
+  float ss = 0.f, s12 = 0.f;  // sums of D^2 and of (A1 V)^2 + (lam A2 V)^2 (V1 cancellation guard)
   if constexpr (MPW == 1) {
     // map 2's wave hands its weighted O to its partner through LDS
     if constexpr (!C::SEPX) __syncthreads();  // every wave is done with the K/V stages
@@ -738,12 +898,15 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
         const f32x4 x = xch[(cb * 4 + g) * 64 + lane];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float dv = o[0][cb][4 * g + j] * inv[0] - x[j];
+          const float a1 = o[0][cb][4 * g + j] * inv[0];
+          const float dv = a1 - x[j];
           o[0][cb][4 * g + j] = dv;
           ss += dv * dv;
+          if constexpr (!V2) s12 += a1 * a1 + x[j] * x[j];
         }
       }
   } else {
+    static_assert(V2 || MPW == 1, "the V1 cancellation guard uses the partner exchange slots");
     if (!active) return;
     const float w = second_weight(inv[1]);
 #pragma unroll
@@ -757,14 +920,17 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
   }
   uint16_t* dst;
   float post = 1.f;
+  uint64_t flagged = 0;  // V1: rows (bit li) whose maps cancel, recomputed exactly below
   if constexpr (!V2) {
     ss += __shfl_xor(ss, 32, 64);
+    s12 += __shfl_xor(s12, 32, 64);
+    flagged = __ballot(row < T && s12 > kCancel2 * ss) & 0xffffffffull;
     post = (1.f - a.lam_init) / sqrtf(ss * (1.f / DV) + 1e-5f);
     dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)row * a.out.st + h * a.out.sh;
   } else {
     dst = (uint16_t*)a.out.p + b * a.out.sb + (int64_t)row * a.out.st + pair * a.out.sh;
   }
-  if (row < T) {
+  if (row < T && !((flagged >> li) & 1)) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -775,6 +941,18 @@ __global__ void __launch_bounds__(NW * 64, (Cfg<D, DV, V2, NW, MPW, PIPE>::MIN_B
         w.y = pack_bf16x2(o[0][cb][4 * g4 + 2] * post, o[0][cb][4 * g4 + 3] * post);
         *(uint2*)(dst + c) = w;
       }
+  }
+  if constexpr (!V2) {
+    if (flagged) {
+      // this slot's exchange area (map 2's values were read above) holds the q rows
+      lds_f32* buf = (lds_f32*)(uintptr_t)(smem_lds + C::XBASE) + slot * (CB * 4 * 64 * 4);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      while (flagged) {
+        const int r = __builtin_ctzll(flagged);
+        flagged &= flagged - 1;
+        v1_exact_row<D, DV>(b, h, i0w + r, lam, buf, lane);
+      }
+    }
   }
 }
 

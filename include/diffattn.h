@@ -164,9 +164,9 @@ da_status diffattn_v2_decode(da_dtype dtype, int B, int L, int Hq, int Hkv, int 
                              void* stream);
 
 /*
- * Off-by-one softmax variants (Hacker News item 41780844: the comment that
- * softmax "should be exp()/1+sum exp()", with 1 added to the denominator,
- * and that adding an extra zero value to the logits does the same).  Each
+ * Off-by-one softmax variants (Hacker News item 41780844, a comment
+ * proposing that the softmax denominator gain an extra 1, equivalently an
+ * extra logit of value 0 among the inputs).  Each
  * entry point computes exactly what its namesake above computes, with every
  * softmax map replaced by
  *     softmax1_j(x) = exp(x_j) / (1 + sum_k exp(x_k))

@@ -144,6 +144,109 @@ def test_v1_bf16_3b_sampled():
     assert_bf16_close(got, ref, w.name)
 
 
+# ------------------------------------------------- V1 cancellation regime
+# Hacker News "Differential Transformer" board, posts #131 and #135: with
+# identical maps A1 = A2 the method gives (1 - lam) A, and lam may take any
+# sign.  Where the two maps nearly agree and lam is near 1, D = A1 V - lam A2 V
+# cancels and the RMSNorm scales it back to O(1); the kernel recomputes such
+# rows exactly, so every case below holds the bf16 bar.
+
+def _set_lambda(x, layer, target):
+    """Rewrite the four lambda vectors (fp32, constant) so that
+    exp(lq1.lk1) - exp(lq2.lk2) + lambda_init = target."""
+    d = x["lq1"].numel()
+    li = oracle.lambda_init(layer)
+    for n in ("lq1", "lk1", "lq2", "lk2"):
+        x[n].zero_()
+    if target >= li:  # exp(a) = 1 + target - li, exp(b) = 1
+        c = math.sqrt(math.log1p(target - li) / d)
+        x["lq1"].fill_(c), x["lk1"].fill_(c)
+    else:             # exp(a) = 1, exp(b) = 1 + li - target
+        c = math.sqrt(math.log1p(li - target) / d)
+        x["lq2"].fill_(c), x["lk2"].fill_(c)
+    got = oracle.v1_lambda(*[x[n].cpu() for n in ("lq1", "lk1", "lq2", "lk2")], layer)
+    assert abs(got - target) < 1e-6, (got, target)
+
+
+def _sdpa_rmsnorm(q, k, v, lam, li):
+    """(1 - lambda_init) RMSNorm((1 - lam) causal_attention(q, k, v)), fp64 on
+    the CPU with torch's SDPA: identical branches in closed form."""
+    qd, kd, vd = [t.cpu().double() for t in (q, k, v)]
+    a = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, is_causal=True)  # [B,H,T,2d]
+    D = (1.0 - lam) * a
+    y = D / torch.sqrt((D * D).mean(-1, keepdim=True) + 1e-5) * (1.0 - li)
+    return y.transpose(1, 2).numpy()  # [B,T,H,2d]
+
+
+@pytest.mark.parametrize("target", [None, 0.95, 1.0, 1.05, -0.5])
+@pytest.mark.parametrize("d", [64, 128])
+def test_v1_identical_branches(d, target):
+    """Q2 = Q1, K2 = K1: out = (1 - li) RMSNorm((1 - lam) A V) (post #131),
+    for the drawn lambda and for lambda built to 0.95, 1, 1.05 and -0.5."""
+    layer = 6
+    x = workloads.v1_inputs(2, 3, 300, d, torch.bfloat16, seed=1400 + d, device=DEV)
+    x["q2"].copy_(x["q1"]), x["k2"].copy_(x["k1"])
+    if target is not None:
+        _set_lambda(x, layer, target)
+    lam = oracle.v1_lambda(*[x[n].cpu() for n in ("lq1", "lk1", "lq2", "lk2")], layer)
+    out = _v1_run(x, layer)
+    assert_bf16_close(out, oracle.v1_fwd(*_v1_cpu(x), layer), f"identical d{d} lam {lam:.4f}")
+    ref = _sdpa_rmsnorm(x["q1"], x["k1"], x["v"], lam, oracle.lambda_init(layer))
+    assert_bf16_close(out, ref, f"identical d{d} lam {lam:.4f} vs SDPA closed form")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_v1_lambda_zero_reduces_to_attention(d):
+    """lambda built to 0 from the vectors: out = (1 - li) RMSNorm(A1 V), the
+    standard causal attention of the first map (torch SDPA, fp64)."""
+    layer = 3
+    x = workloads.v1_inputs(2, 3, 257, d, torch.bfloat16, seed=1500 + d, device=DEV)
+    _set_lambda(x, layer, 0.0)
+    out = _v1_run(x, layer)
+    assert_bf16_close(out, oracle.v1_fwd(*_v1_cpu(x), layer), f"lam 0 d{d}")
+    ref = _sdpa_rmsnorm(x["q1"], x["k1"], x["v"], 0.0, oracle.lambda_init(layer))
+    assert_bf16_close(out, ref, f"lam 0 d{d} vs SDPA")
+
+
+@pytest.mark.parametrize("s1", [False, True])
+@pytest.mark.parametrize("eps", [0.02, 0.2])
+@pytest.mark.parametrize("target", [0.95, 1.0, 1.05])
+@pytest.mark.parametrize("d", [64, 128])
+def test_v1_near_identical_branches(d, target, eps, s1):
+    """Q2 = Q1 + eps N(0,1), K2 = K1 + eps N(0,1) with lambda near 1: the maps
+    nearly agree on every row and D cancels by factors of ~10 to ~1000."""
+    layer = 9
+    x = workloads.v1_inputs(1, 2, 300, d, torch.bfloat16, seed=1600 + d, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(1601 + d)
+    for a, b in (("q2", "q1"), ("k2", "k1")):
+        x[a].copy_((x[b].float() + eps * torch.randn(x[b].shape, generator=g, device=DEV)).to(torch.bfloat16))
+    _set_lambda(x, layer, target)
+    out = _v1_run(x, layer, softmax1=s1)
+    assert_bf16_close(out, oracle.v1_fwd(*_v1_cpu(x), layer, softmax1=s1),
+                      f"near-identical d{d} lam {target} eps {eps} softmax1 {s1}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_v1_near_identical_branches_training_forward_and_rope(d):
+    """The training forward's out is the inference forward's bit for bit, and
+    the RoPE entry point recomputes cancelling rows with q rotated."""
+    layer = 9
+    x = workloads.v1_inputs(1, 2, 200, d, torch.bfloat16, seed=1700 + d, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(1701 + d)
+    for a, b in (("q2", "q1"), ("k2", "k1")):
+        x[a].copy_((x[b].float() + 0.02 * torch.randn(x[b].shape, generator=g, device=DEV)).to(torch.bfloat16))
+    _set_lambda(x, layer, 1.0)
+    args = [x[n] for n in V1_NAMES]
+    out, _, _, _ = binding.v1_fwd_train(*args, layer)
+    inf = binding.v1_fwd(*args, layer)
+    rot = binding.v1_fwd(*args, layer, theta=10000.0)
+    torch.cuda.synchronize()
+    assert torch.equal(out, inf)
+    assert_bf16_close(inf, oracle.v1_fwd(*_v1_cpu(x), layer), f"near-identical d{d}")
+    from oracle import prologue as op
+    assert_bf16_close(rot, op.v1_fwd_rope(*_v1_cpu(x), layer), f"near-identical rope d{d}")
+
+
 def test_v1_strided_layouts_are_bitwise_equal():
     """The interleaved layout of Wilsontomass's module (q viewed as
     [B,T,nh,2,hd], q1 = q[..., 0, :]) is passed as strided views; the
@@ -589,17 +692,15 @@ def test_multi_decode_full_sampled():
 # ------------------------------------------------------- off-by-one softmax
 # (every map's denominator + exp(0); Hacker News item 41780844)
 
+@pytest.mark.parametrize("layer", [0, 4])
 @pytest.mark.parametrize("d,T", [(64, 1), (64, 33), (64, 300), (128, 33), (128, 300)])
-def test_softmax1_v1_bf16(d, T):
-    """(Layer 0: lambda ~ 0.2.  With lambda near 1 a row whose two maps agree
-    -- e.g. row 1, two visible keys -- has D = A1 V - lambda A2 V cancel, and
-    the RMSNorm magnifies the 2^-9 rounding of the bf16 probabilities by
-    |A1 V| / |D|; at this seed at layer 4 one such row (lambda = 1.006,
-    factor 51) exceeds the tolerance for the standard and the off-by-one
-    softmax alike.)"""
+def test_softmax1_v1_bf16(d, T, layer):
+    """(At layer 4, d 128, T 300 this seed draws lambda = 1.006, and row 1 of
+    one head has two maps that nearly agree: D cancels by a factor of ~51,
+    a row the cancellation guard recomputes exactly.)"""
     x = workloads.v1_inputs(2, 3, T, d, torch.bfloat16, seed=500 + d + T, device=DEV)
-    out = _v1_run(x, 0, softmax1=True)
-    assert_bf16_close(out, oracle.v1_fwd(*_v1_cpu(x), 0, softmax1=True), f"softmax1 v1 d{d} T{T}")
+    out = _v1_run(x, layer, softmax1=True)
+    assert_bf16_close(out, oracle.v1_fwd(*_v1_cpu(x), layer, softmax1=True), f"softmax1 v1 d{d} T{T} layer {layer}")
 
 
 @pytest.mark.parametrize("d", [64, 128])
