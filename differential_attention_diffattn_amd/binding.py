@@ -97,6 +97,10 @@ def load_library():
         f.argtypes = [i, i, i, i, i, i, i, DaIn, DaIn, DaIn, i, i, vp, ctypes.c_int64, vp, DaIn, DaOut, vp,
                       ctypes.c_size_t, vp]
         f.restype = i
+    lib.diffattn_v2_decode_noalloc.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaOut, vp]
+    lib.diffattn_v2_decode_noalloc.restype = i
+    lib.diffattn_v2_decode_noalloc_max_bytes.argtypes = []
+    lib.diffattn_v2_decode_noalloc_max_bytes.restype = ctypes.c_size_t
     fl = ctypes.c_float
     lib.diffattn_rope.argtypes = [i, i, i, i, i, DaIn, DaOut, fl, i, vp]
     lib.diffattn_rope.restype = i
@@ -427,6 +431,28 @@ def v2_decode(q, k_cache, v_cache, lam, out: torch.Tensor | None = None,
                             workspace.numel() * workspace.element_size(), _stream(q))
     if st != 0:
         raise DiffAttnError(st, name)
+    return out
+
+
+def v2_decode_noalloc(q, k_cache, v_cache, lam, out: torch.Tensor):
+    """DIFF V2 decode into a caller-given ``out`` [B,Hq/2,d] without any device
+    allocation (the library's static scratch holds the split partials);
+    q [B,Hq,d], caches [B,L,Hkv,d], lam [B,Hq/2]."""
+    lib = load_library()
+    B, Hq, d = q.shape
+    L, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, L, Hkv, d) or tuple(v_cache.shape) != (B, L, Hkv, d):
+        raise ValueError("caches must be [B,L,Hkv,d]")
+    if tuple(lam.shape) != (B, Hq // 2) or lam.dtype != torch.float32:
+        raise ValueError("lam must be fp32 [B,Hq/2]")
+    if tuple(out.shape) != (B, Hq // 2, d):
+        raise ValueError("out must be [B,Hq/2,d]")
+    _check_device(q, k_cache, v_cache, out)
+    st = lib.diffattn_v2_decode_noalloc(_dtype_code(q), B, L, Hq, Hkv, d, _in(q, 0, 1, None), _in(k_cache, 0, 2, 1),
+                                        _in(v_cache, 0, 2, 1), _in(lam, 0, 1, None), _out(out, 0, 1, None),
+                                        _stream(q))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_v2_decode_noalloc")
     return out
 
 

@@ -8,6 +8,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/diffattn.h"
 #include "kernels.hpp"
 
@@ -98,10 +100,10 @@ struct DecodeGeom {
   int ncg;
   da::DecodeSplit sp;
 };
-DecodeGeom decode_geom(int B, int L, int nq, int Hq, int Hkv, int max_chunk) {
+DecodeGeom decode_geom(int B, int L, int nq, int Hq, int Hkv, int max_chunk, int max_splits = 0x7fffffff) {
   DecodeGeom r;
   r.ncg = da::decode_column_groups(nq, Hq / Hkv);
-  r.sp = da::decode_split(B * r.ncg, L, Hkv, max_chunk);
+  r.sp = da::decode_split(B * r.ncg, L, Hkv, max_chunk, max_splits);
   return r;
 }
 bool decode_sizes_ok(int B, int L, int nq, int Hq, int Hkv, int d) {
@@ -109,10 +111,40 @@ bool decode_sizes_ok(int B, int L, int nq, int Hq, int Hkv, int d) {
   if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return false;
   return (long long)B * nq <= 0x7fffffffLL && (long long)nq * Hq <= 0x7fffffffLL;
 }
-size_t decode_ws_bytes(int B, int L, int nq, int Hq, int Hkv, int d, int max_chunk) {
+// Bytes of one split's partials: (m, l, O[d]) fp32 per (b, kv head, column).
+size_t decode_split_bytes(int B, int nq, int Hq, int Hkv, int d) {
+  return (size_t)B * Hkv * (size_t)nq * (size_t)(Hq / Hkv) * (size_t)(d + 2) * sizeof(float);
+}
+size_t decode_ws_bytes(int B, int L, int nq, int Hq, int Hkv, int d, int max_chunk, int max_splits = 0x7fffffff) {
   if (!decode_sizes_ok(B, L, nq, Hq, Hkv, d)) return 0;
-  const DecodeGeom gm = decode_geom(B, L, nq, Hq, Hkv, max_chunk);
-  return (size_t)B * Hkv * gm.sp.nsplit * (size_t)nq * (size_t)(Hq / Hkv) * (size_t)(d + 2) * sizeof(float);
+  const DecodeGeom gm = decode_geom(B, L, nq, Hq, Hkv, max_chunk, max_splits);
+  return gm.sp.nsplit * decode_split_bytes(B, nq, Hq, Hkv, d);
+}
+
+// ---- the decode entry point that allocates nothing --------------------------
+// Its split partials live in this file-scope device array: one copy per GPU,
+// allocated when the library's code object is loaded and held until the
+// process ends.  kScratchBytes bounds the partials (B x Hkv x splits x
+// columns x (d + 2) fp32); the split count is lowered until they fit.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device.  In host code the
+// array's name is only a stand-in: its device address is looked up once per
+// device, with that device current, and kept.
+void* scratch_on_current_device() {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
 }
 
 // Shared by the dense and paged decode entry points.  q, lam and out carry a
@@ -126,7 +158,8 @@ struct PagedArgs {
 };
 da_status decode_impl(int softmax1, da_dtype dtype, int B, int L, int nq, int Hq, int Hkv, int d, da_in q,
                       da_in kc, da_in vc, const PagedArgs* pg, da_in lam, da_out out, void* workspace,
-                      size_t workspace_bytes, void* stream, float rope_theta = 0.f) {
+                      size_t workspace_bytes, void* stream, float rope_theta = 0.f,
+                      int max_splits = 0x7fffffff, bool use_scratch = false) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
   if (rope_theta != 0.f && (!rope_theta_ok(rope_theta) || (long long)L >= kMaxRopePos)) return DA_E_SHAPE;
   if (!decode_sizes_ok(B, L, nq, Hq, Hkv, d)) return DA_E_SHAPE;
@@ -157,9 +190,15 @@ da_status decode_impl(int softmax1, da_dtype dtype, int B, int L, int nq, int Hq
       return DA_E_UNSUPPORTED;
   }
   const int max_chunk = pg ? da::kPagedMaxChunk : 2048;
-  const size_t need = decode_ws_bytes(B, L, nq, Hq, Hkv, d, max_chunk);
+  const size_t need = decode_ws_bytes(B, L, nq, Hq, Hkv, d, max_chunk, max_splits);
+  if (use_scratch) {  // every argument checked: now the static scratch of this device
+    if (need > kScratchBytes) return DA_E_SCRATCH;
+    workspace = scratch_on_current_device();
+    workspace_bytes = kScratchBytes;
+    if (!workspace) return DA_E_LAUNCH;
+  }
   if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return DA_E_WORKSPACE;
-  const DecodeGeom gm = decode_geom(B, L, nq, Hq, Hkv, max_chunk);
+  const DecodeGeom gm = decode_geom(B, L, nq, Hq, Hkv, max_chunk, max_splits);
   if (!grid_fits(da::decode_split_grid(B * gm.ncg, Hkv, gm.sp.nsplit)) || !grid_fits((long long)B * nq * (Hq / 2)))
     return DA_E_SHAPE;
 
@@ -210,6 +249,7 @@ const char* diffattn_status_string(da_status s) {
     case DA_E_UNSUPPORTED: return "no kernel for these (valid) arguments";
     case DA_E_WORKSPACE: return "decode workspace missing, misaligned or too small";
     case DA_E_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case DA_E_SCRATCH: return "sizes need more than the library's static decode scratch";
   }
   return "unknown status";
 }
@@ -508,6 +548,21 @@ da_status diffattn_v2_decode(da_dtype dtype, int B, int L, int Hq, int Hkv, int 
   return decode_impl(0, dtype, B, L, 1, Hq, Hkv, d, q, k_cache, v_cache, nullptr, lam, out, workspace,
                      workspace_bytes, stream);
 }
+
+da_status diffattn_v2_decode_noalloc(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
+                                     da_in v_cache, da_in lam, da_out out, void* stream) {
+  if (!decode_sizes_ok(B, L, 1, Hq, Hkv, d)) return DA_E_SHAPE;
+  // as many splits as the static scratch holds (at least one), never more
+  // than the workspace entry point would use
+  const size_t per_split = decode_split_bytes(B, 1, Hq, Hkv, d);
+  if (per_split > kScratchBytes) return DA_E_SCRATCH;
+  const size_t fit = kScratchBytes / per_split;
+  const int max_splits = fit > 0x7fffffff ? 0x7fffffff : (int)fit;
+  return decode_impl(0, dtype, B, L, 1, Hq, Hkv, d, q, k_cache, v_cache, nullptr, lam, out, nullptr, 0, stream,
+                     0.f, max_splits, /*use_scratch=*/true);
+}
+
+size_t diffattn_v2_decode_noalloc_max_bytes(void) { return kScratchBytes; }
 
 da_status diffattn_v2_decode_softmax1(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
                                       da_in k_cache, da_in v_cache, da_in lam, da_out out, void* workspace,

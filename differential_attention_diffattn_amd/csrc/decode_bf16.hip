@@ -387,9 +387,10 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
-DecodeSplit decode_split(int B, int L, int Hkv, int max_chunk) {
-  // Aim for >= 2048 workgroups (8 per CU) and chunks of <= max_chunk tokens;
-  // a chunk is a multiple of the 4 waves x 32 tokens one step consumes.
+DecodeSplit decode_split(int B, int L, int Hkv, int max_chunk, int max_splits) {
+  // Aim for >= 2048 workgroups (8 per CU) and chunks of <= max_chunk tokens,
+  // with at most max_splits splits; a chunk is a multiple of the 4 waves x 32
+  // tokens one step consumes.
   const int step = kWaves * kBlk;
   const long units = (long)B * Hkv;
   long ns = (L + max_chunk - 1) / max_chunk;
@@ -397,6 +398,7 @@ DecodeSplit decode_split(int B, int L, int Hkv, int max_chunk) {
   if (ns < want) ns = want;
   const long maxns = (L + step - 1) / step;
   if (ns > maxns) ns = maxns;
+  if (ns > max_splits) ns = max_splits;
   if (ns < 1) ns = 1;
   long chunk = (L + ns - 1) / ns;
   chunk = (chunk + step - 1) / step * step;

@@ -166,7 +166,7 @@ int decode_column_groups(int nq, int G);
 struct DecodeSplit {
   int chunk, nsplit;
 };
-DecodeSplit decode_split(int B, int L, int Hkv, int max_chunk = 2048);
+DecodeSplit decode_split(int B, int L, int Hkv, int max_chunk = 2048, int max_splits = 0x7fffffff);
 #ifndef DA_PAGED_CHUNK
 #define DA_PAGED_CHUNK 2048
 #endif

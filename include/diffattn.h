@@ -17,7 +17,9 @@
  * Conventions shared by every entry point
  *   Memory    Every tensor pointer is DEVICE memory, allocated and owned by
  *             the caller; the library allocates nothing, keeps no state
- *             between calls and never frees caller memory.
+ *             between calls and never frees caller memory.  The one
+ *             exception is diffattn_v2_decode_noalloc, whose scratch is a
+ *             static device array of the library (see there).
  *   Layout    A tensor is described by da_in / da_out: a base pointer and
  *             element strides for its batch, head and token axes (the
  *             "role" strides).  The head_dim axis is always unit-stride.
@@ -61,7 +63,9 @@ typedef enum {
     DA_E_LAYOUT = 4,      /* misaligned pointer or a stride breaks the rules    */
     DA_E_UNSUPPORTED = 5, /* valid arguments the library has no kernel for     */
     DA_E_WORKSPACE = 6,   /* decode workspace missing or too small              */
-    DA_E_LAUNCH = 7       /* the HIP runtime rejected a kernel launch           */
+    DA_E_LAUNCH = 7,      /* the HIP runtime rejected a kernel launch           */
+    DA_E_SCRATCH = 8      /* diffattn_v2_decode_noalloc: sizes need more than   */
+                          /* the library's static scratch                       */
 } da_status;
 
 typedef enum { DA_FP32 = 0, DA_BF16 = 1 } da_dtype;
@@ -460,6 +464,26 @@ da_status diffattn_v2_decode_paged_rope(da_dtype dtype, int B, int max_len, int 
                                         const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                                         da_in lam, float theta, da_out out, void* workspace,
                                         size_t workspace_bytes, void* stream);
+
+/*
+ * diffattn_v2_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, checks and result as
+ * diffattn_v2_decode (within the bf16 tolerance: the split of the cache may
+ * differ, so the last bits may), but the split partials go to a static
+ * device array of the library, diffattn_v2_decode_noalloc_max_bytes() = 16 MiB
+ * per GPU, allocated when the library is loaded and held until the process
+ * ends.  The call lowers the number of cache splits until the partials
+ * (B * Hkv * splits * Hq/Hkv * (d + 2) * 4 bytes) fit; if one split does
+ * not fit (B * Hq * (d + 2) * 4 > 16 MiB) it returns DA_E_SCRATCH and
+ * enqueues nothing.  It calls no allocating routine.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in
+ * time on one GPU (different streams, or threads without ordering) race and
+ * give wrong results; calls on one stream are ordered and safe.
+ */
+da_status diffattn_v2_decode_noalloc(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
+                                     da_in k_cache, da_in v_cache, da_in lam, da_out out, void* stream);
+size_t diffattn_v2_decode_noalloc_max_bytes(void);
 
 /*
  * DIFF V2 lambda projection ("Differential Transformer V2" article: a

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         s = lib.diffattn_status_string(code)
         assert s and len(s) > 1
     assert lib.diffattn_status_string(0) == b"ok"
@@ -132,6 +132,22 @@ def test_decode_validation(lib):
     assert _dec(lib, ws=0) == E_WS
     assert _dec(lib, ws=FAKE + 4) == E_WS
     assert _dec(lib, wsb=100) == E_WS
+
+
+def test_noalloc_decode_validation(lib):
+    """The no-alloc decode checks its arguments like diffattn_v2_decode (all
+    before it touches a device), and rejects sizes whose split partials do
+    not fit its static scratch."""
+    assert lib.diffattn_v2_decode_noalloc_max_bytes() == 16 << 20
+    f = lambda B=2, L=100, Hq=8, Hkv=2, d=128, dtype=1, out=None: lib.diffattn_v2_decode_noalloc(
+        dtype, B, L, Hq, Hkv, d, _t(), _t(), _t(), _t(), out if out is not None else _t(out=True), None)
+    assert f(L=0) == E_SHAPE
+    assert f(Hq=10, Hkv=2) == E_SHAPE
+    assert f(dtype=0) == E_UNSUP
+    assert f(Hq=64, Hkv=2) == E_UNSUP
+    # one split of B x Hq x (d + 2) fp32 over 16 MiB
+    assert f(B=2048, Hq=16, Hkv=2) == 8
+    assert lib.diffattn_status_string(8) != lib.diffattn_status_string(7)
 
 
 def test_softmax1_entry_points_validate_like_their_namesakes(lib):
