@@ -3,26 +3,31 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline] [--softmax1]
 
-Headline workload (the `value`): the DIFF V1 causal forward at the GPT-2-small
-shape, B=8, T=1024, 6 differential heads, q/k head_dim 64, V width 128, bf16.
-One step = the 12 layer calls of a 12-layer model (layer index 0..11; only
-lambda_init differs between them).  value = algorithmic TFLOP/s over the K
-timed steps (only unmasked (i, j<=i) pairs are counted: 6*B*H*d*T(T+1) per
-call).  Inputs are seeded synthetic N(0,1) tensors already resident in HBM.
+Headline workload (the `value`): the DIFF V2 causal GQA prefill of the
+"Differential Transformer V2" article's DiffAttnV2 at B=1, T=8192, 64 query
+heads (32 differential pairs), 8 kv heads, head_dim 128, bf16 -- the largest
+configuration of the metric that fits one GPU.  One step = one call.  value =
+algorithmic TFLOP/s over the K timed steps (only unmasked (i, j<=i) pairs are
+counted: 2*B*Hq*d*T(T+1) per call).  Inputs are seeded synthetic N(0,1)
+tensors (lambda logits N(0,1) fp32) already resident in HBM.
 
 The JSON line also carries:
-  roofline      the V1 kernel's per-launch duration (HIP events on the stream
-                the library launches on) against the bf16 dense MFMA peak;
-  cpu_baseline  the fp64 oracle timed on a bounded sample of the same
-                workload on this host's cores;
-  secondary     the other full-size workloads (3B-class V1, V2 GQA prefill,
-                the V1 backward at the GPT-2-small and 3B shapes and the V2
+  roofline      the prefill kernel's per-launch duration (HIP events on the
+                stream the library launches on) against the bf16 dense MFMA
+                peak;
+  cpu_baseline  the fp64 oracle timed on a bounded sample of rows of the same
+                workload on this host's cores (the oracle leg);
+  parity        the oracle leg's check of the timed output: sampled rows of
+                every workload against the oracle (outside the timed region);
+  secondary     the other full-size workloads (V1 at the GPT-2-small and
+                3B-class shapes, the V1 backward at both shapes and the V2
                 backward (each timed without its training forward), V2
                 decode, V2 decode of a ragged batch over a paged cache, V2
                 decode of 4 new tokens per sequence, V2 prefill and decode
                 with the rotary embedding, the V2 lambda projection),
-                each with its own roofline; a secondary step is
-                8 launches of the workload (warm-up ~0.3 s of its own calls).
+                each with its own roofline and parity; a secondary step is
+                8 launches of the workload (warm-up ~0.3 s of its own calls;
+                the GPT-2-small V1 step is its 12 layer calls 0..11).
 Logs go to stderr; stdout holds exactly one JSON line.
 """
 from __future__ import annotations
@@ -40,8 +45,8 @@ if ROOT not in sys.path:
 METRIC = "diff-attn causal fwd TFLOP/s (bf16, % MFMA peak); V2 decode HBM GB/s (% peak)"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
-HEADLINE = "v1_gpt2small_B8_H6_T1024_d64"
-SECONDARY = ["v1_3b_B2_H12_T4096_d128", "v2_prefill_B1_T8192_Hq64_Hkv8_d128", "v1_backward_B8_H6_T1024_d64",
+HEADLINE = "v2_prefill_B1_T8192_Hq64_Hkv8_d128"
+SECONDARY = ["v1_gpt2small_B8_H6_T1024_d64", "v1_3b_B2_H12_T4096_d128", "v1_backward_B8_H6_T1024_d64",
              "v1_backward_B2_H12_T4096_d128", "v2_backward_B1_T8192_Hq64_Hkv8_d128",
              "v2_decode_B64_L32768_Hq64_Hkv8_d128", "v2_decode_paged_B64_Lmax32768_P64_Hq64_Hkv8_d128",
              "v2_decode_multi_B64_L32768_nq4_Hq64_Hkv8_d128", "v2_prefill_rope_B1_T8192_Hq64_Hkv8_d128",
@@ -53,56 +58,61 @@ def log(*a):
 
 
 def _caller(w, x, binding, torch, softmax1=False):
-    """Return (fn(layer) -> None) that enqueues one call of workload w
-    (softmax1: the off-by-one softmax entry points)."""
+    """Return (fn(layer) -> None that enqueues one call of workload w, dict of
+    the tensors that call writes) (softmax1: the off-by-one softmax entry
+    points)."""
     if w.kind == "v1":
         out = torch.empty((w.B, w.T, w.H, 2 * w.d), dtype=w.torch_dtype, device=x["v"].device)
         args = [x[n] for n in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")]
-        return lambda layer: binding.v1_fwd(*args, layer, out=out, softmax1=softmax1)
+        return (lambda layer: binding.v1_fwd(*args, layer, out=out, softmax1=softmax1)), {"out": out}
     if w.kind == "v2":
         out = torch.empty((w.B, w.T, w.Hq // 2, w.d), dtype=w.torch_dtype, device=x["v"].device)
-        return lambda layer: binding.v2_fwd(x["q"], x["k"], x["v"], x["lam"], out=out, softmax1=softmax1)
+        return (lambda layer: binding.v2_fwd(x["q"], x["k"], x["v"], x["lam"], out=out, softmax1=softmax1)), \
+            {"out": out}
     if w.kind == "v2_rope":  # rotary embedding: k rotation pass + prefill with q rotated in its prologue
         out = torch.empty((w.B, w.T, w.Hq // 2, w.d), dtype=w.torch_dtype, device=x["v"].device)
         ws = torch.empty(int(binding.load_library().diffattn_v2_fwd_rope_workspace_bytes(w.B, w.T, w.Hkv, w.d)),
                          dtype=torch.uint8, device=x["v"].device)
-        return lambda layer: binding.v2_fwd(x["q"], x["k"], x["v"], x["lam"], out=out, theta=1e4, workspace=ws)
+        return (lambda layer: binding.v2_fwd(x["q"], x["k"], x["v"], x["lam"], out=out, theta=1e4, workspace=ws)), \
+            {"out": out}
     if w.kind == "lam_proj":
         out = torch.empty((w.B, w.T, w.Hq), dtype=torch.float32, device=x["x"].device)
-        return lambda layer: binding.v2_lambda_proj(x["x"], x["w"], out=out)
+        return (lambda layer: binding.v2_lambda_proj(x["x"], x["w"], out=out)), {"out": out}
     if w.kind == "v1_bwd":  # the timed call is the backward; the training forward runs once, untimed
         args = [x[n] for n in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")]
         layer0 = w.layers[0]
         _, a1, a2, lse = binding.v1_fwd_train(*args, layer0, softmax1=softmax1)
         grads = [torch.empty_like(x[n]) for n in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")]
         ws = torch.empty(binding.v1_bwd_workspace_bytes(w.B, w.H, w.T, w.d), dtype=torch.uint8, device=x["v"].device)
-        return lambda layer: binding.v1_bwd(*args, layer, a1, a2, lse, x["dout"], grads=grads, workspace=ws)
+        return (lambda layer: binding.v1_bwd(*args, layer, a1, a2, lse, x["dout"], grads=grads, workspace=ws)), \
+            {"grads": grads}
     if w.kind == "v2_bwd":  # the timed call is the backward; the training forward runs once, untimed
         _, attn, lse = binding.v2_fwd_train(x["q"], x["k"], x["v"], x["lam"], softmax1=softmax1)
         grads = [torch.empty_like(x[n]) for n in ("q", "k", "v", "lam")]
         ws = torch.empty(binding.v2_bwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.d), dtype=torch.uint8,
                          device=x["v"].device)
-        return lambda layer: binding.v2_bwd(x["q"], x["k"], x["v"], x["lam"], attn, lse, x["dout"], *grads,
-                                            workspace=ws)
+        return (lambda layer: binding.v2_bwd(x["q"], x["k"], x["v"], x["lam"], attn, lse, x["dout"], *grads,
+                                             workspace=ws)), {"grads": grads}
     dev = x["q"].device
     out = torch.empty((w.B, w.Hq // 2, w.d), dtype=w.torch_dtype, device=dev)
     if w.kind == "decode_paged":
         ws = torch.empty(binding.v2_decode_paged_workspace_bytes(w.B, w.T, 1, w.Hq, w.Hkv, w.d), dtype=torch.uint8,
                          device=dev)
-        return lambda layer: binding.v2_decode_paged(x["q"], x["k_pages"], x["v_pages"], x["block_table"],
-                                                     x["seq_lens"], x["lam"], w.T, out=out, workspace=ws,
-                                                     softmax1=softmax1)
+        return (lambda layer: binding.v2_decode_paged(x["q"], x["k_pages"], x["v_pages"], x["block_table"],
+                                                      x["seq_lens"], x["lam"], w.T, out=out, workspace=ws,
+                                                      softmax1=softmax1)), {"out": out}
     if w.kind == "decode_multi":
         out = torch.empty((w.B, w.nq, w.Hq // 2, w.d), dtype=w.torch_dtype, device=dev)
         ws = torch.empty(binding.v2_decode_multi_workspace_bytes(w.B, w.T, w.nq, w.Hq, w.Hkv, w.d), dtype=torch.uint8,
                          device=dev)
-        return lambda layer: binding.v2_decode_multi(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws,
-                                                     softmax1=softmax1)
+        return (lambda layer: binding.v2_decode_multi(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws,
+                                                      softmax1=softmax1)), {"out": out}
     ws = torch.empty(binding.v2_decode_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.d), dtype=torch.uint8, device=dev)
     if w.kind == "decode_rope":  # q rotated in the kernel; the cache is read as holding rotated keys
-        return lambda layer: binding.v2_decode(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws, theta=1e4)
-    return lambda layer: binding.v2_decode(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws,
-                                           softmax1=softmax1)
+        return (lambda layer: binding.v2_decode(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws,
+                                                theta=1e4)), {"out": out}
+    return (lambda layer: binding.v2_decode(x["q"], x["k"], x["v"], x["lam"], out=out, workspace=ws,
+                                            softmax1=softmax1)), {"out": out}
 
 
 def _timed(torch, call, layers, steps, warmup, graph=True):
@@ -166,31 +176,135 @@ def _roofline(w, launch_ms):
             "frac": round(a / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel_ms": round(avg_s * 1e3, 5)}
 
 
-def _cpu_baseline(w, x, min_seconds=10.0, max_seconds=30.0, softmax1=False):
-    """Time the fp64 oracle on a bounded sample of the headline workload: whole
-    layer calls (all rows of all heads) in the step's layer order, repeated
-    until at least `min_seconds` of CPU work (stopping before `max_seconds`)."""
+# ---- the oracle leg: the fp64 oracle timed on the host, and its sampled
+# rows compared with what the GPU wrote (test infrastructure; never on the
+# timed path, and skipped with --no-cpu-baseline).
+
+def _host(t):
+    import numpy as np
+
+    return np.ascontiguousarray(t.detach().to("cpu").double().numpy())
+
+
+def _cpu_baseline(w, x, softmax1=False, min_seconds=10.0, max_seconds=30.0, batch=2048, seed=11):
+    """Time the fp64 oracle on a bounded sample of rows of the headline V2
+    prefill: batches of (t, pair) rows drawn uniformly (so the mean causal row
+    length is the workload's), oracle.v2_rows over each batch, until at least
+    `min_seconds` of work (stopping before `max_seconds`).  The rate counts
+    each sampled row's own algorithmic flops (two heads x (QK^T + PV) over
+    its t+1 visible keys: 8 d (t+1))."""
     import numpy as np
 
     import oracle
 
     cores = oracle.set_threads(len(os.sched_getaffinity(0)))
-    host = {n: np.ascontiguousarray(x[n].detach().to("cpu").double().numpy()) for n in x}
-    args = [host[n] for n in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")]
-    layers = list(w.layers) or [0]
-    calls, t = 0, 0.0
+    q, k, v, lam = (_host(x[n]) for n in ("q", "k", "v", "lam"))
+    rng = np.random.default_rng(seed)
+    rows, flops, t = 0, 0.0, 0.0
     while t < min_seconds:
-        layer = layers[calls % len(layers)]
+        idx = np.stack([np.zeros(batch, np.int64), rng.integers(0, w.T, batch), rng.integers(0, w.Hq // 2, batch)], 1)
         t0 = time.perf_counter()
-        oracle.v1_fwd(*args, layer, softmax1=softmax1)
+        oracle.v2_rows(q, k, v, lam, idx, softmax1=softmax1)
         dt = time.perf_counter() - t0
         t += dt
-        calls += 1
+        rows += batch
+        flops += float(8.0 * w.d * (idx[:, 1] + 1).sum())
         if t + dt > max_seconds:
             break
-    return {"value": round(w.flops() * calls / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": round(t, 3),
-            "sample": f"{calls} whole layer calls of {w.name} (layers {layers[0]}.. in order), fp64 C + OpenMP"}
+            "sample": f"{rows} random (token, pair) rows of {w.name} (of {w.T * w.Hq // 2}), fp64 C + OpenMP; "
+                      f"rate = the sampled rows' own causal flops / time"}
+
+
+def _oracle_parity(w, x, outs, softmax1=False, layer=0, n=16, seed=3):
+    """Sampled outputs of one timed call against the oracle: rows of the
+    prefills, batch entries of the decodes, tokens of the projection, rows /
+    keys of one unit of the backward passes.  Forward outputs: max |err| and
+    the bf16 bar 2e-2 + 1e-2 |ref|; gradients: max |err| and the relative L2
+    error (bar 1e-2)."""
+    import numpy as np
+
+    import oracle
+    from oracle import backward as ob
+    from oracle import prologue as op
+
+    rng = np.random.default_rng(seed)
+    decode = w.kind.startswith("decode")
+    # host fp64 copies of what the sample needs (the decode caches are sliced
+    # to the sampled sequences on the device first)
+    H = {} if decode else {n_: _host(t) for n_, t in x.items()}
+    s1 = dict(softmax1=softmax1)
+    got = ref = None
+    if w.kind == "v1":
+        idx = np.stack([rng.integers(0, w.B, n), rng.integers(0, w.H, n), rng.integers(0, w.T, n)], 1)
+        idx[:3, 2] = [0, 1, w.T - 1]
+        ref = oracle.v1_rows(*[H[k] for k in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")], layer, idx,
+                             **s1)
+        got = _host(outs["out"])[idx[:, 0], idx[:, 2], idx[:, 1]]
+    elif w.kind in ("v2", "v2_rope"):
+        idx = np.stack([rng.integers(0, w.B, n), rng.integers(0, w.T, n), rng.integers(0, w.Hq // 2, n)], 1)
+        idx[:3, 1] = [0, 1, w.T - 1]
+        q, k = H["q"], H["k"]
+        if w.kind == "v2_rope":
+            q, k = op.rope(q, 1e4), op.rope(k, 1e4)
+        ref = oracle.v2_rows(q, k, H["v"], H["lam"], idx, **(s1 if w.kind == "v2" else {}))
+        got = _host(outs["out"])[idx[:, 0], idx[:, 1], idx[:, 2]]
+    elif w.kind in ("decode", "decode_rope", "decode_multi"):
+        bs = np.sort(rng.choice(w.B, 2, replace=False))
+        sub = [_host(x[k][bs]) for k in ("q", "k", "v", "lam")]
+        if w.kind == "decode":
+            ref = oracle.v2_decode(*sub, **s1)
+        elif w.kind == "decode_rope":
+            ref = op.v2_decode_rope(*sub, theta=1e4)
+        else:
+            ref = oracle.v2_decode_multi(*sub, **s1)
+        got = _host(outs["out"])[bs]
+    elif w.kind == "decode_paged":  # the sampled sequences' own pages, renumbered
+        bs = np.sort(rng.choice(w.B, 2, replace=False))
+        table, lens = x["block_table"].cpu().numpy()[bs], x["seq_lens"].cpu().numpy()[bs]
+        npg = [(int(L) + w.page - 1) // w.page for L in lens]
+        used = np.unique(np.concatenate([table[i, :npg[i]] for i in range(len(bs))]))
+        remap = {int(pg): i for i, pg in enumerate(used)}
+        t2 = np.zeros((len(bs), max(npg)), np.int64)
+        for i in range(len(bs)):
+            t2[i, :npg[i]] = [remap[int(pg)] for pg in table[i, :npg[i]]]
+        sel = __import__("torch").as_tensor(used, device=x["k_pages"].device)
+        ref = oracle.v2_decode_paged(_host(x["q"][bs]), _host(x["k_pages"][sel]), _host(x["v_pages"][sel]), t2, lens,
+                                     _host(x["lam"][bs]), **s1)
+        got = _host(outs["out"])[bs]
+    elif w.kind == "lam_proj":
+        ts = rng.integers(0, w.T, n)
+        ref = op.lambda_proj(H["x"][:, ts], H["w"])
+        got = _host(outs["out"])[:, ts]
+    if got is not None:
+        err = np.abs(got - ref)
+        return {"sample": f"{ref.shape[0]} x {ref[0].size}", "max_abs_err": float(err.max()),
+                "ok": bool((err <= 2e-2 + 1e-2 * np.abs(ref)).all())}
+    grads = [_host(g) for g in outs["grads"]]
+    if w.kind == "v2_bwd":  # one GQA group: dq of sampled rows, dk/dv of sampled keys, all its dlam
+        G = w.Hq // w.Hkv
+        g0 = int(rng.integers(0, w.Hkv))
+        hs, ps = slice(g0 * G, (g0 + 1) * G), slice(g0 * G // 2, (g0 + 1) * G // 2)
+        ts, js = rng.integers(0, w.T, 4), rng.integers(0, w.T, 4)
+        rows = [(0, int(t), h) for t in ts for h in range(G)]
+        keys = [(0, int(j), 0) for j in js]
+        rq, rk, rv, rl = ob.v2_bwd_sampled(H["q"][:, :, hs], H["k"][:, :, g0:g0 + 1], H["v"][:, :, g0:g0 + 1],
+                                           H["lam"][:, :, ps], H["dout"][:, :, ps], rows, keys, **s1)
+        pairs = [(np.stack([grads[0][0, t, g0 * G + h] for _, t, h in rows]), rq),
+                 (np.stack([grads[1][0, j, g0] for _, j, _ in keys]), rk),
+                 (np.stack([grads[2][0, j, g0] for _, j, _ in keys]), rv), (grads[3][:, :, ps], rl)]
+        what = f"kv group {g0}: dq of {len(rows)} rows, dk/dv of {len(keys)} keys, dlam of its pairs"
+    else:  # v1_bwd: one (batch, differential head) unit, every gradient element of it
+        b, h = int(rng.integers(0, w.B)), int(rng.integers(0, w.H))
+        sub = [H[k][b:b + 1, h:h + 1] for k in ("q1", "q2", "k1", "k2", "v")]
+        ref = ob.v1_bwd(*sub, *[H[k] for k in ("lq1", "lk1", "lq2", "lk2")], w.layers[0],
+                        H["dout"][b:b + 1, :, h:h + 1], **s1)
+        pairs = [(grads[i][b:b + 1, h:h + 1], ref[i]) for i in range(5)]
+        what = f"(b {b}, head {h}): dq1, dq2, dk1, dk2, dv"
+    rl2 = [float(np.sqrt(((g - r) ** 2).sum() / (r * r).sum())) for g, r in pairs]
+    return {"sample": what, "max_abs_err": max(float(np.abs(g - r).max()) for g, r in pairs),
+            "max_rel_l2": max(rl2), "ok": bool(max(rl2) <= 1e-2)}
 
 
 def _source_sha(kind):
@@ -332,8 +446,8 @@ def summarize(path, match):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--only", default=None,
                     help="time a single workload by name, or 'copy' for the 1 GiB copy calibration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -374,7 +488,7 @@ def main():
     def measure(name, steps, warmup, calls_per_step=None):
         w = workloads.WORKLOADS[name]
         x = workloads.inputs_for(w, dev)
-        call = _caller(w, x, binding, torch, softmax1=args.softmax1)
+        call, outs = _caller(w, x, binding, torch, softmax1=args.softmax1)
         layers = list(w.layers) if w.layers else [0]
         if calls_per_step:  # repeat the layer list so one step holds several launches
             layers = (layers * calls_per_step)[:max(calls_per_step, len(layers))]
@@ -411,6 +525,9 @@ def main():
                        value=round(w.flops() / per_call_s / 1e12, 3))
         else:
             res.update(metric="causal fwd TFLOP/s", unit="TFLOP/s", value=round(w.flops() / per_call_s / 1e12, 3))
+        if not args.no_cpu_baseline:  # the oracle leg: sampled outputs of the last timed call
+            torch.cuda.synchronize()
+            res["parity"] = _oracle_parity(w, x, outs, softmax1=args.softmax1, layer=layers[-1])
         log(json.dumps(res))
         return w, x, res
 
@@ -478,12 +595,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: seeded N(0,1) q/k/v, lambda vectors N(0,0.1) fp32; resident in HBM",
-        "config": {"workload": HEADLINE, "kind": "DIFF V1 causal forward", "B": w.B, "T": w.T, "H": w.H,
-                   "d": w.d, "dv": 2 * w.d, "layers": "0..11 (one step = 12 calls)", "parallelism": "none",
+        "data": "synthetic: seeded N(0,1) q/k/v, lambda logits N(0,1) fp32; resident in HBM",
+        "config": {"workload": HEADLINE, "kind": "DIFF V2 causal GQA prefill", "B": w.B, "T": w.T, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "pairs": w.Hq // 2, "d": w.d, "step": "one call", "parallelism": "none",
                    "softmax": "off_by_one" if args.softmax1 else "standard"},
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        "parity": head.get("parity"),
         "mfma_reference": ref,
         "secondary": secondary,
     }
