@@ -104,17 +104,21 @@ def load_library():
     fl = ctypes.c_float
     lib.diffattn_rope.argtypes = [i, i, i, i, i, DaIn, DaOut, fl, i, vp]
     lib.diffattn_rope.restype = i
-    lib.diffattn_v1_fwd_rope.argtypes = [i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaIn, fp, fp, fp, fp, i, fl, DaOut,
-                                         vp, ctypes.c_size_t, vp]
-    lib.diffattn_v1_fwd_rope.restype = i
-    lib.diffattn_v2_fwd_rope.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, fl, DaOut, vp, ctypes.c_size_t, vp]
-    lib.diffattn_v2_fwd_rope.restype = i
-    lib.diffattn_v2_decode_rope.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, fl, DaOut, vp,
-                                            ctypes.c_size_t, vp]
-    lib.diffattn_v2_decode_rope.restype = i
-    lib.diffattn_v2_decode_paged_rope.argtypes = [i, i, i, i, i, i, i, DaIn, DaIn, DaIn, i, i, vp, ctypes.c_int64,
-                                                  vp, DaIn, fl, DaOut, vp, ctypes.c_size_t, vp]
-    lib.diffattn_v2_decode_paged_rope.restype = i
+    for sfx in ("_rope", "_softmax1_rope"):
+        f = getattr(lib, "diffattn_v1_fwd" + sfx)
+        f.argtypes = [i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, DaIn, fp, fp, fp, fp, i, fl, DaOut, vp, ctypes.c_size_t,
+                      vp]
+        f.restype = i
+        f = getattr(lib, "diffattn_v2_fwd" + sfx)
+        f.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, fl, DaOut, vp, ctypes.c_size_t, vp]
+        f.restype = i
+        f = getattr(lib, "diffattn_v2_decode" + sfx)
+        f.argtypes = [i, i, i, i, i, i, DaIn, DaIn, DaIn, DaIn, fl, DaOut, vp, ctypes.c_size_t, vp]
+        f.restype = i
+        f = getattr(lib, "diffattn_v2_decode_paged" + sfx)
+        f.argtypes = [i, i, i, i, i, i, i, DaIn, DaIn, DaIn, i, i, vp, ctypes.c_int64, vp, DaIn, fl, DaOut, vp,
+                      ctypes.c_size_t, vp]
+        f.restype = i
     for f in (lib.diffattn_v1_fwd_rope_workspace_bytes, lib.diffattn_v2_fwd_rope_workspace_bytes):
         f.argtypes = [i, i, i, i]
         f.restype = ctypes.c_size_t
@@ -211,18 +215,17 @@ def v1_fwd(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, out: torch.Tensor 
         out = torch.empty((B, T, H, 2 * d), dtype=q1.dtype, device=q1.device)
     _check_device(q1, q2, k1, k2, v, out, *lams)
     if theta is not None:
-        if softmax1:
-            raise ValueError("the rotary-embedding entry points use the standard softmax")
         need = int(lib.diffattn_v1_fwd_rope_workspace_bytes(B, H, T, d))
         if workspace is None:
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q1.device)
-        st = lib.diffattn_v1_fwd_rope(_dtype_code(q1), B, H, T, d, _in(q1, 0, 1, 2), _in(q2, 0, 1, 2),
+        name = "diffattn_v1_fwd" + ("_softmax1" if softmax1 else "") + "_rope"
+        st = getattr(lib, name)(_dtype_code(q1), B, H, T, d, _in(q1, 0, 1, 2), _in(q2, 0, 1, 2),
                                       _in(k1, 0, 1, 2), _in(k2, 0, 1, 2), _in(v, 0, 1, 2),
                                       *[x.data_ptr() for x in lams], int(layer), float(theta), _out(out, 0, 2, 1),
                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                       _stream(q1))
         if st != 0:
-            raise DiffAttnError(st, "diffattn_v1_fwd_rope")
+            raise DiffAttnError(st, name)
         return out
     name = "diffattn_v1_fwd" + ("_softmax1" if softmax1 else "")
     st = getattr(lib, name)(_dtype_code(q1), B, H, T, d,
@@ -319,16 +322,15 @@ def v2_fwd(q, k, v, lam, out: torch.Tensor | None = None, softmax1: bool = False
         out = torch.empty((B, T, Hq // 2, d), dtype=q.dtype, device=q.device)
     _check_device(q, k, v, out)
     if theta is not None:
-        if softmax1:
-            raise ValueError("the rotary-embedding entry points use the standard softmax")
         need = int(lib.diffattn_v2_fwd_rope_workspace_bytes(B, T, Hkv, d))
         if workspace is None:
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-        st = lib.diffattn_v2_fwd_rope(_dtype_code(q), B, T, Hq, Hkv, d, _in(q, 0, 2, 1), _in(k, 0, 2, 1),
-                                      _in(v, 0, 2, 1), _in(lam, 0, 2, 1), float(theta), _out(out, 0, 2, 1),
-                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
+        name = "diffattn_v2_fwd" + ("_softmax1" if softmax1 else "") + "_rope"
+        st = getattr(lib, name)(_dtype_code(q), B, T, Hq, Hkv, d, _in(q, 0, 2, 1), _in(k, 0, 2, 1),
+                                _in(v, 0, 2, 1), _in(lam, 0, 2, 1), float(theta), _out(out, 0, 2, 1),
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
         if st != 0:
-            raise DiffAttnError(st, "diffattn_v2_fwd_rope")
+            raise DiffAttnError(st, name)
         return out
     name = "diffattn_v2_fwd" + ("_softmax1" if softmax1 else "")
     st = getattr(lib, name)(_dtype_code(q), B, T, Hq, Hkv, d, _in(q, 0, 2, 1), _in(k, 0, 2, 1),
@@ -421,8 +423,6 @@ def v2_decode(q, k_cache, v_cache, lam, out: torch.Tensor | None = None,
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check_device(q, k_cache, v_cache, out)
-    if theta is not None and softmax1:
-        raise ValueError("the rotary-embedding entry points use the standard softmax")
     name = "diffattn_v2_decode" + ("_softmax1" if softmax1 else "") + ("_rope" if theta is not None else "")
     extra = (ctypes.c_float(theta),) if theta is not None else ()
     st = getattr(lib, name)(_dtype_code(q), B, L, Hq, Hkv, d, _in(q, 0, 1, None),
@@ -515,8 +515,6 @@ def v2_decode_paged(q, k_pages, v_pages, block_table, seq_lens, lam, max_len: in
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check_device(q, k_pages, v_pages, out, block_table, seq_lens)
-    if theta is not None and softmax1:
-        raise ValueError("the rotary-embedding entry points use the standard softmax")
     name = "diffattn_v2_decode_paged" + ("_softmax1" if softmax1 else "") + ("_rope" if theta is not None else "")
     extra = (ctypes.c_float(theta),) if theta is not None else ()
     ax = (0, 2, 1) if multi else (0, 1, None)  # (b, h, t) axes of q / lam / out

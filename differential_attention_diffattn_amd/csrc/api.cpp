@@ -706,6 +706,41 @@ da_status diffattn_v2_decode_paged_rope(da_dtype dtype, int B, int max_len, int 
                      workspace_bytes, stream, theta);
 }
 
+da_status diffattn_v1_fwd_softmax1_rope(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1,
+                                       da_in k2, da_in v, const float* lam_q1, const float* lam_k1,
+                                       const float* lam_q2, const float* lam_k2, int layer_index, float theta,
+                                       da_out out, void* workspace, size_t workspace_bytes, void* stream) {
+  const RopeK r{theta, workspace, workspace_bytes};
+  return v1_fwd_impl(1, dtype, B, H, T, d, q1, q2, k1, k2, v, lam_q1, lam_k1, lam_q2, lam_k2, layer_index, out,
+                     stream, nullptr, nullptr, nullptr, &r);
+}
+
+da_status diffattn_v2_fwd_softmax1_rope(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
+                                       da_in v, da_in lam, float theta, da_out out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const RopeK r{theta, workspace, workspace_bytes};
+  return v2_fwd_impl(1, dtype, B, T, Hq, Hkv, d, q, k, v, lam, out, stream, nullptr, nullptr, &r);
+}
+
+da_status diffattn_v2_decode_softmax1_rope(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
+                                          da_in k_cache, da_in v_cache, da_in lam, float theta, da_out out,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!rope_theta_ok(theta)) return DA_E_SHAPE;
+  return decode_impl(1, dtype, B, L, 1, Hq, Hkv, d, q, k_cache, v_cache, nullptr, lam, out, workspace,
+                     workspace_bytes, stream, theta);
+}
+
+da_status diffattn_v2_decode_paged_softmax1_rope(da_dtype dtype, int B, int max_len, int nq, int Hq, int Hkv, int d,
+                                                da_in q, da_in k_pages, da_in v_pages, int num_pages, int page_size,
+                                                const int32_t* block_table, int64_t bt_stride,
+                                                const int32_t* seq_lens, da_in lam, float theta, da_out out,
+                                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!rope_theta_ok(theta)) return DA_E_SHAPE;
+  const PagedArgs pg{num_pages, page_size, block_table, bt_stride, seq_lens};
+  return decode_impl(1, dtype, B, max_len, nq, Hq, Hkv, d, q, k_pages, v_pages, &pg, lam, out, workspace,
+                     workspace_bytes, stream, theta);
+}
+
 da_status diffattn_rope(da_dtype dtype, int B, int T, int H, int d, da_in x, da_out out, float theta, int pos0,
                         void* stream) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;

@@ -466,6 +466,27 @@ da_status diffattn_v2_decode_paged_rope(da_dtype dtype, int B, int max_len, int 
                                         size_t workspace_bytes, void* stream);
 
 /*
+ * The four rotary-embedding entry points above with every softmax map
+ * replaced by the off-by-one softmax (as the *_softmax1 entry points do):
+ * identical arguments, checks and workspaces.
+ */
+da_status diffattn_v1_fwd_softmax1_rope(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1,
+                                       da_in k2, da_in v, const float* lam_q1, const float* lam_k1,
+                                       const float* lam_q2, const float* lam_k2, int layer_index, float theta,
+                                       da_out out, void* workspace, size_t workspace_bytes, void* stream);
+da_status diffattn_v2_fwd_softmax1_rope(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
+                                       da_in v, da_in lam, float theta, da_out out, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+da_status diffattn_v2_decode_softmax1_rope(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
+                                          da_in k_cache, da_in v_cache, da_in lam, float theta, da_out out,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+da_status diffattn_v2_decode_paged_softmax1_rope(da_dtype dtype, int B, int max_len, int nq, int Hq, int Hkv, int d,
+                                                da_in q, da_in k_pages, da_in v_pages, int num_pages, int page_size,
+                                                const int32_t* block_table, int64_t bt_stride,
+                                                const int32_t* seq_lens, da_in lam, float theta, da_out out,
+                                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * diffattn_v2_decode without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, checks and result as

@@ -302,7 +302,9 @@ def test_prologue_entry_points_are_declared(lib):
     syms = _declared_symbols()
     for need in ("diffattn_rope", "diffattn_v1_fwd_rope", "diffattn_v1_fwd_rope_workspace_bytes",
                  "diffattn_v2_fwd_rope", "diffattn_v2_fwd_rope_workspace_bytes", "diffattn_v2_decode_rope",
-                 "diffattn_v2_decode_paged_rope", "diffattn_v2_lambda_proj"):
+                 "diffattn_v2_decode_paged_rope", "diffattn_v2_lambda_proj", "diffattn_v1_fwd_softmax1_rope",
+                 "diffattn_v2_fwd_softmax1_rope", "diffattn_v2_decode_softmax1_rope",
+                 "diffattn_v2_decode_paged_softmax1_rope"):
         assert need in syms and hasattr(lib, need)
 
 

@@ -159,3 +159,81 @@ def test_lambda_proj_feeds_the_prefill():
     torch.cuda.synchronize()
     ref = oracle.v2_fwd(*[y[n].cpu() for n in ("q", "k", "v")], op.lambda_proj(x.cpu(), w.cpu()))
     assert_bf16_close(got, ref, "projection + prefill")
+
+
+# ---- the off-by-one softmax with the rotary embedding ----------------------------
+
+@pytest.mark.parametrize("kind", ["v1", "v2"])
+def test_prefill_rope_softmax1(kind):
+    if kind == "v1":
+        x = workloads.v1_inputs(2, 2, 200, 64, torch.bfloat16, seed=2900, device=DEV)
+        args = [x[n] for n in ("q1", "q2", "k1", "k2", "v", "lq1", "lk1", "lq2", "lk2")]
+        got = binding.v1_fwd(*args, 3, theta=1e4, softmax1=True)
+        plain = binding.v1_fwd(*args, 3, theta=1e4)
+        ref = op.v1_fwd_rope(*[a.cpu() for a in args], 3, theta=1e4, softmax1=True)
+    else:
+        y = workloads.v2_inputs(1, 300, 8, 2, 128, torch.bfloat16, seed=2901, device=DEV)
+        got = binding.v2_fwd(y["q"], y["k"], y["v"], y["lam"], theta=1e4, softmax1=True)
+        plain = binding.v2_fwd(y["q"], y["k"], y["v"], y["lam"], theta=1e4)
+        ref = op.v2_fwd_rope(*[y[n].cpu() for n in ("q", "k", "v", "lam")], theta=1e4, softmax1=True)
+    torch.cuda.synchronize()
+    assert_bf16_close(got, ref, f"{kind} rope softmax1")
+    assert not torch.equal(got, plain)
+
+
+def test_decode_rope_softmax1_dense_and_paged():
+    B, L, Hq, Hkv, d = 2, 900, 8, 2, 128
+    g = torch.Generator(device=DEV).manual_seed(2902)
+    q = torch.randn((B, Hq, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((B, L, Hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((B, L, Hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    lam = torch.randn((B, Hq // 2), generator=g, device=DEV)
+    got = binding.v2_decode(q, k, v, lam, theta=1e4, softmax1=True)
+    # the same cache as 16-token pages laid end to end
+    page = 16
+    npg = (L + page - 1) // page
+    pool_k = torch.zeros((B * npg, page, Hkv, d), dtype=torch.bfloat16, device=DEV)
+    pool_v = torch.zeros_like(pool_k)
+    for b in range(B):
+        pool_k.view(B, npg * page, Hkv, d)[b, :L] = k[b]
+        pool_v.view(B, npg * page, Hkv, d)[b, :L] = v[b]
+    table = torch.arange(B * npg, dtype=torch.int32, device=DEV).reshape(B, npg)
+    lens = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    gotp = binding.v2_decode_paged(q, pool_k, pool_v, table, lens, lam, L, theta=1e4, softmax1=True)
+    torch.cuda.synchronize()
+    ref = op.v2_decode_rope(q.cpu(), k.cpu(), v.cpu(), lam.cpu(), theta=1e4, softmax1=True)
+    assert_bf16_close(got, ref, "decode rope softmax1")
+    assert_bf16_close(gotp, ref, "paged decode rope softmax1")
+
+
+# ---- the benchmarked RoPE workloads at full size ------------------------------------
+
+def test_v2_prefill_rope_full_sampled():
+    """The V2 prefill workload with the rotary embedding (B 1, T 8192, 64 / 8
+    heads, d 128): sampled rows, including the last positions, against the
+    oracle's rotation (fp64) and prefill rows."""
+    w = workloads.WORKLOADS["v2_prefill_rope_B1_T8192_Hq64_Hkv8_d128"]
+    y = workloads.inputs_for(w, DEV)
+    got = binding.v2_fwd(y["q"], y["k"], y["v"], y["lam"], theta=1e4)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    idx = np.stack([np.zeros(64, np.int64), rng.integers(0, w.T, 64), rng.integers(0, w.Hq // 2, 64)], 1)
+    idx[:6, 1] = [0, 1, 4095, 4096, 8190, 8191]
+    q, k = op.rope(y["q"].cpu(), 1e4), op.rope(y["k"].cpu(), 1e4)
+    ref = oracle.v2_rows(q, k, y["v"].cpu(), y["lam"].cpu(), idx)
+    assert_bf16_close(host64(got)[idx[:, 0], idx[:, 1], idx[:, 2]], ref, "v2 rope prefill T8192 sampled rows")
+
+
+def test_decode_rope_full_sampled():
+    """The V2 decode workload with q rotated to position 32767 in the kernel
+    (B 64, L 32768, 64 / 8 heads, d 128): three sequences against the
+    oracle (the cache read as holding rotated keys)."""
+    w = workloads.WORKLOADS["v2_decode_rope_B64_L32768_Hq64_Hkv8_d128"]
+    x = workloads.inputs_for(w, DEV)
+    got = binding.v2_decode(x["q"], x["k"], x["v"], x["lam"], theta=1e4)
+    torch.cuda.synchronize()
+    bs = [0, 31, 63]
+    ref = op.v2_decode_rope(*[x[n][bs].cpu() for n in ("q", "k", "v", "lam")], theta=1e4)
+    assert_bf16_close(host64(got)[bs], ref, "decode rope L32768 sampled sequences")
+    del x
+    torch.cuda.empty_cache()
