@@ -1,14 +1,16 @@
 """Brute-force fp64 differential attention with explicit T x T maps (numpy).
 
 A second, independent formulation used only to pin the oracle on tiny
-inputs.  It follows the matrix form of notlober's module in the nanoGPT issue
-"How best to implement a differential transformer?": whole score maps,
-masked with -inf above the diagonal, softmax along keys, the two maps
-combined as A1 - lambda*A2 BEFORE multiplying by V, then the per-head norm
-and the (1 - lambda_init) scale.  Two deviations of that module are not
-followed, because the "Differential Transformer V2" article (DiffAttnV1
-pseudo-code) is the authority: the norm is RMSNorm (not LayerNorm with
-affine), and lambda_init uses the layer's own index (not the layer count).
+inputs.  V1 works on whole maps: the two maps of a differential head are
+stacked along a map axis and softmaxed together (scores masked with -inf
+above the diagonal), their combination is a contraction of that axis with
+the coefficient vector (1, -lambda) -- so the combined weights exist BEFORE
+they meet V, as in the explicit-map form of notlober's module in the nanoGPT
+issue "How best to implement a differential transformer?" -- and the RMSNorm
+is written with a vector norm.  Two deviations of that module are not taken,
+because the "Differential Transformer V2" article (DiffAttnV1 pseudo-code) is
+the authority: the norm is RMSNorm (not LayerNorm with affine), and
+lambda_init uses the layer's own index (not the layer count).
 
 This shares no code with ``oracle/`` (which computes one softmax row at a
 time, maps separately, and combines after P.V).
@@ -32,15 +34,16 @@ def _causal_softmax(s: np.ndarray) -> np.ndarray:
 def v1(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer):
     """q*, k* [B,H,T,d]; v [B,H,T,2d]; returns [B,T,H,2d]."""
     d = q1.shape[-1]
-    a1 = _causal_softmax(q1 @ np.swapaxes(k1, -1, -2) / math.sqrt(d))
-    a2 = _causal_softmax(q2 @ np.swapaxes(k2, -1, -2) / math.sqrt(d))
+    n = v.shape[-1]  # 2d channels
     li = 0.8 - 0.6 * math.exp(-0.3 * layer)
-    lam = math.exp(float(np.sum(lq1 * lk1))) - math.exp(float(np.sum(lq2 * lk2))) + li
-    w = a1 - lam * a2  # [B,H,T,T]
-    o = w @ v  # [B,H,T,2d]
-    o = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + 1e-5)
-    o = o * (1.0 - li)
-    return np.transpose(o, (0, 2, 1, 3))
+    coef = np.array([1.0, -(math.exp(float(lq1 @ lk1)) - math.exp(float(lq2 @ lk2)) + li)])
+    Q = np.stack([q1, q2], axis=2)  # [B,H,2,T,d]: the maps side by side
+    K = np.stack([k1, k2], axis=2)
+    A = _causal_softmax(np.einsum("bhmic,bhmjc->bhmij", Q, K) / math.sqrt(d))
+    W = np.einsum("m,bhmij->bhij", coef, A)  # differential weights, [B,H,T,T]
+    D = np.einsum("bhij,bhjc->bihc", W, v)  # [B,T,H,2d]
+    rms = np.linalg.norm(D, axis=-1, keepdims=True) / math.sqrt(n)
+    return (1.0 - li) * D / np.sqrt(rms * rms + 1e-5)
 
 
 def _gqa_attention(q, k, v, causal=True):
