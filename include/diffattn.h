@@ -507,9 +507,9 @@ da_status diffattn_v2_decode_noalloc(da_dtype dtype, int B, int L, int Hq, int H
 size_t diffattn_v2_decode_noalloc_max_bytes(void);
 
 /*
- * DIFF V2 lambda projection ("Differential Transformer V2" article: a
- * projected lambda for each token and each head, read as a linear map
- * without bias of the token's hidden state):
+ * DIFF V2 lambda projection ("Differential Transformer V2" article: lambda
+ * is computed per token and per head by a projection the article does not
+ * show; read here as a linear map without bias of the token's hidden state):
  *   out[b,t,p] = sum_c x[b,t,c] w[p,c]   (fp32 logits; the sigmoid stays in
  *   diffattn_v2_fwd, which takes these logits as lam).
  *   x    logical [B,T,dm] bf16 (roles b, t; sh unused), 16-byte rows.

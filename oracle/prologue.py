@@ -17,9 +17,9 @@ turns by the angle t * w_c, w_c = theta^(-2c/d), at position t:
 (theta = 10000 unless given).  A score between positions s and t then
 depends on s - t only.
 
-V2 lambda projection.  The "Differential Transformer V2" article introduces a
-projected lambda for each token and each head without printing the
-projection; the plainest reading is a linear map (no bias) of the token's
+V2 lambda projection.  The "Differential Transformer V2" article computes
+lambda per token and per head with a projection it does not show; the
+plainest reading is a linear map (no bias) of the token's
 hidden state to one logit per output pair, ``logits[b, t, p] = <x[b, t, :],
 W[p, :]>`` with W laid out like a linear layer's weight [pairs, d_model]; the
 sigmoid stays where the DiffAttnV2 pseudo-code puts it.
