@@ -188,6 +188,8 @@ da_status decode_impl(int softmax1, da_dtype dtype, int B, int L, int nq, int Hq
   if (pg) {  // the kernel addresses a row within a page with a 32-bit element offset
     if ((int64_t)page_size * kc.st >= (int64_t(1) << 31) || (int64_t)page_size * vc.st >= (int64_t(1) << 31))
       return DA_E_UNSUPPORTED;
+  } else if (kc.st >= kMaxTokenStride || vc.st >= kMaxTokenStride) {
+    return DA_E_UNSUPPORTED;  // rows of a 32-token block are addressed with 32-bit byte offsets
   }
   const int max_chunk = pg ? da::kPagedMaxChunk : 2048;
   const size_t need = decode_ws_bytes(B, L, nq, Hq, Hkv, d, max_chunk, max_splits);

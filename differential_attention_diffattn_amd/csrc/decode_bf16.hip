@@ -30,14 +30,33 @@
 
 #include "kernels.hpp"
 #include "rope.hpp"
+#include "tile_ops.hpp"
 
 namespace da {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;         // split geometry: chunks are multiples of kWaves x kBlk tokens
 constexpr int kBlk = 32;          // tokens per wave step
-constexpr int kVtPad = 4;         // bf16 padding of a V^T row (conflict-free 8 B reads)
 constexpr float kLazyLog2 = 8.f;  // rescale only when a head's max grows by > 2^8
+
+// LDS slots per wave.  Dense cache: two (the next block streams in while this
+// one is computed; 128 KB per workgroup at d = 128, one per CU).  Paged,
+// ragged cache: one (64 KB, two workgroups per CU, so a CU whose split ends
+// early takes another): measured faster there.  The slot count changes only
+// when copies are issued, not the arithmetic, so a paged cache whose pages
+// lie in order gives the dense result bit for bit.
+template <bool PAGED>
+constexpr int dec_slots() { return PAGED ? 1 : 2; }
+static_assert(2 * kPagedMaxChunk / (kBlk * kWaves) <= 64, "a paged wave holds its split's page-table entries one per lane");
+
+// 16-byte chunk c of row r of a K or V block sits at chunk c ^ dec_swizzle(r)
+// of its LDS row: the K operand reads (16 rows x one chunk per 16 lanes) and
+// the V^T transpose reads (8 rows x 32 bytes per 32 lanes) then touch every
+// bank once.  Depends on r & 15 only.
+template <int D>
+__device__ __forceinline__ int dec_swizzle(int r) {
+  return D >= 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
 
 __device__ __forceinline__ void lds_fence() {
   // The LDS executes one wave's instructions in order; this waits for the
@@ -47,18 +66,35 @@ __device__ __forceinline__ void lds_fence() {
 }
 
 template <int D, bool PAGED, int NCB>
-__global__ void __launch_bounds__(kWaves * 64, NCB == 1 ? 1 : 2) decode_split_kernel(const DecodeArgs a) {
+__global__ void __launch_bounds__(kWaves * 64, (PAGED || NCB > 1) ? 1 : 3) decode_split_kernel(const DecodeArgs a) {
+  constexpr int W = kWaves;  // waves per workgroup
   constexpr int KS = D / 32;   // k-steps of the score MFMA
   constexpr int CB = D / 16;   // 16-wide column blocks of O^T
-  constexpr int VROW = kBlk + kVtPad;
-  constexpr int VT_ELEMS = D * VROW;               // one wave's V^T slice
-  constexpr int VU = (kBlk / 4) * (D / 8) / 64;    // 4x8 V units per lane
-  static_assert(VU >= 1 && (kBlk / 4) * (D / 8) % 64 == 0, "V block split");
   static_assert(kBlk == 32, "a step is two 16-token sub-blocks");
-  constexpr int LDS_VT = kWaves * VT_ELEMS * 2;            // bytes
-  constexpr int LDS_RED = kWaves * 16 * (D + 2) * 4;       // bytes (one column block at a time)
-  constexpr int LDS_BYTES = LDS_VT > LDS_RED ? LDS_VT : LDS_RED;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
+  constexpr int NST = dec_slots<PAGED>();
+  static_assert(NST >= 1 && NST <= 3, "LDS slots per wave");
+  constexpr int RB = D * 2;                 // bytes of a K / V row
+  constexpr int TBYTES = kBlk * RB;         // one tensor's block
+  constexpr int SLOT = 2 * TBYTES;          // [K block | V block]
+  constexpr int RPI = 1024 / RB;            // rows per 1 KB copy instruction
+  constexpr int NI = kBlk / RPI;            // copy instructions per tensor and block
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static_assert(16 % RPI == 0, "a copy instruction's rows lie in one 16-token sub-block");
+  // Two data paths.  DMA (paged cache, or several new tokens): K and V blocks
+  // are copied into LDS slots by global_load_lds, the next block streaming in
+  // while this one is computed.  Register path (dense cache, one new token):
+  // K is loaded straight into MFMA operand registers and V through registers
+  // into a transposed LDS slice; three workgroups per CU hide the latency --
+  // measured faster for that case.  Both give each wave the same blocks and
+  // the same MFMA sequence, so their results agree bit for bit.
+  constexpr bool DMA = PAGED || NCB > 1;
+  constexpr int VROW = kBlk + 4;                           // V^T row (bf16, padded: conflict-free 8 B reads)
+  constexpr int VT_ELEMS = D * VROW;                       // one wave's V^T slice (register path)
+  constexpr int LDS_STG = DMA ? W * NST * SLOT : W * VT_ELEMS * 2;  // bytes
+  constexpr int LDS_RED = W * 16 * (D + 2) * 4;       // bytes (one column block at a time)
+  constexpr int LDS_BYTES = LDS_STG > LDS_RED ? LDS_STG : LDS_RED;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, kg = lane >> 4;
@@ -115,10 +151,13 @@ __global__ void __launch_bounds__(kWaves * 64, NCB == 1 ? 1 : 2) decode_split_ke
     g = (bid / a.nsplit) % a.Hkv;
     vb = bid / (a.nsplit * a.Hkv);
   }
+  // (uniform by construction; in scalar registers, as the copies' bases must be)
+  vb = __builtin_amdgcn_readfirstlane(vb);
+  s = __builtin_amdgcn_readfirstlane(s);
   const int b = vb / a.ncg, cg = vb % a.ncg;
   const int G = a.G, NQ = a.nq, NC = NQ * G;
   // tokens of this sequence (paged: its own length, at most the longest)
-  const int L = PAGED ? min(max(a.seq_lens[b], 0), a.L) : a.L;
+  const int L = __builtin_amdgcn_readfirstlane(PAGED ? min(max(a.seq_lens[b], 0), a.L) : a.L);
 
   // q fragments: B operand of S = K q^T.  Column n*16 + c16 of the group is
   // query token qi, head hh; it sees cache entries t < lim (the new tokens
@@ -143,20 +182,101 @@ __global__ void __launch_bounds__(kWaves * 64, NCB == 1 ? 1 : 2) decode_split_ke
   const uint16_t* vbase = (const uint16_t*)a.v.p + (PAGED ? 0 : b * a.v.sb) + g * a.v.sh;
   const int64_t kst = a.k.st, vst = a.v.st;
   // Paged cache: pages hold a power of two >= 16 tokens, so each 16-token
-  // sub-block of a step lies in one page and one table entry per sub-block
-  // locates it.  The entries of a wave's next step are loaded one step ahead
-  // (their latency hides behind the current step); a sub-block past the
-  // sequence's end reads the entry of its last token instead (its rows are
-  // masked).  Entries outside [0, num_pages) are clamped.
-  const int32_t* bt_row = PAGED ? a.block_table + (int64_t)b * a.bt_stride : nullptr;
-  auto table_entry = [&](int tok) -> int { return bt_row[min(tok, L - 1) >> a.page_shift]; };
-  auto page_base = [&](int raw, int64_t page_stride) -> int64_t {
-    const int pg = min(max(__builtin_amdgcn_readfirstlane(raw), 0), a.num_pages - 1);
-    return (int64_t)pg * page_stride;
-  };
+  // sub-block of a block lies in one page and one table entry locates it.  A
+  // wave's split holds at most 32 steps, i.e. 64 sub-blocks: lane e holds the
+  // entry of the wave's sub-block e (step e/2), loaded once, read per step
+  // with readlane.  A sub-block past the sequence's end takes the entry of its
+  // last token (its rows are masked); entries outside [0, num_pages) are
+  // clamped.
   const int pmask = PAGED ? a.page_mask : 0;
+  const int t0 = s * a.chunk, t1 = min(L, t0 + a.chunk);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int blk0 = t0 + kBlk * wv;
+  const int nsteps = blk0 < t1 ? (t1 - blk0 + kBlk * W - 1) / (kBlk * W) : 0;
+  int ent = 0;
+  if constexpr (PAGED) {
+    if (L > 0) {
+      const int tok = min(blk0 + kBlk * W * (lane >> 1) + 16 * (lane & 1), L - 1);
+      ent = a.block_table[(int64_t)b * a.bt_stride + (tok >> a.page_shift)];
+    }
+  }
+  // q fragments and table entries have landed before the first copy is issued
+  // (no compiler-placed wait inside the loop, which would also wait for copies)
+  if constexpr (DMA) {
+#pragma unroll
+    for (int n = 0; n < NCB; ++n)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("s_waitcnt vmcnt(0)" : "+v"(qf[n][ks]));
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(ent));
+  }
 
-  uint16_t* vt = (uint16_t*)smem + wave * VT_ELEMS;
+  // ---- copies: this wave's block -> its LDS slot (global_load_lds) ----------
+  // Copy i of a tensor moves rows i*RPI .. i*RPI + RPI-1; the lane moves
+  // source chunk (lane % CPR) ^ swizzle(row) of row i*RPI + lane / CPR into
+  // slot chunk lane % CPR.  Rows past the sequence's end repeat its last row
+  // (finite data; their scores are masked to -inf below).
+  const int r_in = lane / CPR;
+  uint32_t choff[NI];  // the lane's chunk byte offset in copy i (same for K and V)
+#pragma unroll
+  for (int i = 0; i < NI; ++i) choff[i] = (uint32_t)(((lane % CPR) ^ dec_swizzle<D>(i * RPI + r_in)) * 16);
+  const uint32_t krow = (uint32_t)(r_in * kst * 2), vrow = (uint32_t)(r_in * vst * 2);
+  const uint32_t slot0 = lds_base + wv * (NST * SLOT);
+  auto issue = [&](int n, int slot) {
+    const int blk = blk0 + kBlk * W * n;
+    const uint32_t dst = slot0 + slot * SLOT;
+    const bool full = blk + kBlk <= L;  // uniform
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int sub = (i * RPI) / 16;
+      int64_t kb, vb;  // element offsets of the copy's anchor row
+      int anchor;      // token of that row
+      if constexpr (PAGED) {
+        anchor = min(blk + 16 * sub, L - 1);
+        const int raw = __builtin_amdgcn_readlane(ent, 2 * n + sub);
+        const int pg = min(max(raw, 0), a.num_pages - 1);
+        kb = (int64_t)pg * a.k.sb + (int64_t)(anchor & pmask) * kst;
+        vb = (int64_t)pg * a.v.sb + (int64_t)(anchor & pmask) * vst;
+      } else {
+        anchor = blk;
+        kb = (int64_t)blk * kst;
+        vb = (int64_t)blk * vst;
+      }
+      uint32_t ko, vo;
+      if (full) {  // rows anchor + (i*RPI - 16 sub) + r_in
+        const int base_row = i * RPI - (PAGED ? 16 * sub : 0);
+        kb += (int64_t)base_row * kst;
+        vb += (int64_t)base_row * vst;
+        ko = krow + choff[i];
+        vo = vrow + choff[i];
+      } else {
+        const int tok = min(blk + i * RPI + r_in, L - 1);
+        ko = (uint32_t)((tok - anchor) * kst * 2) + choff[i];
+        vo = (uint32_t)((tok - anchor) * vst * 2) + choff[i];
+      }
+      dma16_sbase(kbase + kb, ko, dst + i * 1024);
+      dma16_sbase(vbase + vb, vo, dst + TBYTES + i * 1024);
+    }
+  };
+
+  // per-lane LDS read offsets within a slot
+  //   K operand of S = K q^T: lane (c16, kg) reads row 16 sub + c16, chunk 4 ks + kg
+  //   V^T operand (transpose read): lane (L = lane & 15, kg) points at row
+  //   4 kg + (L >> 2) (+ 16 for the second read), channels 16 cb + 4 (L & 3);
+  //   it receives channel 16 cb + L of tokens 4 kg .. 4 kg + 3 (16 + ...)
+  uint32_t koff[2][KS];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      koff[sub][ks] = (uint32_t)((16 * sub + c16) * RB + (((4 * ks + kg) ^ dec_swizzle<D>(16 * sub + c16)) << 4));
+  uint32_t voff[CB];
+  {
+    const int l16 = lane & 15, vr = 4 * kg + (l16 >> 2);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      voff[cb] = (uint32_t)(TBYTES + vr * RB + (((2 * cb + ((l16 & 3) >> 1)) ^ dec_swizzle<D>(vr)) << 4) + 8 * (l16 & 1));
+  }
+
   const float sl2 = a.sl2;
   float mref[NCB], lsum[NCB];
   f32x4 o[NCB][CB];
@@ -168,123 +288,149 @@ __global__ void __launch_bounds__(kWaves * 64, NCB == 1 ? 1 : 2) decode_split_ke
     for (int cb = 0; cb < CB; ++cb) o[n][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int t0 = s * a.chunk, t1 = min(L, t0 + a.chunk);
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int blk0 = t0 + kBlk * wv;
-  int raw[2] = {0, 0};  // table entries of the step's two sub-blocks
-  if constexpr (PAGED) {
-    if (L > 0) raw[0] = table_entry(blk0), raw[1] = table_entry(blk0 + 16);
-  }
-  for (int blk = blk0; blk < t1; blk += kBlk * kWaves) {
-    // ---- issue the block's K (A operand) and V (transpose units) loads ----
-    // kp/vp: element offset of each sub-block's page (paged) or 0; a token's
-    // row offset within it is 32-bit (the host bounds page_size * stride)
-    int64_t kp[2] = {0, 0}, vp[2] = {0, 0};
-    if constexpr (PAGED) {
+  // Softmax state of column block n2 over one block's scores sc (lane (column
+  // c16, kg) holds tokens blk + 16 sub + 4 kg + r): mask, lazy rescale,
+  // probabilities as the bf16 B operand of P.V (slot t: token 4 kg + t for
+  // t < 4, 16 + 4 kg + t - 4 for t >= 4).
+  auto softmax_block = [&](f32x4* sc, int blk, int n2) -> bf16x8 {
+    float mx = -INFINITY;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        kp[sub] = page_base(raw[sub], a.k.sb);
-        vp[sub] = page_base(raw[sub], a.v.sb);
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (blk + 16 * sub + 4 * kg + r >= lim[n2]) sc[sub][r] = -INFINITY;
+        mx = fmaxf(mx, sc[sub][r]);
       }
-    }
-    // Tokens past the end load the last token's row instead (no branches, so
-    // the loads stay in flight together): their scores are masked to -inf
-    // below, so their probabilities are 0 and the (finite) rows add nothing.
-    // A sub-block that starts past the end was given the last token's page.
-    uint4 kr[2][KS];
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // -inf when the whole block is masked for this column (a later query
+    // token's entries only); then nothing changes below
+    const float mb = mx * sl2;
+    const bool need = mb > mref[n2] + kLazyLog2;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float al = need ? exp2f(mref[n2] - mb) : 1.f;
+      if (need) mref[n2] = mb;
+      lsum[n2] *= al;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int tok = min(blk + 16 * sub + c16, L - 1);
-      const int64_t off = PAGED ? kp[sub] + (uint32_t)((tok & pmask) * (int)kst) : (int64_t)tok * kst;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kr[sub][ks] = load_nt16(kbase + off + 32 * ks + 8 * kg);
+      for (int cb = 0; cb < CB; ++cb) o[n2][cb] *= al;
     }
-    uint4 vr[VU][4];
+    // a column that has seen no visible entry yet has every score -inf:
+    // use 0 for its reference so the probabilities are 0, not NaN
+    const float nm = mref[n2] == -INFINITY ? 0.f : -mref[n2];
+    f32x8 p;
+    float ps = 0.f;
 #pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      const int unit = lane + 64 * u;
-      const int rg = unit % (kBlk / 4), cc = unit / (kBlk / 4);
-      // the group's 4 tokens lie in sub-block 4*rg/16 (and in one page)
-      const int64_t vpage = PAGED ? (rg < 4 ? vp[0] : vp[1]) : 0;
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int tok = min(blk + 4 * rg + qq, L - 1);
-        const int64_t off = PAGED ? vpage + (uint32_t)((tok & pmask) * (int)vst) : (int64_t)tok * vst;
-        vr[u][qq] = load_nt16(vbase + off + cc * 8);
-      }
+    for (int r = 0; r < 4; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(fmaf(sc[0][r], sl2, nm));
+      p[r + 4] = __builtin_amdgcn_exp2f(fmaf(sc[1][r], sl2, nm));
+      ps += p[r] + p[r + 4];
     }
-    if constexpr (PAGED) {  // the next step's table entries (in bounds even past the end)
-      const int nb = blk + kBlk * kWaves;
-      raw[0] = table_entry(nb), raw[1] = table_entry(nb + 16);
-    }
+    lsum[n2] += ps;
+    return cvt_bf16x8(p);
+  };
 
-    // ---- scores S[tok][col], softmax state per column ----
-    bf16x8 pk[NCB];  // slot t: token 4kg+t (t<4), 16+4kg+t-4 (t>=4)
-#pragma unroll
-    for (int n = 0; n < NCB; ++n) {
-      f32x4 sc[2];
+  if constexpr (!DMA) {
+    // ---- register path (dense cache, one new token) ----
+    uint16_t* vt = (uint16_t*)smem + wv * VT_ELEMS;
+    constexpr int VU = (kBlk / 4) * (D / 8) / 64;  // 4x8 V units per lane
+    static_assert(VU >= 1 && (kBlk / 4) * (D / 8) % 64 == 0, "V block split");
+    for (int blk = blk0; blk < t1; blk += kBlk * W) {
+      // Tokens past the end load the last token's row instead (no branches,
+      // so the loads stay in flight together): their scores are masked to
+      // -inf below, so their probabilities are 0 and the rows add nothing.
+      uint4 kr[2][KS];
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
-        sc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tok = min(blk + 16 * sub + c16, L - 1);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sc[sub] = mfma16x16x32(as_bf16x8(kr[sub][ks]), qf[n][ks], sc[sub]);
+        for (int ks = 0; ks < KS; ++ks) kr[sub][ks] = load_nt16(kbase + (int64_t)tok * kst + 32 * ks + 8 * kg);
       }
-      // lane (column c16, kg) holds tokens blk + 16*sub + 4*kg + r
-      float mx = -INFINITY;
+      uint4 vr[VU][4];
+#pragma unroll
+      for (int u = 0; u < VU; ++u) {
+        const int unit = lane + 64 * u;
+        const int rg = unit % (kBlk / 4), cc = unit / (kBlk / 4);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int tok = min(blk + 4 * rg + qq, L - 1);
+          vr[u][qq] = load_nt16(vbase + (int64_t)tok * vst + cc * 8);
+        }
+      }
+      f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (blk + 16 * sub + 4 * kg + r >= lim[n]) sc[sub][r] = -INFINITY;
-          mx = fmaxf(mx, sc[sub][r]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // -inf when the whole block is masked for this column (a later query
-      // token's entries only); then nothing changes below
-      const float mb = mx * sl2;
-      const bool need = mb > mref[n] + kLazyLog2;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float al = need ? exp2f(mref[n] - mb) : 1.f;
-        if (need) mref[n] = mb;
-        lsum[n] *= al;
+        for (int ks = 0; ks < KS; ++ks) sc[sub] = mfma16x16x32(as_bf16x8(kr[sub][ks]), qf[0][ks], sc[sub]);
+      const bf16x8 pk = softmax_block(sc, blk, 0);
+      // V block -> V^T in this wave's LDS slice
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) o[n][cb] *= al;
-      }
-      // a column that has seen no visible entry yet has every score -inf:
-      // use 0 for its reference so the probabilities are 0, not NaN
-      const float nm = mref[n] == -INFINITY ? 0.f : -mref[n];
-      f32x8 p;
-      float ps = 0.f;
+      for (int u = 0; u < VU; ++u) {
+        const int unit = lane + 64 * u;
+        const int rg = unit % (kBlk / 4), cc = unit / (kBlk / 4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(fmaf(sc[0][r], sl2, nm));
-        p[r + 4] = __builtin_amdgcn_exp2f(fmaf(sc[1][r], sl2, nm));
-        ps += p[r] + p[r + 4];
+        for (int e = 0; e < 8; ++e)
+          *(uint2*)(vt + (cc * 8 + e) * VROW + 4 * rg) = column4(vr[u][0], vr[u][1], vr[u][2], vr[u][3], e);
       }
-      lsum[n] += ps;
-      pk[n] = cvt_bf16x8(p);
+      lds_fence();
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint16_t* row = vt + (16 * cb + c16) * VROW + 4 * kg;
+        o[0][cb] = mfma16x16x32(join_bf16x8(*(const uint2*)row, *(const uint2*)(row + 16)), pk, o[0][cb]);
+      }
+      lds_fence();
     }
+  } else {
+  // Block n goes to slot n % NST, issued NST - 1 steps ahead (NST = 1: right
+  // after the previous block's reads); the slot it overwrites was last read
+  // at the end of the step before.
+  if (NST == 1) {
+    if (nsteps > 0) issue(0, 0);
+  } else {
+#pragma unroll
+    for (int p = 0; p < NST - 1; ++p)
+      if (p < nsteps) issue(p, p);
+  }
+  for (int n = 0; n < nsteps; ++n) {
+    const int blk = blk0 + kBlk * W * n;
+    const int cur = n % NST;
+    if (NST > 1 && n + NST - 1 < nsteps) issue(n + NST - 1, (n + NST - 1) % NST);
+    // block n's copies have landed once at most the later blocks' remain
+    const int later = NST == 1 ? 0 : min(NST - 1, nsteps - 1 - n);
+    if (NST > 2 && later >= 2) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NI) : "memory");
+    } else if (NST > 1 && later >= 1) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    const uint32_t sb = slot0 + cur * SLOT;
 
-    // ---- V block -> V^T in this wave's LDS slice ----
+    // ---- scores S[tok][col], softmax state per column ----
+    bf16x8 pk[NCB];  // slot t: token 4kg+t (t<4), 16+4kg+t-4 (t>=4)
+    f32x4 sc[NCB][2];
 #pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      const int unit = lane + 64 * u;
-      const int rg = unit % (kBlk / 4), cc = unit / (kBlk / 4);
+    for (int n2 = 0; n2 < NCB; ++n2) sc[n2][0] = sc[n2][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *(uint2*)(vt + (cc * 8 + e) * VROW + 4 * rg) = column4(vr[u][0], vr[u][1], vr[u][2], vr[u][3], e);
-    }
-    lds_fence();
-    // ---- O^T[c][col] += V^T[c][tok] P^T[tok][col] ----
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ka = lds_read16(sb + koff[sub][ks]);
+#pragma unroll
+        for (int n2 = 0; n2 < NCB; ++n2) sc[n2][sub] = mfma16x16x32(ka, qf[n2][ks], sc[n2][sub]);
+      }
+#pragma unroll
+    for (int n2 = 0; n2 < NCB; ++n2) pk[n2] = softmax_block(sc[n2], blk, n2);
+
+    // ---- O^T[c][col] += V^T[c][tok] P^T[tok][col] (V^T by transpose reads) ----
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const uint16_t* row = vt + (16 * cb + c16) * VROW + 4 * kg;
-      const bf16x8 va = join_bf16x8(*(const uint2*)row, *(const uint2*)(row + 16));
+      const bf16x8 va = join_bf16x8(tr_read(sb + voff[cb]), tr_read(sb + voff[cb] + 16 * RB));
 #pragma unroll
-      for (int n = 0; n < NCB; ++n) o[n][cb] = mfma16x16x32(va, pk[n], o[n][cb]);
+      for (int n2 = 0; n2 < NCB; ++n2) o[n2][cb] = mfma16x16x32(va, pk[n2], o[n2][cb]);
     }
-    lds_fence();
+    lds_fence();  // this slot's reads are done before a later copy rewrites it
+    if (NST == 1 && n + 1 < nsteps) issue(n + 1, 0);
+  }
   }
 
   // ---- per column block: per-wave state -> LDS, then a log-sum-exp merge
@@ -311,14 +457,14 @@ __global__ void __launch_bounds__(kWaves * 64, NCB == 1 ? 1 : 2) decode_split_ke
     __syncthreads();
     const int col0 = (cg * NCB + n) * 16;
     const int ncols = min(16, NC - col0);
-    for (int e = tid; e < ncols * (D + 2); e += kWaves * 64) {
+    for (int e = tid; e < ncols * (D + 2); e += W * 64) {
       const int hh = e / (D + 2), c = e % (D + 2);
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[(w * 16 + hh) * (D + 2)]);
+      for (int w = 0; w < W; ++w) M = fmaxf(M, red[(w * 16 + hh) * (D + 2)]);
       float acc = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < W; ++w) {
         const float mw = red[(w * 16 + hh) * (D + 2)];
         const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
         acc += (c == 0 ? 0.f : red[(w * 16 + hh) * (D + 2) + c]) * f;

@@ -29,8 +29,9 @@
  *             or 4 elements (fp32), so rows can be moved with 128-bit loads.
  *             Lambda tensors (fp32, no head_dim axis) only need 4-byte
  *             alignment and have no stride-multiple rule.  For the bf16
- *             prefill entry points the key/value token strides must be below
- *             2^24 elements (DA_E_UNSUPPORTED otherwise).
+ *             prefill entry points, and for the dense decode caches, the key/value
+ *             token strides must be below 2^24 elements (DA_E_UNSUPPORTED
+ *             otherwise).
  *   Stream    Work is enqueued on `stream` (a hipStream_t; NULL = the
  *             default stream) and the call returns without synchronising.
  *   Errors    Status codes only; nothing is thrown, nothing aborts.  All
