@@ -37,7 +37,6 @@ into a workspace, decode caches holding rotated keys).
 from __future__ import annotations
 
 import ctypes
-import math
 from pathlib import Path
 
 import torch
