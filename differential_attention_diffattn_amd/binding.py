@@ -37,16 +37,19 @@ into a workspace, decode caches holding rotated keys).
 from __future__ import annotations
 
 import ctypes
+import os
 from pathlib import Path
 
 import torch
 
-_LIB_PATH = Path(__file__).resolve().parent / "libdiffattn.so"
+# DIFFATTN_LIBRARY names another build of the same sources to load (the
+# host-sanitizer test links one); by default the in-tree libdiffattn.so.
+_LIB_PATH = Path(os.environ.get("DIFFATTN_LIBRARY") or Path(__file__).resolve().parent / "libdiffattn.so")
 _lib = None
 
 DA_FP32, DA_BF16 = 0, 1
 _STATUS = {0: "DA_OK", 1: "DA_E_NULL", 2: "DA_E_DTYPE", 3: "DA_E_SHAPE", 4: "DA_E_LAYOUT",
-           5: "DA_E_UNSUPPORTED", 6: "DA_E_WORKSPACE", 7: "DA_E_LAUNCH"}
+           5: "DA_E_UNSUPPORTED", 6: "DA_E_WORKSPACE", 7: "DA_E_LAUNCH", 8: "DA_E_SCRATCH"}
 
 
 class DiffAttnError(RuntimeError):

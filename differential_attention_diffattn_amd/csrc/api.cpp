@@ -84,7 +84,7 @@ bool grid_fits(long long n) { return n >= 1 && n <= 0x7fffffffLL; }
 // per-tile base, which bounds the key/value token stride.
 constexpr int64_t kMaxTokenStride = int64_t(1) << 24;  // elements
 
-da_status validate_v2_common(da_dtype dtype, int B, int T, int Hq, int Hkv, int d) {
+da_status validate_v2_common(int dtype, int B, int T, int Hq, int Hkv, int d) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1) return DA_E_SHAPE;
   if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return DA_E_SHAPE;
@@ -156,7 +156,7 @@ struct PagedArgs {
   int64_t bt_stride;
   const int32_t* seq_lens;
 };
-da_status decode_impl(int softmax1, da_dtype dtype, int B, int L, int nq, int Hq, int Hkv, int d, da_in q,
+da_status decode_impl(int softmax1, int dtype, int B, int L, int nq, int Hq, int Hkv, int d, da_in q,
                       da_in kc, da_in vc, const PagedArgs* pg, da_in lam, da_out out, void* workspace,
                       size_t workspace_bytes, void* stream, float rope_theta = 0.f,
                       int max_splits = 0x7fffffff, bool use_scratch = false) {
@@ -256,7 +256,7 @@ const char* diffattn_status_string(da_status s) {
   return "unknown status";
 }
 
-static da_status v1_fwd_impl(int softmax1, da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2,
+static da_status v1_fwd_impl(int softmax1, int dtype, int B, int H, int T, int d, da_in q1, da_in q2,
                              da_in k1, da_in k2,
                           da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
                           const float* lam_k2, int layer_index, da_out out, void* stream,
@@ -342,7 +342,7 @@ static da_status v1_fwd_impl(int softmax1, da_dtype dtype, int B, int H, int T, 
   return launch_status(da::launch_v1_fp32(d, a, s));
 }
 
-static da_status v2_fwd_impl(int softmax1, da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
+static da_status v2_fwd_impl(int softmax1, int dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
                              da_in v,
                           da_in lam, da_out out, void* stream, const da_out* attn = nullptr,
                           float* lse = nullptr, const RopeK* rope = nullptr) {
@@ -408,7 +408,7 @@ static BwdWs bwd_ws(int B, int T, int Hq, int d) {
   return w;
 }
 
-static da_status v2_bwd_impl(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
+static da_status v2_bwd_impl(int dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
                              da_in lam, da_in attn, const float* lse, da_in dout, da_out dq, da_out dk, da_out dv,
                              da_out dlam, void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
@@ -458,7 +458,7 @@ static V1BwdWs v1_bwd_ws(int B, int H, int T, int d) {
   return w;
 }
 
-static da_status v1_bwd_impl(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+static da_status v1_bwd_impl(int dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
                              da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
                              const float* lam_k2, int layer_index, da_in attn1, da_in attn2, const float* lse,
                              da_in dout, da_out dq1, da_out dq2, da_out dk1, da_out dk2, da_out dv, float* dlam_q1,
@@ -519,14 +519,14 @@ size_t diffattn_v2_decode_paged_workspace_bytes(int B, int max_len, int nq, int 
   return decode_ws_bytes(B, max_len, nq, Hq, Hkv, d, da::kPagedMaxChunk);
 }
 
-da_status diffattn_v1_fwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+da_status diffattn_v1_fwd(int dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
                           da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
                           const float* lam_k2, int layer_index, da_out out, void* stream) {
   return v1_fwd_impl(0, dtype, B, H, T, d, q1, q2, k1, k2, v, lam_q1, lam_k1, lam_q2, lam_k2, layer_index, out,
                      stream);
 }
 
-da_status diffattn_v1_fwd_softmax1(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1,
+da_status diffattn_v1_fwd_softmax1(int dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1,
                                    da_in k2, da_in v, const float* lam_q1, const float* lam_k1,
                                    const float* lam_q2, const float* lam_k2, int layer_index, da_out out,
                                    void* stream) {
@@ -534,24 +534,24 @@ da_status diffattn_v1_fwd_softmax1(da_dtype dtype, int B, int H, int T, int d, d
                      stream);
 }
 
-da_status diffattn_v2_fwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
+da_status diffattn_v2_fwd(int dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
                           da_in lam, da_out out, void* stream) {
   return v2_fwd_impl(0, dtype, B, T, Hq, Hkv, d, q, k, v, lam, out, stream);
 }
 
-da_status diffattn_v2_fwd_softmax1(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
+da_status diffattn_v2_fwd_softmax1(int dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
                                    da_in v, da_in lam, da_out out, void* stream) {
   return v2_fwd_impl(1, dtype, B, T, Hq, Hkv, d, q, k, v, lam, out, stream);
 }
 
-da_status diffattn_v2_decode(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
+da_status diffattn_v2_decode(int dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
                              da_in v_cache, da_in lam, da_out out, void* workspace, size_t workspace_bytes,
                              void* stream) {
   return decode_impl(0, dtype, B, L, 1, Hq, Hkv, d, q, k_cache, v_cache, nullptr, lam, out, workspace,
                      workspace_bytes, stream);
 }
 
-da_status diffattn_v2_decode_noalloc(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
+da_status diffattn_v2_decode_noalloc(int dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
                                      da_in v_cache, da_in lam, da_out out, void* stream) {
   if (!decode_sizes_ok(B, L, 1, Hq, Hkv, d)) return DA_E_SHAPE;
   // as many splits as the static scratch holds (at least one), never more
@@ -566,28 +566,28 @@ da_status diffattn_v2_decode_noalloc(da_dtype dtype, int B, int L, int Hq, int H
 
 size_t diffattn_v2_decode_noalloc_max_bytes(void) { return kScratchBytes; }
 
-da_status diffattn_v2_decode_softmax1(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
+da_status diffattn_v2_decode_softmax1(int dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
                                       da_in k_cache, da_in v_cache, da_in lam, da_out out, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   return decode_impl(1, dtype, B, L, 1, Hq, Hkv, d, q, k_cache, v_cache, nullptr, lam, out, workspace,
                      workspace_bytes, stream);
 }
 
-da_status diffattn_v2_decode_multi(da_dtype dtype, int B, int L, int nq, int Hq, int Hkv, int d, da_in q,
+da_status diffattn_v2_decode_multi(int dtype, int B, int L, int nq, int Hq, int Hkv, int d, da_in q,
                                    da_in k_cache, da_in v_cache, da_in lam, da_out out, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   return decode_impl(0, dtype, B, L, nq, Hq, Hkv, d, q, k_cache, v_cache, nullptr, lam, out, workspace,
                      workspace_bytes, stream);
 }
 
-da_status diffattn_v2_decode_multi_softmax1(da_dtype dtype, int B, int L, int nq, int Hq, int Hkv, int d,
+da_status diffattn_v2_decode_multi_softmax1(int dtype, int B, int L, int nq, int Hq, int Hkv, int d,
                                             da_in q, da_in k_cache, da_in v_cache, da_in lam, da_out out,
                                             void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(1, dtype, B, L, nq, Hq, Hkv, d, q, k_cache, v_cache, nullptr, lam, out, workspace,
                      workspace_bytes, stream);
 }
 
-da_status diffattn_v2_decode_paged(da_dtype dtype, int B, int max_len, int nq, int Hq, int Hkv, int d, da_in q,
+da_status diffattn_v2_decode_paged(int dtype, int B, int max_len, int nq, int Hq, int Hkv, int d, da_in q,
                                    da_in k_pages, da_in v_pages, int num_pages, int page_size,
                                    const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                                    da_in lam, da_out out, void* workspace, size_t workspace_bytes,
@@ -597,7 +597,7 @@ da_status diffattn_v2_decode_paged(da_dtype dtype, int B, int max_len, int nq, i
                      workspace_bytes, stream);
 }
 
-da_status diffattn_v2_decode_paged_softmax1(da_dtype dtype, int B, int max_len, int nq, int Hq, int Hkv, int d,
+da_status diffattn_v2_decode_paged_softmax1(int dtype, int B, int max_len, int nq, int Hq, int Hkv, int d,
                                             da_in q, da_in k_pages, da_in v_pages, int num_pages, int page_size,
                                             const int32_t* block_table, int64_t bt_stride,
                                             const int32_t* seq_lens, da_in lam, da_out out, void* workspace,
@@ -607,12 +607,12 @@ da_status diffattn_v2_decode_paged_softmax1(da_dtype dtype, int B, int max_len, 
                      workspace_bytes, stream);
 }
 
-da_status diffattn_v2_fwd_train(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
+da_status diffattn_v2_fwd_train(int dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
                                 da_in lam, da_out out, da_out attn, float* lse, void* stream) {
   return v2_fwd_impl(0, dtype, B, T, Hq, Hkv, d, q, k, v, lam, out, stream, &attn, lse);
 }
 
-da_status diffattn_v2_fwd_train_softmax1(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
+da_status diffattn_v2_fwd_train_softmax1(int dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
                                          da_in v, da_in lam, da_out out, da_out attn, float* lse, void* stream) {
   return v2_fwd_impl(1, dtype, B, T, Hq, Hkv, d, q, k, v, lam, out, stream, &attn, lse);
 }
@@ -624,14 +624,14 @@ size_t diffattn_v2_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d) {
   return w.dA + 2 * w.rows;
 }
 
-da_status diffattn_v2_bwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
+da_status diffattn_v2_bwd(int dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
                           da_in lam, da_in attn, const float* lse, da_in dout, da_out dq, da_out dk, da_out dv,
                           da_out dlam, void* workspace, size_t workspace_bytes, void* stream) {
   return v2_bwd_impl(dtype, B, T, Hq, Hkv, d, q, k, v, lam, attn, lse, dout, dq, dk, dv, dlam, workspace,
                      workspace_bytes, stream);
 }
 
-da_status diffattn_v1_fwd_train(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+da_status diffattn_v1_fwd_train(int dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
                                 da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
                                 const float* lam_k2, int layer_index, da_out out, da_out attn1, da_out attn2,
                                 float* lse, void* stream) {
@@ -639,7 +639,7 @@ da_status diffattn_v1_fwd_train(da_dtype dtype, int B, int H, int T, int d, da_i
                      stream, &attn1, &attn2, lse);
 }
 
-da_status diffattn_v1_fwd_train_softmax1(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2,
+da_status diffattn_v1_fwd_train_softmax1(int dtype, int B, int H, int T, int d, da_in q1, da_in q2,
                                          da_in k1, da_in k2, da_in v, const float* lam_q1, const float* lam_k1,
                                          const float* lam_q2, const float* lam_k2, int layer_index, da_out out,
                                          da_out attn1, da_out attn2, float* lse, void* stream) {
@@ -652,7 +652,7 @@ size_t diffattn_v1_bwd_workspace_bytes(int B, int H, int T, int d) {
   return v1_bwd_ws(B, H, T, d).total();
 }
 
-da_status diffattn_v1_bwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+da_status diffattn_v1_bwd(int dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
                           da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
                           const float* lam_k2, int layer_index, da_in attn1, da_in attn2, const float* lse,
                           da_in dout, da_out dq1, da_out dq2, da_out dk1, da_out dk2, da_out dv, float* dlam_q1,
@@ -668,7 +668,7 @@ size_t diffattn_v1_fwd_rope_workspace_bytes(int B, int H, int T, int d) {
   return 2 * rope_k_bytes(B, T, H, d);
 }
 
-da_status diffattn_v1_fwd_rope(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+da_status diffattn_v1_fwd_rope(int dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
                                da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
                                const float* lam_k2, int layer_index, float theta, da_out out, void* workspace,
                                size_t workspace_bytes, void* stream) {
@@ -682,14 +682,14 @@ size_t diffattn_v2_fwd_rope_workspace_bytes(int B, int T, int Hkv, int d) {
   return rope_k_bytes(B, T, Hkv, d);
 }
 
-da_status diffattn_v2_fwd_rope(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
+da_status diffattn_v2_fwd_rope(int dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
                                da_in lam, float theta, da_out out, void* workspace, size_t workspace_bytes,
                                void* stream) {
   const RopeK r{theta, workspace, workspace_bytes};
   return v2_fwd_impl(0, dtype, B, T, Hq, Hkv, d, q, k, v, lam, out, stream, nullptr, nullptr, &r);
 }
 
-da_status diffattn_v2_decode_rope(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
+da_status diffattn_v2_decode_rope(int dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
                                   da_in v_cache, da_in lam, float theta, da_out out, void* workspace,
                                   size_t workspace_bytes, void* stream) {
   if (!rope_theta_ok(theta)) return DA_E_SHAPE;
@@ -697,7 +697,7 @@ da_status diffattn_v2_decode_rope(da_dtype dtype, int B, int L, int Hq, int Hkv,
                      workspace_bytes, stream, theta);
 }
 
-da_status diffattn_v2_decode_paged_rope(da_dtype dtype, int B, int max_len, int nq, int Hq, int Hkv, int d, da_in q,
+da_status diffattn_v2_decode_paged_rope(int dtype, int B, int max_len, int nq, int Hq, int Hkv, int d, da_in q,
                                         da_in k_pages, da_in v_pages, int num_pages, int page_size,
                                         const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                                         da_in lam, float theta, da_out out, void* workspace,
@@ -708,7 +708,7 @@ da_status diffattn_v2_decode_paged_rope(da_dtype dtype, int B, int max_len, int 
                      workspace_bytes, stream, theta);
 }
 
-da_status diffattn_v1_fwd_softmax1_rope(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1,
+da_status diffattn_v1_fwd_softmax1_rope(int dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1,
                                        da_in k2, da_in v, const float* lam_q1, const float* lam_k1,
                                        const float* lam_q2, const float* lam_k2, int layer_index, float theta,
                                        da_out out, void* workspace, size_t workspace_bytes, void* stream) {
@@ -717,14 +717,14 @@ da_status diffattn_v1_fwd_softmax1_rope(da_dtype dtype, int B, int H, int T, int
                      stream, nullptr, nullptr, nullptr, &r);
 }
 
-da_status diffattn_v2_fwd_softmax1_rope(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
+da_status diffattn_v2_fwd_softmax1_rope(int dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
                                        da_in v, da_in lam, float theta, da_out out, void* workspace,
                                        size_t workspace_bytes, void* stream) {
   const RopeK r{theta, workspace, workspace_bytes};
   return v2_fwd_impl(1, dtype, B, T, Hq, Hkv, d, q, k, v, lam, out, stream, nullptr, nullptr, &r);
 }
 
-da_status diffattn_v2_decode_softmax1_rope(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
+da_status diffattn_v2_decode_softmax1_rope(int dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
                                           da_in k_cache, da_in v_cache, da_in lam, float theta, da_out out,
                                           void* workspace, size_t workspace_bytes, void* stream) {
   if (!rope_theta_ok(theta)) return DA_E_SHAPE;
@@ -732,7 +732,7 @@ da_status diffattn_v2_decode_softmax1_rope(da_dtype dtype, int B, int L, int Hq,
                      workspace_bytes, stream, theta);
 }
 
-da_status diffattn_v2_decode_paged_softmax1_rope(da_dtype dtype, int B, int max_len, int nq, int Hq, int Hkv, int d,
+da_status diffattn_v2_decode_paged_softmax1_rope(int dtype, int B, int max_len, int nq, int Hq, int Hkv, int d,
                                                 da_in q, da_in k_pages, da_in v_pages, int num_pages, int page_size,
                                                 const int32_t* block_table, int64_t bt_stride,
                                                 const int32_t* seq_lens, da_in lam, float theta, da_out out,
@@ -743,7 +743,7 @@ da_status diffattn_v2_decode_paged_softmax1_rope(da_dtype dtype, int B, int max_
                      workspace_bytes, stream, theta);
 }
 
-da_status diffattn_rope(da_dtype dtype, int B, int T, int H, int d, da_in x, da_out out, float theta, int pos0,
+da_status diffattn_rope(int dtype, int B, int T, int H, int d, da_in x, da_out out, float theta, int pos0,
                         void* stream) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
   if (B < 1 || T < 1 || H < 1 || d < 1 || pos0 < 0) return DA_E_SHAPE;
@@ -761,7 +761,7 @@ da_status diffattn_rope(da_dtype dtype, int B, int T, int H, int d, da_in x, da_
   return launch_status(da::launch_rope_bf16(r, (hipStream_t)stream));
 }
 
-da_status diffattn_v2_lambda_proj(da_dtype dtype, int B, int T, int dm, int P, da_in x, da_in w, da_in out,
+da_status diffattn_v2_lambda_proj(int dtype, int B, int T, int dm, int P, da_in x, da_in w, da_in out,
                                   void* stream) {
   if (dtype != DA_FP32 && dtype != DA_BF16) return DA_E_DTYPE;
   if (B < 1 || T < 1 || dm < 1 || P < 1) return DA_E_SHAPE;

@@ -69,6 +69,9 @@ typedef enum {
                           /* the library's static scratch                       */
 } da_status;
 
+/* Element types.  Entry points take the dtype as a plain int holding one of
+ * these values, so any other value a caller passes is reported as
+ * DA_E_DTYPE (an out-of-range enum argument would be undefined in C++). */
 typedef enum { DA_FP32 = 0, DA_BF16 = 1 } da_dtype;
 
 /* Read-only device tensor: base pointer + element strides by role. */
@@ -107,7 +110,7 @@ typedef struct {
  * lam is one scalar per call shared by every head, computed on the device
  * in fp32; it may take any real value (no clamp).
  */
-da_status diffattn_v1_fwd(da_dtype dtype, int B, int H, int T, int d,
+da_status diffattn_v1_fwd(int dtype, int B, int H, int T, int d,
                           da_in q1, da_in q2, da_in k1, da_in k2, da_in v,
                           const float* lam_q1, const float* lam_k1,
                           const float* lam_q2, const float* lam_k2,
@@ -129,7 +132,7 @@ da_status diffattn_v1_fwd(da_dtype dtype, int B, int H, int T, int d,
  *   lam     logical [B,T,Hq/2] fp32 logits (roles b, h = pair, t); +-inf allowed.
  *   out     logical [B,T,Hq/2,d] bf16 (roles b, h = pair, t).
  */
-da_status diffattn_v2_fwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d,
+da_status diffattn_v2_fwd(int dtype, int B, int T, int Hq, int Hkv, int d,
                           da_in q, da_in k, da_in v, da_in lam,
                           da_out out, void* stream);
 
@@ -163,7 +166,7 @@ size_t diffattn_v2_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int d);
  *              do not matter and on return are unspecified.
  * Two kernels are enqueued on `stream` (split, then merge).
  */
-da_status diffattn_v2_decode(da_dtype dtype, int B, int L, int Hq, int Hkv, int d,
+da_status diffattn_v2_decode(int dtype, int B, int L, int Hq, int Hkv, int d,
                              da_in q, da_in k_cache, da_in v_cache, da_in lam,
                              da_out out, void* workspace, size_t workspace_bytes,
                              void* stream);
@@ -181,15 +184,15 @@ da_status diffattn_v2_decode(da_dtype dtype, int B, int L, int Hq, int Hkv, int 
  * Arguments, layouts, validation, workspace and errors are those of the
  * namesake.
  */
-da_status diffattn_v1_fwd_softmax1(da_dtype dtype, int B, int H, int T, int d,
+da_status diffattn_v1_fwd_softmax1(int dtype, int B, int H, int T, int d,
                                    da_in q1, da_in q2, da_in k1, da_in k2, da_in v,
                                    const float* lam_q1, const float* lam_k1,
                                    const float* lam_q2, const float* lam_k2,
                                    int layer_index, da_out out, void* stream);
-da_status diffattn_v2_fwd_softmax1(da_dtype dtype, int B, int T, int Hq, int Hkv, int d,
+da_status diffattn_v2_fwd_softmax1(int dtype, int B, int T, int Hq, int Hkv, int d,
                                    da_in q, da_in k, da_in v, da_in lam,
                                    da_out out, void* stream);
-da_status diffattn_v2_decode_softmax1(da_dtype dtype, int B, int L, int Hq, int Hkv, int d,
+da_status diffattn_v2_decode_softmax1(int dtype, int B, int L, int Hq, int Hkv, int d,
                                       da_in q, da_in k_cache, da_in v_cache, da_in lam,
                                       da_out out, void* workspace, size_t workspace_bytes,
                                       void* stream);
@@ -217,12 +220,12 @@ da_status diffattn_v2_decode_softmax1(da_dtype dtype, int B, int L, int Hq, int 
  * token, head) pairs of a kv head.  Two kernels are enqueued on `stream`.
  */
 size_t diffattn_v2_decode_multi_workspace_bytes(int B, int L, int nq, int Hq, int Hkv, int d);
-da_status diffattn_v2_decode_multi(da_dtype dtype, int B, int L, int nq, int Hq, int Hkv, int d,
+da_status diffattn_v2_decode_multi(int dtype, int B, int L, int nq, int Hq, int Hkv, int d,
                                    da_in q, da_in k_cache, da_in v_cache, da_in lam,
                                    da_out out, void* workspace, size_t workspace_bytes,
                                    void* stream);
 /* Off-by-one softmax variant of diffattn_v2_decode_multi. */
-da_status diffattn_v2_decode_multi_softmax1(da_dtype dtype, int B, int L, int nq, int Hq, int Hkv,
+da_status diffattn_v2_decode_multi_softmax1(int dtype, int B, int L, int nq, int Hq, int Hkv,
                                             int d, da_in q, da_in k_cache, da_in v_cache,
                                             da_in lam, da_out out, void* workspace,
                                             size_t workspace_bytes, void* stream);
@@ -275,7 +278,7 @@ size_t diffattn_v2_decode_paged_workspace_bytes(int B, int max_len, int nq, int 
  * lengths live on the device and are not checked on the host.
  * Two kernels are enqueued on `stream` (split, then merge).
  */
-da_status diffattn_v2_decode_paged(da_dtype dtype, int B, int max_len, int nq, int Hq, int Hkv, int d,
+da_status diffattn_v2_decode_paged(int dtype, int B, int max_len, int nq, int Hq, int Hkv, int d,
                                    da_in q, da_in k_pages, da_in v_pages,
                                    int num_pages, int page_size,
                                    const int32_t* block_table, int64_t bt_stride,
@@ -283,7 +286,7 @@ da_status diffattn_v2_decode_paged(da_dtype dtype, int B, int max_len, int nq, i
                                    void* workspace, size_t workspace_bytes, void* stream);
 /* Off-by-one softmax variant of diffattn_v2_decode_paged (see the
  * *_softmax1 entry points above); a sequence of length 0 also gets 0. */
-da_status diffattn_v2_decode_paged_softmax1(da_dtype dtype, int B, int max_len, int nq, int Hq,
+da_status diffattn_v2_decode_paged_softmax1(int dtype, int B, int max_len, int nq, int Hq,
                                             int Hkv, int d, da_in q, da_in k_pages, da_in v_pages,
                                             int num_pages, int page_size,
                                             const int32_t* block_table, int64_t bt_stride,
@@ -305,10 +308,10 @@ da_status diffattn_v2_decode_paged_softmax1(da_dtype dtype, int B, int max_len, 
  * Other arguments, layouts and errors as for diffattn_v2_fwd; DA_E_NULL for
  * a NULL lse, DA_E_LAYOUT for a misaligned one.
  */
-da_status diffattn_v2_fwd_train(da_dtype dtype, int B, int T, int Hq, int Hkv, int d,
+da_status diffattn_v2_fwd_train(int dtype, int B, int T, int Hq, int Hkv, int d,
                                 da_in q, da_in k, da_in v, da_in lam,
                                 da_out out, da_out attn, float* lse, void* stream);
-da_status diffattn_v2_fwd_train_softmax1(da_dtype dtype, int B, int T, int Hq, int Hkv, int d,
+da_status diffattn_v2_fwd_train_softmax1(int dtype, int B, int T, int Hq, int Hkv, int d,
                                          da_in q, da_in k, da_in v, da_in lam,
                                          da_out out, da_out attn, float* lse, void* stream);
 
@@ -339,7 +342,7 @@ size_t diffattn_v2_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d);
  * sums over heads and keys are taken in a fixed order (deterministic).
  * Token strides of q, k, v must be below 2^24 elements (DA_E_UNSUPPORTED).
  */
-da_status diffattn_v2_bwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d,
+da_status diffattn_v2_bwd(int dtype, int B, int T, int Hq, int Hkv, int d,
                           da_in q, da_in k, da_in v, da_in lam, da_in attn,
                           const float* lse, da_in dout, da_out dq, da_out dk, da_out dv,
                           da_out dlam, void* workspace, size_t workspace_bytes, void* stream);
@@ -360,11 +363,11 @@ da_status diffattn_v2_bwd(da_dtype dtype, int B, int T, int Hq, int Hkv, int d,
  * (DA_E_UNSUPPORTED for fp32); DA_E_NULL for a NULL lse, DA_E_LAYOUT for a
  * misaligned one.
  */
-da_status diffattn_v1_fwd_train(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+da_status diffattn_v1_fwd_train(int dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
                                 da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
                                 const float* lam_k2, int layer_index, da_out out, da_out attn1, da_out attn2,
                                 float* lse, void* stream);
-da_status diffattn_v1_fwd_train_softmax1(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2,
+da_status diffattn_v1_fwd_train_softmax1(int dtype, int B, int H, int T, int d, da_in q1, da_in q2,
                                          da_in k1, da_in k2, da_in v, const float* lam_q1, const float* lam_k1,
                                          const float* lam_q2, const float* lam_k2, int layer_index, da_out out,
                                          da_out attn1, da_out attn2, float* lse, void* stream);
@@ -404,7 +407,7 @@ size_t diffattn_v1_bwd_workspace_bytes(int B, int H, int T, int d);
  * (deterministic).  Token strides of q1 .. v must be below 2^24 elements
  * (DA_E_UNSUPPORTED).
  */
-da_status diffattn_v1_bwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+da_status diffattn_v1_bwd(int dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
                           da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
                           const float* lam_k2, int layer_index, da_in attn1, da_in attn2, const float* lse,
                           da_in dout, da_out dq1, da_out dq2, da_out dk1, da_out dk2, da_out dv, float* dlam_q1,
@@ -425,7 +428,7 @@ da_status diffattn_v1_bwd(da_dtype dtype, int B, int H, int T, int d, da_in q1, 
  *   HBM-bound kernel.  Use it for keys written into a cache, which the
  *   decode entry points below expect rotated.
  */
-da_status diffattn_rope(da_dtype dtype, int B, int T, int H, int d, da_in x, da_out out, float theta, int pos0,
+da_status diffattn_rope(int dtype, int B, int T, int H, int d, da_in x, da_out out, float theta, int pos0,
                         void* stream);
 
 /*
@@ -440,12 +443,12 @@ da_status diffattn_rope(da_dtype dtype, int B, int T, int H, int d, da_in x, da_
  * (DA_E_WORKSPACE otherwise).  bf16 only; T < 2^24.
  */
 size_t diffattn_v1_fwd_rope_workspace_bytes(int B, int H, int T, int d);
-da_status diffattn_v1_fwd_rope(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
+da_status diffattn_v1_fwd_rope(int dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,
                                da_in v, const float* lam_q1, const float* lam_k1, const float* lam_q2,
                                const float* lam_k2, int layer_index, float theta, da_out out, void* workspace,
                                size_t workspace_bytes, void* stream);
 size_t diffattn_v2_fwd_rope_workspace_bytes(int B, int T, int Hkv, int d);
-da_status diffattn_v2_fwd_rope(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
+da_status diffattn_v2_fwd_rope(int dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,
                                da_in lam, float theta, da_out out, void* workspace, size_t workspace_bytes,
                                void* stream);
 
@@ -457,10 +460,10 @@ da_status diffattn_v2_fwd_rope(da_dtype dtype, int B, int T, int Hq, int Hkv, in
  * them).  Arguments, workspace and errors as for diffattn_v2_decode /
  * diffattn_v2_decode_paged, plus theta (DA_E_SHAPE unless finite and > 0).
  */
-da_status diffattn_v2_decode_rope(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
+da_status diffattn_v2_decode_rope(int dtype, int B, int L, int Hq, int Hkv, int d, da_in q, da_in k_cache,
                                   da_in v_cache, da_in lam, float theta, da_out out, void* workspace,
                                   size_t workspace_bytes, void* stream);
-da_status diffattn_v2_decode_paged_rope(da_dtype dtype, int B, int max_len, int nq, int Hq, int Hkv, int d, da_in q,
+da_status diffattn_v2_decode_paged_rope(int dtype, int B, int max_len, int nq, int Hq, int Hkv, int d, da_in q,
                                         da_in k_pages, da_in v_pages, int num_pages, int page_size,
                                         const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                                         da_in lam, float theta, da_out out, void* workspace,
@@ -471,17 +474,17 @@ da_status diffattn_v2_decode_paged_rope(da_dtype dtype, int B, int max_len, int 
  * replaced by the off-by-one softmax (as the *_softmax1 entry points do):
  * identical arguments, checks and workspaces.
  */
-da_status diffattn_v1_fwd_softmax1_rope(da_dtype dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1,
+da_status diffattn_v1_fwd_softmax1_rope(int dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1,
                                        da_in k2, da_in v, const float* lam_q1, const float* lam_k1,
                                        const float* lam_q2, const float* lam_k2, int layer_index, float theta,
                                        da_out out, void* workspace, size_t workspace_bytes, void* stream);
-da_status diffattn_v2_fwd_softmax1_rope(da_dtype dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
+da_status diffattn_v2_fwd_softmax1_rope(int dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k,
                                        da_in v, da_in lam, float theta, da_out out, void* workspace,
                                        size_t workspace_bytes, void* stream);
-da_status diffattn_v2_decode_softmax1_rope(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
+da_status diffattn_v2_decode_softmax1_rope(int dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
                                           da_in k_cache, da_in v_cache, da_in lam, float theta, da_out out,
                                           void* workspace, size_t workspace_bytes, void* stream);
-da_status diffattn_v2_decode_paged_softmax1_rope(da_dtype dtype, int B, int max_len, int nq, int Hq, int Hkv, int d,
+da_status diffattn_v2_decode_paged_softmax1_rope(int dtype, int B, int max_len, int nq, int Hq, int Hkv, int d,
                                                 da_in q, da_in k_pages, da_in v_pages, int num_pages, int page_size,
                                                 const int32_t* block_table, int64_t bt_stride,
                                                 const int32_t* seq_lens, da_in lam, float theta, da_out out,
@@ -503,7 +506,7 @@ da_status diffattn_v2_decode_paged_softmax1_rope(da_dtype dtype, int B, int max_
  * time on one GPU (different streams, or threads without ordering) race and
  * give wrong results; calls on one stream are ordered and safe.
  */
-da_status diffattn_v2_decode_noalloc(da_dtype dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
+da_status diffattn_v2_decode_noalloc(int dtype, int B, int L, int Hq, int Hkv, int d, da_in q,
                                      da_in k_cache, da_in v_cache, da_in lam, da_out out, void* stream);
 size_t diffattn_v2_decode_noalloc_max_bytes(void);
 
@@ -520,7 +523,7 @@ size_t diffattn_v2_decode_noalloc_max_bytes(void);
  *   dm a multiple of 128 (DA_E_UNSUPPORTED otherwise).  One kernel, MFMA,
  *   reads x once; sums over dm in a fixed order (deterministic).
  */
-da_status diffattn_v2_lambda_proj(da_dtype dtype, int B, int T, int dm, int P, da_in x, da_in w, da_in out,
+da_status diffattn_v2_lambda_proj(int dtype, int B, int T, int dm, int P, da_in x, da_in w, da_in out,
                                   void* stream);
 
 /* lambda_init = 0.8 - 0.6*exp(-0.3*layer_index), as the V1 kernels use it

@@ -34,6 +34,9 @@ import numpy as np
 _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "diffattn_oracle.c"
 _LIB = _HERE / "liboracle.so"
+# A prebuilt copy of this same source to load instead (the sanitizer test
+# builds one with -fsanitize=address,undefined); never built here.
+_LIB_OVERRIDE = os.environ.get("DIFFATTN_ORACLE_LIBRARY")
 
 _lib = None
 
@@ -55,6 +58,9 @@ def build(force: bool = True) -> Path:
 def _load():
     global _lib
     if _lib is not None:
+        return _lib
+    if _LIB_OVERRIDE:
+        _lib = _configure(ctypes.CDLL(_LIB_OVERRIDE))
         return _lib
     if not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
         build(force=True)
