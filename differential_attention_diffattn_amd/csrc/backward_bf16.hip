@@ -326,13 +326,27 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
 // over the group's query heads and the row tiles at or after their keys.
 // (Splitting dV and dK over two waves keeps each under 256 registers, so two
 // waves share a SIMD; both rebuild P, only the dK wave needs dP.)
+//
+// Per (row tile, head) iteration a wave issues its LDS operand reads as one
+// batch ahead of the MFMAs that use them, and keeps scalar and vector
+// bookkeeping out of the loop: copy addresses advance by running (head, row)
+// counters from per-lane offsets computed once; the causal and ragged-tail
+// masks are applied only on the tiles that need them (a uniform branch); and
+// no VALU op subtracts D: the dK wave's dP accumulator starts from the
+// tile's D values (read from LDS straight into it) and its V fragments are
+// negated once, so the MFMAs leave D - dP, P (D - dP) = -dS, and the dK
+// accumulator is negated when stored.
 template <int D>
 __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int NW = 2 * kNW;
   constexpr int KS = D / 16, CB = D / 32;
-  using Dma = TileDma<D, NW>;
-  constexpr int TB = Dma::BYTES;
+  constexpr int RB = 2 * D;      // bytes of a tile row
+  constexpr int TB = kBT * RB;   // bytes of one tensor tile
+  constexpr int CH = TB / 1024;  // 1 KB copies per tensor tile
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  static_assert(CH <= NW, "a wave copies at most one 1 KB chunk of a tensor tile");
   constexpr int STAGE = 4 * TB + 256;  // [Q "k" | Q "v" | dA "k" | dA "v" | lse, D of the 32 rows]
+  static_assert(STAGE % 256 == 0 && TB % 256 == 0, "tile bases leave the row's chunk bits free");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * STAGE];  // two pairs of stages
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
@@ -344,27 +358,23 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   // holding two dK waves
   const int kb = wave % kNW;
   const bool kwave = wave >= kNW;  // accumulates dK (else dV)
-  const int T = a.T, BK = 32 * kNW;
-  const int ktiles = (T + BK - 1) / BK;
+  const int T = a.T, G = a.G, BK = 32 * kNW;
   const int units = a.B * a.Hkv;
   const int unit = blockIdx.x % units, kt = blockIdx.x / units;  // low key tiles (most rows) first
   const int b = unit / a.Hkv, g = unit % a.Hkv;
   const int J0 = kt * BK, j0w = J0 + 32 * kb;
-  (void)ktiles;
   const bool active = j0w < T;
   const int key = j0w + li;
   const int nrt = (T + kBT - 1) / kBT;  // row tiles of 32
   const int rt0 = J0 / kBT;
-  const int nit = a.G * (nrt - rt0);    // (row tile, head) iterations
+  const int nit = G * (nrt - rt0);    // (row tile, head) iterations
   // Iteration it: row tile nrt-1 - it/G (rows descending), head g*G + it%G.
   // Every workgroup starts at the last row tile and they step down in
   // lockstep, so the workgroups of one kv group (one XCD: the group varies
   // fastest in the grid order) read the same Q / dA tiles at about the same
   // time, from that XCD's L2; a workgroup stops at its own first keys.
-  auto it_row0 = [&](int it) { return (nrt - 1 - it / a.G) * kBT; };
-  auto it_head = [&](int it) { return g * a.G + it % a.G; };
 
-  // B operands: K^T (both waves) and V^T (the dK wave) of this wave's keys
+  // B operands: K^T (both waves) and -V^T (the dK wave) of this wave's keys
   bf16x8 kf[KS], vf[KS];
   {
     const uint16_t* kr = (const uint16_t*)a.k.p + b * a.k.sb + (int64_t)key * a.k.st + g * a.k.sh;
@@ -378,89 +388,177 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
     for (int ks = 0; ks < KS; ++ks) {
       retire(kf[ks]);
       retire(vf[ks]);
+      const uint4 u = as_u4(vf[ks]);  // sign flip of every bf16 (exact)
+      vf[ks] = as_bf16x8(make_uint4(u.x ^ 0x80008000u, u.y ^ 0x80008000u, u.z ^ 0x80008000u, u.w ^ 0x80008000u));
     }
   }
-  auto issue = [&](int it, int stage) {
-    const int hh = it_head(it), i0 = it_row0(it);
-    const uint16_t* qp = (const uint16_t*)a.q.p + b * a.q.sb + hh * a.q.sh;
-    const uint16_t* ap = a.dA + ((int64_t)b * T * a.Hq + hh) * D;
+
+  // Copies.  Wave w < CH moves 1 KB chunk w of every tensor tile: the lane's
+  // 16 bytes go to destination row cr, chunk cc, and come from source chunk
+  // cc ^ swizzle(cr) (row cr, or the last row of a ragged tile).
+  const bool copier = wave < CH;
+  const int cr = (wave * 64 + lane) / CPR, cc = lane % CPR;
+  const uint32_t qst = (uint32_t)a.q.st, ast = (uint32_t)(a.Hq * D);  // element strides (< 2^24)
+  const int swk = k_swizzle<D>(cr), swv = v_swizzle<D>(cr);
+  auto src_off = [&](int srow, uint32_t st, int sw) {
+    return ((uint32_t)srow * st + (uint32_t)((cc ^ sw) * 8)) * 2u;
+  };
+  const uint32_t o_qk = src_off(cr, qst, swk), o_qv = src_off(cr, qst, swv);
+  const uint32_t o_ak = src_off(cr, ast, swk), o_av = src_off(cr, ast, swv);
+  const uint16_t* qg = (const uint16_t*)a.q.p + b * a.q.sb + (int64_t)g * G * a.q.sh;
+  const uint16_t* ag = a.dA + (int64_t)b * T * a.Hq * D + (int64_t)g * G * D;
+  const float* lg = a.lsew + ((int64_t)b * a.Hq + g * G) * a.Tp;
+  const float* dg = a.Dw + ((int64_t)b * a.Hq + g * G) * a.Tp;
+  int iss_h = 0, iss_r0 = (nrt - 1) * kBT;  // the next iteration to copy
+  auto issue = [&](int stage) {
     const uint32_t st = lds0 + stage * STAGE;
-    Dma::issue(qp, a.q.st, i0, T, false, st, wave, lane);
-    Dma::issue(qp, a.q.st, i0, T, true, st + TB, wave, lane);
-    Dma::issue(ap, (int64_t)a.Hq * D, i0, T, false, st + 2 * TB, wave, lane);
-    Dma::issue(ap, (int64_t)a.Hq * D, i0, T, true, st + 3 * TB, wave, lane);
+    const int i0 = iss_r0, hh = iss_h;
+    if (++iss_h == G) {
+      iss_h = 0;
+      iss_r0 -= kBT;
+    }
+    if (copier) {
+      const uint16_t* qp = qg + (int64_t)hh * a.q.sh + (int64_t)i0 * a.q.st;
+      const uint16_t* ap = ag + (int64_t)hh * D + (int64_t)i0 * ast;
+      uint32_t oqk = o_qk, oqv = o_qv, oak = o_ak, oav = o_av;
+      if (i0 + kBT > T) {  // ragged last row tile: rows past T repeat row T - 1
+        const int rr = min(cr, T - 1 - i0);
+        oqk = src_off(rr, qst, swk);
+        oqv = src_off(rr, qst, swv);
+        oak = src_off(rr, ast, swk);
+        oav = src_off(rr, ast, swv);
+      }
+      const uint32_t dst = st + wave * 1024;
+      dma16_sbase(qp, oqk, dst);
+      dma16_sbase(qp, oqv, dst + TB);
+      dma16_sbase(ap, oak, dst + 2 * TB);
+      dma16_sbase(ap, oav, dst + 3 * TB);
+    }
     // the 32 rows' lse and D (padded arrays: always in bounds), 8 lanes x 16 B each
-    const int64_t rbase = ((int64_t)b * a.Hq + hh) * a.Tp + i0;
-    if (wave == NW - 2 && lane < 8) dma16_sbase(a.lsew + rbase, lane * 16, st + 4 * TB);
-    if (wave == NW - 1 && lane < 8) dma16_sbase(a.Dw + rbase, lane * 16, st + 4 * TB + 128);
+    const int64_t ro = (int64_t)hh * a.Tp + i0;
+    if (wave == NW - 2 && lane < 8) dma16_sbase(lg + ro, lane * 16, st + 4 * TB);
+    if (wave == NW - 1 && lane < 8) dma16_sbase(dg + ro, lane * 16, st + 4 * TB + 128);
   };
   // Two row tiles per barrier: the pair (it, it+1) uses stages 2(it/2 mod 2),
   // +1, and the next pair streams into the other two stages meanwhile.
-  issue(0, 0);
-  if (nit > 1) issue(1, 1);
+  issue(0);
+  issue(1);
 
-  uint32_t rb[KS];
-  row_read_bases<D>(li, hg, rb);
+  // Row reads of A operands X[row li][16 ks + 8 hg ..]: chunk (2 ks + hg) ^
+  // swizzle(li) = 2 ks ^ (hg ^ swizzle(li)); tile bases are multiples of 256,
+  // so the read address is (tile base + rxs) ^ 32 ks.
+  const uint32_t rxs = (uint32_t)(li * RB + ((hg ^ k_swizzle<D>(li)) << 4));
   TrBases<D> tb;
   tb.init(lane);
   const float sl2 = a.sl2;
-  f32x16 acc[CB];  // dV^T or dK^T [c][key]
+  f32x16 acc[CB];  // dV^T or -dK^T [c][key]
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
-  auto tile_step = [&](int it, int stage) {
-    const int i0 = it_row0(it);
-    if (!active || i0 < j0w) return;  // rows before this wave's keys
-    const bool diag = i0 == j0w;
-    const uint32_t st = lds0 + stage * STAGE;
-    f32x16 s, dp;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s = mfma32x32x16(lds_read16(st + rb[ks]), kf[ks], s);  // S = Q K^T
-    if (kwave) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) dp = mfma32x32x16(lds_read16(st + 2 * TB + rb[ks]), vf[ks], dp);  // dP = dA V^T
+  int cmp_h = 0, cmp_r0 = (nrt - 1) * kBT;  // the next iteration to compute
+  auto tile_step = [&](int stage, auto kw) {
+    constexpr bool KW = decltype(kw)::value;
+    const int i0 = cmp_r0;
+    if (++cmp_h == G) {
+      cmp_h = 0;
+      cmp_r0 -= kBT;
     }
+    // Tiles of rows before this wave's keys (at most 3 per head, and none
+    // of an inactive wave's results are stored) run like any other with
+    // every probability masked to 0: an early exit here would make the
+    // compiler keep two copies of the accumulators.
+    const uint32_t sb = lds0 + stage * STAGE;
+    // Per-tile LDS bases, opaque to the compiler: every read below is one of
+    // them plus an immediate offset (or, for the row reads, XOR a constant).
+    // Without this the compiler hoists each "lane base + constant" out of the
+    // loop into a register of its own and spills.
+    uint32_t qrow = sb + rxs, arow = sb + 2 * TB + rxs, rowst = sb + 4 * TB + 16 * hg;
+    uint32_t tbase[TrBases<D>::NV];
+#pragma unroll
+    for (int v = 0; v < TrBases<D>::NV; ++v) tbase[v] = sb + (KW ? TB : 3 * TB) + tb.b[v];
+    asm volatile("" : "+v"(qrow), "+v"(arow), "+v"(rowst));
+#pragma unroll
+    for (int v = 0; v < TrBases<D>::NV; ++v) asm volatile("" : "+v"(tbase[v]));
     // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
-    f32x8 e0, e1;
+    f32x4 lq[4], dq4[4];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(st + 4 * TB + (8 * q4 + 4 * hg) * 4);
-      const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(st + 4 * TB + 128 + (8 * q4 + 4 * hg) * 4);
+      lq[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 32 * q4);
+      if constexpr (KW) dq4[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 128 + 32 * q4);
+    }
+    bf16x8 qa[KS], da[KS];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * q4 + j;
-        const int rw = i0 + 8 * q4 + 4 * hg + j;
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[j]));
-        if (rw >= T || (diag && li > rw - i0)) pr = 0.f;
-        const float x = kwave ? pr * (dp[r] - d4[j]) : pr;  // dS (dK wave) or P (dV wave)
-        if (r < 8) e0[r] = x; else e1[r - 8] = x;
+    for (int ks = 0; ks < KS; ++ks) {
+      qa[ks] = lds_read16(qrow ^ (32u * ks));
+      if constexpr (KW) da[ks] = lds_read16(arow ^ (32u * ks));
+    }
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      if constexpr (KW) dp[r] = dq4[r >> 2][r & 3];  // D of the row
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma32x32x16(qa[ks], kf[ks], s);                      // S = Q K^T
+      if constexpr (KW) dp = mfma32x32x16(da[ks], vf[ks], dp);  // D - dP = D + dA (-V)^T
+    }
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], sl2, -lq[r >> 2][r & 3]);
+    if (i0 <= j0w || i0 + kBT > T) {  // diagonal tile, rows before the keys, or rows past T
+      // row offset ro = 4 hg + c (c = 8(r>>2) + (r&3)) is kept if ro < T - i0
+      // and ro >= li (the key's offset) on the diagonal; nothing is kept
+      // before it
+      int lim = T - i0 - 4 * hg, dlo = i0 == j0w ? li - 4 * hg : (i0 < j0w ? 64 : -64);
+      asm volatile("" : "+v"(lim), "+v"(dlo));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 8 * (r >> 2) + (r & 3);
+        x[r] = (c < lim && c >= dlo) ? x[r] : -INFINITY;
       }
     }
+    f32x8 e0, e1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float pr = __builtin_amdgcn_exp2f(x[r]);
+      if constexpr (KW) pr *= dp[r];  // P (D - dP) = -dS
+      if (r < 8) e0[r] = pr; else e1[r - 8] = pr;
+    }
     const bf16x8 xk[2] = {cvt_bf16x8(e0), cvt_bf16x8(e1)};
-    // dV^T += dA^T P (dV wave), dK^T += Q^T dS (dK wave)
-    const uint32_t src = st + (kwave ? TB : 3 * TB);
+    // dV^T += dA^T P (dV wave), -dK^T += Q^T (-dS) (dK wave)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) acc[cb] = mfma32x32x16(tb.read(src, kk, cb), xk[kk], acc[cb]);
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint32_t q = tbase[cb % TrBases<D>::NV] + 16 * kk * RB + cb * 64;
+        acc[cb] = mfma32x32x16(join_bf16x8(tr_read(q), tr_read(q + 8 * RB)), xk[kk], acc[cb]);
+      }
   };
 
-  for (int it = 0; it < nit; it += 2) {
-    const int sp = (it >> 1) & 1;  // stage pair of tiles it, it+1
-    wait_copies();
-    __syncthreads();  // tiles it, it+1 visible; the other stage pair is free
-    if (it + 2 < nit) issue(it + 2, 2 * (sp ^ 1));
-    if (it + 3 < nit) issue(it + 3, 2 * (sp ^ 1) + 1);
-    tile_step(it, 2 * sp);
-    if (it + 1 < nit) tile_step(it + 1, 2 * sp + 1);
-  }
+  // nit is even (the group size G = Hq / Hkv is even), so every pair is
+  // whole; one loop per role keeps each role's accumulators in one set of
+  // registers (no control flow inside the loop joins two assignments).
+  auto run = [&](auto kw) {
+    for (int it = 0; it < nit; it += 2) {
+      const int sp = (it >> 1) & 1;  // stage pair of tiles it, it+1
+      wait_copies();
+      __syncthreads();  // tiles it, it+1 visible; the other stage pair is free
+      if (it + 2 < nit) {
+        issue(2 * (sp ^ 1));
+        issue(2 * (sp ^ 1) + 1);
+      }
+      tile_step(2 * sp, kw);
+      tile_step(2 * sp + 1, kw);
+    }
+  };
+  if (kwave) run(std::true_type{});
+  else run(std::false_type{});
   if (!active || key >= T) return;
   const TOut& o = kwave ? a.dk : a.dv;
-  const float sc = kwave ? a.scale : 1.f;
+  const float sc = kwave ? -a.scale : 1.f;
   uint16_t* dst = (uint16_t*)o.p + b * o.sb + (int64_t)key * o.st + g * o.sh;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
