@@ -136,6 +136,31 @@ struct TileDma {
   }
 };
 
+// The same copies with the per-lane source offsets of a full tile computed
+// once: wave w moves chunks w, w + NW, ... (PER of them); a ragged tile (rows
+// past T) goes through TileDma::issue instead.
+template <int D, int NW>
+struct TileCopy {
+  static constexpr int CH = TileDma<D, NW>::CH;
+  static constexpr int PER = (CH + NW - 1) / NW;
+  uint32_t off[PER];
+  __device__ void init(int64_t st, bool vlayout, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int pos = (wave + i * NW) * 64 + lane;
+      const int r = pos / (D / 8), sc = pos % (D / 8);
+      const int sw = vlayout ? v_swizzle<D>(r) : k_swizzle<D>(r);
+      off[i] = ((uint32_t)r * (uint32_t)st + (uint32_t)((sc ^ sw) * 8)) * 2u;
+    }
+  }
+  // the copies of a full tile whose row 0 starts at `base` (wave-uniform)
+  __device__ void issue(const uint16_t* base, uint32_t lds, int wave) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (wave + i * NW < CH) dma16_sbase(base, off[i], lds + (wave + i * NW) * 1024);
+  }
+};
+
 // Per-lane LDS byte offsets (from a tile's start) of the row reads of A
 // operands X[row = li][16 ks + 8 hg .. +8] from a "k" layout tile.
 template <int D>
@@ -198,6 +223,13 @@ struct DqCfg {
 };
 // `bid`: the workgroup's index in the dQ grid order; `smem`: DqCfg::SMEM bytes
 // of LDS, 1 KB aligned.
+//
+// As in the dK/dV kernel, the accumulators take one path through the loop
+// body (key tiles after a wave's rows skip the scores and accumulate zeros),
+// the mask is applied only on the diagonal tile, and D is folded into the dP
+// accumulator: the dA fragments are negated once
+// and the accumulator starts at D, so the MFMAs leave D - dP, P (D - dP) =
+// -dS, and dQ is negated when stored.
 template <int D, int DV>
 __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned char* smem) {
   constexpr int KS = D / 16, KSV = DV / 16, CB = D / 32;
@@ -206,6 +238,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
   using DmaV = TileDma<DV>;
   constexpr int TB = Dma::BYTES;
   constexpr int STAGE = DqCfg<D, DV>::STAGE;
+  static_assert(STAGE % (2 * DV) == 0 && TB % (2 * DV) == 0 && TB % (2 * D) == 0,
+                "tile bases leave a row's chunk bits free");
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -227,15 +261,29 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
 
   const uint16_t* kp = (const uint16_t*)a.k.p + b * a.k.sb + g * a.k.sh;
   const uint16_t* vp = (const uint16_t*)a.v.p + b * a.v.sb + g * a.v.sh;
+  TileCopy<D, kNW> ck, ckv;
+  TileCopy<DV, kNW> cv;
+  ck.init(a.k.st, false, wave, lane);
+  ckv.init(a.k.st, true, wave, lane);
+  cv.init(a.v.st, false, wave, lane);
   auto issue = [&](int kt, int stage) {
     const uint32_t st = lds0 + stage * STAGE;
-    Dma::issue(kp, a.k.st, kt * kBT, T, false, st, wave, lane);
-    Dma::issue(kp, a.k.st, kt * kBT, T, true, st + TB, wave, lane);
-    DmaV::issue(vp, a.v.st, kt * kBT, T, false, st + 2 * TB, wave, lane);
+    const int r0 = kt * kBT;
+    if (r0 + kBT > T) {  // ragged last tile
+      Dma::issue(kp, a.k.st, r0, T, false, st, wave, lane);
+      Dma::issue(kp, a.k.st, r0, T, true, st + TB, wave, lane);
+      DmaV::issue(vp, a.v.st, r0, T, false, st + 2 * TB, wave, lane);
+    } else {
+      const uint16_t* kr = kp + (int64_t)r0 * a.k.st;
+      const uint16_t* vr = vp + (int64_t)r0 * a.v.st;
+      ck.issue(kr, st, wave);
+      ckv.issue(kr, st + TB, wave);
+      cv.issue(vr, st + 2 * TB, wave);
+    }
   };
   issue(0, 0);
 
-  // B operands: Q^T and dA^T of this wave's rows; the row's lse and D
+  // B operands: Q^T and -dA^T of this wave's rows; the row's lse and D
   bf16x8 qf[KS], af[KSV];
   {
     const uint16_t* qr = (const uint16_t*)a.q.p + b * a.q.sb + (int64_t)row * a.q.st + h * a.q.sh;
@@ -252,16 +300,22 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) retire(qf[ks]);
 #pragma unroll
-  for (int ks = 0; ks < KSV; ++ks) retire(af[ks]);
+  for (int ks = 0; ks < KSV; ++ks) {
+    retire(af[ks]);
+    const uint4 u = as_u4(af[ks]);  // sign flip of every bf16 (exact)
+    af[ks] = as_bf16x8(make_uint4(u.x ^ 0x80008000u, u.y ^ 0x80008000u, u.z ^ 0x80008000u, u.w ^ 0x80008000u));
+  }
   retire(lse_r);
   retire(D_r);
-  uint32_t rb[KS], rbv[KSV];
-  row_read_bases<D>(li, hg, rb);
-  row_read_bases<DV>(li, hg, rbv);
+  // Row reads (K rows for S^T, V rows for dP^T): chunk (2 ks + hg) ^
+  // swizzle(li) = 2 ks ^ (hg ^ swizzle(li)), so the address is
+  // (tile base + lane part) ^ 32 ks.
+  const uint32_t kxs = (uint32_t)(li * (2 * D) + ((hg ^ k_swizzle<D>(li)) << 4));
+  const uint32_t vxs = (uint32_t)(li * (2 * DV) + ((hg ^ k_swizzle<DV>(li)) << 4));
   TrBases<D> tb;
   tb.init(lane);
   const float sl2 = a.sl2;
-  f32x16 acc[CB];
+  f32x16 acc[CB];  // -dQ^T
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -273,43 +327,83 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
     __syncthreads();  // tile kt visible; the other stage is free
     if (kt + 1 < nkt) issue(kt + 1, stage ^ 1);
     const int j0 = kt * kBT;
-    if (!active || j0 > i0w) continue;  // keys after every row of this wave
-    const bool diag = j0 == i0w;
     const uint32_t st = lds0 + stage * STAGE;
-    f32x16 s, dp;
+    uint32_t krow = st + kxs, vrow = st + 2 * TB + vxs;
+    uint32_t tbase[TrBases<D>::NV];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+    for (int v = 0; v < TrBases<D>::NV; ++v) tbase[v] = st + TB + tb.b[v];
+    asm volatile("" : "+v"(krow), "+v"(vrow));
 #pragma unroll
-    for (int ks = 0; ks < KM; ++ks) {
-      if (ks < KS) s = mfma32x32x16(lds_read16(st + rb[ks]), qf[ks], s);                // S^T = K Q^T
-      if (ks < KSV) dp = mfma32x32x16(lds_read16(st + 2 * TB + rbv[ks]), af[ks], dp);  // dP^T = V dA^T
+    for (int v = 0; v < TrBases<D>::NV; ++v) asm volatile("" : "+v"(tbase[v]));
+    // Key tiles entirely after this wave's rows (the last 3 at most) skip the
+    // scores and accumulate zeros: the accumulators then take one path.
+    bf16x8 dsk[2] = {};
+    if (j0 <= i0w) {
+      bf16x8 ka[KS], va[KSV];
+#pragma unroll
+      for (int ks = 0; ks < KM; ++ks) {
+        if (ks < KS) ka[ks] = lds_read16(krow ^ (32u * ks));
+        if (ks < KSV) va[ks] = lds_read16(vrow ^ (32u * ks));
+      }
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = D_r;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KM; ++ks) {
+        if (ks < KS) s = mfma32x32x16(ka[ks], qf[ks], s);     // S^T = K Q^T
+        if (ks < KSV) dp = mfma32x32x16(va[ks], af[ks], dp);  // D - dP^T = D + V (-dA)^T
+      }
+      constexpr int NMF = KS + KSV;
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < NMF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + 4 < NMF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      // lane: row li; register r: key j0 + 8(r>>2) + 4hg + (r&3)
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], sl2, -lse_r);
+      if (j0 == i0w) {  // the diagonal tile: keys after the row masked
+        int lim = li - 4 * hg;  // kept: key offset 4hg + c <= li
+        asm volatile("" : "+v"(lim));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + (r & 3);
+          x[r] = c <= lim ? x[r] : -INFINITY;
+        }
+      }
+      f32x8 e0, e1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float ds = __builtin_amdgcn_exp2f(x[r]) * dp[r];  // P (D - dP) = -dS
+        if (r < 8) e0[r] = ds; else e1[r - 8] = ds;
+      }
+      dsk[0] = cvt_bf16x8(e0);
+      dsk[1] = cvt_bf16x8(e1);
     }
-    // lane: row li; register r: key j0 + 8(r>>2) + 4hg + (r&3)
-    f32x8 e0, e1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * hg + (r & 3);
-      float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse_r));
-      if (diag && key > li) pr = 0.f;
-      const float ds = pr * (dp[r] - D_r);
-      if (r < 8) e0[r] = ds; else e1[r - 8] = ds;
-    }
-    const bf16x8 dsk[2] = {cvt_bf16x8(e0), cvt_bf16x8(e1)};
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) acc[cb] = mfma32x32x16(tb.read(st + TB, kk, cb), dsk[kk], acc[cb]);
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint32_t q = tbase[cb % TrBases<D>::NV] + 16 * kk * (2 * D) + cb * 64;
+        acc[cb] = mfma32x32x16(join_bf16x8(tr_read(q), tr_read(q + 8 * (2 * D))), dsk[kk], acc[cb]);
+      }
   }
   if (!active || row >= T) return;
   // dQ^T[c][row]: c = 32 cb + 8 (r>>2) + 4 hg + (r&3); dq = dS k / sqrt d
   uint16_t* dst = (uint16_t*)a.dq.p + b * a.dq.sb + (int64_t)row * a.dq.st + h * a.dq.sh;
+  const float sc = -a.scale;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       uint2 w;
-      w.x = pack_bf16x2(acc[cb][4 * g4 + 0] * a.scale, acc[cb][4 * g4 + 1] * a.scale);
-      w.y = pack_bf16x2(acc[cb][4 * g4 + 2] * a.scale, acc[cb][4 * g4 + 3] * a.scale);
+      w.x = pack_bf16x2(acc[cb][4 * g4 + 0] * sc, acc[cb][4 * g4 + 1] * sc);
+      w.y = pack_bf16x2(acc[cb][4 * g4 + 2] * sc, acc[cb][4 * g4 + 3] * sc);
       *(uint2*)(dst + 32 * cb + 8 * g4 + 4 * hg) = w;
     }
 }
@@ -465,10 +559,10 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
       cmp_h = 0;
       cmp_r0 -= kBT;
     }
-    // Tiles of rows before this wave's keys (at most 3 per head, and none
-    // of an inactive wave's results are stored) run like any other with
-    // every probability masked to 0: an early exit here would make the
-    // compiler keep two copies of the accumulators.
+    // Tiles of rows before this wave's keys (at most 3 per head, and every
+    // tile of an inactive wave) skip the scores but still run the
+    // accumulating MFMAs, with zero probabilities: leaving the accumulators
+    // untouched on some paths would make the compiler keep two copies.
     const uint32_t sb = lds0 + stage * STAGE;
     // Per-tile LDS bases, opaque to the compiler: every read below is one of
     // them plus an immediate offset (or, for the row reads, XOR a constant).
@@ -482,52 +576,67 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
 #pragma unroll
     for (int v = 0; v < TrBases<D>::NV; ++v) asm volatile("" : "+v"(tbase[v]));
     // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
-    f32x4 lq[4], dq4[4];
+    bf16x8 xk[2] = {};
+    if (i0 >= j0w) {
+      f32x4 lq[4], dq4[4];
+      if constexpr (KW) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      lq[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 32 * q4);
-      if constexpr (KW) dq4[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 128 + 32 * q4);
-    }
-    bf16x8 qa[KS], da[KS];
+        for (int q4 = 0; q4 < 4; ++q4)
+          dq4[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 128 + 32 * q4);
+      }
+      bf16x8 qa[KS], da[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qa[ks] = lds_read16(qrow ^ (32u * ks));
-      if constexpr (KW) da[ks] = lds_read16(arow ^ (32u * ks));
-    }
-    f32x16 s, dp;
+      for (int ks = 0; ks < KS; ++ks) {
+        qa[ks] = lds_read16(qrow ^ (32u * ks));
+        if constexpr (KW) da[ks] = lds_read16(arow ^ (32u * ks));
+      }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = 0.f;
-      if constexpr (KW) dp[r] = dq4[r >> 2][r & 3];  // D of the row
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = mfma32x32x16(qa[ks], kf[ks], s);                      // S = Q K^T
-      if constexpr (KW) dp = mfma32x32x16(da[ks], vf[ks], dp);  // D - dP = D + dA (-V)^T
-    }
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], sl2, -lq[r >> 2][r & 3]);
-    if (i0 <= j0w || i0 + kBT > T) {  // diagonal tile, rows before the keys, or rows past T
-      // row offset ro = 4 hg + c (c = 8(r>>2) + (r&3)) is kept if ro < T - i0
-      // and ro >= li (the key's offset) on the diagonal; nothing is kept
-      // before it
-      int lim = T - i0 - 4 * hg, dlo = i0 == j0w ? li - 4 * hg : (i0 < j0w ? 64 : -64);
-      asm volatile("" : "+v"(lim), "+v"(dlo));
+      for (int q4 = 0; q4 < 4; ++q4)
+        lq[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 32 * q4);
+      f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int c = 8 * (r >> 2) + (r & 3);
-        x[r] = (c < lim && c >= dlo) ? x[r] : -INFINITY;
+        s[r] = 0.f;
+        if constexpr (KW) dp[r] = dq4[r >> 2][r & 3];  // D of the row
       }
-    }
-    f32x8 e0, e1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float pr = __builtin_amdgcn_exp2f(x[r]);
-      if constexpr (KW) pr *= dp[r];  // P (D - dP) = -dS
-      if (r < 8) e0[r] = pr; else e1[r - 8] = pr;
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32x32x16(qa[ks], kf[ks], s);                      // S = Q K^T
+        if constexpr (KW) dp = mfma32x32x16(da[ks], vf[ks], dp);  // D - dP = D + dA (-V)^T
+      }
+      // Schedule: a batch of LDS reads first, then one MFMA per further read,
+      // so each operand is read several MFMAs before its use.
+      constexpr int NMF = KW ? 2 * KS : KS, NRD = KW ? 2 * KS + 8 : KS + 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
+#pragma unroll
+      for (int i = 0; i < NMF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], sl2, -lq[r >> 2][r & 3]);
+      if (i0 == j0w || i0 + kBT > T) {  // diagonal tile or rows past T
+        // row offset ro = 4 hg + c (c = 8(r>>2) + (r&3)) is kept if ro < T - i0
+        // and ro >= li (the key's offset) on the diagonal
+        int lim = T - i0 - 4 * hg, dlo = i0 == j0w ? li - 4 * hg : -64;
+        asm volatile("" : "+v"(lim), "+v"(dlo));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + (r & 3);
+          x[r] = (c < lim && c >= dlo) ? x[r] : -INFINITY;
+        }
+      }
+      f32x8 e0, e1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(x[r]);
+        if constexpr (KW) pr *= dp[r];  // P (D - dP) = -dS
+        if (r < 8) e0[r] = pr; else e1[r - 8] = pr;
+      }
+      xk[0] = cvt_bf16x8(e0);
+      xk[1] = cvt_bf16x8(e1);
     }
-    const bf16x8 xk[2] = {cvt_bf16x8(e0), cvt_bf16x8(e1)};
     // dV^T += dA^T P (dV wave), -dK^T += Q^T (-dS) (dK wave)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
