@@ -161,14 +161,6 @@ struct TileCopy {
   }
 };
 
-// Per-lane LDS byte offsets (from a tile's start) of the row reads of A
-// operands X[row = li][16 ks + 8 hg .. +8] from a "k" layout tile.
-template <int D>
-__device__ __forceinline__ void row_read_bases(int li, int hg, uint32_t* base) {
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) base[ks] = li * (D * 2) + (((2 * ks + hg) ^ k_swizzle<D>(li)) << 4);
-}
-
 // Per-lane LDS byte offsets of the transpose reads giving A operands
 // X^T[c][rows of k-chunk kk] from a "v" layout tile (rows in the order the
 // P-like B operands hold them: 16kk + 4hg + 0..3, then + 8).
@@ -183,10 +175,6 @@ struct TrBases {
     const int x = v_swizzle<D>(vr);
 #pragma unroll
     for (int v = 0; v < NV; ++v) b[v] = vr * (D * 2) + (((4 * v + cl) ^ x) - 4 * v) * 16 + (l16 & 1) * 8;
-  }
-  __device__ bf16x8 read(uint32_t tile, int kk, int cb) const {
-    const uint32_t q = tile + b[cb % NV] + 16 * kk * (D * 2) + cb * 64;
-    return join_bf16x8(tr_read(q), tr_read(q + 8 * (D * 2)));
   }
 };
 
@@ -846,10 +834,16 @@ __device__ __forceinline__ void bwd_v1_lam_body(const V1BwdArgs& a, float* part)
 // dK of one map: workgroup (b, h, map, 32 kNW keys), wave w owns keys
 // J0 + 32 w and loops over the row tiles at or after them (rows descending).
 // S = Q K^T and dP = dA V^T with K / V fragments of its keys in registers,
-// dS = P (dP - D), dK^T += Q^T dS with transpose reads of the Q tile.
+// dS = P (dP - D), dK^T += Q^T dS with transpose reads of the Q tile.  As in
+// the V2 kernels: the V fragments are negated once and the dP accumulator
+// starts at D (so the MFMAs leave D - dP and the accumulator holds -dK^T),
+// masks apply only on the diagonal and ragged tiles, tiles of rows before
+// the wave's keys accumulate zeros, and copies use per-lane offsets computed
+// once.
 template <int D>
 struct V1DkCfg {
-  static constexpr int STAGE = 2 * TileDma<D>::BYTES + TileDma<2 * D>::BYTES + 256;  // [Q "k" | Q "v" | dA "k" | lse, D]
+  // [Q "k" | Q "v" | dA "k" | lse, D], the stage a multiple of a dA row (2 DV bytes)
+  static constexpr int STAGE = 2 * TileDma<D>::BYTES + TileDma<2 * D>::BYTES + 512;
   static constexpr int SMEM = 2 * STAGE;
 };
 template <int D>
@@ -860,6 +854,7 @@ __device__ __forceinline__ void bwd_v1_dk_body(const V1BwdArgs& a, int bid, unsi
   using DmaV = TileDma<DV>;
   constexpr int TB = Dma::BYTES, TBV = DmaV::BYTES;
   constexpr int STAGE = V1DkCfg<D>::STAGE;
+  static_assert(STAGE % (2 * DV) == 0 && TB % (2 * DV) == 0, "tile bases leave a row's chunk bits free");
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -879,7 +874,7 @@ __device__ __forceinline__ void bwd_v1_dk_body(const V1BwdArgs& a, int bid, unsi
 
   const TIn& tq = a.q[m];
   const TIn& tk = a.k[m];
-  bf16x8 kf[KS], vf[KSV];
+  bf16x8 kf[KS], vf[KSV];  // K^T and -V^T of this wave's keys
   {
     const uint16_t* kr = (const uint16_t*)tk.p + b * tk.sb + (int64_t)key * tk.st + h * tk.sh;
     const uint16_t* vr = (const uint16_t*)a.v.p + b * a.v.sb + (int64_t)key * a.v.st + h * a.v.sh;
@@ -892,36 +887,50 @@ __device__ __forceinline__ void bwd_v1_dk_body(const V1BwdArgs& a, int bid, unsi
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) retire(kf[ks]);
 #pragma unroll
-    for (int ks = 0; ks < KSV; ++ks) retire(vf[ks]);
+    for (int ks = 0; ks < KSV; ++ks) {
+      retire(vf[ks]);
+      const uint4 u = as_u4(vf[ks]);  // sign flip of every bf16 (exact)
+      vf[ks] = as_bf16x8(make_uint4(u.x ^ 0x80008000u, u.y ^ 0x80008000u, u.z ^ 0x80008000u, u.w ^ 0x80008000u));
+    }
   }
   const uint16_t* qp = (const uint16_t*)tq.p + b * tq.sb + h * tq.sh;
   const uint16_t* ap = a.dA[m] + ((int64_t)b * T * a.H + h) * DV;
   const float* lsw = a.lsew[m] + ((int64_t)b * a.H + h) * a.Tp;
   const float* dw = a.Dw[m] + ((int64_t)b * a.H + h) * a.Tp;
+  const int64_t ast = (int64_t)a.H * DV;
+  TileCopy<D, kNW> cq, cqv;
+  TileCopy<DV, kNW> ca;
+  cq.init(tq.st, false, wave, lane);
+  cqv.init(tq.st, true, wave, lane);
+  ca.init(ast, false, wave, lane);
   auto issue = [&](int it, int stage) {
     const int i0 = it_row0(it);
     const uint32_t st = lds0 + stage * STAGE;
-    Dma::issue(qp, tq.st, i0, T, false, st, wave, lane);
-    Dma::issue(qp, tq.st, i0, T, true, st + TB, wave, lane);
-    DmaV::issue(ap, (int64_t)a.H * DV, i0, T, false, st + 2 * TB, wave, lane);
+    if (i0 + kBT > T) {  // ragged last row tile
+      Dma::issue(qp, tq.st, i0, T, false, st, wave, lane);
+      Dma::issue(qp, tq.st, i0, T, true, st + TB, wave, lane);
+      DmaV::issue(ap, ast, i0, T, false, st + 2 * TB, wave, lane);
+    } else {
+      const uint16_t* qr = qp + (int64_t)i0 * tq.st;
+      cq.issue(qr, st, wave);
+      cqv.issue(qr, st + TB, wave);
+      ca.issue(ap + (int64_t)i0 * ast, st + 2 * TB, wave);
+    }
     // the 32 rows' lse and D (padded arrays: always in bounds), 8 lanes x 16 B each
     if (wave == kNW - 2 && lane < 8) dma16_sbase(lsw + i0, lane * 16, st + 2 * TB + TBV);
     if (wave == kNW - 1 && lane < 8) dma16_sbase(dw + i0, lane * 16, st + 2 * TB + TBV + 128);
   };
   issue(0, 0);
 
-  // row reads of the 2d-wide dA tile: chunk (2ks + hg) ^ (li & 15) of a row,
-  // so k-step ks + 8 reads 256 bytes after k-step ks (an immediate offset)
-  static_assert(DV == 128 || DV == 256, "dA row reads");
-  uint32_t rb[KS], rbv[8];
-  row_read_bases<D>(li, hg, rb);
-  row_read_bases<128>(li, hg, rbv);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) rbv[i] += li * (DV * 2 - 256);  // row stride DV*2 bytes
+  // Row reads: chunk (2 ks + hg) ^ swizzle(li) = 2 ks ^ (hg ^ swizzle(li)),
+  // so the address is (tile base + lane part) ^ 32 ks (Q rows of 2D bytes, dA
+  // rows of 2 DV bytes).
+  const uint32_t qxs = (uint32_t)(li * (2 * D) + ((hg ^ k_swizzle<D>(li)) << 4));
+  const uint32_t axs = (uint32_t)(li * (2 * DV) + ((hg ^ k_swizzle<DV>(li)) << 4));
   TrBases<D> tb;
   tb.init(lane);
   const float sl2 = a.sl2;
-  f32x16 acc[CB];  // dK^T [c][key]
+  f32x16 acc[CB];  // -dK^T [c][key]
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -933,61 +942,102 @@ __device__ __forceinline__ void bwd_v1_dk_body(const V1BwdArgs& a, int bid, unsi
     __syncthreads();  // tile it visible; the other stage is free
     if (it + 1 < nit) issue(it + 1, stage ^ 1);
     const int i0 = it_row0(it);
-    if (!active || i0 < j0w) continue;  // rows before this wave's keys
-    const bool diag = i0 == j0w;
     const uint32_t st = lds0 + stage * STAGE;
-    f32x16 s, dp;
+    uint32_t qrow = st + qxs, arow = st + 2 * TB + axs, rowst = st + 2 * TB + TBV + 16 * hg;
+    uint32_t tbase[TrBases<D>::NV];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+    for (int v = 0; v < TrBases<D>::NV; ++v) tbase[v] = st + TB + tb.b[v];
+    asm volatile("" : "+v"(qrow), "+v"(arow), "+v"(rowst));
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s = mfma32x32x16(lds_read16(st + rb[ks]), kf[ks], s);  // S = Q K^T
+    for (int v = 0; v < TrBases<D>::NV; ++v) asm volatile("" : "+v"(tbase[v]));
+    bf16x8 xk[2] = {};
+    if (i0 >= j0w) {  // (else: rows before this wave's keys, or an inactive wave)
+      // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
+      f32x4 lq[4], dq4[4];
 #pragma unroll
-    for (int ks = 0; ks < KSV; ++ks)
-      dp = mfma32x32x16(lds_read16(st + 2 * TB + rbv[ks & 7] + (ks >> 3) * 256), vf[ks], dp);  // dP = dA V^T
-    // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
-    f32x8 e0, e1;
+      for (int q4 = 0; q4 < 4; ++q4)
+        dq4[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 128 + 32 * q4);
+      bf16x8 qa[KS], da[KSV];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(st + 2 * TB + TBV + (8 * q4 + 4 * hg) * 4);
-      const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(st + 2 * TB + TBV + 128 + (8 * q4 + 4 * hg) * 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * q4 + j;
-        const int rw = i0 + 8 * q4 + 4 * hg + j;
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[j]));
-        if (rw >= T || (diag && li > rw - i0)) pr = 0.f;
-        const float x = pr * (dp[r] - d4[j]);
-        if (r < 8) e0[r] = x; else e1[r - 8] = x;
+      for (int ks = 0; ks < KSV; ++ks) {
+        if (ks < KS) qa[ks] = lds_read16(qrow ^ (32u * ks));
+        da[ks] = lds_read16(arow ^ (32u * ks));
       }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        lq[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 32 * q4);
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = dq4[r >> 2][r & 3];  // D of the row
+      }
+#pragma unroll
+      for (int ks = 0; ks < KSV; ++ks) {
+        if (ks < KS) s = mfma32x32x16(qa[ks], kf[ks], s);  // S = Q K^T
+        dp = mfma32x32x16(da[ks], vf[ks], dp);            // D - dP = D + dA (-V)^T
+      }
+      constexpr int NMF = KS + KSV, NRD = KS + KSV + 8;
+      __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
+#pragma unroll
+      for (int i = 0; i < NMF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], sl2, -lq[r >> 2][r & 3]);
+      if (i0 == j0w || i0 + kBT > T) {  // diagonal tile or rows past T
+        int lim = T - i0 - 4 * hg, dlo = i0 == j0w ? li - 4 * hg : -64;
+        asm volatile("" : "+v"(lim), "+v"(dlo));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + (r & 3);
+          x[r] = (c < lim && c >= dlo) ? x[r] : -INFINITY;
+        }
+      }
+      f32x8 e0, e1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(x[r]) * dp[r];  // P (D - dP) = -dS
+        if (r < 8) e0[r] = pr; else e1[r - 8] = pr;
+      }
+      xk[0] = cvt_bf16x8(e0);
+      xk[1] = cvt_bf16x8(e1);
     }
-    const bf16x8 xk[2] = {cvt_bf16x8(e0), cvt_bf16x8(e1)};
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) acc[cb] = mfma32x32x16(tb.read(st + TB, kk, cb), xk[kk], acc[cb]);
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint32_t q = tbase[cb % TrBases<D>::NV] + 16 * kk * (2 * D) + cb * 64;
+        acc[cb] = mfma32x32x16(join_bf16x8(tr_read(q), tr_read(q + 8 * (2 * D))), xk[kk], acc[cb]);
+      }
   }
   if (!active || key >= T) return;
   const TOut& o = a.dk[m];
   uint16_t* dst = (uint16_t*)o.p + b * o.sb + (int64_t)key * o.st + h * o.sh;
+  const float sc = -a.scale;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       uint2 w;
-      w.x = pack_bf16x2(acc[cb][4 * g4 + 0] * a.scale, acc[cb][4 * g4 + 1] * a.scale);
-      w.y = pack_bf16x2(acc[cb][4 * g4 + 2] * a.scale, acc[cb][4 * g4 + 3] * a.scale);
+      w.x = pack_bf16x2(acc[cb][4 * g4 + 0] * sc, acc[cb][4 * g4 + 1] * sc);
+      w.y = pack_bf16x2(acc[cb][4 * g4 + 2] * sc, acc[cb][4 * g4 + 3] * sc);
       *(uint2*)(dst + 32 * cb + 8 * g4 + 4 * hg) = w;
     }
 }
 
 // dV over both maps: workgroup (b, h, 32 kNW keys), wave w owns keys
-// J0 + 32 w; iterations (row tile, map), rows descending, map 1 then map 2
-// of each tile (the stage index is the map).  S_m = Q_m K_m^T with K_1 / K_2
-// fragments of its keys in registers, dV^T += dA_m^T P_m with transpose
-// reads of the dA_m tile.
+// J0 + 32 w; iterations (map, row tile): all row tiles of map 1, then of
+// map 2, rows descending, so only one map's K fragments are held at a time
+// (at d = 128 the 2d-wide dV^T accumulators take 128 registers).  S_m =
+// Q_m K_m^T with the K_m fragments of its keys in registers, dV^T += dA_m^T
+// P_m with transpose reads of the dA_m tile.  Same loop structure as dK.
 template <int D>
 struct V1DvCfg {
-  static constexpr int STAGE = TileDma<D>::BYTES + TileDma<2 * D>::BYTES + 128;  // [Q_m "k" | dA_m "v" | lse]
+  // [Q_m "k" | dA_m "v" | lse], the stage a multiple of a Q row (2D bytes)
+  static constexpr int STAGE = TileDma<D>::BYTES + TileDma<2 * D>::BYTES + 256;
   static constexpr int SMEM = 2 * STAGE;
 };
 template <int D>
@@ -998,6 +1048,7 @@ __device__ __forceinline__ void bwd_v1_dv_body(const V1BwdArgs& a, int bid, unsi
   using DmaV = TileDma<DV>;
   constexpr int TB = Dma::BYTES, TBV = DmaV::BYTES;
   constexpr int STAGE = V1DvCfg<D>::STAGE;
+  static_assert(STAGE % (2 * D) == 0, "tile bases leave a row's chunk bits free");
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -1011,35 +1062,33 @@ __device__ __forceinline__ void bwd_v1_dv_body(const V1BwdArgs& a, int bid, unsi
   const int key = j0w + li;
   const int nrt = (T + kBT - 1) / kBT;
   const int rt0 = J0 / kBT;
-  const int nit = 2 * (nrt - rt0);  // (row tile, map); even
-  auto it_row0 = [&](int it) { return (nrt - 1 - (it >> 1)) * kBT; };
+  const int nr = nrt - rt0;   // row tiles per map
+  const int nit = 2 * nr;     // (map, row tile)
+  auto it_row0 = [&](int it) { return (nrt - 1 - (it < nr ? it : it - nr)) * kBT; };
 
-  bf16x8 kf[2][KS];
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
+  bf16x8 kf[KS];  // K_m^T of this wave's keys, for the map being processed
+  auto load_k = [&](int m) {
     const uint16_t* kr = (const uint16_t*)a.k[m].p + b * a.k[m].sb + (int64_t)key * a.k[m].st + h * a.k[m].sh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      kf[m][ks] = as_bf16x8(key < T ? *(const uint4*)(kr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
-  }
+      kf[ks] = as_bf16x8(key < T ? *(const uint4*)(kr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) retire(kf[m][ks]);
-  auto issue = [&](int it) {  // stage = map = it & 1
-    const int m = it & 1, i0 = it_row0(it);
+    for (int ks = 0; ks < KS; ++ks) retire(kf[ks]);
+  };
+  load_k(0);
+  auto issue = [&](int it, int stage) {
+    const int m = it < nr ? 0 : 1, i0 = it_row0(it);
     const uint16_t* qp = (const uint16_t*)a.q[m].p + b * a.q[m].sb + h * a.q[m].sh;
     const uint16_t* ap = a.dA[m] + ((int64_t)b * T * a.H + h) * DV;
-    const uint32_t st = lds0 + m * STAGE;
+    const uint32_t st = lds0 + stage * STAGE;
     Dma::issue(qp, a.q[m].st, i0, T, false, st, wave, lane);
     DmaV::issue(ap, (int64_t)a.H * DV, i0, T, true, st + TB, wave, lane);
     if (wave == kNW - 1 && lane < 8)
       dma16_sbase(a.lsew[m] + ((int64_t)b * a.H + h) * a.Tp + i0, lane * 16, st + TB + TBV);
   };
-  issue(0);
+  issue(0, 0);
 
-  uint32_t rb[KS];
-  row_read_bases<D>(li, hg, rb);
+  const uint32_t qxs = (uint32_t)(li * (2 * D) + ((hg ^ k_swizzle<D>(li)) << 4));
   TrBases<DV> tb;
   tb.init(lane);
   const float sl2 = a.sl2;
@@ -1049,42 +1098,70 @@ __device__ __forceinline__ void bwd_v1_dv_body(const V1BwdArgs& a, int bid, unsi
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
-  auto tile_step = [&](int it, auto mc) {
-    constexpr int M = decltype(mc)::value;
+  for (int it = 0; it < nit; ++it) {
+    const int stage = it & 1;
+    if (it == nr) load_k(1);  // (its wait also retires the copies in flight: once per call)
     wait_copies();
     __syncthreads();  // tile it visible; the other stage is free
-    if (it + 1 < nit) issue(it + 1);
+    if (it + 1 < nit) issue(it + 1, stage ^ 1);
     const int i0 = it_row0(it);
-    if (!active || i0 < j0w) return;  // rows before this wave's keys
-    const bool diag = i0 == j0w;
-    const uint32_t st = lds0 + M * STAGE;
-    f32x16 s;
+    const uint32_t st = lds0 + stage * STAGE;
+    uint32_t qrow = st + qxs, rowst = st + TB + TBV + 16 * hg;
+    uint32_t tbase[TrBases<DV>::NV];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    for (int v = 0; v < TrBases<DV>::NV; ++v) tbase[v] = st + TB + tb.b[v];
+    asm volatile("" : "+v"(qrow), "+v"(rowst));
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s = mfma32x32x16(lds_read16(st + rb[ks]), kf[M][ks], s);  // S = Q K^T
-    f32x8 e0, e1;
+    for (int v = 0; v < TrBases<DV>::NV; ++v) asm volatile("" : "+v"(tbase[v]));
+    bf16x8 xk[2] = {};
+    if (i0 >= j0w) {  // (else: rows before this wave's keys, or an inactive wave)
+      bf16x8 qa[KS];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(st + TB + TBV + (8 * q4 + 4 * hg) * 4);
+      for (int ks = 0; ks < KS; ++ks) qa[ks] = lds_read16(qrow ^ (32u * ks));
+      f32x4 lq[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * q4 + j;
-        const int rw = i0 + 8 * q4 + 4 * hg + j;
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -l4[j]));
-        if (rw >= T || (diag && li > rw - i0)) pr = 0.f;
+      for (int q4 = 0; q4 < 4; ++q4)
+        lq[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 32 * q4);
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s = mfma32x32x16(qa[ks], kf[ks], s);  // S = Q K^T
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], sl2, -lq[r >> 2][r & 3]);
+      if (i0 == j0w || i0 + kBT > T) {  // diagonal tile or rows past T
+        int lim = T - i0 - 4 * hg, dlo = i0 == j0w ? li - 4 * hg : -64;
+        asm volatile("" : "+v"(lim), "+v"(dlo));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + (r & 3);
+          x[r] = (c < lim && c >= dlo) ? x[r] : -INFINITY;
+        }
+      }
+      f32x8 e0, e1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(x[r]);
         if (r < 8) e0[r] = pr; else e1[r - 8] = pr;
       }
+      xk[0] = cvt_bf16x8(e0);
+      xk[1] = cvt_bf16x8(e1);
     }
-    const bf16x8 xk[2] = {cvt_bf16x8(e0), cvt_bf16x8(e1)};
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int cb = 0; cb < CBV; ++cb) acc[cb] = mfma32x32x16(tb.read(st + TB, kk, cb), xk[kk], acc[cb]);
-  };
-  for (int it = 0; it < nit; it += 2) {
-    tile_step(it, std::integral_constant<int, 0>{});
-    tile_step(it + 1, std::integral_constant<int, 1>{});
+      for (int cb = 0; cb < CBV; ++cb) {
+        const uint32_t q = tbase[cb % TrBases<DV>::NV] + 16 * kk * (2 * DV) + cb * 64;
+        acc[cb] = mfma32x32x16(join_bf16x8(tr_read(q), tr_read(q + 8 * (2 * DV))), xk[kk], acc[cb]);
+      }
   }
   if (!active || key >= T) return;
   uint16_t* dst = (uint16_t*)a.dv.p + b * a.dv.sb + (int64_t)key * a.dv.st + h * a.dv.sh;
