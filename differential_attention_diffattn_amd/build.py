@@ -24,11 +24,16 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
+# Per-source additions.  Decode: MFMA results in VGPRs.  With one wave per
+# SIMD allowed, the compiler otherwise picks the AGPR form for the copy-path
+# kernels and moves the 64 output accumulators between AGPRs and VGPRs on
+# every step.
+EXTRA = {"decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def _compile(src: str) -> Path:
     obj = BUILD_DIR / (Path(src).name + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", str(CSRC / src), "-o", str(obj)]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", str(CSRC / src), "-o", str(obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

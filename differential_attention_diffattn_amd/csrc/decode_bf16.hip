@@ -66,7 +66,7 @@ __device__ __forceinline__ void lds_fence() {
 }
 
 template <int D, bool PAGED, int NCB>
-__global__ void __launch_bounds__(kWaves * 64, (PAGED || NCB > 1) ? 1 : 3) decode_split_kernel(const DecodeArgs a) {
+__global__ void __launch_bounds__(kWaves * 64, (PAGED || NCB > 1) ? 2 : 3) decode_split_kernel(const DecodeArgs a) {
   constexpr int W = kWaves;  // waves per workgroup
   constexpr int KS = D / 32;   // k-steps of the score MFMA
   constexpr int CB = D / 16;   // 16-wide column blocks of O^T
@@ -213,18 +213,51 @@ __global__ void __launch_bounds__(kWaves * 64, (PAGED || NCB > 1) ? 1 : 3) decod
   // ---- copies: this wave's block -> its LDS slot (global_load_lds) ----------
   // Copy i of a tensor moves rows i*RPI .. i*RPI + RPI-1; the lane moves
   // source chunk (lane % CPR) ^ swizzle(row) of row i*RPI + lane / CPR into
-  // slot chunk lane % CPR.  Rows past the sequence's end repeat its last row
-  // (finite data; their scores are masked to -inf below).
+  // slot chunk lane % CPR.  A block is two 16-row halves (each in one page of
+  // a paged cache); copy i = h * CPH + j of half h moves rows 16 h + j*RPI ..,
+  // and its per-lane source offset from the half's first row depends on j
+  // only (the swizzle depends on the row mod 16), so CPH offsets per tensor
+  // are computed once.  Rows past the sequence's end repeat its last row
+  // (finite data; their scores are masked to -inf below): a block holding
+  // them takes the per-copy path.
+  constexpr int CPH = 16 / RPI;  // copies per 16-row half
   const int r_in = lane / CPR;
   uint32_t choff[NI];  // the lane's chunk byte offset in copy i (same for K and V)
 #pragma unroll
   for (int i = 0; i < NI; ++i) choff[i] = (uint32_t)(((lane % CPR) ^ dec_swizzle<D>(i * RPI + r_in)) * 16);
   const uint32_t krow = (uint32_t)(r_in * kst * 2), vrow = (uint32_t)(r_in * vst * 2);
+  uint32_t kho[CPH], vho[CPH];  // full half: offsets of its copies from the half's first row
+#pragma unroll
+  for (int j = 0; j < CPH; ++j) {
+    kho[j] = krow + (uint32_t)(j * RPI * kst * 2) + choff[j];
+    vho[j] = vrow + (uint32_t)(j * RPI * vst * 2) + choff[j];
+  }
   const uint32_t slot0 = lds_base + wv * (NST * SLOT);
   auto issue = [&](int n, int slot) {
     const int blk = blk0 + kBlk * W * n;
     const uint32_t dst = slot0 + slot * SLOT;
-    const bool full = blk + kBlk <= L;  // uniform
+    if (blk + kBlk <= L) {  // full block (uniform)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint16_t *kb, *vb;  // the half's first row
+        if constexpr (PAGED) {
+          const int raw = __builtin_amdgcn_readlane(ent, 2 * n + h);
+          const int pg = min(max(raw, 0), a.num_pages - 1);
+          const int prow = (blk + 16 * h) & pmask;
+          kb = kbase + (int64_t)pg * a.k.sb + (int64_t)prow * kst;
+          vb = vbase + (int64_t)pg * a.v.sb + (int64_t)prow * vst;
+        } else {
+          kb = kbase + (int64_t)(blk + 16 * h) * kst;
+          vb = vbase + (int64_t)(blk + 16 * h) * vst;
+        }
+#pragma unroll
+        for (int j = 0; j < CPH; ++j) {
+          dma16_sbase(kb, kho[j], dst + (h * CPH + j) * 1024);
+          dma16_sbase(vb, vho[j], dst + TBYTES + (h * CPH + j) * 1024);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int sub = (i * RPI) / 16;
@@ -241,40 +274,29 @@ __global__ void __launch_bounds__(kWaves * 64, (PAGED || NCB > 1) ? 1 : 3) decod
         kb = (int64_t)blk * kst;
         vb = (int64_t)blk * vst;
       }
-      uint32_t ko, vo;
-      if (full) {  // rows anchor + (i*RPI - 16 sub) + r_in
-        const int base_row = i * RPI - (PAGED ? 16 * sub : 0);
-        kb += (int64_t)base_row * kst;
-        vb += (int64_t)base_row * vst;
-        ko = krow + choff[i];
-        vo = vrow + choff[i];
-      } else {
-        const int tok = min(blk + i * RPI + r_in, L - 1);
-        ko = (uint32_t)((tok - anchor) * kst * 2) + choff[i];
-        vo = (uint32_t)((tok - anchor) * vst * 2) + choff[i];
-      }
+      const int tok = min(blk + i * RPI + r_in, L - 1);
+      const uint32_t ko = (uint32_t)((tok - anchor) * kst * 2) + choff[i];
+      const uint32_t vo = (uint32_t)((tok - anchor) * vst * 2) + choff[i];
       dma16_sbase(kbase + kb, ko, dst + i * 1024);
       dma16_sbase(vbase + vb, vo, dst + TBYTES + i * 1024);
     }
   };
 
-  // per-lane LDS read offsets within a slot
-  //   K operand of S = K q^T: lane (c16, kg) reads row 16 sub + c16, chunk 4 ks + kg
+  // Per-lane LDS read addresses within a slot, as a base XOR a constant:
+  //   K operand of S = K q^T: lane (c16, kg) reads row 16 sub + c16, chunk
+  //   (4 ks + kg) ^ swizzle(c16) = 4 ks ^ (kg ^ swizzle(c16)): base kxb
+  //   (sub 0) XOR 64 ks, + 16 RB for sub 1 (the swizzle depends on the row
+  //   mod 16, and rows are RB >= 128 bytes: the XOR stays inside a row).
   //   V^T operand (transpose read): lane (L = lane & 15, kg) points at row
-  //   4 kg + (L >> 2) (+ 16 for the second read), channels 16 cb + 4 (L & 3);
-  //   it receives channel 16 cb + L of tokens 4 kg .. 4 kg + 3 (16 + ...)
-  uint32_t koff[2][KS];
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      koff[sub][ks] = (uint32_t)((16 * sub + c16) * RB + (((4 * ks + kg) ^ dec_swizzle<D>(16 * sub + c16)) << 4));
-  uint32_t voff[CB];
+  //   vr = 4 kg + (L >> 2) (+ 16 for the second read), chunk (2 cb + b0) ^
+  //   swizzle(vr) = 2 cb ^ (b0 ^ swizzle(vr)), b0 = (L & 3) >> 1, plus 8 bytes
+  //   for odd L: base vxb XOR 32 cb; it receives channel 16 cb + L of tokens
+  //   4 kg .. 4 kg + 3 (16 + ...)
+  const uint32_t kxb = (uint32_t)(c16 * RB + ((kg ^ dec_swizzle<D>(c16)) << 4));
+  uint32_t vxb;
   {
     const int l16 = lane & 15, vr = 4 * kg + (l16 >> 2);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-      voff[cb] = (uint32_t)(TBYTES + vr * RB + (((2 * cb + ((l16 & 3) >> 1)) ^ dec_swizzle<D>(vr)) << 4) + 8 * (l16 & 1));
+    vxb = (uint32_t)(TBYTES + vr * RB + ((((l16 & 3) >> 1) ^ dec_swizzle<D>(vr)) << 4) + 8 * (l16 & 1));
   }
 
   const float sl2 = a.sl2;
@@ -292,15 +314,24 @@ __global__ void __launch_bounds__(kWaves * 64, (PAGED || NCB > 1) ? 1 : 3) decod
   // c16, kg) holds tokens blk + 16 sub + 4 kg + r): mask, lazy rescale,
   // probabilities as the bf16 B operand of P.V (slot t: token 4 kg + t for
   // t < 4, 16 + 4 kg + t - 4 for t >= 4).
+  // Copy path: only a block reaching the first masked entry (past the
+  // sequence's end, or after a new token's own position) applies the mask
+  // (a uniform test).  Register path: every block applies it with selects
+  // (a branch there costs the loads' schedule: measured 6% slower).
+  const int mask_from = L - NQ + 1;
   auto softmax_block = [&](f32x4* sc, int blk, int n2) -> bf16x8 {
+    if (!DMA || blk + kBlk > mask_from) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (blk + 16 * sub + 4 * kg + r >= lim[n2]) sc[sub][r] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (blk + 16 * sub + 4 * kg + r >= lim[n2]) sc[sub][r] = -INFINITY;
-        mx = fmaxf(mx, sc[sub][r]);
-      }
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[sub][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     // -inf when the whole block is masked for this column (a later query
@@ -404,6 +435,10 @@ __global__ void __launch_bounds__(kWaves * 64, (PAGED || NCB > 1) ? 1 : 3) decod
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     const uint32_t sb = slot0 + cur * SLOT;
+    // (opaque to the compiler: otherwise it keeps base + constant for every
+    // read in a register of its own)
+    uint32_t kb0 = sb + kxb, vb0 = sb + vxb;
+    asm volatile("" : "+v"(kb0), "+v"(vb0));
 
     // ---- scores S[tok][col], softmax state per column ----
     bf16x8 pk[NCB];  // slot t: token 4kg+t (t<4), 16+4kg+t-4 (t>=4)
@@ -411,20 +446,23 @@ __global__ void __launch_bounds__(kWaves * 64, (PAGED || NCB > 1) ? 1 : 3) decod
 #pragma unroll
     for (int n2 = 0; n2 < NCB; ++n2) sc[n2][0] = sc[n2][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t ka_addr = kb0 ^ (64u * ks);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ka = lds_read16(sb + koff[sub][ks]);
+      for (int sub = 0; sub < 2; ++sub) {
+        const bf16x8 ka = lds_read16(ka_addr + sub * 16 * RB);
 #pragma unroll
         for (int n2 = 0; n2 < NCB; ++n2) sc[n2][sub] = mfma16x16x32(ka, qf[n2][ks], sc[n2][sub]);
       }
+    }
 #pragma unroll
     for (int n2 = 0; n2 < NCB; ++n2) pk[n2] = softmax_block(sc[n2], blk, n2);
 
     // ---- O^T[c][col] += V^T[c][tok] P^T[tok][col] (V^T by transpose reads) ----
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const bf16x8 va = join_bf16x8(tr_read(sb + voff[cb]), tr_read(sb + voff[cb] + 16 * RB));
+      const uint32_t va_addr = vb0 ^ (32u * cb);
+      const bf16x8 va = join_bf16x8(tr_read(va_addr), tr_read(va_addr + 16 * RB));
 #pragma unroll
       for (int n2 = 0; n2 < NCB; ++n2) o[n2][cb] = mfma16x16x32(va, pk[n2], o[n2][cb]);
     }
