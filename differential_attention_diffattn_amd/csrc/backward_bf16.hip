@@ -404,20 +404,25 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
 
 // ---- dK, dV ------------------------------------------------------------------
 // Workgroup: (b, kv head g, 32 kNW keys), 2 kNW waves: waves m and m + kNW
-// own keys j0 + 32 m, the first accumulating dV, the second dK, and both loop
-// over the group's query heads and the row tiles at or after their keys.
-// (Splitting dV and dK over two waves keeps each under 256 registers, so two
-// waves share a SIMD; both rebuild P, only the dK wave needs dP.)
-//
-// Per (row tile, head) iteration a wave issues its LDS operand reads as one
-// batch ahead of the MFMAs that use them, and keeps scalar and vector
-// bookkeeping out of the loop: copy addresses advance by running (head, row)
-// counters from per-lane offsets computed once; the causal and ragged-tail
-// masks are applied only on the tiles that need them (a uniform branch); and
-// no VALU op subtracts D: the dK wave's dP accumulator starts from the
-// tile's D values (read from LDS straight into it) and its V fragments are
-// negated once, so the MFMAs leave D - dP, P (D - dP) = -dS, and the dK
-// accumulator is negated when stored.
+// own keys j0 + 32 m (on one SIMD: wave w runs on SIMD w mod 4) and loop over
+// the group's query heads and the row tiles at or after their keys, two
+// tiles per period:
+//   phase 1: the P wave (m) computes S = Q K^T and P for both tiles and
+//            writes P (bf16, the values its own dV product uses) to LDS;
+//            the dS wave (m + kNW) computes D - dP = D + dA (-V)^T for both
+//            tiles (its accumulators start at the tiles' D rows, read from
+//            LDS straight into them, and its V fragments are negated once);
+//   barrier;
+//   phase 2: the P wave accumulates dV^T += dA^T P; the dS wave reads P,
+//            forms P (D - dP) = -dS and accumulates -dK^T += Q^T (-dS).
+// Each product is computed once (S by the P wave only), and both waves of a
+// SIMD issue 16 MFMAs per tile.  A second barrier per period (before the
+// next period's P is written) is the stage barrier the copy ring needs
+// anyway.  Masks (diagonal tile, rows past T) are applied only where needed;
+// tiles of rows before the wave's keys skip the scores and accumulate zeros,
+// so the accumulators take one path through the loop.  Copy addresses
+// advance by running (head, row) counters from per-lane offsets computed
+// once.
 template <int D>
 __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int NW = 2 * kNW;
@@ -429,17 +434,16 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   static_assert(CH <= NW, "a wave copies at most one 1 KB chunk of a tensor tile");
   constexpr int STAGE = 4 * TB + 256;  // [Q "k" | Q "v" | dA "k" | dA "v" | lse, D of the 32 rows]
   static_assert(STAGE % 256 == 0 && TB % 256 == 0, "tile bases leave the row's chunk bits free");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * STAGE];  // two pairs of stages
+  constexpr int PSLOT = 2 * 1024;      // one tile's P of one P wave: 64 lanes x 2 x 16 bytes
+  constexpr int PBASE = 4 * STAGE;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * STAGE + kNW * 2 * PSLOT];
+  static_assert(4 * STAGE + kNW * 2 * PSLOT <= 160 * 1024, "LDS budget");
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, hg = lane >> 5;
-  // waves m and m + kNW own keys j0 + 32 m: the dV and the dK wave of a key
-  // block sit on the same SIMD (wave w runs on SIMD w mod 4), so every SIMD
-  // carries one of each and the per-iteration barrier waits for no SIMD
-  // holding two dK waves
   const int kb = wave % kNW;
-  const bool kwave = wave >= kNW;  // accumulates dK (else dV)
+  const bool swave = wave >= kNW;  // the dS wave (else the P wave)
   const int T = a.T, G = a.G, BK = 32 * kNW;
   const int units = a.B * a.Hkv;
   const int unit = blockIdx.x % units, kt = blockIdx.x / units;  // low key tiles (most rows) first
@@ -456,22 +460,20 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   // fastest in the grid order) read the same Q / dA tiles at about the same
   // time, from that XCD's L2; a workgroup stops at its own first keys.
 
-  // B operands: K^T (both waves) and -V^T (the dK wave) of this wave's keys
-  bf16x8 kf[KS], vf[KS];
+  // B operands: K^T (the P wave) or -V^T (the dS wave) of this wave's keys
+  bf16x8 kv[KS];
   {
-    const uint16_t* kr = (const uint16_t*)a.k.p + b * a.k.sb + (int64_t)key * a.k.st + g * a.k.sh;
-    const uint16_t* vr = (const uint16_t*)a.v.p + b * a.v.sb + (int64_t)key * a.v.st + g * a.v.sh;
+    const TIn& t = swave ? a.v : a.k;
+    const uint16_t* r = (const uint16_t*)t.p + b * t.sb + (int64_t)key * t.st + g * t.sh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kv[ks] = as_bf16x8(key < T ? *(const uint4*)(r + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+    const uint32_t flip = swave ? 0x80008000u : 0u;  // sign flip of every bf16 of V (exact)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = as_bf16x8(key < T ? *(const uint4*)(kr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
-      vf[ks] = as_bf16x8(key < T && kwave ? *(const uint4*)(vr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      retire(kf[ks]);
-      retire(vf[ks]);
-      const uint4 u = as_u4(vf[ks]);  // sign flip of every bf16 (exact)
-      vf[ks] = as_bf16x8(make_uint4(u.x ^ 0x80008000u, u.y ^ 0x80008000u, u.z ^ 0x80008000u, u.w ^ 0x80008000u));
+      retire(kv[ks]);
+      const uint4 u = as_u4(kv[ks]);
+      kv[ks] = as_bf16x8(make_uint4(u.x ^ flip, u.y ^ flip, u.z ^ flip, u.w ^ flip));
     }
   }
 
@@ -521,8 +523,6 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
     if (wave == NW - 2 && lane < 8) dma16_sbase(lg + ro, lane * 16, st + 4 * TB);
     if (wave == NW - 1 && lane < 8) dma16_sbase(dg + ro, lane * 16, st + 4 * TB + 128);
   };
-  // Two row tiles per barrier: the pair (it, it+1) uses stages 2(it/2 mod 2),
-  // +1, and the next pair streams into the other two stages meanwhile.
   issue(0);
   issue(1);
 
@@ -533,74 +533,67 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   TrBases<D> tb;
   tb.init(lane);
   const float sl2 = a.sl2;
-  f32x16 acc[CB];  // dV^T or -dK^T [c][key]
+  // P exchange: the P wave of key block kb writes tile t's P at
+  // pslot(kb, t): two 16-byte chunks per lane, chunk-major (conflict-free).
+  const uint32_t pbase = lds0 + PBASE + kb * 2 * PSLOT + lane * 16;
+  f32x16 acc[CB];  // dV^T (P wave) or -dK^T (dS wave) [c][key]
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
-  int cmp_h = 0, cmp_r0 = (nrt - 1) * kBT;  // the next iteration to compute
-  auto tile_step = [&](int stage, auto kw) {
-    constexpr bool KW = decltype(kw)::value;
-    const int i0 = cmp_r0;
-    if (++cmp_h == G) {
-      cmp_h = 0;
-      cmp_r0 -= kBT;
-    }
-    // Tiles of rows before this wave's keys (at most 3 per head, and every
-    // tile of an inactive wave) skip the scores but still run the
-    // accumulating MFMAs, with zero probabilities: leaving the accumulators
-    // untouched on some paths would make the compiler keep two copies.
+  // Per-tile LDS bases, opaque to the compiler: every read below is one of
+  // them plus an immediate offset (or XOR a constant); otherwise the
+  // compiler hoists each "lane base + constant" into a register of its own.
+  auto bases = [&](int stage, uint32_t& qrow, uint32_t& arow, uint32_t& rowst, uint32_t (&tbase)[TrBases<D>::NV],
+                   uint32_t region) {
     const uint32_t sb = lds0 + stage * STAGE;
-    // Per-tile LDS bases, opaque to the compiler: every read below is one of
-    // them plus an immediate offset (or, for the row reads, XOR a constant).
-    // Without this the compiler hoists each "lane base + constant" out of the
-    // loop into a register of its own and spills.
-    uint32_t qrow = sb + rxs, arow = sb + 2 * TB + rxs, rowst = sb + 4 * TB + 16 * hg;
-    uint32_t tbase[TrBases<D>::NV];
+    qrow = sb + rxs;
+    arow = sb + 2 * TB + rxs;
+    rowst = sb + 4 * TB + 16 * hg;
 #pragma unroll
-    for (int v = 0; v < TrBases<D>::NV; ++v) tbase[v] = sb + (KW ? TB : 3 * TB) + tb.b[v];
+    for (int v = 0; v < TrBases<D>::NV; ++v) tbase[v] = sb + region + tb.b[v];
     asm volatile("" : "+v"(qrow), "+v"(arow), "+v"(rowst));
 #pragma unroll
     for (int v = 0; v < TrBases<D>::NV; ++v) asm volatile("" : "+v"(tbase[v]));
-    // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
-    bf16x8 xk[2] = {};
-    if (i0 >= j0w) {
-      f32x4 lq[4], dq4[4];
-      if constexpr (KW) {
+  };
+  // A += X^T Y over the tile's 32 rows (X^T by transpose reads from tbase, Y the bf16 B operand)
+  auto accumulate = [&](const uint32_t (&tbase)[TrBases<D>::NV], const bf16x8 (&y)[2]) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          dq4[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 128 + 32 * q4);
-      }
-      bf16x8 qa[KS], da[KS];
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        qa[ks] = lds_read16(qrow ^ (32u * ks));
-        if constexpr (KW) da[ks] = lds_read16(arow ^ (32u * ks));
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint32_t q = tbase[cb % TrBases<D>::NV] + 16 * kk * RB + cb * 64;
+        acc[cb] = mfma32x32x16(join_bf16x8(tr_read(q), tr_read(q + 8 * RB)), y[kk], acc[cb]);
       }
+  };
+
+  // ---- the P wave ----
+  // phase 1 of a tile: P (bf16, registers) and its copy in LDS
+  auto p_phase1 = [&](int stage, int i0, int t, bf16x8 (&pk)[2]) {
+    uint32_t qrow, arow, rowst, tbase[TrBases<D>::NV];
+    bases(stage, qrow, arow, rowst, tbase, 3 * TB);
+    pk[0] = pk[1] = bf16x8{};
+    if (i0 >= j0w) {  // (else: rows before this wave's keys, or an inactive wave)
+      bf16x8 qa[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qa[ks] = lds_read16(qrow ^ (32u * ks));
+      f32x4 lq[4];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
         lq[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 32 * q4);
-      f32x16 s, dp;
+      f32x16 s;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        if constexpr (KW) dp[r] = dq4[r >> 2][r & 3];  // D of the row
-      }
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32x32x16(qa[ks], kf[ks], s);                      // S = Q K^T
-        if constexpr (KW) dp = mfma32x32x16(da[ks], vf[ks], dp);  // D - dP = D + dA (-V)^T
-      }
-      // Schedule: a batch of LDS reads first, then one MFMA per further read,
-      // so each operand is read several MFMAs before its use.
-      constexpr int NMF = KW ? 2 * KS : KS, NRD = KW ? 2 * KS + 8 : KS + 4;
-      __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
+      for (int ks = 0; ks < KS; ++ks) s = mfma32x32x16(qa[ks], kv[ks], s);  // S = Q K^T
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int i = 0; i < NMF; ++i) {
+      for (int i = 0; i < KS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], sl2, -lq[r >> 2][r & 3]);
@@ -618,44 +611,121 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
       f32x8 e0, e1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(x[r]);
-        if constexpr (KW) pr *= dp[r];  // P (D - dP) = -dS
+        const float pr = __builtin_amdgcn_exp2f(x[r]);
         if (r < 8) e0[r] = pr; else e1[r - 8] = pr;
       }
-      xk[0] = cvt_bf16x8(e0);
-      xk[1] = cvt_bf16x8(e1);
+      pk[0] = cvt_bf16x8(e0);
+      pk[1] = cvt_bf16x8(e1);
     }
-    // dV^T += dA^T P (dV wave), -dK^T += Q^T (-dS) (dK wave)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const uint32_t q = tbase[cb % TrBases<D>::NV] + 16 * kk * RB + cb * 64;
-        acc[cb] = mfma32x32x16(join_bf16x8(tr_read(q), tr_read(q + 8 * RB)), xk[kk], acc[cb]);
-      }
+    const uint32_t pw = pbase + t * PSLOT;
+    *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)pw = pk[0];
+    *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pw + 1024) = pk[1];
+  };
+  auto p_phase2 = [&](int stage, const bf16x8 (&pk)[2]) {
+    uint32_t qrow, arow, rowst, tbase[TrBases<D>::NV];
+    bases(stage, qrow, arow, rowst, tbase, 3 * TB);
+    accumulate(tbase, pk);  // dV^T += dA^T P
   };
 
-  // nit is even (the group size G = Hq / Hkv is even), so every pair is
-  // whole; one loop per role keeps each role's accumulators in one set of
-  // registers (no control flow inside the loop joins two assignments).
-  auto run = [&](auto kw) {
+  // ---- the dS wave ----
+  // phase 1 of a tile: D - dP in registers
+  auto s_phase1 = [&](int stage, int i0, f32x16& dp) {
+    uint32_t qrow, arow, rowst, tbase[TrBases<D>::NV];
+    bases(stage, qrow, arow, rowst, tbase, TB);
+    if (i0 >= j0w) {
+      f32x4 dq4[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        dq4[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 128 + 32 * q4);
+      bf16x8 da[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) da[ks] = lds_read16(arow ^ (32u * ks));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = dq4[r >> 2][r & 3];  // D of the row
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) dp = mfma32x32x16(da[ks], kv[ks], dp);  // D + dA (-V)^T
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + 4 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+    }
+  };
+  // phase 2 of a tile: -dS = P (D - dP), then -dK^T += Q^T (-dS)
+  auto s_phase2 = [&](int stage, int t, const f32x16& dp) {
+    uint32_t qrow, arow, rowst, tbase[TrBases<D>::NV];
+    bases(stage, qrow, arow, rowst, tbase, TB);
+    const uint32_t pr_ = pbase + t * PSLOT;
+    const uint4 p0 = as_u4(*(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)pr_);
+    const uint4 p1 = as_u4(*(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(pr_ + 1024));
+    const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    f32x8 e0, e1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      // bf16 r of the 16 (element r & 1 of word r >> 1) as fp32
+      const uint32_t w = pw[r >> 1];
+      const float p = __builtin_bit_cast(float, (r & 1) ? (w & 0xffff0000u) : (w << 16));
+      const float ds = p * dp[r];  // P (D - dP) = -dS
+      if (r < 8) e0[r] = ds; else e1[r - 8] = ds;
+    }
+    const bf16x8 y[2] = {cvt_bf16x8(e0), cvt_bf16x8(e1)};
+    accumulate(tbase, y);
+  };
+
+  // nit is even (the group size G = Hq / Hkv is even), so every period has
+  // two tiles; one loop per role keeps each role's accumulators in one set
+  // of registers.
+  int cmp_h = 0, cmp_r0 = (nrt - 1) * kBT;  // the next iteration to compute
+  auto next_row0 = [&]() {
+    const int i0 = cmp_r0;
+    if (++cmp_h == G) {
+      cmp_h = 0;
+      cmp_r0 -= kBT;
+    }
+    return i0;
+  };
+  if (!swave) {
     for (int it = 0; it < nit; it += 2) {
       const int sp = (it >> 1) & 1;  // stage pair of tiles it, it+1
       wait_copies();
-      __syncthreads();  // tiles it, it+1 visible; the other stage pair is free
+      __syncthreads();  // tiles it, it+1 visible; the other stage pair and the P slots are free
       if (it + 2 < nit) {
         issue(2 * (sp ^ 1));
         issue(2 * (sp ^ 1) + 1);
       }
-      tile_step(2 * sp, kw);
-      tile_step(2 * sp + 1, kw);
+      const int i0a = next_row0(), i0b = next_row0();
+      bf16x8 pa[2], pb[2];
+      p_phase1(2 * sp, i0a, 0, pa);
+      p_phase1(2 * sp + 1, i0b, 1, pb);
+      __syncthreads();  // P of both tiles in LDS
+      p_phase2(2 * sp, pa);
+      p_phase2(2 * sp + 1, pb);
     }
-  };
-  if (kwave) run(std::true_type{});
-  else run(std::false_type{});
+  } else {
+    for (int it = 0; it < nit; it += 2) {
+      const int sp = (it >> 1) & 1;
+      wait_copies();
+      __syncthreads();
+      if (it + 2 < nit) {
+        issue(2 * (sp ^ 1));
+        issue(2 * (sp ^ 1) + 1);
+      }
+      const int i0a = next_row0(), i0b = next_row0();
+      f32x16 da_, db_;
+      s_phase1(2 * sp, i0a, da_);
+      s_phase1(2 * sp + 1, i0b, db_);
+      __syncthreads();  // P of both tiles in LDS
+      s_phase2(2 * sp, 0, da_);
+      s_phase2(2 * sp + 1, 1, db_);
+    }
+  }
   if (!active || key >= T) return;
-  const TOut& o = kwave ? a.dk : a.dv;
-  const float sc = kwave ? -a.scale : 1.f;
+  const TOut& o = swave ? a.dk : a.dv;
+  const float sc = swave ? -a.scale : 1.f;
   uint16_t* dst = (uint16_t*)o.p + b * o.sb + (int64_t)key * o.st + g * o.sh;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
