@@ -47,12 +47,6 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// 16-byte global load marked non-temporal (streamed once, not worth caching).
-__device__ __forceinline__ uint4 load_nt16(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
 
@@ -62,23 +56,6 @@ __device__ __forceinline__ bf16x8 join_bf16x8(uint2 lo, uint2 hi) {
 
 // Eight fp32 values -> eight bf16 (v_cvt_pk_bf16_f32, round to nearest even).
 __device__ __forceinline__ bf16x8 cvt_bf16x8(f32x8 v) { return __builtin_convertvector(v, bf16x8); }
-
-// Pack the 16-bit element `e` (0..7) of four 8-element rows into one 64-bit
-// word holding (row0[e], row1[e], row2[e], row3[e]) -- a 4x8 -> 8x4 transpose
-// step done with byte permutes.
-__device__ __forceinline__ uint32_t pick_pair(uint32_t w_lo_row, uint32_t w_hi_row, int odd) {
-  // v_perm_b32: bytes 0-3 come from the second source, 4-7 from the first.
-  return __builtin_amdgcn_perm(w_hi_row, w_lo_row, odd ? 0x07060302u : 0x05040100u);
-}
-__device__ __forceinline__ uint32_t u4_word(const uint4& x, int i) {
-  return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
-}
-__device__ __forceinline__ uint2 column4(const uint4& r0, const uint4& r1, const uint4& r2, const uint4& r3,
-                                         int e) {
-  const int w = e >> 1, odd = e & 1;
-  return make_uint2(pick_pair(u4_word(r0, w), u4_word(r1, w), odd),
-                    pick_pair(u4_word(r2, w), u4_word(r3, w), odd));
-}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);

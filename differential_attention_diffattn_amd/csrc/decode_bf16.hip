@@ -7,15 +7,17 @@
 // The cache is the only large operand (B*L*Hkv*d*2 bf16), so the kernel is
 // built to stream it from HBM exactly once:
 //   * split kernel: a workgroup owns (batch b, kv head g, one chunk of the
-//     cache).  Its 4 waves take interleaved 32-token blocks.  For each block
-//     a wave loads K straight from global memory into MFMA A-operand
-//     registers (16-byte loads, 64 contiguous bytes per row per instruction)
-//     and scores all G query heads of the group at once with
-//     v_mfma_f32_16x16x32_bf16 (tokens x heads), keeps a lazily rescaled
-//     online softmax per head, transposes the V block through a per-wave LDS
-//     slice and accumulates O^T = V^T P^T with the same MFMA.  The four
-//     waves' (max, sum, O) states are then merged in LDS (log-sum-exp) and
-//     one partial per (b, g, chunk, head) goes to the caller's workspace.
+//     cache).  Its 4 waves take interleaved 32-token blocks.  Each block's K
+//     and V rows are copied HBM -> the wave's LDS slot (global_load_lds,
+//     16 bytes per lane, marked non-temporal: read once), the next block's
+//     copy in flight while this one is computed by the other workgroup on
+//     the CU.  The wave scores all G query heads of the group at once with
+//     v_mfma_f32_16x16x32_bf16 (tokens x heads, K read back from LDS as the
+//     operand), keeps a lazily rescaled online softmax per head and
+//     accumulates O^T = V^T P^T with the same MFMA (V^T by transpose reads).
+//     The four waves' (max, sum, O) states are then merged in LDS
+//     (log-sum-exp) and one partial per (b, g, chunk, head) goes to the
+//     caller's workspace.
 //   * merge kernel: per (b, pair), the partials of both heads are merged in
 //     split order (fixed, no atomics: deterministic), normalised and combined
 //     as a_2p - sigmoid(lam[b, p]) a_2p+1.
@@ -86,7 +88,7 @@ __device__ __forceinline__ void lds_fence() {
 }
 
 template <int D, bool PAGED, int NCB>
-__global__ void __launch_bounds__(kWaves * 64, (PAGED || NCB > 1) ? 2 : 3) decode_split_kernel(const DecodeArgs a) {
+__global__ void __launch_bounds__(kWaves * 64, 2) decode_split_kernel(const DecodeArgs a) {
   constexpr int W = kWaves;  // waves per workgroup
   constexpr int KS = D / 32;   // k-steps of the score MFMA
   constexpr int CB = D / 16;   // 16-wide column blocks of O^T
@@ -100,17 +102,9 @@ __global__ void __launch_bounds__(kWaves * 64, (PAGED || NCB > 1) ? 2 : 3) decod
   constexpr int NI = kBlk / RPI;            // copy instructions per tensor and block
   constexpr int CPR = D / 8;                // 16-byte chunks per row
   static_assert(16 % RPI == 0, "a copy instruction's rows lie in one 16-token sub-block");
-  // Two data paths.  DMA (paged cache, or several new tokens): K and V blocks
-  // are copied into LDS slots by global_load_lds, the next block streaming in
-  // while this one is computed.  Register path (dense cache, one new token):
-  // K is loaded straight into MFMA operand registers and V through registers
-  // into a transposed LDS slice; three workgroups per CU hide the latency --
-  // measured faster for that case.  Both give each wave the same blocks and
-  // the same MFMA sequence, so their results agree bit for bit.
-  constexpr bool DMA = PAGED || NCB > 1;
-  constexpr int VROW = kBlk + 4;                           // V^T row (bf16, padded: conflict-free 8 B reads)
-  constexpr int VT_ELEMS = D * VROW;                       // one wave's V^T slice (register path)
-  constexpr int LDS_STG = DMA ? W * NST * SLOT : W * VT_ELEMS * 2;  // bytes
+  // K and V blocks are copied into per-wave LDS slots by global_load_lds;
+  // K is read back as the MFMA operand, V^T by transpose reads.
+  constexpr int LDS_STG = W * NST * SLOT;  // bytes
   constexpr int LDS_RED = W * 16 * (D + 2) * 4;       // bytes (one column block at a time)
   constexpr int LDS_BYTES = LDS_STG > LDS_RED ? LDS_STG : LDS_RED;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
@@ -222,13 +216,11 @@ __global__ void __launch_bounds__(kWaves * 64, (PAGED || NCB > 1) ? 2 : 3) decod
   }
   // q fragments and table entries have landed before the first copy is issued
   // (no compiler-placed wait inside the loop, which would also wait for copies)
-  if constexpr (DMA) {
 #pragma unroll
-    for (int n = 0; n < NCB; ++n)
+  for (int n = 0; n < NCB; ++n)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) asm volatile("s_waitcnt vmcnt(0)" : "+v"(qf[n][ks]));
-    asm volatile("s_waitcnt vmcnt(0)" : "+v"(ent));
-  }
+    for (int ks = 0; ks < KS; ++ks) asm volatile("s_waitcnt vmcnt(0)" : "+v"(qf[n][ks]));
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(ent));
 
   // ---- copies: this wave's block -> its LDS slot (global_load_lds) ----------
   // Copy i of a tensor moves rows i*RPI .. i*RPI + RPI-1; the lane moves
@@ -334,13 +326,11 @@ __global__ void __launch_bounds__(kWaves * 64, (PAGED || NCB > 1) ? 2 : 3) decod
   // c16, kg) holds tokens blk + 16 sub + 4 kg + r): mask, lazy rescale,
   // probabilities as the bf16 B operand of P.V (slot t: token 4 kg + t for
   // t < 4, 16 + 4 kg + t - 4 for t >= 4).
-  // Copy path: only a block reaching the first masked entry (past the
-  // sequence's end, or after a new token's own position) applies the mask
-  // (a uniform test).  Register path: every block applies it with selects
-  // (a branch there costs the loads' schedule: measured 6% slower).
+  // Only a block reaching the first masked entry (past the sequence's end,
+  // or after a new token's own position) applies the mask (a uniform test).
   const int mask_from = L - NQ + 1;
   auto softmax_block = [&](f32x4* sc, int blk, int n2) -> bf16x8 {
-    if (!DMA || blk + kBlk > mask_from) {
+    if (blk + kBlk > mask_from) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -380,57 +370,6 @@ __global__ void __launch_bounds__(kWaves * 64, (PAGED || NCB > 1) ? 2 : 3) decod
     return cvt_bf16x8(p);
   };
 
-  if constexpr (!DMA) {
-    // ---- register path (dense cache, one new token) ----
-    uint16_t* vt = (uint16_t*)smem + wv * VT_ELEMS;
-    constexpr int VU = (kBlk / 4) * (D / 8) / 64;  // 4x8 V units per lane
-    static_assert(VU >= 1 && (kBlk / 4) * (D / 8) % 64 == 0, "V block split");
-    for (int blk = blk0; blk < t1; blk += kBlk * W) {
-      // Tokens past the end load the last token's row instead (no branches,
-      // so the loads stay in flight together): their scores are masked to
-      // -inf below, so their probabilities are 0 and the rows add nothing.
-      uint4 kr[2][KS];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int tok = min(blk + 16 * sub + c16, L - 1);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[sub][ks] = load_nt16(kbase + (int64_t)tok * kst + 32 * ks + 8 * kg);
-      }
-      uint4 vr[VU][4];
-#pragma unroll
-      for (int u = 0; u < VU; ++u) {
-        const int unit = lane + 64 * u;
-        const int rg = unit % (kBlk / 4), cc = unit / (kBlk / 4);
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int tok = min(blk + 4 * rg + qq, L - 1);
-          vr[u][qq] = load_nt16(vbase + (int64_t)tok * vst + cc * 8);
-        }
-      }
-      f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sc[sub] = mfma16x16x32(as_bf16x8(kr[sub][ks]), qf[0][ks], sc[sub]);
-      const bf16x8 pk = softmax_block(sc, blk, 0);
-      // V block -> V^T in this wave's LDS slice
-#pragma unroll
-      for (int u = 0; u < VU; ++u) {
-        const int unit = lane + 64 * u;
-        const int rg = unit % (kBlk / 4), cc = unit / (kBlk / 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *(uint2*)(vt + (cc * 8 + e) * VROW + 4 * rg) = column4(vr[u][0], vr[u][1], vr[u][2], vr[u][3], e);
-      }
-      lds_fence();
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const uint16_t* row = vt + (16 * cb + c16) * VROW + 4 * kg;
-        o[0][cb] = mfma16x16x32(join_bf16x8(*(const uint2*)row, *(const uint2*)(row + 16)), pk, o[0][cb]);
-      }
-      lds_fence();
-    }
-  } else {
   // Block n goes to slot n % NST, issued NST - 1 steps ahead (NST = 1: right
   // after the previous block's reads); the slot it overwrites was last read
   // at the end of the step before.
@@ -488,7 +427,6 @@ __global__ void __launch_bounds__(kWaves * 64, (PAGED || NCB > 1) ? 2 : 3) decod
     }
     lds_fence();  // this slot's reads are done before a later copy rewrites it
     if (NST == 1 && n + 1 < nsteps) issue(n + 1, 0);
-  }
   }
 
   // ---- per column block: per-wave state -> LDS, then a log-sum-exp merge
