@@ -66,20 +66,6 @@ __device__ __forceinline__ int dec_swizzle(int r) {
   return D >= 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
 }
 
-#ifndef DA_DEC_DMA_POLICY
-#define DA_DEC_DMA_POLICY "nt"
-#endif
-// dma16_sbase (tile_ops.hpp) with a cache-policy modifier: the cache is read
-// once, so its copies are marked non-temporal ("nt": streamed through the
-// caches; measured 5-7% faster on the paged and 4-token decodes than the
-// default policy, sc0 / sc1 unchanged).
-__device__ __forceinline__ void dec_dma16(const void* base, uint32_t off, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 " DA_DEC_DMA_POLICY
-               :
-               : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory");
-}
-
 __device__ __forceinline__ void lds_fence() {
   // The LDS executes one wave's instructions in order; this waits for the
   // wave's outstanding LDS accesses and is a compiler barrier for memory, so
@@ -264,8 +250,8 @@ __global__ void __launch_bounds__(kWaves * 64, 2) decode_split_kernel(const Deco
         }
 #pragma unroll
         for (int j = 0; j < CPH; ++j) {
-          dec_dma16(kb, kho[j], dst + (h * CPH + j) * 1024);
-          dec_dma16(vb, vho[j], dst + TBYTES + (h * CPH + j) * 1024);
+          dma16_sbase_nt(kb, kho[j], dst + (h * CPH + j) * 1024);
+          dma16_sbase_nt(vb, vho[j], dst + TBYTES + (h * CPH + j) * 1024);
         }
       }
       return;
@@ -289,8 +275,8 @@ __global__ void __launch_bounds__(kWaves * 64, 2) decode_split_kernel(const Deco
       const int tok = min(blk + i * RPI + r_in, L - 1);
       const uint32_t ko = (uint32_t)((tok - anchor) * kst * 2) + choff[i];
       const uint32_t vo = (uint32_t)((tok - anchor) * vst * 2) + choff[i];
-      dec_dma16(kbase + kb, ko, dst + i * 1024);
-      dec_dma16(vbase + vb, vo, dst + TBYTES + i * 1024);
+      dma16_sbase_nt(kbase + kb, ko, dst + i * 1024);
+      dma16_sbase_nt(vbase + vb, vo, dst + TBYTES + i * 1024);
     }
   };
 

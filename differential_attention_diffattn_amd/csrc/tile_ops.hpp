@@ -23,11 +23,16 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 // that copy only ever targets another LDS stage.  The kernel waits for it
 // explicitly (vmcnt(0) + barrier) before the stage is read.  M0 is used by
 // nothing else in these kernels.
-#ifndef DA_DMA_POLICY
-#define DA_DMA_POLICY ""
-#endif
 __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t off, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 " DA_DMA_POLICY
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+// The same copy marked non-temporal ("nt"), for data read once (a stream):
+// the caches do not keep it at the expense of data that is re-read.
+__device__ __forceinline__ void dma16_sbase_nt(const void* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :
                : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
