@@ -1249,7 +1249,12 @@ __device__ __forceinline__ void bwd_v1_dv_body(const V1BwdArgs& a, int bid, unsi
 // The dQ, dK and dV work of the V1 backward in one grid, so no workgroup
 // waits for another kernel's tail: level L = 0, 1, ... (heaviest first) holds
 // the dQ row tile qt-1-L of both maps, the dK key tile L of both maps and the
-// dV key tile L (each a causal trapezoid of about the same size).
+// dV key tile L (each a causal trapezoid of about the same size).  The
+// hardware deals consecutive workgroups to the 8 XCDs in turn (XCD = id mod
+// 8); when the (batch, head) units divide by 8, XCD x takes the units
+// u = x mod 8 only (its work in level order, then unit, then role), so the
+// workgroups running together on one XCD stream the tiles of a few heads
+// through its L2 instead of every head's.
 template <int D>
 struct V1MainCfg {
   static constexpr int a_ = DqCfg<D, 2 * D>::SMEM, b_ = V1DkCfg<D>::SMEM, c_ = V1DvCfg<D>::SMEM;
@@ -1263,10 +1268,22 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_v1_main_kernel(const V1BwdArg
     return;
   }
   const int bh = a.B * a.H;
-  const int per_level = 5 * bh;
-  const int level = (blockIdx.x - 1) / per_level, r = (blockIdx.x - 1) % per_level;
-  if (r < 2 * bh) {  // dQ of map r / bh, unit r % bh
-    const int m = r / bh;
+  const int id = blockIdx.x - 1;
+  int level, u, role;  // role 0 / 1: dQ of map 0 / 1; 2 / 3: dK of map 0 / 1; 4: dV
+  if (bh % 8 == 0) {
+    const int per = 5 * (bh / 8);  // one XCD's workgroups per level
+    const int sx = id / 8, w = sx % per;
+    level = sx / per;
+    u = id % 8 + 8 * (w / 5);
+    role = w % 5;
+  } else {
+    const int r = id % (5 * bh);
+    level = id / (5 * bh);
+    role = r < 2 * bh ? r / bh : r < 4 * bh ? 2 + (r - 2 * bh) % 2 : 4;
+    u = r < 2 * bh ? r % bh : r < 4 * bh ? (r - 2 * bh) / 2 : r - 4 * bh;
+  }
+  if (role < 2) {  // dQ of map `role`, unit u
+    const int m = role;
     BwdArgs q{};
     q.q = a.q[m], q.k = a.k[m], q.v = a.v;
     q.dq = a.dq[m];
@@ -1275,11 +1292,11 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_v1_main_kernel(const V1BwdArg
     q.lsew = a.lsew[m];
     q.sl2 = a.sl2, q.scale = a.scale;
     q.B = a.B, q.T = a.T, q.Hq = a.H, q.Hkv = a.H, q.G = 1, q.Tp = a.Tp;
-    bwd_dq_body<D, 2 * D>(q, level * bh + r % bh, smem);
-  } else if (r < 4 * bh) {
-    bwd_v1_dk_body<D>(a, level * 2 * bh + (r - 2 * bh), smem);
+    bwd_dq_body<D, 2 * D>(q, level * bh + u, smem);
+  } else if (role < 4) {
+    bwd_v1_dk_body<D>(a, level * 2 * bh + 2 * u + (role - 2), smem);
   } else {
-    bwd_v1_dv_body<D>(a, level * bh + (r - 4 * bh), smem);
+    bwd_v1_dv_body<D>(a, level * bh + u, smem);
   }
 }
 
