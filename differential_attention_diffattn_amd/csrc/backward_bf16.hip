@@ -493,17 +493,34 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   const uint16_t* ag = a.dA + (int64_t)b * T * a.Hq * D + (int64_t)g * G * D;
   const float* lg = a.lsew + ((int64_t)b * a.Hq + g * G) * a.Tp;
   const float* dg = a.Dw + ((int64_t)b * a.Hq + g * G) * a.Tp;
-  int iss_h = 0, iss_r0 = (nrt - 1) * kBT;  // the next iteration to copy
+  // The next iteration to copy, with its Q / dA row pointers and its lse / D
+  // offset, advanced by constant element deltas (next head of the group, or
+  // head 0 of the row tile below) instead of being formed from (head, row)
+  // with 64-bit products for every tile.
+  int iss_h = 0, iss_r0 = (nrt - 1) * kBT;
+  const uint16_t* iss_q = qg + (int64_t)iss_r0 * a.q.st;
+  const uint16_t* iss_a = ag + (int64_t)iss_r0 * ast;
+  int64_t iss_l = iss_r0;  // head * Tp + row
+  const int64_t wq = -(int64_t)(G - 1) * a.q.sh - (int64_t)kBT * a.q.st;
+  const int64_t wa = -(int64_t)(G - 1) * D - (int64_t)kBT * ast, wl = -(int64_t)(G - 1) * a.Tp - kBT;
   auto issue = [&](int stage) {
     const uint32_t st = lds0 + stage * STAGE;
-    const int i0 = iss_r0, hh = iss_h;
+    const int i0 = iss_r0;
+    const uint16_t* qp = iss_q;
+    const uint16_t* ap = iss_a;
+    const int64_t ro = iss_l;
     if (++iss_h == G) {
       iss_h = 0;
       iss_r0 -= kBT;
+      iss_q += wq;
+      iss_a += wa;
+      iss_l += wl;
+    } else {
+      iss_q += a.q.sh;
+      iss_a += D;
+      iss_l += a.Tp;
     }
     if (copier) {
-      const uint16_t* qp = qg + (int64_t)hh * a.q.sh + (int64_t)i0 * a.q.st;
-      const uint16_t* ap = ag + (int64_t)hh * D + (int64_t)i0 * ast;
       uint32_t oqk = o_qk, oqv = o_qv, oak = o_ak, oav = o_av;
       if (i0 + kBT > T) {  // ragged last row tile: rows past T repeat row T - 1
         const int rr = min(cr, T - 1 - i0);
@@ -519,7 +536,6 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
       dma16_sbase(ap, oav, dst + 3 * TB);
     }
     // the 32 rows' lse and D (padded arrays: always in bounds), 8 lanes x 16 B each
-    const int64_t ro = (int64_t)hh * a.Tp + i0;
     if (wave == NW - 2 && lane < 8) dma16_sbase(lg + ro, lane * 16, st + 4 * TB);
     if (wave == NW - 1 && lane < 8) dma16_sbase(dg + ro, lane * 16, st + 4 * TB + 128);
   };
