@@ -113,22 +113,22 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdArgs a) {
 
 // ---- shared tile machinery -------------------------------------------------
 // A streamed tile is kBT rows of D bf16 of one tensor (row stride `st`
-// elements), copied HBM -> LDS in 1 KB chunks.  Layout "k": 16-byte chunks
-// XOR-swizzled for ds_read_b128 row reads; layout "v": swizzled for
-// ds_read_b64_tr_b16 transpose reads.  Rows past the end are clamped to the
-// last row (finite data; masked where used).
+// elements), copied HBM -> LDS in 1 KB chunks, its 16-byte chunks
+// XOR-swizzled for the reads it serves (TileLayout: ds_read_b128 row reads,
+// ds_read_b64_tr_b16 transpose reads, or both).  Rows past the end are
+// clamped to the last row (finite data; masked where used).
 template <int D, int NW = kNW>
 struct TileDma {
   static constexpr int BYTES = kBT * D * 2;
   static constexpr int CH = BYTES / 1024;  // 1 KB copies per tensor tile
   // issue this wave's copies of chunks wave, wave + NW, ... of one tensor tile
-  __device__ static void issue(const uint16_t* base, int64_t st, int row0, int T, bool vlayout, uint32_t lds,
+  __device__ static void issue(const uint16_t* base, int64_t st, int row0, int T, int layout, uint32_t lds,
                                int wave, int lane) {
     const bool tail = row0 + kBT > T;
     for (int ci = wave; ci < CH; ci += NW) {
       const int pos = ci * 64 + lane;
       const int r = pos / (D / 8), sc = pos % (D / 8);
-      const int sw = vlayout ? v_swizzle<D>(r) : k_swizzle<D>(r);
+      const int sw = tile_swizzle<D>(layout, r);
       const int rr = tail ? min(r, T - 1 - row0) : r;
       const uint32_t off = ((uint32_t)rr * (uint32_t)st + (uint32_t)((sc ^ sw) * 8)) * 2u;
       dma16_sbase(base + (int64_t)row0 * st, off, lds + ci * 1024);
@@ -144,12 +144,12 @@ struct TileCopy {
   static constexpr int CH = TileDma<D, NW>::CH;
   static constexpr int PER = (CH + NW - 1) / NW;
   uint32_t off[PER];
-  __device__ void init(int64_t st, bool vlayout, int wave, int lane) {
+  __device__ void init(int64_t st, int layout, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int pos = (wave + i * NW) * 64 + lane;
       const int r = pos / (D / 8), sc = pos % (D / 8);
-      const int sw = vlayout ? v_swizzle<D>(r) : k_swizzle<D>(r);
+      const int sw = tile_swizzle<D>(layout, r);
       off[i] = ((uint32_t)r * (uint32_t)st + (uint32_t)((sc ^ sw) * 8)) * 2u;
     }
   }
@@ -162,9 +162,14 @@ struct TileCopy {
 };
 
 // Per-lane LDS byte offsets of the transpose reads giving A operands
-// X^T[c][rows of k-chunk kk] from a "v" layout tile (rows in the order the
-// P-like B operands hold them: 16kk + 4hg + 0..3, then + 8).
-template <int D>
+// X^T[c][rows of k-chunk kk] from a tile in the transpose (BOTH = false) or
+// the both-ways (BOTH = true) layout (rows in the order the P-like B operands
+// hold them: 16kk + 4hg + 0..3, then + 8).  base(v) + v * 64 addresses
+// column block v of the lane's first row; off(cb, kk, h) is the byte offset
+// of column block cb in rows + 16 kk + 8 h from the base it uses, which is
+// base(cb % NV) (both-ways layout, h = 1: base((cb ^ 1) % NV), since the
+// swizzle of the row 8 further down flips bit 2 of the chunk).
+template <int D, bool BOTH = false>
 struct TrBases {
   static constexpr int NV = D >= 128 ? 4 : 2;
   uint32_t b[NV];
@@ -172,9 +177,18 @@ struct TrBases {
     const int l16 = lane & 15, g16 = lane >> 4;
     const int vr = 4 * (g16 >> 1) + (l16 >> 2);
     const int cl = 2 * (g16 & 1) + ((l16 & 3) >> 1);
-    const int x = v_swizzle<D>(vr);
+    const int x = BOTH ? u_swizzle<D>(vr) : v_swizzle<D>(vr);
 #pragma unroll
     for (int v = 0; v < NV; ++v) b[v] = vr * (D * 2) + (((4 * v + cl) ^ x) - 4 * v) * 16 + (l16 & 1) * 8;
+  }
+  static constexpr int src(int cb, int h) { return ((BOTH && h) ? (cb ^ 1) : cb) % NV; }
+  static constexpr int off(int cb, int kk, int h) {
+    return ((BOTH && h) ? (cb ^ 1) : cb) * 64 + (16 * kk + 8 * h) * (D * 2);
+  }
+  // the bf16 A operand X^T[c of column block cb][rows of k-chunk kk]
+  template <int CB_, int KK>
+  static __device__ __forceinline__ bf16x8 read(const uint32_t (&tbase)[NV]) {
+    return join_bf16x8(tr_read(tbase[src(CB_, 0)] + off(CB_, KK, 0)), tr_read(tbase[src(CB_, 1)] + off(CB_, KK, 1)));
   }
 };
 
@@ -206,7 +220,7 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // q/k head dim; DV: v head dim (V2: D; V1: 2D, one launch per map).
 template <int D, int DV>
 struct DqCfg {
-  static constexpr int STAGE = 2 * TileDma<D>::BYTES + TileDma<DV>::BYTES;  // [K "k" | K "v" | V "k"]
+  static constexpr int STAGE = TileDma<D>::BYTES + TileDma<DV>::BYTES;  // [K (both ways) | V (rows)]
   static constexpr int SMEM = 2 * STAGE;
 };
 // `bid`: the workgroup's index in the dQ grid order; `smem`: DqCfg::SMEM bytes
@@ -249,24 +263,21 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
 
   const uint16_t* kp = (const uint16_t*)a.k.p + b * a.k.sb + g * a.k.sh;
   const uint16_t* vp = (const uint16_t*)a.v.p + b * a.v.sb + g * a.v.sh;
-  TileCopy<D, kNW> ck, ckv;
+  // K is read as rows (S^T = K Q^T) and transposed (dQ += dS K): one copy in
+  // the both-ways layout; V as rows only.
+  TileCopy<D, kNW> ck;
   TileCopy<DV, kNW> cv;
-  ck.init(a.k.st, false, wave, lane);
-  ckv.init(a.k.st, true, wave, lane);
-  cv.init(a.v.st, false, wave, lane);
+  ck.init(a.k.st, kBothLayout, wave, lane);
+  cv.init(a.v.st, kRowLayout, wave, lane);
   auto issue = [&](int kt, int stage) {
     const uint32_t st = lds0 + stage * STAGE;
     const int r0 = kt * kBT;
     if (r0 + kBT > T) {  // ragged last tile
-      Dma::issue(kp, a.k.st, r0, T, false, st, wave, lane);
-      Dma::issue(kp, a.k.st, r0, T, true, st + TB, wave, lane);
-      DmaV::issue(vp, a.v.st, r0, T, false, st + 2 * TB, wave, lane);
+      Dma::issue(kp, a.k.st, r0, T, kBothLayout, st, wave, lane);
+      DmaV::issue(vp, a.v.st, r0, T, kRowLayout, st + TB, wave, lane);
     } else {
-      const uint16_t* kr = kp + (int64_t)r0 * a.k.st;
-      const uint16_t* vr = vp + (int64_t)r0 * a.v.st;
-      ck.issue(kr, st, wave);
-      ckv.issue(kr, st + TB, wave);
-      cv.issue(vr, st + 2 * TB, wave);
+      ck.issue(kp + (int64_t)r0 * a.k.st, st, wave);
+      cv.issue(vp + (int64_t)r0 * a.v.st, st + TB, wave);
     }
   };
   issue(0, 0);
@@ -298,9 +309,10 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
   // Row reads (K rows for S^T, V rows for dP^T): chunk (2 ks + hg) ^
   // swizzle(li) = 2 ks ^ (hg ^ swizzle(li)), so the address is
   // (tile base + lane part) ^ 32 ks.
-  const uint32_t kxs = (uint32_t)(li * (2 * D) + ((hg ^ k_swizzle<D>(li)) << 4));
+  const uint32_t kxs = (uint32_t)(li * (2 * D) + ((hg ^ u_swizzle<D>(li)) << 4));
   const uint32_t vxs = (uint32_t)(li * (2 * DV) + ((hg ^ k_swizzle<DV>(li)) << 4));
-  TrBases<D> tb;
+  using TrB = TrBases<D, true>;
+  TrB tb;
   tb.init(lane);
   const float sl2 = a.sl2;
   f32x16 acc[CB];  // -dQ^T
@@ -316,13 +328,13 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
     if (kt + 1 < nkt) issue(kt + 1, stage ^ 1);
     const int j0 = kt * kBT;
     const uint32_t st = lds0 + stage * STAGE;
-    uint32_t krow = st + kxs, vrow = st + 2 * TB + vxs;
-    uint32_t tbase[TrBases<D>::NV];
+    uint32_t krow = st + kxs, vrow = st + TB + vxs;
+    uint32_t tbase[TrB::NV];
 #pragma unroll
-    for (int v = 0; v < TrBases<D>::NV; ++v) tbase[v] = st + TB + tb.b[v];
+    for (int v = 0; v < TrB::NV; ++v) tbase[v] = st + tb.b[v];
     asm volatile("" : "+v"(krow), "+v"(vrow));
 #pragma unroll
-    for (int v = 0; v < TrBases<D>::NV; ++v) asm volatile("" : "+v"(tbase[v]));
+    for (int v = 0; v < TrB::NV; ++v) asm volatile("" : "+v"(tbase[v]));
     // Key tiles entirely after this wave's rows (the last 3 at most) skip the
     // scores and accumulate zeros: the accumulators then take one path.
     bf16x8 dsk[2] = {};
@@ -377,8 +389,9 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const uint32_t q = tbase[cb % TrBases<D>::NV] + 16 * kk * (2 * D) + cb * 64;
-        acc[cb] = mfma32x32x16(join_bf16x8(tr_read(q), tr_read(q + 8 * (2 * D))), dsk[kk], acc[cb]);
+        const bf16x8 ka = join_bf16x8(tr_read(tbase[TrB::src(cb, 0)] + TrB::off(cb, kk, 0)),
+                                      tr_read(tbase[TrB::src(cb, 1)] + TrB::off(cb, kk, 1)));
+        acc[cb] = mfma32x32x16(ka, dsk[kk], acc[cb]);
       }
   }
   if (!active || row >= T) return;
@@ -432,7 +445,7 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   constexpr int CH = TB / 1024;  // 1 KB copies per tensor tile
   constexpr int CPR = D / 8;     // 16-byte chunks per row
   static_assert(CH <= NW, "a wave copies at most one 1 KB chunk of a tensor tile");
-  constexpr int STAGE = 4 * TB + 256;  // [Q "k" | Q "v" | dA "k" | dA "v" | lse, D of the 32 rows]
+  constexpr int STAGE = 2 * TB + 256;  // [Q | dA (both ways) | lse, D of the 32 rows]
   static_assert(STAGE % 256 == 0 && TB % 256 == 0, "tile bases leave the row's chunk bits free");
   constexpr int PSLOT = 2 * 1024;      // one tile's P of one P wave: 64 lanes x 2 x 16 bytes
   constexpr int PBASE = 4 * STAGE;
@@ -477,18 +490,19 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
     }
   }
 
-  // Copies.  Wave w < CH moves 1 KB chunk w of every tensor tile: the lane's
-  // 16 bytes go to destination row cr, chunk cc, and come from source chunk
-  // cc ^ swizzle(cr) (row cr, or the last row of a ragged tile).
+  // Copies.  Q and dA are each read as rows and transposed, so each tile is
+  // copied once in the both-ways layout.  Wave w < CH moves 1 KB chunk w of
+  // every tensor tile: the lane's 16 bytes go to destination row cr, chunk
+  // cc, and come from source chunk cc ^ swizzle(cr) (row cr, or the last row
+  // of a ragged tile).
   const bool copier = wave < CH;
   const int cr = (wave * 64 + lane) / CPR, cc = lane % CPR;
   const uint32_t qst = (uint32_t)a.q.st, ast = (uint32_t)(a.Hq * D);  // element strides (< 2^24)
-  const int swk = k_swizzle<D>(cr), swv = v_swizzle<D>(cr);
-  auto src_off = [&](int srow, uint32_t st, int sw) {
-    return ((uint32_t)srow * st + (uint32_t)((cc ^ sw) * 8)) * 2u;
+  const int swu = u_swizzle<D>(cr);
+  auto src_off = [&](int srow, uint32_t st) {
+    return ((uint32_t)srow * st + (uint32_t)((cc ^ swu) * 8)) * 2u;
   };
-  const uint32_t o_qk = src_off(cr, qst, swk), o_qv = src_off(cr, qst, swv);
-  const uint32_t o_ak = src_off(cr, ast, swk), o_av = src_off(cr, ast, swv);
+  const uint32_t o_q = src_off(cr, qst), o_a = src_off(cr, ast);
   const uint16_t* qg = (const uint16_t*)a.q.p + b * a.q.sb + (int64_t)g * G * a.q.sh;
   const uint16_t* ag = a.dA + (int64_t)b * T * a.Hq * D + (int64_t)g * G * D;
   const float* lg = a.lsew + ((int64_t)b * a.Hq + g * G) * a.Tp;
@@ -521,23 +535,19 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
       iss_l += a.Tp;
     }
     if (copier) {
-      uint32_t oqk = o_qk, oqv = o_qv, oak = o_ak, oav = o_av;
+      uint32_t oq = o_q, oa = o_a;
       if (i0 + kBT > T) {  // ragged last row tile: rows past T repeat row T - 1
         const int rr = min(cr, T - 1 - i0);
-        oqk = src_off(rr, qst, swk);
-        oqv = src_off(rr, qst, swv);
-        oak = src_off(rr, ast, swk);
-        oav = src_off(rr, ast, swv);
+        oq = src_off(rr, qst);
+        oa = src_off(rr, ast);
       }
       const uint32_t dst = st + wave * 1024;
-      dma16_sbase(qp, oqk, dst);
-      dma16_sbase(qp, oqv, dst + TB);
-      dma16_sbase(ap, oak, dst + 2 * TB);
-      dma16_sbase(ap, oav, dst + 3 * TB);
+      dma16_sbase(qp, oq, dst);
+      dma16_sbase(ap, oa, dst + TB);
     }
     // the 32 rows' lse and D (padded arrays: always in bounds), 8 lanes x 16 B each
-    if (wave == NW - 2 && lane < 8) dma16_sbase(lg + ro, lane * 16, st + 4 * TB);
-    if (wave == NW - 1 && lane < 8) dma16_sbase(dg + ro, lane * 16, st + 4 * TB + 128);
+    if (wave == NW - 2 && lane < 8) dma16_sbase(lg + ro, lane * 16, st + 2 * TB);
+    if (wave == NW - 1 && lane < 8) dma16_sbase(dg + ro, lane * 16, st + 2 * TB + 128);
   };
   issue(0);
   issue(1);
@@ -545,8 +555,9 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   // Row reads of A operands X[row li][16 ks + 8 hg ..]: chunk (2 ks + hg) ^
   // swizzle(li) = 2 ks ^ (hg ^ swizzle(li)); tile bases are multiples of 256,
   // so the read address is (tile base + rxs) ^ 32 ks.
-  const uint32_t rxs = (uint32_t)(li * RB + ((hg ^ k_swizzle<D>(li)) << 4));
-  TrBases<D> tb;
+  const uint32_t rxs = (uint32_t)(li * RB + ((hg ^ u_swizzle<D>(li)) << 4));
+  using TrB = TrBases<D, true>;
+  TrB tb;
   tb.init(lane);
   const float sl2 = a.sl2;
   // P exchange: the P wave of key block kb writes tile t's P at
@@ -561,34 +572,35 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   // Per-tile LDS bases, opaque to the compiler: every read below is one of
   // them plus an immediate offset (or XOR a constant); otherwise the
   // compiler hoists each "lane base + constant" into a register of its own.
-  auto bases = [&](int stage, uint32_t& qrow, uint32_t& arow, uint32_t& rowst, uint32_t (&tbase)[TrBases<D>::NV],
+  auto bases = [&](int stage, uint32_t& qrow, uint32_t& arow, uint32_t& rowst, uint32_t (&tbase)[TrB::NV],
                    uint32_t region) {
     const uint32_t sb = lds0 + stage * STAGE;
     qrow = sb + rxs;
-    arow = sb + 2 * TB + rxs;
-    rowst = sb + 4 * TB + 16 * hg;
+    arow = sb + TB + rxs;
+    rowst = sb + 2 * TB + 16 * hg;
 #pragma unroll
-    for (int v = 0; v < TrBases<D>::NV; ++v) tbase[v] = sb + region + tb.b[v];
+    for (int v = 0; v < TrB::NV; ++v) tbase[v] = sb + region + tb.b[v];
     asm volatile("" : "+v"(qrow), "+v"(arow), "+v"(rowst));
 #pragma unroll
-    for (int v = 0; v < TrBases<D>::NV; ++v) asm volatile("" : "+v"(tbase[v]));
+    for (int v = 0; v < TrB::NV; ++v) asm volatile("" : "+v"(tbase[v]));
   };
   // A += X^T Y over the tile's 32 rows (X^T by transpose reads from tbase, Y the bf16 B operand)
-  auto accumulate = [&](const uint32_t (&tbase)[TrBases<D>::NV], const bf16x8 (&y)[2]) {
+  auto accumulate = [&](const uint32_t (&tbase)[TrB::NV], const bf16x8 (&y)[2]) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const uint32_t q = tbase[cb % TrBases<D>::NV] + 16 * kk * RB + cb * 64;
-        acc[cb] = mfma32x32x16(join_bf16x8(tr_read(q), tr_read(q + 8 * RB)), y[kk], acc[cb]);
+        const bf16x8 xa = join_bf16x8(tr_read(tbase[TrB::src(cb, 0)] + TrB::off(cb, kk, 0)),
+                                      tr_read(tbase[TrB::src(cb, 1)] + TrB::off(cb, kk, 1)));
+        acc[cb] = mfma32x32x16(xa, y[kk], acc[cb]);
       }
   };
 
   // ---- the P wave ----
   // phase 1 of a tile: P (bf16, registers) and its copy in LDS
   auto p_phase1 = [&](int stage, int i0, int t, bf16x8 (&pk)[2]) {
-    uint32_t qrow, arow, rowst, tbase[TrBases<D>::NV];
-    bases(stage, qrow, arow, rowst, tbase, 3 * TB);
+    uint32_t qrow, arow, rowst, tbase[TrB::NV];
+    bases(stage, qrow, arow, rowst, tbase, TB);
     pk[0] = pk[1] = bf16x8{};
     if (i0 >= j0w) {  // (else: rows before this wave's keys, or an inactive wave)
       bf16x8 qa[KS];
@@ -638,16 +650,16 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
     *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pw + 1024) = pk[1];
   };
   auto p_phase2 = [&](int stage, const bf16x8 (&pk)[2]) {
-    uint32_t qrow, arow, rowst, tbase[TrBases<D>::NV];
-    bases(stage, qrow, arow, rowst, tbase, 3 * TB);
+    uint32_t qrow, arow, rowst, tbase[TrB::NV];
+    bases(stage, qrow, arow, rowst, tbase, TB);
     accumulate(tbase, pk);  // dV^T += dA^T P
   };
 
   // ---- the dS wave ----
   // phase 1 of a tile: D - dP in registers
   auto s_phase1 = [&](int stage, int i0, f32x16& dp) {
-    uint32_t qrow, arow, rowst, tbase[TrBases<D>::NV];
-    bases(stage, qrow, arow, rowst, tbase, TB);
+    uint32_t qrow, arow, rowst, tbase[TrB::NV];
+    bases(stage, qrow, arow, rowst, tbase, 0);
     if (i0 >= j0w) {
       f32x4 dq4[4];
 #pragma unroll
@@ -673,8 +685,8 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   };
   // phase 2 of a tile: -dS = P (D - dP), then -dK^T += Q^T (-dS)
   auto s_phase2 = [&](int stage, int t, const f32x16& dp) {
-    uint32_t qrow, arow, rowst, tbase[TrBases<D>::NV];
-    bases(stage, qrow, arow, rowst, tbase, TB);
+    uint32_t qrow, arow, rowst, tbase[TrB::NV];
+    bases(stage, qrow, arow, rowst, tbase, 0);
     const uint32_t pr_ = pbase + t * PSLOT;
     const uint4 p0 = as_u4(*(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)pr_);
     const uint4 p1 = as_u4(*(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(pr_ + 1024));
@@ -928,8 +940,8 @@ __device__ __forceinline__ void bwd_v1_lam_body(const V1BwdArgs& a, float* part)
 // once.
 template <int D>
 struct V1DkCfg {
-  // [Q "k" | Q "v" | dA "k" | lse, D], the stage a multiple of a dA row (2 DV bytes)
-  static constexpr int STAGE = 2 * TileDma<D>::BYTES + TileDma<2 * D>::BYTES + 512;
+  // [Q (both ways) | dA (rows) | lse, D], the stage a multiple of a dA row (2 DV bytes)
+  static constexpr int STAGE = TileDma<D>::BYTES + TileDma<2 * D>::BYTES + 512;
   static constexpr int SMEM = 2 * STAGE;
 };
 template <int D>
@@ -984,36 +996,35 @@ __device__ __forceinline__ void bwd_v1_dk_body(const V1BwdArgs& a, int bid, unsi
   const float* lsw = a.lsew[m] + ((int64_t)b * a.H + h) * a.Tp;
   const float* dw = a.Dw[m] + ((int64_t)b * a.H + h) * a.Tp;
   const int64_t ast = (int64_t)a.H * DV;
-  TileCopy<D, kNW> cq, cqv;
+  // Q is read as rows (S = Q K^T) and transposed (dK += dS^T Q): one copy in
+  // the both-ways layout; dA as rows only.
+  TileCopy<D, kNW> cq;
   TileCopy<DV, kNW> ca;
-  cq.init(tq.st, false, wave, lane);
-  cqv.init(tq.st, true, wave, lane);
-  ca.init(ast, false, wave, lane);
+  cq.init(tq.st, kBothLayout, wave, lane);
+  ca.init(ast, kRowLayout, wave, lane);
   auto issue = [&](int it, int stage) {
     const int i0 = it_row0(it);
     const uint32_t st = lds0 + stage * STAGE;
     if (i0 + kBT > T) {  // ragged last row tile
-      Dma::issue(qp, tq.st, i0, T, false, st, wave, lane);
-      Dma::issue(qp, tq.st, i0, T, true, st + TB, wave, lane);
-      DmaV::issue(ap, ast, i0, T, false, st + 2 * TB, wave, lane);
+      Dma::issue(qp, tq.st, i0, T, kBothLayout, st, wave, lane);
+      DmaV::issue(ap, ast, i0, T, kRowLayout, st + TB, wave, lane);
     } else {
-      const uint16_t* qr = qp + (int64_t)i0 * tq.st;
-      cq.issue(qr, st, wave);
-      cqv.issue(qr, st + TB, wave);
-      ca.issue(ap + (int64_t)i0 * ast, st + 2 * TB, wave);
+      cq.issue(qp + (int64_t)i0 * tq.st, st, wave);
+      ca.issue(ap + (int64_t)i0 * ast, st + TB, wave);
     }
     // the 32 rows' lse and D (padded arrays: always in bounds), 8 lanes x 16 B each
-    if (wave == kNW - 2 && lane < 8) dma16_sbase(lsw + i0, lane * 16, st + 2 * TB + TBV);
-    if (wave == kNW - 1 && lane < 8) dma16_sbase(dw + i0, lane * 16, st + 2 * TB + TBV + 128);
+    if (wave == kNW - 2 && lane < 8) dma16_sbase(lsw + i0, lane * 16, st + TB + TBV);
+    if (wave == kNW - 1 && lane < 8) dma16_sbase(dw + i0, lane * 16, st + TB + TBV + 128);
   };
   issue(0, 0);
 
   // Row reads: chunk (2 ks + hg) ^ swizzle(li) = 2 ks ^ (hg ^ swizzle(li)),
   // so the address is (tile base + lane part) ^ 32 ks (Q rows of 2D bytes, dA
   // rows of 2 DV bytes).
-  const uint32_t qxs = (uint32_t)(li * (2 * D) + ((hg ^ k_swizzle<D>(li)) << 4));
+  const uint32_t qxs = (uint32_t)(li * (2 * D) + ((hg ^ u_swizzle<D>(li)) << 4));
   const uint32_t axs = (uint32_t)(li * (2 * DV) + ((hg ^ k_swizzle<DV>(li)) << 4));
-  TrBases<D> tb;
+  using TrB = TrBases<D, true>;
+  TrB tb;
   tb.init(lane);
   const float sl2 = a.sl2;
   f32x16 acc[CB];  // -dK^T [c][key]
@@ -1029,13 +1040,13 @@ __device__ __forceinline__ void bwd_v1_dk_body(const V1BwdArgs& a, int bid, unsi
     if (it + 1 < nit) issue(it + 1, stage ^ 1);
     const int i0 = it_row0(it);
     const uint32_t st = lds0 + stage * STAGE;
-    uint32_t qrow = st + qxs, arow = st + 2 * TB + axs, rowst = st + 2 * TB + TBV + 16 * hg;
-    uint32_t tbase[TrBases<D>::NV];
+    uint32_t qrow = st + qxs, arow = st + TB + axs, rowst = st + TB + TBV + 16 * hg;
+    uint32_t tbase[TrB::NV];
 #pragma unroll
-    for (int v = 0; v < TrBases<D>::NV; ++v) tbase[v] = st + TB + tb.b[v];
+    for (int v = 0; v < TrB::NV; ++v) tbase[v] = st + tb.b[v];
     asm volatile("" : "+v"(qrow), "+v"(arow), "+v"(rowst));
 #pragma unroll
-    for (int v = 0; v < TrBases<D>::NV; ++v) asm volatile("" : "+v"(tbase[v]));
+    for (int v = 0; v < TrB::NV; ++v) asm volatile("" : "+v"(tbase[v]));
     bf16x8 xk[2] = {};
     if (i0 >= j0w) {  // (else: rows before this wave's keys, or an inactive wave)
       // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
@@ -1095,8 +1106,9 @@ __device__ __forceinline__ void bwd_v1_dk_body(const V1BwdArgs& a, int bid, unsi
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const uint32_t q = tbase[cb % TrBases<D>::NV] + 16 * kk * (2 * D) + cb * 64;
-        acc[cb] = mfma32x32x16(join_bf16x8(tr_read(q), tr_read(q + 8 * (2 * D))), xk[kk], acc[cb]);
+        const bf16x8 qa = join_bf16x8(tr_read(tbase[TrB::src(cb, 0)] + TrB::off(cb, kk, 0)),
+                                      tr_read(tbase[TrB::src(cb, 1)] + TrB::off(cb, kk, 1)));
+        acc[cb] = mfma32x32x16(qa, xk[kk], acc[cb]);
       }
   }
   if (!active || key >= T) return;
@@ -1167,8 +1179,8 @@ __device__ __forceinline__ void bwd_v1_dv_body(const V1BwdArgs& a, int bid, unsi
     const uint16_t* qp = (const uint16_t*)a.q[m].p + b * a.q[m].sb + h * a.q[m].sh;
     const uint16_t* ap = a.dA[m] + ((int64_t)b * T * a.H + h) * DV;
     const uint32_t st = lds0 + stage * STAGE;
-    Dma::issue(qp, a.q[m].st, i0, T, false, st, wave, lane);
-    DmaV::issue(ap, (int64_t)a.H * DV, i0, T, true, st + TB, wave, lane);
+    Dma::issue(qp, a.q[m].st, i0, T, kRowLayout, st, wave, lane);
+    DmaV::issue(ap, (int64_t)a.H * DV, i0, T, kTransLayout, st + TB, wave, lane);
     if (wave == kNW - 1 && lane < 8)
       dma16_sbase(a.lsew[m] + ((int64_t)b * a.H + h) * a.Tp + i0, lane * 16, st + TB + TBV);
   };

@@ -84,5 +84,25 @@ template <int DV>
 __device__ __forceinline__ int v_swizzle(int r) {
   return (DV >= 128 ? 4 : 2) * (r & 3);
 }
+// One layout serving both read forms, for a tile that is read as rows and
+// transposed (d = 64 or 128): the swizzle is a bijection on r mod 16 (so the
+// 16 rows of a ds_read_b128 pass hit distinct chunks), gives each aligned
+// group of 4 rows distinct bits 2-3 (d = 128; bit 2 between rows 2 apart at
+// d = 64) (so a transpose read's 4 rows x 64 bytes per 32 lanes hit distinct
+// banks), and satisfies u(r + 8) = u(r) ^ 4, u(r + 16) = u(r), so the
+// transpose read 8 rows further down lands in column block cb ^ 1 of the
+// same base.  Bits: r2, r1, r1 ^ r3 (and r0 at d = 128).  Checked
+// conflict-free for both forms by a bank simulation of these kernels'
+// addresses.
+template <int D>
+__device__ __forceinline__ int u_swizzle(int r) {
+  const int v = ((r >> 2) & 1) | (((r >> 1) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
+  return D >= 128 ? v | ((r & 1) << 3) : v;
+}
+enum TileLayout { kRowLayout = 0, kTransLayout = 1, kBothLayout = 2 };
+template <int D>
+__device__ __forceinline__ int tile_swizzle(int layout, int r) {
+  return layout == kRowLayout ? k_swizzle<D>(r) : layout == kTransLayout ? v_swizzle<D>(r) : u_swizzle<D>(r);
+}
 
 }  // namespace da
