@@ -649,6 +649,66 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
     *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)pw = pk[0];
     *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pw + 1024) = pk[1];
   };
+  // phase 1 of both tiles of a period (the same row tile: G is even), with
+  // the common case -- rows strictly after this wave's keys, none past T:
+  // no mask -- as one straight-line block, so the exponentials of tile a
+  // run under the score MFMAs of tile b.
+  auto p_phase1_pair = [&](int sa, int sb, int i0, bf16x8 (&pa)[2], bf16x8 (&pb)[2]) {
+    if (!(i0 > j0w && i0 + kBT <= T)) {
+      p_phase1(sa, i0, 0, pa);
+      p_phase1(sb, i0, 1, pb);
+      return;
+    }
+    uint32_t qrow[2], arow_, rowst[2], tbase_[TrB::NV];
+    bases(sa, qrow[0], arow_, rowst[0], tbase_, TB);
+    bases(sb, qrow[1], arow_, rowst[1], tbase_, TB);
+    f32x16 s[2];
+    f32x4 lq[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 qa[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qa[ks] = lds_read16(qrow[t] ^ (32u * ks));
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        lq[t][q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst[t] + 32 * q4);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s[t] = mfma32x32x16(qa[ks], kv[ks], s[t]);  // S = Q K^T
+    }
+    bf16x8* out[2] = {pa, pb};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x8 e0, e1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(fmaf(s[t][r], sl2, -lq[t][r >> 2][r & 3]));
+        if (r < 8) e0[r] = pr; else e1[r - 8] = pr;
+      }
+      out[t][0] = cvt_bf16x8(e0);
+      out[t][1] = cvt_bf16x8(e1);
+    }
+    // reads of tile a, its score MFMAs with the reads of tile b, then the
+    // score MFMAs of tile b with the exponentials of tile a
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t pw = pbase + t * PSLOT;
+      *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)pw = out[t][0];
+      *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pw + 1024) = out[t][1];
+    }
+  };
   auto p_phase2 = [&](int stage, const bf16x8 (&pk)[2]) {
     uint32_t qrow, arow, rowst, tbase[TrB::NV];
     bases(stage, qrow, arow, rowst, tbase, TB);
@@ -727,8 +787,7 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
       }
       const int i0a = next_row0(), i0b = next_row0();
       bf16x8 pa[2], pb[2];
-      p_phase1(2 * sp, i0a, 0, pa);
-      p_phase1(2 * sp + 1, i0b, 1, pb);
+      p_phase1_pair(2 * sp, 2 * sp + 1, i0a, pa, pb);  // (i0b == i0a: G is even)
       __syncthreads();  // P of both tiles in LDS
       p_phase2(2 * sp, pa);
       p_phase2(2 * sp + 1, pb);
