@@ -24,11 +24,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
-# Per-source additions.  Decode: MFMA results in VGPRs.  With one wave per
-# SIMD allowed, the compiler otherwise picks the AGPR form for the copy-path
-# kernels and moves the 64 output accumulators between AGPRs and VGPRs on
-# every step.
-EXTRA = {"decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+# Per-source additions (none at present: every kernel's launch bounds allow
+# at least two waves per SIMD, so the compiler keeps MFMA results in VGPRs).
+EXTRA: dict[str, list[str]] = {}
 
 
 def _compile(src: str) -> Path:

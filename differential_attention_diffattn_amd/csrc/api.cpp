@@ -191,7 +191,7 @@ da_status decode_impl(int softmax1, int dtype, int B, int L, int nq, int Hq, int
   } else if (kc.st >= kMaxTokenStride || vc.st >= kMaxTokenStride) {
     return DA_E_UNSUPPORTED;  // rows of a 32-token block are addressed with 32-bit byte offsets
   }
-  const int max_chunk = pg ? da::kPagedMaxChunk : 2048;
+  const int max_chunk = pg ? da::kPagedMaxChunk : da::kDenseMaxChunk;
   const size_t need = decode_ws_bytes(B, L, nq, Hq, Hkv, d, max_chunk, max_splits);
   if (use_scratch) {  // every argument checked: now the static scratch of this device
     if (need > kScratchBytes) return DA_E_SCRATCH;
@@ -508,11 +508,11 @@ static da_status v1_bwd_impl(int dtype, int B, int H, int T, int d, da_in q1, da
 }
 
 size_t diffattn_v2_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int d) {
-  return decode_ws_bytes(B, L, 1, Hq, Hkv, d, 2048);
+  return decode_ws_bytes(B, L, 1, Hq, Hkv, d, da::kDenseMaxChunk);
 }
 
 size_t diffattn_v2_decode_multi_workspace_bytes(int B, int L, int nq, int Hq, int Hkv, int d) {
-  return decode_ws_bytes(B, L, nq, Hq, Hkv, d, 2048);
+  return decode_ws_bytes(B, L, nq, Hq, Hkv, d, da::kDenseMaxChunk);
 }
 
 size_t diffattn_v2_decode_paged_workspace_bytes(int B, int max_len, int nq, int Hq, int Hkv, int d) {

@@ -168,8 +168,12 @@ struct DecodeSplit {
 };
 DecodeSplit decode_split(int B, int L, int Hkv, int max_chunk = 2048, int max_splits = 0x7fffffff);
 #ifndef DA_PAGED_CHUNK
-#define DA_PAGED_CHUNK 2048
+#define DA_PAGED_CHUNK 4096
 #endif
 constexpr int kPagedMaxChunk = DA_PAGED_CHUNK;  // paged decode: tokens per split at most
+#ifndef DA_DENSE_CHUNK
+#define DA_DENSE_CHUNK 4096
+#endif
+constexpr int kDenseMaxChunk = DA_DENSE_CHUNK;  // dense decode: tokens per split at most
 
 }  // namespace da

@@ -111,8 +111,8 @@ def test_v2_validation(lib):
 
 def test_decode_workspace_query(lib):
     n = lib.diffattn_v2_decode_workspace_bytes(64, 32768, 64, 8, 128)
-    # 64 batch x 8 groups x 16 splits x 8 heads x (128 + 2) floats
-    assert n == 64 * 8 * 16 * 8 * 130 * 4
+    # 64 batch x 8 groups x 8 splits (chunks of at most 4096 tokens) x 8 heads x (128 + 2) floats
+    assert n == 64 * 8 * 8 * 8 * 130 * 4
     assert lib.diffattn_v2_decode_workspace_bytes(1, 1, 2, 1, 128) > 0
     assert lib.diffattn_v2_decode_workspace_bytes(0, 10, 8, 2, 128) == 0
     assert lib.diffattn_v2_decode_workspace_bytes(1, 10, 6, 2, 128) == 0
