@@ -185,11 +185,6 @@ struct TrBases {
   static constexpr int off(int cb, int kk, int h) {
     return ((BOTH && h) ? (cb ^ 1) : cb) * 64 + (16 * kk + 8 * h) * (D * 2);
   }
-  // the bf16 A operand X^T[c of column block cb][rows of k-chunk kk]
-  template <int CB_, int KK>
-  static __device__ __forceinline__ bf16x8 read(const uint32_t (&tbase)[NV]) {
-    return join_bf16x8(tr_read(tbase[src(CB_, 0)] + off(CB_, KK, 0)), tr_read(tbase[src(CB_, 1)] + off(CB_, KK, 1)));
-  }
 };
 
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -91,9 +91,9 @@ __device__ __forceinline__ int v_swizzle(int r) {
 // d = 64) (so a transpose read's 4 rows x 64 bytes per 32 lanes hit distinct
 // banks), and satisfies u(r + 8) = u(r) ^ 4, u(r + 16) = u(r), so the
 // transpose read 8 rows further down lands in column block cb ^ 1 of the
-// same base.  Bits: r2, r1, r1 ^ r3 (and r0 at d = 128).  Checked
-// conflict-free for both forms by a bank simulation of these kernels'
-// addresses.
+// same base.  Bits: r2, r1, r1 ^ r3 (and r0 at d = 128).  The bank behaviour
+// of both read forms and the operands they deliver are checked on the CPU
+// (tests/test_tile_layout.py).
 template <int D>
 __device__ __forceinline__ int u_swizzle(int r) {
   const int v = ((r >> 2) & 1) | (((r >> 1) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
