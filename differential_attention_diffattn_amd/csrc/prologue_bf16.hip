@@ -126,8 +126,8 @@ __global__ void __launch_bounds__(kProjWaves * 64) lambda_proj_kernel(const LamP
 // Streaming form for dm a multiple of 256: a workgroup (4 waves) owns 32
 // tokens x 32 pairs and walks dm in 256-wide chunks.  Each chunk's x rows
 // (32 x 512 B) and w rows (32 x 512 B) go HBM -> LDS by global_load_lds, two
-// whole rows per 1 KB instruction (fully coalesced), into a 4-stage ring with
-// three chunks in flight (the stream is latency-bound otherwise); 16-byte
+// whole rows per 1 KB instruction (fully coalesced), into a 3-stage ring with
+// two chunks in flight (three or four in flight measured 1-3% slower); 16-byte
 // chunk c of a row lands at chunk c ^ (row & 15), so the MFMA operand reads
 // (ds_read_b128, 16 rows per pass) hit distinct banks.  Wave w runs k-steps
 // 4w .. 4w+3 of each chunk; the four partial tiles are added in a fixed order
@@ -135,11 +135,18 @@ __global__ void __launch_bounds__(kProjWaves * 64) lambda_proj_kernel(const LamP
 // an XCD starts at chunk k mod n): when every workgroup read the same columns
 // at the same time, the rows' 8 KB stride kept the reads on a few memory
 // channels and the kernel ran at two thirds of the rate it reaches rotated.
-constexpr int kPsWaves = 4, kPsChunk = 256, kPsStages = 4;  // dm per chunk
+#ifndef DA_PS_STAGES
+#define DA_PS_STAGES 3  // ring depth of the streaming projection (stages - 1 chunks in flight)
+#endif
+#ifndef DA_PS_NT
+#define DA_PS_NT 0  // x copies with the non-temporal policy
+#endif
+constexpr int kPsWaves = 4, kPsChunk = 256, kPsStages = DA_PS_STAGES;  // dm per chunk
 constexpr int kPsRowBytes = kPsChunk * 2;    // 512 B
 constexpr int kPsTile = 32 * kPsRowBytes;    // 16 KB: one operand tile of a chunk
 constexpr int kPsStage = 2 * kPsTile;        // x tile, w tile
 constexpr int kPsCopies = 2 * 16 / kPsWaves; // 1 KB copies per wave per chunk (8)
+static_assert(kPsStages >= 2 && kPsStages <= 5 && kPsStages * kPsStage <= 160 * 1024, "projection ring");
 
 __global__ void __launch_bounds__(kPsWaves * 64) lambda_proj_stream_kernel(const LamProjArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kPsStages * kPsStage];
@@ -181,7 +188,10 @@ __global__ void __launch_bounds__(kPsWaves * 64) lambda_proj_stream_kernel(const
       const int rp = 2 * (4 * wave + i);
       const int chr = ch + rot < nch ? ch + rot : ch + rot - nch;  // chunk of the rotated order
       const uint32_t off = (uint32_t)chr * kPsRowBytes + (uint32_t)((li ^ ((rp + hg) & 15)) << 4);
-      dma16_sbase(xb[i], off + xd[i], st + rp * kPsRowBytes);
+      if (DA_PS_NT)
+        dma16_sbase_nt(xb[i], off + xd[i], st + rp * kPsRowBytes);
+      else
+        dma16_sbase(xb[i], off + xd[i], st + rp * kPsRowBytes);
       dma16_sbase(wb[i], off + wd[i], st + kPsTile + rp * kPsRowBytes);
     }
   };
@@ -194,7 +204,9 @@ __global__ void __launch_bounds__(kPsWaves * 64) lambda_proj_stream_kernel(const
     const int stage = ch % kPsStages;
     // this wave's copies of chunk ch landed (later chunks may stay in flight)
     const int later = min(kPsStages - 2, nch - 1 - ch);
-    if (later >= 2)
+    if (later >= 3)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kPsCopies) : "memory");
+    else if (later == 2)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPsCopies) : "memory");
     else if (later == 1)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPsCopies) : "memory");
