@@ -447,8 +447,8 @@ static da_status v2_bwd_impl(int dtype, int B, int T, int Hq, int Hkv, int d, da
 
 // DIFF V1 backward: workspace regions (each 256-byte aligned).
 struct V1BwdWs {
-  size_t dA, rows, lam;  // bytes of one map's d a; of one [B][H][Tp] fp32 array; of the row terms of d lambda
-  size_t total() const { return 2 * dA + 4 * rows + lam; }
+  size_t dA, rows, lam;  // bytes of dD; of one [B][H][Tp] fp32 array; of the row terms of d lambda
+  size_t total() const { return dA + 4 * rows + lam; }
 };
 static V1BwdWs v1_bwd_ws(int B, int H, int T, int d) {
   V1BwdWs w;
@@ -480,7 +480,7 @@ static da_status v1_bwd_impl(int dtype, int B, int H, int T, int d, da_in q1, da
   const V1BwdWs w = v1_bwd_ws(B, H, T, d);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.total()) return DA_E_WORKSPACE;
   const int qt = (T + 127) / 128;
-  if (!grid_fits((long long)B * H * 2 * qt) || !grid_fits(((long long)B * da::backward_padded_rows(T) * H + 15) / 16))
+  if (!grid_fits(1 + 6LL * B * H * qt) || !grid_fits(((long long)B * da::backward_padded_rows(T) * H + 15) / 16))
     return DA_E_SHAPE;
 
   da::V1BwdArgs a{};
@@ -491,9 +491,8 @@ static da_status v1_bwd_impl(int dtype, int B, int H, int T, int d, da_in q1, da
   a.dq[0] = tout(dq1), a.dq[1] = tout(dq2), a.dk[0] = tout(dk1), a.dk[1] = tout(dk2), a.dv = tout(dv);
   a.dlq1 = dlam_q1, a.dlk1 = dlam_k1, a.dlq2 = dlam_q2, a.dlk2 = dlam_k2;
   char* p = (char*)workspace;
-  a.dA[0] = (uint16_t*)p;
-  a.dA[1] = (uint16_t*)(p + w.dA);
-  p += 2 * w.dA;
+  a.dD = (uint16_t*)p;
+  p += w.dA;
   for (int m = 0; m < 2; ++m) {
     a.Dw[m] = (float*)(p + (2 * m) * w.rows);
     a.lsew[m] = (float*)(p + (2 * m + 1) * w.rows);

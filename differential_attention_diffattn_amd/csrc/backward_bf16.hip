@@ -219,7 +219,8 @@ struct DqCfg {
   static constexpr int SMEM = 2 * STAGE;
 };
 // `bid`: the workgroup's index in the dQ grid order; `smem`: DqCfg::SMEM bytes
-// of LDS, 1 KB aligned.
+// of LDS, 1 KB aligned; `tid`: the thread's index among the kNW * 64 threads
+// that run this body (every one of them reaches the same barriers).
 //
 // As in the dK/dV kernel, the accumulators take one path through the loop
 // body (key tiles after a wave's rows skip the scores and accumulate zeros),
@@ -228,7 +229,7 @@ struct DqCfg {
 // and the accumulator starts at D, so the MFMAs leave D - dP, P (D - dP) =
 // -dS, and dQ is negated when stored.
 template <int D, int DV>
-__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned char* smem) {
+__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned char* smem, int tid) {
   constexpr int KS = D / 16, KSV = DV / 16, CB = D / 32;
   constexpr int KM = KS > KSV ? KS : KSV;
   using Dma = TileDma<D>;
@@ -239,7 +240,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
                 "tile bases leave a row's chunk bits free");
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, hg = lane >> 5;
   const int T = a.T, BM = 32 * kNW;
   const int tiles = (T + BM - 1) / BM;
@@ -407,7 +408,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
 template <int D, int DV>
 __global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[DqCfg<D, DV>::SMEM];
-  bwd_dq_body<D, DV>(a, blockIdx.x, smem);
+  bwd_dq_body<D, DV>(a, blockIdx.x, smem, threadIdx.x);
 }
 
 // ---- dK, dV ------------------------------------------------------------------
@@ -846,10 +847,29 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
 //   da_2 = -lam dD,  dlam = -sum over rows of <dD, a_2>, and per map the
 //   softmax-attention gradients (dv summed over both maps); the lambda
 //   vectors get dlam times the derivative of exp(<lq, lk>).
-// Kernels: a pre-pass per (b, token, head); then one grid holding the dlam
-// reduction (one workgroup, fixed order, writes the four vector gradients),
-// dQ of each map (the V2 dQ code with a 2d-wide v), dK of each map and dV
-// over both maps.
+// Since da_2 = c dD with c = -lam, both maps' softmax gradients come from the
+// one product G = dD v^T:  dS_1 = P_1 (G - E_1),  dS_2 = c P_2 (G - E_2)
+// with E_m = rowsum(dD * a_m), and dv = (P_1 + c P_2)^T dD is one product.
+// Kernels: a pre-pass per (b, token, head) writes dD, E_1, E_2 and the
+// padded lse rows; then one grid holds the dlam reduction (one workgroup,
+// fixed order, writes the four vector gradients), dQ of both maps (the V2
+// dQ code with a 2d-wide v, dD as d attn and c in the map-2 scale) and dK of
+// both maps with dv (four waves per 32-key block sharing S, G and P).
+
+// lam = exp(<lq1, lk1>) - exp(<lq2, lk2>) + lam_init, the same bits in every
+// wave that computes it (the pre-pass and the main grid)
+template <int D>
+__device__ __forceinline__ float v1_lambda(const V1BwdArgs& a) {
+  const int lane = threadIdx.x & 63;
+  float pa = 0.f, pb = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    const int c = lane + 64 * i;
+    pa += a.lq1[c] * a.lk1[c];
+    pb += a.lq2[c] * a.lk2[c];
+  }
+  return expf(wave_sum(pa)) - expf(wave_sum(pb)) + a.lam_init;
+}
 
 // Sixteen lanes per (b, t, h), t < Tp: each lane holds 2d/16 consecutive
 // channels (16-byte loads and stores), four items per wave with consecutive
@@ -858,15 +878,7 @@ template <int D>
 __global__ void __launch_bounds__(256) bwd_v1_pre_kernel(const V1BwdArgs a) {
   constexpr int DV = 2 * D, NV = DV / 128;  // 16-byte vectors (8 channels) per lane
   const int lane = threadIdx.x & 63, l16 = lane & 15;
-  // lambda from the vectors (D / 64 elements per lane), once per wave
-  float pa = 0.f, pb = 0.f;
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) {
-    const int c = lane + 64 * i;
-    pa += a.lq1[c] * a.lk1[c];
-    pb += a.lq2[c] * a.lk2[c];
-  }
-  const float lam = expf(wave_sum(pa)) - expf(wave_sum(pb)) + a.lam_init;
+  const float lam = v1_lambda<D>(a);  // once per wave
   const long long item = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);  // (b, t, h)
   if (item >= (long long)a.B * a.Tp * a.H) return;  // whole rows of 16 lanes
   const int h = (int)(item % a.H);
@@ -904,26 +916,23 @@ __global__ void __launch_bounds__(256) bwd_v1_pre_kernel(const V1BwdArgs a) {
   const float r = rsqrtf(row16_sum(ss) * (1.f / DV) + 1e-5f);
   const float pm = r * r * row16_sum(gd) * (1.f / DV);
   const float cr = (1.f - a.lam_init) * r;
-  uint16_t* d0 = a.dA[0] + (((int64_t)b * a.T + t) * a.H + h) * DV;
-  uint16_t* d1 = a.dA[1] + (((int64_t)b * a.T + t) * a.H + h) * DV;
+  uint16_t* d0 = a.dD + (((int64_t)b * a.T + t) * a.H + h) * DV;
   float s0 = 0.f, s1 = 0.f, sl = 0.f;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    uint32_t w0[4], w1[4];
+    uint32_t w0[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const float dA = cr * (elem(gv[v], e) - dd[v][e] * pm), dB = cr * (elem(gv[v], e + 1) - dd[v][e + 1] * pm);
       w0[e / 2] = pack_bf16x2(dA, dB);
-      w1[e / 2] = pack_bf16x2(-lam * dA, -lam * dB);
-      // D_m from the rounded d a_m the MFMAs see
-      const uint4 r0 = make_uint4(w0[e / 2], 0, 0, 0), r1 = make_uint4(w1[e / 2], 0, 0, 0);
+      // E_m from the rounded dD the MFMAs see
+      const uint4 r0 = make_uint4(w0[e / 2], 0, 0, 0);
       s0 += elem(r0, 0) * elem(xv0[v], e) + elem(r0, 1) * elem(xv0[v], e + 1);
-      s1 += elem(r1, 0) * elem(xv1[v], e) + elem(r1, 1) * elem(xv1[v], e + 1);
+      s1 += elem(r0, 0) * elem(xv1[v], e) + elem(r0, 1) * elem(xv1[v], e + 1);
       sl -= dA * elem(xv1[v], e) + dB * elem(xv1[v], e + 1);
     }
     const int c = 128 * v + 8 * l16;
     *(uint4*)(d0 + c) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
-    *(uint4*)(d1 + c) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
   }
   s0 = row16_sum(s0);
   s1 = row16_sum(s1);
@@ -983,192 +992,303 @@ __device__ __forceinline__ void bwd_v1_lam_body(const V1BwdArgs& a, float* part)
   }
 }
 
-// dK of one map: workgroup (b, h, map, 32 kNW keys), wave w owns keys
-// J0 + 32 w and loops over the row tiles at or after them (rows descending).
-// S = Q K^T and dP = dA V^T with K / V fragments of its keys in registers,
-// dS = P (dP - D), dK^T += Q^T dS with transpose reads of the Q tile.  As in
-// the V2 kernels: the V fragments are negated once and the dP accumulator
-// starts at D (so the MFMAs leave D - dP and the accumulator holds -dK^T),
-// masks apply only on the diagonal and ragged tiles, tiles of rows before
-// the wave's keys accumulate zeros, and copies use per-lane offsets computed
-// once.
-template <int D>
-struct V1DkCfg {
-  // [Q (both ways) | dA (rows) | lse, D], the stage a multiple of a dA row (2 DV bytes)
-  static constexpr int STAGE = TileDma<D>::BYTES + TileDma<2 * D>::BYTES + 512;
-  static constexpr int SMEM = 2 * STAGE;
+// dK of both maps and dv: workgroup (b, h, 32 NKB keys), four waves per
+// 32-key block kb (wave w: kb = w % NKB, role w / NKB), over the row tiles at
+// or after the keys, rows descending, one 32-row tile per step:
+//   role 0 / 1 (map m = role): S_m = Q_m K_m^T with K_m^T of its keys in
+//     registers, P_m (map 2: c P_2) in bf16 to LDS; after the barrier the
+//     other map's P from LDS, P_1 + c P_2, and the d-wide half m of
+//     dv^T += dD^T (P_1 + c P_2) by transpose reads of the dD tile;
+//   role 2 / 3 (half m): the half-m part of -G = -dD v^T (channels m d ..
+//     m d + d - 1 of dD rows, -v^T of its keys in registers) to LDS; after
+//     the barrier -G = both halves (added in one order by both waves),
+//     P_m (E_m - G) = -dS_m with P_m (c P_2 for map 2) from LDS, and
+//     -dK_m^T += Q_m^T (-dS_m) by transpose reads of the Q_m tile.
+// Each wave issues 2 d / 16 MFMAs per tile and each product is formed once
+// (S of each map, G, dv, dK of each map).  With two key blocks, roles 0 and
+// 2 (1 and 3) of one key block share a SIMD.  Q_1, Q_2 and dD are each read
+// as rows and transposed: one copy each in the both-ways layout.
+template <int D, int NKB>
+struct V1DkvCfg {
+  static constexpr int TB = TileDma<D>::BYTES;       // a Q_m tile (32 x d bf16)
+  static constexpr int TBD = TileDma<2 * D>::BYTES;  // the dD tile (32 x 2d)
+  // [Q_1 | Q_2 | dD | lse_1, lse_2, E_1, E_2 of the 32 rows]
+  static constexpr int STAGE = 2 * TB + TBD + 512;
+  static constexpr int PSLOT = 2048;  // a tile's P of one map: 64 lanes x 2 x 16 bytes
+  static constexpr int GSLOT = 4096;  // a half of -G: 64 lanes x 4 x 16 bytes
+  static constexpr int XKB = 2 * PSLOT + 2 * GSLOT;  // exchange slots of one key block
+  static constexpr int XBASE = 2 * STAGE;
+  static constexpr int SMEM = XBASE + NKB * XKB;
+  static_assert(STAGE % (4 * D) == 0 && TB % (4 * D) == 0, "tile bases leave a row's chunk bits free");
 };
-template <int D>
-__device__ __forceinline__ void bwd_v1_dk_body(const V1BwdArgs& a, int bid, unsigned char* smem) {
+template <int D, int NKB>
+__device__ __forceinline__ void bwd_v1_dkv_body(const V1BwdArgs& a, int bid, float c, unsigned char* smem) {
   constexpr int DV = 2 * D;
-  constexpr int KS = D / 16, KSV = DV / 16, CB = D / 32;
-  using Dma = TileDma<D>;
-  using DmaV = TileDma<DV>;
-  constexpr int TB = Dma::BYTES, TBV = DmaV::BYTES;
-  constexpr int STAGE = V1DkCfg<D>::STAGE;
-  static_assert(STAGE % (2 * DV) == 0 && TB % (2 * DV) == 0, "tile bases leave a row's chunk bits free");
+  constexpr int KS = D / 16, CB = D / 32;
+  constexpr int NW = 4 * NKB;
+  using Cfg = V1DkvCfg<D, NKB>;
+  constexpr int TB = Cfg::TB, STAGE = Cfg::STAGE, PSLOT = Cfg::PSLOT, GSLOT = Cfg::GSLOT;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, hg = lane >> 5;
-  const int T = a.T, BK = 32 * kNW;
-  const int units = a.B * a.H * 2;
-  const int unit = bid % units, kt = bid / units;  // low key tiles (most rows) first
-  const int m = unit & 1, bh = unit >> 1;
-  const int b = bh / a.H, h = bh % a.H;
-  const int J0 = kt * BK, j0w = J0 + 32 * wave;
+  const int kb = wave % NKB, role = wave / NKB, m = role & 1;
+  const bool pwave = role < 2;
+  const int T = a.T;
+  const int units = a.B * a.H;
+  const int unit = bid % units, kt = bid / units;  // key tiles, low ones (most rows) first
+  const int b = unit / a.H, h = unit % a.H;
+  const int J0 = kt * 32 * NKB, j0w = J0 + 32 * kb;
+  const int nrt = (T + kBT - 1) / kBT;
+  const int nit = nrt - J0 / kBT;  // row tiles from the last down to J0
+  if (nit <= 0) return;            // (keys past T: the whole workgroup)
   const bool active = j0w < T;
   const int key = j0w + li;
-  const int nrt = (T + kBT - 1) / kBT;
-  const int rt0 = J0 / kBT;
-  const int nit = nrt - rt0;
   auto it_row0 = [&](int it) { return (nrt - 1 - it) * kBT; };
 
-  const TIn& tq = a.q[m];
-  const TIn& tk = a.k[m];
-  bf16x8 kf[KS], vf[KSV];  // K^T and -V^T of this wave's keys
+  // B operands: K_m^T (role 0 / 1) or -v^T of half m (role 2 / 3) of this wave's keys
+  bf16x8 fr[KS];
   {
-    const uint16_t* kr = (const uint16_t*)tk.p + b * tk.sb + (int64_t)key * tk.st + h * tk.sh;
-    const uint16_t* vr = (const uint16_t*)a.v.p + b * a.v.sb + (int64_t)key * a.v.st + h * a.v.sh;
+    const TIn& t = pwave ? a.k[m] : a.v;
+    const uint16_t* r = (const uint16_t*)t.p + b * t.sb + (int64_t)key * t.st + h * t.sh + (pwave ? 0 : m * D);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      kf[ks] = as_bf16x8(key < T ? *(const uint4*)(kr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+      fr[ks] = as_bf16x8(key < T ? *(const uint4*)(r + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+    const uint32_t flip = pwave ? 0u : 0x80008000u;  // sign flip of every bf16 of v (exact)
 #pragma unroll
-    for (int ks = 0; ks < KSV; ++ks)
-      vf[ks] = as_bf16x8(key < T ? *(const uint4*)(vr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) retire(kf[ks]);
-#pragma unroll
-    for (int ks = 0; ks < KSV; ++ks) {
-      retire(vf[ks]);
-      const uint4 u = as_u4(vf[ks]);  // sign flip of every bf16 (exact)
-      vf[ks] = as_bf16x8(make_uint4(u.x ^ 0x80008000u, u.y ^ 0x80008000u, u.z ^ 0x80008000u, u.w ^ 0x80008000u));
+    for (int ks = 0; ks < KS; ++ks) {
+      retire(fr[ks]);
+      const uint4 u = as_u4(fr[ks]);
+      fr[ks] = as_bf16x8(make_uint4(u.x ^ flip, u.y ^ flip, u.z ^ flip, u.w ^ flip));
     }
   }
-  const uint16_t* qp = (const uint16_t*)tq.p + b * tq.sb + h * tq.sh;
-  const uint16_t* ap = a.dA[m] + ((int64_t)b * T * a.H + h) * DV;
-  const float* lsw = a.lsew[m] + ((int64_t)b * a.H + h) * a.Tp;
-  const float* dw = a.Dw[m] + ((int64_t)b * a.H + h) * a.Tp;
-  const int64_t ast = (int64_t)a.H * DV;
-  // Q is read as rows (S = Q K^T) and transposed (dK += dS^T Q): one copy in
-  // the both-ways layout; dA as rows only.
-  TileCopy<D, kNW> cq;
-  TileCopy<DV, kNW> ca;
-  cq.init(tq.st, kBothLayout, wave, lane);
-  ca.init(ast, kRowLayout, wave, lane);
+
+  // Copies: Q_1, Q_2 and dD tiles in the both-ways layout; the last four
+  // waves copy the rows' lse_1, lse_2, E_1, E_2 (padded arrays: always in
+  // bounds).
+  const uint16_t* qb0 = (const uint16_t*)a.q[0].p + b * a.q[0].sb + h * a.q[0].sh;
+  const uint16_t* qb1 = (const uint16_t*)a.q[1].p + b * a.q[1].sb + h * a.q[1].sh;
+  const uint16_t* db = a.dD + ((int64_t)b * T * a.H + h) * DV;
+  const int64_t dst_ = (int64_t)a.H * DV;
+  const int rw4 = wave - (NW - 4);  // 0..3 on the row copiers
+  const float* rowsrc = rw4 == 0 ? a.lsew[0] : rw4 == 1 ? a.lsew[1] : rw4 == 2 ? a.Dw[0] : a.Dw[1];
+  rowsrc += ((int64_t)b * a.H + h) * a.Tp;
+  TileCopy<D, NW> cq0, cq1;
+  TileCopy<DV, NW> cd;
+  cq0.init(a.q[0].st, kBothLayout, wave, lane);
+  cq1.init(a.q[1].st, kBothLayout, wave, lane);
+  cd.init(dst_, kBothLayout, wave, lane);
   auto issue = [&](int it, int stage) {
     const int i0 = it_row0(it);
     const uint32_t st = lds0 + stage * STAGE;
-    if (i0 + kBT > T) {  // ragged last row tile
-      Dma::issue(qp, tq.st, i0, T, kBothLayout, st, wave, lane);
-      DmaV::issue(ap, ast, i0, T, kRowLayout, st + TB, wave, lane);
+    if (i0 + kBT > T) {  // ragged last row tile: rows past T repeat row T - 1
+      TileDma<D, NW>::issue(qb0, a.q[0].st, i0, T, kBothLayout, st, wave, lane);
+      TileDma<D, NW>::issue(qb1, a.q[1].st, i0, T, kBothLayout, st + TB, wave, lane);
+      TileDma<DV, NW>::issue(db, dst_, i0, T, kBothLayout, st + 2 * TB, wave, lane);
     } else {
-      cq.issue(qp + (int64_t)i0 * tq.st, st, wave);
-      ca.issue(ap + (int64_t)i0 * ast, st + TB, wave);
+      cq0.issue(qb0 + (int64_t)i0 * a.q[0].st, st, wave);
+      cq1.issue(qb1 + (int64_t)i0 * a.q[1].st, st + TB, wave);
+      cd.issue(db + (int64_t)i0 * dst_, st + 2 * TB, wave);
     }
-    // the 32 rows' lse and D (padded arrays: always in bounds), 8 lanes x 16 B each
-    if (wave == kNW - 2 && lane < 8) dma16_sbase(lsw + i0, lane * 16, st + TB + TBV);
-    if (wave == kNW - 1 && lane < 8) dma16_sbase(dw + i0, lane * 16, st + TB + TBV + 128);
+    if (rw4 >= 0 && lane < 8) dma16_sbase(rowsrc + i0, lane * 16, st + 4 * TB + 128 * rw4);
   };
   issue(0, 0);
 
   // Row reads: chunk (2 ks + hg) ^ swizzle(li) = 2 ks ^ (hg ^ swizzle(li)),
-  // so the address is (tile base + lane part) ^ 32 ks (Q rows of 2D bytes, dA
-  // rows of 2 DV bytes).
+  // so the address is (tile base + lane part) ^ 32 ks; half m of a dD row
+  // starts at k-step m KS, i.e. XOR 32 m KS.
   const uint32_t qxs = (uint32_t)(li * (2 * D) + ((hg ^ u_swizzle<D>(li)) << 4));
-  const uint32_t axs = (uint32_t)(li * (2 * DV) + ((hg ^ k_swizzle<DV>(li)) << 4));
-  using TrB = TrBases<D, true>;
-  TrB tb;
-  tb.init(lane);
+  const uint32_t dxs = (uint32_t)(li * (2 * DV) + ((hg ^ u_swizzle<DV>(li)) << 4)) ^ (uint32_t)(32 * m * KS);
+  // exchange slots of this key block: P of map mm at pslot(mm), half mm of -G at gslot(mm)
+  const uint32_t xb = lds0 + Cfg::XBASE + kb * Cfg::XKB + lane * 16;
+  auto pslot = [&](int mm) { return xb + mm * PSLOT; };
+  auto gslot = [&](int mm) { return xb + 2 * PSLOT + mm * GSLOT; };
   const float sl2 = a.sl2;
-  f32x16 acc[CB];  // -dK^T [c][key]
+  f32x16 acc[CB];  // dv^T of half m (roles 0 / 1) or -dK_m^T (roles 2 / 3) [c][key]
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+  auto bf16_at = [](const uint32_t (&w)[8], int r) {  // bf16 r of 16 packed pairs, as fp32
+    return __builtin_bit_cast(float, (r & 1) ? (w[r >> 1] & 0xffff0000u) : (w[r >> 1] << 16));
+  };
+  auto load_p = [&](uint32_t at, uint32_t (&w)[8]) {
+    const uint4 p0 = as_u4(*(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)at);
+    const uint4 p1 = as_u4(*(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(at + 1024));
+    w[0] = p0.x, w[1] = p0.y, w[2] = p0.z, w[3] = p0.w, w[4] = p1.x, w[5] = p1.y, w[6] = p1.z, w[7] = p1.w;
+  };
 
-  for (int it = 0; it < nit; ++it) {
-    const int stage = it & 1;
-    wait_copies();
-    __syncthreads();  // tile it visible; the other stage is free
-    if (it + 1 < nit) issue(it + 1, stage ^ 1);
-    const int i0 = it_row0(it);
-    const uint32_t st = lds0 + stage * STAGE;
-    uint32_t qrow = st + qxs, arow = st + TB + axs, rowst = st + TB + TBV + 16 * hg;
-    uint32_t tbase[TrB::NV];
+  if (pwave) {
+    using TrD = TrBases<DV, true>;
+    TrD td;
+    td.init(lane);
+    // Column block cb of half m is block m CB + cb of the dD row: its lane
+    // base is base((m CB + cb) % NV), so the bases are rotated by m CB.
+    uint32_t tdb[TrD::NV];
 #pragma unroll
-    for (int v = 0; v < TrB::NV; ++v) tbase[v] = st + tb.b[v];
-    asm volatile("" : "+v"(qrow), "+v"(arow), "+v"(rowst));
+    for (int v = 0; v < TrD::NV; ++v) tdb[v] = m ? td.b[(v + CB) % TrD::NV] : td.b[v];
+    for (int it = 0; it < nit; ++it) {
+      const int stage = it & 1;
+      wait_copies();
+      __syncthreads();  // tile it visible; the other stage and the exchange slots are free
+      if (it + 1 < nit) issue(it + 1, stage ^ 1);
+      const int i0 = it_row0(it);
+      const uint32_t st = lds0 + stage * STAGE;
+      uint32_t qrow = st + m * TB + qxs, rowst = st + 4 * TB + 128 * m + 16 * hg;
+      uint32_t tbase[TrD::NV];
 #pragma unroll
-    for (int v = 0; v < TrB::NV; ++v) asm volatile("" : "+v"(tbase[v]));
-    bf16x8 xk[2] = {};
-    if (i0 >= j0w) {  // (else: rows before this wave's keys, or an inactive wave)
-      // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
-      f32x4 lq[4], dq4[4];
+      for (int v = 0; v < TrD::NV; ++v) tbase[v] = st + 2 * TB + m * (CB * 64) + tdb[v];
+      asm volatile("" : "+v"(qrow), "+v"(rowst));
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        dq4[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 128 + 32 * q4);
-      bf16x8 qa[KS], da[KSV];
+      for (int v = 0; v < TrD::NV; ++v) asm volatile("" : "+v"(tbase[v]));
+      const bool vis = i0 >= j0w;  // (else: rows before this wave's keys, or an inactive wave)
+      if (vis) {
+        bf16x8 qa[KS];
 #pragma unroll
-      for (int ks = 0; ks < KSV; ++ks) {
-        if (ks < KS) qa[ks] = lds_read16(qrow ^ (32u * ks));
-        da[ks] = lds_read16(arow ^ (32u * ks));
-      }
+        for (int ks = 0; ks < KS; ++ks) qa[ks] = lds_read16(qrow ^ (32u * ks));
+        f32x4 lq[4];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        lq[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 32 * q4);
-      f32x16 s, dp;
+        for (int q4 = 0; q4 < 4; ++q4)
+          lq[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 32 * q4);
+        f32x16 s;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = dq4[r >> 2][r & 3];  // D of the row
-      }
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KSV; ++ks) {
-        if (ks < KS) s = mfma32x32x16(qa[ks], kf[ks], s);  // S = Q K^T
-        dp = mfma32x32x16(da[ks], vf[ks], dp);            // D - dP = D + dA (-V)^T
-      }
-      constexpr int NMF = KS + KSV, NRD = KS + KSV + 8;
-      __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
+        for (int ks = 0; ks < KS; ++ks) s = mfma32x32x16(qa[ks], fr[ks], s);  // S = Q K^T
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int i = 0; i < NMF; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      float x[16];
+        for (int i = 0; i < KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
+        float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], sl2, -lq[r >> 2][r & 3]);
-      if (i0 == j0w || i0 + kBT > T) {  // diagonal tile or rows past T
-        int lim = T - i0 - 4 * hg, dlo = i0 == j0w ? li - 4 * hg : -64;
-        asm volatile("" : "+v"(lim), "+v"(dlo));
+        for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], sl2, -lq[r >> 2][r & 3]);
+        if (i0 == j0w || i0 + kBT > T) {  // diagonal tile or rows past T
+          int lim = T - i0 - 4 * hg, dlo = i0 == j0w ? li - 4 * hg : -64;
+          asm volatile("" : "+v"(lim), "+v"(dlo));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int cc = 8 * (r >> 2) + (r & 3);
+            x[r] = (cc < lim && cc >= dlo) ? x[r] : -INFINITY;
+          }
+        }
+        const float pm = m ? c : 1.f;
+        f32x8 e0, e1;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int c = 8 * (r >> 2) + (r & 3);
-          x[r] = (c < lim && c >= dlo) ? x[r] : -INFINITY;
+          const float pr = __builtin_amdgcn_exp2f(x[r]) * pm;  // P_1, or c P_2
+          if (r < 8) e0[r] = pr; else e1[r - 8] = pr;
+        }
+        const uint32_t pw = pslot(m);
+        *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)pw = cvt_bf16x8(e0);
+        *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pw + 1024) = cvt_bf16x8(e1);
+      }
+      __syncthreads();  // P of both maps in LDS
+      bf16x8 pc[2] = {};
+      if (vis) {
+        uint32_t w1[8], w2[8];
+        load_p(pslot(0), w1);
+        load_p(pslot(1), w2);
+        f32x8 e0, e1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v = bf16_at(w1, r) + bf16_at(w2, r);  // P_1 + c P_2
+          if (r < 8) e0[r] = v; else e1[r - 8] = v;
+        }
+        pc[0] = cvt_bf16x8(e0);
+        pc[1] = cvt_bf16x8(e1);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const bf16x8 xa = join_bf16x8(tr_read(tbase[TrD::src(cb, 0)] + TrD::off(cb, kk, 0)),
+                                        tr_read(tbase[TrD::src(cb, 1)] + TrD::off(cb, kk, 1)));
+          acc[cb] = mfma32x32x16(xa, pc[kk], acc[cb]);  // dv^T += dD^T (P_1 + c P_2)
+        }
+    }
+  } else {
+    using TrQ = TrBases<D, true>;
+    TrQ tq;
+    tq.init(lane);
+    for (int it = 0; it < nit; ++it) {
+      const int stage = it & 1;
+      wait_copies();
+      __syncthreads();
+      if (it + 1 < nit) issue(it + 1, stage ^ 1);
+      const int i0 = it_row0(it);
+      const uint32_t st = lds0 + stage * STAGE;
+      uint32_t drow = st + 2 * TB + dxs, rowst = st + 4 * TB + 256 + 128 * m + 16 * hg;
+      uint32_t tbase[TrQ::NV];
+#pragma unroll
+      for (int v = 0; v < TrQ::NV; ++v) tbase[v] = st + m * TB + tq.b[v];
+      asm volatile("" : "+v"(drow), "+v"(rowst));
+#pragma unroll
+      for (int v = 0; v < TrQ::NV; ++v) asm volatile("" : "+v"(tbase[v]));
+      const bool vis = i0 >= j0w;
+      f32x16 g;
+      if (vis) {
+        bf16x8 da[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) da[ks] = lds_read16(drow ^ (32u * ks));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) g[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) g = mfma32x32x16(da[ks], fr[ks], g);  // half m of -G = dD (-v)^T
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i + 4 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        const uint32_t gw = gslot(m);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = g[4 * q4 + e];
+          *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(gw + 1024 * q4) = v4;
         }
       }
-      f32x8 e0, e1;
+      __syncthreads();  // both halves of -G and P of both maps in LDS
+      bf16x8 y[2] = {};
+      if (vis) {
+        f32x4 go[4], e4[4];
+        const uint32_t gr = gslot(m ^ 1);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(x[r]) * dp[r];  // P (D - dP) = -dS
-        if (r < 8) e0[r] = pr; else e1[r - 8] = pr;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          go[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(gr + 1024 * q4);
+          e4[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 32 * q4);
+        }
+        uint32_t w[8];
+        load_p(pslot(m), w);
+        f32x8 e0, e1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float own = g[r], oth = go[r >> 2][r & 3];
+          const float ng = m ? oth + own : own + oth;   // -G, the halves in one order
+          const float ds = bf16_at(w, r) * (e4[r >> 2][r & 3] + ng);  // P_m (E_m - G) = -dS_m
+          if (r < 8) e0[r] = ds; else e1[r - 8] = ds;
+        }
+        y[0] = cvt_bf16x8(e0);
+        y[1] = cvt_bf16x8(e1);
       }
-      xk[0] = cvt_bf16x8(e0);
-      xk[1] = cvt_bf16x8(e1);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const bf16x8 xa = join_bf16x8(tr_read(tbase[TrQ::src(cb, 0)] + TrQ::off(cb, kk, 0)),
+                                        tr_read(tbase[TrQ::src(cb, 1)] + TrQ::off(cb, kk, 1)));
+          acc[cb] = mfma32x32x16(xa, y[kk], acc[cb]);  // -dK_m^T += Q_m^T (-dS_m)
+        }
     }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const bf16x8 qa = join_bf16x8(tr_read(tbase[TrB::src(cb, 0)] + TrB::off(cb, kk, 0)),
-                                      tr_read(tbase[TrB::src(cb, 1)] + TrB::off(cb, kk, 1)));
-        acc[cb] = mfma32x32x16(qa, xk[kk], acc[cb]);
-      }
   }
   if (!active || key >= T) return;
-  const TOut& o = a.dk[m];
-  uint16_t* dst = (uint16_t*)o.p + b * o.sb + (int64_t)key * o.st + h * o.sh;
-  const float sc = -a.scale;
+  const TOut& o = pwave ? a.dv : a.dk[m];
+  const float sc = pwave ? 1.f : -a.scale;
+  uint16_t* dst = (uint16_t*)o.p + b * o.sb + (int64_t)key * o.st + h * o.sh + (pwave ? m * D : 0);
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -1180,218 +1300,90 @@ __device__ __forceinline__ void bwd_v1_dk_body(const V1BwdArgs& a, int bid, unsi
     }
 }
 
-// dV over both maps: workgroup (b, h, 32 kNW keys), wave w owns keys
-// J0 + 32 w; iterations (map, row tile): all row tiles of map 1, then of
-// map 2, rows descending, so only one map's K fragments are held at a time
-// (at d = 128 the 2d-wide dV^T accumulators take 128 registers).  S_m =
-// Q_m K_m^T with the K_m fragments of its keys in registers, dV^T += dA_m^T
-// P_m with transpose reads of the dA_m tile.  Same loop structure as dK.
-template <int D>
-struct V1DvCfg {
-  // [Q_m "k" | dA_m "v" | lse], the stage a multiple of a Q row (2D bytes)
-  static constexpr int STAGE = TileDma<D>::BYTES + TileDma<2 * D>::BYTES + 256;
-  static constexpr int SMEM = 2 * STAGE;
-};
-template <int D>
-__device__ __forceinline__ void bwd_v1_dv_body(const V1BwdArgs& a, int bid, unsigned char* smem) {
-  constexpr int DV = 2 * D;
-  constexpr int KS = D / 16, CBV = DV / 32;
-  using Dma = TileDma<D>;
-  using DmaV = TileDma<DV>;
-  constexpr int TB = Dma::BYTES, TBV = DmaV::BYTES;
-  constexpr int STAGE = V1DvCfg<D>::STAGE;
-  static_assert(STAGE % (2 * D) == 0, "tile bases leave a row's chunk bits free");
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
-
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int li = lane & 31, hg = lane >> 5;
-  const int T = a.T, BK = 32 * kNW;
-  const int units = a.B * a.H;
-  const int unit = bid % units, kt = bid / units;  // low key tiles (most rows) first
-  const int b = unit / a.H, h = unit % a.H;
-  const int J0 = kt * BK, j0w = J0 + 32 * wave;
-  const bool active = j0w < T;
-  const int key = j0w + li;
-  const int nrt = (T + kBT - 1) / kBT;
-  const int rt0 = J0 / kBT;
-  const int nr = nrt - rt0;   // row tiles per map
-  const int nit = 2 * nr;     // (map, row tile)
-  auto it_row0 = [&](int it) { return (nrt - 1 - (it < nr ? it : it - nr)) * kBT; };
-
-  bf16x8 kf[KS];  // K_m^T of this wave's keys, for the map being processed
-  auto load_k = [&](int m) {
-    const uint16_t* kr = (const uint16_t*)a.k[m].p + b * a.k[m].sb + (int64_t)key * a.k[m].st + h * a.k[m].sh;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kf[ks] = as_bf16x8(key < T ? *(const uint4*)(kr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) retire(kf[ks]);
-  };
-  load_k(0);
-  auto issue = [&](int it, int stage) {
-    const int m = it < nr ? 0 : 1, i0 = it_row0(it);
-    const uint16_t* qp = (const uint16_t*)a.q[m].p + b * a.q[m].sb + h * a.q[m].sh;
-    const uint16_t* ap = a.dA[m] + ((int64_t)b * T * a.H + h) * DV;
-    const uint32_t st = lds0 + stage * STAGE;
-    Dma::issue(qp, a.q[m].st, i0, T, kRowLayout, st, wave, lane);
-    DmaV::issue(ap, (int64_t)a.H * DV, i0, T, kTransLayout, st + TB, wave, lane);
-    if (wave == kNW - 1 && lane < 8)
-      dma16_sbase(a.lsew[m] + ((int64_t)b * a.H + h) * a.Tp + i0, lane * 16, st + TB + TBV);
-  };
-  issue(0, 0);
-
-  const uint32_t qxs = (uint32_t)(li * (2 * D) + ((hg ^ k_swizzle<D>(li)) << 4));
-  TrBases<DV> tb;
-  tb.init(lane);
-  const float sl2 = a.sl2;
-  f32x16 acc[CBV];  // dV^T [c][key]
-#pragma unroll
-  for (int cb = 0; cb < CBV; ++cb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
-
-  for (int it = 0; it < nit; ++it) {
-    const int stage = it & 1;
-    if (it == nr) load_k(1);  // (its wait also retires the copies in flight: once per call)
-    wait_copies();
-    __syncthreads();  // tile it visible; the other stage is free
-    if (it + 1 < nit) issue(it + 1, stage ^ 1);
-    const int i0 = it_row0(it);
-    const uint32_t st = lds0 + stage * STAGE;
-    uint32_t qrow = st + qxs, rowst = st + TB + TBV + 16 * hg;
-    uint32_t tbase[TrBases<DV>::NV];
-#pragma unroll
-    for (int v = 0; v < TrBases<DV>::NV; ++v) tbase[v] = st + TB + tb.b[v];
-    asm volatile("" : "+v"(qrow), "+v"(rowst));
-#pragma unroll
-    for (int v = 0; v < TrBases<DV>::NV; ++v) asm volatile("" : "+v"(tbase[v]));
-    bf16x8 xk[2] = {};
-    if (i0 >= j0w) {  // (else: rows before this wave's keys, or an inactive wave)
-      bf16x8 qa[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qa[ks] = lds_read16(qrow ^ (32u * ks));
-      f32x4 lq[4];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        lq[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 32 * q4);
-      f32x16 s;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s = mfma32x32x16(qa[ks], kf[ks], s);  // S = Q K^T
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], sl2, -lq[r >> 2][r & 3]);
-      if (i0 == j0w || i0 + kBT > T) {  // diagonal tile or rows past T
-        int lim = T - i0 - 4 * hg, dlo = i0 == j0w ? li - 4 * hg : -64;
-        asm volatile("" : "+v"(lim), "+v"(dlo));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = 8 * (r >> 2) + (r & 3);
-          x[r] = (c < lim && c >= dlo) ? x[r] : -INFINITY;
-        }
-      }
-      f32x8 e0, e1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(x[r]);
-        if (r < 8) e0[r] = pr; else e1[r - 8] = pr;
-      }
-      xk[0] = cvt_bf16x8(e0);
-      xk[1] = cvt_bf16x8(e1);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int cb = 0; cb < CBV; ++cb) {
-        const uint32_t q = tbase[cb % TrBases<DV>::NV] + 16 * kk * (2 * DV) + cb * 64;
-        acc[cb] = mfma32x32x16(join_bf16x8(tr_read(q), tr_read(q + 8 * (2 * DV))), xk[kk], acc[cb]);
-      }
-  }
-  if (!active || key >= T) return;
-  uint16_t* dst = (uint16_t*)a.dv.p + b * a.dv.sb + (int64_t)key * a.dv.st + h * a.dv.sh;
-#pragma unroll
-  for (int cb = 0; cb < CBV; ++cb)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      uint2 w;
-      w.x = pack_bf16x2(acc[cb][4 * g4 + 0], acc[cb][4 * g4 + 1]);
-      w.y = pack_bf16x2(acc[cb][4 * g4 + 2], acc[cb][4 * g4 + 3]);
-      *(uint2*)(dst + 32 * cb + 8 * g4 + 4 * hg) = w;
-    }
-}
-
-// The dQ, dK and dV work of the V1 backward in one grid, so no workgroup
+// The dQ, dK and dv work of the V1 backward in one grid, so no workgroup
 // waits for another kernel's tail: level L = 0, 1, ... (heaviest first) holds
-// the dQ row tile qt-1-L of both maps, the dK key tile L of both maps and the
-// dV key tile L (each a causal trapezoid of about the same size).  The
+// the dQ row tile qt-1-L of both maps and the 128 keys 128 L .. of the dK /
+// dv work (each a causal trapezoid of about the same size).  NKB = 2 (d =
+// 128): 512-thread workgroups, per level one dQ workgroup (waves 0-3 map 1,
+// waves 4-7 map 2, in lockstep over the same key tiles) and two 64-key dK /
+// dv workgroups.  NKB = 1 (d = 64, where three 256-thread workgroups fit a
+// CU): one dQ workgroup per map and four 32-key dK / dv workgroups.  The
 // hardware deals consecutive workgroups to the 8 XCDs in turn (XCD = id mod
-// 8); when the (batch, head) units divide by 8, XCD x takes the units
-// u = x mod 8 only (its work in level order, then unit, then role), so the
+// 8); when the (batch, head) units divide by 8, XCD x takes the units u = x
+// mod 8 only (its work in level order, then unit, then role), so the
 // workgroups running together on one XCD stream the tiles of a few heads
 // through its L2 instead of every head's.
+#ifndef DA_V1_D64_NKB
+#define DA_V1_D64_NKB 1
+#endif
+#ifndef DA_V1_D128_NKB
+#define DA_V1_D128_NKB 2
+#endif
 template <int D>
 struct V1MainCfg {
-  static constexpr int a_ = DqCfg<D, 2 * D>::SMEM, b_ = V1DkCfg<D>::SMEM, c_ = V1DvCfg<D>::SMEM;
+  static constexpr int NKB = D == 64 ? DA_V1_D64_NKB : DA_V1_D128_NKB;  // 32-key blocks per dK / dv workgroup
+  static_assert(NKB == 1 || NKB == 2, "key blocks per workgroup");
+  static constexpr int THREADS = NKB * kNW * 64;
+  static constexpr int NQ = NKB == 2 ? 1 : 2;         // dQ workgroups per level
+  static constexpr int NKT = 4 / NKB;                 // dK / dv workgroups per level (128 keys)
+  static constexpr int ROLES = NQ + NKT;
+  static constexpr int a_ = NKB * DqCfg<D, 2 * D>::SMEM, b_ = V1DkvCfg<D, NKB>::SMEM, c_ = THREADS * 4;
   static constexpr int SMEM = a_ > b_ ? (a_ > c_ ? a_ : c_) : (b_ > c_ ? b_ : c_);
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 template <int D>
-__global__ void __launch_bounds__(kNW * 64, 2) bwd_v1_main_kernel(const V1BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[V1MainCfg<D>::SMEM];
+__global__ void __launch_bounds__(V1MainCfg<D>::THREADS, 3 - V1MainCfg<D>::NKB) bwd_v1_main_kernel(const V1BwdArgs a) {
+  using Cfg = V1MainCfg<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::SMEM];
   if (blockIdx.x == 0) {  // the dlam reduction, first so that it overlaps the rest
-    bwd_v1_lam_body<D, kNW * 64>(a, (float*)smem);
+    bwd_v1_lam_body<D, Cfg::THREADS>(a, (float*)smem);
     return;
   }
   const int bh = a.B * a.H;
   const int id = blockIdx.x - 1;
-  int level, u, role;  // role 0 / 1: dQ of map 0 / 1; 2 / 3: dK of map 0 / 1; 4: dV
+  int level, u, role;  // role < NQ: dQ; then the dK / dv key tiles of the level
   if (bh % 8 == 0) {
-    const int per = 5 * (bh / 8);  // one XCD's workgroups per level
+    const int per = Cfg::ROLES * (bh / 8);  // one XCD's workgroups per level
     const int sx = id / 8, w = sx % per;
     level = sx / per;
-    u = id % 8 + 8 * (w / 5);
-    role = w % 5;
+    u = id % 8 + 8 * (w / Cfg::ROLES);
+    role = w % Cfg::ROLES;
   } else {
-    const int r = id % (5 * bh);
-    level = id / (5 * bh);
-    role = r < 2 * bh ? r / bh : r < 4 * bh ? 2 + (r - 2 * bh) % 2 : 4;
-    u = r < 2 * bh ? r % bh : r < 4 * bh ? (r - 2 * bh) / 2 : r - 4 * bh;
+    const int r = id % (Cfg::ROLES * bh);
+    level = id / (Cfg::ROLES * bh);
+    role = r / bh;
+    u = r % bh;
   }
-  if (role < 2) {  // dQ of map `role`, unit u
-    const int m = role;
+  const float c = -v1_lambda<D>(a);  // d a_2 = c dD
+  if (role < Cfg::NQ) {
+    // NKB = 2: waves 4-7 take map 2; NKB = 1: the role is the map
+    const int m = Cfg::NKB == 2 ? (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= kNW ? 1 : 0) : role;
     BwdArgs q{};
     q.q = a.q[m], q.k = a.k[m], q.v = a.v;
     q.dq = a.dq[m];
-    q.dA = a.dA[m];
+    q.dA = a.dD;
     q.Dw = a.Dw[m];
     q.lsew = a.lsew[m];
-    q.sl2 = a.sl2, q.scale = a.scale;
+    q.sl2 = a.sl2, q.scale = m ? a.scale * c : a.scale;
     q.B = a.B, q.T = a.T, q.Hq = a.H, q.Hkv = a.H, q.G = 1, q.Tp = a.Tp;
-    bwd_dq_body<D, 2 * D>(q, level * bh + u, smem);
-  } else if (role < 4) {
-    bwd_v1_dk_body<D>(a, level * 2 * bh + 2 * u + (role - 2), smem);
+    const int part = Cfg::NKB == 2 ? m : 0;
+    bwd_dq_body<D, 2 * D>(q, level * bh + u, smem + part * DqCfg<D, 2 * D>::SMEM, threadIdx.x - part * kNW * 64);
   } else {
-    bwd_v1_dv_body<D>(a, level * bh + u, smem);
+    bwd_v1_dkv_body<D, Cfg::NKB>(a, (Cfg::NKT * level + role - Cfg::NQ) * bh + u, c, smem);
   }
 }
 
 template <int D>
 hipError_t launch_v1(const V1BwdArgs& a, hipStream_t st) {
+  using Cfg = V1MainCfg<D>;
   const void* args[] = {&a};
   const long long items = (long long)a.B * a.Tp * a.H;
   hipError_t e = hipLaunchKernel((const void*)bwd_v1_pre_kernel<D>, dim3((unsigned)((items + 15) / 16)), dim3(256),
                                  (void**)args, 0, st);
   if (e != hipSuccess) return e;
   const int qt = (a.T + 32 * kNW - 1) / (32 * kNW);
-  return hipLaunchKernel((const void*)bwd_v1_main_kernel<D>, dim3(1 + 5 * a.B * a.H * qt), dim3(kNW * 64),
-                         (void**)args, 0, st);
+  return hipLaunchKernel((const void*)bwd_v1_main_kernel<D>, dim3(1 + Cfg::ROLES * a.B * a.H * qt),
+                         dim3(Cfg::THREADS), (void**)args, 0, st);
 }
 
 }  // namespace

@@ -102,8 +102,8 @@ struct V1BwdArgs {
   const float *lq1, *lk1, *lq2, *lk2;  // lambda vectors [d]
   TOut dq[2], dk[2], dv;               // bf16, layouts of q / k / v
   float *dlq1, *dlk1, *dlq2, *dlk2;    // [d] fp32
-  uint16_t* dA[2];    // workspace [B][T][H][2d] bf16: d a_m
-  float* Dw[2];       // workspace [B][H][Tp]: rowsum(d a_m * a_m)
+  uint16_t* dD;       // workspace [B][T][H][2d] bf16: dD (d a_1 = dD, d a_2 = -lam dD)
+  float* Dw[2];       // workspace [B][H][Tp]: E_m = rowsum(dD * a_m)
   float* lsew[2];     // workspace [B][H][Tp]: lse of map m, padded with zeros
   float* lamrow;      // workspace [B][T][H]: each row's term of d lambda
   float lam_init, sl2, scale;

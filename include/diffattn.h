@@ -374,8 +374,8 @@ da_status diffattn_v1_fwd_train_softmax1(int dtype, int B, int H, int T, int d, 
 
 /*
  * Bytes of device workspace diffattn_v1_bwd needs (0 if the sizes are
- * invalid): d a_m of both maps in bf16, four fp32 arrays of B*H rows padded
- * to a multiple of 128 tokens, and one fp32 value per (b, t, h).
+ * invalid): dD in bf16 (B*T*H*2d), four fp32 arrays of B*H rows padded to
+ * a multiple of 128 tokens, and one fp32 value per (b, t, h).
  */
 size_t diffattn_v1_bwd_workspace_bytes(int B, int H, int T, int d);
 
@@ -402,9 +402,9 @@ size_t diffattn_v1_bwd_workspace_bytes(int B, int H, int T, int d);
  *   dlam_q1 .. dlam_k2  DEVICE fp32 [d] each.
  *   workspace  at least diffattn_v1_bwd_workspace_bytes(B,H,T,d) bytes,
  *              256-byte aligned, owned by the caller.
- * Seven kernels are enqueued on `stream` (a pre-pass, the dlam reduction,
- * dq of each map, dk of both maps, dv); every sum is taken in a fixed order
- * (deterministic).  Token strides of q1 .. v must be below 2^24 elements
+ * Two kernels are enqueued on `stream` (a pre-pass, then one grid with the
+ * dlam reduction, dq of both maps, dk of both maps and dv); every sum is
+ * taken in a fixed order (deterministic).  Token strides of q1 .. v must be below 2^24 elements
  * (DA_E_UNSUPPORTED).
  */
 da_status diffattn_v1_bwd(int dtype, int B, int H, int T, int d, da_in q1, da_in q2, da_in k1, da_in k2,

@@ -250,11 +250,11 @@ def test_v1_fwd_train_validation(lib):
 def test_v1_bwd_workspace_query(lib):
     B, H, T, d = 8, 6, 1024, 64
     Tp = 1024
-    want = 2 * B * T * H * 2 * d * 2 + 4 * B * H * Tp * 4 + B * T * H * 4
+    want = B * T * H * 2 * d * 2 + 4 * B * H * Tp * 4 + B * T * H * 4
     assert lib.diffattn_v1_bwd_workspace_bytes(B, H, T, d) == want
     # padded rows and 256-byte aligned regions
-    # B=H=1, T=3, d=64: d a 3*128*2 = 768 B per map, rows padded to 128 (512 B each), 12 B of row terms -> 256
-    assert lib.diffattn_v1_bwd_workspace_bytes(1, 1, 3, 64) == 2 * 768 + 4 * 512 + 256
+    # B=H=1, T=3, d=64: dD 3*128*2 = 768 B, rows padded to 128 (512 B each), 12 B of row terms -> 256
+    assert lib.diffattn_v1_bwd_workspace_bytes(1, 1, 3, 64) == 768 + 4 * 512 + 256
     assert lib.diffattn_v1_bwd_workspace_bytes(0, 1, 3, 64) == 0
 
 

@@ -83,7 +83,7 @@ def tr_read(lds, addrs):
     return out
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_both_ways_swizzle_properties(d):
     rows = [u_sw(d, r) for r in range(16)]
     if d >= 128:
@@ -96,7 +96,7 @@ def test_both_ways_swizzle_properties(d):
         assert u_sw(d, r + 16) == u_sw(d, r)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("layout", ["row", "both"])
 def test_row_reads_conflict_free_and_exact(d, layout):
     sw = k_sw if layout == "row" else u_sw
@@ -109,7 +109,7 @@ def test_row_reads_conflict_free_and_exact(d, layout):
             assert got == [(l & 31) * 1000 + 16 * ks + 8 * (l >> 5) + e for e in range(8)]
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_transpose_reads_conflict_free_and_equal(d):
     old, new = place(d, v_sw), place(d, u_sw)
     for kk in range(2):
@@ -123,9 +123,29 @@ def test_transpose_reads_conflict_free_and_equal(d):
                 assert tr_read(new, a_new) == tr_read(old, a_old)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_single_layouts_conflict_in_the_other_read(d):
     # why the both-ways layout exists: the row swizzle conflicts in transpose
     # reads and the transpose swizzle in row reads
     assert worst_bank_use(tr_addrs(d, k_sw, False, 0, 0, 0), 8, 32) > 1
     assert worst_bank_use(row_addrs(d, v_sw, 0), 16, 16) > 1
+
+
+@pytest.mark.parametrize("dv", [128, 256])
+def test_half_width_transpose_reads(dv):
+    # the V1 dK/dv kernel reads the transposed dD tile (dv = 2d wide) one
+    # d-wide half m at a time: column block cb of half m is block m CB + cb,
+    # read from the lane bases rotated by m CB plus m CB column blocks
+    nv = 4 if dv >= 128 else 2
+    cbh = dv // 64  # column blocks of a half
+    for m in range(2):
+        for lane in range(64):
+            b = trbase(dv, u_sw, lane)
+            rot = [b[(v + m * cbh) % nv] for v in range(nv)]
+            for cb in range(cbh):
+                for kk in range(2):
+                    for h in range(2):
+                        c = (cb ^ 1) if h else cb
+                        got = rot[c % nv] + m * cbh * 64 + c * 64 + (16 * kk + 8 * h) * 2 * dv
+                        want = tr_addrs(dv, u_sw, True, m * cbh + cb, kk, h)[lane]
+                        assert got == want, (m, lane, cb, kk, h)
