@@ -219,8 +219,7 @@ struct DqCfg {
   static constexpr int SMEM = 2 * STAGE;
 };
 // `bid`: the workgroup's index in the dQ grid order; `smem`: DqCfg::SMEM bytes
-// of LDS, 1 KB aligned; `tid`: the thread's index among the kNW * 64 threads
-// that run this body (every one of them reaches the same barriers).
+// of LDS, 1 KB aligned.
 //
 // As in the dK/dV kernel, the accumulators take one path through the loop
 // body (key tiles after a wave's rows skip the scores and accumulate zeros),
@@ -229,7 +228,7 @@ struct DqCfg {
 // and the accumulator starts at D, so the MFMAs leave D - dP, P (D - dP) =
 // -dS, and dQ is negated when stored.
 template <int D, int DV>
-__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned char* smem, int tid) {
+__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned char* smem) {
   constexpr int KS = D / 16, KSV = DV / 16, CB = D / 32;
   constexpr int KM = KS > KSV ? KS : KSV;
   using Dma = TileDma<D>;
@@ -240,7 +239,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
                 "tile bases leave a row's chunk bits free");
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, hg = lane >> 5;
   const int T = a.T, BM = 32 * kNW;
   const int tiles = (T + BM - 1) / BM;
@@ -408,7 +407,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
 template <int D, int DV>
 __global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[DqCfg<D, DV>::SMEM];
-  bwd_dq_body<D, DV>(a, blockIdx.x, smem, threadIdx.x);
+  bwd_dq_body<D, DV>(a, blockIdx.x, smem);
 }
 
 // ---- dK, dV ------------------------------------------------------------------
@@ -852,9 +851,9 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
 // with E_m = rowsum(dD * a_m), and dv = (P_1 + c P_2)^T dD is one product.
 // Kernels: a pre-pass per (b, token, head) writes dD, E_1, E_2 and the
 // padded lse rows; then one grid holds the dlam reduction (one workgroup,
-// fixed order, writes the four vector gradients), dQ of both maps (the V2
-// dQ code with a 2d-wide v, dD as d attn and c in the map-2 scale) and dK of
-// both maps with dv (four waves per 32-key block sharing S, G and P).
+// fixed order, writes the four vector gradients), dQ of both maps (the two
+// maps' waves of the same rows sharing G) and dK of both maps with dv (four
+// waves per 32-key block sharing S, G and P).
 
 // lam = exp(<lq1, lk1>) - exp(<lq2, lk2>) + lam_init, the same bits in every
 // wave that computes it (the pre-pass and the main grid)
@@ -1300,14 +1299,219 @@ __device__ __forceinline__ void bwd_v1_dkv_body(const V1BwdArgs& a, int bid, flo
     }
 }
 
+// dQ of both maps: workgroup (b, h, 32 NRB rows), wave w: map m = w / NRB,
+// rows i0 + 32 (w % NRB); the waves of the two maps of the same rows share
+// the product G = dD v^T.  Per 32-key tile (K_1, K_2 in the both-ways
+// layout, v in the row layout): S_m^T = K_m Q_m^T with Q_m^T of its rows in
+// registers, and half m of -G^T (v channels m d .. m d + d - 1 against the
+// same channels of -dD^T, in registers) to LDS; after the barrier -G^T =
+// both halves (one order), P_m (E_m - G) = -dS_m (the map-2 factor c goes
+// into the output scale), dQ_m^T += K_m^T (-dS_m^T) by transpose reads.
+// 3 d / 16 MFMAs per wave and tile instead of 4 d / 16 with G formed per map.
+template <int D, int NRB>
+struct V1DqCfg {
+  static constexpr int TB = TileDma<D>::BYTES, TBV = TileDma<2 * D>::BYTES;
+  static constexpr int STAGE = 2 * TB + TBV;  // [K_1 | K_2 (both ways) | v (rows)]
+  static constexpr int GSLOT = 4096;           // a half of -G^T: 64 lanes x 4 x 16 bytes
+  static constexpr int XBASE = 2 * STAGE;
+  static constexpr int SMEM = XBASE + NRB * 2 * GSLOT;
+  static_assert(STAGE % (4 * D) == 0 && TB % (4 * D) == 0, "tile bases leave a row's chunk bits free");
+};
+template <int D, int NRB>
+__device__ __forceinline__ void bwd_v1_dq_body(const V1BwdArgs& a, int tile, int unit, float c, unsigned char* smem) {
+  constexpr int DV = 2 * D;
+  constexpr int KS = D / 16, CB = D / 32;
+  constexpr int NW = 2 * NRB;
+  using Cfg = V1DqCfg<D, NRB>;
+  constexpr int TB = Cfg::TB, STAGE = Cfg::STAGE, GSLOT = Cfg::GSLOT;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int li = lane & 31, hg = lane >> 5;
+  const int rb = wave % NRB, m = wave / NRB;
+  const int T = a.T, BM = 32 * NRB;
+  if (tile * BM >= T) return;  // (rows past T: the whole workgroup)
+  const int b = unit / a.H, h = unit % a.H;
+  const int i0w = tile * BM + 32 * rb;
+  const bool active = i0w < T;
+  const int kend = min(T, tile * BM + BM);
+  const int nkt = (kend + kBT - 1) / kBT;
+  const int row = i0w + li;
+
+  const uint16_t* kp0 = (const uint16_t*)a.k[0].p + b * a.k[0].sb + h * a.k[0].sh;
+  const uint16_t* kp1 = (const uint16_t*)a.k[1].p + b * a.k[1].sb + h * a.k[1].sh;
+  const uint16_t* vp = (const uint16_t*)a.v.p + b * a.v.sb + h * a.v.sh;
+  TileCopy<D, NW> ck0, ck1;
+  TileCopy<DV, NW> cv;
+  ck0.init(a.k[0].st, kBothLayout, wave, lane);
+  ck1.init(a.k[1].st, kBothLayout, wave, lane);
+  cv.init(a.v.st, kRowLayout, wave, lane);
+  auto issue = [&](int kt, int stage) {
+    const uint32_t st = lds0 + stage * STAGE;
+    const int r0 = kt * kBT;
+    if (r0 + kBT > T) {  // ragged last tile
+      TileDma<D, NW>::issue(kp0, a.k[0].st, r0, T, kBothLayout, st, wave, lane);
+      TileDma<D, NW>::issue(kp1, a.k[1].st, r0, T, kBothLayout, st + TB, wave, lane);
+      TileDma<DV, NW>::issue(vp, a.v.st, r0, T, kRowLayout, st + 2 * TB, wave, lane);
+    } else {
+      ck0.issue(kp0 + (int64_t)r0 * a.k[0].st, st, wave);
+      ck1.issue(kp1 + (int64_t)r0 * a.k[1].st, st + TB, wave);
+      cv.issue(vp + (int64_t)r0 * a.v.st, st + 2 * TB, wave);
+    }
+  };
+  issue(0, 0);
+
+  // B operands: Q_m^T and half m of -dD^T of this wave's rows; the row's lse and E_m
+  bf16x8 qf[KS], af[KS];
+  {
+    const TIn& tq = a.q[m];
+    const uint16_t* qr = (const uint16_t*)tq.p + b * tq.sb + (int64_t)row * tq.st + h * tq.sh;
+    const uint16_t* ar = a.dD + (((int64_t)b * T + row) * a.H + h) * DV + m * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = as_bf16x8(row < T ? *(const uint4*)(qr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+      af[ks] = as_bf16x8(row < T ? *(const uint4*)(ar + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+    }
+  }
+  const int64_t rr = ((int64_t)b * a.H + h) * a.Tp + min(row, a.Tp - 1);
+  float lse_r = a.lsew[m][rr], E_r = a.Dw[m][rr];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    retire(qf[ks]);
+    retire(af[ks]);
+    const uint4 u = as_u4(af[ks]);  // sign flip of every bf16 (exact)
+    af[ks] = as_bf16x8(make_uint4(u.x ^ 0x80008000u, u.y ^ 0x80008000u, u.z ^ 0x80008000u, u.w ^ 0x80008000u));
+  }
+  retire(lse_r);
+  retire(E_r);
+  // Row reads: chunk (2 ks + hg) ^ swizzle(li) = 2 ks ^ (hg ^ swizzle(li)),
+  // so the address is (tile base + lane part) ^ 32 ks; half m of a v row
+  // starts at k-step m KS (XOR 32 m KS).
+  const uint32_t kxs = (uint32_t)(li * (2 * D) + ((hg ^ u_swizzle<D>(li)) << 4));
+  const uint32_t vxs = (uint32_t)(li * (2 * DV) + ((hg ^ k_swizzle<DV>(li)) << 4)) ^ (uint32_t)(32 * m * KS);
+  using TrB = TrBases<D, true>;
+  TrB tb;
+  tb.init(lane);
+  const uint32_t xs = lds0 + Cfg::XBASE + rb * 2 * GSLOT + lane * 16;  // slots of this row block
+  const float sl2 = a.sl2;
+  f32x16 acc[CB];  // -dQ_m^T (up to c)
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int stage = kt & 1;
+    wait_copies();
+    __syncthreads();  // tile kt visible; the other stage and the slots are free
+    if (kt + 1 < nkt) issue(kt + 1, stage ^ 1);
+    const int j0 = kt * kBT;
+    const uint32_t st = lds0 + stage * STAGE;
+    uint32_t krow = st + m * TB + kxs, vrow = st + 2 * TB + vxs;
+    uint32_t tbase[TrB::NV];
+#pragma unroll
+    for (int v = 0; v < TrB::NV; ++v) tbase[v] = st + m * TB + tb.b[v];
+    asm volatile("" : "+v"(krow), "+v"(vrow));
+#pragma unroll
+    for (int v = 0; v < TrB::NV; ++v) asm volatile("" : "+v"(tbase[v]));
+    // Key tiles entirely after this row block's rows skip the scores and
+    // accumulate zeros (the same for both maps' waves of the rows).
+    const bool vis = j0 <= i0w;
+    f32x16 s, gp;
+    if (vis) {
+      bf16x8 ka[KS], va[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        ka[ks] = lds_read16(krow ^ (32u * ks));
+        va[ks] = lds_read16(vrow ^ (32u * ks));
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = gp[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32x32x16(ka[ks], qf[ks], s);    // S^T = K Q^T
+        gp = mfma32x32x16(va[ks], af[ks], gp);  // half m of -G^T = v (-dD)^T
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + 4 < 2 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      const uint32_t gw = xs + m * GSLOT;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = gp[4 * q4 + e];
+        *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(gw + 1024 * q4) = v4;
+      }
+    }
+    __syncthreads();  // both halves of -G^T of every row block in LDS
+    bf16x8 dsk[2] = {};
+    if (vis) {
+      f32x4 go[4];
+      const uint32_t gr = xs + (m ^ 1) * GSLOT;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        go[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(gr + 1024 * q4);
+      // lane: row li; register r: key j0 + 8(r>>2) + 4hg + (r&3)
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], sl2, -lse_r);
+      if (j0 == i0w) {  // the diagonal tile: keys after the row masked
+        int lim = li - 4 * hg;  // kept: key offset 4hg + c <= li
+        asm volatile("" : "+v"(lim));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int cc = 8 * (r >> 2) + (r & 3);
+          x[r] = cc <= lim ? x[r] : -INFINITY;
+        }
+      }
+      f32x8 e0, e1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float own = gp[r], oth = go[r >> 2][r & 3];
+        const float ng = m ? oth + own : own + oth;  // -G^T, the halves in one order
+        const float ds = __builtin_amdgcn_exp2f(x[r]) * (E_r + ng);  // P (E - G) = -dS
+        if (r < 8) e0[r] = ds; else e1[r - 8] = ds;
+      }
+      dsk[0] = cvt_bf16x8(e0);
+      dsk[1] = cvt_bf16x8(e1);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const bf16x8 ka = join_bf16x8(tr_read(tbase[TrB::src(cb, 0)] + TrB::off(cb, kk, 0)),
+                                      tr_read(tbase[TrB::src(cb, 1)] + TrB::off(cb, kk, 1)));
+        acc[cb] = mfma32x32x16(ka, dsk[kk], acc[cb]);
+      }
+  }
+  if (!active || row >= T) return;
+  // dQ^T[c][row]: c = 32 cb + 8 (r>>2) + 4 hg + (r&3); dq_m = c_m dS_m k_m / sqrt d
+  const TOut& o = a.dq[m];
+  uint16_t* dst = (uint16_t*)o.p + b * o.sb + (int64_t)row * o.st + h * o.sh;
+  const float sc = -a.scale * (m ? c : 1.f);
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      uint2 w;
+      w.x = pack_bf16x2(acc[cb][4 * g4 + 0] * sc, acc[cb][4 * g4 + 1] * sc);
+      w.y = pack_bf16x2(acc[cb][4 * g4 + 2] * sc, acc[cb][4 * g4 + 3] * sc);
+      *(uint2*)(dst + 32 * cb + 8 * g4 + 4 * hg) = w;
+    }
+}
+
 // The dQ, dK and dv work of the V1 backward in one grid, so no workgroup
 // waits for another kernel's tail: level L = 0, 1, ... (heaviest first) holds
-// the dQ row tile qt-1-L of both maps and the 128 keys 128 L .. of the dK /
-// dv work (each a causal trapezoid of about the same size).  NKB = 2 (d =
-// 128): 512-thread workgroups, per level one dQ workgroup (waves 0-3 map 1,
-// waves 4-7 map 2, in lockstep over the same key tiles) and two 64-key dK /
-// dv workgroups.  NKB = 1 (d = 64, where three 256-thread workgroups fit a
-// CU): one dQ workgroup per map and four 32-key dK / dv workgroups.  The
+// the dQ work of the 128 rows qt-1-L of both maps and the dK / dv work of
+// the 128 keys 128 L .. (each a causal trapezoid of about the same size).
+// NKB = 2 (d = 128): 512-thread workgroups, per level one dQ workgroup (128
+// rows) and two 64-key dK / dv workgroups.  NKB = 1 (d = 64, where three
+// 256-thread workgroups fit a CU): two 64-row dQ workgroups and four 32-key
+// dK / dv workgroups.  The
 // hardware deals consecutive workgroups to the 8 XCDs in turn (XCD = id mod
 // 8); when the (batch, head) units divide by 8, XCD x takes the units u = x
 // mod 8 only (its work in level order, then unit, then role), so the
@@ -1324,10 +1528,11 @@ struct V1MainCfg {
   static constexpr int NKB = D == 64 ? DA_V1_D64_NKB : DA_V1_D128_NKB;  // 32-key blocks per dK / dv workgroup
   static_assert(NKB == 1 || NKB == 2, "key blocks per workgroup");
   static constexpr int THREADS = NKB * kNW * 64;
-  static constexpr int NQ = NKB == 2 ? 1 : 2;         // dQ workgroups per level
+  static constexpr int NRB = 2 * NKB;                 // 32-row blocks per dQ workgroup
+  static constexpr int NQ = 4 / NRB;                  // dQ workgroups per level (128 rows)
   static constexpr int NKT = 4 / NKB;                 // dK / dv workgroups per level (128 keys)
   static constexpr int ROLES = NQ + NKT;
-  static constexpr int a_ = NKB * DqCfg<D, 2 * D>::SMEM, b_ = V1DkvCfg<D, NKB>::SMEM, c_ = THREADS * 4;
+  static constexpr int a_ = V1DqCfg<D, NRB>::SMEM, b_ = V1DkvCfg<D, NKB>::SMEM, c_ = THREADS * 4;
   static constexpr int SMEM = a_ > b_ ? (a_ > c_ ? a_ : c_) : (b_ > c_ ? b_ : c_);
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
@@ -1355,19 +1560,9 @@ __global__ void __launch_bounds__(V1MainCfg<D>::THREADS, 3 - V1MainCfg<D>::NKB) 
     u = r % bh;
   }
   const float c = -v1_lambda<D>(a);  // d a_2 = c dD
-  if (role < Cfg::NQ) {
-    // NKB = 2: waves 4-7 take map 2; NKB = 1: the role is the map
-    const int m = Cfg::NKB == 2 ? (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= kNW ? 1 : 0) : role;
-    BwdArgs q{};
-    q.q = a.q[m], q.k = a.k[m], q.v = a.v;
-    q.dq = a.dq[m];
-    q.dA = a.dD;
-    q.Dw = a.Dw[m];
-    q.lsew = a.lsew[m];
-    q.sl2 = a.sl2, q.scale = m ? a.scale * c : a.scale;
-    q.B = a.B, q.T = a.T, q.Hq = a.H, q.Hkv = a.H, q.G = 1, q.Tp = a.Tp;
-    const int part = Cfg::NKB == 2 ? m : 0;
-    bwd_dq_body<D, 2 * D>(q, level * bh + u, smem + part * DqCfg<D, 2 * D>::SMEM, threadIdx.x - part * kNW * 64);
+  if (role < Cfg::NQ) {  // rows 128 (qt-1-level) .., the later (heavier) row tile first
+    const int qt = (a.T + 127) / 128;
+    bwd_v1_dq_body<D, Cfg::NRB>(a, Cfg::NQ * (qt - 1 - level) + (Cfg::NQ - 1 - role), u, c, smem);
   } else {
     bwd_v1_dkv_body<D, Cfg::NKB>(a, (Cfg::NKT * level + role - Cfg::NQ) * bh + u, c, smem);
   }
