@@ -399,12 +399,14 @@ static da_status v2_fwd_impl(int softmax1, int dtype, int B, int T, int Hq, int 
 
 // DIFF V2 backward: sizes of the three workspace regions.
 struct BwdWs {
-  size_t dA, rows;  // bytes of d attn; bytes of each [B][Hq][Tp] fp32 array
+  size_t rows, crow;  // bytes of each [B][Hq][Tp] fp32 array; of the [B][Hq/2][Tp] one
+  size_t total() const { return 2 * rows + crow; }
 };
 static BwdWs bwd_ws(int B, int T, int Hq, int d) {
+  (void)d;
   BwdWs w;
-  w.dA = ((size_t)B * T * Hq * d * 2 + 255) / 256 * 256;
   w.rows = ((size_t)B * Hq * da::backward_padded_rows(T) * 4 + 255) / 256 * 256;
+  w.crow = ((size_t)B * (Hq / 2) * da::backward_padded_rows(T) * 4 + 255) / 256 * 256;
   return w;
 }
 
@@ -423,10 +425,10 @@ static da_status v2_bwd_impl(int dtype, int B, int T, int Hq, int Hkv, int d, da
   if (!aligned(lse, 4)) return DA_E_LAYOUT;
   DA_TRY(validate_v2_common(dtype, B, T, Hq, Hkv, d));
   if (q.st >= kMaxTokenStride || k.st >= kMaxTokenStride || v.st >= kMaxTokenStride ||
-      (int64_t)Hq * d >= kMaxTokenStride)
+      dout.st >= kMaxTokenStride)
     return DA_E_UNSUPPORTED;
   const BwdWs w = bwd_ws(B, T, Hq, d);
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.dA + 2 * w.rows) return DA_E_WORKSPACE;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < w.total()) return DA_E_WORKSPACE;
   const int qt = (T + 127) / 128;
   if (!grid_fits((long long)B * Hq * qt) || !grid_fits(((long long)B * da::backward_padded_rows(T) * (Hq / 2) + 15) / 16))
     return DA_E_SHAPE;
@@ -435,9 +437,9 @@ static da_status v2_bwd_impl(int dtype, int B, int T, int Hq, int Hkv, int d, da
   a.q = tin(q), a.k = tin(k), a.v = tin(v), a.lam = tin(lam), a.attn = tin(attn), a.dout = tin(dout);
   a.lse = lse;
   a.dq = tout(dq), a.dk = tout(dk), a.dv = tout(dv), a.dlam = tout(dlam);
-  a.dA = (uint16_t*)workspace;
-  a.Dw = (float*)((char*)workspace + w.dA);
-  a.lsew = (float*)((char*)workspace + w.dA + w.rows);
+  a.Dw = (float*)workspace;
+  a.lsew = (float*)((char*)workspace + w.rows);
+  a.cw = (float*)((char*)workspace + 2 * w.rows);
   a.sl2 = log2e_over_sqrt(d);
   a.scale = (float)(1.0 / sqrt((double)d));
   a.B = B, a.T = T, a.Hq = Hq, a.Hkv = Hkv, a.G = Hq / Hkv;
@@ -620,7 +622,7 @@ size_t diffattn_v2_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d) {
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1) return 0;
   if (Hq % Hkv != 0 || (Hq / Hkv) % 2 != 0) return 0;
   const BwdWs w = bwd_ws(B, T, Hq, d);
-  return w.dA + 2 * w.rows;
+  return w.total();
 }
 
 da_status diffattn_v2_bwd(int dtype, int B, int T, int Hq, int Hkv, int d, da_in q, da_in k, da_in v,

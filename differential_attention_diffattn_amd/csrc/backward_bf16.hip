@@ -65,8 +65,9 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdArgs a) {
   const int t = (int)((item / P) % a.Tp);
   const int b = (int)(item / ((long long)P * a.Tp));
   const int64_t r0 = ((int64_t)b * a.Hq + 2 * p) * a.Tp + t, r1 = r0 + a.Tp;  // rows of heads 2p, 2p+1
-  if (t >= a.T) {  // padding rows: zero D and lse (masked where read)
-    if (l16 == 0) a.Dw[r0] = a.Dw[r1] = a.lsew[r0] = a.lsew[r1] = 0.f;
+  const int64_t rc = ((int64_t)b * P + p) * a.Tp + t;  // the pair's row
+  if (t >= a.T) {  // padding rows: zero E, lse and c (masked where read)
+    if (l16 == 0) a.Dw[r0] = a.Dw[r1] = a.lsew[r0] = a.lsew[r1] = a.cw[rc] = 0.f;
     return;
   }
   const int c = EL * l16;
@@ -81,32 +82,23 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdArgs a) {
   auto hi = [](uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); };
   const float lg = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)t * a.lam.st + p * a.lam.sh];
   const float s = sigmoid_f32(lg);
-  // The odd head's d attn goes to the MFMAs rounded to bf16; its row sum D
-  // is taken over those same rounded values, so that rowsum(dS) = 0 holds
-  // for the P the kernels see (a row with one visible key then gets dq = 0
-  // up to fp32 summation order).  y (the unrounded <dout, attn_odd>) feeds
-  // d lam only.
-  uint32_t n1[EL / 2];
-#pragma unroll
-  for (int i = 0; i < EL / 2; ++i) n1[i] = pack_bf16x2(-s * lo(gw[i]), -s * hi(gw[i]));
-  float x = 0.f, y = 0.f, z = 0.f;
+  // E_2p = <dout, attn_2p> and E_2p+1 = <dout, attn_2p+1> (the odd head's
+  // d attn is c dout with c = -s, applied in fp32 where it is used); the
+  // second also feeds d lam.
+  float x = 0.f, y = 0.f;
 #pragma unroll
   for (int i = 0; i < EL / 2; ++i) {
     x += lo(gw[i]) * lo(w0[i]) + hi(gw[i]) * hi(w0[i]);
     y += lo(gw[i]) * lo(w1[i]) + hi(gw[i]) * hi(w1[i]);
-    z += lo(n1[i]) * lo(w1[i]) + hi(n1[i]) * hi(w1[i]);
   }
   x = row16_sum(x);
   y = row16_sum(y);
-  z = row16_sum(z);
-  uint16_t* d0 = a.dA + (((int64_t)b * a.T + t) * a.Hq + 2 * p) * D;
-  *(Vec*)(d0 + c) = gv;
-  *(Vec*)(d0 + D + c) = *(const Vec*)n1;
   if (l16 == 0) {
     a.Dw[r0] = x;
-    a.Dw[r1] = z;
+    a.Dw[r1] = y;
     a.lsew[r0] = a.lse[((int64_t)b * a.Hq + 2 * p) * a.T + t];
     a.lsew[r1] = a.lse[((int64_t)b * a.Hq + 2 * p + 1) * a.T + t];
+    a.cw[rc] = -s;
     ((float*)a.dlam.p)[b * a.dlam.sb + (int64_t)t * a.dlam.st + p * a.dlam.sh] = -s * (1.f - s) * y;
   }
 }
@@ -277,11 +269,13 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
   };
   issue(0, 0);
 
-  // B operands: Q^T and -dA^T of this wave's rows; the row's lse and D
+  // B operands: Q^T and -dout^T of this wave's rows (d attn of the pair's
+  // odd head is c dout: c scales its dQ row at the store); the row's lse, E
+  // and c
   bf16x8 qf[KS], af[KSV];
   {
     const uint16_t* qr = (const uint16_t*)a.q.p + b * a.q.sb + (int64_t)row * a.q.st + h * a.q.sh;
-    const uint16_t* ar = a.dA + (((int64_t)b * T + row) * a.Hq + h) * DV;
+    const uint16_t* ar = (const uint16_t*)a.dout.p + b * a.dout.sb + (int64_t)row * a.dout.st + (h >> 1) * a.dout.sh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = as_bf16x8(row < T ? *(const uint4*)(qr + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
@@ -291,6 +285,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
   }
   const int64_t rr = ((int64_t)b * a.Hq + h) * a.Tp + min(row, a.Tp - 1);
   float lse_r = a.lsew[rr], D_r = a.Dw[rr];
+  float c_r = (h & 1) ? a.cw[((int64_t)b * (a.Hq / 2) + (h >> 1)) * a.Tp + min(row, a.Tp - 1)] : 1.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) retire(qf[ks]);
 #pragma unroll
@@ -301,6 +296,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
   }
   retire(lse_r);
   retire(D_r);
+  retire(c_r);
   // Row reads (K rows for S^T, V rows for dP^T): chunk (2 ks + hg) ^
   // swizzle(li) = 2 ks ^ (hg ^ swizzle(li)), so the address is
   // (tile base + lane part) ^ 32 ks.
@@ -390,9 +386,9 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
       }
   }
   if (!active || row >= T) return;
-  // dQ^T[c][row]: c = 32 cb + 8 (r>>2) + 4 hg + (r&3); dq = dS k / sqrt d
+  // dQ^T[c][row]: c = 32 cb + 8 (r>>2) + 4 hg + (r&3); dq = c_row dS k / sqrt d
   uint16_t* dst = (uint16_t*)a.dq.p + b * a.dq.sb + (int64_t)row * a.dq.st + h * a.dq.sh;
-  const float sc = -a.scale;
+  const float sc = -a.scale * c_r;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -411,48 +407,49 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
 }
 
 // ---- dK, dV ------------------------------------------------------------------
+// The two heads of a pair share dout: d attn of head 2p is dout and of head
+// 2p+1 is c dout with c = -sigmoid(lam) per row, so both heads' dP come from
+// the one product G = dout v^T (the odd head's is c G, its row term c E_odd
+// with E_h = rowsum(dout * attn_h)), dS_2p = P_2p (G - E_2p), dS_2p+1 =
+// c P_2p+1 (G - E_2p+1), and the pair's share of dV is the one product
+// (P_2p + c P_2p+1)^T dout.
 // Workgroup: (b, kv head g, 32 kNW keys), 2 kNW waves: waves m and m + kNW
 // own keys j0 + 32 m (on one SIMD: wave w runs on SIMD w mod 4) and loop over
-// the group's query heads and the row tiles at or after their keys, two
-// tiles per period:
-//   phase 1: the P wave (m) computes S = Q K^T and P for both tiles and
-//            writes P (bf16, the values its own dV product uses) to LDS;
-//            the dS wave (m + kNW) computes D - dP = D + dA (-V)^T for both
-//            tiles (its accumulators start at the tiles' D rows, read from
-//            LDS straight into them, and its V fragments are negated once);
+// the row tiles at or after their keys (rows descending) and, per row tile,
+// the group's head pairs, one (row tile, pair) per period:
+//   phase 1: the P wave (m) computes S and P of both heads, writes P_2p and
+//            c P_2p+1 (bf16) to LDS; the dS wave (m + kNW) computes -G =
+//            dout (-v)^T (its v fragments negated once);
 //   barrier;
-//   phase 2: the P wave accumulates dV^T += dA^T P; the dS wave reads P,
-//            forms P (D - dP) = -dS and accumulates -dK^T += Q^T (-dS).
-// Each product is computed once (S by the P wave only), and both waves of a
-// SIMD issue 16 MFMAs per tile.  A second barrier per period (before the
-// next period's P is written) is the stage barrier the copy ring needs
-// anyway.  Masks (diagonal tile, rows past T) are applied only where needed;
-// tiles of rows before the wave's keys skip the scores and accumulate zeros,
-// so the accumulators take one path through the loop.  Copy addresses
-// advance by running (head, row) counters from per-lane offsets computed
-// once.
+//   phase 2: the P wave accumulates dV^T += dout^T (P_2p + c P_2p+1); the
+//            dS wave reads both P, forms P_2p (E_2p - G) = -dS_2p and
+//            c P_2p+1 (E_2p+1 - G) = -dS_2p+1 and accumulates
+//            -dK^T += Q_2p^T (-dS_2p) + Q_2p+1^T (-dS_2p+1).
+// Per pair and wave 3 d / 16 MFMAs of each kind in each phase pair (S twice,
+// dV / G, dK twice: 6 products per pair instead of 8).  A second barrier per
+// period (before the next period's P is written) is the stage barrier the
+// copy ring needs anyway.  Masks (diagonal tile, rows past T) are applied
+// only where needed; tiles of rows before the wave's keys skip the scores
+// and accumulate zeros, so the accumulators take one path through the loop.
+// Copy pointers advance by running (pair, row) counters.
 template <int D>
 __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int NW = 2 * kNW;
   constexpr int KS = D / 16, CB = D / 32;
-  constexpr int RB = 2 * D;      // bytes of a tile row
-  constexpr int TB = kBT * RB;   // bytes of one tensor tile
-  constexpr int CH = TB / 1024;  // 1 KB copies per tensor tile
-  constexpr int CPR = D / 8;     // 16-byte chunks per row
-  static_assert(CH <= NW, "a wave copies at most one 1 KB chunk of a tensor tile");
-  constexpr int STAGE = 2 * TB + 256;  // [Q | dA (both ways) | lse, D of the 32 rows]
+  constexpr int TB = kBT * 2 * D;      // bytes of one tensor tile
+  constexpr int STAGE = 3 * TB + 768;  // [Q_2p | Q_2p+1 | dout (both ways) | lse x 2, E x 2, c of the 32 rows]
   static_assert(STAGE % 256 == 0 && TB % 256 == 0, "tile bases leave the row's chunk bits free");
-  constexpr int PSLOT = 2 * 1024;      // one tile's P of one P wave: 64 lanes x 2 x 16 bytes
-  constexpr int PBASE = 4 * STAGE;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * STAGE + kNW * 2 * PSLOT];
-  static_assert(4 * STAGE + kNW * 2 * PSLOT <= 160 * 1024, "LDS budget");
+  constexpr int PSLOT = 2 * 1024;      // one head's P of one P wave: 64 lanes x 2 x 16 bytes
+  constexpr int PBASE = 2 * STAGE;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE + kNW * 2 * PSLOT];
+  static_assert(2 * STAGE + kNW * 2 * PSLOT <= 160 * 1024, "LDS budget");
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, hg = lane >> 5;
   const int kb = wave % kNW;
   const bool swave = wave >= kNW;  // the dS wave (else the P wave)
-  const int T = a.T, G = a.G, BK = 32 * kNW;
+  const int T = a.T, G = a.G, NP = a.G / 2, BK = 32 * kNW;
   const int units = a.B * a.Hkv;
   const int unit = blockIdx.x % units, kt = blockIdx.x / units;  // low key tiles (most rows) first
   const int b = unit / a.Hkv, g = unit % a.Hkv;
@@ -461,12 +458,12 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   const int key = j0w + li;
   const int nrt = (T + kBT - 1) / kBT;  // row tiles of 32
   const int rt0 = J0 / kBT;
-  const int nit = G * (nrt - rt0);    // (row tile, head) iterations
-  // Iteration it: row tile nrt-1 - it/G (rows descending), head g*G + it%G.
+  const int nit = NP * (nrt - rt0);    // (row tile, pair) iterations
+  // Iteration it: row tile nrt-1 - it/NP (rows descending), pair g*NP + it%NP.
   // Every workgroup starts at the last row tile and they step down in
   // lockstep, so the workgroups of one kv group (one XCD: the group varies
-  // fastest in the grid order) read the same Q / dA tiles at about the same
-  // time, from that XCD's L2; a workgroup stops at its own first keys.
+  // fastest in the grid order) read the same Q / dout tiles at about the
+  // same time, from that XCD's L2; a workgroup stops at its own first keys.
 
   // B operands: K^T (the P wave) or -V^T (the dS wave) of this wave's keys
   bf16x8 kv[KS];
@@ -485,102 +482,79 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
     }
   }
 
-  // Copies.  Q and dA are each read as rows and transposed, so each tile is
-  // copied once in the both-ways layout.  Wave w < CH moves 1 KB chunk w of
-  // every tensor tile: the lane's 16 bytes go to destination row cr, chunk
-  // cc, and come from source chunk cc ^ swizzle(cr) (row cr, or the last row
-  // of a ragged tile).
-  const bool copier = wave < CH;
-  const int cr = (wave * 64 + lane) / CPR, cc = lane % CPR;
-  const uint32_t qst = (uint32_t)a.q.st, ast = (uint32_t)(a.Hq * D);  // element strides (< 2^24)
-  const int swu = u_swizzle<D>(cr);
-  auto src_off = [&](int srow, uint32_t st) {
-    return ((uint32_t)srow * st + (uint32_t)((cc ^ swu) * 8)) * 2u;
-  };
-  const uint32_t o_q = src_off(cr, qst), o_a = src_off(cr, ast);
-  const uint16_t* qg = (const uint16_t*)a.q.p + b * a.q.sb + (int64_t)g * G * a.q.sh;
-  const uint16_t* ag = a.dA + (int64_t)b * T * a.Hq * D + (int64_t)g * G * D;
-  const float* lg = a.lsew + ((int64_t)b * a.Hq + g * G) * a.Tp;
-  const float* dg = a.Dw + ((int64_t)b * a.Hq + g * G) * a.Tp;
-  // The next iteration to copy, with its Q / dA row pointers and its lse / D
-  // offset, advanced by constant element deltas (next head of the group, or
-  // head 0 of the row tile below) instead of being formed from (head, row)
-  // with 64-bit products for every tile.
-  int iss_h = 0, iss_r0 = (nrt - 1) * kBT;
-  const uint16_t* iss_q = qg + (int64_t)iss_r0 * a.q.st;
-  const uint16_t* iss_a = ag + (int64_t)iss_r0 * ast;
-  int64_t iss_l = iss_r0;  // head * Tp + row
-  const int64_t wq = -(int64_t)(G - 1) * a.q.sh - (int64_t)kBT * a.q.st;
-  const int64_t wa = -(int64_t)(G - 1) * D - (int64_t)kBT * ast, wl = -(int64_t)(G - 1) * a.Tp - kBT;
+  // Copies.  Q of both heads and dout are each read as rows and transposed:
+  // one copy each in the both-ways layout.  Waves 3-7 copy the rows' lse and
+  // E of both heads and c (padded arrays: always in bounds).
+  TileCopy<D, NW> cq0, cq1, co;
+  cq0.init(a.q.st, kBothLayout, wave, lane);
+  cq1.init(a.q.st, kBothLayout, wave, lane);
+  co.init(a.dout.st, kBothLayout, wave, lane);
+  const uint16_t* qg = (const uint16_t*)a.q.p + b * a.q.sb + (int64_t)g * G * a.q.sh;  // head g G, row 0
+  const uint16_t* og = (const uint16_t*)a.dout.p + b * a.dout.sb + (int64_t)g * NP * a.dout.sh;
+  const int rw = wave - (NW - 5);  // 0..4 on the row copiers
+  // rows of head g G + 2p (lse, E), + 1, or of pair g NP + p (c): base at row 0, step per pair
+  const float* rsrc = rw <= 1 ? a.lsew + ((int64_t)b * a.Hq + g * G + rw) * a.Tp
+                      : rw <= 3 ? a.Dw + ((int64_t)b * a.Hq + g * G + rw - 2) * a.Tp
+                                : a.cw + ((int64_t)b * (a.Hq / 2) + g * NP) * a.Tp;
+  const int64_t rstep = rw <= 3 ? 2 * (int64_t)a.Tp : (int64_t)a.Tp;
+  // the next iteration to copy: pair, first row, and the pair's head-2p / dout bases
+  int iss_p = 0, iss_r0 = (nrt - 1) * kBT;
+  const uint16_t* iss_q = qg;
+  const uint16_t* iss_o = og;
+  const float* iss_rs = rsrc;
   auto issue = [&](int stage) {
     const uint32_t st = lds0 + stage * STAGE;
     const int i0 = iss_r0;
-    const uint16_t* qp = iss_q;
-    const uint16_t* ap = iss_a;
-    const int64_t ro = iss_l;
-    if (++iss_h == G) {
-      iss_h = 0;
+    const uint16_t* qh = iss_q;
+    const uint16_t* oh = iss_o;
+    const float* rs = iss_rs;
+    if (++iss_p == NP) {
+      iss_p = 0;
       iss_r0 -= kBT;
-      iss_q += wq;
-      iss_a += wa;
-      iss_l += wl;
+      iss_q = qg;
+      iss_o = og;
+      iss_rs = rsrc;
     } else {
-      iss_q += a.q.sh;
-      iss_a += D;
-      iss_l += a.Tp;
+      iss_q += 2 * a.q.sh;
+      iss_o += a.dout.sh;
+      iss_rs += rstep;
     }
-    if (copier) {
-      uint32_t oq = o_q, oa = o_a;
-      if (i0 + kBT > T) {  // ragged last row tile: rows past T repeat row T - 1
-        const int rr = min(cr, T - 1 - i0);
-        oq = src_off(rr, qst);
-        oa = src_off(rr, ast);
-      }
-      const uint32_t dst = st + wave * 1024;
-      dma16_sbase(qp, oq, dst);
-      dma16_sbase(ap, oa, dst + TB);
+    if (i0 + kBT > T) {  // ragged last row tile: rows past T repeat row T - 1
+      TileDma<D, NW>::issue(qh, a.q.st, i0, T, kBothLayout, st, wave, lane);
+      TileDma<D, NW>::issue(qh + a.q.sh, a.q.st, i0, T, kBothLayout, st + TB, wave, lane);
+      TileDma<D, NW>::issue(oh, a.dout.st, i0, T, kBothLayout, st + 2 * TB, wave, lane);
+    } else {
+      cq0.issue(qh + (int64_t)i0 * a.q.st, st, wave);
+      cq1.issue(qh + a.q.sh + (int64_t)i0 * a.q.st, st + TB, wave);
+      co.issue(oh + (int64_t)i0 * a.dout.st, st + 2 * TB, wave);
     }
-    // the 32 rows' lse and D (padded arrays: always in bounds), 8 lanes x 16 B each
-    if (wave == NW - 2 && lane < 8) dma16_sbase(lg + ro, lane * 16, st + 2 * TB);
-    if (wave == NW - 1 && lane < 8) dma16_sbase(dg + ro, lane * 16, st + 2 * TB + 128);
+    if (rw >= 0 && lane < 8) dma16_sbase(rs + i0, lane * 16, st + 3 * TB + 128 * rw);
   };
   issue(0);
-  issue(1);
 
   // Row reads of A operands X[row li][16 ks + 8 hg ..]: chunk (2 ks + hg) ^
   // swizzle(li) = 2 ks ^ (hg ^ swizzle(li)); tile bases are multiples of 256,
   // so the read address is (tile base + rxs) ^ 32 ks.
-  const uint32_t rxs = (uint32_t)(li * RB + ((hg ^ u_swizzle<D>(li)) << 4));
+  const uint32_t rxs = (uint32_t)(li * (2 * D) + ((hg ^ u_swizzle<D>(li)) << 4));
   using TrB = TrBases<D, true>;
   TrB tb;
   tb.init(lane);
   const float sl2 = a.sl2;
-  // P exchange: the P wave of key block kb writes tile t's P at
-  // pslot(kb, t): two 16-byte chunks per lane, chunk-major (conflict-free).
+  // P exchange: the P wave of key block kb writes head e's P at
+  // pslot(kb, e): two 16-byte chunks per lane, chunk-major (conflict-free).
   const uint32_t pbase = lds0 + PBASE + kb * 2 * PSLOT + lane * 16;
   f32x16 acc[CB];  // dV^T (P wave) or -dK^T (dS wave) [c][key]
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
-
-  // Per-tile LDS bases, opaque to the compiler: every read below is one of
-  // them plus an immediate offset (or XOR a constant); otherwise the
-  // compiler hoists each "lane base + constant" into a register of its own.
-  auto bases = [&](int stage, uint32_t& qrow, uint32_t& arow, uint32_t& rowst, uint32_t (&tbase)[TrB::NV],
-                   uint32_t region) {
-    const uint32_t sb = lds0 + stage * STAGE;
-    qrow = sb + rxs;
-    arow = sb + TB + rxs;
-    rowst = sb + 2 * TB + 16 * hg;
+  // A += X^T Y over the tile's 32 rows (X^T by transpose reads of the tile at `tile`)
+  auto accumulate = [&](uint32_t tile, const bf16x8 (&y)[2]) {
+    uint32_t tbase[TrB::NV];
 #pragma unroll
-    for (int v = 0; v < TrB::NV; ++v) tbase[v] = sb + region + tb.b[v];
-    asm volatile("" : "+v"(qrow), "+v"(arow), "+v"(rowst));
+    for (int v = 0; v < TrB::NV; ++v) tbase[v] = tile + tb.b[v];
 #pragma unroll
     for (int v = 0; v < TrB::NV; ++v) asm volatile("" : "+v"(tbase[v]));
-  };
-  // A += X^T Y over the tile's 32 rows (X^T by transpose reads from tbase, Y the bf16 B operand)
-  auto accumulate = [&](const uint32_t (&tbase)[TrB::NV], const bf16x8 (&y)[2]) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -590,219 +564,145 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
         acc[cb] = mfma32x32x16(xa, y[kk], acc[cb]);
       }
   };
-
-  // ---- the P wave ----
-  // phase 1 of a tile: P (bf16, registers) and its copy in LDS
-  auto p_phase1 = [&](int stage, int i0, int t, bf16x8 (&pk)[2]) {
-    uint32_t qrow, arow, rowst, tbase[TrB::NV];
-    bases(stage, qrow, arow, rowst, tbase, TB);
-    pk[0] = pk[1] = bf16x8{};
-    if (i0 >= j0w) {  // (else: rows before this wave's keys, or an inactive wave)
-      bf16x8 qa[KS];
+  auto rows4 = [&](uint32_t at, f32x4 (&v)[4]) {  // 16 row values of the lane: rows 8(r>>2) + 4hg + (r&3)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qa[ks] = lds_read16(qrow ^ (32u * ks));
-      f32x4 lq[4];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        lq[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 32 * q4);
-      f32x16 s;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s = mfma32x32x16(qa[ks], kv[ks], s);  // S = Q K^T
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], sl2, -lq[r >> 2][r & 3]);
-      if (i0 == j0w || i0 + kBT > T) {  // diagonal tile or rows past T
-        // row offset ro = 4 hg + c (c = 8(r>>2) + (r&3)) is kept if ro < T - i0
-        // and ro >= li (the key's offset) on the diagonal
-        int lim = T - i0 - 4 * hg, dlo = i0 == j0w ? li - 4 * hg : -64;
-        asm volatile("" : "+v"(lim), "+v"(dlo));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = 8 * (r >> 2) + (r & 3);
-          x[r] = (c < lim && c >= dlo) ? x[r] : -INFINITY;
-        }
-      }
-      f32x8 e0, e1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(x[r]);
-        if (r < 8) e0[r] = pr; else e1[r - 8] = pr;
-      }
-      pk[0] = cvt_bf16x8(e0);
-      pk[1] = cvt_bf16x8(e1);
-    }
-    const uint32_t pw = pbase + t * PSLOT;
-    *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)pw = pk[0];
-    *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pw + 1024) = pk[1];
-  };
-  // phase 1 of both tiles of a period (the same row tile: G is even), with
-  // the common case -- rows strictly after this wave's keys, none past T:
-  // no mask -- as one straight-line block, so the exponentials of tile a
-  // run under the score MFMAs of tile b.
-  auto p_phase1_pair = [&](int sa, int sb, int i0, bf16x8 (&pa)[2], bf16x8 (&pb)[2]) {
-    if (!(i0 > j0w && i0 + kBT <= T)) {
-      p_phase1(sa, i0, 0, pa);
-      p_phase1(sb, i0, 1, pb);
-      return;
-    }
-    uint32_t qrow[2], arow_, rowst[2], tbase_[TrB::NV];
-    bases(sa, qrow[0], arow_, rowst[0], tbase_, TB);
-    bases(sb, qrow[1], arow_, rowst[1], tbase_, TB);
-    f32x16 s[2];
-    f32x4 lq[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      bf16x8 qa[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qa[ks] = lds_read16(qrow[t] ^ (32u * ks));
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        lq[t][q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst[t] + 32 * q4);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[t] = mfma32x32x16(qa[ks], kv[ks], s[t]);  // S = Q K^T
-    }
-    bf16x8* out[2] = {pa, pb};
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x8 e0, e1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(fmaf(s[t][r], sl2, -lq[t][r >> 2][r & 3]));
-        if (r < 8) e0[r] = pr; else e1[r - 8] = pr;
-      }
-      out[t][0] = cvt_bf16x8(e0);
-      out[t][1] = cvt_bf16x8(e1);
-    }
-    // reads of tile a, its score MFMAs with the reads of tile b, then the
-    // score MFMAs of tile b with the exponentials of tile a
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint32_t pw = pbase + t * PSLOT;
-      *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)pw = out[t][0];
-      *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pw + 1024) = out[t][1];
-    }
-  };
-  auto p_phase2 = [&](int stage, const bf16x8 (&pk)[2]) {
-    uint32_t qrow, arow, rowst, tbase[TrB::NV];
-    bases(stage, qrow, arow, rowst, tbase, TB);
-    accumulate(tbase, pk);  // dV^T += dA^T P
+    for (int q4 = 0; q4 < 4; ++q4) v[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(at + 32 * q4);
   };
 
-  // ---- the dS wave ----
-  // phase 1 of a tile: D - dP in registers
-  auto s_phase1 = [&](int stage, int i0, f32x16& dp) {
-    uint32_t qrow, arow, rowst, tbase[TrB::NV];
-    bases(stage, qrow, arow, rowst, tbase, 0);
-    if (i0 >= j0w) {
-      f32x4 dq4[4];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        dq4[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(rowst + 128 + 32 * q4);
-      bf16x8 da[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) da[ks] = lds_read16(arow ^ (32u * ks));
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = dq4[r >> 2][r & 3];  // D of the row
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) dp = mfma32x32x16(da[ks], kv[ks], dp);  // D + dA (-V)^T
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i + 4 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = 0.f;
-    }
-  };
-  // phase 2 of a tile: -dS = P (D - dP), then -dK^T += Q^T (-dS)
-  auto s_phase2 = [&](int stage, int t, const f32x16& dp) {
-    uint32_t qrow, arow, rowst, tbase[TrB::NV];
-    bases(stage, qrow, arow, rowst, tbase, 0);
-    const uint32_t pr_ = pbase + t * PSLOT;
-    const uint4 p0 = as_u4(*(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)pr_);
-    const uint4 p1 = as_u4(*(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(pr_ + 1024));
-    const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    f32x8 e0, e1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      // bf16 r of the 16 (element r & 1 of word r >> 1) as fp32
-      const uint32_t w = pw[r >> 1];
-      const float p = __builtin_bit_cast(float, (r & 1) ? (w & 0xffff0000u) : (w << 16));
-      const float ds = p * dp[r];  // P (D - dP) = -dS
-      if (r < 8) e0[r] = ds; else e1[r - 8] = ds;
-    }
-    const bf16x8 y[2] = {cvt_bf16x8(e0), cvt_bf16x8(e1)};
-    accumulate(tbase, y);
-  };
-
-  // nit is even (the group size G = Hq / Hkv is even), so every period has
-  // two tiles; one loop per role keeps each role's accumulators in one set
-  // of registers.
-  int cmp_h = 0, cmp_r0 = (nrt - 1) * kBT;  // the next iteration to compute
+  int cmp_p = 0, cmp_r0 = (nrt - 1) * kBT;  // the next iteration to compute
   auto next_row0 = [&]() {
     const int i0 = cmp_r0;
-    if (++cmp_h == G) {
-      cmp_h = 0;
+    if (++cmp_p == NP) {
+      cmp_p = 0;
       cmp_r0 -= kBT;
     }
     return i0;
   };
   if (!swave) {
-    for (int it = 0; it < nit; it += 2) {
-      const int sp = (it >> 1) & 1;  // stage pair of tiles it, it+1
+    for (int it = 0; it < nit; ++it) {
+      const int stage = it & 1;
       wait_copies();
-      __syncthreads();  // tiles it, it+1 visible; the other stage pair and the P slots are free
-      if (it + 2 < nit) {
-        issue(2 * (sp ^ 1));
-        issue(2 * (sp ^ 1) + 1);
+      __syncthreads();  // tile it visible; the other stage and the P slots are free
+      if (it + 1 < nit) issue(stage ^ 1);
+      const int i0 = next_row0();
+      uint32_t sb = lds0 + stage * STAGE;
+      asm volatile("" : "+v"(sb));
+      bf16x8 pc[2] = {};
+      if (i0 >= j0w) {  // (else: rows before this wave's keys, or an inactive wave)
+        f32x16 s[2];
+        f32x4 lq[2][4], cr[4];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          bf16x8 qa[KS];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) qa[ks] = lds_read16((sb + e * TB + rxs) ^ (32u * ks));
+          rows4(sb + 3 * TB + 128 * e + 16 * hg, lq[e]);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[e][r] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) s[e] = mfma32x32x16(qa[ks], kv[ks], s[e]);  // S = Q K^T
+        }
+        rows4(sb + 3 * TB + 512 + 16 * hg, cr);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
+        float x[2][16];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[e][r] = fmaf(s[e][r], sl2, -lq[e][r >> 2][r & 3]);
+        if (i0 == j0w || i0 + kBT > T) {  // diagonal tile or rows past T
+          // row offset ro = 4 hg + cc (cc = 8(r>>2) + (r&3)) is kept if ro < T - i0
+          // and ro >= li (the key's offset) on the diagonal
+          int lim = T - i0 - 4 * hg, dlo = i0 == j0w ? li - 4 * hg : -64;
+          asm volatile("" : "+v"(lim), "+v"(dlo));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int cc = 8 * (r >> 2) + (r & 3);
+            const bool keep = cc < lim && cc >= dlo;
+            x[0][r] = keep ? x[0][r] : -INFINITY;
+            x[1][r] = keep ? x[1][r] : -INFINITY;
+          }
+        }
+        f32x8 e0[2], e1[2], c0, c1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p0 = __builtin_amdgcn_exp2f(x[0][r]);
+          const float p1 = __builtin_amdgcn_exp2f(x[1][r]) * cr[r >> 2][r & 3];  // c P_2p+1
+          if (r < 8) {
+            e0[0][r] = p0, e0[1][r] = p1, c0[r] = p0 + p1;
+          } else {
+            e1[0][r - 8] = p0, e1[1][r - 8] = p1, c1[r - 8] = p0 + p1;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t pw = pbase + e * PSLOT;
+          *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)pw = cvt_bf16x8(e0[e]);
+          *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pw + 1024) = cvt_bf16x8(e1[e]);
+        }
+        pc[0] = cvt_bf16x8(c0);
+        pc[1] = cvt_bf16x8(c1);
       }
-      const int i0a = next_row0(), i0b = next_row0();
-      bf16x8 pa[2], pb[2];
-      p_phase1_pair(2 * sp, 2 * sp + 1, i0a, pa, pb);  // (i0b == i0a: G is even)
-      __syncthreads();  // P of both tiles in LDS
-      p_phase2(2 * sp, pa);
-      p_phase2(2 * sp + 1, pb);
+      __syncthreads();  // P of both heads in LDS
+      accumulate(sb + 2 * TB, pc);  // dV^T += dout^T (P_2p + c P_2p+1)
     }
   } else {
-    for (int it = 0; it < nit; it += 2) {
-      const int sp = (it >> 1) & 1;
+    for (int it = 0; it < nit; ++it) {
+      const int stage = it & 1;
       wait_copies();
       __syncthreads();
-      if (it + 2 < nit) {
-        issue(2 * (sp ^ 1));
-        issue(2 * (sp ^ 1) + 1);
+      if (it + 1 < nit) issue(stage ^ 1);
+      const int i0 = next_row0();
+      uint32_t sb = lds0 + stage * STAGE;
+      asm volatile("" : "+v"(sb));
+      f32x16 ng;
+      if (i0 >= j0w) {
+        bf16x8 oa[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) oa[ks] = lds_read16((sb + 2 * TB + rxs) ^ (32u * ks));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ng[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) ng = mfma32x32x16(oa[ks], kv[ks], ng);  // -G = dout (-V)^T
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i + 4 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
-      const int i0a = next_row0(), i0b = next_row0();
-      f32x16 da_, db_;
-      s_phase1(2 * sp, i0a, da_);
-      s_phase1(2 * sp + 1, i0b, db_);
-      __syncthreads();  // P of both tiles in LDS
-      s_phase2(2 * sp, 0, da_);
-      s_phase2(2 * sp + 1, 1, db_);
+      __syncthreads();  // P of both heads in LDS
+      bf16x8 y[2][2] = {};
+      if (i0 >= j0w) {
+        f32x4 ev[2][4];
+        rows4(sb + 3 * TB + 256 + 16 * hg, ev[0]);
+        rows4(sb + 3 * TB + 384 + 16 * hg, ev[1]);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t pr_ = pbase + e * PSLOT;
+          const uint4 p0 = as_u4(*(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)pr_);
+          const uint4 p1 = as_u4(*(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(pr_ + 1024));
+          const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+          f32x8 d0, d1;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            // bf16 r of the 16 (element r & 1 of word r >> 1) as fp32
+            const uint32_t w = pw[r >> 1];
+            const float p = __builtin_bit_cast(float, (r & 1) ? (w & 0xffff0000u) : (w << 16));
+            const float ds = p * (ev[e][r >> 2][r & 3] + ng[r]);  // P (E - G) = -dS (c inside P for e = 1)
+            if (r < 8) d0[r] = ds; else d1[r - 8] = ds;
+          }
+          y[e][0] = cvt_bf16x8(d0);
+          y[e][1] = cvt_bf16x8(d1);
+        }
+      }
+      accumulate(sb, y[0]);       // -dK^T += Q_2p^T (-dS_2p)
+      accumulate(sb + TB, y[1]);  //         + Q_2p+1^T (-dS_2p+1)
     }
   }
   if (!active || key >= T) return;

@@ -83,9 +83,9 @@ struct BwdArgs {
   const float* lse;  // [B][Hq][T] log2 softmax denominators (training forward)
   TOut dq, dk, dv;   // bf16, layouts of q / k / v
   TOut dlam;         // [B,T,Hq/2] fp32
-  uint16_t* dA;      // workspace [B][T][Hq][d] bf16: d attn per head
-  float* Dw;         // workspace [B][Hq][Tp]: rowsum(d attn * attn)
+  float* Dw;         // workspace [B][Hq][Tp]: E_h = rowsum(dout * attn_h)
   float* lsew;       // workspace [B][Hq][Tp]: lse, padded with zeros
+  float* cw;         // workspace [B][Hq/2][Tp]: c = -sigmoid(lam) (d attn of the odd head = c dout)
   float sl2;         // log2(e) / sqrt(d)
   float scale;       // 1 / sqrt(d)
   int B, T, Hq, Hkv, G, Tp;

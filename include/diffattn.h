@@ -317,8 +317,8 @@ da_status diffattn_v2_fwd_train_softmax1(int dtype, int B, int T, int Hq, int Hk
 
 /*
  * Bytes of device workspace diffattn_v2_bwd needs (0 if the sizes are
- * invalid): d attn per head in bf16 plus two fp32 arrays of B*Hq rows padded
- * to a multiple of 128 tokens.
+ * invalid): two fp32 arrays of B*Hq rows and one of B*Hq/2 rows, each row
+ * padded to a multiple of 128 tokens.
  */
 size_t diffattn_v2_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d);
 
@@ -340,7 +340,8 @@ size_t diffattn_v2_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d);
  *              256-byte aligned, owned by the caller.
  * Three kernels are enqueued on `stream` (a pre-pass, dq, then dk/dv); the
  * sums over heads and keys are taken in a fixed order (deterministic).
- * Token strides of q, k, v must be below 2^24 elements (DA_E_UNSUPPORTED).
+ * Token strides of q, k, v and dout must be below 2^24 elements
+ * (DA_E_UNSUPPORTED).
  */
 da_status diffattn_v2_bwd(int dtype, int B, int T, int Hq, int Hkv, int d,
                           da_in q, da_in k, da_in v, da_in lam, da_in attn,
