@@ -413,25 +413,26 @@ __global__ void __launch_bounds__(kNW * 64, 2) bwd_dq_kernel(const BwdArgs a) {
 // with E_h = rowsum(dout * attn_h)), dS_2p = P_2p (G - E_2p), dS_2p+1 =
 // c P_2p+1 (G - E_2p+1), and the pair's share of dV is the one product
 // (P_2p + c P_2p+1)^T dout.
-// Workgroup: (b, kv head g, 32 kNW keys), 2 kNW waves: waves m and m + kNW
-// own keys j0 + 32 m (on one SIMD: wave w runs on SIMD w mod 4) and loop over
-// the row tiles at or after their keys (rows descending) and, per row tile,
-// the group's head pairs, one (row tile, pair) per period:
-//   phase 1: the P wave (m) computes S and P of both heads, writes P_2p and
-//            c P_2p+1 (bf16) to LDS; the dS wave (m + kNW) computes -G =
-//            dout (-v)^T (its v fragments negated once);
+// Workgroup: (b, kv head g, 32 kNW keys), 2 kNW waves: waves m (A) and
+// m + kNW (B) own keys j0 + 32 m (on one SIMD: wave w runs on SIMD w mod 4)
+// and loop over the row tiles at or after their keys (rows descending) and,
+// per row tile, the group's head pairs, one (row tile, pair) per period:
+//   phase 1: A computes S and P of head 2p and -G = dout (-v)^T (its v
+//            fragments negated once) and writes P_2p (bf16) and -G (fp32)
+//            to LDS; B computes S and c P of head 2p+1;
 //   barrier;
-//   phase 2: the P wave accumulates dV^T += dout^T (P_2p + c P_2p+1); the
-//            dS wave reads both P, forms P_2p (E_2p - G) = -dS_2p and
-//            c P_2p+1 (E_2p+1 - G) = -dS_2p+1 and accumulates
-//            -dK^T += Q_2p^T (-dS_2p) + Q_2p+1^T (-dS_2p+1).
-// Per pair and wave 3 d / 16 MFMAs of each kind in each phase pair (S twice,
-// dV / G, dK twice: 6 products per pair instead of 8).  A second barrier per
-// period (before the next period's P is written) is the stage barrier the
-// copy ring needs anyway.  Masks (diagonal tile, rows past T) are applied
-// only where needed; tiles of rows before the wave's keys skip the scores
-// and accumulate zeros, so the accumulators take one path through the loop.
-// Copy pointers advance by running (pair, row) counters.
+//   phase 2: A forms P_2p (E_2p - G) = -dS_2p and accumulates its part of
+//            -dK^T += Q_2p^T (-dS_2p); B reads -G and P_2p, forms
+//            c P_2p+1 (E_2p+1 - G) = -dS_2p+1, accumulates its part of
+//            -dK^T += Q_2p+1^T (-dS_2p+1) and dV^T += dout^T (P_2p + c P_2p+1).
+// Each wave issues 3 d / 16 MFMAs per pair (one S, G or dV, one dK) and
+// one head's exponentials (6 products per pair instead of 8).  The two
+// waves' dK parts are added in one order at the end.  A second barrier per
+// period (before the next period's slots are written) is the stage barrier
+// the copy ring needs anyway.  Masks (diagonal tile, rows past T) are
+// applied only where needed; tiles of rows before the wave's keys skip the
+// scores and accumulate zeros, so the accumulators take one path through
+// the loop.  Copy pointers advance by running (pair, row) counters.
 template <int D>
 __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int NW = 2 * kNW;
@@ -439,16 +440,20 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   constexpr int TB = kBT * 2 * D;      // bytes of one tensor tile
   constexpr int STAGE = 3 * TB + 768;  // [Q_2p | Q_2p+1 | dout (both ways) | lse x 2, E x 2, c of the 32 rows]
   static_assert(STAGE % 256 == 0 && TB % 256 == 0, "tile bases leave the row's chunk bits free");
-  constexpr int PSLOT = 2 * 1024;      // one head's P of one P wave: 64 lanes x 2 x 16 bytes
-  constexpr int PBASE = 2 * STAGE;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE + kNW * 2 * PSLOT];
-  static_assert(2 * STAGE + kNW * 2 * PSLOT <= 160 * 1024, "LDS budget");
+  constexpr int PSLOT = 2 * 1024;      // P_2p of one key block: 64 lanes x 2 x 16 bytes
+  constexpr int GSLOT = 4 * 1024;      // -G of one key block: 64 lanes x 4 x 16 bytes
+  constexpr int XBASE = 2 * STAGE;
+  constexpr int SMEM_LOOP = XBASE + kNW * (PSLOT + GSLOT);
+  constexpr int SMEM_END = kNW * CB * 16 * 64 * 4;  // B's dK parts, after the loop
+  constexpr int SMEM = SMEM_LOOP > SMEM_END ? SMEM_LOOP : SMEM_END;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, hg = lane >> 5;
   const int kb = wave % kNW;
-  const bool swave = wave >= kNW;  // the dS wave (else the P wave)
+  const bool bwave = wave >= kNW;  // wave B (head 2p+1, dV), else wave A (head 2p, G)
   const int T = a.T, G = a.G, NP = a.G / 2, BK = 32 * kNW;
   const int units = a.B * a.Hkv;
   const int unit = blockIdx.x % units, kt = blockIdx.x / units;  // low key tiles (most rows) first
@@ -465,20 +470,22 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   // fastest in the grid order) read the same Q / dout tiles at about the
   // same time, from that XCD's L2; a workgroup stops at its own first keys.
 
-  // B operands: K^T (the P wave) or -V^T (the dS wave) of this wave's keys
-  bf16x8 kv[KS];
+  // B operands: K^T of this wave's keys (both waves); -V^T (wave A only)
+  bf16x8 kf[KS], vf[KS];
   {
-    const TIn& t = swave ? a.v : a.k;
-    const uint16_t* r = (const uint16_t*)t.p + b * t.sb + (int64_t)key * t.st + g * t.sh;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kv[ks] = as_bf16x8(key < T ? *(const uint4*)(r + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
-    const uint32_t flip = swave ? 0x80008000u : 0u;  // sign flip of every bf16 of V (exact)
+    const uint16_t* r = (const uint16_t*)a.k.p + b * a.k.sb + (int64_t)key * a.k.st + g * a.k.sh;
+    const uint16_t* rv = (const uint16_t*)a.v.p + b * a.v.sb + (int64_t)key * a.v.st + g * a.v.sh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      retire(kv[ks]);
-      const uint4 u = as_u4(kv[ks]);
-      kv[ks] = as_bf16x8(make_uint4(u.x ^ flip, u.y ^ flip, u.z ^ flip, u.w ^ flip));
+      kf[ks] = as_bf16x8(key < T ? *(const uint4*)(r + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+      vf[ks] = as_bf16x8(key < T && !bwave ? *(const uint4*)(rv + 16 * ks + 8 * hg) : make_uint4(0, 0, 0, 0));
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      retire(kf[ks]);
+      retire(vf[ks]);
+      const uint4 u = as_u4(vf[ks]);  // sign flip of every bf16 of V (exact)
+      vf[ks] = as_bf16x8(make_uint4(u.x ^ 0x80008000u, u.y ^ 0x80008000u, u.z ^ 0x80008000u, u.w ^ 0x80008000u));
     }
   }
 
@@ -540,16 +547,15 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   TrB tb;
   tb.init(lane);
   const float sl2 = a.sl2;
-  // P exchange: the P wave of key block kb writes head e's P at
-  // pslot(kb, e): two 16-byte chunks per lane, chunk-major (conflict-free).
-  const uint32_t pbase = lds0 + PBASE + kb * 2 * PSLOT + lane * 16;
-  f32x16 acc[CB];  // dV^T (P wave) or -dK^T (dS wave) [c][key]
+  // Exchange slots of key block kb (16-byte chunks, chunk-major: conflict-free)
+  const uint32_t pslot = lds0 + XBASE + kb * (PSLOT + GSLOT) + lane * 16, gslot = pslot + PSLOT;
+  f32x16 acc[CB], accv[CB];  // -dK^T part (both waves); dV^T (wave B) [c][key]
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[cb][r] = accv[cb][r] = 0.f;
   // A += X^T Y over the tile's 32 rows (X^T by transpose reads of the tile at `tile`)
-  auto accumulate = [&](uint32_t tile, const bf16x8 (&y)[2]) {
+  auto accumulate = [&](f32x16 (&A)[CB], uint32_t tile, const bf16x8 (&y)[2]) {
     uint32_t tbase[TrB::NV];
 #pragma unroll
     for (int v = 0; v < TrB::NV; ++v) tbase[v] = tile + tb.b[v];
@@ -561,7 +567,7 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
       for (int cb = 0; cb < CB; ++cb) {
         const bf16x8 xa = join_bf16x8(tr_read(tbase[TrB::src(cb, 0)] + TrB::off(cb, kk, 0)),
                                       tr_read(tbase[TrB::src(cb, 1)] + TrB::off(cb, kk, 1)));
-        acc[cb] = mfma32x32x16(xa, y[kk], acc[cb]);
+        A[cb] = mfma32x32x16(xa, y[kk], A[cb]);
       }
   };
   auto rows4 = [&](uint32_t at, f32x4 (&v)[4]) {  // 16 row values of the lane: rows 8(r>>2) + 4hg + (r&3)
@@ -578,78 +584,93 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
     }
     return i0;
   };
-  if (!swave) {
+  // S and P of head e (0: 2p, 1: 2p+1, times c) of the tile at sb, rows i0
+  auto probs = [&](uint32_t sb, int i0, int e, f32x8& p0, f32x8& p1) {
+    bf16x8 qa[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qa[ks] = lds_read16((sb + e * TB + rxs) ^ (32u * ks));
+    f32x4 lq[4], cr[4];
+    rows4(sb + 3 * TB + 128 * e + 16 * hg, lq);
+    if (e) rows4(sb + 3 * TB + 512 + 16 * hg, cr);
+    f32x16 sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sc = mfma32x32x16(qa[ks], kf[ks], sc);  // S = Q K^T
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + 4 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = fmaf(sc[r], sl2, -lq[r >> 2][r & 3]);
+    if (i0 == j0w || i0 + kBT > T) {  // diagonal tile or rows past T
+      // row offset ro = 4 hg + cc (cc = 8(r>>2) + (r&3)) is kept if ro < T - i0
+      // and ro >= li (the key's offset) on the diagonal
+      int lim = T - i0 - 4 * hg, dlo = i0 == j0w ? li - 4 * hg : -64;
+      asm volatile("" : "+v"(lim), "+v"(dlo));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int cc = 8 * (r >> 2) + (r & 3);
+        x[r] = (cc < lim && cc >= dlo) ? x[r] : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float pr = __builtin_amdgcn_exp2f(x[r]);
+      if (e) pr *= cr[r >> 2][r & 3];  // c P_2p+1
+      if (r < 8) p0[r] = pr; else p1[r - 8] = pr;
+    }
+  };
+  if (!bwave) {
     for (int it = 0; it < nit; ++it) {
       const int stage = it & 1;
       wait_copies();
-      __syncthreads();  // tile it visible; the other stage and the P slots are free
+      __syncthreads();  // tile it visible; the other stage and the slots are free
       if (it + 1 < nit) issue(stage ^ 1);
       const int i0 = next_row0();
       uint32_t sb = lds0 + stage * STAGE;
       asm volatile("" : "+v"(sb));
-      bf16x8 pc[2] = {};
+      f32x8 p0, p1;
+      f32x16 ng;
       if (i0 >= j0w) {  // (else: rows before this wave's keys, or an inactive wave)
-        f32x16 s[2];
-        f32x4 lq[2][4], cr[4];
+        bf16x8 oa[KS];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          bf16x8 qa[KS];
+        for (int ks = 0; ks < KS; ++ks) oa[ks] = lds_read16((sb + 2 * TB + rxs) ^ (32u * ks));
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) qa[ks] = lds_read16((sb + e * TB + rxs) ^ (32u * ks));
-          rows4(sb + 3 * TB + 128 * e + 16 * hg, lq[e]);
+        for (int r = 0; r < 16; ++r) ng[r] = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[e][r] = 0.f;
+        for (int ks = 0; ks < KS; ++ks) ng = mfma32x32x16(oa[ks], vf[ks], ng);  // -G = dout (-V)^T
+        probs(sb, i0, 0, p0, p1);
+        *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)pslot = cvt_bf16x8(p0);
+        *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pslot + 1024) = cvt_bf16x8(p1);
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) s[e] = mfma32x32x16(qa[ks], kv[ks], s[e]);  // S = Q K^T
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = ng[4 * q4 + e];
+          *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(gslot + 1024 * q4) = v4;
         }
-        rows4(sb + 3 * TB + 512 + 16 * hg, cr);
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * KS; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        // lane: key li; register r: row i0 + 8(r>>2) + 4hg + (r&3)
-        float x[2][16];
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) x[e][r] = fmaf(s[e][r], sl2, -lq[e][r >> 2][r & 3]);
-        if (i0 == j0w || i0 + kBT > T) {  // diagonal tile or rows past T
-          // row offset ro = 4 hg + cc (cc = 8(r>>2) + (r&3)) is kept if ro < T - i0
-          // and ro >= li (the key's offset) on the diagonal
-          int lim = T - i0 - 4 * hg, dlo = i0 == j0w ? li - 4 * hg : -64;
-          asm volatile("" : "+v"(lim), "+v"(dlo));
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int cc = 8 * (r >> 2) + (r & 3);
-            const bool keep = cc < lim && cc >= dlo;
-            x[0][r] = keep ? x[0][r] : -INFINITY;
-            x[1][r] = keep ? x[1][r] : -INFINITY;
-          }
-        }
-        f32x8 e0[2], e1[2], c0, c1;
+      }
+      __syncthreads();  // P_2p and -G in LDS
+      bf16x8 y[2] = {};
+      if (i0 >= j0w) {
+        f32x4 ev[4];
+        rows4(sb + 3 * TB + 256 + 16 * hg, ev);
+        f32x8 d0, d1;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p0 = __builtin_amdgcn_exp2f(x[0][r]);
-          const float p1 = __builtin_amdgcn_exp2f(x[1][r]) * cr[r >> 2][r & 3];  // c P_2p+1
-          if (r < 8) {
-            e0[0][r] = p0, e0[1][r] = p1, c0[r] = p0 + p1;
-          } else {
-            e1[0][r - 8] = p0, e1[1][r - 8] = p1, c1[r - 8] = p0 + p1;
-          }
+          const float p = r < 8 ? p0[r] : p1[r - 8];
+          const float ds = p * (ev[r >> 2][r & 3] + ng[r]);  // P (E - G) = -dS
+          if (r < 8) d0[r] = ds; else d1[r - 8] = ds;
         }
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const uint32_t pw = pbase + e * PSLOT;
-          *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)pw = cvt_bf16x8(e0[e]);
-          *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pw + 1024) = cvt_bf16x8(e1[e]);
-        }
-        pc[0] = cvt_bf16x8(c0);
-        pc[1] = cvt_bf16x8(c1);
+        y[0] = cvt_bf16x8(d0);
+        y[1] = cvt_bf16x8(d1);
       }
-      __syncthreads();  // P of both heads in LDS
-      accumulate(sb + 2 * TB, pc);  // dV^T += dout^T (P_2p + c P_2p+1)
+      accumulate(acc, sb, y);  // -dK^T += Q_2p^T (-dS_2p)
     }
   } else {
     for (int it = 0; it < nit; ++it) {
@@ -660,62 +681,78 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
       const int i0 = next_row0();
       uint32_t sb = lds0 + stage * STAGE;
       asm volatile("" : "+v"(sb));
-      f32x16 ng;
+      f32x8 p0, p1;
+      if (i0 >= j0w) probs(sb, i0, 1, p0, p1);
+      __syncthreads();  // P_2p and -G in LDS
+      bf16x8 y[2] = {}, pc[2] = {};
       if (i0 >= j0w) {
-        bf16x8 oa[KS];
+        f32x4 ev[4], gv[4];
+        rows4(sb + 3 * TB + 384 + 16 * hg, ev);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) oa[ks] = lds_read16((sb + 2 * TB + rxs) ^ (32u * ks));
+        for (int q4 = 0; q4 < 4; ++q4)
+          gv[q4] = *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)(gslot + 1024 * q4);
+        const uint4 w0 = as_u4(*(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)pslot);
+        const uint4 w1 = as_u4(*(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(pslot + 1024));
+        const uint32_t pw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        f32x8 d0, d1, c0, c1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ng[r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) ng = mfma32x32x16(oa[ks], kv[ks], ng);  // -G = dout (-V)^T
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int i = 0; i < KS; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i + 4 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      }
-      __syncthreads();  // P of both heads in LDS
-      bf16x8 y[2][2] = {};
-      if (i0 >= j0w) {
-        f32x4 ev[2][4];
-        rows4(sb + 3 * TB + 256 + 16 * hg, ev[0]);
-        rows4(sb + 3 * TB + 384 + 16 * hg, ev[1]);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const uint32_t pr_ = pbase + e * PSLOT;
-          const uint4 p0 = as_u4(*(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)pr_);
-          const uint4 p1 = as_u4(*(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(pr_ + 1024));
-          const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-          f32x8 d0, d1;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            // bf16 r of the 16 (element r & 1 of word r >> 1) as fp32
-            const uint32_t w = pw[r >> 1];
-            const float p = __builtin_bit_cast(float, (r & 1) ? (w & 0xffff0000u) : (w << 16));
-            const float ds = p * (ev[e][r >> 2][r & 3] + ng[r]);  // P (E - G) = -dS (c inside P for e = 1)
-            if (r < 8) d0[r] = ds; else d1[r - 8] = ds;
+        for (int r = 0; r < 16; ++r) {
+          const float p = r < 8 ? p0[r] : p1[r - 8];  // c P_2p+1
+          const uint32_t w = pw[r >> 1];  // P_2p: bf16 r of the 16 (element r & 1 of word r >> 1)
+          const float pe = __builtin_bit_cast(float, (r & 1) ? (w & 0xffff0000u) : (w << 16));
+          const float ds = p * (ev[r >> 2][r & 3] + gv[r >> 2][r & 3]);  // c P (E - G) = -dS
+          if (r < 8) {
+            d0[r] = ds, c0[r] = pe + p;
+          } else {
+            d1[r - 8] = ds, c1[r - 8] = pe + p;
           }
-          y[e][0] = cvt_bf16x8(d0);
-          y[e][1] = cvt_bf16x8(d1);
         }
+        y[0] = cvt_bf16x8(d0);
+        y[1] = cvt_bf16x8(d1);
+        pc[0] = cvt_bf16x8(c0);
+        pc[1] = cvt_bf16x8(c1);
       }
-      accumulate(sb, y[0]);       // -dK^T += Q_2p^T (-dS_2p)
-      accumulate(sb + TB, y[1]);  //         + Q_2p+1^T (-dS_2p+1)
+      accumulate(acc, sb + TB, y);       // -dK^T += Q_2p+1^T (-dS_2p+1)
+      accumulate(accv, sb + 2 * TB, pc);  // dV^T += dout^T (P_2p + c P_2p+1)
     }
   }
+  // -dK^T = A's part + B's part (one order), through LDS once every wave is done
+  __syncthreads();
+  f32x4* xk = (f32x4*)smem + (size_t)kb * CB * 4 * 64 + lane;  // [kb][cb][q4][lane]
+  if (bwave) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = acc[cb][4 * q4 + e];
+        xk[(cb * 4 + q4) * 64] = v4;
+      }
+  }
+  __syncthreads();
+  if (!bwave) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v4 = xk[(cb * 4 + q4) * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[cb][4 * q4 + e] += v4[e];
+      }
+  }
   if (!active || key >= T) return;
-  const TOut& o = swave ? a.dk : a.dv;
-  const float sc = swave ? -a.scale : 1.f;
+  const TOut& o = bwave ? a.dv : a.dk;
+  const float sc = bwave ? 1.f : -a.scale;
   uint16_t* dst = (uint16_t*)o.p + b * o.sb + (int64_t)key * o.st + g * o.sh;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x16& A = bwave ? accv[cb] : acc[cb];
       uint2 w;
-      w.x = pack_bf16x2(acc[cb][4 * g4 + 0] * sc, acc[cb][4 * g4 + 1] * sc);
-      w.y = pack_bf16x2(acc[cb][4 * g4 + 2] * sc, acc[cb][4 * g4 + 3] * sc);
+      w.x = pack_bf16x2(A[4 * g4 + 0] * sc, A[4 * g4 + 1] * sc);
+      w.y = pack_bf16x2(A[4 * g4 + 2] * sc, A[4 * g4 + 3] * sc);
       *(uint2*)(dst + 32 * cb + 8 * g4 + 4 * hg) = w;
     }
 }
