@@ -10,25 +10,28 @@
 //   log-sum-exp), dP = d attn_h v^T, dS = P o (dP - D) with
 //   D = rowsum(d attn_h o attn_h), dq = dS k / sqrt d, dk += dS^T q / sqrt d,
 //   dv += P^T d attn_h.  (With the off-by-one softmax P carries the extra
-//   term in lse, and the same steps hold.)
+//   term in lse, and the same steps hold.)  Since d attn of both heads of a
+//   pair is a row multiple of dout, the pair's dP are row multiples of the
+//   one G = dout v^T and D_h = c_h E_h with E_h = rowsum(dout o attn_h).
 //
 // Three kernels (designed for gfx950):
-//   * bwd_pre: 16 lanes per (b, token, pair): d attn of both heads (bf16, to
-//     the workspace), D of both heads, d lam, and a copy of lse padded to a
-//     multiple of 128 rows (so row blocks read whole float4 groups).
+//   * bwd_pre: 16 lanes per (b, token, pair): E of both heads, c = -sigmoid
+//     (lam), d lam, and a copy of lse padded to a multiple of 128 rows (so
+//     row blocks read whole float4 groups).
 //   * bwd_dq: the forward's structure with the key loop kept: a wave owns 32
 //     query rows of one head, K/V tiles of 32 keys stream through LDS
-//     (global_load_lds), S^T = K Q^T and dP^T = V dA^T come from
-//     v_mfma_f32_32x32x16_bf16 with Q / dA fragments held in registers, and
-//     dQ^T += K^T dS^T takes K^T through ds_read_b64_tr_b16 (K is copied to
-//     LDS twice, once swizzled for row reads and once for transpose reads).
-//   * bwd_dkdv: the mirror image: two waves own 32 keys of one kv head (one
-//     accumulates dV, the other dK) and loop over the group's heads and the
-//     query rows at or after their keys; S = Q K^T and dP = dA V^T with K / V
-//     fragments in registers, then dV^T += dA^T P and dK^T += Q^T dS with
-//     transpose reads of the Q and dA tiles.  The gradients of a kv head are
-//     summed over its query heads inside a wave, so nothing is reduced
-//     across workgroups (no atomics: deterministic).
+//     (global_load_lds), S^T = K Q^T and G^T = V dout^T come from
+//     v_mfma_f32_32x32x16_bf16 with Q / dout fragments held in registers,
+//     and dQ^T += K^T dS^T takes K^T through ds_read_b64_tr_b16 (K is copied
+//     to LDS once, in a layout that serves both reads); the odd head's dQ
+//     row is scaled by c at the store.
+//   * bwd_dkdv: the mirror image: two waves own 32 keys of one kv head and
+//     loop over the query rows at or after their keys and the group's head
+//     pairs, forming S of each head, G and dV once per pair, and dK of each
+//     head, from K / V fragments in registers and transpose reads of the Q
+//     and dout tiles.  The gradients of a kv head are summed over its query
+//     heads inside the workgroup, so nothing is reduced across workgroups
+//     (no atomics: deterministic).
 #include <math.h>
 
 #include <type_traits>
@@ -215,10 +218,10 @@ struct DqCfg {
 //
 // As in the dK/dV kernel, the accumulators take one path through the loop
 // body (key tiles after a wave's rows skip the scores and accumulate zeros),
-// the mask is applied only on the diagonal tile, and D is folded into the dP
-// accumulator: the dA fragments are negated once
-// and the accumulator starts at D, so the MFMAs leave D - dP, P (D - dP) =
-// -dS, and dQ is negated when stored.
+// the mask is applied only on the diagonal tile, and E is folded into the G
+// accumulator: the dout fragments are negated once and the accumulator
+// starts at E, so the MFMAs leave E - G, P (E - G) = -dS / c, and dQ is
+// scaled by -c when stored.
 template <int D, int DV>
 __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned char* smem) {
   constexpr int KS = D / 16, KSV = DV / 16, CB = D / 32;
@@ -345,7 +348,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
 #pragma unroll
       for (int ks = 0; ks < KM; ++ks) {
         if (ks < KS) s = mfma32x32x16(ka[ks], qf[ks], s);     // S^T = K Q^T
-        if (ks < KSV) dp = mfma32x32x16(va[ks], af[ks], dp);  // D - dP^T = D + V (-dA)^T
+        if (ks < KSV) dp = mfma32x32x16(va[ks], af[ks], dp);  // E - G^T = E + V (-dout)^T
       }
       constexpr int NMF = KS + KSV;
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
