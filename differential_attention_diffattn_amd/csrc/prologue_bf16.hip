@@ -141,11 +141,18 @@ __global__ void __launch_bounds__(kProjWaves * 64) lambda_proj_kernel(const LamP
 #ifndef DA_PS_NT
 #define DA_PS_NT 0  // x copies with the non-temporal policy
 #endif
-constexpr int kPsWaves = 4, kPsChunk = 256, kPsStages = DA_PS_STAGES;  // dm per chunk
-constexpr int kPsRowBytes = kPsChunk * 2;    // 512 B
-constexpr int kPsTile = 32 * kPsRowBytes;    // 16 KB: one operand tile of a chunk
+#ifndef DA_PS_CHUNK
+#define DA_PS_CHUNK 256  // dm per chunk of the streaming projection (256 or 512)
+#endif
+constexpr int kPsWaves = 4, kPsChunk = DA_PS_CHUNK, kPsStages = DA_PS_STAGES;  // dm per chunk
+constexpr int kPsRowBytes = kPsChunk * 2;    // 512 B or 1 KB
+constexpr int kPsRPI = 1024 / kPsRowBytes;   // rows per 1 KB copy (2 or 1)
+constexpr int kPsTile = 32 * kPsRowBytes;    // one operand tile of a chunk
 constexpr int kPsStage = 2 * kPsTile;        // x tile, w tile
-constexpr int kPsCopies = 2 * 16 / kPsWaves; // 1 KB copies per wave per chunk (8)
+constexpr int kPsNIW = 32 / kPsRPI / kPsWaves;  // 1 KB copies per wave per tensor and chunk
+constexpr int kPsCopies = 2 * kPsNIW;        // per wave and chunk
+constexpr int kPsKW = kPsChunk / 16 / kPsWaves;  // k-steps per wave and chunk
+static_assert(kPsChunk == 256 || kPsChunk == 512, "projection chunk");
 static_assert(kPsStages >= 2 && kPsStages <= 5 && kPsStages * kPsStage <= 160 * 1024, "projection ring");
 
 __global__ void __launch_bounds__(kPsWaves * 64) lambda_proj_stream_kernel(const LamProjArgs a) {
@@ -166,28 +173,32 @@ __global__ void __launch_bounds__(kPsWaves * 64) lambda_proj_stream_kernel(const
   // adds each half's distance to the lane offset (the launcher uses this
   // kernel only when every distance between rows fits in 31 bits).  Bases and
   // distances do not depend on the chunk, so they are formed once.
-  const char* xb[kPsCopies / 2];
-  const char* wb[kPsCopies / 2];
-  uint32_t xd[kPsCopies / 2], wd[kPsCopies / 2];
+  // (With 1 KB rows, copy i of wave w moves row NIW w + i whole.)
+  const char* xb[kPsNIW];
+  const char* wb[kPsNIW];
+  uint32_t xd[kPsNIW], wd[kPsNIW];
 #pragma unroll
-  for (int i = 0; i < kPsCopies / 2; ++i) {
-    const int rp = 2 * (4 * wave + i);  // first row of the pair (uniform)
-    const long long t0 = min(r0 + rp, ntok - 1), t1 = min(r0 + rp + 1, ntok - 1);
+  for (int i = 0; i < kPsNIW; ++i) {
+    const int rp = kPsRPI * (kPsNIW * wave + i);  // first row of the copy (uniform)
+    const int r1 = kPsRPI == 2 ? rp + 1 : rp;
+    const long long t0 = min(r0 + rp, ntok - 1), t1 = min(r0 + r1, ntok - 1);
     const char* x0 = (const char*)((const uint16_t*)a.x.p + (t0 / a.T) * a.x.sb + (int64_t)(t0 % a.T) * a.x.st);
     const char* x1 = (const char*)((const uint16_t*)a.x.p + (t1 / a.T) * a.x.sb + (int64_t)(t1 % a.T) * a.x.st);
     xb[i] = x0 < x1 ? x0 : x1;
     xd[i] = (uint32_t)((hg ? x1 : x0) - xb[i]);
     wb[i] = (const char*)((const uint16_t*)a.w.p + (int64_t)min(p0 + rp, a.P - 1) * a.w.sh);
-    const char* w1 = (const char*)((const uint16_t*)a.w.p + (int64_t)min(p0 + rp + 1, a.P - 1) * a.w.sh);
+    const char* w1 = (const char*)((const uint16_t*)a.w.p + (int64_t)min(p0 + r1, a.P - 1) * a.w.sh);
     wd[i] = (uint32_t)((hg ? w1 : wb[i]) - wb[i]);
   }
   auto issue = [&](int ch, int stage) {
     const uint32_t st = lds0 + stage * kPsStage;
 #pragma unroll
-    for (int i = 0; i < kPsCopies / 2; ++i) {
-      const int rp = 2 * (4 * wave + i);
+    for (int i = 0; i < kPsNIW; ++i) {
+      const int rp = kPsRPI * (kPsNIW * wave + i);
       const int chr = ch + rot < nch ? ch + rot : ch + rot - nch;  // chunk of the rotated order
-      const uint32_t off = (uint32_t)chr * kPsRowBytes + (uint32_t)((li ^ ((rp + hg) & 15)) << 4);
+      // lane's destination chunk of its row: li (two rows per copy) or lane (one)
+      const int dchunk = kPsRPI == 2 ? li : lane, drow = kPsRPI == 2 ? rp + hg : rp;
+      const uint32_t off = (uint32_t)chr * kPsRowBytes + (uint32_t)((dchunk ^ (drow & 15)) << 4);
       if (DA_PS_NT)
         dma16_sbase_nt(xb[i], off + xd[i], st + rp * kPsRowBytes);
       else
@@ -216,8 +227,8 @@ __global__ void __launch_bounds__(kPsWaves * 64) lambda_proj_stream_kernel(const
     if (ch + kPsStages - 1 < nch) issue(ch + kPsStages - 1, (ch + kPsStages - 1) % kPsStages);
     const uint32_t st = lds0 + stage * kPsStage;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = 2 * (4 * wave + j) + hg;  // 16-byte chunk of the row this lane's half reads
+    for (int j = 0; j < kPsKW; ++j) {
+      const int q = 2 * (kPsKW * wave + j) + hg;  // 16-byte chunk of the row this lane's half reads
       const uint32_t o = rrow + (uint32_t)((q ^ (li & 15)) << 4);
       acc = mfma32x32x16(lds_read16(st + o), lds_read16(st + kPsTile + o), acc);
     }
