@@ -247,9 +247,9 @@ def test_v1_backward_3b_shape_sampled_heads():
 @pytest.mark.parametrize("G,d", [(2, 64), (8, 128)])
 def test_v2_row0_dq_is_zero(G, d):
     """Row 0 of every head sees one key, so its P is 1 and dS = dP - D = 0:
-    dq there is exactly 0.  The kernels take D from the same bf16 d attn the
-    dP product sees (the odd head's -sigmoid(lam) dout rounded), so what is
-    left is fp32 summation order."""
+    dq there is exactly 0.  The kernels form G = dout v^T and E = <dout,
+    attn> from the same bf16 dout and apply the odd head's -sigmoid(lam) in
+    fp32 to both, so what is left is fp32 summation order."""
     y, dout = _inputs(2, 300, G * 2, 2, d, seed=930 + G)
     _, attn, lse = binding.v2_fwd_train(y["q"], y["k"], y["v"], y["lam"])
     dq = binding.v2_bwd(y["q"], y["k"], y["v"], y["lam"], attn, lse, dout)[0]
