@@ -67,7 +67,7 @@ def test_fwd_train(T, G, d, s1):
 
 
 @pytest.mark.parametrize("T", [1, 31, 32, 33, 100, 300])
-@pytest.mark.parametrize("G,d", [(2, 64), (8, 128), (4, 64), (2, 128)])
+@pytest.mark.parametrize("G,d", [(2, 64), (8, 128), (4, 64), (2, 128), (6, 64)])
 def test_backward(T, G, d):
     Hkv = 2
     B = 2 if T < 200 else 1
