@@ -184,6 +184,17 @@ def test_v1_backward(T, d, layer):
     _v1_check(grads, args, layer, dout, f"T{T} d{d} layer{layer}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_v1_backward_xcd_grouped_ragged(d):
+    """(batch, head) units divisible by 8 (the grid groups a head's work on
+    one XCD) with a ragged T, every gradient element against the oracle."""
+    args, dout = _v1_in(2, 4, 300, d, seed=1150 + d)
+    _, a1, a2, lse = binding.v1_fwd_train(*args, 3)
+    grads = binding.v1_bwd(*args, 3, a1, a2, lse, dout)
+    torch.cuda.synchronize()
+    _v1_check(grads, args, 3, dout, f"B2 H4 T300 d{d}")
+
+
 def test_v1_backward_softmax1():
     args, dout = _v1_in(1, 2, 150, 64, seed=1200)
     _, a1, a2, lse = binding.v1_fwd_train(*args, 2, softmax1=True)
