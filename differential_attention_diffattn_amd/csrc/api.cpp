@@ -397,16 +397,15 @@ static da_status v2_fwd_impl(int softmax1, int dtype, int B, int T, int Hq, int 
   return launch_status(da::launch_prefill_v2_bf16(d, a, (hipStream_t)stream));
 }
 
-// DIFF V2 backward: sizes of the three workspace regions.
+// DIFF V2 backward: sizes of the two workspace regions.
 struct BwdWs {
-  size_t rows, crow;  // bytes of each [B][Hq][Tp] fp32 array; of the [B][Hq/2][Tp] one
-  size_t total() const { return 2 * rows + crow; }
+  size_t rows;  // bytes of each [B][Hq][Tp] fp32 array
+  size_t total() const { return 2 * rows; }
 };
 static BwdWs bwd_ws(int B, int T, int Hq, int d) {
   (void)d;
   BwdWs w;
   w.rows = ((size_t)B * Hq * da::backward_padded_rows(T) * 4 + 255) / 256 * 256;
-  w.crow = ((size_t)B * (Hq / 2) * da::backward_padded_rows(T) * 4 + 255) / 256 * 256;
   return w;
 }
 
@@ -439,7 +438,6 @@ static da_status v2_bwd_impl(int dtype, int B, int T, int Hq, int Hkv, int d, da
   a.dq = tout(dq), a.dk = tout(dk), a.dv = tout(dv), a.dlam = tout(dlam);
   a.Dw = (float*)workspace;
   a.lsew = (float*)((char*)workspace + w.rows);
-  a.cw = (float*)((char*)workspace + 2 * w.rows);
   a.sl2 = log2e_over_sqrt(d);
   a.scale = (float)(1.0 / sqrt((double)d));
   a.B = B, a.T = T, a.Hq = Hq, a.Hkv = Hkv, a.G = Hq / Hkv;

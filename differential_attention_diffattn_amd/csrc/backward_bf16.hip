@@ -68,9 +68,8 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdArgs a) {
   const int t = (int)((item / P) % a.Tp);
   const int b = (int)(item / ((long long)P * a.Tp));
   const int64_t r0 = ((int64_t)b * a.Hq + 2 * p) * a.Tp + t, r1 = r0 + a.Tp;  // rows of heads 2p, 2p+1
-  const int64_t rc = ((int64_t)b * P + p) * a.Tp + t;  // the pair's row
-  if (t >= a.T) {  // padding rows: zero E, lse and c (masked where read)
-    if (l16 == 0) a.Dw[r0] = a.Dw[r1] = a.lsew[r0] = a.lsew[r1] = a.cw[rc] = 0.f;
+  if (t >= a.T) {  // padding rows: zero E and lse (masked where read)
+    if (l16 == 0) a.Dw[r0] = a.Dw[r1] = a.lsew[r0] = a.lsew[r1] = 0.f;
     return;
   }
   const int c = EL * l16;
@@ -85,9 +84,10 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdArgs a) {
   auto hi = [](uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); };
   const float lg = ((const float*)a.lam.p)[b * a.lam.sb + (int64_t)t * a.lam.st + p * a.lam.sh];
   const float s = sigmoid_f32(lg);
-  // E_2p = <dout, attn_2p> and E_2p+1 = <dout, attn_2p+1> (the odd head's
-  // d attn is c dout with c = -s, applied in fp32 where it is used); the
-  // second also feeds d lam.
+  // E_2p = <dout, attn_2p> and E_2p+1 = <dout, attn_2p+1>; the second also
+  // feeds d lam.  The odd head's d attn is c dout with c = -s: its lse is
+  // kept as lse - log2(s), so the P rebuilt from it is s P = -c P (0 where
+  // s is 0), and the kernels fold the sign in.
   float x = 0.f, y = 0.f;
 #pragma unroll
   for (int i = 0; i < EL / 2; ++i) {
@@ -100,8 +100,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdArgs a) {
     a.Dw[r0] = x;
     a.Dw[r1] = y;
     a.lsew[r0] = a.lse[((int64_t)b * a.Hq + 2 * p) * a.T + t];
-    a.lsew[r1] = a.lse[((int64_t)b * a.Hq + 2 * p + 1) * a.T + t];
-    a.cw[rc] = -s;
+    a.lsew[r1] = a.lse[((int64_t)b * a.Hq + 2 * p + 1) * a.T + t] - log2f(s);
     ((float*)a.dlam.p)[b * a.dlam.sb + (int64_t)t * a.dlam.st + p * a.dlam.sh] = -s * (1.f - s) * y;
   }
 }
@@ -220,8 +219,8 @@ struct DqCfg {
 // body (key tiles after a wave's rows skip the scores and accumulate zeros),
 // the mask is applied only on the diagonal tile, and E is folded into the G
 // accumulator: the dout fragments are negated once and the accumulator
-// starts at E, so the MFMAs leave E - G, P (E - G) = -dS / c, and dQ is
-// scaled by -c when stored.
+// starts at E, so the MFMAs leave E - G, P (E - G) = -dS (the odd head: +dS,
+// its P being -c P), and dQ takes the sign when stored.
 template <int D, int DV>
 __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned char* smem) {
   constexpr int KS = D / 16, KSV = DV / 16, CB = D / 32;
@@ -272,9 +271,9 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
   };
   issue(0, 0);
 
-  // B operands: Q^T and -dout^T of this wave's rows (d attn of the pair's
-  // odd head is c dout: c scales its dQ row at the store); the row's lse, E
-  // and c
+  // B operands: Q^T and -dout^T of this wave's rows; the row's lse and E
+  // (the odd head's lse carries -log2(s), so its P is s P = -c P and its dQ
+  // takes the opposite sign at the store)
   bf16x8 qf[KS], af[KSV];
   {
     const uint16_t* qr = (const uint16_t*)a.q.p + b * a.q.sb + (int64_t)row * a.q.st + h * a.q.sh;
@@ -288,7 +287,6 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
   }
   const int64_t rr = ((int64_t)b * a.Hq + h) * a.Tp + min(row, a.Tp - 1);
   float lse_r = a.lsew[rr], D_r = a.Dw[rr];
-  float c_r = (h & 1) ? a.cw[((int64_t)b * (a.Hq / 2) + (h >> 1)) * a.Tp + min(row, a.Tp - 1)] : 1.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) retire(qf[ks]);
 #pragma unroll
@@ -299,7 +297,6 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
   }
   retire(lse_r);
   retire(D_r);
-  retire(c_r);
   // Row reads (K rows for S^T, V rows for dP^T): chunk (2 ks + hg) ^
   // swizzle(li) = 2 ks ^ (hg ^ swizzle(li)), so the address is
   // (tile base + lane part) ^ 32 ks.
@@ -389,9 +386,9 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, unsigned 
       }
   }
   if (!active || row >= T) return;
-  // dQ^T[c][row]: c = 32 cb + 8 (r>>2) + 4 hg + (r&3); dq = c_row dS k / sqrt d
+  // dQ^T[c][row]: c = 32 cb + 8 (r>>2) + 4 hg + (r&3); dq = dS k / sqrt d
   uint16_t* dst = (uint16_t*)a.dq.p + b * a.dq.sb + (int64_t)row * a.dq.st + h * a.dq.sh;
-  const float sc = -a.scale * c_r;
+  const float sc = (h & 1) ? a.scale : -a.scale;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -441,7 +438,7 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   constexpr int NW = 2 * kNW;
   constexpr int KS = D / 16, CB = D / 32;
   constexpr int TB = kBT * 2 * D;      // bytes of one tensor tile
-  constexpr int STAGE = 3 * TB + 768;  // [Q_2p | Q_2p+1 | dout (both ways) | lse x 2, E x 2, c of the 32 rows]
+  constexpr int STAGE = 3 * TB + 512;  // [Q_2p | Q_2p+1 | dout (both ways) | lse x 2, E x 2 of the 32 rows]
   static_assert(STAGE % 256 == 0 && TB % 256 == 0, "tile bases leave the row's chunk bits free");
   constexpr int PSLOT = 2 * 1024;      // P_2p of one key block: 64 lanes x 2 x 16 bytes
   constexpr int GSLOT = 4 * 1024;      // -G of one key block: 64 lanes x 4 x 16 bytes
@@ -493,20 +490,19 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
   }
 
   // Copies.  Q of both heads and dout are each read as rows and transposed:
-  // one copy each in the both-ways layout.  Waves 3-7 copy the rows' lse and
-  // E of both heads and c (padded arrays: always in bounds).
+  // one copy each in the both-ways layout.  Waves 4-7 copy the rows' lse and
+  // E of both heads (padded arrays: always in bounds).
   TileCopy<D, NW> cq0, cq1, co;
   cq0.init(a.q.st, kBothLayout, wave, lane);
   cq1.init(a.q.st, kBothLayout, wave, lane);
   co.init(a.dout.st, kBothLayout, wave, lane);
   const uint16_t* qg = (const uint16_t*)a.q.p + b * a.q.sb + (int64_t)g * G * a.q.sh;  // head g G, row 0
   const uint16_t* og = (const uint16_t*)a.dout.p + b * a.dout.sb + (int64_t)g * NP * a.dout.sh;
-  const int rw = wave - (NW - 5);  // 0..4 on the row copiers
-  // rows of head g G + 2p (lse, E), + 1, or of pair g NP + p (c): base at row 0, step per pair
+  const int rw = wave - (NW - 4);  // 0..3 on the row copiers
+  // rows of head g G + 2p (lse, E) or + 1: base at row 0, step per pair
   const float* rsrc = rw <= 1 ? a.lsew + ((int64_t)b * a.Hq + g * G + rw) * a.Tp
-                      : rw <= 3 ? a.Dw + ((int64_t)b * a.Hq + g * G + rw - 2) * a.Tp
-                                : a.cw + ((int64_t)b * (a.Hq / 2) + g * NP) * a.Tp;
-  const int64_t rstep = rw <= 3 ? 2 * (int64_t)a.Tp : (int64_t)a.Tp;
+                              : a.Dw + ((int64_t)b * a.Hq + g * G + rw - 2) * a.Tp;
+  const int64_t rstep = 2 * (int64_t)a.Tp;
   // the next iteration to copy: pair, first row, and the pair's head-2p / dout bases
   int iss_p = 0, iss_r0 = (nrt - 1) * kBT;
   const uint16_t* iss_q = qg;
@@ -587,14 +583,13 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
     }
     return i0;
   };
-  // S and P of head e (0: 2p, 1: 2p+1, times c) of the tile at sb, rows i0
+  // S and P of head e (0: 2p; 1: 2p+1, times -c) of the tile at sb, rows i0
   auto probs = [&](uint32_t sb, int i0, int e, f32x8& p0, f32x8& p1) {
     bf16x8 qa[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qa[ks] = lds_read16((sb + e * TB + rxs) ^ (32u * ks));
-    f32x4 lq[4], cr[4];
+    f32x4 lq[4];
     rows4(sb + 3 * TB + 128 * e + 16 * hg, lq);
-    if (e) rows4(sb + 3 * TB + 512 + 16 * hg, cr);
     f32x16 sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
@@ -623,8 +618,7 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float pr = __builtin_amdgcn_exp2f(x[r]);
-      if (e) pr *= cr[r >> 2][r & 3];  // c P_2p+1
+      const float pr = __builtin_amdgcn_exp2f(x[r]);  // P_2p, or -c P_2p+1 (its lse carries -log2(s))
       if (r < 8) p0[r] = pr; else p1[r - 8] = pr;
     }
   };
@@ -700,14 +694,14 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
         f32x8 d0, d1, c0, c1;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = r < 8 ? p0[r] : p1[r - 8];  // c P_2p+1
+          const float p = r < 8 ? p0[r] : p1[r - 8];  // -c P_2p+1
           const uint32_t w = pw[r >> 1];  // P_2p: bf16 r of the 16 (element r & 1 of word r >> 1)
           const float pe = __builtin_bit_cast(float, (r & 1) ? (w & 0xffff0000u) : (w << 16));
-          const float ds = p * (ev[r >> 2][r & 3] + gv[r >> 2][r & 3]);  // c P (E - G) = -dS
+          const float ds = p * (ev[r >> 2][r & 3] + gv[r >> 2][r & 3]);  // -c P (E - G) = dS
           if (r < 8) {
-            d0[r] = ds, c0[r] = pe + p;
+            d0[r] = ds, c0[r] = pe - p;  // P_2p + c P_2p+1
           } else {
-            d1[r - 8] = ds, c1[r - 8] = pe + p;
+            d1[r - 8] = ds, c1[r - 8] = pe - p;
           }
         }
         y[0] = cvt_bf16x8(d0);
@@ -715,11 +709,11 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
         pc[0] = cvt_bf16x8(c0);
         pc[1] = cvt_bf16x8(c1);
       }
-      accumulate(acc, sb + TB, y);       // -dK^T += Q_2p+1^T (-dS_2p+1)
+      accumulate(acc, sb + TB, y);       // B's part: dK^T += Q_2p+1^T dS_2p+1
       accumulate(accv, sb + 2 * TB, pc);  // dV^T += dout^T (P_2p + c P_2p+1)
     }
   }
-  // -dK^T = A's part + B's part (one order), through LDS once every wave is done
+  // -dK^T = A's part - B's part (one order), through LDS once every wave is done
   __syncthreads();
   f32x4* xk = (f32x4*)smem + (size_t)kb * CB * 4 * 64 + lane;  // [kb][cb][q4][lane]
   if (bwave) {
@@ -741,7 +735,7 @@ __global__ void __launch_bounds__(2 * kNW * 64, 1) bwd_dkdv_kernel(const BwdArgs
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 v4 = xk[(cb * 4 + q4) * 64];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[cb][4 * q4 + e] += v4[e];
+        for (int e = 0; e < 4; ++e) acc[cb][4 * q4 + e] -= v4[e];
       }
   }
   if (!active || key >= T) return;

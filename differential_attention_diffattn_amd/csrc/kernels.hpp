@@ -84,8 +84,7 @@ struct BwdArgs {
   TOut dq, dk, dv;   // bf16, layouts of q / k / v
   TOut dlam;         // [B,T,Hq/2] fp32
   float* Dw;         // workspace [B][Hq][Tp]: E_h = rowsum(dout * attn_h)
-  float* lsew;       // workspace [B][Hq][Tp]: lse, padded with zeros
-  float* cw;         // workspace [B][Hq/2][Tp]: c = -sigmoid(lam) (d attn of the odd head = c dout)
+  float* lsew;       // workspace [B][Hq][Tp]: lse (odd heads: lse - log2 sigmoid(lam)), padded with zeros
   float sl2;         // log2(e) / sqrt(d)
   float scale;       // 1 / sqrt(d)
   int B, T, Hq, Hkv, G, Tp;

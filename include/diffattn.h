@@ -317,8 +317,8 @@ da_status diffattn_v2_fwd_train_softmax1(int dtype, int B, int T, int Hq, int Hk
 
 /*
  * Bytes of device workspace diffattn_v2_bwd needs (0 if the sizes are
- * invalid): two fp32 arrays of B*Hq rows and one of B*Hq/2 rows, each row
- * padded to a multiple of 128 tokens.
+ * invalid): two fp32 arrays of B*Hq rows, each row padded to a multiple of
+ * 128 tokens.
  */
 size_t diffattn_v2_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d);
 
