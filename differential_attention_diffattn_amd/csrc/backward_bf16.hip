@@ -15,16 +15,17 @@
 //   one G = dout v^T and D_h = c_h E_h with E_h = rowsum(dout o attn_h).
 //
 // Three kernels (designed for gfx950):
-//   * bwd_pre: 16 lanes per (b, token, pair): E of both heads, c = -sigmoid
-//     (lam), d lam, and a copy of lse padded to a multiple of 128 rows (so
-//     row blocks read whole float4 groups).
+//   * bwd_pre: 16 lanes per (b, token, pair): E of both heads, d lam, and a
+//     copy of lse padded to a multiple of 128 rows (so row blocks read whole
+//     float4 groups), the odd head's as lse - log2(sigmoid(lam)) so that the
+//     P rebuilt from it carries the factor -c.
 //   * bwd_dq: the forward's structure with the key loop kept: a wave owns 32
 //     query rows of one head, K/V tiles of 32 keys stream through LDS
 //     (global_load_lds), S^T = K Q^T and G^T = V dout^T come from
 //     v_mfma_f32_32x32x16_bf16 with Q / dout fragments held in registers,
 //     and dQ^T += K^T dS^T takes K^T through ds_read_b64_tr_b16 (K is copied
 //     to LDS once, in a layout that serves both reads); the odd head's dQ
-//     row is scaled by c at the store.
+//     takes the sign of -c at the store.
 //   * bwd_dkdv: the mirror image: two waves own 32 keys of one kv head and
 //     loop over the query rows at or after their keys and the group's head
 //     pairs, forming S of each head, G and dV once per pair, and dK of each
